@@ -1,0 +1,283 @@
+/*
+ * ORACLE — test infrastructure, not part of the product.
+ *
+ * A plain, slow, fp64 CPU evaluation of the routed ternary-expert FFN layer
+ * (router -> softmax/top-k -> per-expert SwiGLU FFN with ternary weights and
+ * one alpha per output row -> weighted combine), and of a stack of such layers
+ * joined by a residual add.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * Sources of each step (the pages print no code and no worked example):
+ *   - Ternary weights w in {-1, 0, +1} scaled by one learned alpha per row;
+ *     a +alpha weight adds the input, -alpha subtracts it, 0 skips it
+ *     (linlog.top article "Maple-Preview", section
+ *     "三值权重：把乘法变成加法"; architecture table row
+ *     "权重精度: 2-bit 三值（每行一个 α 缩放因子）").
+ *     Hence y_i = alpha_i * sum_j w_ij x_j: the oracle evaluates exactly this
+ *     sum in fp64 (every product w_ij x_j is exact).
+ *   - 256 experts, top-8 routing, 24 layers (same article, architecture
+ *     table; papers.ananclaw.com guide "Maple-Preview：三元权重量化推理模型",
+ *     section "这是什么", parameter table).
+ *   - Router = softmax over all experts, selection of the k largest with ties
+ *     to the lower expert index, SwiGLU experts (silu on the gate branch,
+ *     times up, then down), weighted combine: the pages are silent on these;
+ *     this is the plainest reading of a "softmax router / top-8 / SwiGLU"
+ *     MoE FFN and is listed among the readings of the pages.
+ *
+ * Packed weight layout ("layout v1", our own, since the pages only say
+ * "2-bit"): code c = w + 1 in {0,1,2} (3 is invalid).  A matrix is stored
+ * row-major with the reduction index k contiguous; each row is cols/16
+ * little-endian 32-bit words, and k = 16*word + 4*b + q lives in byte q of
+ * that word at bits [2b, 2b+1].  One expert's blob is
+ * [W_gate (I x H)][W_up (I x H)][W_down (H x I)], expert e at byte
+ * e * 3*H*I/4; alphas are fp32 [E][alpha_gate(I) | alpha_up(I) | alpha_down(H)].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- layout v1: one code ------------------------------------------------ */
+
+static int code_at(const uint8_t* row, int64_t k) {
+  const int64_t word = k >> 4;
+  const int q = (int)(k & 3);
+  const int b = (int)((k >> 2) & 3);
+  return (row[4 * word + q] >> (2 * b)) & 3;
+}
+
+/* Pack int8 values in {-1,0,+1} of a [rows x cols] matrix into layout v1.
+ * Returns 0, -1 for a value outside {-1,0,+1}, -2 if cols % 16 != 0. */
+int oracle_pack(const int8_t* w, int64_t rows, int64_t cols, uint8_t* out) {
+  if (cols % 16 != 0) return -2;
+  const int64_t row_bytes = cols / 4;
+  memset(out, 0, (size_t)(rows * row_bytes));
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t k = 0; k < cols; ++k) {
+      const int v = w[r * cols + k];
+      if (v < -1 || v > 1) return -1;
+      const int64_t word = k >> 4;
+      const int q = (int)(k & 3);
+      const int b = (int)((k >> 2) & 3);
+      out[r * row_bytes + 4 * word + q] |= (uint8_t)((v + 1) << (2 * b));
+    }
+  }
+  return 0;
+}
+
+/* Unpack layout v1 back to int8 {-1,0,+1}.  Returns 0, or -1 if any code is 3
+ * (the values of that code are written as 2, i.e. left for the caller to see). */
+int oracle_unpack(const uint8_t* p, int64_t rows, int64_t cols, int8_t* w) {
+  if (cols % 16 != 0) return -2;
+  const int64_t row_bytes = cols / 4;
+  int bad = 0;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < cols; ++k) {
+      const int c = code_at(p + r * row_bytes, k);
+      if (c == 3) bad = 1;
+      w[r * cols + k] = (int8_t)(c - 1);
+    }
+  return bad ? -1 : 0;
+}
+
+/* ---- router ------------------------------------------------------------- */
+
+/* logits[t,e] = sum_j W_r[e,j] * x[t,j] (+ bias[e]), fp64, j ascending. */
+void oracle_router_logits(const double* x, int64_t T, int32_t H, const float* Wr,
+                          const float* bias, int32_t E, double* logits) {
+#pragma omp parallel for schedule(static) if (T * E > 64)
+  for (int64_t te = 0; te < T * E; ++te) {
+    const int64_t t = te / E;
+    const int32_t e = (int32_t)(te % E);
+    double acc = 0.0;
+    for (int32_t j = 0; j < H; ++j) acc += (double)Wr[(int64_t)e * H + j] * x[t * H + j];
+    if (bias) acc += (double)bias[e];
+    logits[te] = acc;
+  }
+}
+
+/* Softmax over all E experts (max-subtracted), then the k experts that come
+ * first in the order (logit descending, expert index ascending).
+ * gate[t,j] = p[idx[t,j]], divided by the selected mass when renorm != 0. */
+void oracle_topk(const double* logits, int64_t T, int32_t E, int32_t k, int32_t renorm,
+                 int32_t* idx, double* gate) {
+  for (int64_t t = 0; t < T; ++t) {
+    const double* l = logits + t * E;
+    double m = l[0];
+    for (int32_t e = 1; e < E; ++e)
+      if (l[e] > m) m = l[e];
+    double z = 0.0;
+    for (int32_t e = 0; e < E; ++e) z += exp(l[e] - m);
+    char* taken = (char*)calloc((size_t)E, 1);
+    double mass = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e; /* strict >: ties keep the lower index */
+      }
+      taken[best] = 1;
+      idx[t * k + j] = best;
+      gate[t * k + j] = exp(l[best] - m) / z;
+      mass += gate[t * k + j];
+    }
+    if (renorm)
+      for (int32_t j = 0; j < k; ++j) gate[t * k + j] /= mass;
+    free(taken);
+  }
+}
+
+/* ---- grouping ----------------------------------------------------------- */
+
+/* All (expert, token) pairs of the routing, listed in (expert asc, token asc)
+ * order.  offsets[e] = number of pairs with expert < e (E+1 entries);
+ * sorted_token[p] = token of pair p; slot_pos[t*k+j] = position of the pair
+ * (idx[t,j], t).  A token selects an expert at most once. */
+void oracle_permute(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t* offsets,
+                    int32_t* sorted_token, int32_t* slot_pos) {
+  int64_t pos = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)pos;
+    for (int64_t t = 0; t < T; ++t)
+      for (int32_t j = 0; j < k; ++j)
+        if (idx[t * k + j] == e) {
+          sorted_token[pos] = (int32_t)t;
+          slot_pos[t * k + j] = (int32_t)pos;
+          ++pos;
+        }
+  }
+  offsets[E] = (int32_t)pos;
+}
+
+/* ---- one expert --------------------------------------------------------- */
+
+/* sum_j w_rj * v_j for one packed row (layout v1), fp64, j ascending. */
+static double ternary_dot(const uint8_t* row, const double* v, int32_t n) {
+  double acc = 0.0;
+  for (int32_t j = 0; j < n; ++j) acc += (double)(code_at(row, j) - 1) * v[j];
+  return acc;
+}
+
+/* g = alpha_g * (W_g x), u = alpha_u * (W_u x), h = silu(g) * u with
+ * silu(z) = z / (1 + exp(-z)), y = alpha_d * (W_d h).  Outputs g, u may be
+ * NULL; h (I doubles) and y (H doubles) are required. */
+void oracle_expert_ffn(const double* x, int32_t H, int32_t I, const uint8_t* blob,
+                       const float* alpha, double* g, double* u, double* h, double* y,
+                       int32_t parallel) {
+  const uint8_t* Wg = blob;
+  const uint8_t* Wu = blob + (int64_t)I * H / 4;
+  const uint8_t* Wd = blob + 2 * (int64_t)I * H / 4;
+  const float* ag = alpha;
+  const float* au = alpha + I;
+  const float* ad = alpha + 2 * I;
+#pragma omp parallel for schedule(static) if (parallel)
+  for (int32_t i = 0; i < I; ++i) {
+    const double gi = (double)ag[i] * ternary_dot(Wg + (int64_t)i * H / 4, x, H);
+    const double ui = (double)au[i] * ternary_dot(Wu + (int64_t)i * H / 4, x, H);
+    if (g) g[i] = gi;
+    if (u) u[i] = ui;
+    h[i] = gi / (1.0 + exp(-gi)) * ui;
+  }
+#pragma omp parallel for schedule(static) if (parallel)
+  for (int32_t o = 0; o < H; ++o) y[o] = (double)ad[o] * ternary_dot(Wd + (int64_t)o * I / 4, h, I);
+}
+
+/* ---- one layer ---------------------------------------------------------- */
+
+static void layer_token(int32_t H, int32_t E, int32_t k, int32_t I, const double* xt,
+                        const uint8_t* packed, const float* alpha, const int32_t* idx_t,
+                        const double* gate_t, double* out_t, double* h, double* y, int32_t par) {
+  const int64_t blob = 3 * (int64_t)H * I / 4;
+  for (int32_t o = 0; o < H; ++o) out_t[o] = 0.0;
+  for (int32_t j = 0; j < k; ++j) {
+    const int32_t e = idx_t[j];
+    oracle_expert_ffn(xt, H, I, packed + e * blob, alpha + (int64_t)e * (2 * I + H), NULL, NULL,
+                      h, y, par);
+    for (int32_t o = 0; o < H; ++o) out_t[o] += gate_t[j] * y[o];
+  }
+  (void)E;
+}
+
+/* out[t] = sum_j gate[t,j] * FFN_{idx[t,j]}(x[t]), summed in selection order.
+ * logits (T x E), idx (T x k), gate (T x k) receive the routing. */
+int oracle_moe_layer(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm, int64_t T,
+                     const double* x, const float* Wr, const float* bias, const uint8_t* packed,
+                     const float* alpha, double* out, double* logits, int32_t* idx,
+                     double* gate) {
+  if (H <= 0 || I <= 0 || H % 16 || I % 16 || k < 1 || k > E || T < 0) return -1;
+  if (T == 0) return 0;
+  oracle_router_logits(x, T, H, Wr, bias, E, logits);
+  oracle_topk(logits, T, E, k, renorm, idx, gate);
+  int nthreads = 1;
+#ifdef _OPENMP
+  nthreads = omp_get_max_threads();
+#endif
+  if (T >= 2 * nthreads) {
+#pragma omp parallel
+    {
+      double* h = (double*)malloc(sizeof(double) * (size_t)I);
+      double* y = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < T; ++t)
+        layer_token(H, E, k, I, x + t * H, packed, alpha, idx + t * k, gate + t * k,
+                    out + t * H, h, y, 0);
+      free(h);
+      free(y);
+    }
+  } else {
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int64_t t = 0; t < T; ++t)
+      layer_token(H, E, k, I, x + t * H, packed, alpha, idx + t * k, gate + t * k, out + t * H,
+                  h, y, 1);
+    free(h);
+    free(y);
+  }
+  return 0;
+}
+
+/* ---- stack -------------------------------------------------------------- */
+
+/* x^(l+1) = x^(l) + MoE_l(x^(l)) for l = 0..L-1, in place on x (T x H).
+ * Per-layer routing and deltas go to the optional outputs:
+ * logits_all [L,T,E], idx_all [L,T,k], gate_all [L,T,k], delta_all [L,T,H]. */
+int oracle_moe_stack(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                     int32_t n_layers, int64_t T, double* x, const float* const* Wr,
+                     const float* const* bias, const uint8_t* const* packed,
+                     const float* const* alpha, double* logits_all, int32_t* idx_all,
+                     double* gate_all, double* delta_all) {
+  if (n_layers < 0) return -1;
+  double* out = (double*)malloc(sizeof(double) * (size_t)(T * H + 1));
+  double* lg = logits_all ? NULL : (double*)malloc(sizeof(double) * (size_t)(T * E + 1));
+  int32_t* id = idx_all ? NULL : (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k + 1));
+  double* gt = gate_all ? NULL : (double*)malloc(sizeof(double) * (size_t)(T * k + 1));
+  int rc = 0;
+  for (int32_t l = 0; l < n_layers && rc == 0; ++l) {
+    double* L_lg = logits_all ? logits_all + (int64_t)l * T * E : lg;
+    int32_t* L_id = idx_all ? idx_all + (int64_t)l * T * k : id;
+    double* L_gt = gate_all ? gate_all + (int64_t)l * T * k : gt;
+    rc = oracle_moe_layer(H, E, k, I, renorm, T, x, Wr[l], bias ? bias[l] : NULL, packed[l],
+                          alpha[l], out, L_lg, L_id, L_gt);
+    for (int64_t i = 0; i < T * H; ++i) {
+      x[i] += out[i];
+      if (delta_all) delta_all[(int64_t)l * T * H + i] = out[i];
+    }
+  }
+  free(out);
+  free(lg);
+  free(id);
+  free(gt);
+  return rc;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
