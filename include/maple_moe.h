@@ -1,0 +1,192 @@
+/*
+ * maple_moe.h — C ABI of the routed ternary-expert FFN library for MI355X
+ * (gfx950): libmaple_moe.so.
+ *
+ * What it computes.  One MoE feed-forward layer of a Maple-Preview-style
+ * model: 256 experts per layer, the top 8 routed per token, 24 layers
+ * (papers.ananclaw.com guide "Maple-Preview：三元权重量化推理模型", section
+ * "这是什么", parameter table; linlog.top article "Maple-Preview", section
+ * "架构设计：为推理速度而生", architecture table).  Every expert weight is
+ * -alpha, 0 or +alpha with one learned alpha per row, stored at 2 bits, so a
+ * matrix-vector product becomes adds, subtracts and skips followed by one
+ * scale per row (linlog.top article, section "三值权重：把乘法变成加法").
+ * For token x (H values):
+ *
+ *   logits_e = sum_j W_r[e,j] x_j (+ bias_e)                       router
+ *   S        = the k experts first in the order (logit desc, index asc)
+ *   p        = softmax(logits) over all E experts;  gate_e = p_e, e in S
+ *              (divided by sum_{e in S} p_e with MAPLE_RENORM_TOPK)
+ *   g_i = a_g[i] sum_j wg_ij x_j,  u_i = a_u[i] sum_j wu_ij x_j     i < I
+ *   h_i = silu(g_i) u_i,  silu(z) = z / (1 + exp(-z))               SwiGLU
+ *   y_o = a_d[o] sum_i wd_oi h_i                                    o < H
+ *   out = sum_{e in S} gate_e y^(e)
+ *
+ * The router nonlinearity, tie rule and SwiGLU form are not given by the
+ * pages; they are the readings this library implements.
+ *
+ * Conventions for every entry point:
+ *   - Status: each function returns 0 (MAPLE_OK) or a negative maple_status;
+ *     maple_last_error() gives a thread-local text for the last failure.
+ *   - Validation of dims, sizes, pointers and alignment happens before any
+ *     HIP call, so it works (and fails cleanly) on machines without a GPU.
+ *   - Ownership: the caller owns every buffer; the forward entry points never
+ *     allocate or free device memory.  Only maple_graph handles own memory.
+ *   - Asynchrony: device work is enqueued on `stream` (a hipStream_t, NULL for
+ *     the default stream); results are valid after the stream is synchronised.
+ *     Launch errors are reported as MAPLE_ERR_HIP; faults surface at the
+ *     caller's synchronisation.  No C++ exception crosses the ABI.
+ *   - Reentrancy: functions are reentrant; two calls that share a workspace
+ *     must not overlap in time (same stream, or externally ordered).
+ *
+ * Packed ternary layout ("layout v1").  Code c = w + 1 in {0,1,2}; 3 is
+ * invalid.  A matrix is row-major with its reduction index k contiguous; each
+ * row is cols/16 little-endian 32-bit words, and k = 16*word + 4*b + q sits in
+ * byte q of its word at bits [2b, 2b+1].  Thus (word >> 2b) & 0x03030303 holds
+ * the codes of four consecutive k, one per byte.
+ * Per expert, one blob of 3*H*I/4 bytes:
+ *   [W_gate (I rows x H)][W_up (I rows x H)][W_down (H rows x I)];
+ * per layer, the E blobs back to back (expert e at byte e*3*H*I/4).
+ * Alphas: fp32 [E][a_g (I) | a_u (I) | a_d (H)].  Router: fp32 [E][H].
+ */
+#ifndef MAPLE_MOE_H
+#define MAPLE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum maple_status {
+  MAPLE_OK = 0,
+  MAPLE_ERR_INVALID_ARG = -1,       /* null pointer, negative size, unknown flag */
+  MAPLE_ERR_UNSUPPORTED_SHAPE = -2, /* dims outside the supported limits */
+  MAPLE_ERR_ALIGNMENT = -3,         /* a pointer is not aligned as documented */
+  MAPLE_ERR_WORKSPACE_TOO_SMALL = -4,
+  MAPLE_ERR_INVALID_CODE = -5,      /* a packed code equals 3, or a weight is not in {-1,0,1} */
+  MAPLE_ERR_NO_DEVICE = -6,         /* no usable HIP device */
+  MAPLE_ERR_HIP = -7                /* a HIP runtime call or launch failed */
+} maple_status;
+
+/* dims.flags */
+#define MAPLE_X_BF16 0x1u         /* x is bf16 [T,H] (else fp32) */
+#define MAPLE_RENORM_TOPK 0x2u    /* gates divided by their sum over the selected experts */
+#define MAPLE_FORCE_GEMV 0x10u    /* expert FFN on the VALU GEMV path whatever T is */
+#define MAPLE_FORCE_GROUPED 0x20u /* expert FFN on the grouped int8-MFMA path whatever T is */
+
+/* Limits: hidden a power of two in [256, 4096]; inter a power of two in
+ * [128, 2048]; 1 <= top_k <= 8; top_k <= n_experts <= 256;
+ * 0 <= n_tokens <= MAPLE_MAX_TOKENS.  The GEMV path takes n_tokens <= 64. */
+#define MAPLE_MAX_TOKENS (1 << 20)
+#define MAPLE_GEMV_MAX_TOKENS 64
+
+typedef struct maple_moe_dims {
+  int32_t hidden;    /* H */
+  int32_t n_experts; /* E */
+  int32_t top_k;     /* k */
+  int32_t inter;     /* I, expert intermediate width */
+  uint32_t flags;
+} maple_moe_dims;
+
+/* Optional device buffers that receive the routing of a call (any may be
+ * NULL).  For the stack entry points each array holds n_layers consecutive
+ * per-layer blocks of the size given here. */
+typedef struct maple_moe_debug {
+  int32_t* idx;          /* [T,k] selected experts, in selection order */
+  float* gate;           /* [T,k] gate weights */
+  float* logits;         /* [T,E] router logits */
+  int32_t* offsets;      /* [E+1] first sorted slot of each expert */
+  int32_t* sorted_token; /* [T*k] token of each slot, (expert asc, token asc) order */
+  int32_t* slot_pos;     /* [T,k] sorted position of slot (t, j) */
+  float* delta;          /* [T,H] layer output before the residual add (stack only) */
+} maple_moe_debug;
+
+typedef struct maple_graph maple_graph;
+
+/* Text of a status code (static storage). */
+const char* maple_status_string(int status);
+/* Detail of the last failure on this thread ("" if none). */
+const char* maple_last_error(void);
+/* Library version: major*10000 + minor*100 + patch. */
+int maple_version(void);
+
+/* Bytes of workspace that a layer or stack call with up to max_tokens tokens
+ * needs (the same figure serves both).  Validates dims.  The workspace must be
+ * device memory aligned to 256 bytes. */
+int maple_moe_workspace_bytes(const maple_moe_dims* dims, int32_t max_tokens, size_t* bytes);
+
+/* ---- packing (layout v1) ------------------------------------------------ */
+
+/* Host: pack int8 weights w[rows][cols] (values in {-1,0,1}) into
+ * out[rows][cols/4] bytes.  cols % 16 == 0.  MAPLE_ERR_INVALID_CODE if a value
+ * is outside {-1,0,1} (out is then partially written). */
+int maple_ternary_pack_host(const int8_t* w, int64_t rows, int64_t cols, uint8_t* out);
+/* Host: inverse of the above.  MAPLE_ERR_INVALID_CODE if a code equals 3. */
+int maple_ternary_unpack_host(const uint8_t* packed, int64_t rows, int64_t cols, int8_t* w);
+/* Host: MAPLE_OK if no 2-bit code in packed[0..n_bytes) equals 3. */
+int maple_ternary_validate_host(const uint8_t* packed, size_t n_bytes);
+/* Device: pack n_values int8 weights (n_values % 16 == 0; every run of 16
+ * consecutive values is one word, so a whole layer [E][3*H*I] packs in one
+ * call).  w and out device pointers, 16- and 4-byte aligned.  bad_count, if
+ * not NULL, is a device int32 that receives the number of values outside
+ * {-1,0,1} (it is overwritten, not accumulated). */
+int maple_ternary_pack_device(const int8_t* w, int64_t n_values, uint8_t* out,
+                              int32_t* bad_count, void* stream);
+
+/* ---- forward ------------------------------------------------------------ */
+
+/* One MoE layer, out = MoE(x) (no residual), for n_tokens tokens.
+ *   x          [T,H] bf16 (MAPLE_X_BF16) or fp32, device, 16-byte aligned
+ *   router_w   [E,H] fp32, device, 16-byte aligned
+ *   router_bias[E] fp32 device, or NULL
+ *   packed_w   layer blob in layout v1, device, 256-byte aligned
+ *   alpha      [E][2I+H] fp32, device, 16-byte aligned
+ *   out        [T,H] fp32, device, 16-byte aligned; may not alias x
+ *   workspace  >= maple_moe_workspace_bytes(dims, n_tokens), 256-byte aligned
+ *   dbg        NULL, or a host struct of optional device pointers
+ * n_tokens == 0 returns MAPLE_OK without touching the device. */
+int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const void* x,
+                            const float* router_w, const float* router_bias,
+                            const uint8_t* packed_w, const float* alpha, float* out,
+                            void* workspace, size_t ws_bytes, const maple_moe_debug* dbg,
+                            void* stream);
+
+/* A stack of n_layers MoE layers joined by a residual add, in place:
+ * x <- x + MoE_l(x) for l = 0..n_layers-1.  x_inout [T,H] fp32 device.
+ * router_w, packed_w, alpha: host arrays of n_layers device pointers;
+ * router_bias: NULL or a host array of n_layers device pointers (entries may be
+ * NULL).  dims.flags' MAPLE_X_BF16 is ignored (the residual stream is fp32). */
+int maple_moe_stack_forward(const maple_moe_dims* dims, int32_t n_layers, int32_t n_tokens,
+                            float* x_inout, const float* const* router_w,
+                            const float* const* router_bias, const uint8_t* const* packed_w,
+                            const float* const* alpha, void* workspace, size_t ws_bytes,
+                            const maple_moe_debug* dbg, void* stream);
+
+/* ---- captured decode step ----------------------------------------------- */
+
+/* Capture one decode step of the stack into a HIP graph.  Each launch takes
+ * step s from a device counter (starting at 0), loads token block
+ * staged_x[s mod n_staged] ([n_staged][T][H], bf16 if MAPLE_X_BF16 else fp32)
+ * into x_work ([T,H] fp32) as the residual stream, runs the n_layers layers
+ * and, if out_all is not NULL, copies the final residual stream to
+ * out_all[s mod n_staged] ([n_staged][T][H] fp32); then the counter advances.
+ * All pointers must stay valid for the graph's lifetime.  The handle owns the
+ * graph and a 256-byte device counter. */
+int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, int32_t n_tokens,
+                                 const void* staged_x, int32_t n_staged, float* x_work,
+                                 float* out_all, const float* const* router_w,
+                                 const float* const* router_bias,
+                                 const uint8_t* const* packed_w, const float* const* alpha,
+                                 void* workspace, size_t ws_bytes, maple_graph** graph);
+/* Launch one captured step on `stream`. */
+int maple_graph_launch(maple_graph* graph, void* stream);
+/* Set the step counter (ordered on `stream`). */
+int maple_graph_set_step(maple_graph* graph, int32_t step, void* stream);
+/* Release the graph and its counter (synchronises the device first). */
+int maple_graph_destroy(maple_graph* graph);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAPLE_MOE_H */

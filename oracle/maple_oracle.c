@@ -55,18 +55,23 @@ static int code_at(const uint8_t* row, int64_t k) {
 int oracle_pack(const int8_t* w, int64_t rows, int64_t cols, uint8_t* out) {
   if (cols % 16 != 0) return -2;
   const int64_t row_bytes = cols / 4;
-  memset(out, 0, (size_t)(rows * row_bytes));
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad) if (rows * cols > (1 << 16))
   for (int64_t r = 0; r < rows; ++r) {
+    memset(out + r * row_bytes, 0, (size_t)row_bytes);
     for (int64_t k = 0; k < cols; ++k) {
       const int v = w[r * cols + k];
-      if (v < -1 || v > 1) return -1;
+      if (v < -1 || v > 1) {
+        bad = 1;
+        continue;
+      }
       const int64_t word = k >> 4;
       const int q = (int)(k & 3);
       const int b = (int)((k >> 2) & 3);
       out[r * row_bytes + 4 * word + q] |= (uint8_t)((v + 1) << (2 * b));
     }
   }
-  return 0;
+  return bad ? -1 : 0;
 }
 
 /* Unpack layout v1 back to int8 {-1,0,+1}.  Returns 0, or -1 if any code is 3

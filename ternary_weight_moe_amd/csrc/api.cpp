@@ -1,0 +1,479 @@
+// C-ABI layer of libmaple_moe.so: argument validation (before any HIP call),
+// workspace carving, dispatch to the kernels and HIP-graph capture of a
+// decode step.  See include/maple_moe.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+#include "maple_moe.h"
+
+struct maple_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int32_t* counter = nullptr;
+  int device = 0;
+};
+
+namespace maple {
+
+// Token count up to which the automatic dispatch uses the VALU GEMV path.
+constexpr int64_t kGemvAuto = 16;
+constexpr int kTileM = 64;
+
+int max_tiles(const Dims& d, int64_t T) { return (int)((T * d.k) / kTileM + d.E + 1); }
+
+size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  const int64_t Tk = T * d.k;
+  const int64_t nb = (T + 63) / 64;
+  const int64_t kb = d.I / 128;
+  ws->logits = (float*)take(sizeof(float) * T * d.E);
+  ws->idx = (int32_t*)take(sizeof(int32_t) * Tk);
+  ws->gate = (float*)take(sizeof(float) * Tk);
+  ws->offsets = (int32_t*)take(sizeof(int32_t) * (d.E + 1));
+  ws->active = (int32_t*)take(sizeof(int32_t) * d.E);
+  ws->n_active = (int32_t*)take(256);
+  ws->n_tiles = ws->n_active ? ws->n_active + 16 : nullptr;
+  ws->sorted_tok = (int32_t*)take(sizeof(int32_t) * Tk);
+  ws->slot_pos = (int32_t*)take(sizeof(int32_t) * Tk);
+  ws->blk_count = (int32_t*)take(sizeof(int32_t) * nb * d.E);
+  ws->blk_rank = (int32_t*)take(sizeof(int32_t) * Tk);
+  ws->tiles = (int32_t*)take(sizeof(int32_t) * 2 * (size_t)max_tiles(d, T));
+  ws->h = (float*)take(sizeof(float) * Tk * d.I);
+  ws->xq = (int8_t*)take((size_t)T * 2 * d.H);
+  ws->xs = (float*)take(sizeof(float) * 2 * T);  // scale and (bit-cast) limb row sum
+  ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
+  ws->hs = (float*)take(sizeof(float) * 2 * Tk * kb);
+  ws->y = (float*)take(sizeof(float) * Tk * d.H);
+  ws->bytes = off;
+  return off;
+}
+
+}  // namespace maple
+
+using maple::Dims;
+using maple::Workspace;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MAPLE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+constexpr uint32_t kKnownFlags =
+    MAPLE_X_BF16 | MAPLE_RENORM_TOPK | MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED;
+
+int check_dims(const maple_moe_dims* d, Dims* out) {
+  if (!d) return fail(MAPLE_ERR_INVALID_ARG, "dims is NULL");
+  if (d->flags & ~kKnownFlags) return fail(MAPLE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if ((d->flags & MAPLE_FORCE_GEMV) && (d->flags & MAPLE_FORCE_GROUPED))
+    return fail(MAPLE_ERR_INVALID_ARG, "MAPLE_FORCE_GEMV and MAPLE_FORCE_GROUPED both set");
+  if (!is_pow2(d->hidden) || d->hidden < 256 || d->hidden > 4096)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "hidden=%d: need a power of two in [256, 4096]",
+                d->hidden);
+  if (!is_pow2(d->inter) || d->inter < 128 || d->inter > 2048)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "inter=%d: need a power of two in [128, 2048]",
+                d->inter);
+  if (d->top_k < 1 || d->top_k > 8)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "top_k=%d: need 1..8", d->top_k);
+  if (d->n_experts < d->top_k || d->n_experts > 256)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_experts=%d: need top_k..256", d->n_experts);
+  *out = Dims{d->hidden, d->n_experts, d->top_k, d->inter, d->flags};
+  return MAPLE_OK;
+}
+
+int check_tokens(const Dims& d, int64_t T) {
+  if (T < 0) return fail(MAPLE_ERR_INVALID_ARG, "n_tokens=%lld < 0", (long long)T);
+  if (T > MAPLE_MAX_TOKENS)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_tokens=%lld > %d", (long long)T, MAPLE_MAX_TOKENS);
+  if ((d.flags & MAPLE_FORCE_GEMV) && T > MAPLE_GEMV_MAX_TOKENS)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "MAPLE_FORCE_GEMV with n_tokens=%lld > %d",
+                (long long)T, MAPLE_GEMV_MAX_TOKENS);
+  return MAPLE_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(MAPLE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % align)
+    return fail(MAPLE_ERR_ALIGNMENT, "%s=%p is not %zu-byte aligned", name, p, align);
+  return MAPLE_OK;
+}
+
+int check_opt_ptr(const void* p, size_t align, const char* name) {
+  return p ? check_ptr(p, align, name) : MAPLE_OK;
+}
+
+int device_ready() {
+  static std::once_flag once;
+  static int status = MAPLE_OK;
+  static char msg[256] = "";
+  std::call_once(once, [] {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0) {
+      status = MAPLE_ERR_NO_DEVICE;
+      snprintf(msg, sizeof msg, "no HIP device (%s, count=%d)", hipGetErrorString(e), n);
+    }
+  });
+  if (status != MAPLE_OK) return fail(status, "%s", msg);
+  return MAPLE_OK;
+}
+
+bool use_gemv(const Dims& d, int64_t T) {
+  if (d.flags & MAPLE_FORCE_GEMV) return true;
+  if (d.flags & MAPLE_FORCE_GROUPED) return false;
+  return T <= maple::kGemvAuto;
+}
+
+// One layer on the device: router, routing, expert FFN (+ combine).
+int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
+              const float* bias, const uint8_t* packed, const float* alpha, float* out,
+              const float* resid, float* delta, const Workspace& ws, const maple_moe_debug* dbg,
+              hipStream_t s) {
+  hipError_t e = maple::launch_router(d, T, x, x_bf16, Wr, bias, ws.logits, s);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  e = maple::launch_route(d, T, ws.logits, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "routing launch");
+  if (use_gemv(d, T))
+    e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
+  else
+    e = maple::launch_grouped_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
+  if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
+  if (dbg) {
+    const int64_t Tk = T * d.k;
+    struct {
+      void* dst;
+      const void* src;
+      size_t n;
+    } cp[] = {{dbg->idx, ws.idx, sizeof(int32_t) * Tk},
+              {dbg->gate, ws.gate, sizeof(float) * Tk},
+              {dbg->logits, ws.logits, sizeof(float) * T * d.E},
+              {dbg->offsets, ws.offsets, sizeof(int32_t) * (d.E + 1)},
+              {dbg->sorted_token, ws.sorted_tok, sizeof(int32_t) * Tk},
+              {dbg->slot_pos, ws.slot_pos, sizeof(int32_t) * Tk}};
+    for (auto& c : cp)
+      if (c.dst) {
+        e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "debug copy");
+      }
+  }
+  return MAPLE_OK;
+}
+
+maple_moe_debug layer_dbg(const maple_moe_debug* dbg, int l, int64_t T, const Dims& d) {
+  maple_moe_debug o{};
+  if (!dbg) return o;
+  const int64_t Tk = T * d.k;
+  o.idx = dbg->idx ? dbg->idx + l * Tk : nullptr;
+  o.gate = dbg->gate ? dbg->gate + l * Tk : nullptr;
+  o.logits = dbg->logits ? dbg->logits + l * T * d.E : nullptr;
+  o.offsets = dbg->offsets ? dbg->offsets + (int64_t)l * (d.E + 1) : nullptr;
+  o.sorted_token = dbg->sorted_token ? dbg->sorted_token + l * Tk : nullptr;
+  o.slot_pos = dbg->slot_pos ? dbg->slot_pos + l * Tk : nullptr;
+  o.delta = dbg->delta ? dbg->delta + l * T * d.H : nullptr;
+  return o;
+}
+
+int check_stack_args(const Dims& d, int32_t n_layers, int64_t T, const float* const* router_w,
+                     const float* const* router_bias, const uint8_t* const* packed_w,
+                     const float* const* alpha, void* workspace, size_t ws_bytes) {
+  if (n_layers < 0) return fail(MAPLE_ERR_INVALID_ARG, "n_layers=%d < 0", n_layers);
+  if (n_layers > 0 && (!router_w || !packed_w || !alpha))
+    return fail(MAPLE_ERR_INVALID_ARG, "router_w / packed_w / alpha array is NULL");
+  char name[64];
+  for (int l = 0; l < n_layers; ++l) {
+    int rc;
+    snprintf(name, sizeof name, "router_w[%d]", l);
+    if ((rc = check_ptr(router_w[l], 16, name))) return rc;
+    snprintf(name, sizeof name, "packed_w[%d]", l);
+    if ((rc = check_ptr(packed_w[l], 256, name))) return rc;
+    snprintf(name, sizeof name, "alpha[%d]", l);
+    if ((rc = check_ptr(alpha[l], 16, name))) return rc;
+    if (router_bias) {
+      snprintf(name, sizeof name, "router_bias[%d]", l);
+      if ((rc = check_opt_ptr(router_bias[l], 4, name))) return rc;
+    }
+  }
+  int rc = check_ptr(workspace, 256, "workspace");
+  if (rc) return rc;
+  Workspace tmp;
+  const size_t need = maple::carve(d, T, nullptr, &tmp);
+  if (ws_bytes < need)
+    return fail(MAPLE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", ws_bytes, need);
+  return MAPLE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* maple_status_string(int status) {
+  switch (status) {
+    case MAPLE_OK: return "MAPLE_OK";
+    case MAPLE_ERR_INVALID_ARG: return "MAPLE_ERR_INVALID_ARG";
+    case MAPLE_ERR_UNSUPPORTED_SHAPE: return "MAPLE_ERR_UNSUPPORTED_SHAPE";
+    case MAPLE_ERR_ALIGNMENT: return "MAPLE_ERR_ALIGNMENT";
+    case MAPLE_ERR_WORKSPACE_TOO_SMALL: return "MAPLE_ERR_WORKSPACE_TOO_SMALL";
+    case MAPLE_ERR_INVALID_CODE: return "MAPLE_ERR_INVALID_CODE";
+    case MAPLE_ERR_NO_DEVICE: return "MAPLE_ERR_NO_DEVICE";
+    case MAPLE_ERR_HIP: return "MAPLE_ERR_HIP";
+  }
+  return "MAPLE_ERR_UNKNOWN";
+}
+
+const char* maple_last_error(void) { return g_err; }
+
+int maple_version(void) { return 100; }
+
+int maple_moe_workspace_bytes(const maple_moe_dims* dims, int32_t max_tokens, size_t* bytes) {
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if ((rc = check_tokens(d, max_tokens))) return rc;
+  if (!bytes) return fail(MAPLE_ERR_INVALID_ARG, "bytes is NULL");
+  Workspace ws;
+  *bytes = maple::carve(d, max_tokens, nullptr, &ws);
+  return MAPLE_OK;
+}
+
+int maple_ternary_pack_host(const int8_t* w, int64_t rows, int64_t cols, uint8_t* out) {
+  if (!w || !out) return fail(MAPLE_ERR_INVALID_ARG, "w or out is NULL");
+  if (rows < 0 || cols < 0 || cols % 16)
+    return fail(MAPLE_ERR_INVALID_ARG, "rows=%lld cols=%lld (cols must be a multiple of 16)",
+                (long long)rows, (long long)cols);
+  const int64_t n_words = rows * cols / 16;
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  for (int64_t i = 0; i < n_words; ++i) {
+    uint32_t word = 0;
+    for (int kk = 0; kk < 16; ++kk) {
+      const int c = w[16 * i + kk] + 1;
+      if (c < 0 || c > 2)
+        return fail(MAPLE_ERR_INVALID_CODE, "weight %lld = %d is not in {-1,0,1}",
+                    (long long)(16 * i + kk), (int)w[16 * i + kk]);
+      word |= (uint32_t)c << (8 * (kk & 3) + 2 * (kk >> 2));
+    }
+    uint8_t bytes[4] = {(uint8_t)word, (uint8_t)(word >> 8), (uint8_t)(word >> 16),
+                        (uint8_t)(word >> 24)};
+    std::memcpy(o + i, bytes, 4);
+  }
+  return MAPLE_OK;
+}
+
+int maple_ternary_unpack_host(const uint8_t* packed, int64_t rows, int64_t cols, int8_t* w) {
+  if (!w || !packed) return fail(MAPLE_ERR_INVALID_ARG, "packed or w is NULL");
+  if (rows < 0 || cols < 0 || cols % 16)
+    return fail(MAPLE_ERR_INVALID_ARG, "rows=%lld cols=%lld (cols must be a multiple of 16)",
+                (long long)rows, (long long)cols);
+  const int64_t n_words = rows * cols / 16;
+  int bad = 0;
+  for (int64_t i = 0; i < n_words; ++i) {
+    const uint32_t word = (uint32_t)packed[4 * i] | (uint32_t)packed[4 * i + 1] << 8 |
+                          (uint32_t)packed[4 * i + 2] << 16 | (uint32_t)packed[4 * i + 3] << 24;
+    for (int kk = 0; kk < 16; ++kk) {
+      const int c = (word >> (8 * (kk & 3) + 2 * (kk >> 2))) & 3;
+      bad |= (c == 3);
+      w[16 * i + kk] = (int8_t)(c - 1);
+    }
+  }
+  if (bad) return fail(MAPLE_ERR_INVALID_CODE, "packed data holds code 3");
+  return MAPLE_OK;
+}
+
+int maple_ternary_validate_host(const uint8_t* packed, size_t n_bytes) {
+  if (!packed && n_bytes) return fail(MAPLE_ERR_INVALID_ARG, "packed is NULL");
+  for (size_t i = 0; i < n_bytes; ++i) {
+    const uint8_t b = packed[i];
+    // a 2-bit field equals 3 iff both of its bits are set
+    if ((b & (b >> 1)) & 0x55u)
+      return fail(MAPLE_ERR_INVALID_CODE, "byte %zu = 0x%02x holds code 3", i, b);
+  }
+  return MAPLE_OK;
+}
+
+int maple_ternary_pack_device(const int8_t* w, int64_t n_values, uint8_t* out,
+                              int32_t* bad_count, void* stream) {
+  int rc;
+  if (n_values < 0 || n_values % 16)
+    return fail(MAPLE_ERR_INVALID_ARG, "n_values=%lld must be a non-negative multiple of 16",
+                (long long)n_values);
+  if ((rc = check_ptr(w, 16, "w")) || (rc = check_ptr(out, 4, "out")) ||
+      (rc = check_opt_ptr(bad_count, 4, "bad_count")))
+    return rc;
+  if ((rc = device_ready())) return rc;
+  const hipError_t e = maple::launch_pack(w, n_values / 16, reinterpret_cast<uint32_t*>(out),
+                                          bad_count, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return MAPLE_OK;
+}
+
+int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const void* x,
+                            const float* router_w, const float* router_bias,
+                            const uint8_t* packed_w, const float* alpha, float* out,
+                            void* workspace, size_t ws_bytes, const maple_moe_debug* dbg,
+                            void* stream) {
+  Dims d;
+  int rc;
+  if ((rc = check_dims(dims, &d))) return rc;
+  if ((rc = check_tokens(d, n_tokens))) return rc;
+  if ((rc = check_ptr(x, 16, "x")) || (rc = check_ptr(router_w, 16, "router_w")) ||
+      (rc = check_opt_ptr(router_bias, 4, "router_bias")) ||
+      (rc = check_ptr(packed_w, 256, "packed_w")) || (rc = check_ptr(alpha, 16, "alpha")) ||
+      (rc = check_ptr(out, 16, "out")) || (rc = check_ptr(workspace, 256, "workspace")))
+    return rc;
+  if ((const void*)out == x) return fail(MAPLE_ERR_INVALID_ARG, "out aliases x");
+  Workspace ws;
+  const size_t need = maple::carve(d, n_tokens, nullptr, &ws);
+  if (ws_bytes < need)
+    return fail(MAPLE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", ws_bytes, need);
+  if (n_tokens == 0) return MAPLE_OK;
+  if ((rc = device_ready())) return rc;
+  maple::carve(d, n_tokens, static_cast<char*>(workspace), &ws);
+  return run_layer(d, n_tokens, x, (d.flags & MAPLE_X_BF16) != 0, router_w, router_bias,
+                   packed_w, alpha, out, nullptr, nullptr, ws, dbg, (hipStream_t)stream);
+}
+
+static int enqueue_stack(const Dims& d, int32_t n_layers, int64_t T, float* x,
+                         const float* const* router_w, const float* const* router_bias,
+                         const uint8_t* const* packed_w, const float* const* alpha,
+                         void* workspace, const maple_moe_debug* dbg, hipStream_t s) {
+  Workspace ws;
+  maple::carve(d, T, static_cast<char*>(workspace), &ws);
+  for (int l = 0; l < n_layers; ++l) {
+    const maple_moe_debug ld = layer_dbg(dbg, l, T, d);
+    const int rc = run_layer(d, T, x, false, router_w[l], router_bias ? router_bias[l] : nullptr,
+                             packed_w[l], alpha[l], x, x, ld.delta, ws, dbg ? &ld : nullptr, s);
+    if (rc) return rc;
+  }
+  return MAPLE_OK;
+}
+
+int maple_moe_stack_forward(const maple_moe_dims* dims, int32_t n_layers, int32_t n_tokens,
+                            float* x_inout, const float* const* router_w,
+                            const float* const* router_bias, const uint8_t* const* packed_w,
+                            const float* const* alpha, void* workspace, size_t ws_bytes,
+                            const maple_moe_debug* dbg, void* stream) {
+  Dims d;
+  int rc;
+  if ((rc = check_dims(dims, &d))) return rc;
+  d.flags &= ~MAPLE_X_BF16;
+  if ((rc = check_tokens(d, n_tokens))) return rc;
+  if ((rc = check_ptr(x_inout, 16, "x_inout"))) return rc;
+  if ((rc = check_stack_args(d, n_layers, n_tokens, router_w, router_bias, packed_w, alpha,
+                             workspace, ws_bytes)))
+    return rc;
+  if (n_tokens == 0 || n_layers == 0) return MAPLE_OK;
+  if ((rc = device_ready())) return rc;
+  return enqueue_stack(d, n_layers, n_tokens, x_inout, router_w, router_bias, packed_w, alpha,
+                       workspace, dbg, (hipStream_t)stream);
+}
+
+int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, int32_t n_tokens,
+                                 const void* staged_x, int32_t n_staged, float* x_work,
+                                 float* out_all, const float* const* router_w,
+                                 const float* const* router_bias,
+                                 const uint8_t* const* packed_w, const float* const* alpha,
+                                 void* workspace, size_t ws_bytes, maple_graph** graph) {
+  Dims d;
+  int rc;
+  if ((rc = check_dims(dims, &d))) return rc;
+  const bool staged_bf16 = (d.flags & MAPLE_X_BF16) != 0;
+  d.flags &= ~MAPLE_X_BF16;
+  if (!graph) return fail(MAPLE_ERR_INVALID_ARG, "graph is NULL");
+  *graph = nullptr;
+  if ((rc = check_tokens(d, n_tokens))) return rc;
+  if (n_tokens < 1) return fail(MAPLE_ERR_INVALID_ARG, "n_tokens must be >= 1 for a graph");
+  if (n_staged < 1) return fail(MAPLE_ERR_INVALID_ARG, "n_staged=%d < 1", n_staged);
+  if ((rc = check_ptr(staged_x, 16, "staged_x")) || (rc = check_ptr(x_work, 16, "x_work")) ||
+      (rc = check_opt_ptr(out_all, 16, "out_all")))
+    return rc;
+  if ((rc = check_stack_args(d, n_layers, n_tokens, router_w, router_bias, packed_w, alpha,
+                             workspace, ws_bytes)))
+    return rc;
+  if ((rc = device_ready())) return rc;
+
+  maple_graph* g = new maple_graph();
+  hipStream_t cs = nullptr;
+  hipError_t e = hipGetDevice(&g->device);
+  if (e == hipSuccess) e = hipMalloc(&g->counter, 256);
+  if (e == hipSuccess) e = hipMemset(g->counter, 0, 256);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    if (g->counter) (void)hipFree(g->counter);
+    delete g;
+    return hip_fail(e, "graph setup");
+  }
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    e = maple::launch_load_token(staged_x, staged_bf16, n_staged, n_tokens, d.H, g->counter,
+                                 x_work, cs);
+    rc = MAPLE_OK;
+    if (e == hipSuccess)
+      rc = enqueue_stack(d, n_layers, n_tokens, x_work, router_w, router_bias, packed_w, alpha,
+                         workspace, nullptr, cs);
+    if (e == hipSuccess && rc == MAPLE_OK && out_all)
+      e = maple::launch_store_token(x_work, n_staged, n_tokens, d.H, g->counter, out_all, cs);
+    const hipError_t e2 = hipStreamEndCapture(cs, &g->graph);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e == hipSuccess && rc == MAPLE_OK) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  (void)hipStreamDestroy(cs);
+  if (e != hipSuccess || rc != MAPLE_OK) {
+    const int out_rc = (rc != MAPLE_OK) ? rc : hip_fail(e, "graph capture");
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    (void)hipFree(g->counter);
+    delete g;
+    return out_rc;
+  }
+  *graph = g;
+  return MAPLE_OK;
+}
+
+int maple_graph_launch(maple_graph* graph, void* stream) {
+  if (!graph || !graph->exec) return fail(MAPLE_ERR_INVALID_ARG, "graph is NULL");
+  const hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return MAPLE_OK;
+}
+
+int maple_graph_set_step(maple_graph* graph, int32_t step, void* stream) {
+  if (!graph || !graph->counter) return fail(MAPLE_ERR_INVALID_ARG, "graph is NULL");
+  const hipError_t e = maple::launch_set_step(graph->counter, step, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "set_step launch");
+  return MAPLE_OK;
+}
+
+int maple_graph_destroy(maple_graph* graph) {
+  if (!graph) return MAPLE_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+  if (graph->graph) (void)hipGraphDestroy(graph->graph);
+  if (graph->counter) (void)hipFree(graph->counter);
+  delete graph;
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  return MAPLE_OK;
+}
+
+}  // extern "C"

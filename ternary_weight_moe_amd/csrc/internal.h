@@ -1,0 +1,64 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the HIP
+// kernels.  Not installed; the public surface is include/maple_moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace maple {
+
+// Workspace carve-up for one layer call with T tokens.  Every region is
+// 256-byte aligned.  The same carve serves the stack (layers run one after
+// another and reuse it).
+struct Workspace {
+  float* logits;        // [T,E]
+  int32_t* idx;         // [T,k]
+  float* gate;          // [T,k]
+  int32_t* offsets;     // [E+1]
+  int32_t* active;      // [E]   non-empty experts, ascending
+  int32_t* n_active;    // [1]   (+ padding)
+  int32_t* sorted_tok;  // [T*k]
+  int32_t* slot_pos;    // [T*k]
+  int32_t* blk_count;   // [nb,E]  per-64-token-block expert counts (large T)
+  int32_t* blk_rank;    // [T*k]   rank of a slot inside its block and expert
+  int32_t* tiles;       // [max_tiles*2] grouped-GEMM tile list (expert, m0)
+  int32_t* n_tiles;     // [1]
+  float* h;             // [T*k, I]  fp32 (GEMV path)
+  int8_t* xq;           // [T, 2, H] two int8 limbs of x (grouped path)
+  float* xs;            // [T]       scale of x's limbs
+  int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
+  float* hs;            // [T*k, I/128] scale per (slot, 128-column block)
+  float* y;             // [T*k, H]  expert outputs before the combine (grouped path)
+  size_t bytes;
+};
+
+struct Dims {
+  int H, E, k, I;
+  uint32_t flags;
+};
+
+size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws);  // base may be null
+int max_tiles(const Dims& d, int64_t T);
+
+// ---- launchers (each returns hipError_t of the launch) ----
+hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
+                       hipStream_t s);
+hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
+                         const float* Wr, const float* bias, float* logits, hipStream_t s);
+hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
+                        hipStream_t s);
+hipError_t launch_gemv_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
+                           const uint8_t* packed, const float* alpha, const Workspace& ws,
+                           float* out, const float* resid, float* delta, hipStream_t s);
+hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
+                              const uint8_t* packed, const float* alpha, const Workspace& ws,
+                              float* out, const float* resid, float* delta, hipStream_t s);
+hipError_t launch_load_token(const void* staged, bool bf16, int n_staged, int64_t T, int H,
+                             int32_t* counter, float* x_work, hipStream_t s);
+hipError_t launch_store_token(const float* x_work, int n_staged, int64_t T, int H,
+                              const int32_t* counter, float* out_all, hipStream_t s);
+hipError_t launch_set_step(int32_t* counter, int32_t step, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+}  // namespace maple

@@ -1,0 +1,185 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, packs on the host exactly as the oracle does, and rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_moe_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from ternary_weight_moe_amd import build
+    build.build()
+    return N.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "maple_moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(maple_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(N.EXPORTS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert N.maple_version() >= 100
+    assert lib.maple_status_string(N.MAPLE_ERR_WORKSPACE_TOO_SMALL) == b"MAPLE_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_host_pack_matches_oracle_and_round_trips(lib):
+    rng = np.random.default_rng(1)
+    w = rng.integers(-1, 2, size=(40, 256), dtype=np.int8)
+    p = N.maple_ternary_pack_host(w)
+    assert np.array_equal(p, oracle.pack(w))
+    assert np.array_equal(N.maple_ternary_unpack_host(p, 40, 256), w)
+    N.maple_ternary_validate_host(p)
+
+
+def test_host_pack_rejects_bad_values_and_code_3(lib):
+    w = np.zeros((1, 16), np.int8)
+    w[0, 5] = 2
+    with pytest.raises(N.MapleError) as e:
+        N.maple_ternary_pack_host(w)
+    assert e.value.status == N.MAPLE_ERR_INVALID_CODE
+    p = np.zeros((1, 4), np.uint8)
+    p[0, 1] = 0b11000000
+    with pytest.raises(N.MapleError) as e:
+        N.maple_ternary_validate_host(p)
+    assert e.value.status == N.MAPLE_ERR_INVALID_CODE
+    with pytest.raises(N.MapleError):
+        N.maple_ternary_unpack_host(p, 1, 16)
+    # every byte without a code-3 field validates
+    ok = np.array([b for b in range(256) if all(((b >> (2 * i)) & 3) != 3 for i in range(4))],
+                  np.uint8)
+    assert ok.size == 81
+    N.maple_ternary_validate_host(ok)
+    bad = np.array([b for b in range(256) if b not in set(ok.tolist())], np.uint8)
+    for b in bad:
+        with pytest.raises(N.MapleError):
+            N.maple_ternary_validate_host(np.array([b], np.uint8))
+
+
+def dims(**kw):
+    d = dict(hidden=2048, n_experts=256, top_k=8, inter=512, flags=N.MAPLE_X_BF16)
+    d.update(kw)
+    return N.make_dims(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=2000), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(hidden=128), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(hidden=8192), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(inter=96), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(inter=4096), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(top_k=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(top_k=9), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_experts=4, top_k=8), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_experts=257), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(flags=0x100), N.MAPLE_ERR_INVALID_ARG),
+    (dict(flags=N.MAPLE_FORCE_GEMV | N.MAPLE_FORCE_GROUPED), N.MAPLE_ERR_INVALID_ARG),
+])
+def test_workspace_query_validates_dims(lib, kw, status):
+    with pytest.raises(N.MapleError) as e:
+        N.maple_moe_workspace_bytes(dims(**kw), 1)
+    assert e.value.status == status
+
+
+def test_workspace_grows_with_tokens(lib):
+    a = N.maple_moe_workspace_bytes(dims(), 1)
+    b = N.maple_moe_workspace_bytes(dims(), 4096)
+    assert 0 < a < b
+    assert b % 256 == 0
+    with pytest.raises(N.MapleError) as e:
+        N.maple_moe_workspace_bytes(dims(), -1)
+    assert e.value.status == N.MAPLE_ERR_INVALID_ARG
+    with pytest.raises(N.MapleError) as e:
+        N.maple_moe_workspace_bytes(dims(), N.MAPLE_MAX_TOKENS + 1)
+    assert e.value.status == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+
+
+class FakeBuf:
+    """Stands in for a device tensor: an address and a size, never dereferenced."""
+
+    def __init__(self, addr, nbytes=1 << 30):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def call_layer(lib, d, T, **over):
+    a = dict(x=FakeBuf(0x100000), router_w=FakeBuf(0x200000), router_bias=None,
+             packed_w=FakeBuf(0x300000), alpha=FakeBuf(0x400000), out=FakeBuf(0x500000),
+             workspace=FakeBuf(0x600000))
+    a.update(over)
+    return lib.maple_moe_layer_forward(
+        ctypes.byref(d), T, a["x"] and a["x"].addr, a["router_w"] and a["router_w"].addr,
+        a["router_bias"] and a["router_bias"].addr, a["packed_w"] and a["packed_w"].addr,
+        a["alpha"] and a["alpha"].addr, a["out"] and a["out"].addr,
+        a["workspace"] and a["workspace"].addr, a["workspace"].nbytes if a["workspace"] else 0,
+        None, None)
+
+
+def test_layer_argument_validation_before_any_device_call(lib):
+    d = dims()
+    assert call_layer(lib, d, 0) == N.MAPLE_OK  # T = 0: nothing to do, no device needed
+    assert call_layer(lib, d, -1) == N.MAPLE_ERR_INVALID_ARG
+    assert call_layer(lib, d, 1, x=None) == N.MAPLE_ERR_INVALID_ARG
+    assert call_layer(lib, d, 1, alpha=None) == N.MAPLE_ERR_INVALID_ARG
+    assert call_layer(lib, d, 1, packed_w=FakeBuf(0x300080)) == N.MAPLE_ERR_ALIGNMENT
+    assert call_layer(lib, d, 1, x=FakeBuf(0x100004)) == N.MAPLE_ERR_ALIGNMENT
+    assert call_layer(lib, d, 1, workspace=FakeBuf(0x600000, 1024)) == \
+        N.MAPLE_ERR_WORKSPACE_TOO_SMALL
+    assert call_layer(lib, d, 1, out=FakeBuf(0x100000)) == N.MAPLE_ERR_INVALID_ARG  # aliases x
+    gemv = dims(flags=N.MAPLE_FORCE_GEMV)
+    assert call_layer(lib, gemv, 65) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert b"n_tokens" in lib.maple_last_error()
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+def test_valid_call_without_device_reports_no_device(lib):
+    assert call_layer(lib, dims(), 1) == N.MAPLE_ERR_NO_DEVICE
+    w = FakeBuf(0x100000)
+    assert lib.maple_ternary_pack_device(w.addr, 64, 0x200000, None, None) == N.MAPLE_ERR_NO_DEVICE
+
+
+def test_stack_and_graph_validation(lib):
+    d = dims(flags=0)
+    P = ctypes.c_void_p
+    arr = (P * 2)(0x200000, 0x200100)
+    pk = (P * 2)(0x300000, 0x300100)
+    badpk = (P * 2)(0x300000, 0x300010)
+    ws = 1 << 30
+    f = lib.maple_moe_stack_forward
+    assert f(ctypes.byref(d), 2, 0, 0x100000, arr, None, pk, arr, 0x600000, ws, None, None) == 0
+    assert f(ctypes.byref(d), -1, 1, 0x100000, arr, None, pk, arr, 0x600000, ws, None, None) == \
+        N.MAPLE_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), 2, 1, 0x100000, arr, None, badpk, arr, 0x600000, ws, None, None) == \
+        N.MAPLE_ERR_ALIGNMENT
+    assert b"packed_w[1]" in lib.maple_last_error()
+    g = P()
+    cg = lib.maple_moe_stack_graph_create
+    assert cg(ctypes.byref(d), 2, 1, 0x100000, 0, 0x700000, None, arr, None, pk, arr, 0x600000,
+              ws, ctypes.byref(g)) == N.MAPLE_ERR_INVALID_ARG  # n_staged = 0
+    assert lib.maple_graph_launch(None, None) == N.MAPLE_ERR_INVALID_ARG
+    assert lib.maple_graph_destroy(None) == N.MAPLE_OK

@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Bit-exact: device packing, top-k sets, offsets, sorted tokens, slot positions.
+Tolerance (rel L2 <= 1e-3, max |d| <= 2e-2): layer outputs, per-layer stack
+deltas and the stack's total delta x_L - x_0.  Every token obeys the router
+gap rule (l_(k) - l_(k+1) >= 1e-4 in the oracle), redrawing the tokens that
+do not, so the routing is unique.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from gpu_helpers import (Layer, assert_close, assert_routing_equal, dims_for,  # noqa: E402
+                         layer_tokens_with_gap, log, stack_tokens_with_gap, x_device)
+from ternary_weight_moe_amd import _native as N  # noqa: E402
+from ternary_weight_moe_amd import synth as S  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def workload(name, **kw):
+    base = S.WORKLOADS[name]
+    f = dict(base.__dict__)
+    f.pop("notes", None)
+    f.update(kw)
+    return S.Workload(**f)
+
+
+def run_layer(w, L, x_host, flags=0):
+    T, H, E, k = x_host.shape[0], w.hidden, w.n_experts, w.top_k
+    d = dims_for(w, flags)
+    x = x_device(w, x_host)
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bufs = dict(idx=torch.empty(T, k, **i32),
+                gate=torch.empty(T, k, dtype=torch.float32, device="cuda"),
+                logits=torch.empty(T, E, dtype=torch.float32, device="cuda"),
+                offsets=torch.empty(E + 1, **i32), sorted_token=torch.empty(T * k, **i32),
+                slot_pos=torch.empty(T, k, **i32))
+    N.maple_moe_layer_forward(d, T, x, L.d_Wr, L.d_bias, L.packed, L.d_alpha, out, ws,
+                              N.make_debug(**bufs))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), {n: b.cpu().numpy() for n, b in bufs.items()}
+
+
+def check_layer(w, L, x_host, flags=0, renorm=False, what=""):
+    log(f"{what}: T={x_host.shape[0]} flags={flags:#x}")
+    got, dbg = run_layer(w, L, x_host, flags | (N.MAPLE_RENORM_TOPK if renorm else 0))
+    x64 = S.x_as_f32(w, x_host).astype(np.float64)
+    ref = L.oracle_layer(x64, w.top_k, w.inter, renorm=renorm)
+    assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
+                         ref["idx"], w.n_experts, what)
+    np.testing.assert_allclose(dbg["logits"], ref["logits"], rtol=0, atol=5e-5)
+    # gates, matched per (token, expert)
+    for t in range(x_host.shape[0]):
+        gr = dict(zip(ref["idx"][t].tolist(), ref["gate"][t].tolist()))
+        gg = dict(zip(dbg["idx"][t].tolist(), dbg["gate"][t].tolist()))
+        for e in gr:
+            assert abs(gg[e] - gr[e]) <= 1e-5 * max(1.0, abs(gr[e])), (t, e)
+    assert_close(got, ref["out"], what)
+    return got
+
+
+# ---- packing ----------------------------------------------------------------------
+
+def test_pack_device_matches_oracle():
+    rng = np.random.default_rng(0)
+    w = rng.integers(-1, 2, size=(96, 2048 + 512), dtype=np.int8)
+    combos = np.array(np.meshgrid(*[np.arange(3)] * 4, indexing="ij")).reshape(4, -1).T - 1
+    for q in range(4):  # all 81 four-code bytes at every byte position of a word
+        for b in range(4):
+            w[:81, 16 * 3 + 4 * b + q] = combos[:, b]
+    dw = torch.from_numpy(w.reshape(-1)).cuda()
+    out = torch.empty(w.size // 4, dtype=torch.uint8, device="cuda")
+    bad = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    N.maple_ternary_pack_device(dw, out, bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert np.array_equal(out.cpu().numpy().reshape(w.shape[0], -1), oracle.pack(w))
+    w2 = w.copy()
+    w2[5, 17] = 2
+    w2[90, 3] = -7
+    N.maple_ternary_pack_device(torch.from_numpy(w2.reshape(-1)).cuda(), out, bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 2
+
+
+# ---- one layer ---------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = S.WORKLOADS["tiny_layer"]
+    return w, Layer(w, 0)
+
+
+@pytest.fixture(scope="module")
+def dec():
+    w = S.WORKLOADS["decode_layer"]
+    return w, Layer(w, 0)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_tiny_layer(tiny, renorm):
+    w, L = tiny
+    x, _ = layer_tokens_with_gap(w, L, w.n_tokens)
+    check_layer(w, L, x, renorm=renorm, what=f"tiny renorm={renorm}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 64])
+def test_decode_layer_gemv(dec, T):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, T, token0=100 * T)
+    check_layer(w, L, x, flags=N.MAPLE_FORCE_GEMV, what=f"decode layer gemv T={T}")
+
+
+def test_decode_layer_deterministic(dec):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, 8, token0=900)
+    a, _ = run_layer(w, L, x)
+    b, _ = run_layer(w, L, x)
+    assert np.array_equal(a, b)
+
+
+def test_fp32_input_and_token_independence(dec):
+    w0, L = dec
+    w = workload("decode_layer", x_bf16=False)
+    x, _ = layer_tokens_with_gap(w, L, 9, token0=3000)
+    full = check_layer(w, L, x, flags=N.MAPLE_FORCE_GEMV, what="decode layer fp32 x")
+    one, _ = run_layer(w, L, x[4:5], flags=N.MAPLE_FORCE_GEMV)
+    assert_close(one, full[4:5], "token alone vs in batch")
+
+
+def test_edge_all_experts_and_k1():
+    # E == k: every token selects every expert
+    w = workload("tiny_layer", n_experts=4, top_k=4, seed=1101, n_tokens=7)
+    L = Layer(w, 0)
+    x, _ = layer_tokens_with_gap(w, L, 7)
+    check_layer(w, L, x, what="E == k")
+    # k = 1
+    w1 = workload("tiny_layer", top_k=1, seed=1102, n_tokens=6)
+    L1 = Layer(w1, 0)
+    x1, _ = layer_tokens_with_gap(w1, L1, 6)
+    check_layer(w1, L1, x1, what="k = 1")
+
+
+def test_edge_max_skew_all_tokens_one_group(dec):
+    """A bias of +50 on eight experts sends every token to the same eight."""
+    w, L = dec
+    hot = [3, 17, 64, 65, 128, 200, 254, 255]
+    bias = np.zeros(w.n_experts, np.float32)
+    bias[hot] = 50.0 + np.arange(8, dtype=np.float32)  # distinct, so the gap rule holds
+    Ls = Layer.__new__(Layer)
+    Ls.__dict__.update(L.__dict__)
+    Ls.bias = bias
+    Ls.d_bias = torch.from_numpy(bias).cuda()
+    x = S.gen_x(w, 64, token0=5000)
+    got = check_layer(w, Ls, x, flags=N.MAPLE_FORCE_GEMV, what="max skew")
+    assert got.shape == (64, w.hidden)
+
+
+def test_zero_tokens_is_a_no_op(dec):
+    w, L = dec
+    d = dims_for(w)
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, 0), dtype=torch.uint8, device="cuda")
+    x = torch.zeros(1, w.hidden, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((1, w.hidden), 3.0, device="cuda")
+    N.maple_moe_layer_forward(d, 0, x, L.d_Wr, None, L.packed, L.d_alpha, out, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)

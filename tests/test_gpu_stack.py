@@ -1,0 +1,103 @@
+"""GPU parity of the 24-layer stack (decode bs=1 weights, and the batched
+Zipf-routed decode) and of its captured HIP graph, against the oracle."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_helpers import (Layer, assert_close, assert_routing_equal, dims_for, log,  # noqa: E402
+                         stack_tokens_with_gap)
+from ternary_weight_moe_amd import _native as N  # noqa: E402
+from ternary_weight_moe_amd import synth as S  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def build_stack(w):
+    layers = []
+    for l in range(w.n_layers):
+        layers.append(Layer(w, l))
+    log(f"{w.name}: {w.n_layers} layers on the device")
+    return layers
+
+
+@pytest.fixture(scope="module")
+def stack3():
+    w = S.WORKLOADS["decode_stack"]
+    return w, build_stack(w)
+
+
+def dev_lists(layers):
+    return ([L.d_Wr for L in layers], [L.d_bias for L in layers] if layers[0].d_bias is not None
+            else None, [L.packed for L in layers], [L.d_alpha for L in layers])
+
+
+def run_stack(w, layers, x_host, flags=0):
+    T, H, E, k, nL = x_host.shape[0], w.hidden, w.n_experts, w.top_k, len(layers)
+    d = dims_for(w, flags, bf16=False)
+    x = torch.from_numpy(S.x_as_f32(w, x_host).copy()).cuda()
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bufs = dict(idx=torch.empty(nL, T, k, **i32), offsets=torch.empty(nL, E + 1, **i32),
+                sorted_token=torch.empty(nL, T * k, **i32), slot_pos=torch.empty(nL, T, k, **i32),
+                delta=torch.empty(nL, T, H, dtype=torch.float32, device="cuda"))
+    rw, rb, pk, al = dev_lists(layers)
+    N.maple_moe_stack_forward(d, T, x, rw, rb, pk, al, ws, N.make_debug(**bufs))
+    torch.cuda.synchronize()
+    return x.cpu().numpy(), {n: b.cpu().numpy() for n, b in bufs.items()}
+
+
+def check_stack(w, layers, x_host, ref, flags=0, what=""):
+    got, dbg = run_stack(w, layers, x_host, flags)
+    x0 = S.x_as_f32(w, x_host).astype(np.float64)
+    for l in range(len(layers)):
+        assert_routing_equal(dbg["idx"][l], dbg["slot_pos"][l], dbg["offsets"][l],
+                             dbg["sorted_token"][l], ref["idx"][l], w.n_experts, f"{what} L{l}")
+    for l in (0, len(layers) // 2, len(layers) - 1):
+        assert_close(dbg["delta"][l], ref["delta"][l], f"{what} delta L{l}")
+    assert_close(got - x0, ref["x"] - x0, f"{what} x_L - x_0")
+    return got
+
+
+def test_decode_stack_24_layers(stack3):
+    w, layers = stack3
+    x, x64, ref, regen = stack_tokens_with_gap(w, layers, 4)
+    log(f"decode stack: regenerated {len(regen)} of 4 tokens")
+    check_stack(w, layers, x, ref, what="decode stack")
+
+
+def test_decode_stack_graph_replays(stack3):
+    """Replays of the captured step, with eager work between them, each match
+    the eager stack call bit for bit and the oracle within tolerance."""
+    w, layers = stack3
+    S_ = 3
+    x, x64, ref, _ = stack_tokens_with_gap(w, layers, S_, token0=40)
+    d = dims_for(w)  # staged tokens are bf16
+    staged = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16).reshape(S_, 1, -1)
+    x_work = torch.empty(1, w.hidden, dtype=torch.float32, device="cuda")
+    out_all = torch.full((S_, 1, w.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, 1), dtype=torch.uint8, device="cuda")
+    rw, rb, pk, al = dev_lists(layers)
+    g = N.MapleGraph(d, 1, staged, S_, x_work, out_all, rw, rb, pk, al, ws)
+    eager = np.stack([run_stack(w, layers, x[s:s + 1])[0][0] for s in range(S_)])
+    for rep in range(2):
+        g.set_step(0)
+        for s in range(S_):
+            g.launch()
+            junk = torch.randn(1024, 1024, device="cuda")
+            (junk @ junk).sum().item()  # eager work and a sync between replays
+        torch.cuda.synchronize()
+        got = out_all.cpu().numpy()[:, 0]
+        assert np.array_equal(got, eager), f"replay round {rep} differs from the eager call"
+    assert_close(got - x64, ref["x"] - x64, "graph x_L - x_0")
+    g.destroy()
+
+
+def test_batched_zipf_stack_one_step():
+    w = S.WORKLOADS["batched_stack_zipf"]
+    layers = build_stack(w)
+    x, x64, ref, regen = stack_tokens_with_gap(w, layers, w.n_tokens)
+    distinct = [len(np.unique(ref["idx"][l])) for l in range(w.n_layers)]
+    log(f"zipf: regenerated {len(regen)} tokens; distinct experts per layer "
+        f"min {min(distinct)} mean {np.mean(distinct):.1f} max {max(distinct)}")
+    check_stack(w, layers, x, ref, flags=N.MAPLE_FORCE_GEMV, what="zipf gemv")
