@@ -51,10 +51,11 @@ def _L():
             "oracle_topk": (None, [_P, _I64, _I32, _I32, _I32, _P, _P]),
             "oracle_permute": (None, [_P, _I64, _I32, _I32, _P, _P, _P]),
             "oracle_expert_ffn": (None, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32]),
-            "oracle_moe_layer": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I64, _P, _P, _P,
-                                                _P, _P, _P, _P, _P, _P]),
-            "oracle_moe_stack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I64, _P,
+            "oracle_moe_layer": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I64, _P,
                                                 _P, _P, _P, _P, _P, _P, _P, _P]),
+            "oracle_moe_stack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
+                                                _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "oracle_rms_normalize": (None, [_P, _I64, _I32, ctypes.c_double, _P]),
             "oracle_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -159,8 +160,21 @@ def expert_ffn(x: np.ndarray, blob: np.ndarray, alpha: np.ndarray, H: int, I: in
     return g, u, h, y
 
 
-def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = False):
-    """One MoE layer in fp64.  Returns dict(out, logits, idx, gate)."""
+RMS_EPS = 1e-6
+
+
+def rms_normalize(x: np.ndarray) -> np.ndarray:
+    """x / sqrt(mean(x^2) + 1e-6) per row, fp64."""
+    x = _c(x, np.float64)
+    T, H = x.shape
+    out = np.empty_like(x)
+    _L().oracle_rms_normalize(_ptr(x), T, H, RMS_EPS, _ptr(out))
+    return out
+
+
+def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = False,
+              prenorm: bool = False):
+    """One MoE layer in fp64 (on x / rms(x) when prenorm).  Returns dict(out, logits, idx, gate)."""
     x = _c(x, np.float64)
     T, H = x.shape
     Wr = _c(Wr, np.float32)
@@ -173,8 +187,8 @@ def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = 
     logits = np.empty((T, E), np.float64)
     idx = np.empty((T, k), np.int32)
     gate = np.empty((T, k), np.float64)
-    rc = _L().oracle_moe_layer(H, E, k, inter, int(renorm), T, _ptr(x), _ptr(Wr), _ptr(bias),
-                               _ptr(packed), _ptr(alpha), _ptr(out), _ptr(logits), _ptr(idx),
+    rc = _L().oracle_moe_layer(H, E, k, inter, int(renorm), int(prenorm), T, _ptr(x), _ptr(Wr),
+                               _ptr(bias), _ptr(packed), _ptr(alpha), _ptr(out), _ptr(logits), _ptr(idx),
                                _ptr(gate))
     if rc != 0:
         raise ValueError(f"oracle_moe_layer failed ({rc})")
@@ -182,8 +196,10 @@ def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = 
 
 
 def moe_stack(x, Wr_list, bias_list, packed_list, alpha_list, *, k: int, inter: int,
-              renorm: bool = False, keep_logits: bool = True, keep_delta: bool = True):
-    """x^(l+1) = x^(l) + MoE_l(x^(l)) over L layers in fp64.
+              renorm: bool = False, prenorm: bool = True, keep_logits: bool = True,
+              keep_delta: bool = True):
+    """x^(l+1) = x^(l) + MoE_l(x^(l) / rms(x^(l))) over L layers in fp64 (no
+    normalisation when prenorm is False).
 
     Returns dict(x=final, logits [L,T,E], idx [L,T,k], gate [L,T,k], delta [L,T,H]).
     """
@@ -206,7 +222,7 @@ def moe_stack(x, Wr_list, bias_list, packed_list, alpha_list, *, k: int, inter: 
     idx = np.empty((L, T, k), np.int32)
     gate = np.empty((L, T, k), np.float64)
     delta = np.empty((L, T, H), np.float64) if keep_delta else None
-    rc = _L().oracle_moe_stack(H, E, k, inter, int(renorm), L, T, _ptr(x),
+    rc = _L().oracle_moe_stack(H, E, k, inter, int(renorm), int(prenorm), L, T, _ptr(x),
                                ctypes.cast(Wr_p, _P), ctypes.cast(b_p, _P) if b_p else None,
                                ctypes.cast(pk_p, _P), ctypes.cast(al_p, _P), _ptr(logits),
                                _ptr(idx), _ptr(gate), _ptr(delta))

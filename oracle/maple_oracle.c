@@ -24,6 +24,12 @@
  *     times up, then down), weighted combine: the pages are silent on these;
  *     this is the plainest reading of a "softmax router / top-8 / SwiGLU"
  *     MoE FFN and is listed among the readings of the pages.
+ *   - Normalisation: the pages never mention one.  A stack joined only by the
+ *     residual add diverges (SwiGLU is quadratic in x, so the residual's scale
+ *     squares per layer and overflows even fp64 within ~16 of the 24 layers),
+ *     so the stack reads each block as pre-norm: the MoE sees
+ *     x / sqrt(mean(x^2) + eps), eps = 1e-6, without a learned scale, and the
+ *     residual adds its output to the un-normalised x.
  *
  * Packed weight layout ("layout v1", our own, since the pages only say
  * "2-bit"): code c = w + 1 in {0,1,2} (3 is invalid).  A matrix is stored
@@ -207,14 +213,34 @@ static void layer_token(int32_t H, int32_t E, int32_t k, int32_t I, const double
   (void)E;
 }
 
+/* x / sqrt(mean(x^2) + eps) for each of T rows of length H (fp64). */
+void oracle_rms_normalize(const double* x, int64_t T, int32_t H, double eps, double* xn) {
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int32_t j = 0; j < H; ++j) ss += x[t * H + j] * x[t * H + j];
+    const double r = sqrt(ss / H + eps);
+    for (int32_t j = 0; j < H; ++j) xn[t * H + j] = x[t * H + j] / r;
+  }
+}
+
+#define ORACLE_RMS_EPS 1e-6
+
 /* out[t] = sum_j gate[t,j] * FFN_{idx[t,j]}(x[t]), summed in selection order.
+ * With prenorm != 0 the router and the experts see x[t] / rms(x[t]).
  * logits (T x E), idx (T x k), gate (T x k) receive the routing. */
-int oracle_moe_layer(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm, int64_t T,
-                     const double* x, const float* Wr, const float* bias, const uint8_t* packed,
-                     const float* alpha, double* out, double* logits, int32_t* idx,
-                     double* gate) {
+int oracle_moe_layer(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                     int32_t prenorm, int64_t T, const double* x_in, const float* Wr,
+                     const float* bias, const uint8_t* packed, const float* alpha, double* out,
+                     double* logits, int32_t* idx, double* gate) {
   if (H <= 0 || I <= 0 || H % 16 || I % 16 || k < 1 || k > E || T < 0) return -1;
   if (T == 0) return 0;
+  double* xn = NULL;
+  const double* x = x_in;
+  if (prenorm) {
+    xn = (double*)malloc(sizeof(double) * (size_t)(T * H));
+    oracle_rms_normalize(x_in, T, H, ORACLE_RMS_EPS, xn);
+    x = xn;
+  }
   oracle_router_logits(x, T, H, Wr, bias, E, logits);
   oracle_topk(logits, T, E, k, renorm, idx, gate);
   int nthreads = 1;
@@ -242,16 +268,18 @@ int oracle_moe_layer(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
     free(h);
     free(y);
   }
+  free(xn);
   return 0;
 }
 
 /* ---- stack -------------------------------------------------------------- */
 
-/* x^(l+1) = x^(l) + MoE_l(x^(l)) for l = 0..L-1, in place on x (T x H).
+/* x^(l+1) = x^(l) + MoE_l(n(x^(l))) for l = 0..L-1, in place on x (T x H), where
+ * n is the pre-norm above when prenorm != 0 and the identity otherwise.
  * Per-layer routing and deltas go to the optional outputs:
  * logits_all [L,T,E], idx_all [L,T,k], gate_all [L,T,k], delta_all [L,T,H]. */
 int oracle_moe_stack(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
-                     int32_t n_layers, int64_t T, double* x, const float* const* Wr,
+                     int32_t prenorm, int32_t n_layers, int64_t T, double* x, const float* const* Wr,
                      const float* const* bias, const uint8_t* const* packed,
                      const float* const* alpha, double* logits_all, int32_t* idx_all,
                      double* gate_all, double* delta_all) {
@@ -265,7 +293,7 @@ int oracle_moe_stack(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
     double* L_lg = logits_all ? logits_all + (int64_t)l * T * E : lg;
     int32_t* L_id = idx_all ? idx_all + (int64_t)l * T * k : id;
     double* L_gt = gate_all ? gate_all + (int64_t)l * T * k : gt;
-    rc = oracle_moe_layer(H, E, k, I, renorm, T, x, Wr[l], bias ? bias[l] : NULL, packed[l],
+    rc = oracle_moe_layer(H, E, k, I, renorm, prenorm, T, x, Wr[l], bias ? bias[l] : NULL, packed[l],
                           alpha[l], out, L_lg, L_id, L_gt);
     for (int64_t i = 0; i < T * H; ++i) {
       x[i] += out[i];

@@ -42,9 +42,11 @@ def make_layer(w, layer=0):
     return x, Wr, bias, W, alpha, packed
 
 
-def dense_reference(x, Wr, bias, W, alpha, H, I, k, renorm=False):
+def dense_reference(x, Wr, bias, W, alpha, H, I, k, renorm=False, prenorm=False):
     """Independent numpy fp64 evaluation on the generator's int8 values."""
     E = Wr.shape[0]
+    if prenorm:
+        x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)
     logits = x @ Wr.astype(np.float64).T
     if bias is not None:
         logits = logits + bias.astype(np.float64)
@@ -330,8 +332,52 @@ def test_stack_is_composition_of_layers():
                          inter=w.inter)
     x = x0.copy()
     for l, L in enumerate(layers):
-        ref, _, idx = dense_reference(x, L[1], L[2], L[3], L[4], w.hidden, w.inter, w.top_k)
+        ref, _, idx = dense_reference(x, L[1], L[2], L[3], L[4], w.hidden, w.inter, w.top_k,
+                                      prenorm=True)
         assert np.array_equal(r["idx"][l], idx)
         assert rel_l2(r["delta"][l], ref) < 1e-12
         x = x + r["delta"][l]
     assert np.array_equal(r["x"], x)
+
+
+def test_stack_without_norm_is_plain_composition():
+    w = tiny(n_tokens=2, n_layers=2, seed=78)
+    layers = [make_layer(w, l) for l in range(w.n_layers)]
+    x0 = layers[0][0]
+    r = oracle.moe_stack(x0, [L[1] for L in layers], [L[2] for L in layers],
+                         [L[5] for L in layers], [L[4] for L in layers], k=w.top_k,
+                         inter=w.inter, prenorm=False)
+    x = x0.copy()
+    for l, L in enumerate(layers):
+        ref, _, _ = dense_reference(x, L[1], L[2], L[3], L[4], w.hidden, w.inter, w.top_k)
+        x = x + ref
+    assert rel_l2(r["x"] - x0, x - x0) < 1e-12
+
+
+# ---- pre-norm ----------------------------------------------------------------------
+
+def test_rms_normalize_closed_form_and_unit_rms():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 256)) * np.array([[1e-3], [1.0], [7.0], [300.0], [1e-9]])
+    n = oracle.rms_normalize(x)
+    want = x / np.sqrt(np.mean(x ** 2, axis=1, keepdims=True) + 1e-6)
+    assert rel_l2(n, want) < 1e-14
+    # rows well above eps come out at unit rms; a row far below eps is damped
+    assert np.allclose(np.sqrt(np.mean(n[1:4] ** 2, axis=1)), 1.0, atol=1e-6)
+    assert np.sqrt(np.mean(n[4] ** 2)) < 1e-5
+
+
+def test_prenorm_layer_is_scale_invariant_and_matches_dense():
+    w = S.WORKLOADS["tiny_layer"]
+    x, Wr, bias, W, alpha, packed = make_layer(w)
+    a = oracle.moe_layer(x, Wr, bias, packed, alpha, k=w.top_k, inter=w.inter, prenorm=True)
+    b = oracle.moe_layer(8.0 * x, Wr, bias, packed, alpha, k=w.top_k, inter=w.inter,
+                         prenorm=True)
+    assert rel_l2(b["out"], a["out"]) < 5e-6  # eps breaks exact invariance at ~eps / rms^2
+    ref, _, idx = dense_reference(x, Wr, bias, W, alpha, w.hidden, w.inter, w.top_k,
+                                  prenorm=True)
+    assert np.array_equal(a["idx"], idx)
+    assert rel_l2(a["out"], ref) < 1e-12
+    # without the norm the same layer differs (x here has rms != 1)
+    c = oracle.moe_layer(8.0 * x, Wr, bias, packed, alpha, k=w.top_k, inter=w.inter)
+    assert rel_l2(c["out"], a["out"]) > 1.0
