@@ -4,13 +4,17 @@
 Default workload (the headline metric): decode of the 24-layer MoE stack at
 batch 1 (hidden 2048, 256 experts, top-8, intermediate 512), one captured HIP
 graph step per token, 256 staged tokens with independent seeded bf16 inputs.
-A step is one token through all 24 layers: router, softmax/top-8, grouping,
-gate/up + SwiGLU, down projection and weighted combine with the residual.
+A step is one token through all 24 pre-norm blocks: router, softmax/top-8,
+grouping, gate/up + SwiGLU, down projection and weighted combine with the
+residual.  ``--workload prefill_4096`` (or ``prefill_16384``) times one
+layer over that many tokens instead; a step is then one layer call.
 
-Prints one JSON line (rank 0).  ``--workload prefill_4096`` times one
-4096-token layer instead.  Inputs are synthetic and seeded; weights are
-generated in host memory, packed on the device and stay resident in HBM
-before the timed region starts.
+Prints one JSON line.  Inputs are synthetic and seeded; weights are generated
+in host memory, packed on the device and resident in HBM before the timed
+region starts.  After the timed region, a profiled pass of the same work
+(HIP events around each kernel, recorded by the library on the stream the
+kernel runs on) gives the dominant kernel's average duration for the
+roofline entry.
 """
 from __future__ import annotations
 
@@ -26,21 +30,43 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode tok/s, 24-layer ternary MoE stack bs=1; % HBM peak; prefill tok/s"
-HBM_PEAK_GBS = 8000.0
-INT8_PEAK_TOPS = 5000.0
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
 
 
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_bytes_per_token_layer(H, E, k, I, T=1):
-    """Algorithmic HBM bytes of one layer for T tokens when every token's
-    experts are distinct: k experts' packed weights and alphas, the fp32
-    router, x read and the output written (fp32)."""
-    expert = 3 * H * I // 4 + 4 * (2 * I + H)
-    return k * T * expert + 4 * E * H + 2 * 4 * T * H
+# ---- algorithmic work per kernel launch ----------------------------------------------
 
+def expert_bytes(H, I):
+    """Packed ternary weights + fp32 alphas of one expert."""
+    return 3 * H * I // 4 + 4 * (2 * I + H)
+
+
+def decode_bytes(kernel, H, E, k, I, T=1):
+    """Algorithmic HBM bytes of one launch of a decode-path kernel for T tokens
+    whose k experts are all distinct (T * k experts read once)."""
+    ne = T * k
+    return {
+        "router_gemv": 4 * E * H + 4 * T * H + 4 * T * E,
+        "route_small": 4 * T * E + 4 * (3 * ne + 2 * E + 1),
+        "gateup_gemv": ne * (2 * I * H // 4 + 4 * 2 * I) + 4 * T * H + 4 * ne * I,
+        "down_combine_gemv": ne * (H * I // 4 + 4 * H) + 4 * ne * I + 2 * 4 * T * H,
+    }.get(kernel)
+
+
+def decode_bytes_per_token_layer(H, E, k, I):
+    return k * expert_bytes(H, I) + 4 * E * H + 2 * 4 * H
+
+
+def prefill_ops(kernel, H, k, I, T):
+    """Algorithmic int8 MAC-ops (2 per multiply-add, one limb) of one launch."""
+    return {"gateup_mfma": 2 * T * k * 2 * H * I, "down_mfma": 2 * T * k * H * I}.get(kernel)
+
+
+# ---- set-up ---------------------------------------------------------------------------
 
 def build_layers(w, torch, N, S):
     layers = []
@@ -61,31 +87,87 @@ def build_layers(w, torch, N, S):
     return layers
 
 
+def oracle_layers(w):
+    import oracle
+    from ternary_weight_moe_amd import synth as S
+    out = []
+    for l in range(w.n_layers):
+        W = S.gen_layer_weights(w, l)
+        out.append(dict(Wr=S.gen_router(w, l), bias=S.gen_router_bias(w, l),
+                        packed=oracle.pack_layer(W, w.hidden, w.inter), alpha=S.gen_alpha(w, l)))
+        del W
+    return out
+
+
 def cpu_baseline_decode(w, budget_s):
-    """The oracle (fp64 C, OpenMP) on a bounded sample: a few tokens through
-    the full 24-layer stack, tok/s on this host."""
+    """The oracle (fp64 C, OpenMP) on a bounded sample: tokens one at a time
+    through the full 24-layer stack; tok/s on this host."""
     import oracle
     from ternary_weight_moe_amd import synth as S
     log("cpu baseline: packing the stack for the oracle")
-    Wr, bias, packed, alpha = [], [], [], []
-    for l in range(w.n_layers):
-        W = S.gen_layer_weights(w, l)
-        packed.append(oracle.pack_layer(W, w.hidden, w.inter))
-        del W
-        Wr.append(S.gen_router(w, l))
-        bias.append(S.gen_router_bias(w, l))
-        alpha.append(S.gen_alpha(w, l))
+    L = oracle_layers(w)
     n, t_used = 0, 0.0
     while t_used < budget_s and n < 256:
         x = S.x_as_f32(w, S.gen_x(w, 1, token0=n)).astype(np.float64)
         t0 = time.perf_counter()
-        oracle.moe_stack(x, Wr, bias, packed, alpha, k=w.top_k, inter=w.inter,
-                         keep_logits=False, keep_delta=False)
+        oracle.moe_stack(x, [l["Wr"] for l in L], [l["bias"] for l in L],
+                         [l["packed"] for l in L], [l["alpha"] for l in L], k=w.top_k,
+                         inter=w.inter, keep_logits=False, keep_delta=False)
         t_used += time.perf_counter() - t0
         n += 1
     return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{n} tokens x {w.n_layers} layers, one token per call ({t_used:.1f} s)")
+                sample=f"{n} tokens x {w.n_layers} layers, one token per call "
+                       f"({t_used:.1f} s of oracle time)")
 
+
+def cpu_baseline_prefill(w, budget_s):
+    """The oracle on a bounded sample of the prefill workload: token batches of
+    the same layer until the time budget is spent; tok/s on this host."""
+    import oracle
+    from ternary_weight_moe_amd import synth as S
+    L = oracle_layers(w)[0]
+    n, t_used, chunk = 0, 0.0, 2 * oracle.num_threads()
+    while t_used < budget_s and n < w.n_tokens:
+        x = S.x_as_f32(w, S.gen_x(w, chunk, token0=n)).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, L["Wr"], L["bias"], L["packed"], L["alpha"], k=w.top_k,
+                         inter=w.inter)
+        t_used += time.perf_counter() - t0
+        n += chunk
+    return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} of {w.n_tokens} tokens of one layer, {chunk} per call "
+                       f"({t_used:.1f} s of oracle time)")
+
+
+def profile_kernels(N, fn, steps):
+    """Run fn() `steps` times with the library's event timing on; returns
+    {kernel: (launches, avg ms)}."""
+    import torch
+    torch.cuda.synchronize()
+    N.maple_profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    summ = N.maple_profile_summary()
+    N.maple_profile_enable(False)
+    return {k: (n, ms / n) for k, (n, ms) in summ.items()}
+
+
+def timed(torch, fn, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+# ---- workloads ------------------------------------------------------------------------
 
 def bench_decode(args, torch, N, S):
     w = S.WORKLOADS["decode_stack"]
@@ -98,55 +180,116 @@ def bench_decode(args, torch, N, S):
     ws = torch.empty(N.maple_moe_workspace_bytes(d, 1), dtype=torch.uint8, device="cuda")
     x_work = torch.empty(1, H, dtype=torch.float32, device="cuda")
     out_all = torch.empty(n_staged, 1, H, dtype=torch.float32, device="cuda")
-    g = N.MapleGraph(d, 1, staged, n_staged, x_work, out_all, [l["Wr"] for l in layers],
-                     None, [l["packed"] for l in layers], [l["alpha"] for l in layers], ws)
+    lists = ([l["Wr"] for l in layers], None, [l["packed"] for l in layers],
+             [l["alpha"] for l in layers])
+    g = N.MapleGraph(d, 1, staged, n_staged, x_work, out_all, *lists, ws)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        g.launch(stream)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        g.launch(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / args.steps
-    tok_s = 1000.0 / ms_per_step
-    assert torch.isfinite(out_all).all().item()
-    bytes_tok = L * decode_bytes_per_token_layer(H, E, k, I)
-    achieved = bytes_tok / (ms_per_step * 1e-3) / 1e9
+    ms_per_step = timed(torch, lambda: g.launch(stream), args.steps, args.warmup)
+    assert torch.isfinite(out_all).all().item(), "non-finite decode output"
     g.destroy()
-    res = dict(
-        metric=METRIC, value=tok_s, unit="tok/s", n_gpus=1, steps=args.steps,
+    log(f"decode: {1000.0 / ms_per_step:.1f} tok/s, {ms_per_step * 1000:.1f} us/step")
+
+    # profiled eager pass over the same work: per-kernel average durations
+    dx = N.make_dims(H, E, k, I, 0)
+    xe = torch.empty(1, H, dtype=torch.float32, device="cuda")
+    tok = [0]
+
+    def eager_step():
+        xe.copy_(staged[tok[0] % n_staged].float())
+        N.maple_moe_stack_forward(dx, 1, xe, *lists, ws)
+        tok[0] += 1
+    prof = profile_kernels(N, eager_step, min(args.steps, 64))
+    per_kernel = {kn: dict(launches=n, avg_us=1000 * avg,
+                           bytes=decode_bytes(kn, H, E, k, I))
+                  for kn, (n, avg) in prof.items()}
+    dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    dom_bytes = decode_bytes(dom, H, E, k, I)
+    dom_avg_s = prof[dom][1] * 1e-3
+    achieved = dom_bytes / dom_avg_s / 1e9
+    bytes_tok = L * decode_bytes_per_token_layer(H, E, k, I)
+    step_gbs = bytes_tok / (ms_per_step * 1e-3) / 1e9
+    return dict(
+        metric=METRIC, value=1000.0 / ms_per_step, unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="f32", data="synthetic",
         config=dict(workload="decode_stack", hidden=H, experts=E, top_k=k, inter=I, layers=L,
-                    batch=1, tokens_staged=n_staged, graph_steps=True),
+                    batch=1, tokens_staged=n_staged, step="one captured HIP graph per token"),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None,
-                      kernel="whole captured decode step",
-                      algorithmic_bytes_per_launch=bytes_tok),
-    )
-    return res, w
+                      frac=achieved / HBM_PEAK_GBS, traffic=None, kernel=dom,
+                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=dom_avg_s * 1e6),
+        step_roofline=dict(algorithmic_bytes_per_step=bytes_tok, achieved_gbs=step_gbs,
+                           frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
+        kernels=per_kernel,
+    ), w
+
+
+def bench_prefill(args, torch, N, S):
+    w = S.WORKLOADS[args.workload]
+    H, E, k, I, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_tokens
+    layer = build_layers(w, torch, N, S)[0]
+    xs = S.gen_x(w, T)
+    x = torch.from_numpy(xs.view(np.int16)).cuda().view(torch.bfloat16)
+    d = N.make_dims(H, E, k, I, N.MAPLE_X_BF16)
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+
+    def step():
+        N.maple_moe_layer_forward(d, T, x, layer["Wr"], layer["bias"], layer["packed"],
+                                  layer["alpha"], out, ws)
+    ms_per_step = timed(torch, step, args.steps, args.warmup)
+    assert torch.isfinite(out).all().item(), "non-finite prefill output"
+    log(f"{args.workload}: {T / ms_per_step * 1000:.0f} tok/s, {ms_per_step * 1000:.1f} us/layer")
+    prof = profile_kernels(N, step, min(args.steps, 20))
+    per_kernel = {kn: dict(launches=n, avg_us=1000 * avg, int8_ops=prefill_ops(kn, H, k, I, T))
+                  for kn, (n, avg) in prof.items()}
+    dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    ops = prefill_ops(dom, H, k, I, T)
+    dom_avg_s = prof[dom][1] * 1e-3
+    if ops:
+        roof = dict(bound="mfma", achieved=ops / dom_avg_s / 1e12, peak=INT8_PEAK_TOPS,
+                    unit="TOP/s", frac=ops / dom_avg_s / 1e12 / INT8_PEAK_TOPS, traffic=None,
+                    kernel=dom, algorithmic_int8_ops_per_launch=ops,
+                    avg_launch_us=dom_avg_s * 1e6)
+    else:
+        roof = dict(bound="mfma", achieved=None, peak=INT8_PEAK_TOPS, unit="TOP/s", frac=None,
+                    traffic=None, kernel=dom, avg_launch_us=dom_avg_s * 1e6)
+    layer_ops = 2 * T * k * 3 * H * I
+    return dict(
+        metric=METRIC, value=T / ms_per_step * 1000.0, unit="tok/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="int8 MFMA (two limbs) + f32", data="synthetic",
+        config=dict(workload=args.workload, hidden=H, experts=E, top_k=k, inter=I, tokens=T,
+                    layers=1, step="one layer call"),
+        roofline=roof,
+        step_roofline=dict(algorithmic_int8_ops_per_step=layer_ops,
+                           achieved_tops=layer_ops / (ms_per_step * 1e-3) / 1e12,
+                           frac_of_int8_peak=layer_ops / (ms_per_step * 1e-3) / 1e12 /
+                           INT8_PEAK_TOPS),
+        kernels=per_kernel,
+    ), w
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="decode_stack", choices=["decode_stack"])
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_stack",
+                    choices=["decode_stack", "prefill_4096", "prefill_16384"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every token is independent; see DESIGN.md for how it would shard). "
+              "(every token is independent, so the path shards by tokens with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    decode = args.workload == "decode_stack"
+    if args.steps is None:
+        args.steps = 256 if decode else 20
+    if args.warmup is None:
+        args.warmup = 16 if decode else 3
     import torch
     from ternary_weight_moe_amd import _native as N
     from ternary_weight_moe_amd import synth as S
@@ -154,10 +297,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     N.load()  # fails loudly if the HIP library is missing
-    res, w = bench_decode(args, torch, N, S)
-    log(f"{res['value']:.1f} tok/s, {res['ms_per_step'] * 1000:.1f} us/step")
+    res, w = (bench_decode if decode else bench_prefill)(args, torch, N, S)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_baseline_seconds)
+        res["cpu_baseline"] = (cpu_baseline_decode if decode else cpu_baseline_prefill)(
+            w, args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)
 
 

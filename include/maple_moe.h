@@ -21,8 +21,13 @@
  *   y_o = a_d[o] sum_i wd_oi h_i                                    o < H
  *   out = sum_{e in S} gate_e y^(e)
  *
- * The router nonlinearity, tie rule and SwiGLU form are not given by the
- * pages; they are the readings this library implements.
+ * With MAPLE_RMS_NORM, x above is first replaced by x / sqrt(mean(x^2) + 1e-6)
+ * (per token, no learned scale); the stack entry points always do this (each
+ * block is x <- x + MoE(x / rms(x))), since without a normalisation the
+ * residual stream of stacked SwiGLU experts grows without bound.
+ *
+ * The router nonlinearity, tie rule, SwiGLU form and pre-norm are not given by
+ * the pages; they are the readings this library implements.
  *
  * Conventions for every entry point:
  *   - Status: each function returns 0 (MAPLE_OK) or a negative maple_status;
@@ -72,14 +77,19 @@ typedef enum maple_status {
 /* dims.flags */
 #define MAPLE_X_BF16 0x1u         /* x is bf16 [T,H] (else fp32) */
 #define MAPLE_RENORM_TOPK 0x2u    /* gates divided by their sum over the selected experts */
+#define MAPLE_RMS_NORM 0x4u       /* the layer sees x / sqrt(mean(x^2) + MAPLE_RMS_EPS) */
+#define MAPLE_RMS_EPS 1e-6f
 #define MAPLE_FORCE_GEMV 0x10u    /* expert FFN on the VALU GEMV path whatever T is */
 #define MAPLE_FORCE_GROUPED 0x20u /* expert FFN on the grouped int8-MFMA path whatever T is */
 
 /* Limits: hidden a power of two in [256, 4096]; inter a power of two in
  * [128, 2048]; 1 <= top_k <= 8; top_k <= n_experts <= 256;
- * 0 <= n_tokens <= MAPLE_MAX_TOKENS.  The GEMV path takes n_tokens <= 64. */
+ * 0 <= n_tokens <= MAPLE_MAX_TOKENS.  The VALU GEMV path (chosen for
+ * n_tokens <= 16, or forced) takes n_tokens <= 64; the grouped int8-MFMA path
+ * (chosen above 16 tokens, or forced) takes inter <= 512. */
 #define MAPLE_MAX_TOKENS (1 << 20)
 #define MAPLE_GEMV_MAX_TOKENS 64
+#define MAPLE_GROUPED_MAX_INTER 512
 
 typedef struct maple_moe_dims {
   int32_t hidden;    /* H */
@@ -152,8 +162,8 @@ int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const 
                             void* workspace, size_t ws_bytes, const maple_moe_debug* dbg,
                             void* stream);
 
-/* A stack of n_layers MoE layers joined by a residual add, in place:
- * x <- x + MoE_l(x) for l = 0..n_layers-1.  x_inout [T,H] fp32 device.
+/* A stack of n_layers pre-norm MoE blocks joined by a residual add, in place:
+ * x <- x + MoE_l(x / rms(x)) for l = 0..n_layers-1 (MAPLE_RMS_NORM implied).  x_inout [T,H] fp32 device.
  * router_w, packed_w, alpha: host arrays of n_layers device pointers;
  * router_bias: NULL or a host array of n_layers device pointers (entries may be
  * NULL).  dims.flags' MAPLE_X_BF16 is ignored (the residual stream is fp32). */
@@ -185,6 +195,21 @@ int maple_graph_launch(maple_graph* graph, void* stream);
 int maple_graph_set_step(maple_graph* graph, int32_t step, void* stream);
 /* Release the graph and its counter (synchronises the device first). */
 int maple_graph_destroy(maple_graph* graph);
+
+/* ---- kernel timing -------------------------------------------------------- */
+
+/* For benchmarks: while enabled on the calling thread, every kernel that the
+ * forward and pack entry points enqueue is bracketed by two HIP events on its
+ * own stream (events are created by the library and reused).  Not for use
+ * during graph capture.  on != 0 starts a fresh record; on == 0 stops. */
+int maple_profile_enable(int on);
+/* Waits for the recorded events and reports, per kernel name (up to max_kinds
+ * of them, in order of first launch): the name (NUL-terminated, at most 63
+ * characters, in names[i*64]), the number of launches and their summed
+ * milliseconds.  names: max_kinds*64 bytes; launches, total_ms: max_kinds
+ * entries; *n_kinds receives the count.  All are host pointers. */
+int maple_profile_summary(int max_kinds, char* names, int64_t* launches, double* total_ms,
+                          int* n_kinds);
 
 #ifdef __cplusplus
 }

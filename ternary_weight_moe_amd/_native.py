@@ -28,6 +28,7 @@ MAPLE_ERR_HIP = -7
 
 MAPLE_X_BF16 = 0x1
 MAPLE_RENORM_TOPK = 0x2
+MAPLE_RMS_NORM = 0x4
 MAPLE_FORCE_GEMV = 0x10
 MAPLE_FORCE_GROUPED = 0x20
 MAPLE_MAX_TOKENS = 1 << 20
@@ -38,7 +39,7 @@ EXPORTS = [
     "maple_ternary_pack_host", "maple_ternary_unpack_host", "maple_ternary_validate_host",
     "maple_ternary_pack_device", "maple_moe_layer_forward", "maple_moe_stack_forward",
     "maple_moe_stack_graph_create", "maple_graph_launch", "maple_graph_set_step",
-    "maple_graph_destroy",
+    "maple_graph_destroy", "maple_profile_enable", "maple_profile_summary",
 ]
 
 
@@ -102,6 +103,9 @@ def load() -> ctypes.CDLL:
         "maple_graph_launch": (ctypes.c_int, [_P, _P]),
         "maple_graph_set_step": (ctypes.c_int, [_P, i32, _P]),
         "maple_graph_destroy": (ctypes.c_int, [_P]),
+        "maple_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+        "maple_profile_summary": (ctypes.c_int, [ctypes.c_int, _P, _P, _P,
+                                                 ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -217,6 +221,25 @@ def maple_moe_stack_forward(dims: Dims, n_tokens: int, x_inout, router_w: Sequen
         ctypes.cast(rb, _P) if rb is not None else None, ctypes.cast(pw, _P),
         ctypes.cast(al, _P), _dptr(workspace), workspace.numel() * workspace.element_size(),
         ctypes.byref(dbg) if dbg else None, _stream(stream)), "maple_moe_stack_forward")
+
+
+def maple_profile_enable(on: bool) -> None:
+    _check(load().maple_profile_enable(1 if on else 0), "maple_profile_enable")
+
+
+def maple_profile_summary(max_kinds: int = 64) -> dict:
+    """{kernel name: (launches, total ms)} of the records since enabling."""
+    names = ctypes.create_string_buffer(64 * max_kinds)
+    launches = (ctypes.c_int64 * max_kinds)()
+    ms = (ctypes.c_double * max_kinds)()
+    n = ctypes.c_int(0)
+    _check(load().maple_profile_summary(max_kinds, names, launches, ms, ctypes.byref(n)),
+           "maple_profile_summary")
+    out = {}
+    for i in range(min(n.value, max_kinds)):
+        name = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
+        out[name] = (int(launches[i]), float(ms[i]))
+    return out
 
 
 class MapleGraph:

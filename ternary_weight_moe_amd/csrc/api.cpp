@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "internal.h"
 #include "maple_moe.h"
@@ -23,7 +25,6 @@ namespace maple {
 
 // Token count up to which the automatic dispatch uses the VALU GEMV path.
 constexpr int64_t kGemvAuto = 16;
-constexpr int kTileM = 64;
 
 int max_tiles(const Dims& d, int64_t T) { return (int)((T * d.k) / kTileM + d.E + 1); }
 
@@ -36,7 +37,6 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   };
   const int64_t Tk = T * d.k;
   const int64_t nb = (T + 63) / 64;
-  const int64_t kb = d.I / 128;
   ws->logits = (float*)take(sizeof(float) * T * d.E);
   ws->idx = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->gate = (float*)take(sizeof(float) * Tk);
@@ -51,12 +51,50 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->tiles = (int32_t*)take(sizeof(int32_t) * 2 * (size_t)max_tiles(d, T));
   ws->h = (float*)take(sizeof(float) * Tk * d.I);
   ws->xq = (int8_t*)take((size_t)T * 2 * d.H);
-  ws->xs = (float*)take(sizeof(float) * 2 * T);  // scale and (bit-cast) limb row sum
+  ws->xs = (float*)take(sizeof(float) * 3 * T);
   ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
-  ws->hs = (float*)take(sizeof(float) * 2 * Tk * kb);
+  ws->hs = (float*)take(sizeof(float) * 2 * Tk);
   ws->y = (float*)take(sizeof(float) * Tk * d.H);
   ws->bytes = off;
   return off;
+}
+
+// ---- kernel timing ----
+
+namespace {
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct ProfState {
+  bool on = false;
+  std::vector<ProfRecord> recs;
+  std::vector<hipEvent_t> pool;  // events reused across records
+  size_t used = 0;
+};
+thread_local ProfState g_prof;
+
+hipEvent_t prof_event() {
+  if (g_prof.used == g_prof.pool.size()) {
+    hipEvent_t ev = nullptr;
+    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(ev);
+  }
+  return g_prof.pool[g_prof.used++];
+}
+}  // namespace
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (!g_prof.on) return;
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return;
+  if (hipEventRecord(a, s) != hipSuccess) return;
+  g_prof.recs.push_back({name, a, b});
+  slot = (int)g_prof.recs.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (slot >= 0) (void)hipEventRecord(g_prof.recs[slot].stop, stream);
 }
 
 }  // namespace maple
@@ -82,8 +120,8 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
-constexpr uint32_t kKnownFlags =
-    MAPLE_X_BF16 | MAPLE_RENORM_TOPK | MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED;
+constexpr uint32_t kKnownFlags = MAPLE_X_BF16 | MAPLE_RENORM_TOPK | MAPLE_RMS_NORM |
+                                 MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED;
 
 int check_dims(const maple_moe_dims* d, Dims* out) {
   if (!d) return fail(MAPLE_ERR_INVALID_ARG, "dims is NULL");
@@ -104,6 +142,12 @@ int check_dims(const maple_moe_dims* d, Dims* out) {
   return MAPLE_OK;
 }
 
+bool use_gemv(const Dims& d, int64_t T) {
+  if (d.flags & MAPLE_FORCE_GEMV) return true;
+  if (d.flags & MAPLE_FORCE_GROUPED) return false;
+  return T <= maple::kGemvAuto;
+}
+
 int check_tokens(const Dims& d, int64_t T) {
   if (T < 0) return fail(MAPLE_ERR_INVALID_ARG, "n_tokens=%lld < 0", (long long)T);
   if (T > MAPLE_MAX_TOKENS)
@@ -111,6 +155,9 @@ int check_tokens(const Dims& d, int64_t T) {
   if ((d.flags & MAPLE_FORCE_GEMV) && T > MAPLE_GEMV_MAX_TOKENS)
     return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "MAPLE_FORCE_GEMV with n_tokens=%lld > %d",
                 (long long)T, MAPLE_GEMV_MAX_TOKENS);
+  if (!use_gemv(d, T) && d.I > MAPLE_GROUPED_MAX_INTER)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "grouped path (n_tokens=%lld) needs inter <= %d",
+                (long long)T, MAPLE_GROUPED_MAX_INTER);
   return MAPLE_OK;
 }
 
@@ -141,22 +188,23 @@ int device_ready() {
   return MAPLE_OK;
 }
 
-bool use_gemv(const Dims& d, int64_t T) {
-  if (d.flags & MAPLE_FORCE_GEMV) return true;
-  if (d.flags & MAPLE_FORCE_GROUPED) return false;
-  return T <= maple::kGemvAuto;
-}
-
 // One layer on the device: router, routing, expert FFN (+ combine).
 int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
               const float* bias, const uint8_t* packed, const float* alpha, float* out,
               const float* resid, float* delta, const Workspace& ws, const maple_moe_debug* dbg,
               hipStream_t s) {
-  hipError_t e = maple::launch_router(d, T, x, x_bf16, Wr, bias, ws.logits, s);
+  const bool gemv = use_gemv(d, T);
+  hipError_t e = hipSuccess;
+  if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and the large-T router use them
+    e = maple::launch_quant_x(d, T, x, x_bf16, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  }
+  e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 2 * T, ws.logits,
+                           s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   e = maple::launch_route(d, T, ws.logits, ws, s);
   if (e != hipSuccess) return hip_fail(e, "routing launch");
-  if (use_gemv(d, T))
+  if (gemv)
     e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
   else
     e = maple::launch_grouped_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
@@ -377,7 +425,7 @@ int maple_moe_stack_forward(const maple_moe_dims* dims, int32_t n_layers, int32_
   Dims d;
   int rc;
   if ((rc = check_dims(dims, &d))) return rc;
-  d.flags &= ~MAPLE_X_BF16;
+  d.flags = (d.flags & ~MAPLE_X_BF16) | MAPLE_RMS_NORM;
   if ((rc = check_tokens(d, n_tokens))) return rc;
   if ((rc = check_ptr(x_inout, 16, "x_inout"))) return rc;
   if ((rc = check_stack_args(d, n_layers, n_tokens, router_w, router_bias, packed_w, alpha,
@@ -399,7 +447,7 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
   int rc;
   if ((rc = check_dims(dims, &d))) return rc;
   const bool staged_bf16 = (d.flags & MAPLE_X_BF16) != 0;
-  d.flags &= ~MAPLE_X_BF16;
+  d.flags = (d.flags & ~MAPLE_X_BF16) | MAPLE_RMS_NORM;
   if (!graph) return fail(MAPLE_ERR_INVALID_ARG, "graph is NULL");
   *graph = nullptr;
   if ((rc = check_tokens(d, n_tokens))) return rc;
@@ -424,6 +472,8 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
     delete g;
     return hip_fail(e, "graph setup");
   }
+  const bool prof_was_on = maple::g_prof.on;
+  maple::g_prof.on = false;  // no event records inside a capture
   e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e == hipSuccess) {
     e = maple::launch_load_token(staged_x, staged_bf16, n_staged, n_tokens, d.H, g->counter,
@@ -437,7 +487,9 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
     const hipError_t e2 = hipStreamEndCapture(cs, &g->graph);
     if (e == hipSuccess) e = e2;
   }
-  if (e == hipSuccess && rc == MAPLE_OK) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  maple::g_prof.on = prof_was_on;
+  if (e == hipSuccess && rc == MAPLE_OK)
+    e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
   (void)hipStreamDestroy(cs);
   if (e != hipSuccess || rc != MAPLE_OK) {
     const int out_rc = (rc != MAPLE_OK) ? rc : hip_fail(e, "graph capture");
@@ -448,6 +500,48 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
     return out_rc;
   }
   *graph = g;
+  return MAPLE_OK;
+}
+
+int maple_profile_enable(int on) {
+  maple::g_prof.on = on != 0;
+  if (on) {
+    maple::g_prof.recs.clear();
+    maple::g_prof.used = 0;
+  }
+  return MAPLE_OK;
+}
+
+int maple_profile_summary(int max_kinds, char* names, int64_t* launches, double* total_ms,
+                          int* n_kinds) {
+  if (max_kinds < 0 || !n_kinds || (max_kinds > 0 && (!names || !launches || !total_ms)))
+    return fail(MAPLE_ERR_INVALID_ARG, "bad summary buffers");
+  std::vector<std::string> order;
+  std::vector<int64_t> cnt;
+  std::vector<double> ms;
+  for (const auto& r : maple::g_prof.recs) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    size_t i = 0;
+    while (i < order.size() && order[i] != r.name) ++i;
+    if (i == order.size()) {
+      order.push_back(r.name);
+      cnt.push_back(0);
+      ms.push_back(0.0);
+    }
+    cnt[i] += 1;
+    ms[i] += t;
+  }
+  const int n = (int)std::min<size_t>(order.size(), (size_t)max_kinds);
+  for (int i = 0; i < n; ++i) {
+    snprintf(names + 64 * i, 64, "%s", order[i].c_str());
+    launches[i] = cnt[i];
+    total_ms[i] = ms[i];
+  }
+  *n_kinds = (int)order.size();
   return MAPLE_OK;
 }
 

@@ -48,11 +48,15 @@ __device__ __forceinline__ void load_chunk64(const void* base, int64_t off, floa
   }
 }
 
-// Sum of the chunk, then pre-scale position 16w+4b+q by 4^-b.
-__device__ __forceinline__ float prep_chunk(float (&v)[64]) {
-  float s = 0.f;
+// Sum (and sum of squares) of the chunk, then pre-scale position 16w+4b+q by 4^-b.
+__device__ __forceinline__ float prep_chunk(float (&v)[64], float* ssq = nullptr) {
+  float s = 0.f, q = 0.f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) s += v[i];
+  for (int i = 0; i < 64; ++i) {
+    s += v[i];
+    q = fmaf(v[i], v[i], q);
+  }
+  if (ssq) *ssq = q;
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     const int b = (i >> 2) & 3;
@@ -89,9 +93,11 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // h[p, i] = silu(a_g[i] * (Wg_i . x_t)) * (a_u[i] * (Wu_i . x_t)) for every slot
 // p of every active expert.  blockIdx.y: active expert; blockIdx.x: row block.
+// With norm, x_t is read as x_t / rms(x_t): the lanes of one row cover all of
+// x_t, so the sum of squares comes with the same group reduction.
 template <int LPR, int NT, bool BF16>
 __global__ __launch_bounds__(256) void k_gateup_gemv(
-    const void* __restrict__ x, int H, int I, const uint8_t* __restrict__ packed,
+    const void* __restrict__ x, int norm, int H, int I, const uint8_t* __restrict__ packed,
     const float* __restrict__ alpha, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_tok, const int32_t* __restrict__ active,
     const int32_t* __restrict__ n_active, float* __restrict__ h) {
@@ -123,12 +129,14 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(
   const int p0 = offsets[e], p1 = offsets[e + 1];
   for (int pb = p0; pb < p1; pb += NT) {
     float xv[NT][64];
-    float xs[NT];
+    float xs[NT], rn[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int tok = sorted_tok[min(pb + t, p1 - 1)];
       load_chunk64<BF16>(x, (int64_t)tok * H + lk * 64, xv[t]);
-      xs[t] = prep_chunk(xv[t]);
+      float q;
+      xs[t] = prep_chunk(xv[t], &q);
+      rn[t] = norm ? rsqrtf(group_sum<LPR>(q) / (float)H + MAPLE_RMS_EPS) : 1.f;
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(
         const float dg = group_sum<LPR>(code_dot(wg[p], xv[t]) - xs[t]);
         const float du = group_sum<LPR>(code_dot(wu[p], xv[t]) - xs[t]);
         if (lk == 0 && pb + t < p1) {
-          const float g = ag[p] * dg, u = au[p] * du;
+          const float g = ag[p] * dg * rn[t], u = au[p] * du * rn[t];
           h[(int64_t)(pb + t) * I + rows[p]] = g / (1.f + expf(-g)) * u;
         }
       }
@@ -192,12 +200,14 @@ template <int LPR, int NT>
 hipError_t gateup(const Dims& d, int64_t T, const void* x, bool bf16, const uint8_t* packed,
                   const float* alpha, const Workspace& ws, hipStream_t s) {
   constexpr int ROWS_WG = 4 * 2 * (64 / LPR);
+  const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   const dim3 grid(d.I / ROWS_WG, (unsigned)std::min<int64_t>(d.E, T * d.k));
+  MAPLE_PROF("gateup_gemv", s);
   if (bf16)
-    k_gateup_gemv<LPR, NT, true><<<grid, 256, 0, s>>>(x, d.H, d.I, packed, alpha, ws.offsets,
+    k_gateup_gemv<LPR, NT, true><<<grid, 256, 0, s>>>(x, norm, d.H, d.I, packed, alpha, ws.offsets,
                                                       ws.sorted_tok, ws.active, ws.n_active, ws.h);
   else
-    k_gateup_gemv<LPR, NT, false><<<grid, 256, 0, s>>>(x, d.H, d.I, packed, alpha, ws.offsets,
+    k_gateup_gemv<LPR, NT, false><<<grid, 256, 0, s>>>(x, norm, d.H, d.I, packed, alpha, ws.offsets,
                                                        ws.sorted_tok, ws.active, ws.n_active, ws.h);
   return hipGetLastError();
 }
@@ -221,6 +231,7 @@ hipError_t down(const Dims& d, int64_t T, const uint8_t* packed, const float* al
                 hipStream_t s) {
   constexpr int RPI = 64 / LPR;
   const size_t lds = (size_t)T * d.k * RPI * sizeof(float);
+  MAPLE_PROF("down_combine_gemv", s);
   k_down_combine<LPR><<<d.H / RPI, 256, lds, s>>>(ws.h, d.H, d.I, packed, alpha, ws.gate,
                                                   ws.offsets, ws.slot_pos, ws.active,
                                                   ws.n_active, (int)T, d.k, out, resid, delta);

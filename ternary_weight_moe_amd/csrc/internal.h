@@ -8,6 +8,9 @@
 
 namespace maple {
 
+// Slots per M tile of the grouped GEMMs (granularity of the tile list).
+constexpr int kTileM = 32;
+
 // Workspace carve-up for one layer call with T tokens.  Every region is
 // 256-byte aligned.  The same carve serves the stack (layers run one after
 // another and reuse it).
@@ -26,9 +29,9 @@ struct Workspace {
   int32_t* n_tiles;     // [1]
   float* h;             // [T*k, I]  fp32 (GEMV path)
   int8_t* xq;           // [T, 2, H] two int8 limbs of x (grouped path)
-  float* xs;            // [T]       scale of x's limbs
+  float* xs;            // [3T]      scale of x's limbs | limb row sum (int bits) | 1/rms(x)
   int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
-  float* hs;            // [T*k, I/128] scale per (slot, 128-column block)
+  float* hs;            // [2, T*k]  scale of h's limbs per slot | limb row sum (int bits)
   float* y;             // [T*k, H]  expert outputs before the combine (grouped path)
   size_t bytes;
 };
@@ -39,15 +42,28 @@ struct Dims {
 };
 
 size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws);  // base may be null
+
+// Kernel timing hook (maple_profile_enable): brackets one launch with events
+// on its stream when the calling thread has profiling on; free otherwise.
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+#define MAPLE_PROF(name, s) ::maple::ProfScope maple_prof_scope_(name, s)
 int max_tiles(const Dims& d, int64_t T);
 
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
-                         const float* Wr, const float* bias, float* logits, hipStream_t s);
+                         const float* Wr, const float* bias, const float* rinv, float* logits,
+                         hipStream_t s);
 hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
                         hipStream_t s);
+hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
+                          const Workspace& ws, hipStream_t s);
 hipError_t launch_gemv_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
                            const uint8_t* packed, const float* alpha, const Workspace& ws,
                            float* out, const float* resid, float* delta, hipStream_t s);

@@ -20,8 +20,6 @@
 namespace maple {
 namespace {
 
-constexpr int kTileM = 64;  // M tile of the grouped GEMM (tile list granularity)
-
 __device__ __forceinline__ float4 load_x4_f32(const float* x) {
   return *reinterpret_cast<const float4*>(x);
 }
@@ -52,17 +50,19 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---- router logits ---------------------------------------------------------
 
 // Small T: one wave per expert, up to 4 tokens per block.  H % 256 == 0.
+// With norm, the dot product is scaled by 1/rms(x) (the norm is linear in the
+// logits, so it is applied after the sum; the wave reads all of x anyway).
 template <bool BF16>
 __global__ __launch_bounds__(64) void k_router_gemv(const void* __restrict__ x, int T, int H,
                                                     const float* __restrict__ Wr,
                                                     const float* __restrict__ bias, int E,
-                                                    float* __restrict__ logits) {
+                                                    int norm, float* __restrict__ logits) {
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * 4;
   const int lane = threadIdx.x;
   const int nt = min(4, T - t0);
   const float* w = Wr + (int64_t)e * H;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, ss[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j = lane * 4; j < H; j += 256) {
     const float4 wv = *reinterpret_cast<const float4*>(w + j);
 #pragma unroll
@@ -73,22 +73,26 @@ __global__ __launch_bounds__(64) void k_router_gemv(const void* __restrict__ x, 
         acc[tt] = fmaf(wv.y, xv.y, acc[tt]);
         acc[tt] = fmaf(wv.z, xv.z, acc[tt]);
         acc[tt] = fmaf(wv.w, xv.w, acc[tt]);
+        ss[tt] = fmaf(xv.x, xv.x, fmaf(xv.y, xv.y, fmaf(xv.z, xv.z, fmaf(xv.w, xv.w, ss[tt]))));
       }
     }
   }
   const float b = bias ? bias[e] : 0.f;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const float s = wave_sum(acc[tt]);
+    float s = wave_sum(acc[tt]);
+    if (norm) s *= rsqrtf(wave_sum(ss[tt]) / (float)H + MAPLE_RMS_EPS);
     if (lane == 0 && tt < nt) logits[(int64_t)(t0 + tt) * E + e] = s + b;
   }
 }
 
 // Large T: 64x64 output tile per block, K step 16 through LDS, 4x4 per thread.
+// rinv (nullable): per-token 1/rms(x), computed beforehand.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_router_gemm(const void* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr,
                                                      const float* __restrict__ bias, int E,
+                                                     const float* __restrict__ rinv,
                                                      float* __restrict__ logits) {
   __shared__ float xs[16][68];
   __shared__ float ws[16][68];
@@ -121,7 +125,8 @@ __global__ __launch_bounds__(256) void k_router_gemm(const void* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = m0 + tm + i, e = n0 + tn + j;
-      if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+      if (t < T && e < E)
+        logits[(int64_t)t * E + e] = acc[i][j] * (rinv ? rinv[t] : 1.f) + (bias ? bias[e] : 0.f);
     }
 }
 
@@ -344,19 +349,25 @@ __global__ __launch_bounds__(256) void k_route_scatter(int64_t n_slots, int E, i
 }  // namespace
 
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
-                         const float* bias, float* logits, hipStream_t s) {
+                         const float* bias, const float* rinv, float* logits, hipStream_t s) {
+  const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   if (T <= 64) {
     const dim3 grid(d.E, (unsigned)((T + 3) / 4));
+    MAPLE_PROF("router_gemv", s);
     if (x_bf16)
-      k_router_gemv<true><<<grid, 64, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, logits);
+      k_router_gemv<true><<<grid, 64, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, norm, logits);
     else
-      k_router_gemv<false><<<grid, 64, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, logits);
+      k_router_gemv<false><<<grid, 64, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, norm, logits);
   } else {
+    if (norm && !rinv) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((T + 63) / 64), (unsigned)((d.E + 63) / 64));
+    MAPLE_PROF("router_gemm", s);
     if (x_bf16)
-      k_router_gemm<true><<<grid, 256, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, logits);
+      k_router_gemm<true><<<grid, 256, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E,
+                                               norm ? rinv : nullptr, logits);
     else
-      k_router_gemm<false><<<grid, 256, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, logits);
+      k_router_gemm<false><<<grid, 256, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E,
+                                                norm ? rinv : nullptr, logits);
   }
   return hipGetLastError();
 }
@@ -365,20 +376,30 @@ hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Wor
                         hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
   if (T <= 64) {
+    MAPLE_PROF("route_small", s);
     k_route_small<<<1, 256, 0, s>>>(logits, (int)T, d.E, d.k, renorm, ws.idx, ws.gate,
                                     ws.offsets, ws.active, ws.n_active, ws.sorted_tok,
                                     ws.slot_pos, ws.tiles, ws.n_tiles);
     return hipGetLastError();
   }
   const int nb = (int)((T + 63) / 64);
-  k_route_block<<<nb, 256, 0, s>>>(logits, (int)T, d.E, d.k, renorm, ws.idx, ws.gate,
-                                   ws.blk_count, ws.blk_rank);
-  k_route_scan<<<1, 256, 0, s>>>(nb, d.E, ws.blk_count, ws.offsets, ws.active, ws.n_active,
-                                 ws.tiles, ws.n_tiles);
+  {
+    MAPLE_PROF("route_block", s);
+    k_route_block<<<nb, 256, 0, s>>>(logits, (int)T, d.E, d.k, renorm, ws.idx, ws.gate,
+                                     ws.blk_count, ws.blk_rank);
+  }
+  {
+    MAPLE_PROF("route_scan", s);
+    k_route_scan<<<1, 256, 0, s>>>(nb, d.E, ws.blk_count, ws.offsets, ws.active, ws.n_active,
+                                   ws.tiles, ws.n_tiles);
+  }
   const int64_t n_slots = T * d.k;
-  k_route_scatter<<<(unsigned)((n_slots + 255) / 256), 256, 0, s>>>(
-      n_slots, d.E, d.k, ws.idx, ws.offsets, ws.blk_count, ws.blk_rank, ws.slot_pos,
-      ws.sorted_tok);
+  {
+    MAPLE_PROF("route_scatter", s);
+    k_route_scatter<<<(unsigned)((n_slots + 255) / 256), 256, 0, s>>>(
+        n_slots, d.E, d.k, ws.idx, ws.offsets, ws.blk_count, ws.blk_rank, ws.slot_pos,
+        ws.sorted_tok);
+  }
   return hipGetLastError();
 }
 

@@ -53,9 +53,9 @@ class Layer:
         self.d_bias = None if self.bias is None else torch.from_numpy(self.bias).to(dev)
         self.d_alpha = torch.from_numpy(self.alpha).to(dev)
 
-    def oracle_layer(self, x64, k, inter, renorm=False):
+    def oracle_layer(self, x64, k, inter, renorm=False, prenorm=False):
         return oracle.moe_layer(x64, self.Wr, self.bias, self.packed_ref, self.alpha, k=k,
-                                inter=inter, renorm=renorm)
+                                inter=inter, renorm=renorm, prenorm=prenorm)
 
 
 def x_device(w: S.Workload, x_host: np.ndarray):

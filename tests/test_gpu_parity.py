@@ -47,21 +47,30 @@ def run_layer(w, L, x_host, flags=0):
     return out.cpu().numpy(), {n: b.cpu().numpy() for n, b in bufs.items()}
 
 
-def check_layer(w, L, x_host, flags=0, renorm=False, what=""):
-    log(f"{what}: T={x_host.shape[0]} flags={flags:#x}")
-    got, dbg = run_layer(w, L, x_host, flags | (N.MAPLE_RENORM_TOPK if renorm else 0))
+def check_layer(w, L, x_host, flags=0, renorm=False, prenorm=False, sample=None, what=""):
+    """Routing of every token bit-exact; outputs of every token, or of the
+    tokens in `sample`, within tolerance."""
+    T = x_host.shape[0]
+    log(f"{what}: T={T} flags={flags:#x}")
+    flags |= (N.MAPLE_RENORM_TOPK if renorm else 0) | (N.MAPLE_RMS_NORM if prenorm else 0)
+    got, dbg = run_layer(w, L, x_host, flags)
     x64 = S.x_as_f32(w, x_host).astype(np.float64)
-    ref = L.oracle_layer(x64, w.top_k, w.inter, renorm=renorm)
+    xr = oracle.rms_normalize(x64) if prenorm else x64
+    logits = oracle.router_logits(xr, L.Wr, L.bias)
+    idx_ref, gate_ref = oracle.topk(logits, w.top_k, renorm)
     assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
-                         ref["idx"], w.n_experts, what)
-    np.testing.assert_allclose(dbg["logits"], ref["logits"], rtol=0, atol=5e-5)
-    # gates, matched per (token, expert)
-    for t in range(x_host.shape[0]):
-        gr = dict(zip(ref["idx"][t].tolist(), ref["gate"][t].tolist()))
+                         idx_ref, w.n_experts, what)
+    np.testing.assert_allclose(dbg["logits"], logits, rtol=0, atol=5e-5)
+    for t in range(T):  # gates, matched per (token, expert)
+        gr = dict(zip(idx_ref[t].tolist(), gate_ref[t].tolist()))
         gg = dict(zip(dbg["idx"][t].tolist(), dbg["gate"][t].tolist()))
         for e in gr:
             assert abs(gg[e] - gr[e]) <= 1e-5 * max(1.0, abs(gr[e])), (t, e)
-    assert_close(got, ref["out"], what)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    ref = L.oracle_layer(x64[rows], w.top_k, w.inter, renorm=renorm, prenorm=prenorm)
+    assert np.array_equal(ref["idx"], idx_ref[rows])
+    assert_close(got[rows], ref["out"], what)
     return got
 
 
@@ -147,7 +156,9 @@ def test_edge_all_experts_and_k1():
     check_layer(w1, L1, x1, what="k = 1")
 
 
-def test_edge_max_skew_all_tokens_one_group(dec):
+@pytest.mark.parametrize("flags", [N.MAPLE_FORCE_GEMV, N.MAPLE_FORCE_GROUPED],
+                         ids=["gemv", "grouped"])
+def test_edge_max_skew_all_tokens_one_group(dec, flags):
     """A bias of +50 on eight experts sends every token to the same eight."""
     w, L = dec
     hot = [3, 17, 64, 65, 128, 200, 254, 255]
@@ -158,7 +169,7 @@ def test_edge_max_skew_all_tokens_one_group(dec):
     Ls.bias = bias
     Ls.d_bias = torch.from_numpy(bias).cuda()
     x = S.gen_x(w, 64, token0=5000)
-    got = check_layer(w, Ls, x, flags=N.MAPLE_FORCE_GEMV, what="max skew")
+    got = check_layer(w, Ls, x, flags=flags, what="max skew")
     assert got.shape == (64, w.hidden)
 
 
@@ -171,3 +182,49 @@ def test_zero_tokens_is_a_no_op(dec):
     N.maple_moe_layer_forward(d, 0, x, L.d_Wr, None, L.packed, L.d_alpha, out, ws)
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+# ---- grouped int8-MFMA path -----------------------------------------------------------
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_tiny_layer_grouped(tiny, renorm):
+    w, L = tiny
+    x, _ = layer_tokens_with_gap(w, L, w.n_tokens)
+    check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED, renorm=renorm, what="tiny grouped")
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 200])
+def test_decode_layer_grouped(dec, T):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, T, token0=7000 + 10 * T)
+    check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED, what=f"decode layer grouped T={T}")
+
+
+def test_grouped_matches_gemv_per_token(dec):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, 48, token0=8800)
+    a, _ = run_layer(w, L, x, N.MAPLE_FORCE_GEMV)
+    b, _ = run_layer(w, L, x, N.MAPLE_FORCE_GROUPED)
+    assert_close(b, a, "grouped vs gemv")
+
+
+@pytest.mark.parametrize("prenorm", [False, True])
+def test_prenorm_flag_both_paths(dec, prenorm):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, 20, token0=9900)
+    xs = (S.x_as_f32(w, x) * 3.0).astype(np.float32)  # rms 3: the norm matters
+    wf = workload("decode_layer", x_bf16=False)
+    for flags in (N.MAPLE_FORCE_GEMV, N.MAPLE_FORCE_GROUPED):
+        check_layer(wf, L, xs, flags=flags, prenorm=prenorm, what=f"prenorm={prenorm}")
+
+
+@pytest.mark.parametrize("name,n_sample", [("prefill_4096", 256), ("prefill_16384", 96)])
+def test_prefill_layer(name, n_sample):
+    w = S.WORKLOADS[name]
+    L = Layer(w, 0)
+    x, regen = layer_tokens_with_gap(w, L, w.n_tokens)
+    log(f"{name}: regenerated {len(regen)} tokens")
+    rng = np.random.default_rng(w.seed)
+    sample = np.sort(np.concatenate([[0, w.n_tokens - 1],
+                                     rng.choice(w.n_tokens, n_sample, replace=False)]))
+    check_layer(w, L, x, sample=sample, what=name)

@@ -93,11 +93,20 @@ def test_decode_stack_graph_replays(stack3):
     g.destroy()
 
 
-def test_batched_zipf_stack_one_step():
+@pytest.fixture(scope="module")
+def zipf():
     w = S.WORKLOADS["batched_stack_zipf"]
     layers = build_stack(w)
     x, x64, ref, regen = stack_tokens_with_gap(w, layers, w.n_tokens)
     distinct = [len(np.unique(ref["idx"][l])) for l in range(w.n_layers)]
+    counts = np.bincount(ref["idx"][0].reshape(-1), minlength=w.n_experts)
     log(f"zipf: regenerated {len(regen)} tokens; distinct experts per layer "
-        f"min {min(distinct)} mean {np.mean(distinct):.1f} max {max(distinct)}")
-    check_stack(w, layers, x, ref, flags=N.MAPLE_FORCE_GEMV, what="zipf gemv")
+        f"min {min(distinct)} mean {np.mean(distinct):.1f} max {max(distinct)}; "
+        f"layer 0 largest groups {sorted(counts)[-5:]} empty {(counts == 0).sum()}")
+    return w, layers, x, ref
+
+
+@pytest.mark.parametrize("flags", [0, N.MAPLE_FORCE_GEMV], ids=["auto", "gemv"])
+def test_batched_zipf_stack_one_step(zipf, flags):
+    w, layers, x, ref = zipf
+    check_stack(w, layers, x, ref, flags=flags, what=f"zipf flags={flags:#x}")
