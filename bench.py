@@ -179,7 +179,7 @@ def bench_decode(args, torch, N, S):
     d = N.make_dims(H, E, k, I, N.MAPLE_X_BF16)
     ws = torch.empty(N.maple_moe_workspace_bytes(d, 1), dtype=torch.uint8, device="cuda")
     x_work = torch.empty(1, H, dtype=torch.float32, device="cuda")
-    out_all = torch.empty(n_staged, 1, H, dtype=torch.float32, device="cuda")
+    out_all = torch.zeros(n_staged, 1, H, dtype=torch.float32, device="cuda")
     lists = ([l["Wr"] for l in layers], None, [l["packed"] for l in layers],
              [l["alpha"] for l in layers])
     g = N.MapleGraph(d, 1, staged, n_staged, x_work, out_all, *lists, ws)

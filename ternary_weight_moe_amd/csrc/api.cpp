@@ -23,8 +23,13 @@ struct maple_graph {
 
 namespace maple {
 
-// Token count up to which the automatic dispatch uses the VALU GEMV path.
+// Token counts up to which the automatic dispatch uses the VALU GEMV path: for
+// a single layer, and inside a stack.  The stack keeps the fp32 GEMV path up to
+// its limit because the grouped path's two-limb activations (about 2e-4
+// relative error per layer) accumulate along the residual stream enough to move
+// router logits by more than 5e-5 within 24 layers.
 constexpr int64_t kGemvAuto = 16;
+constexpr int64_t kGemvAutoStack = MAPLE_GEMV_MAX_TOKENS;
 
 int max_tiles(const Dims& d, int64_t T) { return (int)((T * d.k) / kTileM + d.E + 1); }
 
@@ -142,10 +147,14 @@ int check_dims(const maple_moe_dims* d, Dims* out) {
   return MAPLE_OK;
 }
 
+// Stack calls carry kStackCall in Dims::flags (an internal bit, never accepted
+// from callers).
+constexpr uint32_t kStackCall = 0x80000000u;
+
 bool use_gemv(const Dims& d, int64_t T) {
   if (d.flags & MAPLE_FORCE_GEMV) return true;
   if (d.flags & MAPLE_FORCE_GROUPED) return false;
-  return T <= maple::kGemvAuto;
+  return T <= ((d.flags & kStackCall) ? maple::kGemvAutoStack : maple::kGemvAuto);
 }
 
 int check_tokens(const Dims& d, int64_t T) {
@@ -425,7 +434,7 @@ int maple_moe_stack_forward(const maple_moe_dims* dims, int32_t n_layers, int32_
   Dims d;
   int rc;
   if ((rc = check_dims(dims, &d))) return rc;
-  d.flags = (d.flags & ~MAPLE_X_BF16) | MAPLE_RMS_NORM;
+  d.flags = (d.flags & ~MAPLE_X_BF16) | MAPLE_RMS_NORM | kStackCall;
   if ((rc = check_tokens(d, n_tokens))) return rc;
   if ((rc = check_ptr(x_inout, 16, "x_inout"))) return rc;
   if ((rc = check_stack_args(d, n_layers, n_tokens, router_w, router_bias, packed_w, alpha,
@@ -447,7 +456,7 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
   int rc;
   if ((rc = check_dims(dims, &d))) return rc;
   const bool staged_bf16 = (d.flags & MAPLE_X_BF16) != 0;
-  d.flags = (d.flags & ~MAPLE_X_BF16) | MAPLE_RMS_NORM;
+  d.flags = (d.flags & ~MAPLE_X_BF16) | MAPLE_RMS_NORM | kStackCall;
   if (!graph) return fail(MAPLE_ERR_INVALID_ARG, "graph is NULL");
   *graph = nullptr;
   if ((rc = check_tokens(d, n_tokens))) return rc;
