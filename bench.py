@@ -49,7 +49,12 @@ def decode_bytes(kernel, H, E, k, I, T=1):
     """Algorithmic HBM bytes of one launch of a decode-path kernel for T tokens
     whose k experts are all distinct (T * k experts read once)."""
     ne = T * k
+    router = 4 * E * H + 4 * T * H + 4 * T * E
+    gateup = ne * (2 * I * H // 4 + 4 * 2 * I) + 4 * T * H + 4 * ne * I
+    down = ne * (H * I // 4 + 4 * H) + 4 * ne * I + 2 * 4 * T * H
     return {
+        "d1_router": router, "d1_gateup": gateup + 4 * E, "d1_down": down,
+        "d1m_gateup": gateup + 4 * E, "d1m_down": down, "d1q_router": router + 3 * H,
         "router_gemv": 4 * E * H + 4 * T * H + 4 * T * E,
         "route_small": 4 * T * E + 4 * (3 * ne + 2 * E + 1),
         "gateup_gemv": ne * (2 * I * H // 4 + 4 * 2 * I) + 4 * T * H + 4 * ne * I,

@@ -55,7 +55,8 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->blk_rank = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->tiles = (int32_t*)take(sizeof(int32_t) * 2 * (size_t)max_tiles(d, T));
   ws->h = (float*)take(sizeof(float) * Tk * d.I);
-  ws->xq = (int8_t*)take((size_t)T * 2 * d.H);
+  ws->xq = (int8_t*)take((size_t)T * 4 * d.H);
+  ws->part = (int32_t*)take(sizeof(int32_t) * 4 * d.E);
   ws->xs = (float*)take(sizeof(float) * 3 * T);
   ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
   ws->hs = (float*)take(sizeof(float) * 2 * Tk);
@@ -204,20 +205,25 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
               hipStream_t s) {
   const bool gemv = use_gemv(d, T);
   hipError_t e = hipSuccess;
-  if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and the large-T router use them
-    e = maple::launch_quant_x(d, T, x, x_bf16, ws, s);
-    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  if (gemv && T == 1) {  // one token: router, top-k + gate/up, down + combine
+    e = maple::launch_decode1(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  } else {
+    if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and large-T router use them
+      e = maple::launch_quant_x(d, T, x, x_bf16, ws, s);
+      if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    }
+    e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 2 * T,
+                             ws.logits, s);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    e = maple::launch_route(d, T, ws.logits, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "routing launch");
+    if (gemv)
+      e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
+    else
+      e = maple::launch_grouped_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
+    if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   }
-  e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 2 * T, ws.logits,
-                           s);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
-  e = maple::launch_route(d, T, ws.logits, ws, s);
-  if (e != hipSuccess) return hip_fail(e, "routing launch");
-  if (gemv)
-    e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
-  else
-    e = maple::launch_grouped_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
-  if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   if (dbg) {
     const int64_t Tk = T * d.k;
     struct {

@@ -17,6 +17,7 @@
 // lane's 64 columns stays in registers across all the rows the lane visits.
 #include "internal.h"
 #include "maple_moe.h"
+#include "wave.h"
 
 namespace maple {
 namespace {
@@ -84,13 +85,6 @@ __device__ __forceinline__ float code_dot(const uint4 wq, const float (&v)[64]) 
   return acc0 + acc1;
 }
 
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // h[p, i] = silu(a_g[i] * (Wg_i . x_t)) * (a_u[i] * (Wu_i . x_t)) for every slot
 // p of every active expert.  blockIdx.y: active expert; blockIdx.x: row block.
 // With norm, x_t is read as x_t / rms(x_t): the lanes of one row cover all of
@@ -136,14 +130,14 @@ __global__ __launch_bounds__(256) void k_gateup_gemv(
       load_chunk64<BF16>(x, (int64_t)tok * H + lk * 64, xv[t]);
       float q;
       xs[t] = prep_chunk(xv[t], &q);
-      rn[t] = norm ? rsqrtf(group_sum<LPR>(q) / (float)H + MAPLE_RMS_EPS) : 1.f;
+      rn[t] = norm ? rsqrtf(group_reduce<LPR, OpSum>(q) / (float)H + MAPLE_RMS_EPS) : 1.f;
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float dg = group_sum<LPR>(code_dot(wg[p], xv[t]) - xs[t]);
-        const float du = group_sum<LPR>(code_dot(wu[p], xv[t]) - xs[t]);
+        const float dg = group_reduce<LPR, OpSum>(code_dot(wg[p], xv[t]) - xs[t]);
+        const float du = group_reduce<LPR, OpSum>(code_dot(wu[p], xv[t]) - xs[t]);
         if (lk == 0 && pb + t < p1) {
           const float g = ag[p] * dg * rn[t], u = au[p] * du * rn[t];
           h[(int64_t)(pb + t) * I + rows[p]] = g / (1.f + expf(-g)) * u;
@@ -181,7 +175,7 @@ __global__ __launch_bounds__(256) void k_down_combine(
       float hv[64];
       load_chunk64<false>(h, (int64_t)p * I + lk * 64, hv);
       const float hs = prep_chunk(hv);
-      const float d = group_sum<LPR>(code_dot(wd, hv) - hs);
+      const float d = group_reduce<LPR, OpSum>(code_dot(wd, hv) - hs);
       if (lk == 0) s_contrib[p * RPI + lr] = ad * d;
     }
   }

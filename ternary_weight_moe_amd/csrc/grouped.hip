@@ -30,6 +30,7 @@
 
 #include "internal.h"
 #include "maple_moe.h"
+#include "wave.h"
 
 namespace maple {
 namespace {
@@ -39,22 +40,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int TM = kTileM;        // slots per M tile
 constexpr float kQMax = 16256.f;  // 127 * 128
 constexpr uint32_t kCodeMask = 0x03030303u;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 __device__ __forceinline__ v4i unpack_word(uint32_t w) {
   v4i r;
@@ -100,8 +85,8 @@ __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int
       ss = fmaf(f, f, ss);
     }
   }
-  amax = wave_max(amax);
-  ss = wave_sum(ss);
+  amax = wave_max_f(amax);
+  ss = wave_sum_f(ss);
   if (lane == 0) {
     s_a[wave] = amax;
     s_s[wave] = ss;
@@ -283,9 +268,7 @@ __global__ __launch_bounds__(NW * 64) void k_gateup_mfma(
         hv[a][b][i] = h;
         mx = fmaxf(mx, fabsf(h));
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      rmax[a][i] = mx;
+      rmax[a][i] = group_reduce<16, OpMax>(mx);
     }
   if (c16 == 0)
 #pragma unroll
@@ -316,9 +299,7 @@ __global__ __launch_bounds__(NW * 64) void k_gateup_mfma(
         sH[TM * I + m * I + col] = (int8_t)(q - (hi << 7));
         qs += q;
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) qs += __shfl_xor(qs, o, 64);
-      rsum[a][i] = qs;
+      rsum[a][i] = group_reduce_i<16, OpSum>(qs);
       if (wave == 0 && c16 == 0 && m < np) hs[p0 + m] = sc;
     }
   if (c16 == 0)

@@ -28,7 +28,9 @@ struct Workspace {
   int32_t* tiles;       // [max_tiles*2] grouped-GEMM tile list (expert, m0)
   int32_t* n_tiles;     // [1]
   float* h;             // [T*k, I]  fp32 (GEMV path)
-  int8_t* xq;           // [T, 2, H] two int8 limbs of x (grouped path)
+  int8_t* xq;           // [T, 4, H] int8 limbs of x (two on the grouped path, three on
+                        //           the one-token path)
+  int32_t* part;        // [E, 4]    per-router-block partial limb sums (one-token path)
   float* xs;            // [3T]      scale of x's limbs | limb row sum (int bits) | 1/rms(x)
   int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
   float* hs;            // [2, T*k]  scale of h's limbs per slot | limb row sum (int bits)
@@ -62,6 +64,10 @@ hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          hipStream_t s);
 hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
                         hipStream_t s);
+hipError_t launch_decode1(const Dims& d, const void* x, bool x_bf16, const float* Wr,
+                          const float* bias, const uint8_t* packed, const float* alpha,
+                          const Workspace& ws, float* out, const float* resid, float* delta,
+                          hipStream_t s);
 hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
                           const Workspace& ws, hipStream_t s);
 hipError_t launch_gemv_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,

@@ -16,6 +16,7 @@
 
 #include "internal.h"
 #include "maple_moe.h"
+#include "wave.h"
 
 namespace maple {
 namespace {
@@ -34,17 +35,6 @@ __device__ __forceinline__ float4 load_x4(const void* x, int64_t off) {
     return load_x4_bf16(reinterpret_cast<const uint16_t*>(x) + off);
   else
     return load_x4_f32(reinterpret_cast<const float*>(x) + off);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
 }
 
 // ---- router logits ---------------------------------------------------------
@@ -80,8 +70,8 @@ __global__ __launch_bounds__(64) void k_router_gemv(const void* __restrict__ x, 
   const float b = bias ? bias[e] : 0.f;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    float s = wave_sum(acc[tt]);
-    if (norm) s *= rsqrtf(wave_sum(ss[tt]) / (float)H + MAPLE_RMS_EPS);
+    float s = wave_sum_f(acc[tt]);
+    if (norm) s *= rsqrtf(wave_sum_f(ss[tt]) / (float)H + MAPLE_RMS_EPS);
     if (lane == 0 && tt < nt) logits[(int64_t)(t0 + tt) * E + e] = s + b;
   }
 }
@@ -128,65 +118,6 @@ __global__ __launch_bounds__(256) void k_router_gemm(const void* __restrict__ x,
       if (t < T && e < E)
         logits[(int64_t)t * E + e] = acc[i][j] * (rinv ? rinv[t] : 1.f) + (bias ? bias[e] : 0.f);
     }
-}
-
-// ---- softmax + top-k for one token, on one wave ------------------------------
-
-// Lane holds logits e = lane + 64*m (m < 4; E <= 256).  Selection order is
-// (logit desc, index asc); NaN logits rank as -inf so the k indices are always
-// valid experts.  Lane j < k returns the j-th selection and its gate.
-__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k,
-                                          bool renorm, int lane, int* my_idx, float* my_gate) {
-  float v[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int e = lane + 64 * m;
-    float l = (e < E) ? lrow[e] : -INFINITY;
-    if (l != l) l = -INFINITY;
-    v[m] = l;
-  }
-  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-  mx = wave_max(mx);
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    if (lane + 64 * m < E) s += expf(v[m] - mx);
-  s = wave_sum(s);
-  unsigned taken = 0;
-  float gsum = 0.f;
-  int out_i = 0;
-  float out_g = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = lane + 64 * m;
-      if (e < E && !(taken & (1u << m)) && (v[m] > bv || (v[m] == bv && e < bi))) {
-        bv = v[m];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    const float g = expf(bv - mx) / s;
-    gsum += g;
-    if (lane == j) {
-      out_i = bi;
-      out_g = g;
-    }
-  }
-  if (renorm) out_g /= gsum;
-  *my_idx = out_i;
-  *my_gate = out_g;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -256,7 +187,7 @@ __global__ __launch_bounds__(256) void k_route_small(
   for (int t = wave; t < T; t += 4) {
     int i;
     float g;
-    wave_topk(logits + (int64_t)t * E, E, k, renorm != 0, lane, &i, &g);
+    wave_softmax_topk(logits + (int64_t)t * E, E, k, renorm != 0, lane, &i, &g);
     if (lane < k) {
       idx[t * k + lane] = i;
       gate[t * k + lane] = g;
@@ -294,7 +225,7 @@ __global__ __launch_bounds__(256) void k_route_block(const float* __restrict__ l
   for (int tl = wave; tl < nt; tl += 4) {
     int i;
     float g;
-    wave_topk(logits + (int64_t)(t0 + tl) * E, E, k, renorm != 0, lane, &i, &g);
+    wave_softmax_topk(logits + (int64_t)(t0 + tl) * E, E, k, renorm != 0, lane, &i, &g);
     if (lane < k) {
       idx[(int64_t)(t0 + tl) * k + lane] = i;
       gate[(int64_t)(t0 + tl) * k + lane] = g;

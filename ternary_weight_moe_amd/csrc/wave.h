@@ -1,0 +1,275 @@
+// Cross-lane reductions for wave64 on gfx950 without the LDS crossbar.
+//
+// Within a row of 16 lanes the DPP controls quad_perm[1,0,3,2] (pairs i^1),
+// quad_perm[2,3,0,1] (pairs i^2), row_half_mirror (i <-> 7-i) and row_mirror
+// (i <-> 15-i) each join two equal-sized, already-reduced groups, so four
+// steps reduce 16 lanes.  v_permlane16_swap and v_permlane32_swap exchange
+// whole rows (16 <-> 16 and 32 <-> 32 lanes) in one VALU op.  Every lane ends
+// with the same bits: each step combines the same two operands in every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace maple {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+struct OpSum {
+  __device__ static float f(float a, float b) { return a + b; }
+  __device__ static int i(int a, int b) { return a + b; }
+};
+struct OpMax {
+  __device__ static float f(float a, float b) { return fmaxf(a, b); }
+  __device__ static int i(int a, int b) { return max(a, b); }
+};
+struct OpMin {
+  __device__ static float f(float a, float b) { return fminf(a, b); }
+  __device__ static int i(int a, int b) { return min(a, b); }
+};
+
+// Reduce over aligned groups of N lanes (N a power of two, 1..64); every lane
+// of a group receives the group's result.
+template <int N, class Op>
+__device__ __forceinline__ float group_reduce(float v) {
+  if constexpr (N >= 2) v = Op::f(v, dpp_f<kDppXor1>(v));
+  if constexpr (N >= 4) v = Op::f(v, dpp_f<kDppXor2>(v));
+  if constexpr (N >= 8) v = Op::f(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = Op::f(v, dpp_f<kDppMirror>(v));
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
+
+template <int N, class Op>
+__device__ __forceinline__ int group_reduce_i(int v) {
+  if constexpr (N >= 2) v = Op::i(v, dpp_i<kDppXor1>(v));
+  if constexpr (N >= 4) v = Op::i(v, dpp_i<kDppXor2>(v));
+  if constexpr (N >= 8) v = Op::i(v, dpp_i<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = Op::i(v, dpp_i<kDppMirror>(v));
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    v = Op::i((int)r[0], (int)r[1]);
+  }
+  if constexpr (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    v = Op::i((int)r[0], (int)r[1]);
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) { return group_reduce<64, OpSum>(v); }
+__device__ __forceinline__ float wave_max_f(float v) { return group_reduce<64, OpMax>(v); }
+__device__ __forceinline__ int wave_sum_i(int v) { return group_reduce_i<64, OpSum>(v); }
+__device__ __forceinline__ int wave_min_i(int v) { return group_reduce_i<64, OpMin>(v); }
+
+// Softmax over E <= 256 logits and the k first experts in the order
+// (logit desc, index asc), on one wave.  Lane holds logits e = lane + 64 m;
+// NaN ranks as -inf so the k indices are always valid experts.  Lane j < k
+// returns the j-th selection and its gate (divided by the selected mass when
+// renorm).
+__device__ __forceinline__ void wave_softmax_topk(const float* __restrict__ lrow, int E, int k,
+                                                  bool renorm, int lane, int* my_idx,
+                                                  float* my_gate) {
+  float v[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    float l = (e < E) ? lrow[e] : -INFINITY;
+    if (l != l) l = -INFINITY;
+    v[m] = l;
+  }
+  const float mx = wave_max_f(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (lane + 64 * m < E) s += expf(v[m] - mx);
+  s = wave_sum_f(s);
+  unsigned taken = 0;
+  float gsum = 0.f;
+  int out_i = 0;
+  float out_g = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * m;
+      if (e < E && !(taken & (1u << m)) && (v[m] > bv || (v[m] == bv && e < bi))) {
+        bv = v[m];
+        bi = e;
+      }
+    }
+    const float best = wave_max_f(bi == 0x7fffffff ? -INFINITY : bv);
+    const int sel = wave_min_i((bi != 0x7fffffff && bv == best) ? bi : 0x7fffffff);
+    if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
+    const float g = expf(best - mx) / s;
+    gsum += g;
+    if (lane == j) {
+      out_i = sel;
+      out_g = g;
+    }
+  }
+  if (renorm) out_g /= gsum;
+  *my_idx = out_i;
+  *my_gate = out_g;
+}
+
+// Order-preserving int key of a float: signed comparison of keys equals the
+// float comparison for non-NaN values (-0 sorts just below +0).  NaN and -inf
+// share the key of -inf; kKeyTaken sorts below every float.
+constexpr int kKeyTaken = (int)0x80000000;
+__device__ __forceinline__ int float_key(float f) {
+  if (f != f) f = -INFINITY;
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : (b ^ 0x7fffffff);
+}
+__device__ __forceinline__ float key_float(int k) {
+  return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff));
+}
+
+// Max of an int over the whole wave, returned as a wave-uniform value: DPP
+// within each row of 16, then the four row results through readlane.
+__device__ __forceinline__ int wave_max_i_uniform(int v) {
+  v = max(v, dpp_i<kDppXor1>(v));
+  v = max(v, dpp_i<kDppXor2>(v));
+  v = max(v, dpp_i<kDppHalfMirror>(v));
+  v = max(v, dpp_i<kDppMirror>(v));
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Softmax over E <= 256 logits and the k (<= 64) experts first in the order
+// (logit desc, index asc), computed by one wave with wave-uniform results:
+// sel[j] and gate[j] (divided by the selected mass when renorm) for j < k are
+// written by lane 0 to the given (shared or global) arrays.  Each of the k
+// rounds takes the wave max of the remaining keys and, among the lanes that
+// hold it, the lowest expert index (ballot, lowest set bit, lowest m first).
+__device__ __forceinline__ void wave_topk_uniform(const float* __restrict__ lrow, int E, int k,
+                                                  bool renorm, int lane, int* sel, float* gate) {
+  int key[4];
+  float mxl = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    const float l = (e < E) ? lrow[e] : -INFINITY;
+    key[m] = (e < E) ? float_key(l) : kKeyTaken;
+    mxl = fmaxf(mxl, (e < E && l == l) ? l : -INFINITY);
+  }
+  const float mx = wave_max_f(mxl);
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    if (e < E) s += expf(key_float(key[m]) - mx);
+  }
+  s = wave_sum_f(s);
+  float gsum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int best = wave_max_i_uniform(max(max(key[0], key[1]), max(key[2], key[3])));
+    int e = 0;
+#pragma unroll
+    for (int m = 3; m >= 0; --m) {  // lowest m with a match wins: scan from the top down
+      const unsigned long long b = __ballot(key[m] == best);
+      if (b) e = 64 * m + (int)__builtin_ctzll(b);
+    }
+    if ((e & 63) == lane) key[e >> 6] = kKeyTaken;
+    const float g = expf(key_float(best) - mx) / s;
+    gsum += g;
+    if (lane == 0) {
+      sel[j] = e;
+      gate[j] = g;
+    }
+  }
+  if (renorm && lane == 0)
+    for (int j = 0; j < k; ++j) gate[j] /= gsum;
+}
+
+// Lower-latency variant for one wave: each lane first sorts its 4 keys
+// (descending; equal keys keep the lower expert first), so a round only takes
+// the wave max of one head key per lane, finds the holder (ballot; on a tie
+// across lanes, the lowest expert among the holders) and advances that lane's
+// head.  Lane 0 writes sel[j] and the selected logit val[j] to LDS as it goes;
+// the softmax normaliser is returned (wave-uniform) together with the max, so
+// gates can be formed after the rounds.  E <= 256, k <= 64.
+__device__ __forceinline__ void wave_topk_rounds(const float* __restrict__ lrow, int E, int k,
+                                                 int lane, int* s_sel, float* s_val,
+                                                 float* out_max, float* out_sum) {
+  int key[4], em[4];
+  float mxl = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    const float l = (e < E) ? lrow[e] : -INFINITY;
+    key[m] = (e < E) ? float_key(l) : kKeyTaken;
+    em[m] = e;
+    mxl = fmaxf(mxl, (e < E && l == l) ? l : -INFINITY);
+  }
+  // the softmax normaliser does not depend on the rounds: issue it first
+  const float mx = wave_max_f(mxl);
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (em[m] < E) s += expf(key_float(key[m]) - mx);
+  s = wave_sum_f(s);
+  // sort (key desc, e asc) with a 5-comparator network
+  auto cs = [&](int a, int b) {
+    const bool sw = key[b] > key[a] || (key[b] == key[a] && em[b] < em[a]);
+    const int ka = key[a], ea = em[a];
+    key[a] = sw ? key[b] : key[a];
+    em[a] = sw ? em[b] : em[a];
+    key[b] = sw ? ka : key[b];
+    em[b] = sw ? ea : em[b];
+  };
+  cs(0, 1);
+  cs(2, 3);
+  cs(0, 2);
+  cs(1, 3);
+  cs(1, 2);
+  int hk = key[0], he = em[0];
+  int head = 0;
+  for (int j = 0; j < k; ++j) {
+    const int best = wave_max_i_uniform(hk);
+    const unsigned long long b = __ballot(hk == best);
+    int e;
+    if (__popcll(b) == 1) {
+      e = __builtin_amdgcn_readlane(he, (int)__builtin_ctzll(b));
+    } else {  // equal logits in several lanes: the lowest expert index wins
+      e = -wave_max_i_uniform(hk == best ? -he : (int)0x80000001);
+    }
+    if (he == e) {
+      ++head;
+      hk = head == 1 ? key[1] : head == 2 ? key[2] : head == 3 ? key[3] : kKeyTaken;
+      he = head == 1 ? em[1] : head == 2 ? em[2] : head == 3 ? em[3] : 0x7fffffff;
+    }
+    if (lane == 0) {
+      s_sel[j] = e;
+      s_val[j] = key_float(best);
+    }
+  }
+  *out_max = mx;
+  *out_sum = s;
+}
+
+}  // namespace maple
