@@ -207,7 +207,8 @@ def bench_decode(args, torch, N, S):
     per_kernel = {kn: dict(launches=n, avg_us=1000 * avg,
                            bytes=decode_bytes(kn, H, E, k, I))
                   for kn, (n, avg) in prof.items()}
-    dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    known = [kn for kn in prof if decode_bytes(kn, H, E, k, I) is not None]
+    dom = max(known, key=lambda kn: prof[kn][0] * prof[kn][1])
     dom_bytes = decode_bytes(dom, H, E, k, I)
     dom_avg_s = prof[dom][1] * 1e-3
     achieved = dom_bytes / dom_avg_s / 1e9

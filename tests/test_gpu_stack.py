@@ -66,6 +66,17 @@ def test_decode_stack_24_layers(stack3):
     check_stack(w, layers, x, ref, what="decode stack")
 
 
+def test_decode_stack_one_token_chain(stack3):
+    """One token per call: each layer's router rides on the previous layer's
+    down kernel (partial dots), checked layer by layer."""
+    w, layers = stack3
+    x, x64, ref, regen = stack_tokens_with_gap(w, layers, 3, token0=20)
+    for t in range(3):
+        sub = {k: (v[:, t:t + 1] if v is not None and v.ndim == 3 else v) for k, v in ref.items()}
+        sub["x"] = ref["x"][t:t + 1]
+        check_stack(w, layers, x[t:t + 1], sub, what=f"one-token chain t={t}")
+
+
 def test_decode_stack_graph_replays(stack3):
     """Replays of the captured step, with eager work between them, each match
     the eager stack call bit for bit and the oracle within tolerance."""
