@@ -158,6 +158,19 @@ def profile_kernels(N, fn, steps):
     return {k: (n, ms / n) for k, (n, ms) in summ.items()}
 
 
+def copy_probe(torch, mib):
+    """A plain device-to-device copy of known size, launched a few times, so that
+    hardware counter runs over this script can scale FETCH_SIZE / WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 x {mib} MiB device-to-device copies")
+    del src, dst
+
+
 def timed(torch, fn, steps, warmup):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -284,6 +297,8 @@ def main():
                     choices=["decode_stack", "prefill_4096", "prefill_16384"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -303,6 +318,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     N.load()  # fails loudly if the HIP library is missing
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
     res, w = (bench_decode if decode else bench_prefill)(args, torch, N, S)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_decode if decode else cpu_baseline_prefill)(

@@ -61,6 +61,8 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
   ws->hs = (float*)take(sizeof(float) * 2 * Tk);
   ws->y = (float*)take(sizeof(float) * Tk * d.H);
+  ws->xb = (uint16_t*)take(sizeof(uint16_t) * 2 * T * d.H);
+  ws->wb = (uint16_t*)take(sizeof(uint16_t) * 2 * d.E * d.H);
   ws->bytes = off;
   return off;
 }
@@ -90,17 +92,14 @@ hipEvent_t prof_event() {
 }
 }  // namespace
 
-ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
-  if (!g_prof.on) return;
+bool prof_slot(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof.on) return false;
   hipEvent_t a = prof_event(), b = prof_event();
-  if (!a || !b) return;
-  if (hipEventRecord(a, s) != hipSuccess) return;
+  if (!a || !b) return false;
   g_prof.recs.push_back({name, a, b});
-  slot = (int)g_prof.recs.size() - 1;
-}
-
-ProfScope::~ProfScope() {
-  if (slot >= 0) (void)hipEventRecord(g_prof.recs[slot].stop, stream);
+  *start = a;
+  *stop = b;
+  return true;
 }
 
 }  // namespace maple
@@ -202,11 +201,12 @@ int device_ready() {
 int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
               const float* bias, const uint8_t* packed, const float* alpha, float* out,
               const float* resid, float* delta, const Workspace& ws, const maple_moe_debug* dbg,
-              hipStream_t s) {
+              const float* next_wr, hipStream_t s) {
   const bool gemv = use_gemv(d, T);
   hipError_t e = hipSuccess;
   if (gemv && T == 1) {  // one token: router, top-k + gate/up, down + combine
-    e = maple::launch_decode1(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta, s);
+    e = maple::launch_decode1(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta,
+                              next_wr, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   } else {
     if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and large-T router use them
@@ -214,7 +214,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }
     e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 2 * T,
-                             ws.logits, s);
+                             ws.logits, ws.xb, ws.wb, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     e = maple::launch_route(d, T, ws.logits, ws, s);
     if (e != hipSuccess) return hip_fail(e, "routing launch");
@@ -414,7 +414,7 @@ int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const 
   if ((rc = device_ready())) return rc;
   maple::carve(d, n_tokens, static_cast<char*>(workspace), &ws);
   return run_layer(d, n_tokens, x, (d.flags & MAPLE_X_BF16) != 0, router_w, router_bias,
-                   packed_w, alpha, out, nullptr, nullptr, ws, dbg, (hipStream_t)stream);
+                   packed_w, alpha, out, nullptr, nullptr, ws, dbg, nullptr, (hipStream_t)stream);
 }
 
 static int enqueue_stack(const Dims& d, int32_t n_layers, int64_t T, float* x,
@@ -425,8 +425,10 @@ static int enqueue_stack(const Dims& d, int32_t n_layers, int64_t T, float* x,
   maple::carve(d, T, static_cast<char*>(workspace), &ws);
   for (int l = 0; l < n_layers; ++l) {
     const maple_moe_debug ld = layer_dbg(dbg, l, T, d);
+    const float* next_wr = l + 1 < n_layers ? router_w[l + 1] : nullptr;
     const int rc = run_layer(d, T, x, false, router_w[l], router_bias ? router_bias[l] : nullptr,
-                             packed_w[l], alpha[l], x, x, ld.delta, ws, dbg ? &ld : nullptr, s);
+                             packed_w[l], alpha[l], x, x, ld.delta, ws, dbg ? &ld : nullptr,
+                             next_wr, s);
     if (rc) return rc;
   }
   return MAPLE_OK;

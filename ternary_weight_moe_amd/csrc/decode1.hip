@@ -396,7 +396,7 @@ __global__ __launch_bounds__(512) void k_d1m_gateup(
     int I, const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     float* __restrict__ h, int32_t* __restrict__ idx, float* __restrict__ gate,
     int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_pos) {
+    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_pos, uint32_t* sink) {
   constexpr int NW = 8;
   constexpr int KW = H / NW;     // codes per wave
   constexpr int NSS = KW / 256;  // super-steps per wave
@@ -452,18 +452,26 @@ __global__ __launch_bounds__(512) void k_d1m_gateup(
   }
   const float ag = alpha[(int64_t)e * (2 * I + H) + row];
   const float au = alpha[(int64_t)e * (2 * I + H) + I + row];
-  // Warm the last-level cache with the down-projection rows of this expert
-  // that the next kernel reads: block x of I/16 takes H/(I/16) rows of
-  // W_down[e].  The loads feed a never-taken store so they are kept.
+  // Warm the L2 that the down kernel will read W_down[e] through.  Work-groups
+  // go to the 8 XCDs round-robin by linear id, so down block b (8 rows) runs
+  // on XCD b % 8 and this block on XCD blockIdx.x % 8 (I/16 is a multiple of
+  // 8).  The blocks of this XCD for selection j split the rows of the down
+  // blocks of the same XCD: block r = blockIdx.x / 8 takes down blocks
+  // b = xc + 8m, m in [r*MB, (r+1)*MB).  The words feed a store under `sink`,
+  // which the host always passes as null, so the loads are kept.
   uint4 pf = make_uint4(0u, 0u, 0u, 0u);
   {
     const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * row_bytes;
-    const int64_t span = (int64_t)(H / (I / 16)) * (I / 4);  // bytes
-    const int64_t base = (int64_t)blockIdx.x * span;
-    for (int64_t o = (int64_t)tid * 16; o < span; o += 512 * 16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(Wd + base + o);
+    const int xc = blockIdx.x & 7, r = blockIdx.x >> 3;
+    const int MB = 2 * H / I;  // down blocks per gate/up block
+    const int upb = I / 8;     // 16-byte units per down block (8 rows of I/4 bytes)
+    for (int u = tid; u < MB * upb; u += 512) {
+      const int b = xc + 8 * (r * MB + u / upb);
+      const uint4 v = *reinterpret_cast<const uint4*>(Wd + (int64_t)b * 2 * I + (u % upb) * 16);
       pf.x ^= v.x;
-      pf.y ^= v.w;
+      pf.y ^= v.y;
+      pf.z ^= v.z;
+      pf.w ^= v.w;
     }
   }
   if (blockIdx.x == 0 && blockIdx.y == 0) {  // block-uniform branch
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(512) void k_d1m_gateup(
     const float gv = ag * sr * v[0], uv = au * sr * v[1];
     h[(int64_t)j * I + row] = gv / (1.f + expf(-gv)) * uv;
   }
-  if (pf.x == 0x9e3779b9u && pf.y == 0x7f4a7c15u && pf.z == 1u) h[0] = 0.f;  // never true
+  if (sink) reinterpret_cast<uint4*>(sink)[tid] = pf;
 }
 
 // blockIdx.x: block of 8 output rows (lanes c16 >= 8 carry zero weights).
@@ -546,7 +554,9 @@ __global__ __launch_bounds__(512) void k_d1m_down(const float* __restrict__ h, i
                                                   const float* __restrict__ alpha,
                                                   const int32_t* __restrict__ idx,
                                                   const float* __restrict__ gate, float* out,
-                                                  const float* resid, float* __restrict__ delta) {
+                                                  const float* resid, float* __restrict__ delta,
+                                                  const float* __restrict__ next_wr, int E,
+                                                  uint32_t* sink) {
   constexpr int PER = I / 64;   // h values per lane
   constexpr int NSS = I / 256;  // super-steps
   __shared__ __align__(16) int8_t sH[8][4][I];
@@ -577,6 +587,27 @@ __global__ __launch_bounds__(512) void k_d1m_down(const float* __restrict__ h, i
     hv[i + 2] = f.z;
     hv[i + 3] = f.w;
     am = fmaxf(am, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+  }
+  // Warm the L2 with the next layer's router rows: router block e runs on XCD
+  // e % 8 and reads row e (4H bytes); this block (XCD b % 8, b = blockIdx.x)
+  // takes its share, 32E bytes, of the rows of its own XCD.  The words feed a
+  // store under `sink`, which the host always passes as null.
+  uint4 pf = make_uint4(0u, 0u, 0u, 0u);
+  if (next_wr) {
+    const int xc = blockIdx.x & 7, m = blockIdx.x >> 3;
+    const int64_t row_b = 4 * (int64_t)H;
+    for (int u = tid; u < 2 * E; u += 512) {
+      const int64_t q = (int64_t)m * 32 * E + 16 * (int64_t)u;
+      const int er = xc + 8 * (int)(q / row_b);
+      if (er < E) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const uint8_t*>(next_wr) + (int64_t)er * row_b + q % row_b);
+        pf.x ^= v.x;
+        pf.y ^= v.y;
+        pf.z ^= v.z;
+        pf.w ^= v.w;
+      }
+    }
   }
   am = wave_max_f(am);
   const float scale = am > 0.f ? am / kQMax3 : 1.f;
@@ -617,6 +648,7 @@ __global__ __launch_bounds__(512) void k_d1m_down(const float* __restrict__ h, i
     if (delta) delta[o] = acc;
     out[o] = resid ? resid[o] + acc : acc;
   }
+  if (sink) reinterpret_cast<uint4*>(sink)[tid] = pf;
 }
 
 template <int LPR_H, bool BF16>
@@ -625,10 +657,9 @@ hipError_t gateup1(const Dims& d, const void* x, const uint8_t* packed, const fl
   constexpr int ROWS_WG = 4 * 2 * (64 / LPR_H);
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
-  MAPLE_PROF("d1_gateup", s);
-  k_d1_gateup<LPR_H, BF16><<<dim3(d.I / ROWS_WG, d.k), 256, 0, s>>>(
-      x, ws.logits, d.E, d.k, norm, renorm, d.I, packed, alpha, ws.h, ws.idx, ws.gate,
-      ws.offsets, ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos);
+  launch("d1_gateup", k_d1_gateup<LPR_H, BF16>, dim3(d.I / ROWS_WG, d.k), 256, 0, s, x, ws.logits,
+         d.E, d.k, norm, renorm, d.I, packed, alpha, ws.h, ws.idx, ws.gate, ws.offsets, ws.active,
+         ws.n_active, ws.sorted_tok, ws.slot_pos);
   return hipGetLastError();
 }
 
@@ -636,8 +667,7 @@ template <int H, bool BF16>
 hipError_t router1(const Dims& d, const void* x, const float* Wr, const float* bias,
                    float* logits, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
-  MAPLE_PROF("d1_router", s);
-  k_d1_router<H, BF16><<<d.E, 64, 0, s>>>(x, Wr, bias, norm, logits);
+  launch("d1_router", k_d1_router<H, BF16>, d.E, 64, 0, s, x, Wr, bias, norm, logits);
   return hipGetLastError();
 }
 
@@ -645,9 +675,8 @@ template <int LPR_I>
 hipError_t down1(const Dims& d, const uint8_t* packed, const float* alpha, const Workspace& ws,
                  float* out, const float* resid, float* delta, hipStream_t s) {
   constexpr int RPI = 64 / LPR_I;
-  MAPLE_PROF("d1_down", s);
-  k_d1_down<LPR_I><<<d.H / RPI, 256, 0, s>>>(ws.h, d.H, d.k, packed, alpha, ws.idx, ws.gate,
-                                             out, resid, delta);
+  launch("d1_down", k_d1_down<LPR_I>, d.H / RPI, 256, 0, s, ws.h, d.H, d.k, packed, alpha, ws.idx,
+         ws.gate, out, resid, delta);
   return hipGetLastError();
 }
 
@@ -683,9 +712,8 @@ template <int H, bool BF16>
 hipError_t router1q(const Dims& d, const void* x, const float* Wr, const float* bias,
                     const Workspace& ws, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
-  MAPLE_PROF("d1q_router", s);
-  k_d1q_router<H, BF16><<<d.E, 64, 0, s>>>(x, Wr, bias, norm, d.E, ws.logits, ws.xq, ws.part,
-                                           ws.xs);
+  launch("d1q_router", k_d1q_router<H, BF16>, d.E, 64, 0, s, x, Wr, bias, norm, d.E, ws.logits,
+         ws.xq, ws.part, ws.xs);
   return hipGetLastError();
 }
 
@@ -693,33 +721,32 @@ template <int H>
 hipError_t gateup1m(const Dims& d, const uint8_t* packed, const float* alpha,
                     const Workspace& ws, hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
-  MAPLE_PROF("d1m_gateup", s);
-  k_d1m_gateup<H><<<dim3(d.I / 16, d.k), 512, 0, s>>>(
-      ws.xq, ws.part, ws.xs, ws.logits, d.E, d.k, renorm, d.I, packed, alpha, ws.h, ws.idx,
-      ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos);
+  launch("d1m_gateup", k_d1m_gateup<H>, dim3(d.I / 16, d.k), 512, 0, s, ws.xq, ws.part, ws.xs,
+         ws.logits, d.E, d.k, renorm, d.I, packed, alpha, ws.h, ws.idx, ws.gate, ws.offsets,
+         ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos, (uint32_t*)nullptr);
   return hipGetLastError();
 }
 
 template <int I>
 hipError_t down1m(const Dims& d, const uint8_t* packed, const float* alpha, const Workspace& ws,
-                  float* out, const float* resid, float* delta, hipStream_t s) {
-  MAPLE_PROF("d1m_down", s);
-  k_d1m_down<I><<<d.H / 8, 512, 0, s>>>(ws.h, d.H, d.k, packed, alpha, ws.idx, ws.gate, out,
-                                        resid, delta);
+                  float* out, const float* resid, float* delta, const float* next_wr,
+                  hipStream_t s) {
+  launch("d1m_down", k_d1m_down<I>, d.H / 8, 512, 0, s, ws.h, d.H, d.k, packed, alpha, ws.idx,
+         ws.gate, out, resid, delta, next_wr, d.E, (uint32_t*)nullptr);
   return hipGetLastError();
 }
 
 template <int H>
 hipError_t decode1m(const Dims& d, const void* x, bool bf16, const float* Wr, const float* bias,
                     const uint8_t* packed, const float* alpha, const Workspace& ws, float* out,
-                    const float* resid, float* delta, hipStream_t s) {
+                    const float* resid, float* delta, const float* next_wr, hipStream_t s) {
   hipError_t e = bf16 ? router1q<H, true>(d, x, Wr, bias, ws, s)
                       : router1q<H, false>(d, x, Wr, bias, ws, s);
   if (e != hipSuccess) return e;
   e = gateup1m<H>(d, packed, alpha, ws, s);
   if (e != hipSuccess) return e;
-  return d.I == 256 ? down1m<256>(d, packed, alpha, ws, out, resid, delta, s)
-                    : down1m<512>(d, packed, alpha, ws, out, resid, delta, s);
+  return d.I == 256 ? down1m<256>(d, packed, alpha, ws, out, resid, delta, next_wr, s)
+                    : down1m<512>(d, packed, alpha, ws, out, resid, delta, next_wr, s);
 }
 
 bool decode1_matrix_cores(const Dims& d) {
@@ -730,11 +757,12 @@ bool decode1_matrix_cores(const Dims& d) {
 hipError_t launch_decode1(const Dims& d, const void* x, bool x_bf16, const float* Wr,
                           const float* bias, const uint8_t* packed, const float* alpha,
                           const Workspace& ws, float* out, const float* resid, float* delta,
-                          hipStream_t s) {
+                          const float* next_wr, hipStream_t s) {
   if (decode1_matrix_cores(d))
-    return d.H == 2048
-               ? decode1m<2048>(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta, s)
-               : decode1m<4096>(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta, s);
+    return d.H == 2048 ? decode1m<2048>(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid,
+                                        delta, next_wr, s)
+                       : decode1m<4096>(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid,
+                                        delta, next_wr, s);
   hipError_t e = x_bf16 ? d1_router_h<true>(d, x, Wr, bias, ws.logits, s)
                         : d1_router_h<false>(d, x, Wr, bias, ws.logits, s);
   if (e != hipSuccess) return e;

@@ -196,13 +196,12 @@ hipError_t gateup(const Dims& d, int64_t T, const void* x, bool bf16, const uint
   constexpr int ROWS_WG = 4 * 2 * (64 / LPR);
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   const dim3 grid(d.I / ROWS_WG, (unsigned)std::min<int64_t>(d.E, T * d.k));
-  MAPLE_PROF("gateup_gemv", s);
   if (bf16)
-    k_gateup_gemv<LPR, NT, true><<<grid, 256, 0, s>>>(x, norm, d.H, d.I, packed, alpha, ws.offsets,
-                                                      ws.sorted_tok, ws.active, ws.n_active, ws.h);
+    launch("gateup_gemv", k_gateup_gemv<LPR, NT, true>, grid, 256, 0, s, x, norm, d.H, d.I, packed,
+           alpha, ws.offsets, ws.sorted_tok, ws.active, ws.n_active, ws.h);
   else
-    k_gateup_gemv<LPR, NT, false><<<grid, 256, 0, s>>>(x, norm, d.H, d.I, packed, alpha, ws.offsets,
-                                                       ws.sorted_tok, ws.active, ws.n_active, ws.h);
+    launch("gateup_gemv", k_gateup_gemv<LPR, NT, false>, grid, 256, 0, s, x, norm, d.H, d.I, packed,
+           alpha, ws.offsets, ws.sorted_tok, ws.active, ws.n_active, ws.h);
   return hipGetLastError();
 }
 
@@ -225,10 +224,9 @@ hipError_t down(const Dims& d, int64_t T, const uint8_t* packed, const float* al
                 hipStream_t s) {
   constexpr int RPI = 64 / LPR;
   const size_t lds = (size_t)T * d.k * RPI * sizeof(float);
-  MAPLE_PROF("down_combine_gemv", s);
-  k_down_combine<LPR><<<d.H / RPI, 256, lds, s>>>(ws.h, d.H, d.I, packed, alpha, ws.gate,
-                                                  ws.offsets, ws.slot_pos, ws.active,
-                                                  ws.n_active, (int)T, d.k, out, resid, delta);
+  launch("down_combine_gemv", k_down_combine<LPR>, d.H / RPI, 256, lds, s, ws.h, d.H, d.I, packed,
+         alpha, ws.gate, ws.offsets, ws.slot_pos, ws.active, ws.n_active, (int)T, d.k, out, resid,
+         delta);
   return hipGetLastError();
 }
 

@@ -36,6 +36,7 @@ namespace maple {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int TM = kTileM;        // slots per M tile
 constexpr float kQMax = 16256.f;  // 127 * 128
@@ -52,6 +53,19 @@ __device__ __forceinline__ v4i unpack_word(uint32_t w) {
 
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int s) {
   return s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+}
+
+// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
+// own L2.  Tile t of the expert-ordered tile list is given to the block with
+// linear id b where b % 8 = t / per_xcd and b / 8 = t % per_xcd: every XCD
+// takes one contiguous run of tiles, so the tiles of one expert (which read the
+// same weights) run side by side under one L2.  Returns -1 for spare blocks.
+__device__ __forceinline__ int xcd_tile(int b, int n_tiles) {
+  const int per_xcd = (n_tiles + 7) >> 3;
+  const int local = b >> 3;
+  if (local >= per_xcd) return -1;
+  const int t = (b & 7) * per_xcd + local;
+  return t < n_tiles ? t : -1;
 }
 
 __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
@@ -122,191 +136,242 @@ __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int
 
 // ---- gate/up + SwiGLU + re-coding of h --------------------------------------------
 
-// One block: one M tile (TM slots of one expert) x all I columns of h, i.e.
-// 2I weight rows; wave w owns h columns [64w, 64w+64): gate N-subtiles b = 0..3
-// and up N-subtiles b = 4..7 with identical (row, column) positions per lane,
-// so silu(g)*u is formed in registers.  K advances in super-steps of 128 codes
-// (SS = 2 MFMA steps); A (x limbs) is double-buffered in LDS, B (the weights)
-// in registers one super-step ahead.
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_gateup_mfma(
-    const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H, int I,
+// v_mfma_i32_32x32x32_i8: A lane l supplies row l % 32 and 16 bytes of K
+// group l / 32; B lane l column l % 32, same K group; accumulator register j
+// of lane l holds row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.  One wave
+// per SIMD issues these at nearly the full int8 rate (the 16x16x64 form needs
+// two waves per SIMD for that).
+//
+// K order.  A stage covers 256 codes of a row, 16 words of 16 codes.  Lane
+// group kg = lane / 32 holds words 4kg..4kg+3 (steps 0-3) and 8+4kg..8+4kg+3
+// (steps 4-7), so MFMA step s uses word 8 (s / 4) + 4 kg + s % 4; the x limbs
+// of the same step come from the same 16 codes.
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (about 1e-7
+// relative error); z -> -inf gives -0, z -> +inf gives z.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * z));
+}
+
+__device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// One block (4 waves, one per SIMD): one M tile (TM = 32 slots of one expert)
+// x all I columns of h, i.e. 2I weight rows.  Wave w owns h columns
+// [w I/4, (w+1) I/4): gate N-subtiles b < NBG and up N-subtiles b >= NBG (32
+// columns each) with identical (row, column) positions per lane, so
+// silu(g)*u is formed in registers.  The accumulators (2 limbs x 2 NBG
+// N-subtiles x 16) fill the accumulation registers.
+//
+// Weights go straight from global memory into B operands: per N-subtile and
+// stage each lane holds two 16-byte pieces of one weight row (one load
+// instruction covers 32 contiguous bytes of 32 rows), refilled with the next
+// stage right after their last use, a full stage ahead.  The x limbs
+// (gathered through sorted_token) pass through registers into a
+// double-buffered LDS tile, two stages ahead; rows are padded to 272 bytes.
+template <int I>
+__global__ __launch_bounds__(256) void k_gateup_mfma(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     int8_t* __restrict__ hq, float* __restrict__ hs, int64_t Tk) {
-  constexpr int NTH = NW * 64;
-  constexpr int SS = 2;                     // MFMA steps per super-step
-  constexpr int KSS = 64 * SS;              // codes per super-step
-  constexpr int ROWB = KSS + 16;            // padded LDS row of one limb, one super-step
-  constexpr int SEGK = KSS / 16;            // 16-byte segments per limb row
-  constexpr int SEGS = 2 * TM * SEGK;       // segments of A per super-step
-  constexpr int SEG_T = SEGS / NTH;         // per thread (NW in {2,4,8})
-  constexpr int HBYTES = 2 * TM * 512;      // h-limb staging at the largest I
-  constexpr int ABYTES = 2 * 2 * TM * ROWB;
-  __shared__ __align__(16) int8_t smem[ABYTES > HBYTES ? ABYTES : HBYTES];
+  constexpr int NW = 4;
+  constexpr int NBG = I / 128;          // gate N-subtiles per wave (and as many up)
+  constexpr int NB = 2 * NBG;
+  constexpr int KS = 256;               // codes per stage (8 MFMA steps)
+  constexpr int ROWB = KS + 16;         // padded LDS row: one limb of one slot
+  constexpr int ABUF = 2 * TM * ROWB;   // one stage of x limbs
+  constexpr int HBYTES = 2 * TM * I;    // h-limb staging in the epilogue
+  constexpr int SMEM = 2 * ABUF > HBYTES ? 2 * ABUF : HBYTES;
+  static_assert(TM == 32 && NB % 2 == 0, "tile shape");
+  __shared__ __align__(16) int8_t smem[SMEM];
   __shared__ float s_sx[TM];
   __shared__ int s_xsum[TM], s_tok[TM];
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
-  auto sA = [&](int buf, int limb, int r) -> int8_t* {
-    return smem + ((buf * 2 + limb) * TM + r) * ROWB;
-  };
-  const int tile = blockIdx.x;
-  if (tile >= *n_tiles) return;
+  const int tile = xcd_tile(blockIdx.x, *n_tiles);
+  if (tile < 0) return;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int p0 = offsets[e] + m0;
   const int np = min(TM, offsets[e + 1] - p0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int kg = lane >> 5, r32 = lane & 31;
   if (tid < TM) {
     const int tok = tid < np ? sorted_tok[p0 + tid] : -1;
     s_tok[tid] = tok;
     s_sx[tid] = tok >= 0 ? xs[tok] * xs[2 * T + tok] : 0.f;
     s_xsum[tid] = tok >= 0 ? reinterpret_cast<const int*>(xs)[T + tok] : 0;
   }
-  __syncthreads();
-
-  // lane's weight bytes: row (64*wave + 16*(b&3) + c16) of gate (b < 4) or up,
-  // 8 bytes per super-step at offset 8*g
   const int rowb = H / 4;
-  const uint8_t* wbase = packed + (int64_t)e * 3 * H * I / 4 +
-                         (int64_t)(64 * wave + c16) * rowb + 8 * g;
-  const int64_t up_off = (int64_t)I * rowb;
-  auto load_b = [&](int ks, uint2 (&bq)[8]) {
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      bq[b] = *reinterpret_cast<const uint2*>(wbase + (b < 4 ? 0 : up_off) +
-                                              (int64_t)(16 * (b & 3)) * rowb + ks * (KSS / 4));
+  const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
+  const int col0 = wave * (I / 4) + r32;
+  const uint8_t* brow = We + (int64_t)col0 * rowb + 16 * kg;
+  auto bsrc = [&](int b, int st) -> const uint8_t* {
+    return brow + (b < NBG ? 0 : (int64_t)I * rowb) + (int64_t)(32 * (b % NBG)) * rowb + st * 64;
   };
-
-  v4i acc_hi[2][8], acc_lo[2][8];
+  const float* al = alpha + (int64_t)e * (2 * I + H);
+  float ag[NBG], au[NBG];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) acc_hi[a][b] = acc_lo[a][b] = v4i{0, 0, 0, 0};
-
-  uint4 stage[SEG_T];
-  auto fetch_A = [&](int ks) {
-#pragma unroll
-    for (int j = 0; j < SEG_T; ++j) {
-      const int c = tid + j * NTH;
-      const int limb = c / (TM * SEGK), r = (c / SEGK) % TM, seg = c % SEGK;
-      const int tok = s_tok[r];
-      stage[j] = tok >= 0 ? *reinterpret_cast<const uint4*>(xq + (int64_t)tok * 2 * H +
-                                                             (int64_t)limb * H + ks * KSS + seg * 16)
-                          : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_A = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < SEG_T; ++j) {
-      const int c = tid + j * NTH;
-      const int limb = c / (TM * SEGK), r = (c / SEGK) % TM, seg = c % SEGK;
-      *reinterpret_cast<uint4*>(sA(buf, limb, r) + seg * 16) = stage[j];
-    }
-  };
-
-  const int nks = H / KSS;
-  uint2 bcur[8], bnext[8];
-  fetch_A(0);
-  load_b(0, bcur);
-  store_A(0);
+  for (int b = 0; b < NBG; ++b) {
+    ag[b] = al[col0 + 32 * b];
+    au[b] = al[I + col0 + 32 * b];
+  }
   __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nks;
-    if (more) {
-      fetch_A(ks + 1);
-      load_b(ks + 1, bnext);
-    }
+
+  // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
+  // 16-byte segment u % 16.  Rows past np read slot 0's token (discarded).
+  const int8_t* asrc[4];
+  int adst[4];
 #pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      v4i ahi[2], alo[2];
+  for (int r = 0; r < 4; ++r) {
+    const int u = r * 256 + tid;
+    const int limb = u >> 9, slot = (u >> 4) & 31, seg = u & 15;
+    const int tok = s_tok[slot] >= 0 ? s_tok[slot] : s_tok[0];
+    asrc[r] = xq + (int64_t)tok * 2 * H + (int64_t)limb * H + 16 * seg;
+    adst[r] = (limb * TM + slot) * ROWB + 16 * seg;
+  }
+  uint4 as0, as1, as2, as3;  // one stage of x limbs in flight (named: kept in registers)
+  auto fetch_a = [&](int st) {
+    as0 = *reinterpret_cast<const uint4*>(asrc[0] + st * KS);
+    as1 = *reinterpret_cast<const uint4*>(asrc[1] + st * KS);
+    as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
+    as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
+  };
+  auto store_a = [&](int buf) {
+    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[0]) = as0;
+    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[1]) = as1;
+    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[2]) = as2;
+    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[3]) = as3;
+  };
+
+  v16i acc[2][NB];  // [limb][N-subtile]
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        ahi[a] = *reinterpret_cast<const v4i*>(sA(buf, 0, 16 * a + c16) + 16 * (SS * g + s));
-        alo[a] = *reinterpret_cast<const v4i*>(sA(buf, 1, 16 * a + c16) + 16 * (SS * g + s));
-      }
+  for (int l = 0; l < 2; ++l)
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const v4i bf = unpack_word(s == 0 ? bcur[b].x : bcur[b].y);
+    for (int b = 0; b < NB; ++b) acc[l][b] = v16i{};
+
+  const int nst = H / KS;
+  uint4 bq[2][NB];  // [half][N-subtile]: words of steps 0-3 / 4-7
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          acc_hi[a][b] = mfma(ahi[a], bf, acc_hi[a][b]);
-          acc_lo[a][b] = mfma(alo[a], bf, acc_lo[a][b]);
+  for (int b = 0; b < NB; ++b) {
+    bq[0][b] = *reinterpret_cast<const uint4*>(bsrc(b, 0));
+    bq[1][b] = *reinterpret_cast<const uint4*>(bsrc(b, 0) + 32);
+  }
+  fetch_a(0);
+  store_a(0);
+  fetch_a(min(1, nst - 1));
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int8_t* sa = smem + (st & 1) * ABUF + r32 * ROWB + 64 * kg;
+    // loads are issued unconditionally (the last stage reloads itself) so the
+    // count of loads in flight is the same at every use and the waits stay
+    // partial
+    const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v4i af[4][2];  // [step in half][limb]
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int l = 0; l < 2; ++l)
+          af[s2][l] = *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 128 * half + 16 * s2);
+      // N-subtiles in pairs: four independent accumulators between two
+      // updates of one.  The B operands of the next step are unpacked (7 VALU
+      // per word) while the MFMAs of this step run; the group barriers ask
+      // the scheduler for that interleave (an MFMA, then 3-4 VALU), and a
+      // scheduling barrier per pair bounds the registers it may hoist.
+      v4i u0 = unpack_word(word_of(bq[half][0], 0)), u1 = unpack_word(word_of(bq[half][1], 0));
+#pragma unroll
+      for (int b = 0; b < NB; b += 2) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const v4i b0 = u0, b1 = u1;
+          if (s2 < 3) {
+            u0 = unpack_word(word_of(bq[half][b], s2 + 1));
+            u1 = unpack_word(word_of(bq[half][b + 1], s2 + 1));
+          } else if (b + 2 < NB) {
+            u0 = unpack_word(word_of(bq[half][b + 2], 0));
+            u1 = unpack_word(word_of(bq[half][b + 3], 0));
+          }
+          acc[0][b] = mfma32(af[s2][0], b0, acc[0][b]);
+          acc[1][b] = mfma32(af[s2][1], b0, acc[1][b]);
+          acc[0][b + 1] = mfma32(af[s2][0], b1, acc[0][b + 1]);
+          acc[1][b + 1] = mfma32(af[s2][1], b1, acc[1][b + 1]);
         }
+        bq[half][b] = *reinterpret_cast<const uint4*>(bsrc(b, st1) + 32 * half);
+        bq[half][b + 1] = *reinterpret_cast<const uint4*>(bsrc(b + 1, st1) + 32 * half);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) {
-      store_A(buf ^ 1);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) bcur[b] = bnext[b];
-    }
+    store_a((st + 1) & 1);  // stage st1; its buffer was last read in stage st - 1
+    fetch_a(st2);
     __syncthreads();
   }
 
-  // Epilogue.  Lane holds rows m = 16a + 4g + i, columns 64*wave + 16b + c16.
-  const float* al = alpha + (int64_t)e * (2 * I + H);
-  float hv[2][4][4];
-  float rmax[2][4];
+  // Epilogue.  Lane holds rows m_j = 8 (j / 4) + 4 kg + j % 4 (j < 16) and
+  // columns col0 + 32 b.
+  float hv[NBG][16];
+  float rmax[16];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int j = 0; j < 16; ++j) {
+    const int m = 8 * (j >> 2) + 4 * kg + (j & 3);
+    const float sx = s_sx[m];
+    const int xsum = s_xsum[m];
+    float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * a + 4 * g + i;
-      const float sx = s_sx[m];
-      const int xsum = s_xsum[m];
-      float mx = 0.f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int col = 64 * wave + 16 * b + c16;
-        const float gv = (float)(128 * acc_hi[a][b][i] + acc_lo[a][b][i] - xsum) * sx * al[col];
-        const float uv =
-            (float)(128 * acc_hi[a][b + 4][i] + acc_lo[a][b + 4][i] - xsum) * sx * al[I + col];
-        const float h = gv / (1.f + expf(-gv)) * uv;
-        hv[a][b][i] = h;
-        mx = fmaxf(mx, fabsf(h));
-      }
-      rmax[a][i] = group_reduce<16, OpMax>(mx);
+    for (int b = 0; b < NBG; ++b) {
+      const float gv = (float)(128 * acc[0][b][j] + acc[1][b][j] - xsum) * (sx * ag[b]);
+      const float uv = (float)(128 * acc[0][b + NBG][j] + acc[1][b + NBG][j] - xsum) * (sx * au[b]);
+      const float h = silu_fast(gv) * uv;
+      hv[b][j] = h;
+      mx = fmaxf(mx, fabsf(h));
     }
-  if (c16 == 0)
+    rmax[j] = group_reduce<32, OpMax>(mx);
+  }
+  if (r32 == 0)
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_red[wave][16 * a + 4 * g + i] = rmax[a][i];
+    for (int j = 0; j < 16; ++j) s_red[wave][8 * (j >> 2) + 4 * kg + (j & 3)] = rmax[j];
   __syncthreads();
-  // h limbs staged in LDS (reusing the A buffers) as [limb][row][I]
+  // h limbs staged in LDS (reusing the x buffers) as [limb][row][I]
   int8_t* sH = smem;
-  int rsum[2][4];
+  int rsum[16];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int j = 0; j < 16; ++j) {
+    const int m = 8 * (j >> 2) + 4 * kg + (j & 3);
+    float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * a + 4 * g + i;
-      float mx = 0.f;
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_red[w][m]);
+    const float sc = mx > 0.f ? mx / kQMax : 1.f;
+    const float inv = mx > 0.f ? kQMax / mx : 1.f;
+    int qs = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_red[w][m]);
-      const float sc = mx > 0.f ? mx / kQMax : 1.f;
-      int qs = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int col = 64 * wave + 16 * b + c16;
-        int q = (int)rintf(hv[a][b][i] / sc);
-        q = max(-16256, min(16256, q));
-        const int hi = (q + 64) >> 7;
-        sH[m * I + col] = (int8_t)hi;
-        sH[TM * I + m * I + col] = (int8_t)(q - (hi << 7));
-        qs += q;
-      }
-      rsum[a][i] = group_reduce_i<16, OpSum>(qs);
-      if (wave == 0 && c16 == 0 && m < np) hs[p0 + m] = sc;
+    for (int b = 0; b < NBG; ++b) {
+      const int col = col0 + 32 * b;
+      int q = (int)rintf(hv[b][j] * inv);
+      q = max(-16256, min(16256, q));
+      const int hi = (q + 64) >> 7;
+      sH[m * I + col] = (int8_t)hi;
+      sH[TM * I + m * I + col] = (int8_t)(q - (hi << 7));
+      qs += q;
     }
-  if (c16 == 0)
+    rsum[j] = group_reduce_i<32, OpSum>(qs);
+    if (wave == 0 && r32 == 0 && m < np) hs[p0 + m] = sc;
+  }
+  if (r32 == 0)
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_redi[wave][16 * a + 4 * g + i] = rsum[a][i];
+    for (int j = 0; j < 16; ++j) s_redi[wave][8 * (j >> 2) + 4 * kg + (j & 3)] = rsum[j];
   __syncthreads();
   if (tid < np) {
     int tot = 0;
@@ -315,13 +380,14 @@ __global__ __launch_bounds__(NW * 64) void k_gateup_mfma(
     reinterpret_cast<int*>(hs)[Tk + p0 + tid] = tot;
   }
   // rows [0, np) of both limbs to hq[slot][limb][I], 16 bytes per thread
-  const int segs_row = I / 16;
-  for (int c = tid; c < 2 * np * segs_row; c += NTH) {
-    const int limb = c / (np * segs_row);
-    const int r = (c / segs_row) % np;
-    const int seg = c % segs_row;
-    *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + r) * 2 * I + (int64_t)limb * I + seg * 16) =
-        *reinterpret_cast<const uint4*>(sH + limb * TM * I + r * I + seg * 16);
+  constexpr int segs_row = I / 16;
+#pragma unroll
+  for (int c0 = 0; c0 < 2 * TM * segs_row; c0 += 256) {
+    const int c = c0 + tid;
+    const int limb = c / (TM * segs_row), r = (c / segs_row) % TM, seg = c % segs_row;
+    if (r < np)
+      *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + r) * 2 * I + (int64_t)limb * I + seg * 16) =
+          *reinterpret_cast<const uint4*>(sH + limb * TM * I + r * I + seg * 16);
   }
 }
 
@@ -343,14 +409,19 @@ __global__ __launch_bounds__(256) void k_down_mfma(
   __shared__ __align__(16) int8_t sA[2][TM][ROWB];
   __shared__ float s_hs[TM];
   __shared__ int s_hsum[TM];
-  const int tile = blockIdx.x;
-  if (tile >= *n_tiles) return;
+  // blocks of one (tile, 256-row chunk) pair: NCH consecutive ids of one XCD
+  // share a tile (its h limbs), neighbouring tiles share the weight chunks
+  const int NCH = H / 256;
+  const int local = blockIdx.x >> 3;
+  const int tile = xcd_tile(8 * (local / NCH) + (blockIdx.x & 7), *n_tiles);
+  if (tile < 0) return;
+  const int chunk = local % NCH;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int p0 = offsets[e] + m0;
   const int np = min(TM, offsets[e + 1] - p0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int obase = blockIdx.y * 256 + 64 * wave;
+  const int obase = chunk * 256 + 64 * wave;
 
   // weights first: they come from HBM
   const uint8_t* Wd = packed + (int64_t)e * 3 * H * I_ / 4 + 2 * (int64_t)I_ * H / 4;
@@ -464,11 +535,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
 hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
                           const Workspace& ws, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
-  MAPLE_PROF("quant_x", s);
   if (x_bf16)
-    k_quant_x<true><<<(unsigned)T, 256, 0, s>>>(x, (int)T, d.H, norm, ws.xq, ws.xs);
+    launch("quant_x", k_quant_x<true>, (unsigned)T, 256, 0, s, x, (int)T, d.H, norm, ws.xq, ws.xs);
   else
-    k_quant_x<false><<<(unsigned)T, 256, 0, s>>>(x, (int)T, d.H, norm, ws.xq, ws.xs);
+    launch("quant_x", k_quant_x<false>, (unsigned)T, 256, 0, s, x, (int)T, d.H, norm, ws.xq, ws.xs);
   return hipGetLastError();
 }
 
@@ -478,39 +548,35 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf
   (void)x;
   (void)x_bf16;
   const int64_t Tk = T * d.k;
-  const unsigned nt = (unsigned)max_tiles(d, T);
-  auto gateup = [&](auto nw_tag) {
-    constexpr int NW = decltype(nw_tag)::value;
-    MAPLE_PROF("gateup_mfma", s);
-    k_gateup_mfma<NW><<<nt, NW * 64, 0, s>>>(ws.xq, ws.xs, (int)T, d.H, d.I, packed, alpha,
-                                              ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles,
-                                              ws.hq, ws.hs, Tk);
+  const unsigned nt = (unsigned)((max_tiles(d, T) + 7) & ~7);  // whole rounds of 8 XCDs
+  auto gateup = [&](auto i_tag) {
+    constexpr int I_ = decltype(i_tag)::value;
+    launch("gateup_mfma", k_gateup_mfma<I_>, nt, 256, 0, s, ws.xq, ws.xs, (int)T, d.H, packed,
+           alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
   };
   auto down = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
-    MAPLE_PROF("down_mfma", s);
-    k_down_mfma<I_><<<dim3(nt, d.H / 256), 256, 0, s>>>(ws.hq, ws.hs, Tk, d.H, packed, alpha,
-                                                        ws.offsets, ws.tiles, ws.n_tiles, ws.y);
+    launch("down_mfma", k_down_mfma<I_>, nt * (d.H / 256), 256, 0, s, ws.hq, ws.hs, Tk, d.H,
+           packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, ws.y);
   };
   switch (d.I) {
     case 128:
-      gateup(std::integral_constant<int, 2>{});
+      gateup(std::integral_constant<int, 128>{});
       down(std::integral_constant<int, 128>{});
       break;
     case 256:
-      gateup(std::integral_constant<int, 4>{});
+      gateup(std::integral_constant<int, 256>{});
       down(std::integral_constant<int, 256>{});
       break;
     case 512:
-      gateup(std::integral_constant<int, 8>{});
+      gateup(std::integral_constant<int, 512>{});
       down(std::integral_constant<int, 512>{});
       break;
     default:
       return hipErrorNotSupported;
   }
-  MAPLE_PROF("combine", s);
-  k_combine<<<dim3((unsigned)T, (unsigned)((d.H + 1023) / 1024)), 256, 0, s>>>(
-      ws.y, ws.gate, ws.slot_pos, d.H, d.k, out, resid, delta);
+  launch("combine", k_combine, dim3((unsigned)T, (unsigned)((d.H + 1023) / 1024)), 256, 0, s, ws.y,
+         ws.gate, ws.slot_pos, d.H, d.k, out, resid, delta);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -35,6 +36,8 @@ struct Workspace {
   int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
   float* hs;            // [2, T*k]  scale of h's limbs per slot | limb row sum (int bits)
   float* y;             // [T*k, H]  expert outputs before the combine (grouped path)
+  uint16_t* xb;         // [2, T, H] bf16 hi/lo planes of fp32 x (large-T router)
+  uint16_t* wb;         // [2, E, H] bf16 hi/lo planes of the router (large-T router)
   size_t bytes;
 };
 
@@ -45,29 +48,38 @@ struct Dims {
 
 size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws);  // base may be null
 
-// Kernel timing hook (maple_profile_enable): brackets one launch with events
-// on its stream when the calling thread has profiling on; free otherwise.
-struct ProfScope {
-  ProfScope(const char* name, hipStream_t s);
-  ~ProfScope();
-  int slot;
-  hipStream_t stream;
-};
-#define MAPLE_PROF(name, s) ::maple::ProfScope maple_prof_scope_(name, s)
+// Kernel timing hook (maple_profile_enable).  When the calling thread has
+// profiling on, prof_slot hands out a start/stop event pair and the launch
+// passes it to hipExtLaunchKernelGGL, which stamps the events at the kernel's
+// own begin and end (the dispatch timestamps, not the queue around it).
+bool prof_slot(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+// Every library kernel launch goes through here, named for the timing hook.
+template <typename... P, typename... A>
+void launch(const char* name, void (*kernel)(P...), dim3 grid, dim3 block, unsigned lds,
+            hipStream_t s, A... args) {
+  hipEvent_t a, b;
+  if (prof_slot(name, &a, &b))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, a, b, 0u, static_cast<P>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<P>(args)...);
+}
 int max_tiles(const Dims& d, int64_t T);
 
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
+// xb, wb: bf16-plane scratch (ws.xb, ws.wb) used above the small-T sizes
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          const float* Wr, const float* bias, const float* rinv, float* logits,
-                         hipStream_t s);
+                         uint16_t* xb, uint16_t* wb, hipStream_t s);
 hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
                         hipStream_t s);
+// next_wr: the next layer's router (only read to warm the caches), or null
 hipError_t launch_decode1(const Dims& d, const void* x, bool x_bf16, const float* Wr,
                           const float* bias, const uint8_t* packed, const float* alpha,
                           const Workspace& ws, float* out, const float* resid, float* delta,
-                          hipStream_t s);
+                          const float* next_wr, hipStream_t s);
 hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
                           const Workspace& ws, hipStream_t s);
 hipError_t launch_gemv_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,

@@ -84,9 +84,8 @@ hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t*
   if (bad) {
     k_fill_i32<<<1, 256, 0, s>>>(bad, 0, 1);
   }
-  MAPLE_PROF("pack", s);
   if (n_words > 0)
-    k_pack<<<(unsigned)((n_words + 255) / 256), 256, 0, s>>>(w, n_words, out, bad);
+    launch("pack", k_pack, (unsigned)((n_words + 255) / 256), 256, 0, s, w, n_words, out, bad);
   return hipGetLastError();
 }
 

@@ -76,48 +76,148 @@ __global__ __launch_bounds__(64) void k_router_gemv(const void* __restrict__ x, 
   }
 }
 
-// Large T: 64x64 output tile per block, K step 16 through LDS, 4x4 per thread.
-// rinv (nullable): per-token 1/rms(x), computed beforehand.
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_router_gemm(const void* __restrict__ x, int T, int H,
-                                                     const float* __restrict__ Wr,
-                                                     const float* __restrict__ bias, int E,
+// ---- Large T: router logits on the matrix cores -----------------------------
+//
+// The fp32 router rows are split once per call into two bf16 planes,
+// W = W_hi + W_lo with W_hi = bf16(W) and W_lo = bf16(W - W_hi): 16 bits of
+// mantissa, a relative error of at most 2^-17 per weight (about 3e-6 on a
+// logit at the configured scales, far inside the top-k gap rule's 1e-4).  x is
+// bf16 already (one plane, exact) or split the same way (two planes), and
+// v_mfma_f32_32x32x16_bf16 accumulates x_hi W_hi + x_hi W_lo (+ x_lo W_hi) in
+// fp32.
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// src [n] fp32 -> hi [n], lo [n] bf16 bits; n % 4 == 0.
+__global__ __launch_bounds__(256) void k_split_bf16(const float* __restrict__ src, int64_t n,
+                                                    uint16_t* __restrict__ hi,
+                                                    uint16_t* __restrict__ lo) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const float4 v = *reinterpret_cast<const float4*>(src + i);
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h[q] = bf16_rne_bits(f[q]);
+    l[q] = bf16_rne_bits(f[q] - __uint_as_float(h[q] << 16));
+  }
+  *reinterpret_cast<uint2*>(hi + i) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2*>(lo + i) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+// 64 tokens x 64 experts per block; wave (wm, wn) owns 32 x 32 of it.  K runs
+// in chunks of 64 through a double-buffered LDS tile (rows padded to 144 B).
+// Global loads run three chunks ahead through two register sets: chunk c is
+// loaded at the end of chunk c - 3 and written to LDS at the end of chunk
+// c - 1.  Inside a chunk lane group kg = lane / 32 covers K [32 kg, 32 kg + 32)
+// and MFMA step s its 8-element piece s, for both operands.  Rows past T or E
+// read the last valid row; their results are not stored.  H % 64 == 0.
+// xp: NXP bf16 planes of x, plane stride T*H; wp: 2 bf16 planes of the
+// router, plane stride E*H.
+template <int NXP>
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ xp, int T, int H,
+                                                     const uint16_t* __restrict__ wp, int E,
+                                                     const float* __restrict__ bias,
                                                      const float* __restrict__ rinv,
                                                      float* __restrict__ logits) {
-  __shared__ float xs[16][68];
-  __shared__ float ws[16][68];
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
-  const int lr = tid >> 2, lk = (tid & 3) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < H; k0 += 16) {
-    float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), wv = xv;
-    if (m0 + lr < T) xv = load_x4<BF16>(x, (int64_t)(m0 + lr) * H + k0 + lk);
-    if (n0 + lr < E) wv = *reinterpret_cast<const float4*>(Wr + (int64_t)(n0 + lr) * H + k0 + lk);
-    __syncthreads();
-    xs[lk + 0][lr] = xv.x; xs[lk + 1][lr] = xv.y; xs[lk + 2][lr] = xv.z; xs[lk + 3][lr] = xv.w;
-    ws[lk + 0][lr] = wv.x; ws[lk + 1][lr] = wv.y; ws[lk + 2][lr] = wv.z; ws[lk + 3][lr] = wv.w;
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(&xs[kk][tm]);
-      const float4 b = *reinterpret_cast<const float4*>(&ws[kk][tn]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-    }
+  constexpr int ROWB = 144;
+  __shared__ __align__(16) char sA[2][NXP][64][ROWB];
+  __shared__ __align__(16) char sB[2][2][64][ROWB];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, r32 = lane & 31, kg = lane >> 5;
+  // staging: 64 rows x 128 B per plane = 512 16-byte units, 2 per thread
+  const int row0 = tid >> 3, seg = tid & 7, row1 = row0 + 32;
+  const int64_t xps = (int64_t)T * H, wps = (int64_t)E * H;
+  const uint16_t* pa0 = xp + (int64_t)min(t0 + row0, T - 1) * H + 8 * seg;
+  const uint16_t* pa1 = xp + (int64_t)min(t0 + row1, T - 1) * H + 8 * seg;
+  const uint16_t* pb0 = wp + (int64_t)min(e0 + row0, E - 1) * H + 8 * seg;
+  const uint16_t* pb1 = wp + (int64_t)min(e0 + row1, E - 1) * H + 8 * seg;
+  const uint32_t la0 = (uint32_t)(row0 * ROWB + 16 * seg), la1 = la0 + 32 * ROWB;
+  char* const A0 = &sA[0][0][0][0];
+  char* const B0 = &sB[0][0][0][0];
+  constexpr uint32_t ABUF = NXP * 64 * ROWB, BBUF = 2 * 64 * ROWB, PL = 64 * ROWB;
+  // one register set: x planes (2 NXP units) and router planes (4 units)
+#define MAPLE_RF(R, kc)                                                            \
+  {                                                                                \
+    const int k0_ = (kc) * 64;                                                     \
+    R##a00 = *reinterpret_cast<const uint4*>(pa0 + k0_);                           \
+    R##a01 = *reinterpret_cast<const uint4*>(pa1 + k0_);                           \
+    if constexpr (NXP == 2) {                                                      \
+      R##a10 = *reinterpret_cast<const uint4*>(pa0 + xps + k0_);                   \
+      R##a11 = *reinterpret_cast<const uint4*>(pa1 + xps + k0_);                   \
+    }                                                                              \
+    R##b00 = *reinterpret_cast<const uint4*>(pb0 + k0_);                           \
+    R##b01 = *reinterpret_cast<const uint4*>(pb1 + k0_);                           \
+    R##b10 = *reinterpret_cast<const uint4*>(pb0 + wps + k0_);                     \
+    R##b11 = *reinterpret_cast<const uint4*>(pb1 + wps + k0_);                     \
   }
+#define MAPLE_RS(R, buf)                                                           \
+  {                                                                                \
+    *reinterpret_cast<uint4*>(A0 + (buf) * ABUF + la0) = R##a00;                   \
+    *reinterpret_cast<uint4*>(A0 + (buf) * ABUF + la1) = R##a01;                   \
+    if constexpr (NXP == 2) {                                                      \
+      *reinterpret_cast<uint4*>(A0 + (buf) * ABUF + PL + la0) = R##a10;            \
+      *reinterpret_cast<uint4*>(A0 + (buf) * ABUF + PL + la1) = R##a11;            \
+    }                                                                              \
+    *reinterpret_cast<uint4*>(B0 + (buf) * BBUF + la0) = R##b00;                   \
+    *reinterpret_cast<uint4*>(B0 + (buf) * BBUF + la1) = R##b01;                   \
+    *reinterpret_cast<uint4*>(B0 + (buf) * BBUF + PL + la0) = R##b10;              \
+    *reinterpret_cast<uint4*>(B0 + (buf) * BBUF + PL + la1) = R##b11;              \
+  }
+  uint4 pa00, pa01, pa10, pa11, pb00, pb01, pb10, pb11;
+  uint4 qa00, qa01, qa10, qa11, qb00, qb01, qb10, qb11;
+  v16f acc = {};
+  const uint32_t ra = (uint32_t)((32 * wm + r32) * ROWB + 64 * kg);
+  const uint32_t rb = (uint32_t)((32 * wn + r32) * ROWB + 64 * kg);
+  auto compute = [&](int buf) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = m0 + tm + i, e = n0 + tn + j;
-      if (t < T && e < E)
-        logits[(int64_t)t * E + e] = acc[i][j] * (rinv ? rinv[t] : 1.f) + (bias ? bias[e] : 0.f);
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const v8bf a0 = *reinterpret_cast<const v8bf*>(A0 + buf * ABUF + ra + 16 * s2);
+      const v8bf b0 = *reinterpret_cast<const v8bf*>(B0 + buf * BBUF + rb + 16 * s2);
+      const v8bf b1 = *reinterpret_cast<const v8bf*>(B0 + buf * BBUF + PL + rb + 16 * s2);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc, 0, 0, 0);
+      if constexpr (NXP == 2) {
+        const v8bf a1 = *reinterpret_cast<const v8bf*>(A0 + buf * ABUF + PL + ra + 16 * s2);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc, 0, 0, 0);
+      }
     }
+  };
+  const int nk = H / 64;  // >= 4, even
+  MAPLE_RF(p, 0);
+  MAPLE_RF(q, 1);
+  MAPLE_RS(p, 0);
+  MAPLE_RF(p, 2);
+  __syncthreads();
+  // loads past the last chunk re-read it (kept unconditional: the waits stay partial)
+  for (int kc = 0; kc < nk; kc += 2) {
+    compute(0);
+    MAPLE_RS(q, 1);  // chunk kc + 1
+    MAPLE_RF(q, min(kc + 3, nk - 1));
+    __syncthreads();
+    compute(1);
+    MAPLE_RS(p, 0);  // chunk kc + 2
+    MAPLE_RF(p, min(kc + 4, nk - 1));
+    __syncthreads();
+  }
+#undef MAPLE_RF
+#undef MAPLE_RS
+  // accumulator register j: token 8 (j / 4) + 4 kg + j % 4, expert r32 of the wave's tile
+  const int e = e0 + 32 * wn + r32;
+  const float b = (bias && e < E) ? bias[e] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int t = t0 + 32 * wm + 8 * (j >> 2) + 4 * kg + (j & 3);
+    if (t < T && e < E) logits[(int64_t)t * E + e] = acc[j] * (rinv ? rinv[t] : 1.f) + b;
+  }
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -210,33 +310,49 @@ __global__ __launch_bounds__(256) void k_route_small(
 
 // ---- large T: per-block selection, one scan block, parallel scatter --------------
 
-__global__ __launch_bounds__(256) void k_route_block(const float* __restrict__ logits, int T,
-                                                     int E, int k, int renorm,
-                                                     int32_t* __restrict__ idx,
-                                                     float* __restrict__ gate,
-                                                     int32_t* __restrict__ blk_count,
-                                                     int32_t* __restrict__ blk_rank) {
+// One block per 64 tokens, 16 waves with 4 tokens each; the logits of the
+// wave's 4 tokens are loaded together before the selections.
+__global__ __launch_bounds__(1024) void k_route_block(const float* __restrict__ logits, int T,
+                                                      int E, int k, int renorm,
+                                                      int32_t* __restrict__ idx,
+                                                      float* __restrict__ gate,
+                                                      int32_t* __restrict__ blk_count,
+                                                      int32_t* __restrict__ blk_rank) {
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 64;
   const int nt = min(64, T - t0);
-  s_mask[tid] = 0ull;
-  for (int tl = wave; tl < nt; tl += 4) {
-    int i;
-    float g;
-    wave_softmax_topk(logits + (int64_t)(t0 + tl) * E, E, k, renorm != 0, lane, &i, &g);
-    if (lane < k) {
-      idx[(int64_t)(t0 + tl) * k + lane] = i;
-      gate[(int64_t)(t0 + tl) * k + lane] = g;
-      s_idx[tl * k + lane] = i;
+  if (tid < 256) s_mask[tid] = 0ull;
+  float lv[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tl = wave + 16 * r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * m;
+      lv[r][m] = (tl < nt && e < E) ? logits[(int64_t)(t0 + tl) * E + e] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tl = wave + 16 * r;
+    if (tl < nt) {  // wave-uniform
+      int i;
+      float g;
+      wave_topk_lanes(lv[r], E, k, renorm != 0, lane, &i, &g);
+      if (lane < k) {
+        idx[(int64_t)(t0 + tl) * k + lane] = i;
+        gate[(int64_t)(t0 + tl) * k + lane] = g;
+        s_idx[tl * k + lane] = i;
+      }
     }
   }
   __syncthreads();
-  for (int q = tid; q < nt * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
+  for (int q = tid; q < nt * k; q += 1024) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   if (tid < E) blk_count[(int64_t)blockIdx.x * E + tid] = __popcll(s_mask[tid]);
-  for (int q = tid; q < nt * k; q += 256) {
+  for (int q = tid; q < nt * k; q += 1024) {
     const int tl = q / k, e = s_idx[q];
     blk_rank[(int64_t)t0 * k + q] = __popcll(s_mask[e] & ((1ull << tl) - 1ull));
   }
@@ -280,25 +396,35 @@ __global__ __launch_bounds__(256) void k_route_scatter(int64_t n_slots, int E, i
 }  // namespace
 
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
-                         const float* bias, const float* rinv, float* logits, hipStream_t s) {
+                         const float* bias, const float* rinv, float* logits, uint16_t* xb,
+                         uint16_t* wb, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   if (T <= 64) {
     const dim3 grid(d.E, (unsigned)((T + 3) / 4));
-    MAPLE_PROF("router_gemv", s);
     if (x_bf16)
-      k_router_gemv<true><<<grid, 64, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, norm, logits);
+      launch("router_gemv", k_router_gemv<true>, grid, 64, 0, s, x, (int)T, d.H, Wr, bias, d.E,
+             norm, logits);
     else
-      k_router_gemv<false><<<grid, 64, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E, norm, logits);
+      launch("router_gemv", k_router_gemv<false>, grid, 64, 0, s, x, (int)T, d.H, Wr, bias, d.E,
+             norm, logits);
   } else {
     if (norm && !rinv) return hipErrorInvalidValue;
+    if (!xb || !wb) return hipErrorInvalidValue;
+    const int64_t nw = (int64_t)d.E * d.H;
+    launch("split_router", k_split_bf16, (unsigned)((nw / 4 + 255) / 256), 256, 0, s, Wr, nw, wb,
+           wb + nw);
     const dim3 grid((unsigned)((T + 63) / 64), (unsigned)((d.E + 63) / 64));
-    MAPLE_PROF("router_gemm", s);
-    if (x_bf16)
-      k_router_gemm<true><<<grid, 256, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E,
-                                               norm ? rinv : nullptr, logits);
-    else
-      k_router_gemm<false><<<grid, 256, 0, s>>>(x, (int)T, d.H, Wr, bias, d.E,
-                                                norm ? rinv : nullptr, logits);
+    if (x_bf16) {
+      launch("router_mfma", k_router_mfma<1>, grid, 256, 0, s,
+             reinterpret_cast<const uint16_t*>(x), (int)T, d.H, (const uint16_t*)wb, d.E, bias,
+             norm ? rinv : nullptr, logits);
+    } else {
+      const int64_t nx = T * d.H;
+      launch("split_x", k_split_bf16, (unsigned)((nx / 4 + 255) / 256), 256, 0, s,
+             reinterpret_cast<const float*>(x), nx, xb, xb + nx);
+      launch("router_mfma", k_router_mfma<2>, grid, 256, 0, s, (const uint16_t*)xb, (int)T, d.H,
+             (const uint16_t*)wb, d.E, bias, norm ? rinv : nullptr, logits);
+    }
   }
   return hipGetLastError();
 }
@@ -307,29 +433,24 @@ hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Wor
                         hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
   if (T <= 64) {
-    MAPLE_PROF("route_small", s);
-    k_route_small<<<1, 256, 0, s>>>(logits, (int)T, d.E, d.k, renorm, ws.idx, ws.gate,
-                                    ws.offsets, ws.active, ws.n_active, ws.sorted_tok,
-                                    ws.slot_pos, ws.tiles, ws.n_tiles);
+    launch("route_small", k_route_small, 1, 256, 0, s, logits, (int)T, d.E, d.k, renorm, ws.idx,
+           ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos, ws.tiles,
+           ws.n_tiles);
     return hipGetLastError();
   }
   const int nb = (int)((T + 63) / 64);
   {
-    MAPLE_PROF("route_block", s);
-    k_route_block<<<nb, 256, 0, s>>>(logits, (int)T, d.E, d.k, renorm, ws.idx, ws.gate,
-                                     ws.blk_count, ws.blk_rank);
+    launch("route_block", k_route_block, nb, 1024, 0, s, logits, (int)T, d.E, d.k, renorm, ws.idx,
+           ws.gate, ws.blk_count, ws.blk_rank);
   }
   {
-    MAPLE_PROF("route_scan", s);
-    k_route_scan<<<1, 256, 0, s>>>(nb, d.E, ws.blk_count, ws.offsets, ws.active, ws.n_active,
-                                   ws.tiles, ws.n_tiles);
+    launch("route_scan", k_route_scan, 1, 256, 0, s, nb, d.E, ws.blk_count, ws.offsets, ws.active,
+           ws.n_active, ws.tiles, ws.n_tiles);
   }
   const int64_t n_slots = T * d.k;
   {
-    MAPLE_PROF("route_scatter", s);
-    k_route_scatter<<<(unsigned)((n_slots + 255) / 256), 256, 0, s>>>(
-        n_slots, d.E, d.k, ws.idx, ws.offsets, ws.blk_count, ws.blk_rank, ws.slot_pos,
-        ws.sorted_tok);
+    launch("route_scatter", k_route_scatter, (unsigned)((n_slots + 255) / 256), 256, 0, s, n_slots,
+           d.E, d.k, ws.idx, ws.offsets, ws.blk_count, ws.blk_rank, ws.slot_pos, ws.sorted_tok);
   }
   return hipGetLastError();
 }

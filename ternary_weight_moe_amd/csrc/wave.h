@@ -272,4 +272,66 @@ __device__ __forceinline__ void wave_topk_rounds(const float* __restrict__ lrow,
   *out_sum = s;
 }
 
+// The same rounds on logits already in registers (lane holds experts lane +
+// 64 m, m < 4; entries with e >= E ignored); lane j < k receives selection j
+// (expert and gate, renormalised over the k when asked).
+__device__ __forceinline__ void wave_topk_lanes(const float (&l)[4], int E, int k, bool renorm,
+                                                int lane, int* my_sel, float* my_gate) {
+  int key[4], em[4];
+  float mxl = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    key[m] = (e < E) ? float_key(l[m]) : kKeyTaken;
+    em[m] = e;
+    mxl = fmaxf(mxl, (e < E && l[m] == l[m]) ? l[m] : -INFINITY);
+  }
+  const float mx = wave_max_f(mxl);
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (em[m] < E) s += expf(key_float(key[m]) - mx);
+  s = wave_sum_f(s);
+  auto cs = [&](int a, int b) {
+    const bool sw = key[b] > key[a] || (key[b] == key[a] && em[b] < em[a]);
+    const int ka = key[a], ea = em[a];
+    key[a] = sw ? key[b] : key[a];
+    em[a] = sw ? em[b] : em[a];
+    key[b] = sw ? ka : key[b];
+    em[b] = sw ? ea : em[b];
+  };
+  cs(0, 1);
+  cs(2, 3);
+  cs(0, 2);
+  cs(1, 3);
+  cs(1, 2);
+  int hk = key[0], he = em[0];
+  int head = 0;
+  int sel = 0;
+  float val = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    const int best = wave_max_i_uniform(hk);
+    const unsigned long long b = __ballot(hk == best);
+    int e;
+    if (__popcll(b) == 1) {
+      e = __builtin_amdgcn_readlane(he, (int)__builtin_ctzll(b));
+    } else {  // equal logits in several lanes: the lowest expert index wins
+      e = -wave_max_i_uniform(hk == best ? -he : (int)0x80000001);
+    }
+    if (he == e) {
+      ++head;
+      hk = head == 1 ? key[1] : head == 2 ? key[2] : head == 3 ? key[3] : kKeyTaken;
+      he = head == 1 ? em[1] : head == 2 ? em[2] : head == 3 ? em[3] : 0x7fffffff;
+    }
+    if (lane == j) {
+      sel = e;
+      val = key_float(best);
+    }
+  }
+  float g = lane < k ? expf(val - mx) / s : 0.f;
+  if (renorm) g /= wave_sum_f(g);
+  *my_sel = sel;
+  *my_gate = g;
+}
+
 }  // namespace maple

@@ -381,3 +381,49 @@ def test_prenorm_layer_is_scale_invariant_and_matches_dense():
     # without the norm the same layer differs (x here has rms != 1)
     c = oracle.moe_layer(8.0 * x, Wr, bias, packed, alpha, k=w.top_k, inter=w.inter)
     assert rel_l2(c["out"], a["out"]) > 1.0
+
+
+def test_hand_worked_micro_layer_closed_form():
+    """A micro layer whose output is written out by hand.  x = 1 (H = 16);
+    router rows c_e/16 give logits c = (0.5, 0.25, 0, -0.25), so the top 2 are
+    experts 0 and 1 with gates softmax(c)_0, softmax(c)_1.  Expert 0: W_g = +1,
+    W_u = -1, W_d = +1 everywhere, so h_i = silu(16 a_g) (-16 a_u) and
+    y_o = a_d 16 h.  Expert 1: W_g = -1, W_u = +1, W_d row o = +1 on the first
+    8 columns and 0 elsewhere, with a per-row a_d, so y_o = a_d[o] 8 h.
+    Experts 2 and 3 hold random codes and must not contribute."""
+    H = I = 16
+    E, k = 4, 2
+    c = np.array([0.5, 0.25, 0.0, -0.25])
+    Wr = np.repeat((c / 16.0)[:, None], H, axis=1).astype(np.float32)
+    rng = np.random.default_rng(3)
+    W = rng.integers(-1, 2, size=(E, 3 * H * I), dtype=np.int8)
+    n = H * I
+    W[0, :n] = 1
+    W[0, n:2 * n] = -1
+    W[0, 2 * n:] = 1
+    W[1, :n] = -1
+    W[1, n:2 * n] = 1
+    wd1 = np.zeros((H, I), np.int8)
+    wd1[:, :8] = 1
+    W[1, 2 * n:] = wd1.reshape(-1)
+    alpha = np.zeros((E, 2 * I + H), np.float32)
+    alpha[0, :I], alpha[0, I:2 * I], alpha[0, 2 * I:] = 0.1, 0.05, 0.02
+    alpha[1, :I], alpha[1, I:2 * I] = 0.03, 0.07
+    alpha[1, 2 * I:] = (0.04 + 0.001 * np.arange(H)).astype(np.float32)
+    alpha[2:] = 0.05
+    packed = oracle.pack_layer(W, H, I)
+    x = np.ones((1, H))
+    r = oracle.moe_layer(x, Wr, None, packed, alpha, k=k, inter=I)
+
+    def silu(z):
+        return z / (1.0 + math.exp(-z))
+    a = alpha.astype(np.float64)
+    h0 = silu(16 * a[0, 0]) * (-16 * a[0, I])
+    h1 = silu(-16 * a[1, 0]) * (16 * a[1, I])
+    y0 = a[0, 2 * I:] * 16 * h0
+    y1 = a[1, 2 * I:] * 8 * h1
+    p = np.exp(c - c.max()) / np.exp(c - c.max()).sum()
+    expect = p[0] * y0 + p[1] * y1
+    assert list(r["idx"][0]) == [0, 1]
+    np.testing.assert_allclose(r["gate"][0], p[:2], rtol=1e-14)
+    np.testing.assert_allclose(r["out"][0], expect, rtol=1e-13, atol=0)
