@@ -74,62 +74,74 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
 
 // ---- x -> two int8 limbs, per-token scale, row sum of q, 1/rms ---------------
 
+// One wave per token, 4 tokens per block; lane holds H/64 contiguous values
+// (H % 256 == 0), loaded 4 at a time.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int T, int H,
                                                  int norm, int8_t* __restrict__ xq,
                                                  float* __restrict__ xs) {
-  __shared__ float s_a[4], s_s[4];
-  __shared__ int s_i[4];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = H / 256;  // 1..16, contiguous per thread
-  const int64_t base = (int64_t)t * H + (int64_t)tid * per;
-  float v[16];
+  constexpr int MAXP = 64;  // values per lane at H = 4096
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int per = H / 64;
+  const int64_t base = (int64_t)t * H + (int64_t)lane * per;
+  float v[MAXP];
   float amax = 0.f, ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < MAXP; i += 4) {
     if (i < per) {
-      float f;
-      if constexpr (BF16)
-        f = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[base + i] << 16);
-      else
-        f = reinterpret_cast<const float*>(x)[base + i];
-      v[i] = f;
-      amax = fmaxf(amax, fabsf(f));
-      ss = fmaf(f, f, ss);
+      float f[4];
+      if constexpr (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + base + i);
+        f[0] = __uint_as_float(u.x << 16);
+        f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        f[2] = __uint_as_float(u.y << 16);
+        f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base + i);
+        f[0] = a.x;
+        f[1] = a.y;
+        f[2] = a.z;
+        f[3] = a.w;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[i + q] = f[q];
+        amax = fmaxf(amax, fabsf(f[q]));
+        ss = fmaf(f[q], f[q], ss);
+      }
     }
   }
   amax = wave_max_f(amax);
   ss = wave_sum_f(ss);
-  if (lane == 0) {
-    s_a[wave] = amax;
-    s_s[wave] = ss;
-  }
-  __syncthreads();
-  amax = fmaxf(fmaxf(s_a[0], s_a[1]), fmaxf(s_a[2], s_a[3]));
-  ss = s_s[0] + s_s[1] + s_s[2] + s_s[3];
   const float scale = amax > 0.f ? amax / kQMax : 1.f;
-  int8_t* hi_row = xq + (int64_t)t * 2 * H;
+  const float inv = amax > 0.f ? kQMax / amax : 1.f;
+  int8_t* hi_row = xq + (int64_t)t * 2 * H + lane * per;
   int8_t* lo_row = hi_row + H;
   int qsum = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < MAXP; i += 4) {
     if (i < per) {
-      int q = (int)rintf(v[i] / scale);
-      q = max(-16256, min(16256, q));
-      const int hi = (q + 64) >> 7;
-      const int lo = q - (hi << 7);
-      hi_row[tid * per + i] = (int8_t)hi;
-      lo_row[tid * per + i] = (int8_t)lo;
-      qsum += q;
+      uint32_t hw = 0u, lw = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int qq = (int)rintf(v[i + q] * inv);
+        qq = max(-16256, min(16256, qq));
+        const int hi = (qq + 64) >> 7;
+        const int lo = qq - (hi << 7);
+        hw |= (uint32_t)(hi & 0xFF) << (8 * q);
+        lw |= (uint32_t)(lo & 0xFF) << (8 * q);
+        qsum += qq;
+      }
+      *reinterpret_cast<uint32_t*>(hi_row + i) = hw;
+      *reinterpret_cast<uint32_t*>(lo_row + i) = lw;
     }
   }
   qsum = wave_sum_i(qsum);
-  if (lane == 0) s_i[wave] = qsum;
-  __syncthreads();
-  if (tid == 0) {
+  if (lane == 0) {
     xs[t] = scale;
-    reinterpret_cast<int*>(xs)[T + t] = s_i[0] + s_i[1] + s_i[2] + s_i[3];
+    reinterpret_cast<int*>(xs)[T + t] = qsum;
     xs[2 * T + t] = norm ? rsqrtf(ss / (float)H + MAPLE_RMS_EPS) : 1.f;
   }
 }
@@ -393,109 +405,119 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
 
 // ---- down projection ----------------------------------------------------------------
 
-// One block: one M tile x 256 output rows (4 waves x 64).  All of K = I sits
-// in LDS; the weights go straight from global memory into B operands.
-template <int I_>
+// One block (4 waves, one per SIMD): one M tile (TM = 32 slots of one expert)
+// x all H outputs, in chunks of 128 NBW outputs: wave w owns NBW N-subtiles of
+// 32 outputs per chunk.  The tile's h limbs (all of K = I) sit in LDS for the
+// whole block.  The weights are the MFMA's first operand (rows = outputs) and
+// h the second (columns = slots), so a lane ends with 4 consecutive outputs
+// of one slot per register quad and writes them as one 16-byte store.  The
+// weight registers of 128 codes are refilled with the next chunk right after
+// their last step, a full chunk ahead of their next use.
+// K order: MFMA step s uses word 8 (s / 4) + 4 kg + s % 4 of the row (I/16
+// words), so a lane holds 16 contiguous bytes per 128 codes of each row.
+template <int I, int NBW>
 __global__ __launch_bounds__(256) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, float* __restrict__ y) {
-  constexpr int SS = I_ >= 256 ? 4 : 2;  // MFMA steps per super-step
-  constexpr int KSS = 64 * SS;           // codes per super-step
-  constexpr int NSS = I_ / KSS;
-  constexpr int ROWB = I_ + 16;
-  constexpr int SEGR = I_ / 16;          // 16-byte segments per limb row
+  constexpr int NQ = I / 128;           // 16-byte pieces per lane and row
+  constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
+  constexpr int CH = 128 * NBW;         // outputs per chunk
   __shared__ __align__(16) int8_t sA[2][TM][ROWB];
-  __shared__ float s_hs[TM];
-  __shared__ int s_hsum[TM];
-  // blocks of one (tile, 256-row chunk) pair: NCH consecutive ids of one XCD
-  // share a tile (its h limbs), neighbouring tiles share the weight chunks
-  const int NCH = H / 256;
-  const int local = blockIdx.x >> 3;
-  const int tile = xcd_tile(8 * (local / NCH) + (blockIdx.x & 7), *n_tiles);
+  extern __shared__ __align__(16) float s_ad[];  // a_d of the expert: H floats
+  const int tile = xcd_tile(blockIdx.x, *n_tiles);
   if (tile < 0) return;
-  const int chunk = local % NCH;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int p0 = offsets[e] + m0;
   const int np = min(TM, offsets[e + 1] - p0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int obase = chunk * 256 + 64 * wave;
-
-  // weights first: they come from HBM
-  const uint8_t* Wd = packed + (int64_t)e * 3 * H * I_ / 4 + 2 * (int64_t)I_ * H / 4;
-  uint4 bq[NSS][4];
+  const int kg = lane >> 5, r32 = lane & 31;
+  const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4;
+  const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I;
+  const int nch = H / CH;
+  // lane's weight row in N-subtile b of chunk c: c*CH + 32*(NBW*wave + b) + r32
+  const uint8_t* wrow = Wd + (int64_t)(32 * NBW * wave + r32) * (I / 4) + 16 * kg;
+  auto bptr = [&](int c, int b, int q) {
+    return reinterpret_cast<const uint4*>(wrow + (int64_t)(c * CH + 32 * b) * (I / 4) + 32 * q);
+  };
+  uint4 bq[NBW][NQ];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint8_t* row = Wd + (int64_t)(obase + 16 * b + c16) * (I_ / 4);
+  for (int b = 0; b < NBW; ++b)
 #pragma unroll
-    for (int ss = 0; ss < NSS; ++ss) {
-      if constexpr (SS == 4) {
-        bq[ss][b] = *reinterpret_cast<const uint4*>(row + ss * (KSS / 4) + 16 * g);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(row + ss * (KSS / 4) + 8 * g);
-        bq[ss][b] = make_uint4(v.x, v.y, 0u, 0u);
-      }
-    }
+    for (int q = 0; q < NQ; ++q) bq[b][q] = *bptr(0, b, q);
+  // h limbs of the tile's slots: 2 * TM rows of I bytes; rows past np are zero.
+  // All loads are issued before the first LDS store.
+  constexpr int SEGR = I / 16;
+  constexpr int NHU = 2 * TM * SEGR / 256;  // 16-byte units per thread
+  uint4 hv[NHU];
+#pragma unroll
+  for (int i = 0; i < NHU; ++i) {
+    const int u = tid + 256 * i;
+    const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
+    hv[i] = r < np ? *reinterpret_cast<const uint4*>(hq + (int64_t)(p0 + r) * 2 * I +
+                                                     (int64_t)limb * I + 16 * sg)
+                   : make_uint4(0u, 0u, 0u, 0u);
   }
-  for (int c = tid; c < 2 * TM * SEGR; c += 256) {
-    const int limb = c / (TM * SEGR), r = (c / SEGR) % TM, seg = c % SEGR;
-    const uint4 v = r < np ? *reinterpret_cast<const uint4*>(hq + (int64_t)(p0 + r) * 2 * I_ +
-                                                             (int64_t)limb * I_ + seg * 16)
-                           : make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&sA[limb][r][seg * 16]) = v;
+#pragma unroll
+  for (int i = 0; i < NHU; ++i) {
+    const int u = tid + 256 * i;
+    const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
+    *reinterpret_cast<uint4*>(&sA[limb][r][16 * sg]) = hv[i];
   }
-  if (tid < TM) {
-    s_hs[tid] = tid < np ? hs[p0 + tid] : 0.f;
-    s_hsum[tid] = tid < np ? reinterpret_cast<const int*>(hs)[Tk + p0 + tid] : 0;
-  }
+  // a_d through LDS: the epilogue's reads then never wait behind the weight
+  // loads in flight for the next chunk
+  for (int u = tid; u < H / 4; u += 256)
+    reinterpret_cast<float4*>(s_ad)[u] = reinterpret_cast<const float4*>(ad)[u];
+  // this lane's slot (the accumulator column) and its scale and limb row sum
+  const bool live = r32 < np;
+  const float sc = live ? hs[p0 + r32] : 0.f;
+  const int hsum = live ? reinterpret_cast<const int*>(hs)[Tk + p0 + r32] : 0;
+  float* yrow = y + (int64_t)(p0 + r32) * H;
   __syncthreads();
+  const int8_t* sa = &sA[0][r32][64 * kg];
 
-  v4i acc_hi[2][4], acc_lo[2][4];
+  for (int c = 0; c < nch; ++c) {
+    const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
+    v16i acc[2][NBW];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int l = 0; l < 2; ++l)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc_hi[a][b] = acc_lo[a][b] = v4i{0, 0, 0, 0};
+      for (int b = 0; b < NBW; ++b) acc[l][b] = v16i{};
 #pragma unroll
-  for (int ss = 0; ss < NSS; ++ss) {
+    for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      const int off = ss * KSS + 16 * (SS * g + s);
-      v4i ahi[2], alo[2];
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const v4i a0 = *reinterpret_cast<const v4i*>(sa + 128 * q + 16 * s4);
+        const v4i a1 = *reinterpret_cast<const v4i*>(sa + TM * ROWB + 128 * q + 16 * s4);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        ahi[a] = *reinterpret_cast<const v4i*>(&sA[0][16 * a + c16][off]);
-        alo[a] = *reinterpret_cast<const v4i*>(&sA[1][16 * a + c16][off]);
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const v4i bf = unpack_word(word_of(bq[ss][b], s));
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          acc_hi[a][b] = mfma(ahi[a], bf, acc_hi[a][b]);
-          acc_lo[a][b] = mfma(alo[a], bf, acc_lo[a][b]);
+        for (int b = 0; b < NBW; ++b) {
+          const v4i wf = unpack_word(word_of(bq[b][q], s4));
+          acc[0][b] = mfma32(wf, a0, acc[0][b]);
+          acc[1][b] = mfma32(wf, a1, acc[1][b]);
         }
       }
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
+    }
+    // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk:
+    // y[slot][o] = a_d[o] * s * (128 C_hi + C_lo - rowsum)
+    if (live) {
+#pragma unroll
+      for (int b = 0; b < NBW; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = c * CH + 32 * (NBW * wave + b) + 8 * i + 4 * kg;
+          const float4 a = *reinterpret_cast<const float4*>(s_ad + o);
+          float4 v;
+          v.x = a.x * sc * (float)(128 * acc[0][b][4 * i] + acc[1][b][4 * i] - hsum);
+          v.y = a.y * sc * (float)(128 * acc[0][b][4 * i + 1] + acc[1][b][4 * i + 1] - hsum);
+          v.z = a.z * sc * (float)(128 * acc[0][b][4 * i + 2] + acc[1][b][4 * i + 2] - hsum);
+          v.w = a.w * sc * (float)(128 * acc[0][b][4 * i + 3] + acc[1][b][4 * i + 3] - hsum);
+          *reinterpret_cast<float4*>(yrow + o) = v;
+        }
     }
   }
-  const float* ad = alpha + (int64_t)e * (2 * I_ + H) + 2 * I_;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * a + 4 * g + i;
-      if (m < np) {
-        const float sc = s_hs[m];
-        const int hsum = s_hsum[m];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int o = obase + 16 * b + c16;
-          y[(int64_t)(p0 + m) * H + o] =
-              ad[o] * sc * (float)(128 * acc_hi[a][b][i] + acc_lo[a][b][i] - hsum);
-        }
-      }
-    }
 }
 
 // ---- weighted combine ---------------------------------------------------------------
@@ -536,9 +558,11 @@ hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
                           const Workspace& ws, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   if (x_bf16)
-    launch("quant_x", k_quant_x<true>, (unsigned)T, 256, 0, s, x, (int)T, d.H, norm, ws.xq, ws.xs);
+    launch("quant_x", k_quant_x<true>, (unsigned)((T + 3) / 4), 256, 0, s, x, (int)T, d.H, norm,
+           ws.xq, ws.xs);
   else
-    launch("quant_x", k_quant_x<false>, (unsigned)T, 256, 0, s, x, (int)T, d.H, norm, ws.xq, ws.xs);
+    launch("quant_x", k_quant_x<false>, (unsigned)((T + 3) / 4), 256, 0, s, x, (int)T, d.H, norm,
+           ws.xq, ws.xs);
   return hipGetLastError();
 }
 
@@ -556,8 +580,12 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf
   };
   auto down = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
-    launch("down_mfma", k_down_mfma<I_>, nt * (d.H / 256), 256, 0, s, ws.hq, ws.hs, Tk, d.H,
-           packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, ws.y);
+    if (d.H % 512 == 0)
+      launch("down_mfma", k_down_mfma<I_, 4>, nt, 256, 4 * d.H, s, ws.hq, ws.hs, Tk, d.H, packed, alpha,
+             ws.offsets, ws.tiles, ws.n_tiles, ws.y);
+    else
+      launch("down_mfma", k_down_mfma<I_, 2>, nt, 256, 4 * d.H, s, ws.hq, ws.hs, Tk, d.H, packed, alpha,
+             ws.offsets, ws.tiles, ws.n_tiles, ws.y);
   };
   switch (d.I) {
     case 128:

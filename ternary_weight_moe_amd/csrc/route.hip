@@ -369,10 +369,16 @@ __global__ __launch_bounds__(256) void k_route_scan(int nb, int E, int32_t* __re
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E)
-    for (int b = 0; b < nb; ++b) {
-      const int c = blk_count[(int64_t)b * E + e];
-      blk_count[(int64_t)b * E + e] = cnt;  // becomes the block's base within expert e
-      cnt += c;
+    for (int b0 = 0; b0 < nb; b0 += 16) {  // 16 loads in flight per thread
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nb ? blk_count[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (b0 + i < nb) {
+          blk_count[(int64_t)(b0 + i) * E + e] = cnt;  // becomes the block's base within expert e
+          cnt += c[i];
+        }
     }
   finish_offsets(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
 }
