@@ -164,6 +164,18 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * z));
 }
 
+// two fp32 -> packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
@@ -202,6 +214,7 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
   __shared__ int s_xsum[TM], s_tok[TM];
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
+  __shared__ __align__(16) float s_al[2 * I];
   const int tile = xcd_tile(blockIdx.x, *n_tiles);
   if (tile < 0) return;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
@@ -222,13 +235,11 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
   auto bsrc = [&](int b, int st) -> const uint8_t* {
     return brow + (b < NBG ? 0 : (int64_t)I * rowb) + (int64_t)(32 * (b % NBG)) * rowb + st * 64;
   };
+  // a_g | a_u of the expert (2I floats) in LDS for the epilogue
   const float* al = alpha + (int64_t)e * (2 * I + H);
-  float ag[NBG], au[NBG];
-#pragma unroll
-  for (int b = 0; b < NBG; ++b) {
-    ag[b] = al[col0 + 32 * b];
-    au[b] = al[I + col0 + 32 * b];
-  }
+  for (int u = tid; u < I / 2; u += 256)
+    reinterpret_cast<float4*>(s_al)[u] = reinterpret_cast<const float4*>(al)[u];
+  const int cbase = wave * (I / 4);
   __syncthreads();
 
   // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
@@ -306,10 +317,10 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
             u0 = unpack_word(word_of(bq[half][b + 2], 0));
             u1 = unpack_word(word_of(bq[half][b + 3], 0));
           }
-          acc[0][b] = mfma32(af[s2][0], b0, acc[0][b]);
-          acc[1][b] = mfma32(af[s2][1], b0, acc[1][b]);
-          acc[0][b + 1] = mfma32(af[s2][0], b1, acc[0][b + 1]);
-          acc[1][b + 1] = mfma32(af[s2][1], b1, acc[1][b + 1]);
+          acc[0][b] = mfma32(b0, af[s2][0], acc[0][b]);
+          acc[1][b] = mfma32(b0, af[s2][1], acc[1][b]);
+          acc[0][b + 1] = mfma32(b1, af[s2][0], acc[0][b + 1]);
+          acc[1][b + 1] = mfma32(b1, af[s2][1], acc[1][b + 1]);
         }
         bq[half][b] = *reinterpret_cast<const uint4*>(bsrc(b, st1) + 32 * half);
         bq[half][b + 1] = *reinterpret_cast<const uint4*>(bsrc(b + 1, st1) + 32 * half);
@@ -332,58 +343,70 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
     __syncthreads();
   }
 
-  // Epilogue.  Lane holds rows m_j = 8 (j / 4) + 4 kg + j % 4 (j < 16) and
-  // columns col0 + 32 b.
+  // Epilogue.  The weights were the MFMA's first operand, so lane (r32, kg)
+  // holds slot m = r32 and, in register 4i + t of N-subtile b, h column
+  // cbase + 32 b + 8 i + 4 kg + t (cbase = wave I/4): four consecutive columns
+  // per register quad.
+  const int m = r32;
+  const float sx = s_sx[m];
+  const int xsum = s_xsum[m];
   float hv[NBG][16];
-  float rmax[16];
+  float mx = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int m = 8 * (j >> 2) + 4 * kg + (j & 3);
-    const float sx = s_sx[m];
-    const int xsum = s_xsum[m];
-    float mx = 0.f;
+  for (int b = 0; b < NBG; ++b)
 #pragma unroll
-    for (int b = 0; b < NBG; ++b) {
-      const float gv = (float)(128 * acc[0][b][j] + acc[1][b][j] - xsum) * (sx * ag[b]);
-      const float uv = (float)(128 * acc[0][b + NBG][j] + acc[1][b + NBG][j] - xsum) * (sx * au[b]);
-      const float h = silu_fast(gv) * uv;
-      hv[b][j] = h;
-      mx = fmaxf(mx, fabsf(h));
+    for (int i = 0; i < 4; ++i) {
+      const int c = cbase + 32 * b + 8 * i + 4 * kg;
+      const float4 ga = *reinterpret_cast<const float4*>(s_al + c);
+      const float4 ua = *reinterpret_cast<const float4*>(s_al + I + c);
+      const float gs[4] = {ga.x, ga.y, ga.z, ga.w}, us[4] = {ua.x, ua.y, ua.z, ua.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = 4 * i + t;
+        const float gv = (float)(128 * acc[0][b][j] + acc[1][b][j] - xsum) * (sx * gs[t]);
+        const float uv = (float)(128 * acc[0][b + NBG][j] + acc[1][b + NBG][j] - xsum) * (sx * us[t]);
+        const float h = silu_fast(gv) * uv;
+        hv[b][j] = h;
+        mx = fmaxf(mx, fabsf(h));
+      }
     }
-    rmax[j] = group_reduce<32, OpMax>(mx);
+  // the slot's other columns of this wave sit in lane r32 + 32 (the other kg)
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
-  if (r32 == 0)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s_red[wave][8 * (j >> 2) + 4 * kg + (j & 3)] = rmax[j];
+  if (kg == 0) s_red[wave][m] = mx;
   __syncthreads();
-  // h limbs staged in LDS (reusing the x buffers) as [limb][row][I]
+  mx = fmaxf(fmaxf(s_red[0][m], s_red[1][m]), fmaxf(s_red[2][m], s_red[3][m]));
+  const float sc = mx > 0.f ? mx / kQMax : 1.f;
+  const float inv = mx > 0.f ? kQMax / mx : 1.f;
+  // h limbs staged in LDS (reusing the x buffers) as [limb][row][I], 4 bytes at a time
   int8_t* sH = smem;
-  int rsum[16];
+  int qs = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int m = 8 * (j >> 2) + 4 * kg + (j & 3);
-    float mx = 0.f;
+  for (int b = 0; b < NBG; ++b)
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_red[w][m]);
-    const float sc = mx > 0.f ? mx / kQMax : 1.f;
-    const float inv = mx > 0.f ? kQMax / mx : 1.f;
-    int qs = 0;
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hw = 0u, lw = 0u;
 #pragma unroll
-    for (int b = 0; b < NBG; ++b) {
-      const int col = col0 + 32 * b;
-      int q = (int)rintf(hv[b][j] * inv);
-      q = max(-16256, min(16256, q));
-      const int hi = (q + 64) >> 7;
-      sH[m * I + col] = (int8_t)hi;
-      sH[TM * I + m * I + col] = (int8_t)(q - (hi << 7));
-      qs += q;
+      for (int t = 0; t < 4; ++t) {
+        int q = (int)rintf(hv[b][4 * i + t] * inv);
+        q = max(-16256, min(16256, q));
+        const int hi = (q + 64) >> 7;
+        hw |= (uint32_t)(hi & 0xFF) << (8 * t);
+        lw |= (uint32_t)((q - (hi << 7)) & 0xFF) << (8 * t);
+        qs += q;
+      }
+      const int c = cbase + 32 * b + 8 * i + 4 * kg;
+      *reinterpret_cast<uint32_t*>(sH + m * I + c) = hw;
+      *reinterpret_cast<uint32_t*>(sH + TM * I + m * I + c) = lw;
     }
-    rsum[j] = group_reduce_i<32, OpSum>(qs);
-    if (wave == 0 && r32 == 0 && m < np) hs[p0 + m] = sc;
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)qs, (unsigned)qs, false, false);
+    qs = (int)r[0] + (int)r[1];
   }
-  if (r32 == 0)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s_redi[wave][8 * (j >> 2) + 4 * kg + (j & 3)] = rsum[j];
+  if (kg == 0) s_redi[wave][m] = qs;
+  if (wave == 0 && kg == 0 && m < np) hs[p0 + m] = sc;
   __syncthreads();
   if (tid < np) {
     int tot = 0;
@@ -420,7 +443,7 @@ __global__ __launch_bounds__(256) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, float* __restrict__ y) {
+    const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y) {
   constexpr int NQ = I / 128;           // 16-byte pieces per lane and row
   constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
   constexpr int CH = 128 * NBW;         // outputs per chunk
@@ -473,7 +496,7 @@ __global__ __launch_bounds__(256) void k_down_mfma(
   const bool live = r32 < np;
   const float sc = live ? hs[p0 + r32] : 0.f;
   const int hsum = live ? reinterpret_cast<const int*>(hs)[Tk + p0 + r32] : 0;
-  float* yrow = y + (int64_t)(p0 + r32) * H;
+  uint16_t* yrow = y + (int64_t)(p0 + r32) * H;
   __syncthreads();
   const int8_t* sa = &sA[0][r32][64 * kg];
 
@@ -501,7 +524,7 @@ __global__ __launch_bounds__(256) void k_down_mfma(
       for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
     }
     // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk:
-    // y[slot][o] = a_d[o] * s * (128 C_hi + C_lo - rowsum)
+    // y[slot][o] = a_d[o] * s * (128 C_hi + C_lo - rowsum), stored as fp16
     if (live) {
 #pragma unroll
       for (int b = 0; b < NBW; ++b)
@@ -509,12 +532,14 @@ __global__ __launch_bounds__(256) void k_down_mfma(
         for (int i = 0; i < 4; ++i) {
           const int o = c * CH + 32 * (NBW * wave + b) + 8 * i + 4 * kg;
           const float4 a = *reinterpret_cast<const float4*>(s_ad + o);
-          float4 v;
-          v.x = a.x * sc * (float)(128 * acc[0][b][4 * i] + acc[1][b][4 * i] - hsum);
-          v.y = a.y * sc * (float)(128 * acc[0][b][4 * i + 1] + acc[1][b][4 * i + 1] - hsum);
-          v.z = a.z * sc * (float)(128 * acc[0][b][4 * i + 2] + acc[1][b][4 * i + 2] - hsum);
-          v.w = a.w * sc * (float)(128 * acc[0][b][4 * i + 3] + acc[1][b][4 * i + 3] - hsum);
-          *reinterpret_cast<float4*>(yrow + o) = v;
+          const float v0 = a.x * sc * (float)(128 * acc[0][b][4 * i] + acc[1][b][4 * i] - hsum);
+          const float v1 =
+              a.y * sc * (float)(128 * acc[0][b][4 * i + 1] + acc[1][b][4 * i + 1] - hsum);
+          const float v2 =
+              a.z * sc * (float)(128 * acc[0][b][4 * i + 2] + acc[1][b][4 * i + 2] - hsum);
+          const float v3 =
+              a.w * sc * (float)(128 * acc[0][b][4 * i + 3] + acc[1][b][4 * i + 3] - hsum);
+          *reinterpret_cast<uint2*>(yrow + o) = make_uint2(pack_f16(v0, v1), pack_f16(v2, v3));
         }
     }
   }
@@ -522,34 +547,48 @@ __global__ __launch_bounds__(256) void k_down_mfma(
 
 // ---- weighted combine ---------------------------------------------------------------
 
-// out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order.
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
+// out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order
+// in fp32; a thread owns 8 consecutive outputs (one 16-byte fp16 load per slot).
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const float* __restrict__ gate,
                                                  const int32_t* __restrict__ slot_pos, int H,
                                                  int k, float* out, const float* resid,
                                                  float* __restrict__ delta) {
   const int64_t t = blockIdx.x;
-  const int o = (blockIdx.y * 256 + threadIdx.x) * 4;
+  const int o = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (o >= H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const float gj = gate[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)slot_pos[t * k + j] * H + o);
-    acc.x = fmaf(gj, v.x, acc.x);
-    acc.y = fmaf(gj, v.y, acc.y);
-    acc.z = fmaf(gj, v.z, acc.z);
-    acc.w = fmaf(gj, v.w, acc.w);
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)slot_pos[t * k + j] * H + o);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(gj, f16_lo(w[q]), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(gj, f16_hi(w[q]), acc[2 * q + 1]);
+    }
   }
   const int64_t off = t * H + o;
-  if (delta) *reinterpret_cast<float4*>(delta + off) = acc;
-  if (resid) {
-    const float4 r = *reinterpret_cast<const float4*>(resid + off);
-    acc.x += r.x;
-    acc.y += r.y;
-    acc.z += r.z;
-    acc.w += r.w;
+  float4 a0 = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  float4 a1 = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (delta) {
+    *reinterpret_cast<float4*>(delta + off) = a0;
+    *reinterpret_cast<float4*>(delta + off + 4) = a1;
   }
-  *reinterpret_cast<float4*>(out + off) = acc;
+  if (resid) {
+    const float4 r0 = *reinterpret_cast<const float4*>(resid + off);
+    const float4 r1 = *reinterpret_cast<const float4*>(resid + off + 4);
+    a0.x += r0.x;
+    a0.y += r0.y;
+    a0.z += r0.z;
+    a0.w += r0.w;
+    a1.x += r1.x;
+    a1.y += r1.y;
+    a1.z += r1.z;
+    a1.w += r1.w;
+  }
+  *reinterpret_cast<float4*>(out + off) = a0;
+  *reinterpret_cast<float4*>(out + off + 4) = a1;
 }
 
 }  // namespace
@@ -603,7 +642,7 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf
     default:
       return hipErrorNotSupported;
   }
-  launch("combine", k_combine, dim3((unsigned)T, (unsigned)((d.H + 1023) / 1024)), 256, 0, s, ws.y,
+  launch("combine", k_combine, dim3((unsigned)T, (unsigned)((d.H + 2047) / 2048)), 256, 0, s, ws.y,
          ws.gate, ws.slot_pos, d.H, d.k, out, resid, delta);
   return hipGetLastError();
 }
