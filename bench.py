@@ -71,6 +71,43 @@ def prefill_ops(kernel, H, k, I, T):
     return {"gateup_mfma": 2 * T * k * 2 * H * I, "down_mfma": 2 * T * k * H * I}.get(kernel)
 
 
+# ---- measured HBM traffic --------------------------------------------------------------
+
+# HBM bytes per launch of a kernel, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE; summaries in profiles/*_traffic.md), FETCH_SIZE
+# scaled by the factor a plain device copy of known size gives (2.0 here: the
+# counter formula books a 128-byte request as 64 bytes) and WRITE_SIZE by 1.0.
+# An entry holds only while the kernel's sources hash as recorded; otherwise the
+# kernel has changed since the counters were taken and the traffic is unknown.
+TRAFFIC = {
+    "combine": {"bytes": 168827973, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+    "d1m_down": {"bytes": 4617793, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+    "d1m_gateup": {"bytes": 6567871, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+    "d1q_router": {"bytes": 2252634, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+    "down_mfma": {"bytes": 243229061, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+    "gateup_mfma": {"bytes": 310170764, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+    "quant_x": {"bytes": 33757477, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+    "route_block": {"bytes": 4844101, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
+    "router_mfma": {"bytes": 37816408, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
+}
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "ternary_weight_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    ent = TRAFFIC.get(kernel)
+    if ent is None or source_digest(ent["sources"]) != ent["digest"]:
+        return None
+    return ent["bytes"]
+
+
 # ---- set-up ---------------------------------------------------------------------------
 
 def build_layers(w, torch, N, S):
@@ -234,7 +271,7 @@ def bench_decode(args, torch, N, S):
         config=dict(workload="decode_stack", hidden=H, experts=E, top_k=k, inter=I, layers=L,
                     batch=1, tokens_staged=n_staged, step="one captured HIP graph per token"),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None, kernel=dom,
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic_for(dom), kernel=dom,
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=dom_avg_s * 1e6),
         step_roofline=dict(algorithmic_bytes_per_step=bytes_tok, achieved_gbs=step_gbs,
                            frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
@@ -266,7 +303,8 @@ def bench_prefill(args, torch, N, S):
     dom_avg_s = prof[dom][1] * 1e-3
     if ops:
         roof = dict(bound="mfma", achieved=ops / dom_avg_s / 1e12, peak=INT8_PEAK_TOPS,
-                    unit="TOP/s", frac=ops / dom_avg_s / 1e12 / INT8_PEAK_TOPS, traffic=None,
+                    unit="TOP/s", frac=ops / dom_avg_s / 1e12 / INT8_PEAK_TOPS,
+                    traffic=traffic_for(dom),
                     kernel=dom, algorithmic_int8_ops_per_launch=ops,
                     avg_launch_us=dom_avg_s * 1e6)
     else:
