@@ -428,27 +428,31 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
 
 // ---- down projection ----------------------------------------------------------------
 
-// One block (4 waves, one per SIMD): one M tile (TM = 32 slots of one expert)
-// x all H outputs, in chunks of 128 NBW outputs: wave w owns NBW N-subtiles of
-// 32 outputs per chunk.  The tile's h limbs (all of K = I) sit in LDS for the
-// whole block.  The weights are the MFMA's first operand (rows = outputs) and
-// h the second (columns = slots), so a lane ends with 4 consecutive outputs
-// of one slot per register quad and writes them as one 16-byte store.  The
-// weight registers of 128 codes are refilled with the next chunk right after
-// their last step, a full chunk ahead of their next use.
+// One block (NWV waves): one M tile (TM = 32 slots of one expert) x all H
+// outputs, in chunks of 32 NBW NWV outputs: wave w owns NBW N-subtiles of 32
+// outputs per chunk.  With 8 waves of 2 N-subtiles, two waves share each
+// SIMD and cover each other's waits.  The tile's h limbs (all of K = I) sit in
+// LDS for the whole block.  The weights are the MFMA's first operand (rows =
+// outputs) and h the second (columns = slots), so a lane ends with 4
+// consecutive outputs of one slot per register quad and writes them with one
+// store.  The weight registers of 128 codes are refilled with the next chunk
+// right after their last step, a full chunk ahead of their next use.  The lo
+// accumulators start at -rowsum(q) of the lane's slot (the offset-code term).
 // K order: MFMA step s uses word 8 (s / 4) + 4 kg + s % 4 of the row (I/16
 // words), so a lane holds 16 contiguous bytes per 128 codes of each row.
-template <int I, int NBW>
-__global__ __launch_bounds__(256) void k_down_mfma(
+template <int I, int NBW, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y) {
+  constexpr int NTH = 64 * NWV;
   constexpr int NQ = I / 128;           // 16-byte pieces per lane and row
   constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
-  constexpr int CH = 128 * NBW;         // outputs per chunk
+  constexpr int CH = 32 * NBW * NWV;    // outputs per chunk
   __shared__ __align__(16) int8_t sA[2][TM][ROWB];
-  extern __shared__ __align__(16) float s_ad[];  // a_d of the expert: H floats
+  // dynamic LDS: a_d of the expert (H floats), then one fp16 output patch per wave
+  extern __shared__ __align__(16) float s_ad[];
   const int tile = xcd_tile(blockIdx.x, *n_tiles);
   if (tile < 0) return;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
@@ -472,41 +476,53 @@ __global__ __launch_bounds__(256) void k_down_mfma(
   // h limbs of the tile's slots: 2 * TM rows of I bytes; rows past np are zero.
   // All loads are issued before the first LDS store.
   constexpr int SEGR = I / 16;
-  constexpr int NHU = 2 * TM * SEGR / 256;  // 16-byte units per thread
+  constexpr int NHU = 2 * TM * SEGR / NTH;  // 16-byte units per thread
+  static_assert(NHU >= 1, "h units");
   uint4 hv[NHU];
 #pragma unroll
   for (int i = 0; i < NHU; ++i) {
-    const int u = tid + 256 * i;
+    const int u = tid + NTH * i;
     const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
     hv[i] = r < np ? *reinterpret_cast<const uint4*>(hq + (int64_t)(p0 + r) * 2 * I +
                                                      (int64_t)limb * I + 16 * sg)
                    : make_uint4(0u, 0u, 0u, 0u);
   }
-#pragma unroll
-  for (int i = 0; i < NHU; ++i) {
-    const int u = tid + 256 * i;
-    const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
-    *reinterpret_cast<uint4*>(&sA[limb][r][16 * sg]) = hv[i];
-  }
   // a_d through LDS: the epilogue's reads then never wait behind the weight
-  // loads in flight for the next chunk
-  for (int u = tid; u < H / 4; u += 256)
-    reinterpret_cast<float4*>(s_ad)[u] = reinterpret_cast<const float4*>(ad)[u];
+  // loads in flight for the next chunk.  H / 4 <= 4 NTH.
+  float4 av[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    av[i] = reinterpret_cast<const float4*>(ad)[min(tid + NTH * i, H / 4 - 1)];
   // this lane's slot (the accumulator column) and its scale and limb row sum
   const bool live = r32 < np;
   const float sc = live ? hs[p0 + r32] : 0.f;
   const int hsum = live ? reinterpret_cast<const int*>(hs)[Tk + p0 + r32] : 0;
-  uint16_t* yrow = y + (int64_t)(p0 + r32) * H;
+#pragma unroll
+  for (int i = 0; i < NHU; ++i) {
+    const int u = tid + NTH * i;
+    const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
+    *reinterpret_cast<uint4*>(&sA[limb][r][16 * sg]) = hv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (tid + NTH * i < H / 4) reinterpret_cast<float4*>(s_ad)[tid + NTH * i] = av[i];
   __syncthreads();
   const int8_t* sa = &sA[0][r32][64 * kg];
+  constexpr int YROW = 64 * NBW + 16;  // padded row of a wave's output patch (bytes)
+  int8_t* sY = reinterpret_cast<int8_t*>(s_ad + H) + wave * 32 * YROW;
 
   for (int c = 0; c < nch; ++c) {
+    // keeps the A-operand LDS reads inside the loop (hoisted, they would hold
+    // 128 registers for the whole block and halve the blocks a CU can run)
+    asm volatile("" ::: "memory");
     const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
     v16i acc[2][NBW];
 #pragma unroll
-    for (int l = 0; l < 2; ++l)
+    for (int b = 0; b < NBW; ++b) {
+      acc[0][b] = v16i{};
 #pragma unroll
-      for (int b = 0; b < NBW; ++b) acc[l][b] = v16i{};
+      for (int j = 0; j < 16; ++j) acc[1][b][j] = -hsum;
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -524,23 +540,29 @@ __global__ __launch_bounds__(256) void k_down_mfma(
       for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
     }
     // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk:
-    // y[slot][o] = a_d[o] * s * (128 C_hi + C_lo - rowsum), stored as fp16
-    if (live) {
+    // y[slot][o] = a_d[o] * s * (128 C_hi + C_lo) as fp16, first into the wave's
+    // LDS patch [slot][32 NBW outputs], then out in whole 128-byte lines
 #pragma unroll
-      for (int b = 0; b < NBW; ++b)
+    for (int b = 0; b < NBW; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int o = c * CH + 32 * (NBW * wave + b) + 8 * i + 4 * kg;
-          const float4 a = *reinterpret_cast<const float4*>(s_ad + o);
-          const float v0 = a.x * sc * (float)(128 * acc[0][b][4 * i] + acc[1][b][4 * i] - hsum);
-          const float v1 =
-              a.y * sc * (float)(128 * acc[0][b][4 * i + 1] + acc[1][b][4 * i + 1] - hsum);
-          const float v2 =
-              a.z * sc * (float)(128 * acc[0][b][4 * i + 2] + acc[1][b][4 * i + 2] - hsum);
-          const float v3 =
-              a.w * sc * (float)(128 * acc[0][b][4 * i + 3] + acc[1][b][4 * i + 3] - hsum);
-          *reinterpret_cast<uint2*>(yrow + o) = make_uint2(pack_f16(v0, v1), pack_f16(v2, v3));
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int ol = 32 * b + 8 * i + 4 * kg;  // output within the wave's part of the chunk
+        const float4 a = *reinterpret_cast<const float4*>(s_ad + c * CH + 32 * NBW * wave + ol);
+        const float v0 = (a.x * sc) * (float)(128 * acc[0][b][4 * i] + acc[1][b][4 * i]);
+        const float v1 = (a.y * sc) * (float)(128 * acc[0][b][4 * i + 1] + acc[1][b][4 * i + 1]);
+        const float v2 = (a.z * sc) * (float)(128 * acc[0][b][4 * i + 2] + acc[1][b][4 * i + 2]);
+        const float v3 = (a.w * sc) * (float)(128 * acc[0][b][4 * i + 3] + acc[1][b][4 * i + 3]);
+        *reinterpret_cast<uint2*>(sY + r32 * YROW + 2 * ol) =
+            make_uint2(pack_f16(v0, v1), pack_f16(v2, v3));
+      }
+    // the patch is 32 rows of 64 NBW bytes; 16-byte pieces, whole rows per instruction
+    constexpr int PPR = 4 * NBW;  // pieces per row
+#pragma unroll
+    for (int k2 = 0; k2 < 32 * PPR / 64; ++k2) {
+      const int r = k2 * (64 / PPR) + lane / PPR, pc = lane % PPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(sY + r * YROW + 16 * pc);
+      if (r < np)
+        *reinterpret_cast<uint4*>(y + (int64_t)(p0 + r) * H + c * CH + 32 * NBW * wave + 8 * pc) = v;
     }
   }
 }
@@ -619,12 +641,9 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf
   };
   auto down = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
-    if (d.H % 512 == 0)
-      launch("down_mfma", k_down_mfma<I_, 4>, nt, 256, 4 * d.H, s, ws.hq, ws.hs, Tk, d.H, packed, alpha,
-             ws.offsets, ws.tiles, ws.n_tiles, ws.y);
-    else
-      launch("down_mfma", k_down_mfma<I_, 2>, nt, 256, 4 * d.H, s, ws.hq, ws.hs, Tk, d.H, packed, alpha,
-             ws.offsets, ws.tiles, ws.n_tiles, ws.y);
+    // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
+    launch("down_mfma", k_down_mfma<I_, 2, 4>, nt, 256, 4 * d.H + 4 * 32 * (64 * 2 + 16), s,
+           ws.hq, ws.hs, Tk, d.H, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, ws.y);
   };
   switch (d.I) {
     case 128:
