@@ -59,7 +59,7 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->part = (int32_t*)take(sizeof(int32_t) * 4 * d.E);
   ws->xs = (float*)take(sizeof(float) * 3 * T);
   ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
-  ws->hs = (float*)take(sizeof(float) * 2 * Tk);
+  ws->hs = (float*)take(sizeof(float) * 4 * Tk);
   ws->y = (uint16_t*)take(sizeof(uint16_t) * Tk * d.H);
   ws->xb = (uint16_t*)take(sizeof(uint16_t) * 2 * T * d.H);
   ws->wb = (uint16_t*)take(sizeof(uint16_t) * 2 * d.E * d.H);

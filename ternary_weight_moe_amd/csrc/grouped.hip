@@ -180,12 +180,14 @@ __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-// One block (4 waves, one per SIMD): one M tile (TM = 32 slots of one expert)
-// x all I columns of h, i.e. 2I weight rows.  Wave w owns h columns
-// [w I/4, (w+1) I/4): gate N-subtiles b < NBG and up N-subtiles b >= NBG (32
-// columns each) with identical (row, column) positions per lane, so
-// silu(g)*u is formed in registers.  The accumulators (2 limbs x 2 NBG
-// N-subtiles x 16) fill the accumulation registers.
+// One block (4 waves): one M tile (TM = 32 slots of one expert) x one of NS
+// column parts of h, i.e. 2I/NS weight rows.  Wave w owns h columns
+// [cb + w I/(4 NS), cb + (w+1) I/(4 NS)) of part cb: gate N-subtiles b < NBG
+// and up N-subtiles b >= NBG (32 columns each) with identical (row, column)
+// positions per lane, so silu(g)*u is formed in registers.  With NS = 2 the
+// accumulators (2 limbs x 2 NBG N-subtiles x 16) take 128 registers and two
+// blocks share a CU; h is then re-coded with one scale per slot and part, and
+// the down projection sums the parts' contributions with their own scales.
 //
 // Weights go straight from global memory into B operands: per N-subtile and
 // stage each lane holds two 16-byte pieces of one weight row (one load
@@ -193,20 +195,21 @@ __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
 // stage right after their last use, a full stage ahead.  The x limbs
 // (gathered through sorted_token) pass through registers into a
 // double-buffered LDS tile, two stages ahead; rows are padded to 272 bytes.
-template <int I>
-__global__ __launch_bounds__(256) void k_gateup_mfma(
+template <int I, int NS>
+__global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     int8_t* __restrict__ hq, float* __restrict__ hs, int64_t Tk) {
   constexpr int NW = 4;
-  constexpr int NBG = I / 128;          // gate N-subtiles per wave (and as many up)
+  constexpr int IP = I / NS;            // h columns of the block's part
+  constexpr int NBG = IP / 128;         // gate N-subtiles per wave (and as many up)
   constexpr int NB = 2 * NBG;
   constexpr int KS = 256;               // codes per stage (8 MFMA steps)
   constexpr int ROWB = KS + 16;         // padded LDS row: one limb of one slot
   constexpr int ABUF = 2 * TM * ROWB;   // one stage of x limbs
-  constexpr int HBYTES = 2 * TM * I;    // h-limb staging in the epilogue
+  constexpr int HBYTES = 2 * TM * IP;   // h-limb staging in the epilogue
   constexpr int SMEM = 2 * ABUF > HBYTES ? 2 * ABUF : HBYTES;
   static_assert(TM == 32 && NB % 2 == 0, "tile shape");
   __shared__ __align__(16) int8_t smem[SMEM];
@@ -215,7 +218,9 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
   __shared__ __align__(16) float s_al[2 * I];
-  const int tile = xcd_tile(blockIdx.x, *n_tiles);
+  // the NS parts of a tile: consecutive blocks of one XCD (they share the x tile)
+  const int local = blockIdx.x >> 3, part = local % NS;
+  const int tile = xcd_tile(8 * (local / NS) + (blockIdx.x & 7), *n_tiles);
   if (tile < 0) return;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int p0 = offsets[e] + m0;
@@ -230,8 +235,9 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
   }
   const int rowb = H / 4;
   const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
-  const int col0 = wave * (I / 4) + r32;
-  const uint8_t* brow = We + (int64_t)col0 * rowb + 16 * kg;
+  const int pbase = part * IP;             // first h column of the part
+  const int cbase = pbase + wave * (IP / 4);  // first h column of the wave
+  const uint8_t* brow = We + (int64_t)(cbase + r32) * rowb + 16 * kg;
   auto bsrc = [&](int b, int st) -> const uint8_t* {
     return brow + (b < NBG ? 0 : (int64_t)I * rowb) + (int64_t)(32 * (b % NBG)) * rowb + st * 64;
   };
@@ -239,7 +245,6 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
   const float* al = alpha + (int64_t)e * (2 * I + H);
   for (int u = tid; u < I / 2; u += 256)
     reinterpret_cast<float4*>(s_al)[u] = reinterpret_cast<const float4*>(al)[u];
-  const int cbase = wave * (I / 4);
   __syncthreads();
 
   // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
   mx = fmaxf(fmaxf(s_red[0][m], s_red[1][m]), fmaxf(s_red[2][m], s_red[3][m]));
   const float sc = mx > 0.f ? mx / kQMax : 1.f;
   const float inv = mx > 0.f ? kQMax / mx : 1.f;
-  // h limbs staged in LDS (reusing the x buffers) as [limb][row][I], 4 bytes at a time
+  // h limbs of the part staged in LDS (reusing the x buffers) as [limb][row][IP]
   int8_t* sH = smem;
   int qs = 0;
 #pragma unroll
@@ -397,32 +402,34 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
         lw |= (uint32_t)((q - (hi << 7)) & 0xFF) << (8 * t);
         qs += q;
       }
-      const int c = cbase + 32 * b + 8 * i + 4 * kg;
-      *reinterpret_cast<uint32_t*>(sH + m * I + c) = hw;
-      *reinterpret_cast<uint32_t*>(sH + TM * I + m * I + c) = lw;
+      const int c = cbase - pbase + 32 * b + 8 * i + 4 * kg;
+      *reinterpret_cast<uint32_t*>(sH + m * IP + c) = hw;
+      *reinterpret_cast<uint32_t*>(sH + TM * IP + m * IP + c) = lw;
     }
   {
     const auto r = __builtin_amdgcn_permlane32_swap((unsigned)qs, (unsigned)qs, false, false);
     qs = (int)r[0] + (int)r[1];
   }
   if (kg == 0) s_redi[wave][m] = qs;
-  if (wave == 0 && kg == 0 && m < np) hs[p0 + m] = sc;
+  // hs: [part][scale | limb row sum (int bits)][slot]
+  if (wave == 0 && kg == 0 && m < np) hs[2 * part * Tk + p0 + m] = sc;
   __syncthreads();
   if (tid < np) {
     int tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += s_redi[w][tid];
-    reinterpret_cast<int*>(hs)[Tk + p0 + tid] = tot;
+    reinterpret_cast<int*>(hs)[(2 * part + 1) * Tk + p0 + tid] = tot;
   }
-  // rows [0, np) of both limbs to hq[slot][limb][I], 16 bytes per thread
-  constexpr int segs_row = I / 16;
+  // rows [0, np) of both limbs to hq[slot][limb][I] (the part's columns), 16 bytes per thread
+  constexpr int segs_row = IP / 16;
 #pragma unroll
   for (int c0 = 0; c0 < 2 * TM * segs_row; c0 += 256) {
     const int c = c0 + tid;
     const int limb = c / (TM * segs_row), r = (c / segs_row) % TM, seg = c % segs_row;
     if (r < np)
-      *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + r) * 2 * I + (int64_t)limb * I + seg * 16) =
-          *reinterpret_cast<const uint4*>(sH + limb * TM * I + r * I + seg * 16);
+      *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + r) * 2 * I + (int64_t)limb * I + pbase +
+                                seg * 16) =
+          *reinterpret_cast<const uint4*>(sH + limb * TM * IP + r * IP + seg * 16);
   }
 }
 
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(
 // accumulators start at -rowsum(q) of the lane's slot (the offset-code term).
 // K order: MFMA step s uses word 8 (s / 4) + 4 kg + s % 4 of the row (I/16
 // words), so a lane holds 16 contiguous bytes per 128 codes of each row.
-template <int I, int NBW, int NWV>
+template <int I, int NBW, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
@@ -493,10 +500,15 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     av[i] = reinterpret_cast<const float4*>(ad)[min(tid + NTH * i, H / 4 - 1)];
-  // this lane's slot (the accumulator column) and its scale and limb row sum
+  // this lane's slot (the accumulator column): scale and limb row sum per h part
   const bool live = r32 < np;
-  const float sc = live ? hs[p0 + r32] : 0.f;
-  const int hsum = live ? reinterpret_cast<const int*>(hs)[Tk + p0 + r32] : 0;
+  float sc[NS];
+  int hsum[NS];
+#pragma unroll
+  for (int h2 = 0; h2 < NS; ++h2) {
+    sc[h2] = live ? hs[2 * h2 * Tk + p0 + r32] : 0.f;
+    hsum[h2] = live ? reinterpret_cast<const int*>(hs)[(2 * h2 + 1) * Tk + p0 + r32] : 0;
+  }
 #pragma unroll
   for (int i = 0; i < NHU; ++i) {
     const int u = tid + NTH * i;
@@ -516,15 +528,18 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     // 128 registers for the whole block and halve the blocks a CU can run)
     asm volatile("" ::: "memory");
     const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
-    v16i acc[2][NBW];
+    v16i acc[NS][2][NBW];  // [h part][limb][N-subtile]
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) {
-      acc[0][b] = v16i{};
+    for (int h2 = 0; h2 < NS; ++h2)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[1][b][j] = -hsum;
-    }
+      for (int b = 0; b < NBW; ++b) {
+        acc[h2][0][b] = v16i{};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[h2][1][b][j] = -hsum[h2];
+      }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
+      const int h2 = q / (NQ / NS);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const v4i a0 = *reinterpret_cast<const v4i*>(sa + 128 * q + 16 * s4);
@@ -532,15 +547,15 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
           const v4i wf = unpack_word(word_of(bq[b][q], s4));
-          acc[0][b] = mfma32(wf, a0, acc[0][b]);
-          acc[1][b] = mfma32(wf, a1, acc[1][b]);
+          acc[h2][0][b] = mfma32(wf, a0, acc[h2][0][b]);
+          acc[h2][1][b] = mfma32(wf, a1, acc[h2][1][b]);
         }
       }
 #pragma unroll
       for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
     }
     // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk:
-    // y[slot][o] = a_d[o] * s * (128 C_hi + C_lo) as fp16, first into the wave's
+    // y[slot][o] = a_d[o] * sum_parts s * (128 C_hi + C_lo) as fp16, first into the wave's
     // LDS patch [slot][32 NBW outputs], then out in whole 128-byte lines
 #pragma unroll
     for (int b = 0; b < NBW; ++b)
@@ -548,10 +563,14 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
       for (int i = 0; i < 4; ++i) {
         const int ol = 32 * b + 8 * i + 4 * kg;  // output within the wave's part of the chunk
         const float4 a = *reinterpret_cast<const float4*>(s_ad + c * CH + 32 * NBW * wave + ol);
-        const float v0 = (a.x * sc) * (float)(128 * acc[0][b][4 * i] + acc[1][b][4 * i]);
-        const float v1 = (a.y * sc) * (float)(128 * acc[0][b][4 * i + 1] + acc[1][b][4 * i + 1]);
-        const float v2 = (a.z * sc) * (float)(128 * acc[0][b][4 * i + 2] + acc[1][b][4 * i + 2]);
-        const float v3 = (a.w * sc) * (float)(128 * acc[0][b][4 * i + 3] + acc[1][b][4 * i + 3]);
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h2 = 0; h2 < NS; ++h2)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            v[t] = fmaf(sc[h2], (float)(128 * acc[h2][0][b][4 * i + t] + acc[h2][1][b][4 * i + t]),
+                        v[t]);
+        const float v0 = a.x * v[0], v1 = a.y * v[1], v2 = a.z * v[2], v3 = a.w * v[3];
         *reinterpret_cast<uint2*>(sY + r32 * YROW + 2 * ol) =
             make_uint2(pack_f16(v0, v1), pack_f16(v2, v3));
       }
@@ -634,15 +653,18 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf
   (void)x_bf16;
   const int64_t Tk = T * d.k;
   const unsigned nt = (unsigned)((max_tiles(d, T) + 7) & ~7);  // whole rounds of 8 XCDs
+  // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
   auto gateup = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
-    launch("gateup_mfma", k_gateup_mfma<I_>, nt, 256, 0, s, ws.xq, ws.xs, (int)T, d.H, packed,
-           alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
+    constexpr int NS_ = I_ >= 512 ? 2 : 1;
+    launch("gateup_mfma", k_gateup_mfma<I_, NS_>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T, d.H,
+           packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
   };
   auto down = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
+    constexpr int NS_ = I_ >= 512 ? 2 : 1;
     // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
-    launch("down_mfma", k_down_mfma<I_, 2, 4>, nt, 256, 4 * d.H + 4 * 32 * (64 * 2 + 16), s,
+    launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt, 256, 4 * d.H + 4 * 32 * (64 * 2 + 16), s,
            ws.hq, ws.hs, Tk, d.H, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, ws.y);
   };
   switch (d.I) {

@@ -34,7 +34,7 @@ struct Workspace {
   int32_t* part;        // [E, 4]    per-router-block partial limb sums (one-token path)
   float* xs;            // [3T]      scale of x's limbs | limb row sum (int bits) | 1/rms(x)
   int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
-  float* hs;            // [2, T*k]  scale of h's limbs per slot | limb row sum (int bits)
+  float* hs;            // [2, 2, T*k] per h column part: limb scale per slot | limb row sum (int bits)
   uint16_t* y;          // [T*k, H]  fp16 expert outputs before the combine (grouped path)
   uint16_t* xb;         // [2, T, H] bf16 hi/lo planes of fp32 x (large-T router)
   uint16_t* wb;         // [2, E, H] bf16 hi/lo planes of the router (large-T router)
