@@ -74,42 +74,43 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
 
 // ---- x -> two int8 limbs, per-token scale, row sum of q, 1/rms ---------------
 
-// One wave per token, 4 tokens per block; lane holds H/64 contiguous values
-// (H % 256 == 0), loaded 4 at a time.
+// One wave per token, 4 tokens per block.  The row is read in 16-byte pieces
+// spread over the wave (piece p of a row goes to lane p % 64), so every load
+// instruction covers up to 1 KB of contiguous row; a lane holds its pieces of 8
+// (bf16) or 4 (fp32) values.  H % 256 == 0.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int T, int H,
                                                  int norm, int8_t* __restrict__ xq,
                                                  float* __restrict__ xs) {
-  constexpr int MAXP = 64;  // values per lane at H = 4096
+  constexpr int VPP = BF16 ? 8 : 4;   // values per 16-byte piece
+  constexpr int MAXN = 64 / VPP;      // pieces per lane at H = 4096
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int per = H / 64;
-  const int64_t base = (int64_t)t * H + (int64_t)lane * per;
-  float v[MAXP];
+  const int npr = H / VPP;            // pieces per row
+  const int npl = (npr + 63) / 64;    // pieces per lane (the last may be partial)
+  float v[MAXN][VPP] = {};
   float amax = 0.f, ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXP; i += 4) {
-    if (i < per) {
-      float f[4];
-      if constexpr (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + base + i);
-        f[0] = __uint_as_float(u.x << 16);
-        f[1] = __uint_as_float(u.x & 0xFFFF0000u);
-        f[2] = __uint_as_float(u.y << 16);
-        f[3] = __uint_as_float(u.y & 0xFFFF0000u);
-      } else {
-        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base + i);
-        f[0] = a.x;
-        f[1] = a.y;
-        f[2] = a.z;
-        f[3] = a.w;
-      }
+  for (int i = 0; i < MAXN; ++i) {
+    if (i < npl && 64 * i + lane < npr) {
+      const int64_t e0 = (int64_t)t * H + (int64_t)(64 * i + lane) * VPP;
+      const uint4 u = BF16 ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + e0)
+                           : *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + e0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v[i + q] = f[q];
-        amax = fmaxf(amax, fabsf(f[q]));
-        ss = fmaf(f[q], f[q], ss);
+        if constexpr (BF16) {
+          v[i][2 * q] = __uint_as_float(w[q] << 16);
+          v[i][2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        } else {
+          v[i][q] = __uint_as_float(w[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < VPP; ++q) {
+        amax = fmaxf(amax, fabsf(v[i][q]));
+        ss = fmaf(v[i][q], v[i][q], ss);
       }
     }
   }
@@ -117,25 +118,31 @@ __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int
   ss = wave_sum_f(ss);
   const float scale = amax > 0.f ? amax / kQMax : 1.f;
   const float inv = amax > 0.f ? kQMax / amax : 1.f;
-  int8_t* hi_row = xq + (int64_t)t * 2 * H + lane * per;
+  int8_t* hi_row = xq + (int64_t)t * 2 * H;
   int8_t* lo_row = hi_row + H;
   int qsum = 0;
 #pragma unroll
-  for (int i = 0; i < MAXP; i += 4) {
-    if (i < per) {
-      uint32_t hw = 0u, lw = 0u;
+  for (int i = 0; i < MAXN; ++i) {
+    if (i < npl && 64 * i + lane < npr) {
+      uint32_t hw[VPP / 4] = {}, lw[VPP / 4] = {};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int qq = (int)rintf(v[i + q] * inv);
+      for (int q = 0; q < VPP; ++q) {
+        int qq = (int)rintf(v[i][q] * inv);
         qq = max(-16256, min(16256, qq));
         const int hi = (qq + 64) >> 7;
         const int lo = qq - (hi << 7);
-        hw |= (uint32_t)(hi & 0xFF) << (8 * q);
-        lw |= (uint32_t)(lo & 0xFF) << (8 * q);
+        hw[q >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (q & 3));
+        lw[q >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (q & 3));
         qsum += qq;
       }
-      *reinterpret_cast<uint32_t*>(hi_row + i) = hw;
-      *reinterpret_cast<uint32_t*>(lo_row + i) = lw;
+      const int c0 = (64 * i + lane) * VPP;
+      if constexpr (VPP == 8) {
+        *reinterpret_cast<uint2*>(hi_row + c0) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(lo_row + c0) = make_uint2(lw[0], lw[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(hi_row + c0) = hw[0];
+        *reinterpret_cast<uint32_t*>(lo_row + c0) = lw[0];
+      }
     }
   }
   qsum = wave_sum_i(qsum);
