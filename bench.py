@@ -162,6 +162,26 @@ def cpu_baseline_decode(w, budget_s):
                        f"({t_used:.1f} s of oracle time)")
 
 
+def cpu_baseline_batched(w, budget_s):
+    """The oracle on a bounded sample of the batched workload: groups of 8 of the
+    step's tokens through the whole stack until the budget is spent; tok/s."""
+    import oracle
+    from ternary_weight_moe_amd import synth as S
+    L = oracle_layers(w)
+    x_all = S.x_as_f32(w, S.gen_x(w, w.n_tokens)).astype(np.float64)
+    n, t_used = 0, 0.0
+    while t_used < budget_s and n < w.n_tokens:
+        t0 = time.perf_counter()
+        oracle.moe_stack(x_all[n:n + 8], [l["Wr"] for l in L], [l["bias"] for l in L],
+                         [l["packed"] for l in L], [l["alpha"] for l in L], k=w.top_k,
+                         inter=w.inter, keep_logits=False, keep_delta=False)
+        t_used += time.perf_counter() - t0
+        n += 8
+    return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} of the {w.n_tokens} tokens of one step, 8 per call, "
+                       f"{w.n_layers} layers ({t_used:.1f} s of oracle time)")
+
+
 def cpu_baseline_prefill(w, budget_s):
     """The oracle on a bounded sample of the prefill workload: token batches of
     the same layer until the time budget is spent; tok/s on this host."""
@@ -279,6 +299,42 @@ def bench_decode(args, torch, N, S):
     ), w
 
 
+def bench_batched(args, torch, N, S):
+    """Batched decode: 64 tokens per step through the 24-layer stack, router logits
+    biased so that expert popularity is Zipf-skewed (skewed groups, empty
+    experts).  A step is one call of maple_moe_stack_forward on 64 tokens."""
+    w = S.WORKLOADS["batched_stack_zipf"]
+    H, E, k, I, L, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_layers, w.n_tokens
+    layers = build_layers(w, torch, N, S)
+    xs = S.gen_x(w, T)
+    x0 = torch.from_numpy(xs.view(np.int16)).cuda().view(torch.bfloat16).float()
+    d = N.make_dims(H, E, k, I, 0)
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    x = torch.empty_like(x0)
+    lists = ([l["Wr"] for l in layers], [l["bias"] for l in layers], [l["packed"] for l in layers],
+             [l["alpha"] for l in layers])
+
+    def step():
+        x.copy_(x0)
+        N.maple_moe_stack_forward(d, T, x, *lists, ws)
+    ms_per_step = timed(torch, step, args.steps, args.warmup)
+    assert torch.isfinite(x).all().item(), "non-finite batched output"
+    log(f"batched_stack_zipf: {T / ms_per_step * 1000:.0f} tok/s, {ms_per_step * 1000:.1f} us/step")
+    prof = profile_kernels(N, step, min(args.steps, 8))
+    per_kernel = {kn: dict(launches=n, avg_us=1000 * avg) for kn, (n, avg) in prof.items()}
+    dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    return dict(
+        metric=METRIC, value=T / ms_per_step * 1000.0, unit="tok/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload="batched_stack_zipf", hidden=H, experts=E, top_k=k, inter=I,
+                    layers=L, tokens_per_step=T, step="one stack call on 64 tokens"),
+        roofline=dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None,
+                      traffic=None, kernel=dom, avg_launch_us=prof[dom][1] * 1e3),
+        kernels=per_kernel,
+    ), w
+
+
 def bench_prefill(args, torch, N, S):
     w = S.WORKLOADS[args.workload]
     H, E, k, I, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_tokens
@@ -332,7 +388,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_stack",
-                    choices=["decode_stack", "prefill_4096", "prefill_16384"])
+                    choices=["decode_stack", "prefill_4096", "prefill_16384",
+                             "batched_stack_zipf"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -358,9 +415,12 @@ def main():
     N.load()  # fails loudly if the HIP library is missing
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
-    res, w = (bench_decode if decode else bench_prefill)(args, torch, N, S)
+    runner = {"decode_stack": bench_decode, "batched_stack_zipf": bench_batched}.get(
+        args.workload, bench_prefill)
+    res, w = runner(args, torch, N, S)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = (cpu_baseline_decode if decode else cpu_baseline_prefill)(
+        base = {"decode_stack": cpu_baseline_decode, "batched_stack_zipf": cpu_baseline_batched}
+        res["cpu_baseline"] = base.get(args.workload, cpu_baseline_prefill)(
             w, args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)
 

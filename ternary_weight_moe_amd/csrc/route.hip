@@ -229,31 +229,38 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Exclusive scan over a 256-thread block.  s_tmp: 4 ints of LDS.
+// Exclusive scan over a block of NWV waves.  s_tmp: NWV ints of LDS.
+template <int NWV>
 __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int inc = wave_incl_scan(v, lane);
   if (lane == 63) s_tmp[wave] = inc;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += s_tmp[w];
-  *total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    base += w < wave ? s_tmp[w] : 0;
+    all += s_tmp[w];
+  }
+  *total = all;
   __syncthreads();
   return base + inc - v;
 }
 
 // Per-expert counts -> offsets, the active-expert list and the grouped-GEMM
-// tile list.  Thread e holds cnt of expert e (0 for e >= E).  256 threads.
+// tile list.  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
+// the block (NWV waves, 64 NWV >= E) calls it.
+template <int NWV>
 __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
                                                int32_t* active, int32_t* n_active,
                                                int32_t* tiles, int32_t* n_tiles, int* s_off,
                                                int* s_tmp) {
   const int e = threadIdx.x;
   int total, n_act, n_t;
-  const int off = block_excl_scan(cnt, s_tmp, &total);
-  const int apos = block_excl_scan(cnt > 0 ? 1 : 0, s_tmp, &n_act);
+  const int off = block_excl_scan<NWV>(cnt, s_tmp, &total);
+  const int apos = block_excl_scan<NWV>(cnt > 0 ? 1 : 0, s_tmp, &n_act);
   const int nt = (cnt + kTileM - 1) / kTileM;
-  const int tpos = block_excl_scan(nt, s_tmp, &n_t);
+  const int tpos = block_excl_scan<NWV>(nt, s_tmp, &n_t);
   if (e < E) {
     offsets[e] = off;
     s_off[e] = off;
@@ -273,7 +280,9 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
 
 // ---- T <= 64: everything in one block --------------------------------------------
 
-__global__ __launch_bounds__(256) void k_route_small(
+// 16 waves, 4 tokens each (logits loaded together, register top-k); counts by
+// expert bitmask, then offsets, scatter.
+__global__ __launch_bounds__(1024) void k_route_small(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ idx,
     float* __restrict__ gate, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_tok,
@@ -281,26 +290,40 @@ __global__ __launch_bounds__(256) void k_route_small(
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
   __shared__ int s_off[256];
-  __shared__ int s_tmp[4];
+  __shared__ int s_tmp[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  s_mask[tid] = 0ull;
-  for (int t = wave; t < T; t += 4) {
-    int i;
-    float g;
-    wave_softmax_topk(logits + (int64_t)t * E, E, k, renorm != 0, lane, &i, &g);
-    if (lane < k) {
-      idx[t * k + lane] = i;
-      gate[t * k + lane] = g;
-      s_idx[t * k + lane] = i;
+  if (tid < 256) s_mask[tid] = 0ull;
+  float lv[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = wave + 16 * r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * m;
+      lv[r][m] = (t < T && e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = wave + 16 * r;
+    if (t < T) {  // wave-uniform
+      int i;
+      float g;
+      wave_topk_lanes(lv[r], E, k, renorm != 0, lane, &i, &g);
+      if (lane < k) {
+        idx[t * k + lane] = i;
+        gate[t * k + lane] = g;
+        s_idx[t * k + lane] = i;
+      }
     }
   }
   __syncthreads();
-  for (int q = tid; q < T * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
+  for (int q = tid; q < T * k; q += 1024) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   const int cnt = (tid < E) ? __popcll(s_mask[tid]) : 0;
-  finish_offsets(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
+  finish_offsets<16>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
   __syncthreads();
-  for (int q = tid; q < T * k; q += 256) {
+  for (int q = tid; q < T * k; q += 1024) {
     const int t = q / k, e = s_idx[q];
     const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
     slot_pos[q] = pos;
@@ -380,7 +403,7 @@ __global__ __launch_bounds__(256) void k_route_scan(int nb, int E, int32_t* __re
           cnt += c[i];
         }
     }
-  finish_offsets(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
+  finish_offsets<4>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
 }
 
 __global__ __launch_bounds__(256) void k_route_scatter(int64_t n_slots, int E, int k,
@@ -439,7 +462,7 @@ hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Wor
                         hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
   if (T <= 64) {
-    launch("route_small", k_route_small, 1, 256, 0, s, logits, (int)T, d.E, d.k, renorm, ws.idx,
+    launch("route_small", k_route_small, 1, 1024, 0, s, logits, (int)T, d.E, d.k, renorm, ws.idx,
            ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos, ws.tiles,
            ws.n_tiles);
     return hipGetLastError();
