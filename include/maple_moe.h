@@ -81,6 +81,11 @@ typedef enum maple_status {
 #define MAPLE_RMS_EPS 1e-6f
 #define MAPLE_FORCE_GEMV 0x10u    /* expert FFN on the VALU GEMV path whatever T is */
 #define MAPLE_FORCE_GROUPED 0x20u /* expert FFN on the grouped int8-MFMA path whatever T is */
+/* Grouped path in its fine form: activations coded in three int8 limbs, h and
+ * the per-slot expert outputs kept in fp32 (error near fp32 rounding, about
+ * 1.5x the matrix work of the default two-limb form).  Stack calls always use
+ * the fine form; for a layer call this flag asks for it. */
+#define MAPLE_FINE_LIMBS 0x40u
 
 /* Limits: hidden a power of two in [256, 4096]; inter a power of two in
  * [128, 2048]; 1 <= top_k <= 8; top_k <= n_experts <= 256;

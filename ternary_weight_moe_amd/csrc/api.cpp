@@ -57,10 +57,10 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->h = (float*)take(sizeof(float) * Tk * d.I);
   ws->xq = (int8_t*)take((size_t)T * 4 * d.H);
   ws->part = (int32_t*)take(sizeof(int32_t) * 4 * d.E);
-  ws->xs = (float*)take(sizeof(float) * 3 * T);
+  ws->xs = (float*)take(sizeof(float) * 5 * T);
   ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
   ws->hs = (float*)take(sizeof(float) * 4 * Tk);
-  ws->y = (uint16_t*)take(sizeof(uint16_t) * Tk * d.H);
+  ws->y = take(sizeof(float) * Tk * d.H);
   ws->xb = (uint16_t*)take(sizeof(uint16_t) * 2 * T * d.H);
   ws->wb = (uint16_t*)take(sizeof(uint16_t) * 2 * d.E * d.H);
   ws->bytes = off;
@@ -126,7 +126,7 @@ int hip_fail(hipError_t e, const char* what) {
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 constexpr uint32_t kKnownFlags = MAPLE_X_BF16 | MAPLE_RENORM_TOPK | MAPLE_RMS_NORM |
-                                 MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED;
+                                 MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED | MAPLE_FINE_LIMBS;
 
 int check_dims(const maple_moe_dims* d, Dims* out) {
   if (!d) return fail(MAPLE_ERR_INVALID_ARG, "dims is NULL");
@@ -203,6 +203,9 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
               const float* resid, float* delta, const Workspace& ws, const maple_moe_debug* dbg,
               const float* next_wr, hipStream_t s) {
   const bool gemv = use_gemv(d, T);
+  // stack calls take the fine grouped form: their routing sits downstream of
+  // every earlier layer's error
+  const bool fine = (d.flags & (kStackCall | MAPLE_FINE_LIMBS)) != 0;
   hipError_t e = hipSuccess;
   if (gemv && T == 1) {  // one token: router, top-k + gate/up, down + combine
     e = maple::launch_decode1(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta,
@@ -210,10 +213,10 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   } else {
     if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and large-T router use them
-      e = maple::launch_quant_x(d, T, x, x_bf16, ws, s);
+      e = maple::launch_quant_x(d, T, x, x_bf16, fine, ws, s);
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }
-    e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 2 * T,
+    e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 4 * T,
                              ws.logits, ws.xb, ws.wb, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     e = maple::launch_route(d, T, ws.logits, ws, s);
@@ -221,7 +224,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
     if (gemv)
       e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
     else
-      e = maple::launch_grouped_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
+      e = maple::launch_grouped_ffn(d, T, fine, packed, alpha, ws, out, resid, delta, s);
     if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   }
   if (dbg) {

@@ -9,6 +9,7 @@
 // power of two, exact); alpha scales each row once (linlog.top article
 // "Maple-Preview", section "三值权重：把乘法变成加法").
 #include "internal.h"
+#include "limbs.h"
 #include "maple_moe.h"
 #include "wave.h"
 
@@ -288,7 +289,6 @@ __global__ __launch_bounds__(256) void k_d1_down(const float* __restrict__ h, in
 // A bytes come from the same k (64g + 16s + [0,16)).
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr float kQMax3 = 2080768.f;  // 127 * 2^14
 
 __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
   v4i r;
@@ -301,14 +301,10 @@ __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
 __device__ __forceinline__ uint32_t word_s(const uint4& q, int s) {
   return s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
 }
-__device__ __forceinline__ void split3(float v, float inv_scale, int8_t* hi, int8_t* mid,
-                                       int8_t* lo, int* qh, int* qm, int* ql) {
-  int q = (int)rintf(v * inv_scale);
-  q = max(-2080768, min(2080768, q));
-  const int h = (q + 8192) >> 14;
-  const int r = q - (h << 14);
-  const int m = (r + 64) >> 7;
-  const int l = r - (m << 7);
+__device__ __forceinline__ void code3(float v, float inv_scale, int8_t* hi, int8_t* mid,
+                                      int8_t* lo, int* qh, int* qm, int* ql) {
+  int h, m, l;
+  split3(code_q(v, inv_scale, 2080768), &h, &m, &l);
   *hi = (int8_t)h;
   *mid = (int8_t)m;
   *lo = (int8_t)l;
@@ -364,11 +360,11 @@ __global__ __launch_bounds__(64) void k_d1q_router(const void* __restrict__ x,
   const float dot = wave_sum_f(acc);
   const float rinv = norm ? rsqrtf(wave_sum_f(ss) / (float)H + MAPLE_RMS_EPS) : 1.f;
   const float amax = wave_max_f(am);
-  const float scale = amax > 0.f ? amax / kQMax3 : 1.f;
+  const float scale = amax > 0.f ? amax / kQ3Max : 1.f;
   int qh = 0, qm = 0, ql = 0;
   if (lane < S) {
     const int c = e * S + lane;
-    split3(xs, 1.f / scale, &xq[c], &xq[H + c], &xq[2 * H + c], &qh, &qm, &ql);
+    code3(xs, 1.f / scale, &xq[c], &xq[H + c], &xq[2 * H + c], &qh, &qm, &ql);
   }
   qh = wave_sum_i(qh);
   qm = wave_sum_i(qm);
@@ -610,13 +606,13 @@ __global__ __launch_bounds__(512) void k_d1m_down(const float* __restrict__ h, i
     }
   }
   am = wave_max_f(am);
-  const float scale = am > 0.f ? am / kQMax3 : 1.f;
+  const float scale = am > 0.f ? am / kQ3Max : 1.f;
   const float inv = 1.f / scale;
   int qh = 0, qm = 0, ql = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = lane * PER + i;
-    split3(hv[i], inv, &sH[j][0][c], &sH[j][1][c], &sH[j][2][c], &qh, &qm, &ql);
+    code3(hv[i], inv, &sH[j][0][c], &sH[j][1][c], &sH[j][2][c], &qh, &qm, &ql);
     sH[j][3][c] = 0;
   }
   qh = wave_sum_i(qh);

@@ -9,13 +9,13 @@
 //
 // Precision.  Weights enter the MFMA as their offset codes c = w + 1 in
 // {0,1,2}; sum_k w_k q_k = sum_k c_k q_k - sum_k q_k, with the row sum of q
-// taken once per row.  An activation row v (x, or h) is coded per row as
-// s = absmax/16256, q = rint(v/s) in [-16256, 16256], and split exactly into two
-// int8 limbs q = 128*hi + lo, hi in [-127, 127], lo in [-64, 63], so
-// sum_k c_k q_k = 128 * sum c hi + sum c lo in int32 with no overflow.  The
-// result is s * (that - rowsum), then alpha per output row.  The coding error
-// is |v|max * 2^-15 per element, far inside the output tolerance; one limb
-// (|v|max * 2^-8) would not be.
+// taken once per row.  An activation row v (x, or h) is coded per row into
+// int8 limbs (limbs.h).  Two limbs (coding error |v|max * 2^-15 per element,
+// inside a single layer's output tolerance; one limb, |v|max * 2^-8, would not
+// be) with per-slot fp16 expert outputs make the fast form.  Three limbs with
+// fp32 h and fp32 expert outputs make the fine form, whose error stays near
+// fp32 rounding: a 24-layer residual stack needs that, since its routing
+// decisions sit downstream of every earlier layer's error.
 //
 // Weight unpacking.  In layout v1 one 32-bit word holds 16 consecutive k, and
 // (word >> 2b) & 0x03030303 gives k = 4b..4b+3 as four bytes, so a word
@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "limbs.h"
 #include "maple_moe.h"
 #include "wave.h"
 
@@ -39,7 +40,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int TM = kTileM;        // slots per M tile
-constexpr float kQMax = 16256.f;  // 127 * 128
 constexpr uint32_t kCodeMask = 0x03030303u;
 
 __device__ __forceinline__ v4i unpack_word(uint32_t w) {
@@ -72,18 +72,22 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// ---- x -> two int8 limbs, per-token scale, row sum of q, 1/rms ---------------
+// ---- x -> int8 limbs, per-token scale, limb row sums, 1/rms ---------------------
 
 // One wave per token, 4 tokens per block.  The row is read in 16-byte pieces
 // spread over the wave (piece p of a row goes to lane p % 64), so every load
 // instruction covers up to 1 KB of contiguous row; a lane holds its pieces of 8
 // (bf16) or 4 (fp32) values.  H % 256 == 0.
-template <bool BF16>
+// xq: [T][NL][H] limbs.  xs planes of T: scale | row sums (int bits: sum q for
+// two limbs; sum hi, sum mid, sum lo for three) | 1/rms at plane 4.
+template <bool BF16, int NL>
 __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int T, int H,
                                                  int norm, int8_t* __restrict__ xq,
                                                  float* __restrict__ xs) {
   constexpr int VPP = BF16 ? 8 : 4;   // values per 16-byte piece
   constexpr int MAXN = 64 / VPP;      // pieces per lane at H = 4096
+  constexpr float QM = NL == 2 ? kQ2Max : kQ3Max;
+  constexpr int QI = NL == 2 ? 16256 : 2080768;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -116,40 +120,59 @@ __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int
   }
   amax = wave_max_f(amax);
   ss = wave_sum_f(ss);
-  const float scale = amax > 0.f ? amax / kQMax : 1.f;
-  const float inv = amax > 0.f ? kQMax / amax : 1.f;
-  int8_t* hi_row = xq + (int64_t)t * 2 * H;
-  int8_t* lo_row = hi_row + H;
-  int qsum = 0;
+  const float scale = amax > 0.f ? amax / QM : 1.f;
+  const float inv = amax > 0.f ? QM / amax : 1.f;
+  int8_t* row = xq + (int64_t)t * NL * H;
+  int sum0 = 0, sum1 = 0, sum2 = 0;
 #pragma unroll
   for (int i = 0; i < MAXN; ++i) {
     if (i < npl && 64 * i + lane < npr) {
-      uint32_t hw[VPP / 4] = {}, lw[VPP / 4] = {};
+      uint32_t lw[NL][VPP / 4] = {};
 #pragma unroll
       for (int q = 0; q < VPP; ++q) {
-        int qq = (int)rintf(v[i][q] * inv);
-        qq = max(-16256, min(16256, qq));
-        const int hi = (qq + 64) >> 7;
-        const int lo = qq - (hi << 7);
-        hw[q >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (q & 3));
-        lw[q >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (q & 3));
-        qsum += qq;
+        const int qq = code_q(v[i][q], inv, QI);
+        const int sh = 8 * (q & 3);
+        if constexpr (NL == 2) {
+          int hi, lo;
+          split2(qq, &hi, &lo);
+          lw[0][q >> 2] |= (uint32_t)(hi & 0xFF) << sh;
+          lw[1][q >> 2] |= (uint32_t)(lo & 0xFF) << sh;
+          sum0 += qq;
+        } else {
+          int hi, mid, lo;
+          split3(qq, &hi, &mid, &lo);
+          lw[0][q >> 2] |= (uint32_t)(hi & 0xFF) << sh;
+          lw[1][q >> 2] |= (uint32_t)(mid & 0xFF) << sh;
+          lw[NL - 1][q >> 2] |= (uint32_t)(lo & 0xFF) << sh;
+          sum0 += hi;
+          sum1 += mid;
+          sum2 += lo;
+        }
       }
       const int c0 = (64 * i + lane) * VPP;
-      if constexpr (VPP == 8) {
-        *reinterpret_cast<uint2*>(hi_row + c0) = make_uint2(hw[0], hw[1]);
-        *reinterpret_cast<uint2*>(lo_row + c0) = make_uint2(lw[0], lw[1]);
-      } else {
-        *reinterpret_cast<uint32_t*>(hi_row + c0) = hw[0];
-        *reinterpret_cast<uint32_t*>(lo_row + c0) = lw[0];
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        if constexpr (VPP == 8)
+          *reinterpret_cast<uint2*>(row + (int64_t)l * H + c0) = make_uint2(lw[l][0], lw[l][1]);
+        else
+          *reinterpret_cast<uint32_t*>(row + (int64_t)l * H + c0) = lw[l][0];
       }
     }
   }
-  qsum = wave_sum_i(qsum);
+  sum0 = wave_sum_i(sum0);
+  if constexpr (NL == 3) {
+    sum1 = wave_sum_i(sum1);
+    sum2 = wave_sum_i(sum2);
+  }
   if (lane == 0) {
+    int* xi = reinterpret_cast<int*>(xs);
     xs[t] = scale;
-    reinterpret_cast<int*>(xs)[T + t] = qsum;
-    xs[2 * T + t] = norm ? rsqrtf(ss / (float)H + MAPLE_RMS_EPS) : 1.f;
+    xi[T + t] = sum0;
+    if constexpr (NL == 3) {
+      xi[2 * T + t] = sum1;
+      xi[3 * T + t] = sum2;
+    }
+    xs[4 * T + t] = norm ? rsqrtf(ss / (float)H + MAPLE_RMS_EPS) : 1.f;
   }
 }
 
@@ -196,32 +219,37 @@ __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
 // blocks share a CU; h is then re-coded with one scale per slot and part, and
 // the down projection sums the parts' contributions with their own scales.
 //
+// The fine form (NL = 3 limbs) runs NS = I / 128 parts (96 accumulation
+// registers per wave, two blocks per CU) and writes h in fp32 for the down
+// projection to code.
+//
 // Weights go straight from global memory into B operands: per N-subtile and
 // stage each lane holds two 16-byte pieces of one weight row (one load
 // instruction covers 32 contiguous bytes of 32 rows), refilled with the next
 // stage right after their last use, a full stage ahead.  The x limbs
 // (gathered through sorted_token) pass through registers into a
 // double-buffered LDS tile, two stages ahead; rows are padded to 272 bytes.
-template <int I, int NS>
-__global__ __launch_bounds__(256, NS) void k_gateup_mfma(
+template <int I, int NS, int NL>
+__global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    int8_t* __restrict__ hq, float* __restrict__ hs, int64_t Tk) {
+    int8_t* __restrict__ hq, float* __restrict__ hs, float* __restrict__ hf, int64_t Tk) {
   constexpr int NW = 4;
   constexpr int IP = I / NS;            // h columns of the block's part
   constexpr int NBG = IP / 128;         // gate N-subtiles per wave (and as many up)
   constexpr int NB = 2 * NBG;
   constexpr int KS = 256;               // codes per stage (8 MFMA steps)
   constexpr int ROWB = KS + 16;         // padded LDS row: one limb of one slot
-  constexpr int ABUF = 2 * TM * ROWB;   // one stage of x limbs
-  constexpr int HBYTES = 2 * TM * IP;   // h-limb staging in the epilogue
+  constexpr int ABUF = NL * TM * ROWB;  // one stage of x limbs
+  constexpr int HBYTES = 2 * TM * IP;   // h-limb staging in the epilogue (two limbs)
   constexpr int SMEM = 2 * ABUF > HBYTES ? 2 * ABUF : HBYTES;
   static_assert(TM == 32 && NB % 2 == 0, "tile shape");
+  static_assert(NL == 2 || (NL == 3 && NBG == 1), "three limbs: one 128-column part per block");
   __shared__ __align__(16) int8_t smem[SMEM];
   __shared__ float s_sx[TM];
-  __shared__ int s_xsum[TM], s_tok[TM];
+  __shared__ int s_xsum[NL == 2 ? 1 : 3][TM], s_tok[TM];
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
   __shared__ __align__(16) float s_al[2 * I];
@@ -237,8 +265,13 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   if (tid < TM) {
     const int tok = tid < np ? sorted_tok[p0 + tid] : -1;
     s_tok[tid] = tok;
-    s_sx[tid] = tok >= 0 ? xs[tok] * xs[2 * T + tok] : 0.f;
-    s_xsum[tid] = tok >= 0 ? reinterpret_cast<const int*>(xs)[T + tok] : 0;
+    const int* xi = reinterpret_cast<const int*>(xs);
+    s_sx[tid] = tok >= 0 ? xs[tok] * xs[4 * T + tok] : 0.f;
+    s_xsum[0][tid] = tok >= 0 ? xi[T + tok] : 0;
+    if constexpr (NL == 3) {
+      s_xsum[1][tid] = tok >= 0 ? xi[2 * T + tok] : 0;
+      s_xsum[2][tid] = tok >= 0 ? xi[3 * T + tok] : 0;
+    }
   }
   const int rowb = H / 4;
   const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
@@ -256,33 +289,42 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
 
   // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
   // 16-byte segment u % 16.  Rows past np read slot 0's token (discarded).
-  const int8_t* asrc[4];
-  int adst[4];
+  constexpr int NR = 2 * NL;  // units per thread
+  const int8_t* asrc[NR];
+  int adst[NR];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int u = r * 256 + tid;
     const int limb = u >> 9, slot = (u >> 4) & 31, seg = u & 15;
     const int tok = s_tok[slot] >= 0 ? s_tok[slot] : s_tok[0];
-    asrc[r] = xq + (int64_t)tok * 2 * H + (int64_t)limb * H + 16 * seg;
+    asrc[r] = xq + (int64_t)tok * NL * H + (int64_t)limb * H + 16 * seg;
     adst[r] = (limb * TM + slot) * ROWB + 16 * seg;
   }
-  uint4 as0, as1, as2, as3;  // one stage of x limbs in flight (named: kept in registers)
+  uint4 as0, as1, as2, as3, as4, as5;  // one stage of x limbs in flight (named: kept in registers)
   auto fetch_a = [&](int st) {
     as0 = *reinterpret_cast<const uint4*>(asrc[0] + st * KS);
     as1 = *reinterpret_cast<const uint4*>(asrc[1] + st * KS);
     as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
     as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
+    if constexpr (NL == 3) {
+      as4 = *reinterpret_cast<const uint4*>(asrc[4] + st * KS);
+      as5 = *reinterpret_cast<const uint4*>(asrc[5] + st * KS);
+    }
   };
   auto store_a = [&](int buf) {
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[0]) = as0;
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[1]) = as1;
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[2]) = as2;
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[3]) = as3;
+    if constexpr (NL == 3) {
+      *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[4]) = as4;
+      *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[5]) = as5;
+    }
   };
 
-  v16i acc[2][NB];  // [limb][N-subtile]
+  v16i acc[NL][NB];  // [limb][N-subtile]
 #pragma unroll
-  for (int l = 0; l < 2; ++l)
+  for (int l = 0; l < NL; ++l)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[l][b] = v16i{};
 
@@ -305,11 +347,11 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      v4i af[4][2];  // [step in half][limb]
+      v4i af[4][NL];  // [step in half][limb]
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-        for (int l = 0; l < 2; ++l)
+        for (int l = 0; l < NL; ++l)
           af[s2][l] = *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 128 * half + 16 * s2);
       // N-subtiles in pairs: four independent accumulators between two
       // updates of one.  The B operands of the next step are unpacked (7 VALU
@@ -329,23 +371,30 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
             u0 = unpack_word(word_of(bq[half][b + 2], 0));
             u1 = unpack_word(word_of(bq[half][b + 3], 0));
           }
-          acc[0][b] = mfma32(b0, af[s2][0], acc[0][b]);
-          acc[1][b] = mfma32(b0, af[s2][1], acc[1][b]);
-          acc[0][b + 1] = mfma32(b1, af[s2][0], acc[0][b + 1]);
-          acc[1][b + 1] = mfma32(b1, af[s2][1], acc[1][b + 1]);
+#pragma unroll
+          for (int l = 0; l < NL; ++l) acc[l][b] = mfma32(b0, af[s2][l], acc[l][b]);
+#pragma unroll
+          for (int l = 0; l < NL; ++l) acc[l][b + 1] = mfma32(b1, af[s2][l], acc[l][b + 1]);
         }
         bq[half][b] = *reinterpret_cast<const uint4*>(bsrc(b, st1) + 32 * half);
         bq[half][b + 1] = *reinterpret_cast<const uint4*>(bsrc(b + 1, st1) + 32 * half);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
+          // 2 NL MFMAs against the 14 VALU of the next two unpacks
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 4 : 3, 0);  // VALU
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 4 : 3, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 3 : 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 3 : 2, 0);
+          if constexpr (NL == 3) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -361,7 +410,33 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   // per register quad.
   const int m = r32;
   const float sx = s_sx[m];
-  const int xsum = s_xsum[m];
+  if constexpr (NL == 3) {
+    // fine form: h = silu(g) u in fp32 to hf[slot][I]; the down kernel codes it
+    const int xs0 = s_xsum[0][m], xs1 = s_xsum[1][m], xs2 = s_xsum[2][m];
+    auto dot3 = [&](int b, int j) {
+      return fmaf(16384.f, (float)(acc[0][b][j] - xs0),
+                  fmaf(128.f, (float)(acc[1][b][j] - xs1), (float)(acc[2][b][j] - xs2)));
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = cbase + 8 * i + 4 * kg;
+      const float4 ga = *reinterpret_cast<const float4*>(s_al + c);
+      const float4 ua = *reinterpret_cast<const float4*>(s_al + I + c);
+      const float gs[4] = {ga.x, ga.y, ga.z, ga.w}, us[4] = {ua.x, ua.y, ua.z, ua.w};
+      float hv4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float gv = dot3(0, 4 * i + t) * (sx * gs[t]);
+        const float uv = dot3(1, 4 * i + t) * (sx * us[t]);
+        hv4[t] = silu_fast(gv) * uv;
+      }
+      if (m < np)
+        *reinterpret_cast<float4*>(hf + (int64_t)(p0 + m) * I + c) =
+            make_float4(hv4[0], hv4[1], hv4[2], hv4[3]);
+    }
+    return;
+  }
+  const int xsum = s_xsum[0][m];
   float hv[NBG][16];
   float mx = 0.f;
 #pragma unroll
@@ -390,8 +465,8 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   if (kg == 0) s_red[wave][m] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red[0][m], s_red[1][m]), fmaxf(s_red[2][m], s_red[3][m]));
-  const float sc = mx > 0.f ? mx / kQMax : 1.f;
-  const float inv = mx > 0.f ? kQMax / mx : 1.f;
+  const float sc = mx > 0.f ? mx / kQ2Max : 1.f;
+  const float inv = mx > 0.f ? kQ2Max / mx : 1.f;
   // h limbs of the part staged in LDS (reusing the x buffers) as [limb][row][IP]
   int8_t* sH = smem;
   int qs = 0;
@@ -402,11 +477,11 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
       uint32_t hw = 0u, lw = 0u;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        int q = (int)rintf(hv[b][4 * i + t] * inv);
-        q = max(-16256, min(16256, q));
-        const int hi = (q + 64) >> 7;
+        const int q = code_q(hv[b][4 * i + t], inv, 16256);
+        int hi, lo;
+        split2(q, &hi, &lo);
         hw |= (uint32_t)(hi & 0xFF) << (8 * t);
-        lw |= (uint32_t)((q - (hi << 7)) & 0xFF) << (8 * t);
+        lw |= (uint32_t)(lo & 0xFF) << (8 * t);
         qs += q;
       }
       const int c = cbase - pbase + 32 * b + 8 * i + 4 * kg;
@@ -593,11 +668,179 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   }
 }
 
+// Fine form of the down projection.  The tile's h rows arrive in fp32 and are
+// coded here into three limbs, one scale per slot over all I columns (wave w
+// codes rows [w TM/NWV, (w+1) TM/NWV)).  NHB blocks share a tile, each taking
+// H / NHB consecutive outputs; like the gate/up parts they are consecutive
+// blocks of one XCD.  Otherwise the loop is that of k_down_mfma, with three
+// limb accumulators per N-subtile that start at minus the slot's limb row sums,
+// and fp32 outputs stored straight from the accumulators (four consecutive
+// outputs of one slot per lane and store).
+template <int I, int NBW, int NWV>
+__global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
+    const float* __restrict__ hf, int H, int NHB, const uint8_t* __restrict__ packed,
+    const float* __restrict__ alpha, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+    float* __restrict__ y) {
+  constexpr int NTH = 64 * NWV;
+  constexpr int NQ = I / 128;           // 16-byte pieces per lane and row
+  constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
+  constexpr int CH = 32 * NBW * NWV;    // outputs per chunk
+  constexpr int RPW = TM / NWV;         // h rows coded per wave
+  constexpr int VW = I >= 256 ? 4 : 2;  // h values per piece
+  constexpr int NPC = I / (64 * VW);    // pieces per lane and row
+  static_assert(RPW * NWV == TM && NPC * 64 * VW == I, "coding shape");
+  __shared__ __align__(16) int8_t sA[3][TM][ROWB];
+  __shared__ float s_sc[TM];
+  __shared__ int s_sum[3][TM];
+  extern __shared__ __align__(16) float s_ad[];  // a_d of the block's outputs
+  const int local = blockIdx.x >> 3, hp = local % NHB;
+  const int tile = xcd_tile(8 * (local / NHB) + (blockIdx.x & 7), *n_tiles);
+  if (tile < 0) return;
+  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
+  const int p0 = offsets[e] + m0;
+  const int np = min(TM, offsets[e + 1] - p0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 5, r32 = lane & 31;
+  const int nch = H / CH / NHB;  // chunks of this block
+  const int o0 = hp * nch * CH;  // its first output
+  const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4;
+  const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0;
+  const uint8_t* wrow = Wd + (int64_t)(o0 + 32 * NBW * wave + r32) * (I / 4) + 16 * kg;
+  auto bptr = [&](int c, int b, int q) {
+    return reinterpret_cast<const uint4*>(wrow + (int64_t)(c * CH + 32 * b) * (I / 4) + 32 * q);
+  };
+  uint4 bq[NBW][NQ];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) bq[b][q] = *bptr(0, b, q);
+  // the wave's h rows (rows past np are zero), all loads before any use
+  typedef float hv_t __attribute__((ext_vector_type(VW)));
+  hv_t hv[RPW][NPC];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = wave * RPW + r;
+#pragma unroll
+    for (int j = 0; j < NPC; ++j)
+      hv[r][j] = row < np ? *reinterpret_cast<const hv_t*>(hf + (int64_t)(p0 + row) * I +
+                                                           VW * (lane + 64 * j))
+                          : hv_t{};
+  }
+  for (int u = tid; u < nch * CH / 4; u += NTH)
+    reinterpret_cast<float4*>(s_ad)[u] = reinterpret_cast<const float4*>(ad)[u];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = wave * RPW + r;
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPC; ++j)
+#pragma unroll
+      for (int t = 0; t < VW; ++t) mx = fmaxf(mx, fabsf(hv[r][j][t]));
+    mx = wave_max_f(mx);
+    const float inv = mx > 0.f ? kQ3Max / mx : 1.f;
+    int sh = 0, sm = 0, sl = 0;
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+      uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+#pragma unroll
+      for (int t = 0; t < VW; ++t) {
+        int hi, mid, lo;
+        split3(code_q(hv[r][j][t], inv, 2080768), &hi, &mid, &lo);
+        w0 |= (uint32_t)(hi & 0xFF) << (8 * t);
+        w1 |= (uint32_t)(mid & 0xFF) << (8 * t);
+        w2 |= (uint32_t)(lo & 0xFF) << (8 * t);
+        sh += hi;
+        sm += mid;
+        sl += lo;
+      }
+      const int c = VW * (lane + 64 * j);
+      if constexpr (VW == 4) {
+        *reinterpret_cast<uint32_t*>(&sA[0][row][c]) = w0;
+        *reinterpret_cast<uint32_t*>(&sA[1][row][c]) = w1;
+        *reinterpret_cast<uint32_t*>(&sA[2][row][c]) = w2;
+      } else {
+        *reinterpret_cast<uint16_t*>(&sA[0][row][c]) = (uint16_t)w0;
+        *reinterpret_cast<uint16_t*>(&sA[1][row][c]) = (uint16_t)w1;
+        *reinterpret_cast<uint16_t*>(&sA[2][row][c]) = (uint16_t)w2;
+      }
+    }
+    sh = wave_sum_i(sh);
+    sm = wave_sum_i(sm);
+    sl = wave_sum_i(sl);
+    if (lane == 0) {
+      s_sc[row] = mx > 0.f ? mx / kQ3Max : 0.f;
+      s_sum[0][row] = sh;
+      s_sum[1][row] = sm;
+      s_sum[2][row] = sl;
+    }
+  }
+  __syncthreads();
+  const float sc = s_sc[r32];
+  const int sum0 = s_sum[0][r32], sum1 = s_sum[1][r32], sum2 = s_sum[2][r32];
+  const int8_t* sa = &sA[0][r32][64 * kg];
+  float* yrow = y + (int64_t)(p0 + r32) * H + o0 + 32 * NBW * wave;
+
+  for (int c = 0; c < nch; ++c) {
+    // keeps the A-operand LDS reads inside the loop (hoisted, they would hold
+    // 192 registers for the whole block)
+    asm volatile("" ::: "memory");
+    const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
+    v16i acc[3][NBW];  // [limb][N-subtile]
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc[0][b][j] = -sum0;
+        acc[1][b][j] = -sum1;
+        acc[2][b][j] = -sum2;
+      }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const v4i a0 = *reinterpret_cast<const v4i*>(sa + 128 * q + 16 * s4);
+        const v4i a1 = *reinterpret_cast<const v4i*>(sa + TM * ROWB + 128 * q + 16 * s4);
+        const v4i a2 = *reinterpret_cast<const v4i*>(sa + 2 * TM * ROWB + 128 * q + 16 * s4);
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+          const v4i wf = unpack_word(word_of(bq[b][q], s4));
+          acc[0][b] = mfma32(wf, a0, acc[0][b]);
+          acc[1][b] = mfma32(wf, a1, acc[1][b]);
+          acc[2][b] = mfma32(wf, a2, acc[2][b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
+    }
+    // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ol = 32 * b + 8 * i + 4 * kg;
+        const float4 a = *reinterpret_cast<const float4*>(s_ad + c * CH + 32 * NBW * wave + ol);
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = 4 * i + t;
+          v[t] = sc * fmaf(16384.f, (float)acc[0][b][j],
+                           fmaf(128.f, (float)acc[1][b][j], (float)acc[2][b][j]));
+        }
+        if (r32 < np)
+          *reinterpret_cast<float4*>(yrow + c * CH + ol) =
+              make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
+      }
+  }
+}
+
 // ---- weighted combine ---------------------------------------------------------------
 
 // out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order
-// in fp32; a thread owns 8 consecutive outputs (one 16-byte fp16 load per slot).
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
+// in fp32; a thread owns 8 consecutive outputs (y fp16: one 16-byte load per
+// slot; fp32: two).
+template <typename YT>
+__global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
                                                  const float* __restrict__ gate,
                                                  const int32_t* __restrict__ slot_pos, int H,
                                                  int k, float* out, const float* resid,
@@ -608,12 +851,21 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const float gj = gate[t * k + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)slot_pos[t * k + j] * H + o);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const YT* src = y + (int64_t)slot_pos[t * k + j] * H + o;
+    if constexpr (std::is_same<YT, float>::value) {
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(gj, f16_lo(w[q]), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(gj, f16_hi(w[q]), acc[2 * q + 1]);
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(gj, w[q], acc[q]);
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(gj, f16_lo(w[q]), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(gj, f16_hi(w[q]), acc[2 * q + 1]);
+      }
     }
   }
   const int64_t off = t * H + o;
@@ -641,57 +893,70 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
 
 }  // namespace
 
-hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
+hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, bool fine,
                           const Workspace& ws, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
+  const unsigned nb = (unsigned)((T + 3) / 4);
   if (x_bf16)
-    launch("quant_x", k_quant_x<true>, (unsigned)((T + 3) / 4), 256, 0, s, x, (int)T, d.H, norm,
-           ws.xq, ws.xs);
+    launch("quant_x", fine ? k_quant_x<true, 3> : k_quant_x<true, 2>, nb, 256, 0, s, x, (int)T,
+           d.H, norm, ws.xq, ws.xs);
   else
-    launch("quant_x", k_quant_x<false>, (unsigned)((T + 3) / 4), 256, 0, s, x, (int)T, d.H, norm,
-           ws.xq, ws.xs);
+    launch("quant_x", fine ? k_quant_x<false, 3> : k_quant_x<false, 2>, nb, 256, 0, s, x, (int)T,
+           d.H, norm, ws.xq, ws.xs);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
-                              const uint8_t* packed, const float* alpha, const Workspace& ws,
-                              float* out, const float* resid, float* delta, hipStream_t s) {
-  (void)x;
-  (void)x_bf16;
+hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t* packed,
+                              const float* alpha, const Workspace& ws, float* out,
+                              const float* resid, float* delta, hipStream_t s) {
   const int64_t Tk = T * d.k;
-  const unsigned nt = (unsigned)((max_tiles(d, T) + 7) & ~7);  // whole rounds of 8 XCDs
-  // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
-  auto gateup = [&](auto i_tag) {
+  const int mt = max_tiles(d, T);
+  const unsigned nt = (unsigned)((mt + 7) & ~7);  // whole rounds of 8 XCDs
+  // fine form: outputs of a tile split over NHB blocks while the grid is small
+  constexpr int kCH3 = 32 * 2 * 4;
+  int nhb = 1;
+  while (nhb < d.H / kCH3 && (int64_t)mt * nhb < 1024) nhb *= 2;
+  auto run = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
-    constexpr int NS_ = I_ >= 512 ? 2 : 1;
-    launch("gateup_mfma", k_gateup_mfma<I_, NS_>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T, d.H,
-           packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
-  };
-  auto down = [&](auto i_tag) {
-    constexpr int I_ = decltype(i_tag)::value;
-    constexpr int NS_ = I_ >= 512 ? 2 : 1;
-    // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
-    launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt, 256, 4 * d.H + 4 * 32 * (64 * 2 + 16), s,
-           ws.hq, ws.hs, Tk, d.H, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, ws.y);
+    if (fine) {
+      constexpr int NS_ = I_ / 128;
+      launch("gateup_mfma", k_gateup_mfma<I_, NS_, 3>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T,
+             d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs,
+             ws.h, Tk);
+      launch("down_mfma", k_down3_mfma<I_, 2, 4>, nt * nhb, 256, 4 * d.H / nhb, s, ws.h, d.H, nhb,
+             packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, (float*)ws.y);
+    } else {
+      // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
+      constexpr int NS_ = I_ >= 512 ? 2 : 1;
+      launch("gateup_mfma", k_gateup_mfma<I_, NS_, 2>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T,
+             d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs,
+             ws.h, Tk);
+      // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
+      launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt, 256, 4 * d.H + 4 * 32 * (64 * 2 + 16), s,
+             ws.hq, ws.hs, Tk, d.H, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles,
+             (uint16_t*)ws.y);
+    }
   };
   switch (d.I) {
     case 128:
-      gateup(std::integral_constant<int, 128>{});
-      down(std::integral_constant<int, 128>{});
+      run(std::integral_constant<int, 128>{});
       break;
     case 256:
-      gateup(std::integral_constant<int, 256>{});
-      down(std::integral_constant<int, 256>{});
+      run(std::integral_constant<int, 256>{});
       break;
     case 512:
-      gateup(std::integral_constant<int, 512>{});
-      down(std::integral_constant<int, 512>{});
+      run(std::integral_constant<int, 512>{});
       break;
     default:
       return hipErrorNotSupported;
   }
-  launch("combine", k_combine, dim3((unsigned)T, (unsigned)((d.H + 2047) / 2048)), 256, 0, s, ws.y,
-         ws.gate, ws.slot_pos, d.H, d.k, out, resid, delta);
+  const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
+  if (fine)
+    launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate, ws.slot_pos,
+           d.H, d.k, out, resid, delta);
+  else
+    launch("combine", k_combine<uint16_t>, cgrid, 256, 0, s, (const uint16_t*)ws.y, ws.gate,
+           ws.slot_pos, d.H, d.k, out, resid, delta);
   return hipGetLastError();
 }
 

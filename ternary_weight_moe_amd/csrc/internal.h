@@ -28,14 +28,16 @@ struct Workspace {
   int32_t* blk_rank;    // [T*k]   rank of a slot inside its block and expert
   int32_t* tiles;       // [max_tiles*2] grouped-GEMM tile list (expert, m0)
   int32_t* n_tiles;     // [1]
-  float* h;             // [T*k, I]  fp32 (GEMV path)
-  int8_t* xq;           // [T, 4, H] int8 limbs of x (two on the grouped path, three on
-                        //           the one-token path)
+  float* h;             // [T*k, I]  fp32 h (GEMV path, fine grouped path)
+  int8_t* xq;           // [T, 4, H] int8 limbs of x (two or three on the grouped path,
+                        //           three on the one-token path)
   int32_t* part;        // [E, 4]    per-router-block partial limb sums (one-token path)
-  float* xs;            // [3T]      scale of x's limbs | limb row sum (int bits) | 1/rms(x)
+  float* xs;            // [5T]      scale of x's limbs | limb row sums (int bits, up to
+                        //           three planes) | 1/rms(x) at plane 4
   int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
   float* hs;            // [2, 2, T*k] per h column part: limb scale per slot | limb row sum (int bits)
-  uint16_t* y;          // [T*k, H]  fp16 expert outputs before the combine (grouped path)
+  void* y;              // [T*k, H]  expert outputs before the combine (grouped path):
+                        //           fp16 in the fast form, fp32 in the fine form
   uint16_t* xb;         // [2, T, H] bf16 hi/lo planes of fp32 x (large-T router)
   uint16_t* wb;         // [2, E, H] bf16 hi/lo planes of the router (large-T router)
   size_t bytes;
@@ -80,14 +82,17 @@ hipError_t launch_decode1(const Dims& d, const void* x, bool x_bf16, const float
                           const float* bias, const uint8_t* packed, const float* alpha,
                           const Workspace& ws, float* out, const float* resid, float* delta,
                           const float* next_wr, hipStream_t s);
-hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16,
+// fine: three limbs (else two); pairs with launch_grouped_ffn's fine
+hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, bool fine,
                           const Workspace& ws, hipStream_t s);
 hipError_t launch_gemv_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
                            const uint8_t* packed, const float* alpha, const Workspace& ws,
                            float* out, const float* resid, float* delta, hipStream_t s);
-hipError_t launch_grouped_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
-                              const uint8_t* packed, const float* alpha, const Workspace& ws,
-                              float* out, const float* resid, float* delta, hipStream_t s);
+// fine: three-limb activations, fp32 h and expert outputs (else two limbs and
+// fp16 expert outputs)
+hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t* packed,
+                              const float* alpha, const Workspace& ws, float* out,
+                              const float* resid, float* delta, hipStream_t s);
 hipError_t launch_load_token(const void* staged, bool bf16, int n_staged, int64_t T, int H,
                              int32_t* counter, float* x_work, hipStream_t s);
 hipError_t launch_store_token(const float* x_work, int n_staged, int64_t T, int H,

@@ -156,8 +156,9 @@ def test_edge_all_experts_and_k1():
     check_layer(w1, L1, x1, what="k = 1")
 
 
-@pytest.mark.parametrize("flags", [N.MAPLE_FORCE_GEMV, N.MAPLE_FORCE_GROUPED],
-                         ids=["gemv", "grouped"])
+@pytest.mark.parametrize("flags", [N.MAPLE_FORCE_GEMV, N.MAPLE_FORCE_GROUPED,
+                                   N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS],
+                         ids=["gemv", "grouped", "grouped_fine"])
 def test_edge_max_skew_all_tokens_one_group(dec, flags):
     """A bias of +50 on eight experts sends every token to the same eight."""
     w, L = dec
@@ -186,18 +187,43 @@ def test_zero_tokens_is_a_no_op(dec):
 
 # ---- grouped int8-MFMA path -----------------------------------------------------------
 
+GROUPED_FORMS = pytest.mark.parametrize(
+    "gflags", [N.MAPLE_FORCE_GROUPED, N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS],
+    ids=["fast", "fine"])
+
+
+@GROUPED_FORMS
 @pytest.mark.parametrize("renorm", [False, True])
-def test_tiny_layer_grouped(tiny, renorm):
+def test_tiny_layer_grouped(tiny, renorm, gflags):
     w, L = tiny
     x, _ = layer_tokens_with_gap(w, L, w.n_tokens)
-    check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED, renorm=renorm, what="tiny grouped")
+    check_layer(w, L, x, flags=gflags, renorm=renorm, what="tiny grouped")
 
 
+@GROUPED_FORMS
 @pytest.mark.parametrize("T", [1, 17, 64, 200])
-def test_decode_layer_grouped(dec, T):
+def test_decode_layer_grouped(dec, T, gflags):
     w, L = dec
     x, _ = layer_tokens_with_gap(w, L, T, token0=7000 + 10 * T)
-    check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED, what=f"decode layer grouped T={T}")
+    check_layer(w, L, x, flags=gflags, what=f"decode layer grouped T={T}")
+
+
+def test_fine_form_error_near_fp32(dec):
+    """Three limbs and fp32 intermediates: the layer error is that of coding
+    each activation to 2^-22 of its row's absmax (a few 1e-7 per element, so
+    about 1e-6 relative on the output, within an order of the fp32 GEMV path),
+    and at least 100 times below the two-limb form's."""
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, 64, token0=12000)
+    ref = L.oracle_layer(S.x_as_f32(w, x).astype(np.float64), w.top_k, w.inter)["out"]
+    err = {}
+    for name, flags in (("gemv", N.MAPLE_FORCE_GEMV), ("fast", N.MAPLE_FORCE_GROUPED),
+                        ("fine", N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS)):
+        got, _ = run_layer(w, L, x, flags)
+        err[name] = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    log(f"rel L2 against the oracle: {err}")
+    assert err["fine"] <= 5e-6
+    assert err["fine"] <= 0.01 * err["fast"]
 
 
 def test_grouped_matches_gemv_per_token(dec):
@@ -220,8 +246,10 @@ def test_prenorm_flag_both_paths(dec, prenorm):
         check_layer(wf, L, xs, flags=flags, prenorm=prenorm, what=f"prenorm={prenorm}")
 
 
-@pytest.mark.parametrize("name,n_sample", [("prefill_4096", 256), ("prefill_16384", 96)])
-def test_prefill_layer(name, n_sample):
+@pytest.mark.parametrize("name,n_sample,flags", [("prefill_4096", 256, 0), ("prefill_16384", 96, 0),
+                                                ("prefill_4096", 128, N.MAPLE_FINE_LIMBS)],
+                         ids=["4096", "16384", "4096_fine"])
+def test_prefill_layer(name, n_sample, flags):
     w = S.WORKLOADS[name]
     L = Layer(w, 0)
     x, regen = layer_tokens_with_gap(w, L, w.n_tokens)
@@ -229,4 +257,4 @@ def test_prefill_layer(name, n_sample):
     rng = np.random.default_rng(w.seed)
     sample = np.sort(np.concatenate([[0, w.n_tokens - 1],
                                      rng.choice(w.n_tokens, n_sample, replace=False)]))
-    check_layer(w, L, x, sample=sample, what=name)
+    check_layer(w, L, x, flags=flags, sample=sample, what=name)

@@ -117,7 +117,8 @@ def zipf():
     return w, layers, x, ref
 
 
-@pytest.mark.parametrize("flags", [0, N.MAPLE_FORCE_GEMV], ids=["auto", "gemv"])
+@pytest.mark.parametrize("flags", [0, N.MAPLE_FORCE_GEMV, N.MAPLE_FORCE_GROUPED],
+                         ids=["auto", "gemv", "grouped"])
 def test_batched_zipf_stack_one_step(zipf, flags):
     w, layers, x, ref = zipf
     check_stack(w, layers, x, ref, flags=flags, what=f"zipf flags={flags:#x}")
