@@ -62,6 +62,20 @@ def decode_bytes(kernel, H, E, k, I, T=1):
     }.get(kernel)
 
 
+def grouped_fine_bytes(kernel, H, E, k, I, T, D):
+    """Algorithmic HBM bytes of one launch of a fine-form grouped kernel for T
+    tokens whose slots fall on D distinct experts (each expert's weights read
+    once): int8 limbs of x (3 planes), fp32 h and fp32 per-slot outputs."""
+    Tk = T * k
+    return {
+        "quant_x": 4 * T * H + 3 * T * H + 20 * T,
+        "gateup_mfma": D * (2 * I * H // 4 + 4 * 2 * I) + 3 * T * H + 20 * T + 4 * Tk * I,
+        "down_mfma": D * (H * I // 4 + 4 * H) + 4 * Tk * I + 4 * Tk * H,
+        "combine": 4 * Tk * H + 2 * 4 * T * H + 8 * Tk,
+        "router_gemv": 4 * E * H + 4 * T * H + 4 * T * E,
+    }.get(kernel)
+
+
 def decode_bytes_per_token_layer(H, E, k, I):
     return k * expert_bytes(H, I) + 4 * E * H + 2 * 4 * H
 
@@ -80,15 +94,19 @@ def prefill_ops(kernel, H, k, I, T):
 # An entry holds only while the kernel's sources hash as recorded; otherwise the
 # kernel has changed since the counters were taken and the traffic is unknown.
 TRAFFIC = {
-    "combine": {"bytes": 168827973, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-    "d1m_down": {"bytes": 4617793, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
-    "d1m_gateup": {"bytes": 6567871, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
-    "d1q_router": {"bytes": 2252634, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
-    "down_mfma": {"bytes": 243229061, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-    "gateup_mfma": {"bytes": 310170764, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-    "quant_x": {"bytes": 33757477, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-    "route_block": {"bytes": 4844101, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
-    "router_mfma": {"bytes": 37816408, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
+    "decode_stack": {
+        "d1m_down": {"bytes": 4617793, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+        "d1m_gateup": {"bytes": 6567871, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+        "d1q_router": {"bytes": 2252634, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+    },
+    "prefill_4096": {
+        "combine": {"bytes": 168827973, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+        "down_mfma": {"bytes": 243229061, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+        "gateup_mfma": {"bytes": 310170764, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+        "quant_x": {"bytes": 33757477, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
+        "route_block": {"bytes": 4844101, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
+        "router_mfma": {"bytes": 37816408, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
+    },
 }
 
 
@@ -101,8 +119,8 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel):
-    ent = TRAFFIC.get(kernel)
+def traffic_for(workload, kernel):
+    ent = TRAFFIC.get(workload, {}).get(kernel)
     if ent is None or source_digest(ent["sources"]) != ent["digest"]:
         return None
     return ent["bytes"]
@@ -291,7 +309,8 @@ def bench_decode(args, torch, N, S):
         config=dict(workload="decode_stack", hidden=H, experts=E, top_k=k, inter=I, layers=L,
                     batch=1, tokens_staged=n_staged, step="one captured HIP graph per token"),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=traffic_for(dom), kernel=dom,
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("decode_stack", dom),
+                      kernel=dom,
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=dom_avg_s * 1e6),
         step_roofline=dict(algorithmic_bytes_per_step=bytes_tok, achieved_gbs=step_gbs,
                            frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
@@ -323,14 +342,40 @@ def bench_batched(args, torch, N, S):
     prof = profile_kernels(N, step, min(args.steps, 8))
     per_kernel = {kn: dict(launches=n, avg_us=1000 * avg) for kn, (n, avg) in prof.items()}
     dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    # the realised routing of the step (the same call, with its routing copied out)
+    idx = torch.empty(L, T, k, dtype=torch.int32, device="cuda")
+    x.copy_(x0)
+    N.maple_moe_stack_forward(d, T, x, *lists, ws, N.make_debug(idx=idx))
+    idx = idx.cpu().numpy()
+    counts = np.stack([np.bincount(idx[l].reshape(-1), minlength=E) for l in range(L)])
+    distinct = (counts > 0).sum(1)
+    D = float(distinct.mean())
+    step_bytes = int(sum(int(dl) * expert_bytes(H, I) + 4 * E * H + T * H * 8 for dl in distinct))
+    dom_bytes = grouped_fine_bytes(dom, H, E, k, I, T, D)
+    dom_avg_s = prof[dom][1] * 1e-3
+    achieved = dom_bytes / dom_avg_s / 1e9 if dom_bytes else None
+    routing = dict(distinct_experts_per_layer=dict(min=int(distinct.min()), mean=D,
+                                                   max=int(distinct.max())),
+                   empty_experts_mean=float((counts == 0).sum(1).mean()),
+                   largest_group=int(counts.max()),
+                   layer0_group_sizes_desc=sorted(counts[0][counts[0] > 0].tolist(), reverse=True))
+    log(f"routing: {routing['distinct_experts_per_layer']} distinct experts per layer, "
+        f"largest group {routing['largest_group']}")
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     return dict(
         metric=METRIC, value=T / ms_per_step * 1000.0, unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="f32", data="synthetic",
         config=dict(workload="batched_stack_zipf", hidden=H, experts=E, top_k=k, inter=I,
                     layers=L, tokens_per_step=T, step="one stack call on 64 tokens"),
-        roofline=dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None,
-                      traffic=None, kernel=dom, avg_launch_us=prof[dom][1] * 1e3),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS if achieved else None,
+                      traffic=traffic_for("batched_stack_zipf", dom), kernel=dom,
+                      algorithmic_bytes_per_launch=dom_bytes,
+                      avg_launch_us=dom_avg_s * 1e6),
+        step_roofline=dict(algorithmic_bytes_per_step=step_bytes, achieved_gbs=step_gbs,
+                           frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
+        routing=routing,
         kernels=per_kernel,
     ), w
 
@@ -360,7 +405,7 @@ def bench_prefill(args, torch, N, S):
     if ops:
         roof = dict(bound="mfma", achieved=ops / dom_avg_s / 1e12, peak=INT8_PEAK_TOPS,
                     unit="TOP/s", frac=ops / dom_avg_s / 1e12 / INT8_PEAK_TOPS,
-                    traffic=traffic_for(dom),
+                    traffic=traffic_for(args.workload, dom),
                     kernel=dom, algorithmic_int8_ops_per_launch=ops,
                     avg_launch_us=dom_avg_s * 1e6)
     else:

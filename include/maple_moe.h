@@ -90,9 +90,8 @@ typedef enum maple_status {
 /* Limits: hidden a power of two in [256, 4096]; inter a power of two in
  * [128, 2048]; 1 <= top_k <= 8; top_k <= n_experts <= 256;
  * 0 <= n_tokens <= MAPLE_MAX_TOKENS.  The fp32 VALU GEMV path (chosen for
- * n_tokens <= 16 in a layer call and n_tokens <= 64 in a stack call, or forced)
- * takes n_tokens <= 64; the grouped int8-MFMA path (chosen above those counts,
- * or forced) takes inter <= 512. */
+ * n_tokens <= 2, for inter > 512, or forced) takes n_tokens <= 64; the grouped
+ * int8-MFMA path (chosen otherwise, or forced) takes inter <= 512. */
 #define MAPLE_MAX_TOKENS (1 << 20)
 #define MAPLE_GEMV_MAX_TOKENS 64
 #define MAPLE_GROUPED_MAX_INTER 512

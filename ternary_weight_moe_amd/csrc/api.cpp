@@ -23,13 +23,13 @@ struct maple_graph {
 
 namespace maple {
 
-// Token counts up to which the automatic dispatch uses the VALU GEMV path: for
-// a single layer, and inside a stack.  The stack keeps the fp32 GEMV path up to
-// its limit because the grouped path's two-limb activations (about 2e-4
-// relative error per layer) accumulate along the residual stream enough to move
-// router logits by more than 5e-5 within 24 layers.
-constexpr int64_t kGemvAuto = 16;
-constexpr int64_t kGemvAutoStack = MAPLE_GEMV_MAX_TOKENS;
+// Token counts up to which the automatic dispatch uses the VALU GEMV path, for
+// a layer call and inside a stack (one token takes the one-token path).  Timed
+// on the 24-layer stack: the GEMV path costs about 0.36 ms per extra token,
+// the grouped path about 1.4 ms flat up to 16 tokens, so the grouped path wins
+// from 3 tokens on.
+constexpr int64_t kGemvAuto = 2;
+constexpr int64_t kGemvAutoStack = 2;
 
 int max_tiles(const Dims& d, int64_t T) { return (int)((T * d.k) / kTileM + d.E + 1); }
 
@@ -154,6 +154,7 @@ constexpr uint32_t kStackCall = 0x80000000u;
 bool use_gemv(const Dims& d, int64_t T) {
   if (d.flags & MAPLE_FORCE_GEMV) return true;
   if (d.flags & MAPLE_FORCE_GROUPED) return false;
+  if (d.I > MAPLE_GROUPED_MAX_INTER) return true;  // beyond the grouped kernels' shapes
   return T <= ((d.flags & kStackCall) ? maple::kGemvAutoStack : maple::kGemvAuto);
 }
 
@@ -161,9 +162,10 @@ int check_tokens(const Dims& d, int64_t T) {
   if (T < 0) return fail(MAPLE_ERR_INVALID_ARG, "n_tokens=%lld < 0", (long long)T);
   if (T > MAPLE_MAX_TOKENS)
     return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_tokens=%lld > %d", (long long)T, MAPLE_MAX_TOKENS);
-  if ((d.flags & MAPLE_FORCE_GEMV) && T > MAPLE_GEMV_MAX_TOKENS)
-    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "MAPLE_FORCE_GEMV with n_tokens=%lld > %d",
-                (long long)T, MAPLE_GEMV_MAX_TOKENS);
+  if (use_gemv(d, T) && T > MAPLE_GEMV_MAX_TOKENS)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "GEMV path (%s) with n_tokens=%lld > %d",
+                (d.flags & MAPLE_FORCE_GEMV) ? "forced" : "inter > 512", (long long)T,
+                MAPLE_GEMV_MAX_TOKENS);
   if (!use_gemv(d, T) && d.I > MAPLE_GROUPED_MAX_INTER)
     return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "grouped path (n_tokens=%lld) needs inter <= %d",
                 (long long)T, MAPLE_GROUPED_MAX_INTER);

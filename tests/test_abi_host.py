@@ -154,6 +154,13 @@ def test_layer_argument_validation_before_any_device_call(lib):
     gemv = dims(flags=N.MAPLE_FORCE_GEMV)
     assert call_layer(lib, gemv, 65) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
     assert b"n_tokens" in lib.maple_last_error()
+    # inter > 512 is beyond the grouped kernels: the GEMV path serves it, up to
+    # its token limit, and forcing the grouped path is refused
+    wide = dims(inter=1024)
+    assert call_layer(lib, wide, 65) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert b"inter > 512" in lib.maple_last_error()
+    assert call_layer(lib, dims(inter=1024, flags=N.MAPLE_FORCE_GROUPED), 3) == \
+        N.MAPLE_ERR_UNSUPPORTED_SHAPE
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
