@@ -49,6 +49,7 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->active = (int32_t*)take(sizeof(int32_t) * d.E);
   ws->n_active = (int32_t*)take(256);
   ws->n_tiles = ws->n_active ? ws->n_active + 16 : nullptr;
+  ws->route_ctr = ws->n_active ? ws->n_active + 32 : nullptr;
   ws->sorted_tok = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->slot_pos = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->blk_count = (int32_t*)take(sizeof(int32_t) * nb * d.E);
@@ -219,7 +220,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }
     e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 4 * T,
-                             ws.logits, ws.xb, ws.wb, s);
+                             ws.logits, ws.xb, ws.wb, ws.route_ctr, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     e = maple::launch_route(d, T, ws.logits, ws, s);
     if (e != hipSuccess) return hip_fail(e, "routing launch");

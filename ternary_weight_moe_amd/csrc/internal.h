@@ -28,6 +28,7 @@ struct Workspace {
   int32_t* blk_rank;    // [T*k]   rank of a slot inside its block and expert
   int32_t* tiles;       // [max_tiles*2] grouped-GEMM tile list (expert, m0)
   int32_t* n_tiles;     // [1]
+  int32_t* route_ctr;   // [1]   arrival counter of the small-T routing kernel
   float* h;             // [T*k, I]  fp32 h (GEMV path, fine grouped path)
   int8_t* xq;           // [T, 4, H] int8 limbs of x (two or three on the grouped path,
                         //           three on the one-token path)
@@ -71,10 +72,11 @@ int max_tiles(const Dims& d, int64_t T);
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
-// xb, wb: bf16-plane scratch (ws.xb, ws.wb) used above the small-T sizes
+// xb, wb: bf16-plane scratch (ws.xb, ws.wb) used above the small-T sizes;
+// route_ctr: the small-T routing kernel's arrival counter (zeroed here)
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          const float* Wr, const float* bias, const float* rinv, float* logits,
-                         uint16_t* xb, uint16_t* wb, hipStream_t s);
+                         uint16_t* xb, uint16_t* wb, int32_t* route_ctr, hipStream_t s);
 hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
                         hipStream_t s);
 // next_wr: the next layer's router (only read to warm the caches), or null

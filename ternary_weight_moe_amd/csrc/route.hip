@@ -14,6 +14,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "maple_moe.h"
 #include "wave.h"
@@ -39,41 +41,77 @@ __device__ __forceinline__ float4 load_x4(const void* x, int64_t off) {
 
 // ---- router logits ---------------------------------------------------------
 
-// Small T: one wave per expert, up to 4 tokens per block.  H % 256 == 0.
-// With norm, the dot product is scaled by 1/rms(x) (the norm is linear in the
-// logits, so it is applied after the sum; the wave reads all of x anyway).
-template <bool BF16>
-__global__ __launch_bounds__(64) void k_router_gemv(const void* __restrict__ x, int T, int H,
-                                                    const float* __restrict__ Wr,
-                                                    const float* __restrict__ bias, int E,
-                                                    int norm, float* __restrict__ logits) {
-  const int e = blockIdx.x;
-  const int t0 = blockIdx.y * 4;
-  const int lane = threadIdx.x;
-  const int nt = min(4, T - t0);
-  const float* w = Wr + (int64_t)e * H;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f}, ss[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = lane * 4; j < H; j += 256) {
-    const float4 wv = *reinterpret_cast<const float4*>(w + j);
+// Sums N per-lane partials (N a power of two <= 64) across the wave with a
+// halving exchange: each step over lane bit m (m = 32, 16, ...) keeps half of
+// the values and adds the partner's other half, so after log2 N steps lane l
+// holds value l >> (6 - log2 N), summed over the lanes that agree with it in
+// those bits; xor steps over the lower lane bits complete the sums.  The order
+// of the additions is fixed, so the result is deterministic.
+template <int N>
+__device__ __forceinline__ float wave_sum_n(float (&v)[N], int lane) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (tt < nt) {
-        const float4 xv = load_x4<BF16>(x, (int64_t)(t0 + tt) * H + j);
-        acc[tt] = fmaf(wv.x, xv.x, acc[tt]);
-        acc[tt] = fmaf(wv.y, xv.y, acc[tt]);
-        acc[tt] = fmaf(wv.z, xv.z, acc[tt]);
-        acc[tt] = fmaf(wv.w, xv.w, acc[tt]);
-        ss[tt] = fmaf(xv.x, xv.x, fmaf(xv.y, xv.y, fmaf(xv.z, xv.z, fmaf(xv.w, xv.w, ss[tt]))));
-      }
+  for (int h = N / 2, m = 32; h >= 1; h /= 2, m /= 2) {
+    const bool up = lane & m;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float keep = up ? v[i + h] : v[i], give = up ? v[i] : v[i + h];
+      v[i] = keep + __shfl_xor(give, m, 64);
     }
   }
-  const float b = bias ? bias[e] : 0.f;
+  float r = v[0];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    float s = wave_sum_f(acc[tt]);
-    if (norm) s *= rsqrtf(wave_sum_f(ss[tt]) / (float)H + MAPLE_RMS_EPS);
-    if (lane == 0 && tt < nt) logits[(int64_t)(t0 + tt) * E + e] = s + b;
+  for (int m = 32 / N; m >= 1; m /= 2) r += __shfl_xor(r, m, 64);
+  return r;
+}
+
+// Small T (<= 64): a block is 4 experts (one per wave) x TT tokens.  Lane j
+// keeps its expert row's pieces [4j + 256i, +4), i < NPL = H / 256, in
+// registers and reads the same pieces of the TT token rows, all loads in
+// flight together (the block's waves read the same rows: cache hits).
+// 1/rms(x) comes from rinv when given, else from the rows read here.  Block
+// (0,0) also zeroes the arrival counter of the routing kernel that runs next
+// on the stream.
+template <bool BF16, int NPL>
+__global__ __launch_bounds__(256) void k_router_small(const void* __restrict__ x, int T,
+                                                      const float* __restrict__ Wr,
+                                                      const float* __restrict__ bias, int E,
+                                                      int norm, const float* __restrict__ rinv,
+                                                      float* __restrict__ logits,
+                                                      int32_t* __restrict__ route_ctr) {
+  constexpr int H = 256 * NPL;
+  constexpr int TT = NPL >= 16 ? 2 : 4;           // tokens per wave
+  constexpr int LB = TT == 4 ? 4 : 5;             // lane bits below the token index
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t0 = blockIdx.y * TT;
+  if (route_ctr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *route_ctr = 0;
+  if (e >= E) return;  // wave-uniform; no block barrier follows
+  float4 w[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i)
+    w[i] = *reinterpret_cast<const float4*>(Wr + (int64_t)e * H + 4 * lane + 256 * i);
+  const bool own_rms = norm && !rinv;
+  float acc[TT], ss[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = min(t0 + tt, T - 1);  // rows past T repeat the last one (discarded)
+    float a = 0.f, q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float4 xv = load_x4<BF16>(x, (int64_t)t * H + 4 * lane + 256 * i);
+      a = fmaf(w[i].x, xv.x, fmaf(w[i].y, xv.y, fmaf(w[i].z, xv.z, fmaf(w[i].w, xv.w, a))));
+      if (own_rms) q = fmaf(xv.x, xv.x, fmaf(xv.y, xv.y, fmaf(xv.z, xv.z, fmaf(xv.w, xv.w, q))));
+    }
+    acc[tt] = a;
+    ss[tt] = q;
   }
+  const float dot = wave_sum_n<TT>(acc, lane);
+  const int t = t0 + (lane >> LB);
+  float r = 1.f;
+  if (own_rms) r = rsqrtf(wave_sum_n<TT>(ss, lane) / (float)H + MAPLE_RMS_EPS);
+  else if (norm) r = rinv[min(t, T - 1)];
+  if ((lane & ((1 << LB) - 1)) == 0 && t < T)
+    logits[(int64_t)t * E + e] = dot * r + (bias ? bias[e] : 0.f);
 }
 
 // ---- Large T: router logits on the matrix cores -----------------------------
@@ -278,56 +316,60 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
   }
 }
 
-// ---- T <= 64: everything in one block --------------------------------------------
+// ---- T <= 64: selection in parallel, grouping by the last block to finish ----------
 
-// 16 waves, 4 tokens each (logits loaded together, register top-k); counts by
-// expert bitmask, then offsets, scatter.
-__global__ __launch_bounds__(1024) void k_route_small(
+// One wave per token, 4 per block.  Each block publishes its selections and
+// takes a ticket from an arrival counter (zeroed by the router kernel before
+// this kernel starts); the block with the last ticket then sees every
+// selection and counts (one 64-bit token mask per expert), scans and scatters
+// for all T tokens.  Nothing waits on another block.
+__global__ __launch_bounds__(256) void k_route_small(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ idx,
     float* __restrict__ gate, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_tok,
-    int32_t* __restrict__ slot_pos, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    int32_t* __restrict__ ctr) {
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
   __shared__ int s_off[256];
-  __shared__ int s_tmp[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 256) s_mask[tid] = 0ull;
-  float lv[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = wave + 16 * r;
+  __shared__ int s_tmp[4];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int t = blockIdx.x * 4 + (tid >> 6);
+  if (t < T) {  // wave-uniform
+    float lv[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = lane + 64 * m;
-      lv[r][m] = (t < T && e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
+      lv[m] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+    }
+    int i;
+    float g;
+    wave_topk_lanes(lv, E, k, renorm != 0, lane, &i, &g);
+    if (lane < k) {
+      idx[t * k + lane] = i;
+      gate[t * k + lane] = g;
     }
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = wave + 16 * r;
-    if (t < T) {  // wave-uniform
-      int i;
-      float g;
-      wave_topk_lanes(lv[r], E, k, renorm != 0, lane, &i, &g);
-      if (lane < k) {
-        idx[t * k + lane] = i;
-        gate[t * k + lane] = g;
-        s_idx[t * k + lane] = i;
-      }
-    }
-  }
+  __threadfence();  // release the selections before the ticket
   __syncthreads();
-  for (int q = tid; q < T * k; q += 1024) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
+  if (tid == 0) s_last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;  // block-uniform
+  __threadfence();      // acquire every block's selections
+  s_mask[tid] = 0ull;
+  for (int q = tid; q < T * k; q += 256) s_idx[q] = idx[q];
+  __syncthreads();
+  for (int q = tid; q < T * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   const int cnt = (tid < E) ? __popcll(s_mask[tid]) : 0;
-  finish_offsets<16>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
+  finish_offsets<4>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
   __syncthreads();
-  for (int q = tid; q < T * k; q += 1024) {
-    const int t = q / k, e = s_idx[q];
-    const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
+  for (int q = tid; q < T * k; q += 256) {
+    const int tq = q / k, e = s_idx[q];
+    const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << tq) - 1ull));
     slot_pos[q] = pos;
-    sorted_tok[pos] = t;
+    sorted_tok[pos] = tq;
   }
 }
 
@@ -426,16 +468,24 @@ __global__ __launch_bounds__(256) void k_route_scatter(int64_t n_slots, int E, i
 
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
                          const float* bias, const float* rinv, float* logits, uint16_t* xb,
-                         uint16_t* wb, hipStream_t s) {
+                         uint16_t* wb, int32_t* route_ctr, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   if (T <= 64) {
-    const dim3 grid(d.E, (unsigned)((T + 3) / 4));
-    if (x_bf16)
-      launch("router_gemv", k_router_gemv<true>, grid, 64, 0, s, x, (int)T, d.H, Wr, bias, d.E,
-             norm, logits);
-    else
-      launch("router_gemv", k_router_gemv<false>, grid, 64, 0, s, x, (int)T, d.H, Wr, bias, d.E,
-             norm, logits);
+    const unsigned tt = d.H >= 4096 ? 2 : 4;  // tokens per block (k_router_small's TT)
+    const dim3 grid((unsigned)((d.E + 3) / 4), (unsigned)((T + tt - 1) / tt));
+    auto go = [&](auto npl_tag) {
+      constexpr int NPL = decltype(npl_tag)::value;
+      launch("router_small", x_bf16 ? k_router_small<true, NPL> : k_router_small<false, NPL>,
+             grid, 256, 0, s, x, (int)T, Wr, bias, d.E, norm, rinv, logits, route_ctr);
+    };
+    switch (d.H) {
+      case 256: go(std::integral_constant<int, 1>{}); break;
+      case 512: go(std::integral_constant<int, 2>{}); break;
+      case 1024: go(std::integral_constant<int, 4>{}); break;
+      case 2048: go(std::integral_constant<int, 8>{}); break;
+      case 4096: go(std::integral_constant<int, 16>{}); break;
+      default: return hipErrorNotSupported;
+    }
   } else {
     if (norm && !rinv) return hipErrorInvalidValue;
     if (!xb || !wb) return hipErrorInvalidValue;
@@ -462,9 +512,9 @@ hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Wor
                         hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
   if (T <= 64) {
-    launch("route_small", k_route_small, 1, 1024, 0, s, logits, (int)T, d.E, d.k, renorm, ws.idx,
-           ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos, ws.tiles,
-           ws.n_tiles);
+    launch("route_small", k_route_small, (unsigned)((T + 3) / 4), 256, 0, s, logits, (int)T, d.E,
+           d.k, renorm, ws.idx, ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok,
+           ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr);
     return hipGetLastError();
   }
   const int nb = (int)((T + 63) / 64);
