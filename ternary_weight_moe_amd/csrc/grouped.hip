@@ -517,9 +517,10 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
 
 // ---- down projection ----------------------------------------------------------------
 
-// One block (NWV waves): one M tile (TM = 32 slots of one expert) x all H
-// outputs, in chunks of 32 NBW NWV outputs: wave w owns NBW N-subtiles of 32
-// outputs per chunk.  With 8 waves of 2 N-subtiles, two waves share each
+// One block (NWV waves): one M tile (TM = 32 slots of one expert) x H / NHB
+// consecutive outputs (NHB blocks per tile, consecutive blocks of one XCD),
+// in chunks of 32 NBW NWV outputs: wave w owns NBW N-subtiles of 32 outputs
+// per chunk.  With 8 waves of 2 N-subtiles, two waves share each
 // SIMD and cover each other's waits.  The tile's h limbs (all of K = I) sit in
 // LDS for the whole block.  The weights are the MFMA's first operand (rows =
 // outputs) and h the second (columns = slots), so a lane ends with 4
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
 // words), so a lane holds 16 contiguous bytes per 128 codes of each row.
 template <int I, int NBW, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
-    const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H,
+    const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H, int NHB,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y) {
@@ -540,9 +541,10 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
   constexpr int CH = 32 * NBW * NWV;    // outputs per chunk
   __shared__ __align__(16) int8_t sA[2][TM][ROWB];
-  // dynamic LDS: a_d of the expert (H floats), then one fp16 output patch per wave
+  // dynamic LDS: a_d of the block's H / NHB outputs, then one fp16 output patch per wave
   extern __shared__ __align__(16) float s_ad[];
-  const int tile = xcd_tile(blockIdx.x, *n_tiles);
+  const int local = blockIdx.x >> 3, hp = local % NHB;
+  const int tile = xcd_tile(8 * (local / NHB) + (blockIdx.x & 7), *n_tiles);
   if (tile < 0) return;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int p0 = offsets[e] + m0;
@@ -550,10 +552,12 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 5, r32 = lane & 31;
   const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4;
-  const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I;
-  const int nch = H / CH;
-  // lane's weight row in N-subtile b of chunk c: c*CH + 32*(NBW*wave + b) + r32
-  const uint8_t* wrow = Wd + (int64_t)(32 * NBW * wave + r32) * (I / 4) + 16 * kg;
+  const int nch = H / CH / NHB;  // chunks of this block
+  const int HB = nch * CH;       // its outputs
+  const int o0 = hp * HB;        // the first of them
+  const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0;
+  // lane's weight row in N-subtile b of chunk c: o0 + c*CH + 32*(NBW*wave + b) + r32
+  const uint8_t* wrow = Wd + (int64_t)(o0 + 32 * NBW * wave + r32) * (I / 4) + 16 * kg;
   auto bptr = [&](int c, int b, int q) {
     return reinterpret_cast<const uint4*>(wrow + (int64_t)(c * CH + 32 * b) * (I / 4) + 32 * q);
   };
@@ -577,11 +581,11 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
                    : make_uint4(0u, 0u, 0u, 0u);
   }
   // a_d through LDS: the epilogue's reads then never wait behind the weight
-  // loads in flight for the next chunk.  H / 4 <= 4 NTH.
+  // loads in flight for the next chunk.  HB / 4 <= 4 NTH.
   float4 av[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    av[i] = reinterpret_cast<const float4*>(ad)[min(tid + NTH * i, H / 4 - 1)];
+    av[i] = reinterpret_cast<const float4*>(ad)[min(tid + NTH * i, HB / 4 - 1)];
   // this lane's slot (the accumulator column): scale and limb row sum per h part
   const bool live = r32 < np;
   float sc[NS];
@@ -599,11 +603,11 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (tid + NTH * i < H / 4) reinterpret_cast<float4*>(s_ad)[tid + NTH * i] = av[i];
+    if (tid + NTH * i < HB / 4) reinterpret_cast<float4*>(s_ad)[tid + NTH * i] = av[i];
   __syncthreads();
   const int8_t* sa = &sA[0][r32][64 * kg];
   constexpr int YROW = 64 * NBW + 16;  // padded row of a wave's output patch (bytes)
-  int8_t* sY = reinterpret_cast<int8_t*>(s_ad + H) + wave * 32 * YROW;
+  int8_t* sY = reinterpret_cast<int8_t*>(s_ad + HB) + wave * 32 * YROW;
 
   for (int c = 0; c < nch; ++c) {
     // keeps the A-operand LDS reads inside the loop (hoisted, they would hold
@@ -663,7 +667,8 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
       const int r = k2 * (64 / PPR) + lane / PPR, pc = lane % PPR;
       const uint4 v = *reinterpret_cast<const uint4*>(sY + r * YROW + 16 * pc);
       if (r < np)
-        *reinterpret_cast<uint4*>(y + (int64_t)(p0 + r) * H + c * CH + 32 * NBW * wave + 8 * pc) = v;
+        *reinterpret_cast<uint4*>(y + (int64_t)(p0 + r) * H + o0 + c * CH + 32 * NBW * wave +
+                                  8 * pc) = v;
     }
   }
 }
@@ -912,10 +917,13 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t
   const int64_t Tk = T * d.k;
   const int mt = max_tiles(d, T);
   const unsigned nt = (unsigned)((mt + 7) & ~7);  // whole rounds of 8 XCDs
-  // fine form: outputs of a tile split over NHB blocks while the grid is small
-  constexpr int kCH3 = 32 * 2 * 4;
+  // the down projection's outputs of a tile split over NHB blocks while the
+  // grid is small: at least 1024 blocks for the fine form, 2048 for the fast
+  // form (whose blocks run two per CU in several waves of blocks)
+  constexpr int kCH = 32 * 2 * 4;
+  const int64_t want = fine ? 1024 : 2048;
   int nhb = 1;
-  while (nhb < d.H / kCH3 && (int64_t)mt * nhb < 1024) nhb *= 2;
+  while (nhb < d.H / kCH && (int64_t)mt * nhb < want) nhb *= 2;
   auto run = [&](auto i_tag) {
     constexpr int I_ = decltype(i_tag)::value;
     if (fine) {
@@ -932,9 +940,9 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t
              d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs,
              ws.h, Tk);
       // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
-      launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt, 256, 4 * d.H + 4 * 32 * (64 * 2 + 16), s,
-             ws.hq, ws.hs, Tk, d.H, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles,
-             (uint16_t*)ws.y);
+      launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt * nhb, 256,
+             4 * d.H / nhb + 4 * 32 * (64 * 2 + 16), s, ws.hq, ws.hs, Tk, d.H, nhb, packed, alpha,
+             ws.offsets, ws.tiles, ws.n_tiles, (uint16_t*)ws.y);
     }
   };
   switch (d.I) {

@@ -212,7 +212,9 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   }
   uint4 pa00, pa01, pa10, pa11, pb00, pb01, pb10, pb11;
   uint4 qa00, qa01, qa10, qa11, qb00, qb01, qb10, qb11;
-  v16f acc = {};
+  // independent accumulators (step parity x product term), so consecutive
+  // MFMAs do not wait on each other's results; summed after the K loop
+  v16f acc[2][NXP + 1] = {};
   const uint32_t ra = (uint32_t)((32 * wm + r32) * ROWB + 64 * kg);
   const uint32_t rb = (uint32_t)((32 * wn + r32) * ROWB + 64 * kg);
   auto compute = [&](int buf) {
@@ -221,11 +223,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
       const v8bf a0 = *reinterpret_cast<const v8bf*>(A0 + buf * ABUF + ra + 16 * s2);
       const v8bf b0 = *reinterpret_cast<const v8bf*>(B0 + buf * BBUF + rb + 16 * s2);
       const v8bf b1 = *reinterpret_cast<const v8bf*>(B0 + buf * BBUF + PL + rb + 16 * s2);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc, 0, 0, 0);
+      v16f* ac = acc[s2 & 1];
+      ac[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, ac[0], 0, 0, 0);
+      ac[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, ac[1], 0, 0, 0);
       if constexpr (NXP == 2) {
         const v8bf a1 = *reinterpret_cast<const v8bf*>(A0 + buf * ABUF + PL + ra + 16 * s2);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc, 0, 0, 0);
+        ac[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, ac[2], 0, 0, 0);
       }
     }
   };
@@ -248,13 +251,18 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   }
 #undef MAPLE_RF
 #undef MAPLE_RS
+  v16f sum = {};
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+    for (int q = 0; q <= NXP; ++q) sum += acc[p2][q];
   // accumulator register j: token 8 (j / 4) + 4 kg + j % 4, expert r32 of the wave's tile
   const int e = e0 + 32 * wn + r32;
   const float b = (bias && e < E) ? bias[e] : 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int t = t0 + 32 * wm + 8 * (j >> 2) + 4 * kg + (j & 3);
-    if (t < T && e < E) logits[(int64_t)t * E + e] = acc[j] * (rinv ? rinv[t] : 1.f) + b;
+    if (t < T && e < E) logits[(int64_t)t * E + e] = sum[j] * (rinv ? rinv[t] : 1.f) + b;
   }
 }
 
@@ -337,18 +345,18 @@ __global__ __launch_bounds__(256) void k_route_small(
   const int tid = threadIdx.x, lane = tid & 63;
   const int t = blockIdx.x * 4 + (tid >> 6);
   if (t < T) {  // wave-uniform
-    float lv[4];
+    float lv[1][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = lane + 64 * m;
-      lv[m] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+      lv[0][m] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
     }
-    int i;
-    float g;
-    wave_topk_lanes(lv, E, k, renorm != 0, lane, &i, &g);
+    int i[1];
+    float g[1];
+    wave_topk_lanes<1>(lv, E, k, renorm != 0, lane, i, g);
     if (lane < k) {
-      idx[t * k + lane] = i;
-      gate[t * k + lane] = g;
+      idx[t * k + lane] = i[0];
+      gate[t * k + lane] = g[0];
     }
   }
   __threadfence();  // release the selections before the ticket
@@ -375,51 +383,50 @@ __global__ __launch_bounds__(256) void k_route_small(
 
 // ---- large T: per-block selection, one scan block, parallel scatter --------------
 
-// One block per 64 tokens, 16 waves with 4 tokens each; the logits of the
-// wave's 4 tokens are loaded together before the selections.
-__global__ __launch_bounds__(1024) void k_route_block(const float* __restrict__ logits, int T,
-                                                      int E, int k, int renorm,
-                                                      int32_t* __restrict__ idx,
-                                                      float* __restrict__ gate,
-                                                      int32_t* __restrict__ blk_count,
-                                                      int32_t* __restrict__ blk_rank) {
+// Selection: one wave per token, 4 tokens per block, so the work spreads over
+// the whole chip.
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
+                                                    int E, int k, int renorm,
+                                                    int32_t* __restrict__ idx,
+                                                    float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform; no block barrier follows
+  float lv[1][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    lv[0][m] = e < E ? logits[t * E + e] : -INFINITY;
+  }
+  int sel[1];
+  float g[1];
+  wave_topk_lanes<1>(lv, E, k, renorm != 0, lane, sel, g);
+  if (lane < k) {
+    idx[t * k + lane] = sel[0];
+    gate[t * k + lane] = g[0];
+  }
+}
+
+// Counting per 64-token block: one 64-bit token mask per expert gives the
+// block's count of each expert and each slot's rank within its expert.
+__global__ __launch_bounds__(256) void k_route_block(int T, int E, int k,
+                                                     const int32_t* __restrict__ idx,
+                                                     int32_t* __restrict__ blk_count,
+                                                     int32_t* __restrict__ blk_rank) {
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * 64;
-  const int nt = min(64, T - t0);
-  if (tid < 256) s_mask[tid] = 0ull;
-  float lv[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tl = wave + 16 * r;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = lane + 64 * m;
-      lv[r][m] = (tl < nt && e < E) ? logits[(int64_t)(t0 + tl) * E + e] : -INFINITY;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tl = wave + 16 * r;
-    if (tl < nt) {  // wave-uniform
-      int i;
-      float g;
-      wave_topk_lanes(lv[r], E, k, renorm != 0, lane, &i, &g);
-      if (lane < k) {
-        idx[(int64_t)(t0 + tl) * k + lane] = i;
-        gate[(int64_t)(t0 + tl) * k + lane] = g;
-        s_idx[tl * k + lane] = i;
-      }
-    }
-  }
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int nt = (int)min((int64_t)64, T - t0);
+  s_mask[tid] = 0ull;
+  for (int q = tid; q < nt * k; q += 256) s_idx[q] = idx[t0 * k + q];
   __syncthreads();
-  for (int q = tid; q < nt * k; q += 1024) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
+  for (int q = tid; q < nt * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   if (tid < E) blk_count[(int64_t)blockIdx.x * E + tid] = __popcll(s_mask[tid]);
-  for (int q = tid; q < nt * k; q += 1024) {
+  for (int q = tid; q < nt * k; q += 256) {
     const int tl = q / k, e = s_idx[q];
-    blk_rank[(int64_t)t0 * k + q] = __popcll(s_mask[e] & ((1ull << tl) - 1ull));
+    blk_rank[t0 * k + q] = __popcll(s_mask[e] & ((1ull << tl) - 1ull));
   }
 }
 
@@ -518,10 +525,10 @@ hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Wor
     return hipGetLastError();
   }
   const int nb = (int)((T + 63) / 64);
-  {
-    launch("route_block", k_route_block, nb, 1024, 0, s, logits, (int)T, d.E, d.k, renorm, ws.idx,
-           ws.gate, ws.blk_count, ws.blk_rank);
-  }
+  launch("route_topk", k_route_topk, (unsigned)((T + 3) / 4), 256, 0, s, logits, (int)T, d.E, d.k,
+         renorm, ws.idx, ws.gate);
+  launch("route_block", k_route_block, nb, 256, 0, s, (int)T, d.E, d.k, ws.idx, ws.blk_count,
+         ws.blk_rank);
   {
     launch("route_scan", k_route_scan, 1, 256, 0, s, nb, d.E, ws.blk_count, ws.offsets, ws.active,
            ws.n_active, ws.tiles, ws.n_tiles);

@@ -273,65 +273,90 @@ __device__ __forceinline__ void wave_topk_rounds(const float* __restrict__ lrow,
 }
 
 // The same rounds on logits already in registers (lane holds experts lane +
-// 64 m, m < 4; entries with e >= E ignored); lane j < k receives selection j
-// (expert and gate, renormalised over the k when asked).
-__device__ __forceinline__ void wave_topk_lanes(const float (&l)[4], int E, int k, bool renorm,
-                                                int lane, int* my_sel, float* my_gate) {
-  int key[4], em[4];
-  float mxl = -INFINITY;
+// 64 m, m < 4; entries with e >= E ignored), for NT tokens at once: the rounds
+// of the NT tokens are independent and run in lockstep, so their reduction
+// chains overlap.  Lane j < k receives selection j of token t in sel[t] and
+// gate[t] (renormalised over the k when asked).
+template <int NT>
+__device__ __forceinline__ void wave_topk_lanes(const float (&l)[NT][4], int E, int k, bool renorm,
+                                                int lane, int (&sel)[NT], float (&gate)[NT]) {
+  int key[NT][4], em[NT][4];
+  float mx[NT], s[NT];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int e = lane + 64 * m;
-    key[m] = (e < E) ? float_key(l[m]) : kKeyTaken;
-    em[m] = e;
-    mxl = fmaxf(mxl, (e < E && l[m] == l[m]) ? l[m] : -INFINITY);
+  for (int t = 0; t < NT; ++t) {
+    float mxl = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * m;
+      key[t][m] = (e < E) ? float_key(l[t][m]) : kKeyTaken;
+      em[t][m] = e;
+      mxl = fmaxf(mxl, (e < E && l[t][m] == l[t][m]) ? l[t][m] : -INFINITY);
+    }
+    mx[t] = wave_max_f(mxl);
   }
-  const float mx = wave_max_f(mxl);
-  float s = 0.f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    if (em[m] < E) s += expf(key_float(key[m]) - mx);
-  s = wave_sum_f(s);
-  auto cs = [&](int a, int b) {
-    const bool sw = key[b] > key[a] || (key[b] == key[a] && em[b] < em[a]);
-    const int ka = key[a], ea = em[a];
-    key[a] = sw ? key[b] : key[a];
-    em[a] = sw ? em[b] : em[a];
-    key[b] = sw ? ka : key[b];
-    em[b] = sw ? ea : em[b];
-  };
-  cs(0, 1);
-  cs(2, 3);
-  cs(0, 2);
-  cs(1, 3);
-  cs(1, 2);
-  int hk = key[0], he = em[0];
-  int head = 0;
-  int sel = 0;
-  float val = -INFINITY;
+  for (int t = 0; t < NT; ++t) {
+    float sl = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (em[t][m] < E) sl += expf(key_float(key[t][m]) - mx[t]);
+    s[t] = wave_sum_f(sl);
+  }
+  int hk[NT], he[NT], head[NT];
+  float val[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int* kk = key[t];
+    int* ee = em[t];
+    auto cs = [&](int a, int b) {
+      const bool sw = kk[b] > kk[a] || (kk[b] == kk[a] && ee[b] < ee[a]);
+      const int ka = kk[a], ea = ee[a];
+      kk[a] = sw ? kk[b] : kk[a];
+      ee[a] = sw ? ee[b] : ee[a];
+      kk[b] = sw ? ka : kk[b];
+      ee[b] = sw ? ea : ee[b];
+    };
+    cs(0, 1);
+    cs(2, 3);
+    cs(0, 2);
+    cs(1, 3);
+    cs(1, 2);
+    hk[t] = kk[0];
+    he[t] = ee[0];
+    head[t] = 0;
+    sel[t] = 0;
+    val[t] = -INFINITY;
+  }
   for (int j = 0; j < k; ++j) {
-    const int best = wave_max_i_uniform(hk);
-    const unsigned long long b = __ballot(hk == best);
-    int e;
-    if (__popcll(b) == 1) {
-      e = __builtin_amdgcn_readlane(he, (int)__builtin_ctzll(b));
-    } else {  // equal logits in several lanes: the lowest expert index wins
-      e = -wave_max_i_uniform(hk == best ? -he : (int)0x80000001);
-    }
-    if (he == e) {
-      ++head;
-      hk = head == 1 ? key[1] : head == 2 ? key[2] : head == 3 ? key[3] : kKeyTaken;
-      he = head == 1 ? em[1] : head == 2 ? em[2] : head == 3 ? em[3] : 0x7fffffff;
-    }
-    if (lane == j) {
-      sel = e;
-      val = key_float(best);
+    int best[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) best[t] = wave_max_i_uniform(hk[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const unsigned long long b = __ballot(hk[t] == best[t]);
+      int e;
+      if (__popcll(b) == 1) {
+        e = __builtin_amdgcn_readlane(he[t], (int)__builtin_ctzll(b));
+      } else {  // equal logits in several lanes: the lowest expert index wins
+        e = -wave_max_i_uniform(hk[t] == best[t] ? -he[t] : (int)0x80000001);
+      }
+      if (he[t] == e) {
+        const int h = ++head[t];
+        hk[t] = h == 1 ? key[t][1] : h == 2 ? key[t][2] : h == 3 ? key[t][3] : kKeyTaken;
+        he[t] = h == 1 ? em[t][1] : h == 2 ? em[t][2] : h == 3 ? em[t][3] : 0x7fffffff;
+      }
+      if (lane == j) {
+        sel[t] = e;
+        val[t] = key_float(best[t]);
+      }
     }
   }
-  float g = lane < k ? expf(val - mx) / s : 0.f;
-  if (renorm) g /= wave_sum_f(g);
-  *my_sel = sel;
-  *my_gate = g;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float g = lane < k ? expf(val[t] - mx[t]) / s[t] : 0.f;
+    if (renorm) g /= wave_sum_f(g);
+    gate[t] = g;
+  }
 }
 
 }  // namespace maple
