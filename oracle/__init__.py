@@ -1,13 +1,13 @@
 """ORACLE — test infrastructure, not part of the product.
 
-A plain fp64 CPU evaluation of the routed ternary-expert FFN (``maple_oracle.c``)
-behind a thin ctypes wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+A plain fp64 CPU evaluation of the routed ternary-expert FFN and of the
+clustered output head (``maple_oracle.c``) behind a thin ctypes wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package; the HIP library
 and its Python binding never do, and share no code with it.
 
 Every function cites, in ``maple_oracle.c``, the passage of the pages it
 follows.  Parity pins (what fixes the oracle independently of itself) live in
-``tests/test_oracle_pins.py``.  Parity unpinned: agreement with the real
+``tests/test_oracle_pins.py`` and ``tests/test_oracle_head_pins.py``.  Parity unpinned: agreement with the real
 Maple-Preview model (no trained weights exist here, and the pages give no
 exact expert form).
 """
@@ -57,6 +57,11 @@ def _L():
                                                 _P, _P, _P, _P, _P, _P, _P, _P, _P]),
             "oracle_rms_normalize": (None, [_P, _I64, _I32, ctypes.c_double, _P]),
             "oracle_num_threads": (ctypes.c_int, []),
+            "oracle_head_scores": (None, [_P, _I32, _P, _I32, _P]),
+            "oracle_head_probe": (None, [_P, _I32, _I32, _P]),
+            "oracle_head_search": (_I64, [_P, _I32, _P, _P, _P, _P, _I32, _P, _P, _P]),
+            "oracle_flashhead": (None, [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -237,3 +242,49 @@ def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
     if s.shape[-1] <= k:
         return np.full(s.shape[:-1], np.inf)
     return s[..., k - 1] - s[..., k]
+
+
+# ---- FlashHead output head -------------------------------------------------------
+
+def head_scores(h: np.ndarray, centroids: np.ndarray) -> np.ndarray:
+    """<centroid_c, h> for one token; centroids are bf16 bits [C, H]."""
+    h = _c(h, np.float64).reshape(-1)
+    centroids = _c(centroids, np.uint16)
+    C, H = centroids.shape
+    out = np.empty(C, np.float64)
+    _L().oracle_head_scores(_ptr(h), H, _ptr(centroids), C, _ptr(out))
+    return out
+
+
+def head_probe(scores: np.ndarray, P: int) -> np.ndarray:
+    """The P clusters first in (score desc, id asc), ascending ids."""
+    scores = _c(scores, np.float64).reshape(-1)
+    out = np.empty(P, np.int32)
+    _L().oracle_head_probe(_ptr(scores), scores.size, P, _ptr(out))
+    return out
+
+
+def flashhead(h, centroids, rows, off, row_token, P: int, keep_cand: bool = True):
+    """FlashHead for T tokens in fp64.  h [T,H]; centroids, rows: bf16 bits
+    [C,H], [V,H] (rows grouped by cluster); off [C+1]; row_token [V].
+    Returns dict(scores, probed, cand, n_cand, token, logit)."""
+    h = _c(np.atleast_2d(h), np.float64)
+    T, H = h.shape
+    centroids = _c(centroids, np.uint16)
+    rows = _c(rows, np.uint16)
+    off = _c(off, np.int32)
+    row_token = _c(row_token, np.int32)
+    C, V = centroids.shape[0], rows.shape[0]
+    assert centroids.shape[1] == H and rows.shape[1] == H and off.size == C + 1
+    assert row_token.size == V and off[0] == 0 and off[-1] == V and np.all(np.diff(off) >= 0)
+    assert 1 <= P <= C
+    scores = np.empty((T, C), np.float64)
+    probed = np.empty((T, P), np.int32)
+    cand = np.full((T, V), np.nan) if keep_cand else None
+    n_cand = np.empty(T, np.int64)
+    token = np.empty(T, np.int32)
+    logit = np.empty(T, np.float64)
+    _L().oracle_flashhead(T, H, C, P, V, _ptr(h), _ptr(centroids), _ptr(rows), _ptr(off),
+                          _ptr(row_token), _ptr(scores), _ptr(probed), _ptr(cand), _ptr(n_cand),
+                          _ptr(token), _ptr(logit))
+    return dict(scores=scores, probed=probed, cand=cand, n_cand=n_cand, token=token, logit=logit)

@@ -3,8 +3,9 @@
  *
  * A plain, slow, fp64 CPU evaluation of the routed ternary-expert FFN layer
  * (router -> softmax/top-k -> per-expert SwiGLU FFN with ternary weights and
- * one alpha per output row -> weighted combine), and of a stack of such layers
- * joined by a residual add.  Only the tests, the smoke check and the
+ * one alpha per output row -> weighted combine), of a stack of such layers
+ * joined by a residual add, and of the clustered output head (FlashHead; see
+ * its section at the end of this file).  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library.
  *
@@ -313,4 +314,117 @@ int oracle_num_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* ---- FlashHead output head ------------------------------------------------
+ *
+ * The pages (linlog.top article "Maple-Preview", section
+ * "架构设计：为推理速度而生", FlashHead paragraph) describe the head as:
+ * the vocabulary is clustered offline by k-means into about 4748 clusters;
+ * per generated token only the cluster centres are scored, the 512 best
+ * clusters are kept, and the rows inside them are scored exactly to find the
+ * token.  Readings taken here where the pages are silent: a score is the
+ * inner product with the hidden state (the same form as a logit); clusters
+ * rank by (score desc, cluster id asc); the token is the candidate with the
+ * largest logit, ties to the lower vocabulary id; no candidate gives token -1.
+ *
+ * Index layout (an input, built offline): the rows of the vocabulary matrix
+ * are stored grouped by cluster, cluster c owning rows [off[c], off[c+1]);
+ * row_token[r] is the vocabulary id of stored row r.  Centroids and rows are
+ * bf16 bit patterns; every score and logit is an fp64 sum of exact products.
+ */
+static double bf16_to_double(uint16_t b) {
+  union {
+    uint32_t u;
+    float f;
+  } v;
+  v.u = (uint32_t)b << 16;
+  return (double)v.f;
+}
+
+static double bf16_dot(const uint16_t* row, const double* h, int32_t H) {
+  double s = 0.0;
+  for (int32_t j = 0; j < H; ++j) s += bf16_to_double(row[j]) * h[j];
+  return s;
+}
+
+/* scores[c] = <centroid_c, h> */
+void oracle_head_scores(const double* h, int32_t H, const uint16_t* centroids, int32_t C,
+                        double* scores) {
+  for (int32_t c = 0; c < C; ++c) scores[c] = bf16_dot(centroids + (int64_t)c * H, h, H);
+}
+
+typedef struct {
+  double s;
+  int32_t i;
+} score_id;
+
+static int by_score_desc_id_asc(const void* a, const void* b) {
+  const score_id* x = (const score_id*)a;
+  const score_id* y = (const score_id*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->i > y->i) - (x->i < y->i);
+}
+
+static int int_asc(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* The P clusters first in (score desc, id asc), listed by ascending id. */
+void oracle_head_probe(const double* scores, int32_t C, int32_t P, int32_t* probed) {
+  score_id* v = (score_id*)malloc(sizeof(score_id) * (size_t)C);
+  for (int32_t c = 0; c < C; ++c) {
+    v[c].s = scores[c];
+    v[c].i = c;
+  }
+  qsort(v, (size_t)C, sizeof(score_id), by_score_desc_id_asc);
+  for (int32_t p = 0; p < P; ++p) probed[p] = v[p].i;
+  qsort(probed, (size_t)P, sizeof(int32_t), int_asc);
+  free(v);
+}
+
+/* Exact logits of every row of the probed clusters, in probed order and row
+ * order (cand[n] for n < return value), and the best candidate. */
+int64_t oracle_head_search(const double* h, int32_t H, const uint16_t* rows, const int32_t* off,
+                           const int32_t* row_token, const int32_t* probed, int32_t P,
+                           double* cand, int32_t* best_token, double* best_logit) {
+  int64_t n = 0;
+  int32_t bt = -1;
+  double bl = -INFINITY;
+  for (int32_t p = 0; p < P; ++p) {
+    const int32_t c = probed[p];
+    for (int32_t r = off[c]; r < off[c + 1]; ++r) {
+      const double z = bf16_dot(rows + (int64_t)r * H, h, H);
+      if (cand) cand[n] = z;
+      ++n;
+      const int32_t tok = row_token[r];
+      if (bt < 0 || z > bl || (z == bl && tok < bt)) {
+        bt = tok;
+        bl = z;
+      }
+    }
+  }
+  *best_token = bt;
+  *best_logit = bl;
+  return n;
+}
+
+/* T tokens: h [T,H]; outputs scores [T,C], probed [T,P], cand [T,V] (may be
+ * NULL), n_cand [T], token [T], logit [T]. */
+void oracle_flashhead(int64_t T, int32_t H, int32_t C, int32_t P, int32_t V, const double* h,
+                      const uint16_t* centroids, const uint16_t* rows, const int32_t* off,
+                      const int32_t* row_token, double* scores, int32_t* probed, double* cand,
+                      int64_t* n_cand, int32_t* token, double* logit) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < T; ++t) {
+    const double* ht = h + t * H;
+    double* st = scores + t * C;
+    int32_t* pt = probed + t * P;
+    oracle_head_scores(ht, H, centroids, C, st);
+    oracle_head_probe(st, C, P, pt);
+    n_cand[t] = oracle_head_search(ht, H, rows, off, row_token, pt, P, cand ? cand + t * V : NULL,
+                                   &token[t], &logit[t]);
+  }
 }

@@ -25,6 +25,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 # Tensor ids folded into the stream keys.
 T_X, T_ROUTER, T_WEIGHTS, T_ALPHA, T_ZIPF = 1, 2, 3, 4, 5
+T_HEAD_SIZE, T_HEAD_CENTER, T_HEAD_ROW, T_HEAD_PERM, T_HEAD_H = 6, 7, 8, 9, 10
 
 
 def build_lib(force: bool = False) -> str:
@@ -199,3 +200,76 @@ def gen_alpha(w: Workload, layer: int = 0) -> np.ndarray:
     n = w.n_experts * (2 * w.inter + w.hidden)
     return uniform_f32(key(w.layer_seed(layer), T_ALPHA), n, w.alpha_lo, w.alpha_hi).reshape(
         w.n_experts, 2 * w.inter + w.hidden)
+
+
+# ---------------------------------------------------------------------------
+# Output-head (FlashHead) inputs
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@dataclass(frozen=True)
+class HeadWorkload:
+    """A clustered vocabulary index and hidden states for the output head.
+
+    The index is what an offline k-means over the vocabulary rows would hand
+    to the head: cluster c has a centre mu_c ~ N(0, center_sigma^2) per
+    element and a size drawn uniformly from [size_lo, size_hi]; its rows are
+    bf16(mu_c + N(0, noise_sigma^2)), stored contiguously by cluster, and the
+    centroid given to the head is bf16(mu_c).  Vocabulary ids are a seeded
+    permutation of the stored rows.  The vocabulary size V is the sum of the
+    drawn sizes.  Hidden states are N(0, 1) fp32.
+    """
+    name: str
+    hidden: int
+    n_clusters: int
+    n_probe: int
+    n_tokens: int
+    seed: int
+    size_lo: int = 14
+    size_hi: int = 41
+    center_sigma: float = 0.02
+    noise_sigma: float = 0.01
+
+
+HEAD_WORKLOADS = {
+    "head_tiny": HeadWorkload("head_tiny", 256, 64, 8, 4, 6001, size_lo=0, size_hi=12),
+    # about 4748 clusters, 512 probed (the pages' FlashHead figures); sizes
+    # 14..41 give V of about 130k (the pages put Maple's vocabulary at 100k-250k)
+    "flashhead_decode": HeadWorkload("flashhead_decode", 2048, 4748, 512, 1, 7001),
+}
+
+
+def gen_head_index(w: HeadWorkload):
+    """(centroids bf16 [C,H], rows bf16 [V,H], off int32 [C+1], row_token int32 [V])."""
+    C, H = w.n_clusters, w.hidden
+    u = uniform_f32(key(w.seed, T_HEAD_SIZE), C, 0.0, 1.0).astype(np.float64)
+    sizes = np.minimum(w.size_lo + np.floor(u * (w.size_hi - w.size_lo + 1)), w.size_hi)
+    off = np.zeros(C + 1, np.int32)
+    off[1:] = np.cumsum(sizes.astype(np.int64))
+    V = int(off[-1])
+    mu = normal_f32(key(w.seed, T_HEAD_CENTER), C * H, w.center_sigma).reshape(C, H)
+    rows = np.empty((V, H), np.uint16)
+    for c0 in range(0, C, 512):  # in slices, to bound the float32 temporaries
+        c1 = min(C, c0 + 512)
+        r0, r1 = int(off[c0]), int(off[c1])
+        noise = normal_f32(key(w.seed, T_HEAD_ROW, c0), (r1 - r0) * H, w.noise_sigma)
+        owner = np.repeat(np.arange(c0, c1), np.diff(off[c0:c1 + 1]))
+        rows[r0:r1] = f32_to_bf16_bits(mu[owner] + noise.reshape(r1 - r0, H))
+    row_token = permutation(key(w.seed, T_HEAD_PERM), V)
+    return f32_to_bf16_bits(mu), rows, off, row_token
+
+
+def gen_head_h(w: HeadWorkload, n_tokens: int | None = None, token0: int = 0,
+               regen: dict | None = None) -> np.ndarray:
+    """Hidden states fp32 [T, H], one stream per token (regen as in gen_x)."""
+    T = w.n_tokens if n_tokens is None else n_tokens
+    regen = regen or {}
+    out = np.empty((T, w.hidden), np.float32)
+    for i, t in enumerate(range(token0, token0 + T)):
+        out[i] = normal_f32(key(w.seed, T_HEAD_H, t, regen.get(t, 0)), w.hidden)
+    return out

@@ -74,3 +74,31 @@ def test_zipf_bias_is_a_log_rank_permutation():
     ranks = np.exp(-b / (w.zipf_beta * w.zipf_s))
     assert np.allclose(np.sort(ranks), np.arange(1, w.n_experts + 1), rtol=1e-5)
     assert S.gen_router_bias(S.WORKLOADS["prefill_4096"]) is None
+
+
+def test_head_index_recipe():
+    w = S.HEAD_WORKLOADS["head_tiny"]
+    cen, rows, off, rt = S.gen_head_index(w)
+    C, H = w.n_clusters, w.hidden
+    sizes = np.diff(off)
+    assert cen.shape == (C, H) and off[0] == 0 and rows.shape == (int(off[-1]), H)
+    assert sizes.min() >= w.size_lo and sizes.max() <= w.size_hi
+    assert np.array_equal(np.sort(rt), np.arange(rows.shape[0]))
+    again = S.gen_head_index(w)
+    assert all(np.array_equal(a, b) for a, b in zip((cen, rows, off, rt), again))
+    # rows scatter around their cluster's centre with the noise sigma
+    mu = S.bf16_bits_to_f32(cen).astype(np.float64)
+    r = S.bf16_bits_to_f32(rows).astype(np.float64)
+    owner = np.repeat(np.arange(C), sizes)
+    d = r - mu[owner]
+    assert abs(d.std() - w.noise_sigma) < 0.1 * w.noise_sigma
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e-3], np.float32)
+    b = S.f32_to_bf16_bits(x)
+    back = S.bf16_bits_to_f32(b)
+    assert back[0] == 1.0 and back[1] == 1.0            # halfway: to the even neighbour
+    assert back[2] == np.float32(1.0 + 2 ** -6)         # halfway: up to the even neighbour
+    assert back[3] == -2.5
+    assert abs(back[4] - 3.0e-3) <= 2 ** -8 * 3.0e-3        # half an ulp of 7 stored bits
