@@ -41,6 +41,7 @@ EXPORTS = [
     "maple_ternary_pack_device", "maple_moe_layer_forward", "maple_moe_stack_forward",
     "maple_moe_stack_graph_create", "maple_graph_launch", "maple_graph_set_step",
     "maple_graph_destroy", "maple_profile_enable", "maple_profile_summary",
+    "maple_head_workspace_bytes", "maple_flashhead_forward",
 ]
 
 
@@ -66,6 +67,16 @@ class Dims(ctypes.Structure):
 class Debug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("idx", "gate", "logits", "offsets", "sorted_token", "slot_pos", "delta")]
+
+
+class HeadDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_clusters", ctypes.c_int32), ("n_probe", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class HeadDebug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("scores", "probed", "cand_logits", "n_cand")]
 
 
 _P = ctypes.c_void_p
@@ -107,6 +118,11 @@ def load() -> ctypes.CDLL:
         "maple_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "maple_profile_summary": (ctypes.c_int, [ctypes.c_int, _P, _P, _P,
                                                  ctypes.POINTER(ctypes.c_int)]),
+        "maple_head_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(HeadDims), i32,
+                                                      ctypes.POINTER(sz)]),
+        "maple_flashhead_forward": (ctypes.c_int, [ctypes.POINTER(HeadDims), i32, _P, _P, _P,
+                                                   _P, _P, _P, _P, _P, sz,
+                                                   ctypes.POINTER(HeadDebug), _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -278,3 +294,36 @@ class MapleGraph:
             self.destroy()
         except Exception:
             pass
+
+
+# ---- output head (FlashHead) ------------------------------------------------------
+
+MAPLE_HEAD_MAX_CLUSTERS = 14336
+MAPLE_HEAD_MAX_PROBE = 1024
+MAPLE_HEAD_MAX_TOKENS = 4096
+
+
+def make_head_dims(hidden: int, vocab: int, n_clusters: int, n_probe: int,
+                   flags: int = 0) -> HeadDims:
+    return HeadDims(hidden, vocab, n_clusters, n_probe, flags)
+
+
+def make_head_debug(**bufs) -> HeadDebug:
+    return HeadDebug(**{k: _dptr(v) for k, v in bufs.items()})
+
+
+def maple_head_workspace_bytes(dims: HeadDims, max_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().maple_head_workspace_bytes(ctypes.byref(dims), max_tokens, ctypes.byref(n)),
+           "maple_head_workspace_bytes")
+    return n.value
+
+
+def maple_flashhead_forward(dims: HeadDims, n_tokens: int, h, centroids, rows, cluster_off,
+                            row_token, token_out, logit_out, workspace,
+                            dbg: Optional[HeadDebug] = None, stream=None) -> None:
+    _check(load().maple_flashhead_forward(
+        ctypes.byref(dims), n_tokens, _dptr(h), _dptr(centroids), _dptr(rows),
+        _dptr(cluster_off), _dptr(row_token), _dptr(token_out), _dptr(logit_out),
+        _dptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(dbg) if dbg else None, _stream(stream)), "maple_flashhead_forward")

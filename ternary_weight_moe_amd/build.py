@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmaple_moe.so")
-SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "misc.hip"]
+SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "misc.hip", "head.hip"]
 HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(CSRC, "wave.h"),
            os.path.join(ROOT, "include", "maple_moe.h")]
 

@@ -13,6 +13,7 @@
 
 #include "internal.h"
 #include "maple_moe.h"
+#include "maple_head.h"
 
 struct maple_graph {
   hipGraph_t graph = nullptr;
@@ -64,6 +65,23 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->y = take(sizeof(float) * Tk * d.H);
   ws->xb = (uint16_t*)take(sizeof(uint16_t) * 2 * T * d.H);
   ws->wb = (uint16_t*)take(sizeof(uint16_t) * 2 * d.E * d.H);
+  ws->bytes = off;
+  return off;
+}
+
+size_t carve_head(const HeadDims& d, int64_t T, char* base, HeadWorkspace* ws) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  ws->scores = (float*)take(sizeof(float) * T * d.C);
+  ws->probed = (int32_t*)take(sizeof(int32_t) * T * d.P);
+  ws->cand_base = (int32_t*)take(sizeof(int32_t) * T * (d.P + 1));
+  ws->part_z = (float*)take(sizeof(float) * T * d.P);
+  ws->part_tok = (int32_t*)take(sizeof(int32_t) * T * d.P);
+  ws->ctr = (int32_t*)take(sizeof(int32_t) * T);
   ws->bytes = off;
   return off;
 }
@@ -590,6 +608,84 @@ int maple_graph_destroy(maple_graph* graph) {
   if (graph->counter) (void)hipFree(graph->counter);
   delete graph;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  return MAPLE_OK;
+}
+
+// ---- output head (FlashHead) ----
+
+static int check_head_dims(const maple_head_dims* d, maple::HeadDims* out) {
+  if (!d) return fail(MAPLE_ERR_INVALID_ARG, "dims is NULL");
+  if (d->flags) return fail(MAPLE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (!is_pow2(d->hidden) || d->hidden < 256 || d->hidden > 4096)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "hidden=%d: need a power of two in [256, 4096]",
+                d->hidden);
+  if (d->n_clusters < 1 || d->n_clusters > MAPLE_HEAD_MAX_CLUSTERS)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_clusters=%d: need 1..%d", d->n_clusters,
+                MAPLE_HEAD_MAX_CLUSTERS);
+  if (d->n_probe < 1 || d->n_probe > d->n_clusters || d->n_probe > MAPLE_HEAD_MAX_PROBE)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_probe=%d: need 1..min(n_clusters, %d)",
+                d->n_probe, MAPLE_HEAD_MAX_PROBE);
+  if (d->vocab < 1) return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "vocab=%d: need >= 1", d->vocab);
+  *out = maple::HeadDims{d->hidden, d->vocab, d->n_clusters, d->n_probe};
+  return MAPLE_OK;
+}
+
+int maple_head_workspace_bytes(const maple_head_dims* dims, int32_t max_tokens, size_t* bytes) {
+  maple::HeadDims d;
+  int rc;
+  if ((rc = check_head_dims(dims, &d))) return rc;
+  if (max_tokens < 0 || max_tokens > MAPLE_HEAD_MAX_TOKENS)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "max_tokens=%d: need 0..%d", max_tokens,
+                MAPLE_HEAD_MAX_TOKENS);
+  if (!bytes) return fail(MAPLE_ERR_INVALID_ARG, "bytes is NULL");
+  maple::HeadWorkspace ws;
+  *bytes = maple::carve_head(d, max_tokens, nullptr, &ws);
+  return MAPLE_OK;
+}
+
+int maple_flashhead_forward(const maple_head_dims* dims, int32_t n_tokens, const float* h,
+                            const uint16_t* centroids, const uint16_t* rows,
+                            const int32_t* cluster_off, const int32_t* row_token,
+                            int32_t* token_out, float* logit_out, void* workspace,
+                            size_t ws_bytes, const maple_head_debug* dbg, void* stream) {
+  maple::HeadDims d;
+  int rc;
+  if ((rc = check_head_dims(dims, &d))) return rc;
+  if (n_tokens < 0) return fail(MAPLE_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (n_tokens > MAPLE_HEAD_MAX_TOKENS)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_tokens=%d > %d", n_tokens, MAPLE_HEAD_MAX_TOKENS);
+  if ((rc = check_ptr(h, 16, "h")) || (rc = check_ptr(centroids, 16, "centroids")) ||
+      (rc = check_ptr(rows, 16, "rows")) || (rc = check_ptr(cluster_off, 4, "cluster_off")) ||
+      (rc = check_ptr(row_token, 4, "row_token")) || (rc = check_ptr(token_out, 4, "token_out")) ||
+      (rc = check_ptr(logit_out, 4, "logit_out")) || (rc = check_ptr(workspace, 256, "workspace")))
+    return rc;
+  if (dbg && ((rc = check_opt_ptr(dbg->scores, 4, "dbg.scores")) ||
+              (rc = check_opt_ptr(dbg->probed, 4, "dbg.probed")) ||
+              (rc = check_opt_ptr(dbg->cand_logits, 4, "dbg.cand_logits")) ||
+              (rc = check_opt_ptr(dbg->n_cand, 4, "dbg.n_cand"))))
+    return rc;
+  maple::HeadWorkspace ws;
+  const size_t need = maple::carve_head(d, n_tokens, nullptr, &ws);
+  if (ws_bytes < need)
+    return fail(MAPLE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", ws_bytes, need);
+  if (n_tokens == 0) return MAPLE_OK;
+  if ((rc = device_ready())) return rc;
+  maple::carve_head(d, n_tokens, static_cast<char*>(workspace), &ws);
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = maple::launch_head(d, n_tokens, h, centroids, rows, cluster_off, row_token,
+                                    token_out, logit_out, ws, dbg ? dbg->cand_logits : nullptr,
+                                    dbg ? dbg->n_cand : nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "head launch");
+  if (dbg) {
+    if (dbg->scores &&
+        (e = hipMemcpyAsync(dbg->scores, ws.scores, sizeof(float) * n_tokens * d.C,
+                            hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "debug copy");
+    if (dbg->probed &&
+        (e = hipMemcpyAsync(dbg->probed, ws.probed, sizeof(int32_t) * n_tokens * d.P,
+                            hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "debug copy");
+  }
   return MAPLE_OK;
 }
 

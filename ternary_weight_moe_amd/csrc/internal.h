@@ -102,4 +102,24 @@ hipError_t launch_store_token(const float* x_work, int n_staged, int64_t T, int 
 hipError_t launch_set_step(int32_t* counter, int32_t step, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
+// ---- output head (FlashHead) ----
+struct HeadDims {
+  int H, V, C, P;
+};
+struct HeadWorkspace {
+  float* scores;       // [T, C] centroid scores
+  int32_t* probed;     // [T, P] probed clusters, ascending
+  int32_t* cand_base;  // [T, P+1] first candidate position of each probed cluster | total
+  float* part_z;       // [T, P] best logit of each probed cluster
+  int32_t* part_tok;   // [T, P] its vocabulary id
+  int32_t* ctr;        // [T] arrival counters of the search kernel
+  size_t bytes;
+};
+size_t carve_head(const HeadDims& d, int64_t T, char* base, HeadWorkspace* ws);  // base may be null
+// cand_out: NULL or [T, V] candidate logits; n_cand_out: NULL or [T]
+hipError_t launch_head(const HeadDims& d, int64_t T, const float* h, const uint16_t* cen,
+                       const uint16_t* rows, const int32_t* off, const int32_t* row_token,
+                       int32_t* token_out, float* logit_out, const HeadWorkspace& ws,
+                       float* cand_out, int32_t* n_cand_out, hipStream_t s);
+
 }  // namespace maple

@@ -41,29 +41,6 @@ __device__ __forceinline__ float4 load_x4(const void* x, int64_t off) {
 
 // ---- router logits ---------------------------------------------------------
 
-// Sums N per-lane partials (N a power of two <= 64) across the wave with a
-// halving exchange: each step over lane bit m (m = 32, 16, ...) keeps half of
-// the values and adds the partner's other half, so after log2 N steps lane l
-// holds value l >> (6 - log2 N), summed over the lanes that agree with it in
-// those bits; xor steps over the lower lane bits complete the sums.  The order
-// of the additions is fixed, so the result is deterministic.
-template <int N>
-__device__ __forceinline__ float wave_sum_n(float (&v)[N], int lane) {
-#pragma unroll
-  for (int h = N / 2, m = 32; h >= 1; h /= 2, m /= 2) {
-    const bool up = lane & m;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      const float keep = up ? v[i + h] : v[i], give = up ? v[i] : v[i + h];
-      v[i] = keep + __shfl_xor(give, m, 64);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int m = 32 / N; m >= 1; m /= 2) r += __shfl_xor(r, m, 64);
-  return r;
-}
-
 // Small T (<= 64): a block is 4 experts (one per wave) x TT tokens.  Lane j
 // keeps its expert row's pieces [4j + 256i, +4), i < NPL = H / 256, in
 // registers and reads the same pieces of the TT token rows, all loads in
@@ -264,33 +241,6 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     const int t = t0 + 32 * wm + 8 * (j >> 2) + 4 * kg + (j & 3);
     if (t < T && e < E) logits[(int64_t)t * E + e] = sum[j] * (rinv ? rinv[t] : 1.f) + b;
   }
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
-  return v;
-}
-
-// Exclusive scan over a block of NWV waves.  s_tmp: NWV ints of LDS.
-template <int NWV>
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int inc = wave_incl_scan(v, lane);
-  if (lane == 63) s_tmp[wave] = inc;
-  __syncthreads();
-  int base = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) {
-    base += w < wave ? s_tmp[w] : 0;
-    all += s_tmp[w];
-  }
-  *total = all;
-  __syncthreads();
-  return base + inc - v;
 }
 
 // Per-expert counts -> offsets, the active-expert list and the grouped-GEMM

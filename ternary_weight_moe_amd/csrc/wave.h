@@ -83,6 +83,57 @@ __device__ __forceinline__ float wave_max_f(float v) { return group_reduce<64, O
 __device__ __forceinline__ int wave_sum_i(int v) { return group_reduce_i<64, OpSum>(v); }
 __device__ __forceinline__ int wave_min_i(int v) { return group_reduce_i<64, OpMin>(v); }
 
+// Sums N per-lane partials (N a power of two <= 64) across the wave with a
+// halving exchange: each step over lane bit m (m = 32, 16, ...) keeps half of
+// the values and adds the partner's other half, so after log2 N steps lane l
+// holds value l >> (6 - log2 N), summed over the lanes that agree with it in
+// those bits; xor steps over the lower lane bits complete the sums.  The order
+// of the additions is fixed, so the result is deterministic.
+template <int N>
+__device__ __forceinline__ float wave_sum_n(float (&v)[N], int lane) {
+#pragma unroll
+  for (int h = N / 2, m = 32; h >= 1; h /= 2, m /= 2) {
+    const bool up = lane & m;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float keep = up ? v[i + h] : v[i], give = up ? v[i] : v[i + h];
+      v[i] = keep + __shfl_xor(give, m, 64);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int m = 32 / N; m >= 1; m /= 2) r += __shfl_xor(r, m, 64);
+  return r;
+}
+
+// Inclusive scan over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive scan over a block of NWV waves.  s_tmp: NWV ints of LDS.
+template <int NWV>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    base += w < wave ? s_tmp[w] : 0;
+    all += s_tmp[w];
+  }
+  *total = all;
+  __syncthreads();
+  return base + inc - v;
+}
+
 // Softmax over E <= 256 logits and the k first experts in the order
 // (logit desc, index asc), on one wave.  Lane holds logits e = lane + 64 m;
 // NaN ranks as -inf so the k indices are always valid experts.  Lane j < k

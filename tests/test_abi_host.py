@@ -22,9 +22,13 @@ def lib():
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "maple_moe.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(maple_\w+)\s*\(", text)))
+    names = set()
+    for hdr in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if hdr.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", hdr)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(maple_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -190,3 +194,63 @@ def test_stack_and_graph_validation(lib):
               ws, ctypes.byref(g)) == N.MAPLE_ERR_INVALID_ARG  # n_staged = 0
     assert lib.maple_graph_launch(None, None) == N.MAPLE_ERR_INVALID_ARG
     assert lib.maple_graph_destroy(None) == N.MAPLE_OK
+
+
+# ---- output head -------------------------------------------------------------------
+
+def head_dims(**kw):
+    d = dict(hidden=2048, vocab=131072, n_clusters=4748, n_probe=512)
+    d.update(kw)
+    return N.make_head_dims(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=2000), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(hidden=8192), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_clusters=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_clusters=N.MAPLE_HEAD_MAX_CLUSTERS + 1, n_probe=8), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_probe=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_clusters=100, n_probe=101), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_probe=N.MAPLE_HEAD_MAX_PROBE + 1), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(vocab=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(flags=1), N.MAPLE_ERR_INVALID_ARG),
+])
+def test_head_dims_validation(lib, kw, status):
+    n = ctypes.c_size_t(0)
+    assert lib.maple_head_workspace_bytes(ctypes.byref(head_dims(**kw)), 1, ctypes.byref(n)) == status
+
+
+def test_head_workspace_grows_with_tokens(lib):
+    a = N.maple_head_workspace_bytes(head_dims(), 1)
+    b = N.maple_head_workspace_bytes(head_dims(), 64)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+
+
+def call_head(lib, d, T, **over):
+    a = dict(h=FakeBuf(0x100000), centroids=FakeBuf(0x200000), rows=FakeBuf(0x300000),
+             off=FakeBuf(0x400000), row_token=FakeBuf(0x500000), token=FakeBuf(0x600000),
+             logit=FakeBuf(0x700000), workspace=FakeBuf(0x800000))
+    a.update(over)
+    p = {k: (v.addr if v else None) for k, v in a.items()}
+    return lib.maple_flashhead_forward(
+        ctypes.byref(d), T, p["h"], p["centroids"], p["rows"], p["off"], p["row_token"],
+        p["token"], p["logit"], p["workspace"], a["workspace"].nbytes if a["workspace"] else 0,
+        None, None)
+
+
+def test_head_argument_validation_before_any_device_call(lib):
+    d = head_dims()
+    assert call_head(lib, d, 0) == N.MAPLE_OK
+    assert call_head(lib, d, -1) == N.MAPLE_ERR_INVALID_ARG
+    assert call_head(lib, d, N.MAPLE_HEAD_MAX_TOKENS + 1) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert call_head(lib, d, 1, h=None) == N.MAPLE_ERR_INVALID_ARG
+    assert call_head(lib, d, 1, rows=FakeBuf(0x300008)) == N.MAPLE_ERR_ALIGNMENT
+    assert call_head(lib, d, 1, off=FakeBuf(0x400002)) == N.MAPLE_ERR_ALIGNMENT
+    assert call_head(lib, d, 1, workspace=FakeBuf(0x800000, 256)) == \
+        N.MAPLE_ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in lib.maple_last_error()
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+def test_head_valid_call_without_device_reports_no_device(lib):
+    assert call_head(lib, head_dims(), 1) == N.MAPLE_ERR_NO_DEVICE
