@@ -8,6 +8,9 @@ A step is one token through all 24 pre-norm blocks: router, softmax/top-8,
 grouping, gate/up + SwiGLU, down projection and weighted combine with the
 residual.  ``--workload prefill_4096`` (or ``prefill_16384``) times one
 layer over that many tokens instead; a step is then one layer call.
+``--workload batched_stack_zipf`` runs 64 tokens per step through the stack
+with Zipf-skewed routing; ``--workload flashhead_decode`` times the clustered
+output head alone, one token per call.
 
 Prints one JSON line.  Inputs are synthetic and seeded; weights are generated
 in host memory, packed on the device and resident in HBM before the timed
@@ -380,6 +383,120 @@ def bench_batched(args, torch, N, S):
     ), w
 
 
+def head_bytes(kernel, H, C, P, n_cand):
+    """Algorithmic HBM bytes of one launch of an output-head kernel for one
+    token with n_cand candidate rows (bf16 rows, fp32 h)."""
+    return {
+        "head_scores": C * 2 * H + 4 * H + 4 * C,
+        "head_select": 4 * C + 8 * P + 4 * (P + 1),
+        "head_search": n_cand * (2 * H + 4) + 4 * H + 8 * P + 8 * P,
+    }.get(kernel)
+
+
+def bench_head(args, torch, N, S):
+    """Output head (FlashHead) for one token per call: centroid scores, the
+    n_probe best clusters, exact search of their rows.  256 staged hidden
+    states; calls are replayed from captured HIP graphs of 16 calls."""
+    w = S.HEAD_WORKLOADS["flashhead_decode"]
+    H, C, P = w.hidden, w.n_clusters, w.n_probe
+    cen, rows, off, rt = S.gen_head_index(w)
+    V = rows.shape[0]
+    log(f"head index: V={V} rows, C={C} clusters, P={P} probed")
+    dev = "cuda"
+    d_cen = torch.from_numpy(cen.view(np.int16)).to(dev)
+    d_rows = torch.from_numpy(rows.view(np.int16)).to(dev)
+    d_off = torch.from_numpy(off).to(dev)
+    d_rt = torch.from_numpy(rt).to(dev)
+    NS = 256
+    hs = torch.from_numpy(S.gen_head_h(w, NS)).to(dev)
+    tok = torch.empty(NS, dtype=torch.int32, device=dev)
+    lg = torch.empty(NS, device=dev)
+    d = N.make_head_dims(H, V, C, P)
+    ws = torch.empty(N.maple_head_workspace_bytes(d, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def call(i, s=None):
+        N.maple_flashhead_forward(d, 1, hs[i], d_cen, d_rows, d_off, d_rt, tok[i:i + 1],
+                                  lg[i:i + 1], ws, stream=s)
+    G = 16
+    graphs = []
+    with torch.cuda.stream(stream):
+        for i in range(G):  # warm the caches of every path once, eagerly
+            call(i, stream)
+    torch.cuda.synchronize()
+    for g0 in range(0, NS, G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(g0, g0 + G):
+                call(i, stream)
+        graphs.append(g)
+    replays = max(1, args.steps // G)
+    for r in range(max(1, args.warmup // G)):
+        graphs[r % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for r in range(replays):
+        graphs[r % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    n_tok = replays * G
+    ms_per_step = start.elapsed_time(end) / n_tok
+    assert bool((tok >= 0).all().item()), "head returned no token"
+    log(f"flashhead: {1000 / ms_per_step:.0f} tok/s, {ms_per_step * 1000:.2f} us per token")
+    # candidate counts of the staged tokens, from the library's own debug output
+    ncand = torch.empty(1, dtype=torch.int32, device=dev)
+    counts = []
+    for i in range(32):
+        N.maple_flashhead_forward(d, 1, hs[i], d_cen, d_rows, d_off, d_rt, tok[i:i + 1],
+                                  lg[i:i + 1], ws, N.make_head_debug(n_cand=ncand))
+        counts.append(int(ncand.item()))
+    n_cand = float(np.mean(counts))
+    prof = profile_kernels(N, lambda: [call(i) for i in range(32)], 4)
+    per_kernel = {kn: dict(launches=n, avg_us=1000 * avg) for kn, (n, avg) in prof.items()}
+    dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    dom_bytes = head_bytes(dom, H, C, P, n_cand)
+    dom_avg_s = prof[dom][1] * 1e-3
+    achieved = dom_bytes / dom_avg_s / 1e9
+    tok_bytes = sum(head_bytes(k, H, C, P, n_cand) for k in ("head_scores", "head_select",
+                                                              "head_search"))
+    step_gbs = tok_bytes / (ms_per_step * 1e-3) / 1e9
+    return dict(
+        metric="output-head tok/s (clustered FlashHead search, one token per call)",
+        value=1000.0 / ms_per_step, unit="tok/s", n_gpus=1, steps=n_tok, warmup=args.warmup,
+        ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16 rows, f32 sums", data="synthetic",
+        config=dict(workload="flashhead_decode", hidden=H, vocab=V, clusters=C, probed=P,
+                    mean_candidate_rows=n_cand, step="one head call for one token"),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("flashhead_decode", dom),
+                      kernel=dom, algorithmic_bytes_per_launch=dom_bytes,
+                      avg_launch_us=dom_avg_s * 1e6),
+        step_roofline=dict(algorithmic_bytes_per_step=tok_bytes, achieved_gbs=step_gbs,
+                           frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS,
+                           dense_head_bytes=V * 2 * H,
+                           fraction_of_dense_head_bytes=tok_bytes / (V * 2 * H)),
+        kernels=per_kernel,
+    ), (w, cen, rows, off, rt, hs.cpu().numpy())
+
+
+def cpu_baseline_head(ctx, budget_s):
+    """The oracle on a bounded sample: the staged tokens 16 per call (its
+    threads take one token each) until the budget is spent; tok/s."""
+    import oracle
+    w, cen, rows, off, rt, h = ctx
+    n, t_used = 0, 0.0
+    while t_used < budget_s and n < h.shape[0]:
+        t0 = time.perf_counter()
+        oracle.flashhead(h[n:n + 16].astype(np.float64), cen, rows, off, rt, w.n_probe,
+                         keep_cand=False)
+        t_used += time.perf_counter() - t0
+        n += 16
+    return dict(value=n / t_used, unit="tok/s", cores=min(16, oracle.num_threads()),
+                kind="oracle",
+                sample=f"{n} staged tokens, 16 per call ({t_used:.2f} s of oracle time)")
+
+
 def bench_prefill(args, torch, N, S):
     w = S.WORKLOADS[args.workload]
     H, E, k, I, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_tokens
@@ -434,7 +551,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_stack",
                     choices=["decode_stack", "prefill_4096", "prefill_16384",
-                             "batched_stack_zipf"])
+                             "batched_stack_zipf", "flashhead_decode"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -446,7 +563,7 @@ def main():
               "(every token is independent, so the path shards by tokens with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    decode = args.workload == "decode_stack"
+    decode = args.workload in ("decode_stack", "flashhead_decode")
     if args.steps is None:
         args.steps = 256 if decode else 20
     if args.warmup is None:
@@ -460,11 +577,12 @@ def main():
     N.load()  # fails loudly if the HIP library is missing
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
-    runner = {"decode_stack": bench_decode, "batched_stack_zipf": bench_batched}.get(
-        args.workload, bench_prefill)
+    runner = {"decode_stack": bench_decode, "batched_stack_zipf": bench_batched,
+              "flashhead_decode": bench_head}.get(args.workload, bench_prefill)
     res, w = runner(args, torch, N, S)
     if not args.no_cpu_baseline:
-        base = {"decode_stack": cpu_baseline_decode, "batched_stack_zipf": cpu_baseline_batched}
+        base = {"decode_stack": cpu_baseline_decode, "batched_stack_zipf": cpu_baseline_batched,
+                "flashhead_decode": cpu_baseline_head}
         res["cpu_baseline"] = base.get(args.workload, cpu_baseline_prefill)(
             w, args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)

@@ -74,7 +74,7 @@ typedef struct maple_head_debug {
 int maple_head_workspace_bytes(const maple_head_dims* dims, int32_t max_tokens, size_t* bytes);
 
 /* The head for n_tokens tokens: h fp32 [T][H] (16-byte aligned) ->
- * token_out int32 [T], logit_out fp32 [T], all device memory.  Enqueues three
+ * token_out int32 [T], logit_out fp32 [T], all device memory.  Enqueues four
  * kernels on `stream` (a hipStream_t or NULL); allocates nothing, so the call
  * may be captured into a HIP graph when dbg is NULL (the debug copies use
  * hipMemcpyAsync).  The workspace must not be shared by overlapping calls.

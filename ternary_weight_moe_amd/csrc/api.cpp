@@ -79,9 +79,9 @@ size_t carve_head(const HeadDims& d, int64_t T, char* base, HeadWorkspace* ws) {
   ws->scores = (float*)take(sizeof(float) * T * d.C);
   ws->probed = (int32_t*)take(sizeof(int32_t) * T * d.P);
   ws->cand_base = (int32_t*)take(sizeof(int32_t) * T * (d.P + 1));
-  ws->part_z = (float*)take(sizeof(float) * T * d.P);
-  ws->part_tok = (int32_t*)take(sizeof(int32_t) * T * d.P);
-  ws->ctr = (int32_t*)take(sizeof(int32_t) * T);
+  ws->rstart = (int32_t*)take(sizeof(int32_t) * T * d.P);
+  ws->part_z = (float*)take(sizeof(float) * T * kSearchBlocks);
+  ws->part_tok = (int32_t*)take(sizeof(int32_t) * T * kSearchBlocks);
   ws->bytes = off;
   return off;
 }

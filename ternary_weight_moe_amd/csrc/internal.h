@@ -106,13 +106,14 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 struct HeadDims {
   int H, V, C, P;
 };
+constexpr int kSearchBlocks = 1024;  // blocks per token of the candidate search
 struct HeadWorkspace {
   float* scores;       // [T, C] centroid scores
   int32_t* probed;     // [T, P] probed clusters, ascending
   int32_t* cand_base;  // [T, P+1] first candidate position of each probed cluster | total
-  float* part_z;       // [T, P] best logit of each probed cluster
-  int32_t* part_tok;   // [T, P] its vocabulary id
-  int32_t* ctr;        // [T] arrival counters of the search kernel
+  int32_t* rstart;     // [T, P] first row of each probed cluster
+  float* part_z;       // [T, kSearchBlocks] best logit of each search block
+  int32_t* part_tok;   // [T, kSearchBlocks] its vocabulary id
   size_t bytes;
 };
 size_t carve_head(const HeadDims& d, int64_t T, char* base, HeadWorkspace* ws);  // base may be null

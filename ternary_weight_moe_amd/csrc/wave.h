@@ -89,17 +89,23 @@ __device__ __forceinline__ int wave_min_i(int v) { return group_reduce_i<64, OpM
 // holds value l >> (6 - log2 N), summed over the lanes that agree with it in
 // those bits; xor steps over the lower lane bits complete the sums.  The order
 // of the additions is fixed, so the result is deterministic.
+template <int HALF, int M>
+__device__ __forceinline__ void wave_sum_halve(float* v, int lane) {
+  if constexpr (HALF >= 1) {
+    const bool up = lane & M;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      const float keep = up ? v[i + HALF] : v[i], give = up ? v[i] : v[i + HALF];
+      v[i] = keep + __shfl_xor(give, M, 64);
+    }
+    wave_sum_halve<HALF / 2, M / 2>(v, lane);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ float wave_sum_n(float (&v)[N], int lane) {
-#pragma unroll
-  for (int h = N / 2, m = 32; h >= 1; h /= 2, m /= 2) {
-    const bool up = lane & m;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      const float keep = up ? v[i + h] : v[i], give = up ? v[i] : v[i + h];
-      v[i] = keep + __shfl_xor(give, m, 64);
-    }
-  }
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N: a power of two <= 64");
+  wave_sum_halve<N / 2, 32>(v, lane);
   float r = v[0];
 #pragma unroll
   for (int m = 32 / N; m >= 1; m /= 2) r += __shfl_xor(r, m, 64);
