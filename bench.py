@@ -98,17 +98,37 @@ def prefill_ops(kernel, H, k, I, T):
 # kernel has changed since the counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "d1m_down": {"bytes": 4617793, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
-        "d1m_gateup": {"bytes": 6567871, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
-        "d1q_router": {"bytes": 2252634, "sources": ["decode1.hip", "internal.h", "wave.h"], "digest": "12230794b678fc80"},
+        "d1m_down": {"bytes": 4617741, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
+        "d1m_gateup": {"bytes": 6567798, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
+        "d1q_router": {"bytes": 2252610, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
+        "load_token": {"bytes": 15737, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7a5bfeb49a928526"},
+        "store_token": {"bytes": 42185, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7a5bfeb49a928526"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 168827973, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-        "down_mfma": {"bytes": 243229061, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-        "gateup_mfma": {"bytes": 310170764, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-        "quant_x": {"bytes": 33757477, "sources": ["grouped.hip", "internal.h", "wave.h"], "digest": "b062b90b03f6e480"},
-        "route_block": {"bytes": 4844101, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
-        "router_mfma": {"bytes": 37816408, "sources": ["internal.h", "route.hip", "wave.h"], "digest": "43a84f1887f6cd51"},
+        "combine": {"bytes": 168823326, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "down_mfma": {"bytes": 240393815, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "gateup_mfma": {"bytes": 304759529, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "quant_x": {"bytes": 33759056, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "route_block": {"bytes": 359407, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "route_scan": {"bytes": 149657, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "route_scatter": {"bytes": 1226228, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "route_topk": {"bytes": 4519504, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "router_mfma": {"bytes": 37832774, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "split_router": {"bytes": 4218255, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+    },
+    "batched_stack_zipf": {
+        "combine": {"bytes": 5280333, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "down_mfma": {"bytes": 38735808, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "gateup_mfma": {"bytes": 68219709, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "quant_x": {"bytes": 1074726, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
+        "route_small": {"bytes": 165691, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "router_small": {"bytes": 6490718, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+    },
+    "flashhead_decode": {
+        "head_final": {"bytes": 12735, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
+        "head_scores": {"bytes": 19583752, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
+        "head_search": {"bytes": 58843185, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
+        "head_select": {"bytes": 59799, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
     },
 }
 
