@@ -54,6 +54,7 @@ __device__ __forceinline__ v4i unpack_word(uint32_t w) {
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int s) {
   return s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
 }
+__device__ __forceinline__ uint32_t word_of(const uint2& q, int s) { return s == 0 ? q.x : q.y; }
 
 // Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
 // own L2.  Tile t of the expert-ordered tile list is given to the block with
@@ -219,23 +220,20 @@ __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
 // blocks share a CU; h is then re-coded with one scale per slot and part, and
 // the down projection sums the parts' contributions with their own scales.
 //
-// The fine form (NL = 3 limbs) runs NS = I / 128 parts (96 accumulation
-// registers per wave, two blocks per CU) and writes h in fp32 for the down
-// projection to code.
-//
 // Weights go straight from global memory into B operands: per N-subtile and
 // stage each lane holds two 16-byte pieces of one weight row (one load
 // instruction covers 32 contiguous bytes of 32 rows), refilled with the next
 // stage right after their last use, a full stage ahead.  The x limbs
 // (gathered through sorted_token) pass through registers into a
 // double-buffered LDS tile, two stages ahead; rows are padded to 272 bytes.
-template <int I, int NS, int NL>
-__global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
+template <int I, int NS>
+__global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    int8_t* __restrict__ hq, float* __restrict__ hs, float* __restrict__ hf, int64_t Tk) {
+    int8_t* __restrict__ hq, float* __restrict__ hs, int64_t Tk) {
+  constexpr int NL = 2;  // limbs
   constexpr int NW = 4;
   constexpr int IP = I / NS;            // h columns of the block's part
   constexpr int NBG = IP / 128;         // gate N-subtiles per wave (and as many up)
@@ -246,10 +244,9 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
   constexpr int HBYTES = 2 * TM * IP;   // h-limb staging in the epilogue (two limbs)
   constexpr int SMEM = 2 * ABUF > HBYTES ? 2 * ABUF : HBYTES;
   static_assert(TM == 32 && NB % 2 == 0, "tile shape");
-  static_assert(NL == 2 || (NL == 3 && NBG == 1), "three limbs: one 128-column part per block");
   __shared__ __align__(16) int8_t smem[SMEM];
   __shared__ float s_sx[TM];
-  __shared__ int s_xsum[NL == 2 ? 1 : 3][TM], s_tok[TM];
+  __shared__ int s_xsum[1][TM], s_tok[TM];
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
   __shared__ __align__(16) float s_al[2 * I];
@@ -268,10 +265,6 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
     const int* xi = reinterpret_cast<const int*>(xs);
     s_sx[tid] = tok >= 0 ? xs[tok] * xs[4 * T + tok] : 0.f;
     s_xsum[0][tid] = tok >= 0 ? xi[T + tok] : 0;
-    if constexpr (NL == 3) {
-      s_xsum[1][tid] = tok >= 0 ? xi[2 * T + tok] : 0;
-      s_xsum[2][tid] = tok >= 0 ? xi[3 * T + tok] : 0;
-    }
   }
   const int rowb = H / 4;
   const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
@@ -300,26 +293,18 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
     asrc[r] = xq + (int64_t)tok * NL * H + (int64_t)limb * H + 16 * seg;
     adst[r] = (limb * TM + slot) * ROWB + 16 * seg;
   }
-  uint4 as0, as1, as2, as3, as4, as5;  // one stage of x limbs in flight (named: kept in registers)
+  uint4 as0, as1, as2, as3;  // one stage of x limbs in flight (named: kept in registers)
   auto fetch_a = [&](int st) {
     as0 = *reinterpret_cast<const uint4*>(asrc[0] + st * KS);
     as1 = *reinterpret_cast<const uint4*>(asrc[1] + st * KS);
     as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
     as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
-    if constexpr (NL == 3) {
-      as4 = *reinterpret_cast<const uint4*>(asrc[4] + st * KS);
-      as5 = *reinterpret_cast<const uint4*>(asrc[5] + st * KS);
-    }
   };
   auto store_a = [&](int buf) {
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[0]) = as0;
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[1]) = as1;
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[2]) = as2;
     *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[3]) = as3;
-    if constexpr (NL == 3) {
-      *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[4]) = as4;
-      *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[5]) = as5;
-    }
   };
 
   v16i acc[NL][NB];  // [limb][N-subtile]
@@ -380,21 +365,15 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
         bq[half][b + 1] = *reinterpret_cast<const uint4*>(bsrc(b + 1, st1) + 32 * half);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          // 2 NL MFMAs against the 14 VALU of the next two unpacks
+          // 4 MFMAs against the 14 VALU of the next two unpacks
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 4 : 3, 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 4 : 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 3 : 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, NL == 2 ? 3 : 2, 0);
-          if constexpr (NL == 3) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          }
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -410,32 +389,6 @@ __global__ __launch_bounds__(256, NL == 2 ? NS : 2) void k_gateup_mfma(
   // per register quad.
   const int m = r32;
   const float sx = s_sx[m];
-  if constexpr (NL == 3) {
-    // fine form: h = silu(g) u in fp32 to hf[slot][I]; the down kernel codes it
-    const int xs0 = s_xsum[0][m], xs1 = s_xsum[1][m], xs2 = s_xsum[2][m];
-    auto dot3 = [&](int b, int j) {
-      return fmaf(16384.f, (float)(acc[0][b][j] - xs0),
-                  fmaf(128.f, (float)(acc[1][b][j] - xs1), (float)(acc[2][b][j] - xs2)));
-    };
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = cbase + 8 * i + 4 * kg;
-      const float4 ga = *reinterpret_cast<const float4*>(s_al + c);
-      const float4 ua = *reinterpret_cast<const float4*>(s_al + I + c);
-      const float gs[4] = {ga.x, ga.y, ga.z, ga.w}, us[4] = {ua.x, ua.y, ua.z, ua.w};
-      float hv4[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float gv = dot3(0, 4 * i + t) * (sx * gs[t]);
-        const float uv = dot3(1, 4 * i + t) * (sx * us[t]);
-        hv4[t] = silu_fast(gv) * uv;
-      }
-      if (m < np)
-        *reinterpret_cast<float4*>(hf + (int64_t)(p0 + m) * I + c) =
-            make_float4(hv4[0], hv4[1], hv4[2], hv4[3]);
-    }
-    return;
-  }
   const int xsum = s_xsum[0][m];
   float hv[NBG][16];
   float mx = 0.f;
@@ -673,28 +626,207 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   }
 }
 
-// Fine form of the down projection.  The tile's h rows arrive in fp32 and are
-// coded here into three limbs, one scale per slot over all I columns (wave w
-// codes rows [w TM/NWV, (w+1) TM/NWV)).  NHB blocks share a tile, each taking
-// H / NHB consecutive outputs; like the gate/up parts they are consecutive
-// blocks of one XCD.  Otherwise the loop is that of k_down_mfma, with three
-// limb accumulators per N-subtile that start at minus the slot's limb row sums,
-// and fp32 outputs stored straight from the accumulators (four consecutive
-// outputs of one slot per lane and store).
-template <int I, int NBW, int NWV>
+// ---- fine form: three limbs on 16x16x64 MFMAs ------------------------------------
+
+// v_mfma_i32_16x16x64_i8: A lane l supplies row l % 16 and 16 bytes of K group
+// l / 16; B lane l column l % 16, same K group; accumulator register j of lane
+// l holds row 4 (l / 16) + j, column l % 16.  With the weights as A and the
+// slots as B, a tile's 32 slots are two 16-column halves, and a tile with at
+// most 16 slots (the common case at a few tokens per expert) skips the second
+// half: half the matrix work of a 32-slot MFMA on a mostly empty tile.
+//
+// K order.  A stage (gate/up) or piece (down) covers 64 PW codes of a row:
+// 4 PW words of 16 codes (PW = 4; the down projection of I = 128 uses PW = 2).
+// Lane group kg = lane / 16 holds words PW kg .. PW kg + PW - 1 (one load) and
+// MFMA step s uses word PW kg + s; the activation bytes of that step sit at
+// offset 16 (PW kg + s) of the same 64 PW codes.
+
+// Gate/up: one block (4 waves) = one 32-slot tile x one 128-column part of h
+// (NS = I / 128 blocks per tile, consecutive blocks of one XCD).  Wave w owns
+// h columns [cb + 32 w, cb + 32 w + 32): gate subtiles b = 0, 1 and up subtiles
+// b = 2, 3 of 16 rows, so silu(g) u is formed in registers.  x arrives as three
+// int8 limbs through a double-buffered LDS tile; h leaves in fp32.
+template <int I>
+__global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
+    const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+    float* __restrict__ hf) {
+  constexpr int NS = I / 128;
+  constexpr int KS = 256;               // codes per stage (4 MFMA steps)
+  constexpr int ROWB = KS + 16;         // padded LDS row: one limb of one slot
+  constexpr int ABUF = 3 * TM * ROWB;   // one stage of x limbs
+  __shared__ __align__(16) int8_t smem[2 * ABUF];
+  __shared__ float s_sx[TM];
+  __shared__ int s_xsum[3][TM], s_tok[TM];
+  __shared__ __align__(16) float s_al[256];  // a_g | a_u of the part's 128 columns
+  const int local = blockIdx.x >> 3, part = local % NS;
+  const int tile = xcd_tile(8 * (local / NS) + (blockIdx.x & 7), *n_tiles);
+  if (tile < 0) return;
+  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
+  const int p0 = offsets[e] + m0;
+  const int np = min(TM, offsets[e + 1] - p0);
+  const bool two = np > 16;  // block-uniform: the second slot half has work
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, r16 = lane & 15;
+  if (tid < TM) {
+    const int tok = tid < np ? sorted_tok[p0 + tid] : -1;
+    s_tok[tid] = tok;
+    const int* xi = reinterpret_cast<const int*>(xs);
+    s_sx[tid] = tok >= 0 ? xs[tok] * xs[4 * T + tok] : 0.f;
+    s_xsum[0][tid] = tok >= 0 ? xi[T + tok] : 0;
+    s_xsum[1][tid] = tok >= 0 ? xi[2 * T + tok] : 0;
+    s_xsum[2][tid] = tok >= 0 ? xi[3 * T + tok] : 0;
+  }
+  const int rowb = H / 4;
+  const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
+  const int pbase = part * 128;             // first h column of the part
+  const int cbase = pbase + wave * 32;      // first h column of the wave
+  const uint8_t* brow = We + (int64_t)(cbase + r16) * rowb + 16 * kg;
+  auto bsrc = [&](int b, int st) -> const uint4* {
+    return reinterpret_cast<const uint4*>(brow + (b >= 2 ? (int64_t)I * rowb : 0) +
+                                          (int64_t)(16 * (b & 1)) * rowb + st * 64);
+  };
+  const float* al = alpha + (int64_t)e * (2 * I + H);
+  s_al[tid] = tid < 128 ? al[pbase + tid] : al[I + pbase + tid - 128];
+  __syncthreads();
+
+  // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
+  // 16-byte segment u % 16.  Rows past np read slot 0's token (discarded).
+  const int8_t* asrc[6];
+  int adst[6];
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int u = r * 256 + tid;
+    const int limb = u >> 9, slot = (u >> 4) & 31, seg = u & 15;
+    const int tok = s_tok[slot] >= 0 ? s_tok[slot] : s_tok[0];
+    asrc[r] = xq + (int64_t)tok * 3 * H + (int64_t)limb * H + 16 * seg;
+    adst[r] = (limb * TM + slot) * ROWB + 16 * seg;
+  }
+  uint4 as0, as1, as2, as3, as4, as5;  // one stage of x limbs in flight (named: kept in registers)
+  auto fetch_a = [&](int st) {
+    as0 = *reinterpret_cast<const uint4*>(asrc[0] + st * KS);
+    as1 = *reinterpret_cast<const uint4*>(asrc[1] + st * KS);
+    as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
+    as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
+    as4 = *reinterpret_cast<const uint4*>(asrc[4] + st * KS);
+    as5 = *reinterpret_cast<const uint4*>(asrc[5] + st * KS);
+  };
+  auto store_a = [&](int buf) {
+    int8_t* d = smem + buf * ABUF;
+    *reinterpret_cast<uint4*>(d + adst[0]) = as0;
+    *reinterpret_cast<uint4*>(d + adst[1]) = as1;
+    *reinterpret_cast<uint4*>(d + adst[2]) = as2;
+    *reinterpret_cast<uint4*>(d + adst[3]) = as3;
+    *reinterpret_cast<uint4*>(d + adst[4]) = as4;
+    *reinterpret_cast<uint4*>(d + adst[5]) = as5;
+  };
+
+  v4i acc[2][3][4];  // [slot half][limb][subtile]
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int l = 0; l < 3; ++l)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[h2][l][b] = v4i{0, 0, 0, 0};
+  const int nst = H / KS;
+  uint4 bq[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) bq[b] = *bsrc(b, 0);
+  fetch_a(0);
+  store_a(0);
+  fetch_a(min(1, nst - 1));
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int8_t* sa = smem + (st & 1) * ABUF + r16 * ROWB + 64 * kg;
+    // loads are issued unconditionally (past the end a stage reloads the last)
+    // so the count of loads in flight is the same at every use and the waits
+    // stay partial
+    const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      v4i wf[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) wf[b] = unpack_word(word_of(bq[b], s4));
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        const v4i x0 = *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 16 * s4);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[0][l][b] = mfma(wf[b], x0, acc[0][l][b]);
+      }
+      if (two) {
+#pragma unroll
+        for (int l = 0; l < 3; ++l) {
+          const v4i x1 = *reinterpret_cast<const v4i*>(sa + (l * TM + 16) * ROWB + 16 * s4);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[1][l][b] = mfma(wf[b], x1, acc[1][l][b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bq[b] = *bsrc(b, st1);
+    store_a((st + 1) & 1);  // stage st1; its buffer was last read in stage st - 1
+    fetch_a(st2);
+    __syncthreads();
+  }
+
+  // Epilogue: lane (r16, kg) holds slot 16 h2 + r16 and, in register j of
+  // subtile b, h column cbase + 16 (b & 1) + 4 kg + j.
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    if (h2 == 1 && !two) break;
+    const int m = 16 * h2 + r16;
+    const float sx = s_sx[m];
+    const int xs0 = s_xsum[0][m], xs1 = s_xsum[1][m], xs2 = s_xsum[2][m];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int cl = wave * 32 + 16 * b + 4 * kg;  // column within the part
+      const float4 ga = *reinterpret_cast<const float4*>(s_al + cl);
+      const float4 ua = *reinterpret_cast<const float4*>(s_al + 128 + cl);
+      const float gs[4] = {ga.x, ga.y, ga.z, ga.w}, us[4] = {ua.x, ua.y, ua.z, ua.w};
+      float hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gd = fmaf(16384.f, (float)(acc[h2][0][b][j] - xs0),
+                              fmaf(128.f, (float)(acc[h2][1][b][j] - xs1),
+                                   (float)(acc[h2][2][b][j] - xs2)));
+        const float ud = fmaf(16384.f, (float)(acc[h2][0][b + 2][j] - xs0),
+                              fmaf(128.f, (float)(acc[h2][1][b + 2][j] - xs1),
+                                   (float)(acc[h2][2][b + 2][j] - xs2)));
+        hv[j] = silu_fast(gd * (sx * gs[j])) * (ud * (sx * us[j]));
+      }
+      if (m < np)
+        *reinterpret_cast<float4*>(hf + (int64_t)(p0 + m) * I + pbase + cl) =
+            make_float4(hv[0], hv[1], hv[2], hv[3]);
+    }
+  }
+}
+
+// Down projection: the tile's h rows arrive in fp32 and are coded here into
+// three limbs, one scale per slot over all I columns (wave w codes rows
+// [w TM/NWV, (w+1) TM/NWV)).  NHB blocks share a tile, each taking H / NHB
+// consecutive outputs in chunks of CH = 64 NWV; like the gate/up parts they
+// are consecutive blocks of one XCD.  Wave w owns 4 subtiles of 16 outputs per
+// chunk; its accumulators start at minus the slot's limb row sums, and the fp32
+// outputs are stored straight from them (four consecutive outputs of one slot
+// per lane and store).
+template <int I, int NWV>
 __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     const float* __restrict__ hf, int H, int NHB, const uint8_t* __restrict__ packed,
     const float* __restrict__ alpha, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     float* __restrict__ y) {
   constexpr int NTH = 64 * NWV;
-  constexpr int NQ = I / 128;           // 16-byte pieces per lane and row
+  constexpr int PW = I >= 256 ? 4 : 2;  // words per lane and piece (I = 128: 128-code pieces)
+  constexpr int NQ = I / (64 * PW);     // pieces of a row (one load of PW words each)
   constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
-  constexpr int CH = 32 * NBW * NWV;    // outputs per chunk
+  constexpr int CH = 64 * NWV;          // outputs per chunk
   constexpr int RPW = TM / NWV;         // h rows coded per wave
   constexpr int VW = I >= 256 ? 4 : 2;  // h values per piece
   constexpr int NPC = I / (64 * VW);    // pieces per lane and row
-  static_assert(RPW * NWV == TM && NPC * 64 * VW == I, "coding shape");
+  static_assert(RPW * NWV == TM && NPC * 64 * VW == I && NQ >= 1, "coding shape");
+  typedef typename std::conditional<PW == 4, uint4, uint2>::type wq_t;
   __shared__ __align__(16) int8_t sA[3][TM][ROWB];
   __shared__ float s_sc[TM];
   __shared__ int s_sum[3][TM];
@@ -705,19 +837,21 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int p0 = offsets[e] + m0;
   const int np = min(TM, offsets[e + 1] - p0);
+  const bool two = np > 16;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kg = lane >> 5, r32 = lane & 31;
+  const int kg = lane >> 4, r16 = lane & 15;
   const int nch = H / CH / NHB;  // chunks of this block
   const int o0 = hp * nch * CH;  // its first output
   const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4;
   const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0;
-  const uint8_t* wrow = Wd + (int64_t)(o0 + 32 * NBW * wave + r32) * (I / 4) + 16 * kg;
+  const uint8_t* wrow = Wd + (int64_t)(o0 + 64 * wave + r16) * (I / 4) + 4 * PW * kg;
   auto bptr = [&](int c, int b, int q) {
-    return reinterpret_cast<const uint4*>(wrow + (int64_t)(c * CH + 32 * b) * (I / 4) + 32 * q);
+    return reinterpret_cast<const wq_t*>(wrow + (int64_t)(c * CH + 16 * b) * (I / 4) +
+                                         16 * PW * q);
   };
-  uint4 bq[NBW][NQ];
+  wq_t bq[4][NQ];
 #pragma unroll
-  for (int b = 0; b < NBW; ++b)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int q = 0; q < NQ; ++q) bq[b][q] = *bptr(0, b, q);
   // the wave's h rows (rows past np are zero), all loads before any use
@@ -781,61 +915,78 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     }
   }
   __syncthreads();
-  const float sc = s_sc[r32];
-  const int sum0 = s_sum[0][r32], sum1 = s_sum[1][r32], sum2 = s_sum[2][r32];
-  const int8_t* sa = &sA[0][r32][64 * kg];
-  float* yrow = y + (int64_t)(p0 + r32) * H + o0 + 32 * NBW * wave;
+  float sc[2];
+  int sum[2][3];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int m = 16 * h2 + r16;
+    sc[h2] = s_sc[m];
+    sum[h2][0] = s_sum[0][m];
+    sum[h2][1] = s_sum[1][m];
+    sum[h2][2] = s_sum[2][m];
+  }
+  const int8_t* sa = &sA[0][r16][16 * PW * kg];
 
   for (int c = 0; c < nch; ++c) {
-    // keeps the A-operand LDS reads inside the loop (hoisted, they would hold
-    // 192 registers for the whole block)
+    // keeps the B-operand LDS reads inside the loop (hoisted, they would hold
+    // most of the registers for the whole block)
     asm volatile("" ::: "memory");
     const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
-    v16i acc[3][NBW];  // [limb][N-subtile]
+    v4i acc[2][3][4];  // [slot half][limb][subtile]
 #pragma unroll
-    for (int b = 0; b < NBW; ++b)
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        acc[0][b][j] = -sum0;
-        acc[1][b][j] = -sum1;
-        acc[2][b][j] = -sum2;
-      }
+      for (int l = 0; l < 3; ++l)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[h2][l][b] = v4i{-sum[h2][l], -sum[h2][l], -sum[h2][l],
+                                                        -sum[h2][l]};
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const v4i a0 = *reinterpret_cast<const v4i*>(sa + 128 * q + 16 * s4);
-        const v4i a1 = *reinterpret_cast<const v4i*>(sa + TM * ROWB + 128 * q + 16 * s4);
-        const v4i a2 = *reinterpret_cast<const v4i*>(sa + 2 * TM * ROWB + 128 * q + 16 * s4);
+      for (int s4 = 0; s4 < PW; ++s4) {
+        v4i wf[4];
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-          const v4i wf = unpack_word(word_of(bq[b][q], s4));
-          acc[0][b] = mfma32(wf, a0, acc[0][b]);
-          acc[1][b] = mfma32(wf, a1, acc[1][b]);
-          acc[2][b] = mfma32(wf, a2, acc[2][b]);
+        for (int b = 0; b < 4; ++b) wf[b] = unpack_word(word_of(bq[b][q], s4));
+#pragma unroll
+        for (int l = 0; l < 3; ++l) {
+          const v4i x0 =
+              *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 64 * PW * q + 16 * s4);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[0][l][b] = mfma(wf[b], x0, acc[0][l][b]);
+        }
+        if (two) {
+#pragma unroll
+          for (int l = 0; l < 3; ++l) {
+            const v4i x1 = *reinterpret_cast<const v4i*>(sa + (l * TM + 16) * ROWB +
+                                                         64 * PW * q + 16 * s4);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[1][l][b] = mfma(wf[b], x1, acc[1][l][b]);
+          }
         }
       }
 #pragma unroll
-      for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
+      for (int b = 0; b < 4; ++b) bq[b][q] = *bptr(cn, b, q);
     }
-    // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk
+    // register j of subtile b: output 64 wave + 16 b + 4 kg + j of the chunk
 #pragma unroll
-    for (int b = 0; b < NBW; ++b)
+    for (int h2 = 0; h2 < 2; ++h2) {
+      if (h2 == 1 && !two) break;
+      const int m = 16 * h2 + r16;
+      float* yrow = y + (int64_t)(p0 + m) * H + o0 + c * CH + 64 * wave;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ol = 32 * b + 8 * i + 4 * kg;
-        const float4 a = *reinterpret_cast<const float4*>(s_ad + c * CH + 32 * NBW * wave + ol);
+      for (int b = 0; b < 4; ++b) {
+        const int ol = 16 * b + 4 * kg;
+        const float4 a = *reinterpret_cast<const float4*>(s_ad + c * CH + 64 * wave + ol);
         float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int j = 4 * i + t;
-          v[t] = sc * fmaf(16384.f, (float)acc[0][b][j],
-                           fmaf(128.f, (float)acc[1][b][j], (float)acc[2][b][j]));
-        }
-        if (r32 < np)
-          *reinterpret_cast<float4*>(yrow + c * CH + ol) =
+        for (int j = 0; j < 4; ++j)
+          v[j] = sc[h2] * fmaf(16384.f, (float)acc[h2][0][b][j],
+                               fmaf(128.f, (float)acc[h2][1][b][j], (float)acc[h2][2][b][j]));
+        if (m < np)
+          *reinterpret_cast<float4*>(yrow + ol) =
               make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
       }
+    }
   }
 }
 
@@ -928,17 +1079,15 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t
     constexpr int I_ = decltype(i_tag)::value;
     if (fine) {
       constexpr int NS_ = I_ / 128;
-      launch("gateup_mfma", k_gateup_mfma<I_, NS_, 3>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T,
-             d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs,
-             ws.h, Tk);
-      launch("down_mfma", k_down3_mfma<I_, 2, 4>, nt * nhb, 256, 4 * d.H / nhb, s, ws.h, d.H, nhb,
+      launch("gateup_mfma", k_gateup3_mfma<I_>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T, d.H,
+             packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.h);
+      launch("down_mfma", k_down3_mfma<I_, 4>, nt * nhb, 256, 4 * d.H / nhb, s, ws.h, d.H, nhb,
              packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, (float*)ws.y);
     } else {
       // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
       constexpr int NS_ = I_ >= 512 ? 2 : 1;
-      launch("gateup_mfma", k_gateup_mfma<I_, NS_, 2>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T,
-             d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs,
-             ws.h, Tk);
+      launch("gateup_mfma", k_gateup_mfma<I_, NS_>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T,
+             d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
       // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
       launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt * nhb, 256,
              4 * d.H / nhb + 4 * 32 * (64 * 2 + 16), s, ws.hq, ws.hs, Tk, d.H, nhb, packed, alpha,
