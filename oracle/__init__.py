@@ -55,6 +55,10 @@ def _L():
                                                 _P, _P, _P, _P, _P, _P, _P, _P]),
             "oracle_moe_stack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
                                                 _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "oracle_moe_layer_a8": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I64, _P,
+                                                   _P, _P, _P, _P, _P, _P, _P, _P]),
+            "oracle_moe_stack_a8": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
             "oracle_rms_normalize": (None, [_P, _I64, _I32, ctypes.c_double, _P]),
             "oracle_num_threads": (ctypes.c_int, []),
             "oracle_head_scores": (None, [_P, _I32, _P, _I32, _P]),
@@ -178,8 +182,9 @@ def rms_normalize(x: np.ndarray) -> np.ndarray:
 
 
 def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = False,
-              prenorm: bool = False):
-    """One MoE layer in fp64 (on x / rms(x) when prenorm).  Returns dict(out, logits, idx, gate)."""
+              prenorm: bool = False, a8: bool = False):
+    """One MoE layer in fp64 (on x / rms(x) when prenorm).  Returns dict(out, logits, idx, gate).
+    a8: the integer-activation variant (x and h coded as int8 with a per-row scale)."""
     x = _c(x, np.float64)
     T, H = x.shape
     Wr = _c(Wr, np.float32)
@@ -192,9 +197,9 @@ def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = 
     logits = np.empty((T, E), np.float64)
     idx = np.empty((T, k), np.int32)
     gate = np.empty((T, k), np.float64)
-    rc = _L().oracle_moe_layer(H, E, k, inter, int(renorm), int(prenorm), T, _ptr(x), _ptr(Wr),
-                               _ptr(bias), _ptr(packed), _ptr(alpha), _ptr(out), _ptr(logits), _ptr(idx),
-                               _ptr(gate))
+    fn = _L().oracle_moe_layer_a8 if a8 else _L().oracle_moe_layer
+    rc = fn(H, E, k, inter, int(renorm), int(prenorm), T, _ptr(x), _ptr(Wr), _ptr(bias),
+            _ptr(packed), _ptr(alpha), _ptr(out), _ptr(logits), _ptr(idx), _ptr(gate))
     if rc != 0:
         raise ValueError(f"oracle_moe_layer failed ({rc})")
     return dict(out=out, logits=logits, idx=idx, gate=gate)
@@ -202,7 +207,7 @@ def moe_layer(x, Wr, bias, packed, alpha, *, k: int, inter: int, renorm: bool = 
 
 def moe_stack(x, Wr_list, bias_list, packed_list, alpha_list, *, k: int, inter: int,
               renorm: bool = False, prenorm: bool = True, keep_logits: bool = True,
-              keep_delta: bool = True):
+              keep_delta: bool = True, a8: bool = False):
     """x^(l+1) = x^(l) + MoE_l(x^(l) / rms(x^(l))) over L layers in fp64 (no
     normalisation when prenorm is False).
 
@@ -227,10 +232,10 @@ def moe_stack(x, Wr_list, bias_list, packed_list, alpha_list, *, k: int, inter: 
     idx = np.empty((L, T, k), np.int32)
     gate = np.empty((L, T, k), np.float64)
     delta = np.empty((L, T, H), np.float64) if keep_delta else None
-    rc = _L().oracle_moe_stack(H, E, k, inter, int(renorm), int(prenorm), L, T, _ptr(x),
-                               ctypes.cast(Wr_p, _P), ctypes.cast(b_p, _P) if b_p else None,
-                               ctypes.cast(pk_p, _P), ctypes.cast(al_p, _P), _ptr(logits),
-                               _ptr(idx), _ptr(gate), _ptr(delta))
+    fn = _L().oracle_moe_stack_a8 if a8 else _L().oracle_moe_stack
+    rc = fn(H, E, k, inter, int(renorm), int(prenorm), L, T, _ptr(x), ctypes.cast(Wr_p, _P),
+            ctypes.cast(b_p, _P) if b_p else None, ctypes.cast(pk_p, _P), ctypes.cast(al_p, _P),
+            _ptr(logits), _ptr(idx), _ptr(gate), _ptr(delta))
     if rc != 0:
         raise ValueError(f"oracle_moe_stack failed ({rc})")
     return dict(x=x, logits=logits, idx=idx, gate=gate, delta=delta)

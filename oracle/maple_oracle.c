@@ -200,6 +200,59 @@ void oracle_expert_ffn(const double* x, int32_t H, int32_t I, const uint8_t* blo
 
 /* ---- one layer ---------------------------------------------------------- */
 
+/* ---- integer-activation (A8) variant --------------------------------------
+ *
+ * A reading of the pages' "integer additions" (linlog.top article
+ * "Maple-Preview", section "三值权重：把乘法变成加法") in which the activations
+ * are integers too: an activation row v is coded as
+ *   q_j = clamp(rint(v_j * (127 / max|v|)), -127, 127),  scale = max|v| / 127,
+ * with fp32 arithmetic for the coding (so that both implementations take the
+ * same integer decisions), x once per token (before the norm's scalar) and h
+ * once per routed (token, expert) over all I.  The products of ternary weights
+ * and q are exact integer sums; everything else is the plain layer in fp64. */
+static void code_a8(const float* v, int32_t n, int32_t* q, double* scale) {
+  float amax = 0.f;
+  for (int32_t j = 0; j < n; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const float s = amax > 0.f ? amax / 127.f : 1.f;
+  const float inv = amax > 0.f ? 127.f / amax : 1.f;
+  for (int32_t j = 0; j < n; ++j) {
+    const float p = v[j] * inv;
+    long r = lrintf(p);
+    if (r > 127) r = 127;
+    if (r < -127) r = -127;
+    q[j] = (int32_t)r;
+  }
+  *scale = (double)s;
+}
+
+/* sum_j w_rj * q_j for one packed row, exact in int64. */
+static int64_t ternary_dot_i(const uint8_t* row, const int32_t* q, int32_t n) {
+  int64_t acc = 0;
+  for (int32_t j = 0; j < n; ++j) acc += (int64_t)(code_at(row, j) - 1) * q[j];
+  return acc;
+}
+
+/* One expert on coded x (qx, scale sx, which includes the norm's scalar):
+ * g, u from integer sums, h = silu(g) u rounded to fp32 and coded, y from
+ * integer sums.  hf (I floats) and qh (I ints) are scratch. */
+static void expert_ffn_a8(const int32_t* qx, double sx, int32_t H, int32_t I,
+                          const uint8_t* blob, const float* alpha, double* y, float* hf,
+                          int32_t* qh) {
+  const uint8_t* Wg = blob;
+  const uint8_t* Wu = blob + (int64_t)I * H / 4;
+  const uint8_t* Wd = blob + 2 * (int64_t)I * H / 4;
+  for (int32_t i = 0; i < I; ++i) {
+    const double gi = (double)alpha[i] * sx * (double)ternary_dot_i(Wg + (int64_t)i * H / 4, qx, H);
+    const double ui =
+        (double)alpha[I + i] * sx * (double)ternary_dot_i(Wu + (int64_t)i * H / 4, qx, H);
+    hf[i] = (float)(gi / (1.0 + exp(-gi)) * ui);
+  }
+  double sh;
+  code_a8(hf, I, qh, &sh);
+  for (int32_t o = 0; o < H; ++o)
+    y[o] = (double)alpha[2 * I + o] * sh * (double)ternary_dot_i(Wd + (int64_t)o * I / 4, qh, I);
+}
+
 static void layer_token(int32_t H, int32_t E, int32_t k, int32_t I, const double* xt,
                         const uint8_t* packed, const float* alpha, const int32_t* idx_t,
                         const double* gate_t, double* out_t, double* h, double* y, int32_t par) {
@@ -229,6 +282,11 @@ void oracle_rms_normalize(const double* x, int64_t T, int32_t H, double eps, dou
 /* out[t] = sum_j gate[t,j] * FFN_{idx[t,j]}(x[t]), summed in selection order.
  * With prenorm != 0 the router and the experts see x[t] / rms(x[t]).
  * logits (T x E), idx (T x k), gate (T x k) receive the routing. */
+static int moe_layer_a8(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                        int32_t prenorm, int64_t T, const double* x_in, const float* Wr,
+                        const float* bias, const uint8_t* packed, const float* alpha,
+                        double* out, double* logits, int32_t* idx, double* gate);
+
 int oracle_moe_layer(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
                      int32_t prenorm, int64_t T, const double* x_in, const float* Wr,
                      const float* bias, const uint8_t* packed, const float* alpha, double* out,
@@ -273,13 +331,103 @@ int oracle_moe_layer(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
   return 0;
 }
 
+/* The A8 layer: routing as in oracle_moe_layer (fp64 logits of x, or of
+ * x / rms(x) with prenorm); experts on coded activations (see expert_ffn_a8),
+ * x coded from the raw row and the norm's scalar 1/rms applied to its scale. */
+static int moe_layer_a8(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                        int32_t prenorm, int64_t T, const double* x_in, const float* Wr,
+                        const float* bias, const uint8_t* packed, const float* alpha,
+                        double* out, double* logits, int32_t* idx, double* gate) {
+  if (H <= 0 || I <= 0 || H % 16 || I % 16 || k < 1 || k > E || T < 0) return -1;
+  if (T == 0) return 0;
+  double* xn = NULL;
+  const double* xr = x_in;
+  if (prenorm) {
+    xn = (double*)malloc(sizeof(double) * (size_t)(T * H));
+    oracle_rms_normalize(x_in, T, H, ORACLE_RMS_EPS, xn);
+    xr = xn;
+  }
+  oracle_router_logits(xr, T, H, Wr, bias, E, logits);
+  oracle_topk(logits, T, E, k, renorm, idx, gate);
+  const int64_t blob = 3 * (int64_t)H * I / 4;
+#pragma omp parallel
+  {
+    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    int32_t* qx = (int32_t*)malloc(sizeof(int32_t) * (size_t)H);
+    float* hf = (float*)malloc(sizeof(float) * (size_t)I);
+    int32_t* qh = (int32_t*)malloc(sizeof(int32_t) * (size_t)I);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      const double* xt = x_in + t * H;
+      double ss = 0.0;
+      for (int32_t j = 0; j < H; ++j) {
+        xf[j] = (float)xt[j];
+        ss += xt[j] * xt[j];
+      }
+      double sx;
+      code_a8(xf, H, qx, &sx);
+      if (prenorm) sx /= sqrt(ss / H + ORACLE_RMS_EPS);
+      double* ot = out + t * H;
+      for (int32_t o = 0; o < H; ++o) ot[o] = 0.0;
+      for (int32_t j = 0; j < k; ++j) {
+        const int32_t e = idx[t * k + j];
+        expert_ffn_a8(qx, sx, H, I, packed + e * blob, alpha + (int64_t)e * (2 * I + H), y, hf,
+                      qh);
+        for (int32_t o = 0; o < H; ++o) ot[o] += gate[t * k + j] * y[o];
+      }
+    }
+    free(xf);
+    free(qx);
+    free(hf);
+    free(qh);
+    free(y);
+  }
+  free(xn);
+  return 0;
+}
+
+int oracle_moe_layer_a8(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                        int32_t prenorm, int64_t T, const double* x_in, const float* Wr,
+                        const float* bias, const uint8_t* packed, const float* alpha,
+                        double* out, double* logits, int32_t* idx, double* gate) {
+  return moe_layer_a8(H, E, k, I, renorm, prenorm, T, x_in, Wr, bias, packed, alpha, out, logits,
+                      idx, gate);
+}
+
 /* ---- stack -------------------------------------------------------------- */
 
 /* x^(l+1) = x^(l) + MoE_l(n(x^(l))) for l = 0..L-1, in place on x (T x H), where
  * n is the pre-norm above when prenorm != 0 and the identity otherwise.
  * Per-layer routing and deltas go to the optional outputs:
  * logits_all [L,T,E], idx_all [L,T,k], gate_all [L,T,k], delta_all [L,T,H]. */
+static int moe_stack(int32_t a8, int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                     int32_t prenorm, int32_t n_layers, int64_t T, double* x, const float* const* Wr,
+                     const float* const* bias, const uint8_t* const* packed,
+                     const float* const* alpha, double* logits_all, int32_t* idx_all,
+                     double* gate_all, double* delta_all);
+
 int oracle_moe_stack(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                     int32_t prenorm, int32_t n_layers, int64_t T, double* x, const float* const* Wr,
+                     const float* const* bias, const uint8_t* const* packed,
+                     const float* const* alpha, double* logits_all, int32_t* idx_all,
+                     double* gate_all, double* delta_all) {
+  return moe_stack(0, H, E, k, I, renorm, prenorm, n_layers, T, x, Wr, bias, packed, alpha,
+                   logits_all, idx_all, gate_all, delta_all);
+}
+
+/* The same stack with every layer in the A8 variant. */
+int oracle_moe_stack_a8(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
+                        int32_t prenorm, int32_t n_layers, int64_t T, double* x,
+                        const float* const* Wr, const float* const* bias,
+                        const uint8_t* const* packed, const float* const* alpha,
+                        double* logits_all, int32_t* idx_all, double* gate_all,
+                        double* delta_all) {
+  return moe_stack(1, H, E, k, I, renorm, prenorm, n_layers, T, x, Wr, bias, packed, alpha,
+                   logits_all, idx_all, gate_all, delta_all);
+}
+
+static int moe_stack(int32_t a8, int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
                      int32_t prenorm, int32_t n_layers, int64_t T, double* x, const float* const* Wr,
                      const float* const* bias, const uint8_t* const* packed,
                      const float* const* alpha, double* logits_all, int32_t* idx_all,
@@ -294,8 +442,9 @@ int oracle_moe_stack(int32_t H, int32_t E, int32_t k, int32_t I, int32_t renorm,
     double* L_lg = logits_all ? logits_all + (int64_t)l * T * E : lg;
     int32_t* L_id = idx_all ? idx_all + (int64_t)l * T * k : id;
     double* L_gt = gate_all ? gate_all + (int64_t)l * T * k : gt;
-    rc = oracle_moe_layer(H, E, k, I, renorm, prenorm, T, x, Wr[l], bias ? bias[l] : NULL, packed[l],
-                          alpha[l], out, L_lg, L_id, L_gt);
+    rc = (a8 ? moe_layer_a8 : oracle_moe_layer)(H, E, k, I, renorm, prenorm, T, x, Wr[l],
+                                               bias ? bias[l] : NULL, packed[l], alpha[l], out,
+                                               L_lg, L_id, L_gt);
     for (int64_t i = 0; i < T * H; ++i) {
       x[i] += out[i];
       if (delta_all) delta_all[(int64_t)l * T * H + i] = out[i];

@@ -427,3 +427,68 @@ def test_hand_worked_micro_layer_closed_form():
     assert list(r["idx"][0]) == [0, 1]
     np.testing.assert_allclose(r["gate"][0], p[:2], rtol=1e-14)
     np.testing.assert_allclose(r["out"][0], expect, rtol=1e-13, atol=0)
+
+
+# ---- integer-activation (A8) variant ----------------------------------------------
+
+def test_a8_on_codable_inputs_equals_the_hand_worked_layer():
+    """The micro layer above again, in the A8 variant.  x = 1 is on the int8 grid
+    (q = 127, scale 1/127) and every expert's h has equal entries (per-row alphas
+    are constant), so h codes exactly too (q = +-127): the A8 result equals the
+    closed form up to the fp32 rounding of the two scales."""
+    H = I = 16
+    E, k = 4, 2
+    c = np.array([0.5, 0.25, 0.0, -0.25])
+    Wr = np.repeat((c / 16.0)[:, None], H, axis=1).astype(np.float32)
+    rng = np.random.default_rng(3)
+    W = rng.integers(-1, 2, size=(E, 3 * H * I), dtype=np.int8)
+    n = H * I
+    W[0, :n], W[0, n:2 * n], W[0, 2 * n:] = 1, -1, 1
+    W[1, :n], W[1, n:2 * n] = -1, 1
+    wd1 = np.zeros((H, I), np.int8)
+    wd1[:, :8] = 1
+    W[1, 2 * n:] = wd1.reshape(-1)
+    alpha = np.zeros((E, 2 * I + H), np.float32)
+    alpha[0, :I], alpha[0, I:2 * I], alpha[0, 2 * I:] = 0.1, 0.05, 0.02
+    alpha[1, :I], alpha[1, I:2 * I] = 0.03, 0.07
+    alpha[1, 2 * I:] = (0.04 + 0.001 * np.arange(H)).astype(np.float32)
+    alpha[2:] = 0.05
+    packed = oracle.pack_layer(W, H, I)
+    x = np.ones((1, H))
+    r = oracle.moe_layer(x, Wr, None, packed, alpha, k=k, inter=I, a8=True)
+
+    def silu(z):
+        return z / (1.0 + math.exp(-z))
+    a = alpha.astype(np.float64)
+    h0 = silu(16 * a[0, 0]) * (-16 * a[0, I])
+    h1 = silu(-16 * a[1, 0]) * (16 * a[1, I])
+    p = np.exp(c - c.max()) / np.exp(c - c.max()).sum()
+    expect = p[0] * a[0, 2 * I:] * 16 * h0 + p[1] * a[1, 2 * I:] * 8 * h1
+    assert list(r["idx"][0]) == [0, 1]
+    np.testing.assert_allclose(r["out"][0], expect, rtol=2e-6, atol=0)
+
+
+def test_a8_error_is_that_of_8_bit_activations():
+    """On the decode-layer inputs the A8 result differs from the exact layer by
+    the coding error of 8-bit activations (a few percent), with the same routing."""
+    w = S.WORKLOADS["decode_layer"]
+    _, Wr, _, _, alpha, packed = make_layer(w)
+    x = S.x_as_f32(w, S.gen_x(w, 8)).astype(np.float64)
+    a = oracle.moe_layer(x, Wr, None, packed, alpha, k=w.top_k, inter=w.inter)
+    b = oracle.moe_layer(x, Wr, None, packed, alpha, k=w.top_k, inter=w.inter, a8=True)
+    assert np.array_equal(a["idx"], b["idx"])
+    rel = np.linalg.norm(a["out"] - b["out"]) / np.linalg.norm(a["out"])
+    assert 5e-3 < rel < 6e-2, rel
+
+
+def test_a8_prenorm_ignores_power_of_two_scale():
+    """With the pre-norm, x and 2^m x give the same A8 output: the codes are the
+    same integers and the scale's factor cancels against 1/rms (only eps, 1e-6
+    against mean(x^2) ~ 1, breaks the cancellation)."""
+    w = S.WORKLOADS["tiny_layer"]
+    x, Wr, _, _, alpha, packed = make_layer(w)
+    a = oracle.moe_layer(x, Wr, None, packed, alpha, k=w.top_k, inter=w.inter, prenorm=True,
+                         a8=True)
+    b = oracle.moe_layer(8.0 * x, Wr, None, packed, alpha, k=w.top_k, inter=w.inter,
+                         prenorm=True, a8=True)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-5, atol=1e-6)
