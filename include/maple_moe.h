@@ -86,6 +86,15 @@ typedef enum maple_status {
  * 1.5x the matrix work of the default two-limb form).  Stack calls always use
  * the fine form; for a layer call this flag asks for it. */
 #define MAPLE_FINE_LIMBS 0x40u
+/* Integer-activation (A8) variant, a different computation from the layer
+ * above: x (per token, before the norm's scalar) and h (per routed token and
+ * expert, over all I) are coded as q = clamp(rint(v * 127 / max|v|), -127, 127)
+ * with scale max|v| / 127 (fp32 arithmetic), so every ternary product is a sum
+ * of int8 activations (one reading of the pages' "integer additions": the
+ * linlog.top article, section "三值权重：把乘法变成加法").  About 2.6e-2 relative
+ * error against the exact layer.  Always on the grouped path; excludes
+ * MAPLE_FORCE_GEMV and MAPLE_FINE_LIMBS; applies to layer and stack calls. */
+#define MAPLE_ACT_INT8 0x80u
 
 /* Limits: hidden a power of two in [256, 4096]; inter a power of two in
  * [128, 2048]; 1 <= top_k <= 8; top_k <= n_experts <= 256;

@@ -32,6 +32,7 @@ MAPLE_RMS_NORM = 0x4
 MAPLE_FORCE_GEMV = 0x10
 MAPLE_FORCE_GROUPED = 0x20
 MAPLE_FINE_LIMBS = 0x40
+MAPLE_ACT_INT8 = 0x80
 MAPLE_MAX_TOKENS = 1 << 20
 MAPLE_GEMV_MAX_TOKENS = 64
 

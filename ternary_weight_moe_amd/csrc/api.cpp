@@ -145,13 +145,17 @@ int hip_fail(hipError_t e, const char* what) {
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 constexpr uint32_t kKnownFlags = MAPLE_X_BF16 | MAPLE_RENORM_TOPK | MAPLE_RMS_NORM |
-                                 MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED | MAPLE_FINE_LIMBS;
+                                 MAPLE_FORCE_GEMV | MAPLE_FORCE_GROUPED | MAPLE_FINE_LIMBS |
+                                 MAPLE_ACT_INT8;
 
 int check_dims(const maple_moe_dims* d, Dims* out) {
   if (!d) return fail(MAPLE_ERR_INVALID_ARG, "dims is NULL");
   if (d->flags & ~kKnownFlags) return fail(MAPLE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
   if ((d->flags & MAPLE_FORCE_GEMV) && (d->flags & MAPLE_FORCE_GROUPED))
     return fail(MAPLE_ERR_INVALID_ARG, "MAPLE_FORCE_GEMV and MAPLE_FORCE_GROUPED both set");
+  if ((d->flags & MAPLE_ACT_INT8) && (d->flags & (MAPLE_FORCE_GEMV | MAPLE_FINE_LIMBS)))
+    return fail(MAPLE_ERR_INVALID_ARG,
+                "MAPLE_ACT_INT8 excludes MAPLE_FORCE_GEMV and MAPLE_FINE_LIMBS");
   if (!is_pow2(d->hidden) || d->hidden < 256 || d->hidden > 4096)
     return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "hidden=%d: need a power of two in [256, 4096]",
                 d->hidden);
@@ -172,7 +176,7 @@ constexpr uint32_t kStackCall = 0x80000000u;
 
 bool use_gemv(const Dims& d, int64_t T) {
   if (d.flags & MAPLE_FORCE_GEMV) return true;
-  if (d.flags & MAPLE_FORCE_GROUPED) return false;
+  if (d.flags & (MAPLE_FORCE_GROUPED | MAPLE_ACT_INT8)) return false;
   if (d.I > MAPLE_GROUPED_MAX_INTER) return true;  // beyond the grouped kernels' shapes
   return T <= ((d.flags & kStackCall) ? maple::kGemvAutoStack : maple::kGemvAuto);
 }
@@ -225,8 +229,9 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
               const float* next_wr, hipStream_t s) {
   const bool gemv = use_gemv(d, T);
   // stack calls take the fine grouped form: their routing sits downstream of
-  // every earlier layer's error
-  const bool fine = (d.flags & (kStackCall | MAPLE_FINE_LIMBS)) != 0;
+  // every earlier layer's error; MAPLE_ACT_INT8 asks for one-limb activations
+  const int nl = (d.flags & MAPLE_ACT_INT8) ? 1
+                 : (d.flags & (kStackCall | MAPLE_FINE_LIMBS)) ? 3 : 2;
   hipError_t e = hipSuccess;
   if (gemv && T == 1) {  // one token: router, top-k + gate/up, down + combine
     e = maple::launch_decode1(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta,
@@ -234,7 +239,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   } else {
     if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and large-T router use them
-      e = maple::launch_quant_x(d, T, x, x_bf16, fine, ws, s);
+      e = maple::launch_quant_x(d, T, x, x_bf16, nl, ws, s);
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }
     e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 4 * T,
@@ -245,7 +250,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
     if (gemv)
       e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);
     else
-      e = maple::launch_grouped_ffn(d, T, fine, packed, alpha, ws, out, resid, delta, s);
+      e = maple::launch_grouped_ffn(d, T, nl, packed, alpha, ws, out, resid, delta, s);
     if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   }
   if (dbg) {

@@ -15,7 +15,10 @@
 // be) with per-slot fp16 expert outputs make the fast form.  Three limbs with
 // fp32 h and fp32 expert outputs make the fine form, whose error stays near
 // fp32 rounding: a 24-layer residual stack needs that, since its routing
-// decisions sit downstream of every earlier layer's error.
+// decisions sit downstream of every earlier layer's error.  The same kernels
+// with one limb (q = rint(v 127 / max|v|)) are the integer-activation (A8)
+// variant: the ternary products become sums of int8 activations, at about
+// 2.6e-2 relative error against the exact layer.
 //
 // Weight unpacking.  In layout v1 one 32-bit word holds 16 consecutive k, and
 // (word >> 2b) & 0x03030303 gives k = 4b..4b+3 as four bytes, so a word
@@ -80,15 +83,15 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
 // instruction covers up to 1 KB of contiguous row; a lane holds its pieces of 8
 // (bf16) or 4 (fp32) values.  H % 256 == 0.
 // xq: [T][NL][H] limbs.  xs planes of T: scale | row sums (int bits: sum q for
-// two limbs; sum hi, sum mid, sum lo for three) | 1/rms at plane 4.
+// one or two limbs; sum hi, sum mid, sum lo for three) | 1/rms at plane 4.
 template <bool BF16, int NL>
 __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int T, int H,
                                                  int norm, int8_t* __restrict__ xq,
                                                  float* __restrict__ xs) {
   constexpr int VPP = BF16 ? 8 : 4;   // values per 16-byte piece
   constexpr int MAXN = 64 / VPP;      // pieces per lane at H = 4096
-  constexpr float QM = NL == 2 ? kQ2Max : kQ3Max;
-  constexpr int QI = NL == 2 ? 16256 : 2080768;
+  constexpr float QM = NL == 1 ? 127.f : NL == 2 ? kQ2Max : kQ3Max;
+  constexpr int QI = NL == 1 ? 127 : NL == 2 ? 16256 : 2080768;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -133,7 +136,10 @@ __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int
       for (int q = 0; q < VPP; ++q) {
         const int qq = code_q(v[i][q], inv, QI);
         const int sh = 8 * (q & 3);
-        if constexpr (NL == 2) {
+        if constexpr (NL == 1) {
+          lw[0][q >> 2] |= (uint32_t)(qq & 0xFF) << sh;
+          sum0 += qq;
+        } else if constexpr (NL == 2) {
           int hi, lo;
           split2(qq, &hi, &lo);
           lw[0][q >> 2] |= (uint32_t)(hi & 0xFF) << sh;
@@ -626,7 +632,7 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   }
 }
 
-// ---- fine form: three limbs on 16x16x64 MFMAs ------------------------------------
+// ---- fine form (three limbs) and A8 (one limb) on 16x16x64 MFMAs ---------------
 
 // v_mfma_i32_16x16x64_i8: A lane l supplies row l % 16 and 16 bytes of K group
 // l / 16; B lane l column l % 16, same K group; accumulator register j of lane
@@ -646,20 +652,21 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
 // h columns [cb + 32 w, cb + 32 w + 32): gate subtiles b = 0, 1 and up subtiles
 // b = 2, 3 of 16 rows, so silu(g) u is formed in registers.  x arrives as three
 // int8 limbs through a double-buffered LDS tile; h leaves in fp32.
-template <int I>
+template <int I, int NL>
 __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     float* __restrict__ hf) {
+  static_assert(NL == 1 || NL == 3, "one or three limbs");
   constexpr int NS = I / 128;
   constexpr int KS = 256;               // codes per stage (4 MFMA steps)
   constexpr int ROWB = KS + 16;         // padded LDS row: one limb of one slot
-  constexpr int ABUF = 3 * TM * ROWB;   // one stage of x limbs
+  constexpr int ABUF = NL * TM * ROWB;  // one stage of x limbs
   __shared__ __align__(16) int8_t smem[2 * ABUF];
   __shared__ float s_sx[TM];
-  __shared__ int s_xsum[3][TM], s_tok[TM];
+  __shared__ int s_xsum[NL][TM], s_tok[TM];
   __shared__ __align__(16) float s_al[256];  // a_g | a_u of the part's 128 columns
   const int local = blockIdx.x >> 3, part = local % NS;
   const int tile = xcd_tile(8 * (local / NS) + (blockIdx.x & 7), *n_tiles);
@@ -675,9 +682,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
     s_tok[tid] = tok;
     const int* xi = reinterpret_cast<const int*>(xs);
     s_sx[tid] = tok >= 0 ? xs[tok] * xs[4 * T + tok] : 0.f;
-    s_xsum[0][tid] = tok >= 0 ? xi[T + tok] : 0;
-    s_xsum[1][tid] = tok >= 0 ? xi[2 * T + tok] : 0;
-    s_xsum[2][tid] = tok >= 0 ? xi[3 * T + tok] : 0;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) s_xsum[l][tid] = tok >= 0 ? xi[(1 + l) * T + tok] : 0;
   }
   const int rowb = H / 4;
   const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
@@ -694,40 +700,45 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
 
   // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
   // 16-byte segment u % 16.  Rows past np read slot 0's token (discarded).
-  const int8_t* asrc[6];
-  int adst[6];
+  constexpr int NR = 2 * NL;  // units per thread
+  const int8_t* asrc[NR];
+  int adst[NR];
 #pragma unroll
-  for (int r = 0; r < 6; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int u = r * 256 + tid;
     const int limb = u >> 9, slot = (u >> 4) & 31, seg = u & 15;
     const int tok = s_tok[slot] >= 0 ? s_tok[slot] : s_tok[0];
-    asrc[r] = xq + (int64_t)tok * 3 * H + (int64_t)limb * H + 16 * seg;
+    asrc[r] = xq + (int64_t)tok * NL * H + (int64_t)limb * H + 16 * seg;
     adst[r] = (limb * TM + slot) * ROWB + 16 * seg;
   }
   uint4 as0, as1, as2, as3, as4, as5;  // one stage of x limbs in flight (named: kept in registers)
   auto fetch_a = [&](int st) {
     as0 = *reinterpret_cast<const uint4*>(asrc[0] + st * KS);
     as1 = *reinterpret_cast<const uint4*>(asrc[1] + st * KS);
-    as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
-    as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
-    as4 = *reinterpret_cast<const uint4*>(asrc[4] + st * KS);
-    as5 = *reinterpret_cast<const uint4*>(asrc[5] + st * KS);
+    if constexpr (NL == 3) {
+      as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
+      as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
+      as4 = *reinterpret_cast<const uint4*>(asrc[4] + st * KS);
+      as5 = *reinterpret_cast<const uint4*>(asrc[5] + st * KS);
+    }
   };
   auto store_a = [&](int buf) {
     int8_t* d = smem + buf * ABUF;
     *reinterpret_cast<uint4*>(d + adst[0]) = as0;
     *reinterpret_cast<uint4*>(d + adst[1]) = as1;
-    *reinterpret_cast<uint4*>(d + adst[2]) = as2;
-    *reinterpret_cast<uint4*>(d + adst[3]) = as3;
-    *reinterpret_cast<uint4*>(d + adst[4]) = as4;
-    *reinterpret_cast<uint4*>(d + adst[5]) = as5;
+    if constexpr (NL == 3) {
+      *reinterpret_cast<uint4*>(d + adst[2]) = as2;
+      *reinterpret_cast<uint4*>(d + adst[3]) = as3;
+      *reinterpret_cast<uint4*>(d + adst[4]) = as4;
+      *reinterpret_cast<uint4*>(d + adst[5]) = as5;
+    }
   };
 
-  v4i acc[2][3][4];  // [slot half][limb][subtile]
+  v4i acc[2][NL][4];  // [slot half][limb][subtile]
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int l = 0; l < 3; ++l)
+    for (int l = 0; l < NL; ++l)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[h2][l][b] = v4i{0, 0, 0, 0};
   const int nst = H / KS;
@@ -750,14 +761,14 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
 #pragma unroll
       for (int b = 0; b < 4; ++b) wf[b] = unpack_word(word_of(bq[b], s4));
 #pragma unroll
-      for (int l = 0; l < 3; ++l) {
+      for (int l = 0; l < NL; ++l) {
         const v4i x0 = *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 16 * s4);
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[0][l][b] = mfma(wf[b], x0, acc[0][l][b]);
       }
       if (two) {
 #pragma unroll
-        for (int l = 0; l < 3; ++l) {
+        for (int l = 0; l < NL; ++l) {
           const v4i x1 = *reinterpret_cast<const v4i*>(sa + (l * TM + 16) * ROWB + 16 * s4);
 #pragma unroll
           for (int b = 0; b < 4; ++b) acc[1][l][b] = mfma(wf[b], x1, acc[1][l][b]);
@@ -778,7 +789,19 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
     if (h2 == 1 && !two) break;
     const int m = 16 * h2 + r16;
     const float sx = s_sx[m];
-    const int xs0 = s_xsum[0][m], xs1 = s_xsum[1][m], xs2 = s_xsum[2][m];
+    int xsl[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) xsl[l] = s_xsum[l][m];
+    // sum_k w_k q_k of limb combination: exact integers, combined in fp32
+    auto dotq = [&](int b, int j) -> float {
+      if constexpr (NL == 1) {
+        return (float)(acc[h2][0][b][j] - xsl[0]);
+      } else {
+        return fmaf(16384.f, (float)(acc[h2][0][b][j] - xsl[0]),
+                    fmaf(128.f, (float)(acc[h2][1][b][j] - xsl[1]),
+                         (float)(acc[h2][2][b][j] - xsl[2])));
+      }
+    };
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int cl = wave * 32 + 16 * b + 4 * kg;  // column within the part
@@ -787,15 +810,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
       const float gs[4] = {ga.x, ga.y, ga.z, ga.w}, us[4] = {ua.x, ua.y, ua.z, ua.w};
       float hv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float gd = fmaf(16384.f, (float)(acc[h2][0][b][j] - xs0),
-                              fmaf(128.f, (float)(acc[h2][1][b][j] - xs1),
-                                   (float)(acc[h2][2][b][j] - xs2)));
-        const float ud = fmaf(16384.f, (float)(acc[h2][0][b + 2][j] - xs0),
-                              fmaf(128.f, (float)(acc[h2][1][b + 2][j] - xs1),
-                                   (float)(acc[h2][2][b + 2][j] - xs2)));
-        hv[j] = silu_fast(gd * (sx * gs[j])) * (ud * (sx * us[j]));
-      }
+      for (int j = 0; j < 4; ++j)
+        hv[j] = silu_fast(dotq(b, j) * (sx * gs[j])) * (dotq(b + 2, j) * (sx * us[j]));
       if (m < np)
         *reinterpret_cast<float4*>(hf + (int64_t)(p0 + m) * I + pbase + cl) =
             make_float4(hv[0], hv[1], hv[2], hv[3]);
@@ -811,7 +827,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
 // chunk; its accumulators start at minus the slot's limb row sums, and the fp32
 // outputs are stored straight from them (four consecutive outputs of one slot
 // per lane and store).
-template <int I, int NWV>
+template <int I, int NWV, int NL>
 __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     const float* __restrict__ hf, int H, int NHB, const uint8_t* __restrict__ packed,
     const float* __restrict__ alpha, const int32_t* __restrict__ offsets,
@@ -827,9 +843,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
   constexpr int NPC = I / (64 * VW);    // pieces per lane and row
   static_assert(RPW * NWV == TM && NPC * 64 * VW == I && NQ >= 1, "coding shape");
   typedef typename std::conditional<PW == 4, uint4, uint2>::type wq_t;
-  __shared__ __align__(16) int8_t sA[3][TM][ROWB];
+  static_assert(NL == 1 || NL == 3, "one or three limbs");
+  constexpr float QM = NL == 1 ? 127.f : kQ3Max;
+  constexpr int QI = NL == 1 ? 127 : 2080768;
+  __shared__ __align__(16) int8_t sA[NL][TM][ROWB];
   __shared__ float s_sc[TM];
-  __shared__ int s_sum[3][TM];
+  __shared__ int s_sum[NL][TM];
   extern __shared__ __align__(16) float s_ad[];  // a_d of the block's outputs
   const int local = blockIdx.x >> 3, hp = local % NHB;
   const int tile = xcd_tile(8 * (local / NHB) + (blockIdx.x & 7), *n_tiles);
@@ -877,53 +896,54 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 #pragma unroll
       for (int t = 0; t < VW; ++t) mx = fmaxf(mx, fabsf(hv[r][j][t]));
     mx = wave_max_f(mx);
-    const float inv = mx > 0.f ? kQ3Max / mx : 1.f;
-    int sh = 0, sm = 0, sl = 0;
+    const float inv = mx > 0.f ? QM / mx : 1.f;
+    int sl[NL] = {};
 #pragma unroll
     for (int j = 0; j < NPC; ++j) {
-      uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+      uint32_t wl[NL] = {};
 #pragma unroll
       for (int t = 0; t < VW; ++t) {
-        int hi, mid, lo;
-        split3(code_q(hv[r][j][t], inv, 2080768), &hi, &mid, &lo);
-        w0 |= (uint32_t)(hi & 0xFF) << (8 * t);
-        w1 |= (uint32_t)(mid & 0xFF) << (8 * t);
-        w2 |= (uint32_t)(lo & 0xFF) << (8 * t);
-        sh += hi;
-        sm += mid;
-        sl += lo;
+        const int q = code_q(hv[r][j][t], inv, QI);
+        if constexpr (NL == 1) {
+          wl[0] |= (uint32_t)(q & 0xFF) << (8 * t);
+          sl[0] += q;
+        } else {
+          int hi, mid, lo;
+          split3(q, &hi, &mid, &lo);
+          wl[0] |= (uint32_t)(hi & 0xFF) << (8 * t);
+          wl[1] |= (uint32_t)(mid & 0xFF) << (8 * t);
+          wl[NL - 1] |= (uint32_t)(lo & 0xFF) << (8 * t);
+          sl[0] += hi;
+          sl[1] += mid;
+          sl[NL - 1] += lo;
+        }
       }
       const int c = VW * (lane + 64 * j);
-      if constexpr (VW == 4) {
-        *reinterpret_cast<uint32_t*>(&sA[0][row][c]) = w0;
-        *reinterpret_cast<uint32_t*>(&sA[1][row][c]) = w1;
-        *reinterpret_cast<uint32_t*>(&sA[2][row][c]) = w2;
-      } else {
-        *reinterpret_cast<uint16_t*>(&sA[0][row][c]) = (uint16_t)w0;
-        *reinterpret_cast<uint16_t*>(&sA[1][row][c]) = (uint16_t)w1;
-        *reinterpret_cast<uint16_t*>(&sA[2][row][c]) = (uint16_t)w2;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        if constexpr (VW == 4)
+          *reinterpret_cast<uint32_t*>(&sA[l][row][c]) = wl[l];
+        else
+          *reinterpret_cast<uint16_t*>(&sA[l][row][c]) = (uint16_t)wl[l];
       }
     }
-    sh = wave_sum_i(sh);
-    sm = wave_sum_i(sm);
-    sl = wave_sum_i(sl);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) sl[l] = wave_sum_i(sl[l]);
     if (lane == 0) {
-      s_sc[row] = mx > 0.f ? mx / kQ3Max : 0.f;
-      s_sum[0][row] = sh;
-      s_sum[1][row] = sm;
-      s_sum[2][row] = sl;
+      s_sc[row] = mx > 0.f ? mx / QM : 0.f;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) s_sum[l][row] = sl[l];
     }
   }
   __syncthreads();
   float sc[2];
-  int sum[2][3];
+  int sum[2][NL];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     const int m = 16 * h2 + r16;
     sc[h2] = s_sc[m];
-    sum[h2][0] = s_sum[0][m];
-    sum[h2][1] = s_sum[1][m];
-    sum[h2][2] = s_sum[2][m];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) sum[h2][l] = s_sum[l][m];
   }
   const int8_t* sa = &sA[0][r16][16 * PW * kg];
 
@@ -932,11 +952,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     // most of the registers for the whole block)
     asm volatile("" ::: "memory");
     const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
-    v4i acc[2][3][4];  // [slot half][limb][subtile]
+    v4i acc[2][NL][4];  // [slot half][limb][subtile]
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int l = 0; l < 3; ++l)
+      for (int l = 0; l < NL; ++l)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[h2][l][b] = v4i{-sum[h2][l], -sum[h2][l], -sum[h2][l],
                                                         -sum[h2][l]};
@@ -948,7 +968,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 #pragma unroll
         for (int b = 0; b < 4; ++b) wf[b] = unpack_word(word_of(bq[b][q], s4));
 #pragma unroll
-        for (int l = 0; l < 3; ++l) {
+        for (int l = 0; l < NL; ++l) {
           const v4i x0 =
               *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 64 * PW * q + 16 * s4);
 #pragma unroll
@@ -956,7 +976,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
         }
         if (two) {
 #pragma unroll
-          for (int l = 0; l < 3; ++l) {
+          for (int l = 0; l < NL; ++l) {
             const v4i x1 = *reinterpret_cast<const v4i*>(sa + (l * TM + 16) * ROWB +
                                                          64 * PW * q + 16 * s4);
 #pragma unroll
@@ -979,9 +999,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
         const float4 a = *reinterpret_cast<const float4*>(s_ad + c * CH + 64 * wave + ol);
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          v[j] = sc[h2] * fmaf(16384.f, (float)acc[h2][0][b][j],
-                               fmaf(128.f, (float)acc[h2][1][b][j], (float)acc[h2][2][b][j]));
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (NL == 1)
+            v[j] = sc[h2] * (float)acc[h2][0][b][j];
+          else
+            v[j] = sc[h2] * fmaf(16384.f, (float)acc[h2][0][b][j],
+                                 fmaf(128.f, (float)acc[h2][1][b][j], (float)acc[h2][2][b][j]));
+        }
         if (m < np)
           *reinterpret_cast<float4*>(yrow + ol) =
               make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
@@ -1049,23 +1073,25 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
 
 }  // namespace
 
-hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, bool fine,
+hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, int nl,
                           const Workspace& ws, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   const unsigned nb = (unsigned)((T + 3) / 4);
-  if (x_bf16)
-    launch("quant_x", fine ? k_quant_x<true, 3> : k_quant_x<true, 2>, nb, 256, 0, s, x, (int)T,
-           d.H, norm, ws.xq, ws.xs);
-  else
-    launch("quant_x", fine ? k_quant_x<false, 3> : k_quant_x<false, 2>, nb, 256, 0, s, x, (int)T,
-           d.H, norm, ws.xq, ws.xs);
+  auto k = x_bf16 ? (nl == 1   ? k_quant_x<true, 1>
+                     : nl == 3 ? k_quant_x<true, 3>
+                               : k_quant_x<true, 2>)
+                  : (nl == 1   ? k_quant_x<false, 1>
+                     : nl == 3 ? k_quant_x<false, 3>
+                               : k_quant_x<false, 2>);
+  launch("quant_x", k, nb, 256, 0, s, x, (int)T, d.H, norm, ws.xq, ws.xs);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t* packed,
+hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* packed,
                               const float* alpha, const Workspace& ws, float* out,
                               const float* resid, float* delta, hipStream_t s) {
   const int64_t Tk = T * d.k;
+  const bool fine = nl != 2;  // the fp32-h kernels: three limbs, or one (A8)
   const int mt = max_tiles(d, T);
   const unsigned nt = (unsigned)((mt + 7) & ~7);  // whole rounds of 8 XCDs
   // the down projection's outputs of a tile split over NHB blocks while the
@@ -1079,10 +1105,12 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t
     constexpr int I_ = decltype(i_tag)::value;
     if (fine) {
       constexpr int NS_ = I_ / 128;
-      launch("gateup_mfma", k_gateup3_mfma<I_>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T, d.H,
-             packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.h);
-      launch("down_mfma", k_down3_mfma<I_, 4>, nt * nhb, 256, 4 * d.H / nhb, s, ws.h, d.H, nhb,
-             packed, alpha, ws.offsets, ws.tiles, ws.n_tiles, (float*)ws.y);
+      launch("gateup_mfma", nl == 1 ? k_gateup3_mfma<I_, 1> : k_gateup3_mfma<I_, 3>, nt * NS_, 256,
+             0, s, ws.xq, ws.xs, (int)T, d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles,
+             ws.n_tiles, ws.h);
+      launch("down_mfma", nl == 1 ? k_down3_mfma<I_, 4, 1> : k_down3_mfma<I_, 4, 3>, nt * nhb, 256,
+             4 * d.H / nhb, s, ws.h, d.H, nhb, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles,
+             (float*)ws.y);
     } else {
       // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
       constexpr int NS_ = I_ >= 512 ? 2 : 1;

@@ -84,15 +84,17 @@ hipError_t launch_decode1(const Dims& d, const void* x, bool x_bf16, const float
                           const float* bias, const uint8_t* packed, const float* alpha,
                           const Workspace& ws, float* out, const float* resid, float* delta,
                           const float* next_wr, hipStream_t s);
-// fine: three limbs (else two); pairs with launch_grouped_ffn's fine
-hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, bool fine,
+// nl: int8 limbs per activation (2: fast form, 3: fine form, 1: A8); pairs
+// with launch_grouped_ffn's nl
+hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, int nl,
                           const Workspace& ws, hipStream_t s);
 hipError_t launch_gemv_ffn(const Dims& d, int64_t T, const void* x, bool x_bf16,
                            const uint8_t* packed, const float* alpha, const Workspace& ws,
                            float* out, const float* resid, float* delta, hipStream_t s);
-// fine: three-limb activations, fp32 h and expert outputs (else two limbs and
-// fp16 expert outputs)
-hipError_t launch_grouped_ffn(const Dims& d, int64_t T, bool fine, const uint8_t* packed,
+// nl = 2: two-limb activations, fp16 expert outputs (fast form); nl = 3:
+// three limbs, fp32 h and expert outputs (fine form); nl = 1: one limb with
+// fp32 h and outputs (A8)
+hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* packed,
                               const float* alpha, const Workspace& ws, float* out,
                               const float* resid, float* delta, hipStream_t s);
 hipError_t launch_load_token(const void* staged, bool bf16, int n_staged, int64_t T, int H,

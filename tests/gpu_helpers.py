@@ -80,16 +80,17 @@ def layer_tokens_with_gap(w: S.Workload, layer: Layer, T: int, token0: int = 0):
     raise RuntimeError("gap rule did not converge")
 
 
-def stack_tokens_with_gap(w: S.Workload, layers: list, T: int, token0: int = 0):
+def stack_tokens_with_gap(w: S.Workload, layers: list, T: int, token0: int = 0,
+                          a8: bool = False):
     """Tokens whose oracle routing keeps a gap >= GAP in every layer, and the
-    oracle's stack result for them."""
+    oracle's stack result for them (of the A8 variant when a8)."""
     regen: dict = {}
     for _ in range(64):
         x = S.gen_x(w, T, token0=token0, regen=regen)
         x64 = S.x_as_f32(w, x).astype(np.float64)
         r = oracle.moe_stack(x64, [L.Wr for L in layers], [L.bias for L in layers],
                              [L.packed_ref for L in layers], [L.alpha for L in layers],
-                             k=w.top_k, inter=w.inter)
+                             k=w.top_k, inter=w.inter, a8=a8)
         gaps = oracle.topk_gap(r["logits"], w.top_k)  # [L, T]
         bad = np.flatnonzero((gaps < GAP).any(axis=0))
         if bad.size == 0:

@@ -95,6 +95,8 @@ def dims(**kw):
     (dict(n_experts=257), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
     (dict(flags=0x100), N.MAPLE_ERR_INVALID_ARG),
     (dict(flags=N.MAPLE_FORCE_GEMV | N.MAPLE_FORCE_GROUPED), N.MAPLE_ERR_INVALID_ARG),
+    (dict(flags=N.MAPLE_ACT_INT8 | N.MAPLE_FORCE_GEMV), N.MAPLE_ERR_INVALID_ARG),
+    (dict(flags=N.MAPLE_ACT_INT8 | N.MAPLE_FINE_LIMBS), N.MAPLE_ERR_INVALID_ARG),
 ])
 def test_workspace_query_validates_dims(lib, kw, status):
     with pytest.raises(N.MapleError) as e:

@@ -1,0 +1,81 @@
+"""GPU parity of the integer-activation (A8) variant against the oracle's A8
+mode, on the same seeded inputs.
+
+Bit-exact: routing (top-k sets, offsets, sorted tokens, slot positions).
+Tolerance (rel L2 <= 1e-3, max |d| <= 2e-2): outputs against the A8 oracle,
+whose coding decisions are taken in fp32 like the kernels'.  The GPU's h is
+an fp32 SwiGLU while the oracle's is fp64 rounded to fp32, so an h code can
+differ by one where v * 127 / max|v| falls within rounding of a half-integer;
+that changes one product term by one step and stays far inside the tolerance.
+The A8 result itself differs from the exact layer by the coding error of
+8-bit activations (about 2.6e-2), which is logged and bounded.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from gpu_helpers import (Layer, assert_close, assert_routing_equal, layer_tokens_with_gap,  # noqa: E402
+                         log)
+from test_gpu_parity import run_layer  # noqa: E402
+from ternary_weight_moe_amd import _native as N  # noqa: E402
+from ternary_weight_moe_amd import synth as S  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def check_a8(w, L, x_host, sample=None, prenorm=False, what=""):
+    flags = N.MAPLE_ACT_INT8 | (N.MAPLE_RMS_NORM if prenorm else 0)
+    got, dbg = run_layer(w, L, x_host, flags)
+    x64 = S.x_as_f32(w, x_host).astype(np.float64)
+    rows = np.arange(x_host.shape[0]) if sample is None else np.asarray(sample)
+    ref = oracle.moe_layer(x64[rows], L.Wr, L.bias, L.packed_ref, L.alpha, k=w.top_k,
+                           inter=w.inter, prenorm=prenorm, a8=True)
+    if sample is None:
+        assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
+                             ref["idx"], w.n_experts, what)
+    else:
+        assert np.array_equal(np.sort(dbg["idx"][rows], 1), np.sort(ref["idx"], 1)), what
+    assert_close(got[rows], ref["out"], f"{what} vs A8 oracle")
+    exact = oracle.moe_layer(x64[rows], L.Wr, L.bias, L.packed_ref, L.alpha, k=w.top_k,
+                             inter=w.inter, prenorm=prenorm)["out"]
+    rel = np.linalg.norm(got[rows] - exact) / np.linalg.norm(exact)
+    log(f"{what}: A8 against the exact layer rel L2 {rel:.3e}")
+    assert rel < 6e-2
+    return got
+
+
+@pytest.fixture(scope="module")
+def dec():
+    w = S.WORKLOADS["decode_layer"]
+    return w, Layer(w, 0)
+
+
+def test_a8_tiny_layer():
+    w = S.WORKLOADS["tiny_layer"]
+    L = Layer(w, 0)
+    x, _ = layer_tokens_with_gap(w, L, w.n_tokens)
+    check_a8(w, L, x, what="a8 tiny")
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 200])
+def test_a8_decode_layer(dec, T):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, T, token0=15000 + 10 * T)
+    check_a8(w, L, x, what=f"a8 decode layer T={T}")
+
+
+def test_a8_prenorm(dec):
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, 24, token0=16000)
+    check_a8(w, L, x, prenorm=True, what="a8 prenorm")
+
+
+def test_a8_prefill_4096_sampled():
+    w = S.WORKLOADS["prefill_4096"]
+    L = Layer(w, 0)
+    x, _ = layer_tokens_with_gap(w, L, w.n_tokens)
+    rng = np.random.default_rng(w.seed + 8)
+    sample = np.sort(np.concatenate([[0, w.n_tokens - 1], rng.choice(w.n_tokens, 126, replace=False)]))
+    check_a8(w, L, x, sample=sample, what="a8 prefill_4096")

@@ -66,6 +66,15 @@ def test_decode_stack_24_layers(stack3):
     check_stack(w, layers, x, ref, what="decode stack")
 
 
+def test_decode_stack_a8(stack3):
+    """The 24-layer stack in the integer-activation variant, against the
+    oracle's A8 stack (routing per layer bit-exact, deltas to tolerance)."""
+    w, layers = stack3
+    x, x64, ref, regen = stack_tokens_with_gap(w, layers, 4, token0=60, a8=True)
+    log(f"a8 stack: regenerated {len(regen)} of 4 tokens")
+    check_stack(w, layers, x, ref, flags=N.MAPLE_ACT_INT8, what="a8 stack")
+
+
 def test_decode_stack_one_token_chain(stack3):
     """One token per call: each layer's router rides on the previous layer's
     down kernel (partial dots), checked layer by layer."""
