@@ -223,9 +223,10 @@ def cpu_baseline_batched(w, budget_s):
                        f"{w.n_layers} layers ({t_used:.1f} s of oracle time)")
 
 
-def cpu_baseline_prefill(w, budget_s):
+def cpu_baseline_prefill(w, budget_s, a8=False):
     """The oracle on a bounded sample of the prefill workload: token batches of
-    the same layer until the time budget is spent; tok/s on this host."""
+    the same layer until the time budget is spent; tok/s on this host.  With
+    a8 the oracle runs its integer-activation mode."""
     import oracle
     from ternary_weight_moe_amd import synth as S
     L = oracle_layers(w)[0]
@@ -234,11 +235,12 @@ def cpu_baseline_prefill(w, budget_s):
         x = S.x_as_f32(w, S.gen_x(w, chunk, token0=n)).astype(np.float64)
         t0 = time.perf_counter()
         oracle.moe_layer(x, L["Wr"], L["bias"], L["packed"], L["alpha"], k=w.top_k,
-                         inter=w.inter)
+                         inter=w.inter, a8=a8)
         t_used += time.perf_counter() - t0
         n += chunk
     return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{n} of {w.n_tokens} tokens of one layer, {chunk} per call "
+                sample=f"{n} of {w.n_tokens} tokens of one layer{' (A8 mode)' if a8 else ''}, "
+                       f"{chunk} per call "
                        f"({t_used:.1f} s of oracle time)")
 
 
@@ -518,12 +520,13 @@ def cpu_baseline_head(ctx, budget_s):
 
 
 def bench_prefill(args, torch, N, S):
-    w = S.WORKLOADS[args.workload]
+    a8 = args.workload.endswith("_a8")
+    w = S.WORKLOADS[args.workload[:-3] if a8 else args.workload]
     H, E, k, I, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_tokens
     layer = build_layers(w, torch, N, S)[0]
     xs = S.gen_x(w, T)
     x = torch.from_numpy(xs.view(np.int16)).cuda().view(torch.bfloat16)
-    d = N.make_dims(H, E, k, I, N.MAPLE_X_BF16)
+    d = N.make_dims(H, E, k, I, N.MAPLE_X_BF16 | (N.MAPLE_ACT_INT8 if a8 else 0))
     ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
     out = torch.empty(T, H, dtype=torch.float32, device="cuda")
 
@@ -552,9 +555,11 @@ def bench_prefill(args, torch, N, S):
     return dict(
         metric=METRIC, value=T / ms_per_step * 1000.0, unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
-        vs_baseline=None, dtype="int8 MFMA (two limbs) + f32", data="synthetic",
+        vs_baseline=None, data="synthetic",
+        dtype="int8 MFMA (int8 activations) + f32" if a8 else "int8 MFMA (two limbs) + f32",
         config=dict(workload=args.workload, hidden=H, experts=E, top_k=k, inter=I, tokens=T,
-                    layers=1, step="one layer call"),
+                    layers=1, step="one layer call",
+                    activations="int8 (one limb)" if a8 else "fp32 coded in two int8 limbs"),
         roofline=roof,
         step_roofline=dict(algorithmic_int8_ops_per_step=layer_ops,
                            achieved_tops=layer_ops / (ms_per_step * 1e-3) / 1e12,
@@ -570,7 +575,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_stack",
-                    choices=["decode_stack", "prefill_4096", "prefill_16384",
+                    choices=["decode_stack", "prefill_4096", "prefill_16384", "prefill_4096_a8",
                              "batched_stack_zipf", "flashhead_decode"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -603,8 +608,11 @@ def main():
     if not args.no_cpu_baseline:
         base = {"decode_stack": cpu_baseline_decode, "batched_stack_zipf": cpu_baseline_batched,
                 "flashhead_decode": cpu_baseline_head}
-        res["cpu_baseline"] = base.get(args.workload, cpu_baseline_prefill)(
-            w, args.cpu_baseline_seconds)
+        if args.workload in base:
+            res["cpu_baseline"] = base[args.workload](w, args.cpu_baseline_seconds)
+        else:
+            res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_baseline_seconds,
+                                                       a8=args.workload.endswith("_a8"))
     print(json.dumps(res), flush=True)
 
 

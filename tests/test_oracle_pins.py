@@ -492,3 +492,22 @@ def test_a8_prenorm_ignores_power_of_two_scale():
     b = oracle.moe_layer(8.0 * x, Wr, None, packed, alpha, k=w.top_k, inter=w.inter,
                          prenorm=True, a8=True)
     np.testing.assert_allclose(b["out"], a["out"], rtol=1e-5, atol=1e-6)
+
+
+def test_a8_stack_is_composition_of_a8_layers():
+    """The A8 stack applies the A8 layer (with the pre-norm) layer after layer and
+    adds each result to the residual stream."""
+    w = tiny(n_tokens=3, n_layers=3, seed=79)
+    layers = [make_layer(w, l) for l in range(w.n_layers)]
+    x0 = layers[0][0]
+    r = oracle.moe_stack(x0, [L[1] for L in layers], [L[2] for L in layers],
+                         [L[5] for L in layers], [L[4] for L in layers], k=w.top_k,
+                         inter=w.inter, a8=True)
+    x = x0.copy()
+    for l, L in enumerate(layers):
+        one = oracle.moe_layer(x, L[1], L[2], L[5], L[4], k=w.top_k, inter=w.inter,
+                               prenorm=True, a8=True)
+        assert np.array_equal(r["idx"][l], one["idx"])
+        assert np.array_equal(r["delta"][l], one["out"])
+        x = x + one["out"]
+    assert np.array_equal(r["x"], x)
