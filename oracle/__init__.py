@@ -1,13 +1,15 @@
 """ORACLE — test infrastructure, not part of the product.
 
-A plain fp64 CPU evaluation of the routed ternary-expert FFN and of the
-clustered output head (``maple_oracle.c``) behind a thin ctypes wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+A plain fp64 CPU evaluation of the routed ternary-expert FFN, of the
+clustered output head and of decode attention (``maple_oracle.c``) behind a
+thin ctypes wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package; the HIP library
 and its Python binding never do, and share no code with it.
 
 Every function cites, in ``maple_oracle.c``, the passage of the pages it
 follows.  Parity pins (what fixes the oracle independently of itself) live in
-``tests/test_oracle_pins.py`` and ``tests/test_oracle_head_pins.py``.  Parity unpinned: agreement with the real
+``tests/test_oracle_pins.py``, ``tests/test_oracle_head_pins.py`` and
+``tests/test_oracle_attn_pins.py``.  Parity unpinned: agreement with the real
 Maple-Preview model (no trained weights exist here, and the pages give no
 exact expert form).
 """
@@ -66,6 +68,8 @@ def _L():
             "oracle_head_search": (_I64, [_P, _I32, _P, _P, _P, _P, _I32, _P, _P, _P]),
             "oracle_flashhead": (None, [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _P, _P, _P]),
+            "oracle_attn_decode": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                                  _I64, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -293,3 +297,25 @@ def flashhead(h, centroids, rows, off, row_token, P: int, keep_cand: bool = True
                           _ptr(row_token), _ptr(scores), _ptr(probed), _ptr(cand), _ptr(n_cand),
                           _ptr(token), _ptr(logit))
     return dict(scores=scores, probed=probed, cand=cand, n_cand=n_cand, token=token, logit=logit)
+
+
+# ---- decode attention ------------------------------------------------------------
+
+def attn_decode(q, k, v, pos, *, window: int):
+    """Decode attention in fp64.  q: bf16 bits [B, n_q, D]; k, v: bf16 bits
+    [B, n_kv, S, D], the history with each new token's key and value at
+    position pos[b]; window W > 0 attends to [max(0, pos-W+1), pos], 0 to
+    [0, pos].  Returns out [B, n_q, D] (fp64)."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    pos = _c(np.atleast_1d(pos), np.int32)
+    B, n_q, D = q.shape
+    n_kv, S = k.shape[1], k.shape[2]
+    assert k.shape == (B, n_kv, S, D) and v.shape == k.shape and pos.shape == (B,)
+    out = np.empty((B, n_q, D), np.float64)
+    rc = _L().oracle_attn_decode(B, n_q, n_kv, D, window, _ptr(q), _ptr(k), _ptr(v), S,
+                                 _ptr(pos), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_attn_decode: inconsistent arguments")
+    return out

@@ -4,8 +4,9 @@
  * A plain, slow, fp64 CPU evaluation of the routed ternary-expert FFN layer
  * (router -> softmax/top-k -> per-expert SwiGLU FFN with ternary weights and
  * one alpha per output row -> weighted combine), of a stack of such layers
- * joined by a residual add, and of the clustered output head (FlashHead; see
- * its section at the end of this file).  Only the tests, the smoke check and the
+ * joined by a residual add, of the clustered output head (FlashHead) and of
+ * decode attention over a sliding window or the whole context (see their
+ * sections at the end of this file).  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library.
  *
@@ -576,4 +577,65 @@ void oracle_flashhead(int64_t T, int32_t H, int32_t C, int32_t P, int32_t V, con
     n_cand[t] = oracle_head_search(ht, H, rows, off, row_token, pt, P, cand ? cand + t * V : NULL,
                                    &token[t], &logit[t]);
   }
+}
+
+/* ---- decode attention: sliding-window and global layers -------------------
+ *
+ * The pages (linlog.top article "Maple-Preview", section
+ * "架构设计：为推理速度而生", hybrid sliding-window paragraph, and the
+ * parameter table of the papers.ananclaw.com guide) give the layer pattern:
+ * three of every four layers attend over a 512-token sliding window, one over
+ * the whole context (up to 131,072 tokens).  They give no formula, head count
+ * or head size.  Readings taken here: scaled dot-product attention,
+ *   s_p = <q, k_p> / sqrt(D),   out = sum_p softmax(s)_p v_p,
+ * over the positions p in [lo, pos] of the new token at position pos, with
+ * lo = max(0, pos - W + 1) for a window of W positions (the new token and the
+ * W - 1 before it) and lo = 0 for a global layer; query head hq reads
+ * key/value head hq / (n_q / n_kv) (grouped-query attention).
+ *
+ * q [B][n_q][D], k and v [B][n_kv][S][D] (the history, the new token's key
+ * and value at position pos[b]) are bf16 bit patterns, converted exactly; the
+ * sums, the exponentials and the weighted average are fp64.  out [B][n_q][D].
+ * Returns -1 on inconsistent arguments (pos outside [0, S)). */
+int oracle_attn_decode(int32_t B, int32_t n_q, int32_t n_kv, int32_t D, int32_t window,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t S,
+                       const int32_t* pos, double* out) {
+  if (B < 0 || n_kv < 1 || n_q < n_kv || n_q % n_kv || D < 1 || window < 0) return -1;
+  for (int32_t b = 0; b < B; ++b)
+    if (pos[b] < 0 || pos[b] >= S) return -1;
+  const int32_t G = n_q / n_kv;
+  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t hq = 0; hq < n_q; ++hq) {
+      const int32_t hk = hq / G;
+      const int64_t p1 = pos[b];
+      const int64_t p0 = window > 0 && p1 - window + 1 > 0 ? p1 - window + 1 : 0;
+      const uint16_t* qv = q + ((int64_t)b * n_q + hq) * D;
+      const uint16_t* kh = k + ((int64_t)b * n_kv + hk) * S * D;
+      const uint16_t* vh = v + ((int64_t)b * n_kv + hk) * S * D;
+      double* s = (double*)malloc(sizeof(double) * (size_t)(p1 - p0 + 1));
+      double m = -INFINITY;
+      for (int64_t p = p0; p <= p1; ++p) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < D; ++j)
+          acc += bf16_to_double(qv[j]) * bf16_to_double(kh[p * D + j]);
+        s[p - p0] = acc * inv_sqrt_d;
+        if (s[p - p0] > m) m = s[p - p0];
+      }
+      double z = 0.0;
+      for (int64_t p = p0; p <= p1; ++p) {
+        s[p - p0] = exp(s[p - p0] - m);
+        z += s[p - p0];
+      }
+      double* o = out + ((int64_t)b * n_q + hq) * D;
+      for (int32_t j = 0; j < D; ++j) {
+        double acc = 0.0;
+        for (int64_t p = p0; p <= p1; ++p) acc += s[p - p0] * bf16_to_double(vh[p * D + j]);
+        o[j] = acc / z;
+      }
+      free(s);
+    }
+  }
+  return 0;
 }

@@ -26,6 +26,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 # Tensor ids folded into the stream keys.
 T_X, T_ROUTER, T_WEIGHTS, T_ALPHA, T_ZIPF = 1, 2, 3, 4, 5
 T_HEAD_SIZE, T_HEAD_CENTER, T_HEAD_ROW, T_HEAD_PERM, T_HEAD_H = 6, 7, 8, 9, 10
+T_ATTN_Q, T_ATTN_K, T_ATTN_V, T_ATTN_POS = 11, 12, 13, 14
 
 
 def build_lib(force: bool = False) -> str:
@@ -272,4 +273,99 @@ def gen_head_h(w: HeadWorkload, n_tokens: int | None = None, token0: int = 0,
     out = np.empty((T, w.hidden), np.float32)
     for i, t in enumerate(range(token0, token0 + T)):
         out[i] = normal_f32(key(w.seed, T_HEAD_H, t, regen.get(t, 0)), w.hidden)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Decode-attention inputs (sliding-window and global layers)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Decode attention of one layer: `batch` sequences each adding one token.
+
+    The new token of sequence b sits at position pos[b]; the longest sequence
+    has `ctx` positions (pos = ctx - 1) and, when `ragged`, the others have
+    pos uniform in [ctx/2, ctx - 1].  window > 0 is a sliding layer over that
+    many positions, 0 a global layer.  Keys and values are bf16(N(0, 1)),
+    queries bf16(N(0, q_sigma^2)), so that scores <q, k>/sqrt(D) spread with
+    standard deviation q_sigma.  History is drawn per (sequence, kv head,
+    position), so any range of it can be generated on its own.
+    """
+    name: str
+    n_q: int
+    n_kv: int
+    head_dim: int
+    window: int
+    batch: int
+    ctx: int
+    seed: int
+    ragged: bool = False
+    q_sigma: float = 2.0
+
+    @property
+    def capacity(self) -> int:
+        """Cache positions per sequence and head: the window (a ring) or the
+        context, rounded up to the 32-position cache tile."""
+        n = self.window if self.window > 0 else self.ctx
+        return (n + 31) // 32 * 32
+
+
+ATTN_WORKLOADS = {
+    "attn_tiny_swa": AttnWorkload("attn_tiny_swa", 4, 2, 128, 64, 3, 150, 8001, ragged=True),
+    "attn_tiny_global": AttnWorkload("attn_tiny_global", 6, 2, 64, 0, 3, 200, 8002, ragged=True),
+    # Maple's layer pattern: 3 of 4 layers slide over 512 positions, 1 of 4 is
+    # global, context up to 131,072 positions; 16 query heads of 128 and 4 kv heads
+    "attn_swa_decode": AttnWorkload("attn_swa_decode", 16, 4, 128, 512, 1, 131072, 8101),
+    "attn_global_decode": AttnWorkload("attn_global_decode", 16, 4, 128, 0, 1, 131072, 8201),
+}
+
+
+def gen_attn_pos(w: AttnWorkload) -> np.ndarray:
+    """Position of each sequence's new token, int32 [B]; sequence 0 is the longest."""
+    pos = np.full(w.batch, w.ctx - 1, np.int32)
+    if w.ragged and w.batch > 1:
+        u = uniform_f32(key(w.seed, T_ATTN_POS), w.batch, 0.0, 1.0).astype(np.float64)
+        lo = w.ctx // 2
+        pos[1:] = np.minimum(lo + np.floor(u[1:] * (w.ctx - lo)), w.ctx - 1).astype(np.int32)
+    return pos
+
+
+def gen_attn_q(w: AttnWorkload, step: int = 0) -> np.ndarray:
+    """Queries, bf16 bits [B, n_q, D] (one stream per sequence and step)."""
+    out = np.empty((w.batch, w.n_q, w.head_dim), np.uint16)
+    for b in range(w.batch):
+        out[b] = normal_bf16(key(w.seed, T_ATTN_Q, b, step), w.n_q * w.head_dim,
+                             w.q_sigma).reshape(w.n_q, w.head_dim)
+    return out
+
+
+def gen_attn_kv(w: AttnWorkload, p0: int, p1: int, layer: int = 0):
+    """Keys and values of positions [p0, p1) for every sequence and kv head,
+    bf16 bits [B, n_kv, p1 - p0, D] each.  Position p of (b, h) has its own
+    stream, so a range is the same whatever range it is drawn with."""
+    n = p1 - p0
+    D = w.head_dim
+    k = np.empty((w.batch, w.n_kv, n, D), np.uint16)
+    v = np.empty((w.batch, w.n_kv, n, D), np.uint16)
+    for b in range(w.batch):
+        for h in range(w.n_kv):
+            sub = (b * w.n_kv + h) * (1 << 20) + layer
+            k[b, h] = _range_bf16(key(w.seed, T_ATTN_K, sub), p0, p1, D)
+            v[b, h] = _range_bf16(key(w.seed, T_ATTN_V, sub), p0, p1, D)
+    return k, v
+
+
+def _range_bf16(k0: int, p0: int, p1: int, D: int) -> np.ndarray:
+    """Rows p0..p1-1 of an endless bf16(N(0,1)) matrix with D columns: rows are
+    drawn in blocks of 1024 keyed by block index."""
+    out = np.empty((p1 - p0, D), np.uint16)
+    r = p0
+    while r < p1:
+        blk = r // 1024
+        b0 = blk * 1024
+        rows = normal_bf16(key(k0, T_ATTN_K, blk), 1024 * D).reshape(1024, D)
+        e = min(p1, b0 + 1024)
+        out[r - p0:e - p0] = rows[r - b0:e - b0]
+        r = e
     return out

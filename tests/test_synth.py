@@ -102,3 +102,19 @@ def test_bf16_rounding_is_nearest_even():
     assert back[2] == np.float32(1.0 + 2 ** -6)         # halfway: up to the even neighbour
     assert back[3] == -2.5
     assert abs(back[4] - 3.0e-3) <= 2 ** -8 * 3.0e-3        # half an ulp of 7 stored bits
+
+
+def test_attn_history_ranges_and_positions():
+    w = S.ATTN_WORKLOADS["attn_tiny_swa"]
+    k, v = S.gen_attn_kv(w, 0, w.ctx)
+    k2, v2 = S.gen_attn_kv(w, 90, 149)
+    assert np.array_equal(k[:, :, 90:149], k2) and np.array_equal(v[:, :, 90:149], v2)
+    assert not np.array_equal(k, v)
+    kf = S.bf16_bits_to_f32(k).astype(np.float64)
+    assert abs(kf.mean()) < 0.02 and abs(kf.std() - 1.0) < 0.02
+    pos = S.gen_attn_pos(w)
+    assert pos[0] == w.ctx - 1 and np.all(pos >= w.ctx // 2) and np.all(pos < w.ctx)
+    assert w.capacity == 64 and S.ATTN_WORKLOADS["attn_tiny_global"].capacity == 224
+    q = S.gen_attn_q(w)
+    assert q.shape == (w.batch, w.n_q, w.head_dim)
+    assert abs(S.bf16_bits_to_f32(q).std() - w.q_sigma) < 0.2
