@@ -43,6 +43,8 @@ EXPORTS = [
     "maple_moe_stack_graph_create", "maple_graph_launch", "maple_graph_set_step",
     "maple_graph_destroy", "maple_profile_enable", "maple_profile_summary",
     "maple_head_workspace_bytes", "maple_flashhead_forward",
+    "maple_attn_cache_bytes", "maple_attn_workspace_bytes", "maple_attn_cache_fill",
+    "maple_attn_decode",
 ]
 
 
@@ -78,6 +80,12 @@ class HeadDims(ctypes.Structure):
 
 class HeadDebug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("scores", "probed", "cand_logits", "n_cand")]
+
+
+class AttnDims(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 _P = ctypes.c_void_p
@@ -124,6 +132,14 @@ def load() -> ctypes.CDLL:
         "maple_flashhead_forward": (ctypes.c_int, [ctypes.POINTER(HeadDims), i32, _P, _P, _P,
                                                    _P, _P, _P, _P, _P, sz,
                                                    ctypes.POINTER(HeadDebug), _P]),
+        "maple_attn_cache_bytes": (ctypes.c_int, [ctypes.POINTER(AttnDims), i32,
+                                                  ctypes.POINTER(sz)]),
+        "maple_attn_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AttnDims), i32, i32,
+                                                      ctypes.POINTER(sz)]),
+        "maple_attn_cache_fill": (ctypes.c_int, [ctypes.POINTER(AttnDims), i32, i32, i32, _P,
+                                                 _P, _P, _P, _P]),
+        "maple_attn_decode": (ctypes.c_int, [ctypes.POINTER(AttnDims), i32, i32, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, sz, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -328,3 +344,44 @@ def maple_flashhead_forward(dims: HeadDims, n_tokens: int, h, centroids, rows, c
         _dptr(cluster_off), _dptr(row_token), _dptr(token_out), _dptr(logit_out),
         _dptr(workspace), workspace.numel() * workspace.element_size(),
         ctypes.byref(dbg) if dbg else None, _stream(stream)), "maple_flashhead_forward")
+
+
+# ---- decode attention ---------------------------------------------------------------
+
+MAPLE_ATTN_TILE = 32
+MAPLE_ATTN_MAX_GROUP = 16
+MAPLE_ATTN_MAX_BATCH = 4096
+
+
+def make_attn_dims(n_q_heads: int, n_kv_heads: int, head_dim: int, window: int, capacity: int,
+                   flags: int = 0) -> AttnDims:
+    return AttnDims(n_q_heads, n_kv_heads, head_dim, window, capacity, flags)
+
+
+def maple_attn_cache_bytes(dims: AttnDims, batch: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().maple_attn_cache_bytes(ctypes.byref(dims), batch, ctypes.byref(n)),
+           "maple_attn_cache_bytes")
+    return n.value
+
+
+def maple_attn_workspace_bytes(dims: AttnDims, batch: int, max_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().maple_attn_workspace_bytes(ctypes.byref(dims), batch, max_len,
+                                             ctypes.byref(n)), "maple_attn_workspace_bytes")
+    return n.value
+
+
+def maple_attn_cache_fill(dims: AttnDims, batch: int, p_begin: int, n_pos: int, k_lin, v_lin,
+                          k_cache, v_cache, stream=None) -> None:
+    _check(load().maple_attn_cache_fill(ctypes.byref(dims), batch, p_begin, n_pos, _dptr(k_lin),
+                                        _dptr(v_lin), _dptr(k_cache), _dptr(v_cache),
+                                        _stream(stream)), "maple_attn_cache_fill")
+
+
+def maple_attn_decode(dims: AttnDims, batch: int, max_len: int, q, k_new, v_new, pos, k_cache,
+                      v_cache, out, workspace, stream=None) -> None:
+    _check(load().maple_attn_decode(
+        ctypes.byref(dims), batch, max_len, _dptr(q), _dptr(k_new), _dptr(v_new), _dptr(pos),
+        _dptr(k_cache), _dptr(v_cache), _dptr(out), _dptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "maple_attn_decode")

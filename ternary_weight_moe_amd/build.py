@@ -17,9 +17,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmaple_moe.so")
-SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "misc.hip", "head.hip"]
+SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "misc.hip", "head.hip",
+           "attn.hip"]
 HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(CSRC, "wave.h"),
-           os.path.join(ROOT, "include", "maple_moe.h")]
+           os.path.join(CSRC, "limbs.h"), os.path.join(ROOT, "include", "maple_moe.h"),
+           os.path.join(ROOT, "include", "maple_head.h"),
+           os.path.join(ROOT, "include", "maple_attn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

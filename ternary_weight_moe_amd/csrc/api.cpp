@@ -14,6 +14,7 @@
 #include "internal.h"
 #include "maple_moe.h"
 #include "maple_head.h"
+#include "maple_attn.h"
 
 struct maple_graph {
   hipGraph_t graph = nullptr;
@@ -691,6 +692,126 @@ int maple_flashhead_forward(const maple_head_dims* dims, int32_t n_tokens, const
                             hipMemcpyDeviceToDevice, s)) != hipSuccess)
       return hip_fail(e, "debug copy");
   }
+  return MAPLE_OK;
+}
+
+
+// ---- decode attention ----
+
+static int check_attn_dims(const maple_attn_dims* d, maple::AttnDims* out) {
+  if (!d) return fail(MAPLE_ERR_INVALID_ARG, "dims is NULL");
+  if (d->flags) return fail(MAPLE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "head_dim=%d: need 64 or 128", d->head_dim);
+  if (d->n_kv_heads < 1 || d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads ||
+      d->n_q_heads / d->n_kv_heads > MAPLE_ATTN_MAX_GROUP)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE,
+                "n_q_heads=%d, n_kv_heads=%d: need a multiple with at most %d query heads per "
+                "kv head", d->n_q_heads, d->n_kv_heads, MAPLE_ATTN_MAX_GROUP);
+  if (d->window < 0) return fail(MAPLE_ERR_INVALID_ARG, "window=%d < 0", d->window);
+  if (d->capacity < MAPLE_ATTN_TILE || d->capacity % MAPLE_ATTN_TILE)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "capacity=%d: need a positive multiple of %d",
+                d->capacity, MAPLE_ATTN_TILE);
+  if (d->window > d->capacity)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "capacity=%d below window=%d", d->capacity,
+                d->window);
+  *out = maple::AttnDims{d->n_q_heads, d->n_kv_heads, d->head_dim, d->window, d->capacity};
+  return MAPLE_OK;
+}
+
+static int check_attn_batch(int32_t batch) {
+  if (batch < 0) return fail(MAPLE_ERR_INVALID_ARG, "batch=%d < 0", batch);
+  if (batch > MAPLE_ATTN_MAX_BATCH)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "batch=%d > %d", batch, MAPLE_ATTN_MAX_BATCH);
+  return MAPLE_OK;
+}
+
+static size_t attn_ws_bytes(const maple::AttnDims& d, int32_t batch, int32_t max_len) {
+  int tps, nspl;
+  maple::attn_split(d, batch, max_len, &tps, &nspl);
+  if (nspl == 1) return 256;
+  const size_t rows = (size_t)batch * d.Hq * nspl;
+  const size_t o = (sizeof(float) * rows * d.D + 255) & ~(size_t)255;
+  const size_t ml = (sizeof(float) * rows * 2 + 255) & ~(size_t)255;
+  return o + ml;
+}
+
+int maple_attn_cache_bytes(const maple_attn_dims* dims, int32_t batch, size_t* bytes) {
+  maple::AttnDims d;
+  int rc;
+  if ((rc = check_attn_dims(dims, &d)) || (rc = check_attn_batch(batch))) return rc;
+  if (!bytes) return fail(MAPLE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = (size_t)batch * d.Hkv * d.cap * d.D * sizeof(uint16_t);
+  return MAPLE_OK;
+}
+
+int maple_attn_workspace_bytes(const maple_attn_dims* dims, int32_t batch, int32_t max_len,
+                               size_t* bytes) {
+  maple::AttnDims d;
+  int rc;
+  if ((rc = check_attn_dims(dims, &d)) || (rc = check_attn_batch(batch))) return rc;
+  if (max_len < 1) return fail(MAPLE_ERR_INVALID_ARG, "max_len=%d < 1", max_len);
+  if (!bytes) return fail(MAPLE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = attn_ws_bytes(d, batch, max_len);
+  return MAPLE_OK;
+}
+
+int maple_attn_cache_fill(const maple_attn_dims* dims, int32_t batch, int32_t p_begin,
+                          int32_t n_pos, const uint16_t* k_lin, const uint16_t* v_lin,
+                          uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+  maple::AttnDims d;
+  int rc;
+  if ((rc = check_attn_dims(dims, &d)) || (rc = check_attn_batch(batch))) return rc;
+  if (p_begin < 0 || n_pos < 0)
+    return fail(MAPLE_ERR_INVALID_ARG, "p_begin=%d, n_pos=%d: need >= 0", p_begin, n_pos);
+  if ((int64_t)p_begin + n_pos > INT32_MAX)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "positions beyond int32");
+  if (d.W == 0 && (int64_t)p_begin + n_pos > d.cap)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE,
+                "global layer: positions up to %lld exceed capacity=%d",
+                (long long)p_begin + n_pos, d.cap);
+  if ((rc = check_ptr(k_lin, 16, "k_lin")) || (rc = check_ptr(v_lin, 16, "v_lin")) ||
+      (rc = check_ptr(k_cache, 16, "k_cache")) || (rc = check_ptr(v_cache, 16, "v_cache")))
+    return rc;
+  if (batch == 0 || n_pos == 0) return MAPLE_OK;
+  if ((rc = device_ready())) return rc;
+  const hipError_t e = maple::launch_attn_fill(d, batch, p_begin, n_pos, k_lin, v_lin, k_cache,
+                                               v_cache, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn fill launch");
+  return MAPLE_OK;
+}
+
+int maple_attn_decode(const maple_attn_dims* dims, int32_t batch, int32_t max_len,
+                      const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                      const int32_t* pos, uint16_t* k_cache, uint16_t* v_cache, float* out,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  maple::AttnDims d;
+  int rc;
+  if ((rc = check_attn_dims(dims, &d)) || (rc = check_attn_batch(batch))) return rc;
+  if (max_len < 1) return fail(MAPLE_ERR_INVALID_ARG, "max_len=%d < 1", max_len);
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k_new, 16, "k_new")) ||
+      (rc = check_ptr(v_new, 16, "v_new")) || (rc = check_ptr(pos, 4, "pos")) ||
+      (rc = check_ptr(k_cache, 16, "k_cache")) || (rc = check_ptr(v_cache, 16, "v_cache")) ||
+      (rc = check_ptr(out, 16, "out")) || (rc = check_ptr(workspace, 256, "workspace")))
+    return rc;
+  const size_t need = attn_ws_bytes(d, batch, max_len);
+  if (ws_bytes < need)
+    return fail(MAPLE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", ws_bytes, need);
+  if (batch == 0) return MAPLE_OK;
+  if ((rc = device_ready())) return rc;
+  int tps, nspl;
+  maple::attn_split(d, batch, max_len, &tps, &nspl);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = nullptr;
+  if (nspl > 1) {
+    const size_t rows = (size_t)batch * d.Hq * nspl;
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       ((sizeof(float) * rows * d.D + 255) & ~(size_t)255));
+  }
+  const hipError_t e = maple::launch_attn_decode(d, batch, max_len, q, k_new, v_new, pos, k_cache,
+                                                 v_cache, out, part_o, part_ml,
+                                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn decode launch");
   return MAPLE_OK;
 }
 

@@ -125,4 +125,23 @@ hipError_t launch_head(const HeadDims& d, int64_t T, const float* h, const uint1
                        int32_t* token_out, float* logit_out, const HeadWorkspace& ws,
                        float* cand_out, int32_t* n_cand_out, hipStream_t s);
 
+// ---- decode attention (sliding-window and global layers) ----
+struct AttnDims {
+  int Hq, Hkv, D, W, cap;
+};
+// Work-groups a split attention call aims for (about four per CU).
+constexpr int kAttnTargetBlocks = 1024;
+// Tiles per split (tps) and splits per (sequence, kv head) (nspl) for a call
+// with B sequences and positions below max_len.
+void attn_split(const AttnDims& d, int64_t B, int max_len, int* tps, int* nspl);
+// part_o [B, Hq, nspl, D] and part_ml [B, Hq, nspl, 2]: split partials (unused
+// when nspl == 1)
+hipError_t launch_attn_decode(const AttnDims& d, int64_t B, int max_len, const uint16_t* q,
+                              const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos,
+                              uint16_t* kc, uint16_t* vc, float* out, float* part_o,
+                              float* part_ml, hipStream_t s);
+hipError_t launch_attn_fill(const AttnDims& d, int64_t B, int p_begin, int n_pos,
+                            const uint16_t* k_lin, const uint16_t* v_lin, uint16_t* kc,
+                            uint16_t* vc, hipStream_t s);
+
 }  // namespace maple

@@ -256,3 +256,83 @@ def test_head_argument_validation_before_any_device_call(lib):
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
 def test_head_valid_call_without_device_reports_no_device(lib):
     assert call_head(lib, head_dims(), 1) == N.MAPLE_ERR_NO_DEVICE
+
+
+# ---- decode attention -------------------------------------------------------------
+
+def attn_dims(**kw):
+    d = dict(n_q_heads=16, n_kv_heads=4, head_dim=128, window=512, capacity=512)
+    d.update(kw)
+    return N.make_attn_dims(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_kv_heads=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_q_heads=18), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_q_heads=2), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(n_q_heads=68, n_kv_heads=4), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(window=-1), N.MAPLE_ERR_INVALID_ARG),
+    (dict(capacity=500), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(capacity=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(window=513), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(flags=1), N.MAPLE_ERR_INVALID_ARG),
+    (dict(n_q_heads=64, n_kv_heads=4, head_dim=64, window=0, capacity=131072), N.MAPLE_OK),
+])
+def test_attn_dims_validation(lib, kw, status):
+    n = ctypes.c_size_t(0)
+    assert lib.maple_attn_cache_bytes(ctypes.byref(attn_dims(**kw)), 1, ctypes.byref(n)) == status
+
+
+def test_attn_sizes(lib):
+    assert N.maple_attn_cache_bytes(attn_dims(), 3) == 3 * 4 * 512 * 128 * 2
+    g = attn_dims(window=0, capacity=131072)
+    assert N.maple_attn_cache_bytes(g, 1) == 4 * 131072 * 128 * 2
+    # a short sliding layer needs no split partials; a long global layer does
+    assert N.maple_attn_workspace_bytes(attn_dims(), 1, 131072) == 256
+    big = N.maple_attn_workspace_bytes(g, 1, 131072)
+    assert big > 16 * 128 * 4 and big % 256 == 0
+    assert N.maple_attn_workspace_bytes(g, 8, 131072) > big
+
+
+def call_attn(lib, d, B, max_len, **over):
+    a = dict(q=FakeBuf(0x100000), k_new=FakeBuf(0x200000), v_new=FakeBuf(0x300000),
+             pos=FakeBuf(0x400000), kc=FakeBuf(0x500000), vc=FakeBuf(0x600000),
+             out=FakeBuf(0x700000), workspace=FakeBuf(0x800000))
+    a.update(over)
+    p = {k: (v.addr if v else None) for k, v in a.items()}
+    return lib.maple_attn_decode(ctypes.byref(d), B, max_len, p["q"], p["k_new"], p["v_new"],
+                                 p["pos"], p["kc"], p["vc"], p["out"], p["workspace"],
+                                 a["workspace"].nbytes if a["workspace"] else 0, None)
+
+
+def test_attn_argument_validation_before_any_device_call(lib):
+    d = attn_dims()
+    assert call_attn(lib, d, 0, 1) == N.MAPLE_OK
+    assert call_attn(lib, d, -1, 1) == N.MAPLE_ERR_INVALID_ARG
+    assert call_attn(lib, d, N.MAPLE_ATTN_MAX_BATCH + 1, 1) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert call_attn(lib, d, 1, 0) == N.MAPLE_ERR_INVALID_ARG
+    assert call_attn(lib, d, 1, 100, q=None) == N.MAPLE_ERR_INVALID_ARG
+    assert call_attn(lib, d, 1, 100, kc=FakeBuf(0x500008)) == N.MAPLE_ERR_ALIGNMENT
+    assert call_attn(lib, d, 1, 100, pos=FakeBuf(0x400002)) == N.MAPLE_ERR_ALIGNMENT
+    g = attn_dims(window=0, capacity=131072)
+    assert call_attn(lib, g, 1, 131072, workspace=FakeBuf(0x800000, 256)) == \
+        N.MAPLE_ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in lib.maple_last_error()
+
+
+def test_attn_fill_validation(lib):
+    g = attn_dims(window=0, capacity=1024)
+    k = lambda d, B, p0, n, **o: lib.maple_attn_cache_fill(  # noqa: E731
+        ctypes.byref(d), B, p0, n, o.get("kl", 0x100000), 0x200000, o.get("kc", 0x300000),
+        0x400000, None)
+    assert k(g, 1, 0, 0) == N.MAPLE_OK
+    assert k(g, 1, -1, 4) == N.MAPLE_ERR_INVALID_ARG
+    assert k(g, 1, 1000, 25) == N.MAPLE_ERR_UNSUPPORTED_SHAPE  # beyond a global capacity
+    assert k(g, 1, 0, 8, kl=None) == N.MAPLE_ERR_INVALID_ARG
+    assert k(g, 1, 0, 8, kc=0x300004) == N.MAPLE_ERR_ALIGNMENT
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+def test_attn_valid_call_without_device_reports_no_device(lib):
+    assert call_attn(lib, attn_dims(), 1, 100) == N.MAPLE_ERR_NO_DEVICE
