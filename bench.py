@@ -10,7 +10,10 @@ residual.  ``--workload prefill_4096`` (or ``prefill_16384``) times one
 layer over that many tokens instead; a step is then one layer call.
 ``--workload batched_stack_zipf`` runs 64 tokens per step through the stack
 with Zipf-skewed routing; ``--workload flashhead_decode`` times the clustered
-output head alone, one token per call.
+output head alone, one token per call; ``--workload hybrid_attn_decode`` times
+the attention of one decode step through the 24-layer sliding-window/global
+pattern at 131,072 positions; ``--workload prefill_4096_a8`` is the 4096-token
+layer with int8 activations.
 
 Prints one JSON line.  Inputs are synthetic and seeded; weights are generated
 in host memory, packed on the device and resident in HBM before the timed
@@ -79,6 +82,15 @@ def grouped_fine_bytes(kernel, H, E, k, I, T, D):
     }.get(kernel)
 
 
+def attn_bytes(Hq, Hkv, D, n):
+    """Algorithmic HBM bytes of one decode-attention launch for one sequence
+    attending to n positions: their keys and values (bf16, the new token's
+    read from its input), the new key and value stored to the cache, the
+    bf16 queries and the fp32 outputs.  Split partials are overhead, not
+    counted."""
+    return 2 * Hkv * n * D * 2 + 2 * Hkv * D * 2 + Hq * D * 2 + Hq * D * 4
+
+
 def decode_bytes_per_token_layer(H, E, k, I):
     return k * expert_bytes(H, I) + 4 * E * H + 2 * 4 * H
 
@@ -123,6 +135,11 @@ TRAFFIC = {
         "quant_x": {"bytes": 1074726, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
         "route_small": {"bytes": 165691, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
         "router_small": {"bytes": 6490718, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+    },
+    "hybrid_attn_decode": {
+        "attn_combine": {"bytes": 1123206, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "3776f293e49f447d"},
+        "attn_global": {"bytes": 269742773, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "3776f293e49f447d"},
+        "attn_window": {"bytes": 1164706, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "3776f293e49f447d"},
     },
     "flashhead_decode": {
         "head_final": {"bytes": 12735, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
@@ -502,6 +519,137 @@ def bench_head(args, torch, N, S):
     ), (w, cen, rows, off, rt, hs.cpu().numpy())
 
 
+def bench_attn(args, torch, N, S):
+    """Attention of one decode step through the 24 layers of the hybrid
+    pattern (layers 3, 7, .., 23 global, the other 18 sliding over 512
+    positions), one sequence whose new token sits at position 131,071: 16
+    query heads of 128 over 4 kv heads, bf16 caches.  Every global layer has
+    its own 268 MB cache (the same history copied in), so each step streams
+    1.6 GB from HBM.  Steps are replayed from captured HIP graphs of 4 steps;
+    each call stores the new token at the same position, so steps repeat."""
+    wg = S.ATTN_WORKLOADS["attn_global_decode"]
+    wsw = S.ATTN_WORKLOADS["attn_swa_decode"]
+    Hq, Hkv, D, W = wg.n_q, wg.n_kv, wg.head_dim, wsw.window
+    L = 24
+    is_global = [l % 4 == 3 for l in range(L)]
+    p = wg.ctx - 1
+    dev = "cuda"
+    kg, vg = S.gen_attn_kv(wg, 0, wg.ctx)
+    kw, vw = S.gen_attn_kv(wsw, p - W + 1, p + 1)
+    q = S.gen_attn_q(wg)
+    log(f"attention histories drawn: global {kg.nbytes * 2 / 1e6:.0f} MB, window "
+        f"{kw.nbytes * 2 / 1e6:.1f} MB")
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    dims_g = N.make_attn_dims(Hq, Hkv, D, 0, wg.capacity)
+    dims_w = N.make_attn_dims(Hq, Hkv, D, W, wsw.capacity)
+    d_q, d_pos = d16(q), torch.tensor([p], dtype=torch.int32, device=dev)
+    lin_g = (d16(kg[0, :, :p]), d16(vg[0, :, :p]))
+    lin_w = (d16(kw[0, :, :-1]), d16(vw[0, :, :-1]))
+    new_g = (d16(kg[:, :, p]), d16(vg[:, :, p]))
+    new_w = (d16(kw[:, :, -1]), d16(vw[:, :, -1]))
+    caches = []
+    for l in range(L):
+        dims = dims_g if is_global[l] else dims_w
+        n = N.maple_attn_cache_bytes(dims, 1) // 2
+        kc = torch.empty(n, dtype=torch.int16, device=dev)
+        vc = torch.empty(n, dtype=torch.int16, device=dev)
+        lk, lv = lin_g if is_global[l] else lin_w
+        N.maple_attn_cache_fill(dims, 1, 0 if is_global[l] else p - W + 1, lk.shape[1], lk, lv,
+                                kc, vc)
+        caches.append((kc, vc))
+    del lin_g, lin_w
+    torch.cuda.synchronize()
+    ws_g = torch.empty(N.maple_attn_workspace_bytes(dims_g, 1, wg.ctx), dtype=torch.uint8,
+                       device=dev)
+    ws_w = torch.empty(N.maple_attn_workspace_bytes(dims_w, 1, wg.ctx), dtype=torch.uint8,
+                       device=dev)
+    out = torch.empty(L, 1, Hq, D, dtype=torch.float32, device=dev)
+
+    def step(s=None):
+        for l in range(L):
+            g = is_global[l]
+            kn, vn = new_g if g else new_w
+            N.maple_attn_decode(dims_g if g else dims_w, 1, wg.ctx, d_q, kn, vn, d_pos,
+                                caches[l][0], caches[l][1], out[l], ws_g if g else ws_w,
+                                stream=s)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step(stream)
+    torch.cuda.synchronize()
+    G = 4
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(G):
+            step(stream)
+    for _ in range(max(1, args.warmup // G)):
+        graph.replay()
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // G)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    n_steps = replays * G
+    ms_per_step = start.elapsed_time(end) / n_steps
+    assert bool(torch.isfinite(out).all().item()), "non-finite attention output"
+    log(f"hybrid attention: {1000 / ms_per_step:.0f} tok/s, {ms_per_step * 1000:.1f} us per step")
+    prof = profile_kernels(N, step, 8)
+    per_kernel = {kn: dict(launches=n, avg_us=1000 * avg) for kn, (n, avg) in prof.items()}
+    gbytes = attn_bytes(Hq, Hkv, D, p + 1)
+    wbytes = attn_bytes(Hq, Hkv, D, W)
+    for kn, b in (("attn_global", gbytes), ("attn_window", wbytes)):
+        if kn in per_kernel:
+            per_kernel[kn]["algorithmic_bytes"] = b
+            per_kernel[kn]["achieved_gbs"] = b / (per_kernel[kn]["avg_us"] * 1e-6) / 1e9
+    dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
+    dom_bytes = {"attn_global": gbytes, "attn_window": wbytes}.get(dom)
+    dom_avg_s = prof[dom][1] * 1e-3
+    achieved = dom_bytes / dom_avg_s / 1e9 if dom_bytes else None
+    step_bytes = 6 * gbytes + 18 * wbytes
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    return dict(
+        metric="decode-attention tok/s (24-layer hybrid sliding-window/global pattern, one sequence "
+               "at 131,072 positions)",
+        value=1000.0 / ms_per_step, unit="tok/s", n_gpus=1, steps=n_steps, warmup=args.warmup,
+        ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16 MFMA, f32 softmax and sums", data="synthetic",
+        config=dict(workload="hybrid_attn_decode", layers=L, global_layers=6, window=W,
+                    position=p, batch=1, q_heads=Hq, kv_heads=Hkv, head_dim=D,
+                    step="attention of one token through 24 layers"),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS if achieved else None,
+                      traffic=traffic_for("hybrid_attn_decode", dom), kernel=dom,
+                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=dom_avg_s * 1e6),
+        step_roofline=dict(algorithmic_bytes_per_step=step_bytes, achieved_gbs=step_gbs,
+                           frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
+        kernels=per_kernel,
+    ), (wg, wsw, q, kg, vg, kw, vw)
+
+
+def cpu_baseline_attn(ctx, budget_s):
+    """The oracle on a bounded sample: whole steps (6 global layers at 131,072
+    positions and 18 sliding layers) until the budget is spent; tok/s."""
+    import oracle
+    wg, wsw, q, kg, vg, kw, vw = ctx
+    p = wg.ctx - 1
+    n, t_used = 0, 0.0
+    while t_used < budget_s or n == 0:
+        t0 = time.perf_counter()
+        for l in range(24):
+            if l % 4 == 3:
+                oracle.attn_decode(q, kg, vg, [p], window=0)
+            else:
+                oracle.attn_decode(q, kw, vw, [wsw.window - 1], window=wsw.window)
+        t_used += time.perf_counter() - t0
+        n += 1
+    return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} whole steps of 24 layers ({t_used:.1f} s of oracle time)")
+
+
 def cpu_baseline_head(ctx, budget_s):
     """The oracle on a bounded sample: the staged tokens 16 per call (its
     threads take one token each) until the budget is spent; tok/s."""
@@ -576,7 +724,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_stack",
                     choices=["decode_stack", "prefill_4096", "prefill_16384", "prefill_4096_a8",
-                             "batched_stack_zipf", "flashhead_decode"])
+                             "batched_stack_zipf", "flashhead_decode", "hybrid_attn_decode"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -588,7 +736,7 @@ def main():
               "(every token is independent, so the path shards by tokens with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    decode = args.workload in ("decode_stack", "flashhead_decode")
+    decode = args.workload in ("decode_stack", "flashhead_decode", "hybrid_attn_decode")
     if args.steps is None:
         args.steps = 256 if decode else 20
     if args.warmup is None:
@@ -603,11 +751,12 @@ def main():
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
     runner = {"decode_stack": bench_decode, "batched_stack_zipf": bench_batched,
-              "flashhead_decode": bench_head}.get(args.workload, bench_prefill)
+              "flashhead_decode": bench_head,
+              "hybrid_attn_decode": bench_attn}.get(args.workload, bench_prefill)
     res, w = runner(args, torch, N, S)
     if not args.no_cpu_baseline:
         base = {"decode_stack": cpu_baseline_decode, "batched_stack_zipf": cpu_baseline_batched,
-                "flashhead_decode": cpu_baseline_head}
+                "flashhead_decode": cpu_baseline_head, "hybrid_attn_decode": cpu_baseline_attn}
         if args.workload in base:
             res["cpu_baseline"] = base[args.workload](w, args.cpu_baseline_seconds)
         else:

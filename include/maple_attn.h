@@ -50,9 +50,11 @@ extern "C" {
 
 /* Limits: head_dim 64 or 128; 1 <= n_kv_heads, n_q_heads a multiple of
  * n_kv_heads with at most MAPLE_ATTN_MAX_GROUP query heads per kv head;
- * capacity a positive multiple of MAPLE_ATTN_TILE, at least window for a
- * sliding layer; 0 <= batch <= MAPLE_ATTN_MAX_BATCH. */
+ * capacity a positive multiple of MAPLE_ATTN_TILE, at most
+ * MAPLE_ATTN_MAX_CAPACITY, and at least window for a sliding layer;
+ * 0 <= batch <= MAPLE_ATTN_MAX_BATCH. */
 #define MAPLE_ATTN_TILE 32
+#define MAPLE_ATTN_MAX_CAPACITY (1 << 22)
 #define MAPLE_ATTN_MAX_GROUP 16
 #define MAPLE_ATTN_MAX_BATCH 4096
 

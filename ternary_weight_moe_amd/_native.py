@@ -351,6 +351,7 @@ def maple_flashhead_forward(dims: HeadDims, n_tokens: int, h, centroids, rows, c
 MAPLE_ATTN_TILE = 32
 MAPLE_ATTN_MAX_GROUP = 16
 MAPLE_ATTN_MAX_BATCH = 4096
+MAPLE_ATTN_MAX_CAPACITY = 1 << 22
 
 
 def make_attn_dims(n_q_heads: int, n_kv_heads: int, head_dim: int, window: int, capacity: int,

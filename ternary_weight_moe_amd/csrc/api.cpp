@@ -709,9 +709,11 @@ static int check_attn_dims(const maple_attn_dims* d, maple::AttnDims* out) {
                 "n_q_heads=%d, n_kv_heads=%d: need a multiple with at most %d query heads per "
                 "kv head", d->n_q_heads, d->n_kv_heads, MAPLE_ATTN_MAX_GROUP);
   if (d->window < 0) return fail(MAPLE_ERR_INVALID_ARG, "window=%d < 0", d->window);
-  if (d->capacity < MAPLE_ATTN_TILE || d->capacity % MAPLE_ATTN_TILE)
-    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "capacity=%d: need a positive multiple of %d",
-                d->capacity, MAPLE_ATTN_TILE);
+  if (d->capacity < MAPLE_ATTN_TILE || d->capacity % MAPLE_ATTN_TILE ||
+      d->capacity > MAPLE_ATTN_MAX_CAPACITY)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE,
+                "capacity=%d: need a positive multiple of %d, at most %d", d->capacity,
+                MAPLE_ATTN_TILE, MAPLE_ATTN_MAX_CAPACITY);
   if (d->window > d->capacity)
     return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "capacity=%d below window=%d", d->capacity,
                 d->window);

@@ -27,7 +27,8 @@
 // contiguous memory.
 //
 // The tile holding the new token takes its key and value rows from k_new and
-// v_new (patched into the registers) and stores them into the cache; no other
+// v_new (staged in LDS at the start, patched into the registers) and stores
+// them into the cache; no other
 // work-group reads that slot unmasked in the same call.  Positions outside
 // [lo, pos] in the first and last tile are masked: scores to -inf and their
 // values to zero (never-written slots may hold any bits).
@@ -36,6 +37,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "wave.h"
 
 namespace maple {
 namespace {
@@ -46,7 +48,13 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kT = 32;   // positions per cache tile
 constexpr int kNW = 4;   // waves per work-group
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ v8bf as_bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+__device__ __forceinline__ uint4 as_u4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
 
 // Element offsets inside one 32 x D tile (the layout of maple_attn.h).
 __device__ __forceinline__ int key_off(int r, int d) { return ((d >> 5) * kT + r) * 32 + (d & 31); }
@@ -76,7 +84,9 @@ __device__ __forceinline__ Range attn_range(int p, int W) {
   return r;
 }
 
-template <int D>
+// SLIDE: a sliding layer (ring cache); otherwise global (W = 0, every
+// position below capacity, slot = position).
+template <int D, bool SLIDE>
 __global__ __launch_bounds__(256, 2) void k_attn_decode(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ pos, uint16_t* kc,
@@ -87,7 +97,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   constexpr int ND = D / 16;  // 16-dim blocks of the output
   __shared__ float s_m[kNW][16], s_l[kNW][16];
   __shared__ __align__(16) float s_o[kNW][16][D + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __align__(16) uint16_t s_new[2][D];  // the new token's key and value rows
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile bases in SGPRs
   const int c16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
@@ -115,6 +127,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   const int64_t head = (int64_t)b * Hkv + h;
   uint16_t* kh = kc + head * cap * D;
   uint16_t* vh = vc + head * cap * D;
+  if (te == rg.t1 + 1 && tid < D / 4) {  // this split holds the new token's tile
+    const uint16_t* src = (tid < D / 8 ? k_new : v_new) + head * D + 8 * (tid % (D / 8));
+    *reinterpret_cast<uint4*>(&s_new[tid / (D / 8)][8 * (tid % (D / 8))]) =
+        *reinterpret_cast<const uint4*>(src);
+  }
+  __syncthreads();
   const float sc = 1.4426950408889634f / sqrtf((float)D);
 
   float m = -INFINITY, l = 0.f;
@@ -122,134 +140,149 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 kr[2 * NS], vr[ND];
+  uint4 ka[2 * NS], va[ND], kb[2 * NS], vb[ND];
+  // Tiles are read with buffer loads: one SGPR descriptor per cache head,
+  // the tile's byte base as the SGPR offset and a 32-bit lane offset, so no
+  // 64-bit addresses occupy registers.
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(kh, 0, cap * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(vh, 0, cap * D * 2, kBufferWord3);
+  const int koff = 2 * (c16 * 32 + 8 * g), voff = 2 * ((c16 * 4 + g) * 8);
   auto load = [&](int t, uint4 (&kk)[2 * NS], uint4 (&vv)[ND]) {
-    const int64_t base = (int64_t)(((t * kT) % cap) / kT) * kT * D;
+    const int tb = (SLIDE ? (t * kT) % cap : t * kT) * D * 2;  // byte offset of the tile
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int be = 0; be < 2; ++be)
-        kk[2 * s + be] =
-            *reinterpret_cast<const uint4*>(kh + base + ((s * kT + 16 * be + c16) * 32 + 8 * g));
+        kk[2 * s + be] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(
+            rk, koff + 2 * (s * kT + 16 * be) * 32, tb, 0));
 #pragma unroll
     for (int dl = 0; dl < ND; ++dl)
-      vv[dl] = *reinterpret_cast<const uint4*>(vh + base + ((16 * dl + c16) * 4 + g) * 8);
+      vv[dl] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rv, voff + 2 * 16 * dl * 4 * 8, tb, 0));
   };
 
-  int t = ts + wave;
-  if (t < te) load(t, kr, vr);
-  for (; t < te; t += kNW) {
-    uint4 kn[2 * NS], vn[ND];
-    const bool more = t + kNW < te;
-    if (more) load(t + kNW, kn, vn);
-    const int pa = t * kT;
-    const int first = max(rg.lo - pa, 0), last = min(p - pa, kT - 1);  // valid rows
-    if (t == rg.t1) {
-      // the new token's row r = p - pa: registers from k_new / v_new, stored to the cache
-      const int r = p - pa;
-      const int64_t base = (int64_t)(((t * kT) % cap) / kT) * kT * D;
-      const uint16_t* kn_row = k_new + head * D;
-      const uint16_t* vn_row = v_new + head * D;
-      if (c16 == (r & 15)) {
-        const int be = r >> 4;
+  // One tile: the new token's row patched in, masked rows cleared, scores,
+  // the online softmax update and the value MFMAs.
+  auto tile = [&](const int t, uint4 (&kr)[2 * NS], uint4 (&vr)[ND]) {
+      const int pa = t * kT;
+      const int first = max(rg.lo - pa, 0), last = min(p - pa, kT - 1);  // valid rows
+      if (t == rg.t1) {
+        // the new token's row r = p - pa: registers from k_new / v_new, stored to the cache
+        const int r = p - pa;
+        const int64_t base = (int64_t)(SLIDE ? (t * kT) % cap : t * kT) * D;
+        if (c16 == (r & 15)) {
+          const int be = r >> 4;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const uint4 u = *reinterpret_cast<const uint4*>(kn_row + 32 * s + 8 * g);
+          for (int s = 0; s < NS; ++s) {
+            const uint4 u = *reinterpret_cast<const uint4*>(&s_new[0][32 * s + 8 * g]);
 #pragma unroll
-          for (int b2 = 0; b2 < 2; ++b2)
-            if (b2 == be) kr[2 * s + b2] = u;
-          *reinterpret_cast<uint4*>(kh + base + ((s * kT + r) * 32 + 8 * g)) = u;
+            for (int b2 = 0; b2 < 2; ++b2)
+              if (b2 == be) kr[2 * s + b2] = u;
+            *reinterpret_cast<uint4*>(kh + base + ((s * kT + r) * 32 + 8 * g)) = u;
+          }
+        }
+        if (g == ((r & 15) >> 2)) {
+          const int i = ((r >> 4) << 2) | (r & 3);
+#pragma unroll
+          for (int dl = 0; dl < ND; ++dl) {
+            const uint32_t val = s_new[1][16 * dl + c16];
+            uint32_t* w = reinterpret_cast<uint32_t*>(&vr[dl]);
+            // element i of the 8 is half (i & 1) of word i >> 1
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (j == (i >> 1))
+                w[j] = (i & 1) ? ((w[j] & 0x0000FFFFu) | (val << 16)) : ((w[j] & 0xFFFF0000u) | val);
+            vh[base + ((16 * dl + c16) * 4 + g) * 8 + i] = (uint16_t)val;
+          }
         }
       }
-      if (g == ((r & 15) >> 2)) {
-        const int i = ((r >> 4) << 2) | (r & 3);
+      if (first > 0 || last < kT - 1) {
+        // zero the values of masked rows: element i of lane group g is row
+        // 16 (i / 4) + 4 g + i % 4
+        uint32_t keep[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t mk = 0;
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int i = 2 * j + hb;
+            const int r = 16 * (i >> 2) + 4 * g + (i & 3);
+            if (r >= first && r <= last) mk |= 0xFFFFu << (16 * hb);
+          }
+          keep[j] = mk;
+        }
 #pragma unroll
         for (int dl = 0; dl < ND; ++dl) {
-          const uint32_t val = vn_row[16 * dl + c16];
-          uint32_t* w = reinterpret_cast<uint32_t*>(&vr[dl]);
-          // element i of the 8 is half (i & 1) of word i >> 1
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (j == (i >> 1))
-              w[j] = (i & 1) ? ((w[j] & 0x0000FFFFu) | (val << 16)) : ((w[j] & 0xFFFF0000u) | val);
-          vh[base + ((16 * dl + c16) * 4 + g) * 8 + i] = (uint16_t)val;
+          vr[dl].x &= keep[0];
+          vr[dl].y &= keep[1];
+          vr[dl].z &= keep[2];
+          vr[dl].w &= keep[3];
         }
       }
-    }
-    if (first > 0 || last < kT - 1) {
-      // zero the values of masked rows: element i of lane group g is row
-      // 16 (i / 4) + 4 g + i % 4
-      uint32_t keep[4];
+      // scores: rows 16 be + 4 g + j of the tile, query column c16
+      v4f sf[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int be = 0; be < 2; ++be)
+          sf[be] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[2 * s + be]), qf[s], sf[be], 0,
+                                                           0, 0);
+      float sv[8];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 16 * (i >> 2) + 4 * g + (i & 3);
+        sv[i] = (r >= first && r <= last) ? sf[i >> 2][i & 3] * sc : -INFINITY;
+        tm = fmaxf(tm, sv[i]);
+      }
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mn = fmaxf(m, tm);  // finite: every tile in range has a valid row
+      const float al = exp2f(m - mn);
+      m = mn;
+      float ps = 0.f;
+      uint32_t ph[4], pl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t mk = 0;
+        uint32_t hb2[2], lb2[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const int i = 2 * j + hb;
-          const int r = 16 * (i >> 2) + 4 * g + (i & 3);
-          if (r >= first && r <= last) mk |= 0xFFFFu << (16 * hb);
+          const float pv = exp2f(sv[2 * j + hb] - mn);
+          ps += pv;
+          const uint32_t hi = bf16_rne(pv);
+          hb2[hb] = hi;
+          lb2[hb] = bf16_rne(pv - __uint_as_float(hi << 16));
         }
-        keep[j] = mk;
+        ph[j] = hb2[0] | (hb2[1] << 16);
+        pl[j] = lb2[0] | (lb2[1] << 16);
       }
+      l = l * al + ps;
+      const v8bf bh = as_bf(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      const v8bf bl = as_bf(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
       for (int dl = 0; dl < ND; ++dl) {
-        vr[dl].x &= keep[0];
-        vr[dl].y &= keep[1];
-        vr[dl].z &= keep[2];
-        vr[dl].w &= keep[3];
+        acc[dl] *= al;
+        acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bh, acc[dl], 0, 0, 0);
+        acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bl, acc[dl], 0, 0, 0);
       }
-    }
-    // scores: rows 16 be + 4 g + j of the tile, query column c16
-    v4f sf[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int be = 0; be < 2; ++be)
-        sf[be] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[2 * s + be]), qf[s], sf[be], 0,
-                                                         0, 0);
-    float sv[8];
-    float tm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 16 * (i >> 2) + 4 * g + (i & 3);
-      sv[i] = (r >= first && r <= last) ? sf[i >> 2][i & 3] * sc : -INFINITY;
-      tm = fmaxf(tm, sv[i]);
-    }
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
-    const float mn = fmaxf(m, tm);  // finite: every tile in range has a valid row
-    const float al = exp2f(m - mn);
-    m = mn;
-    float ps = 0.f;
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t hb2[2], lb2[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const float pv = exp2f(sv[2 * j + hb] - mn);
-        ps += pv;
-        const uint32_t hi = bf16_rne(pv);
-        hb2[hb] = hi;
-        lb2[hb] = bf16_rne(pv - __uint_as_float(hi << 16));
-      }
-      ph[j] = hb2[0] | (hb2[1] << 16);
-      pl[j] = lb2[0] | (lb2[1] << 16);
-    }
-    l = l * al + ps;
-    const v8bf bh = as_bf(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const v8bf bl = as_bf(make_uint4(pl[0], pl[1], pl[2], pl[3]));
-#pragma unroll
-    for (int dl = 0; dl < ND; ++dl) {
-      acc[dl] *= al;
-      acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bh, acc[dl], 0, 0, 0);
-      acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bl, acc[dl], 0, 0, 0);
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 2 * NS; ++i) kr[i] = kn[i];
-#pragma unroll
-      for (int i = 0; i < ND; ++i) vr[i] = vn[i];
+  };
+
+  // Two register sets in turn: the loads of the tile after next are issued
+  // before this tile's work, always (the current tile again after the last,
+  // an L2 hit), so the waits before this tile's MFMAs never drain them.
+  int t = ts + wave;
+  if (t < te) {
+    load(t, ka, va);
+    for (;;) {
+      load(t + kNW < te ? t + kNW : t, kb, vb);
+      tile(t, ka, va);
+      t += kNW;
+      if (t >= te) break;
+      load(t + kNW < te ? t + kNW : t, ka, va);
+      tile(t, kb, vb);
+      t += kNW;
+      if (t >= te) break;
     }
   }
   // merge the four waves (a wave without tiles has m = -inf, l = 0, acc = 0)
@@ -289,33 +322,59 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
 }
 
 // The splits of one (sequence, query head): out = sum_s O_s 2^(m_s - M) /
-// sum_s L_s 2^(m_s - M), splits in ascending order.
+// sum_s L_s 2^(m_s - M).  Work-group = (row, 32 output dims); its 256
+// threads find M and the split weights together (weights kept in LDS), then
+// 8 groups of 32 threads each sum every eighth split for the 32 dims
+// (128-byte loads), and the 8 partial sums are added in group order.
 template <int D>
-__global__ __launch_bounds__(D) void k_attn_combine(const int32_t* __restrict__ pos,
-                                                    const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    float* __restrict__ out, int Hq, int W, int cap,
-                                                    int max_len, int tps, int nspl) {
-  const int row = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(256) void k_attn_combine(const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      float* __restrict__ out, int Hq, int W,
+                                                      int cap, int max_len, int tps, int nspl) {
+  __shared__ float s_f[kAttnMaxSplits];
+  __shared__ float s_red[2][4];
+  __shared__ float s_o[8][32];
+  const int row = blockIdx.x, d0 = 32 * blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = row / Hq;
   const int p = pos[b];
   if (!pos_valid(p, max_len, W, cap)) {
-    out[(int64_t)row * D + d] = __builtin_nanf("");
+    if (tid < 32) out[(int64_t)row * D + d0 + tid] = __builtin_nanf("");
     return;
   }
   const Range rg = attn_range(p, W);
   const int n = (rg.t1 - rg.t0 + tps) / tps;  // non-empty splits
   const float* ml = part_ml + (int64_t)row * nspl * 2;
-  const float* po = part_o + (int64_t)row * nspl * D + d;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < n; ++s) {
+  float mx = -INFINITY;
+  for (int s = tid; s < n; s += 256) mx = fmaxf(mx, ml[2 * s]);
+  mx = wave_max_f(mx);
+  if (lane == 0) s_red[0][wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  float lsum = 0.f;
+  for (int s = tid; s < n; s += 256) {
     const float f = exp2f(ml[2 * s] - M);
-    L += ml[2 * s + 1] * f;
-    O += po[(int64_t)s * D] * f;
+    s_f[s] = f;
+    lsum += ml[2 * s + 1] * f;
   }
-  out[(int64_t)row * D + d] = O / L;
+  lsum = wave_sum_f(lsum);
+  if (lane == 0) s_red[1][wave] = lsum;
+  __syncthreads();
+  const int grp = tid >> 5, dd = tid & 31;
+  const float* po = part_o + (int64_t)row * nspl * D + d0 + dd;
+  float o = 0.f;
+#pragma unroll 4
+  for (int s = grp; s < n; s += 8) o += po[(int64_t)s * D] * s_f[s];
+  s_o[grp][dd] = o;
+  __syncthreads();
+  if (tid < 32) {
+    float acc = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 8; ++g2) acc += s_o[g2][tid];
+    const float L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+    out[(int64_t)row * D + d0 + tid] = acc / L;
+  }
 }
 
 // Position-major history -> tiled cache.  Thread = (position, 8 dims).
@@ -348,18 +407,24 @@ __global__ __launch_bounds__(256) void k_attn_fill(const uint16_t* __restrict__ 
 }  // namespace
 
 void attn_split(const AttnDims& d, int64_t B, int max_len, int* tps, int* nspl) {
-  const int span = d.W > 0 ? std::min(d.W, max_len) : max_len;
-  const int tiles = (span + kT - 2) / kT + 1;  // tiles a run of `span` positions can touch
-  if (tiles <= 8 * kNW) {
+  // tiles one sequence's range can touch: a window anywhere, or [0, max_len)
+  const int tiles = d.W > 0 && d.W < max_len ? (d.W + kT - 2) / kT + 1 : (max_len + kT - 1) / kT;
+  if (tiles <= kAttnOneSplitTiles) {  // short ranges: no combine kernel
     *tps = tiles;
     *nspl = 1;
     return;
   }
   const int64_t total = B * d.Hkv * (int64_t)tiles;
-  int t = (int)((total + kAttnTargetBlocks - 1) / kAttnTargetBlocks);
-  t = (std::max(t, kNW) + kNW - 1) / kNW * kNW;
-  *tps = t;
-  *nspl = (tiles + t - 1) / t;
+  int64_t t = (total + kAttnTargetBlocks - 1) / kAttnTargetBlocks;
+  t = std::max<int64_t>(t, (tiles + kAttnMaxSplits - 1) / kAttnMaxSplits);
+  t = (std::max<int64_t>(t, kNW) + kNW - 1) / kNW * kNW;
+  if (t >= tiles) {
+    *tps = tiles;
+    *nspl = 1;
+    return;
+  }
+  *tps = (int)t;
+  *nspl = (int)((tiles + t - 1) / t);
 }
 
 hipError_t launch_attn_decode(const AttnDims& d, int64_t B, int max_len, const uint16_t* q,
@@ -369,18 +434,27 @@ hipError_t launch_attn_decode(const AttnDims& d, int64_t B, int max_len, const u
   int tps, nspl;
   attn_split(d, B, max_len, &tps, &nspl);
   const dim3 grid(nspl, d.Hkv, (unsigned)B);
+  const dim3 cgrid((unsigned)(B * d.Hq), d.D / 32);
   if (d.D == 128) {
-    launch("attn_decode", k_attn_decode<128>, grid, 256, 0, s, q, k_new, v_new, pos, kc, vc, out,
-           part_o, part_ml, d.Hq, d.Hkv, d.W, d.cap, max_len, tps, nspl);
+    if (d.W > 0)
+      launch("attn_window", k_attn_decode<128, true>, grid, 256, 0, s, q, k_new, v_new, pos, kc,
+             vc, out, part_o, part_ml, d.Hq, d.Hkv, d.W, d.cap, max_len, tps, nspl);
+    else
+      launch("attn_global", k_attn_decode<128, false>, grid, 256, 0, s, q, k_new, v_new, pos, kc,
+             vc, out, part_o, part_ml, d.Hq, d.Hkv, 0, d.cap, max_len, tps, nspl);
     if (nspl > 1)
-      launch("attn_combine", k_attn_combine<128>, dim3((unsigned)(B * d.Hq)), 128, 0, s, pos,
-             part_o, part_ml, out, d.Hq, d.W, d.cap, max_len, tps, nspl);
+      launch("attn_combine", k_attn_combine<128>, cgrid, 256, 0, s, pos, part_o, part_ml, out,
+             d.Hq, d.W, d.cap, max_len, tps, nspl);
   } else {
-    launch("attn_decode", k_attn_decode<64>, grid, 256, 0, s, q, k_new, v_new, pos, kc, vc, out,
-           part_o, part_ml, d.Hq, d.Hkv, d.W, d.cap, max_len, tps, nspl);
+    if (d.W > 0)
+      launch("attn_window", k_attn_decode<64, true>, grid, 256, 0, s, q, k_new, v_new, pos, kc,
+             vc, out, part_o, part_ml, d.Hq, d.Hkv, d.W, d.cap, max_len, tps, nspl);
+    else
+      launch("attn_global", k_attn_decode<64, false>, grid, 256, 0, s, q, k_new, v_new, pos, kc,
+             vc, out, part_o, part_ml, d.Hq, d.Hkv, 0, d.cap, max_len, tps, nspl);
     if (nspl > 1)
-      launch("attn_combine", k_attn_combine<64>, dim3((unsigned)(B * d.Hq)), 64, 0, s, pos,
-             part_o, part_ml, out, d.Hq, d.W, d.cap, max_len, tps, nspl);
+      launch("attn_combine", k_attn_combine<64>, cgrid, 256, 0, s, pos, part_o, part_ml, out,
+             d.Hq, d.W, d.cap, max_len, tps, nspl);
   }
   return hipGetLastError();
 }

@@ -129,8 +129,15 @@ hipError_t launch_head(const HeadDims& d, int64_t T, const float* h, const uint1
 struct AttnDims {
   int Hq, Hkv, D, W, cap;
 };
-// Work-groups a split attention call aims for (about four per CU).
-constexpr int kAttnTargetBlocks = 1024;
+// Work-groups a split attention call aims for: one round of two per CU (the
+// decode kernel holds 256 registers per lane, so two work-groups fit a CU).
+constexpr int kAttnTargetBlocks = 512;
+// Ranges of at most this many tiles are never split (a 512-position window
+// touches 17): the waves of one work-group walk them faster than a second
+// kernel could combine split partials.
+constexpr int kAttnOneSplitTiles = 24;
+// Most splits per (sequence, kv head); the combine keeps one weight per split in LDS.
+constexpr int kAttnMaxSplits = 1024;
 // Tiles per split (tps) and splits per (sequence, kv head) (nspl) for a call
 // with B sequences and positions below max_len.
 void attn_split(const AttnDims& d, int64_t B, int max_len, int* tps, int* nspl);

@@ -275,6 +275,7 @@ def attn_dims(**kw):
     (dict(window=-1), N.MAPLE_ERR_INVALID_ARG),
     (dict(capacity=500), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
     (dict(capacity=0), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
+    (dict(window=0, capacity=N.MAPLE_ATTN_MAX_CAPACITY + 32), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
     (dict(window=513), N.MAPLE_ERR_UNSUPPORTED_SHAPE),
     (dict(flags=1), N.MAPLE_ERR_INVALID_ARG),
     (dict(n_q_heads=64, n_kv_heads=4, head_dim=64, window=0, capacity=131072), N.MAPLE_OK),
@@ -288,11 +289,11 @@ def test_attn_sizes(lib):
     assert N.maple_attn_cache_bytes(attn_dims(), 3) == 3 * 4 * 512 * 128 * 2
     g = attn_dims(window=0, capacity=131072)
     assert N.maple_attn_cache_bytes(g, 1) == 4 * 131072 * 128 * 2
-    # a short sliding layer needs no split partials; a long global layer does
-    assert N.maple_attn_workspace_bytes(attn_dims(), 1, 131072) == 256
+    # many sequences over a short window need no split partials; a long global layer does
+    assert N.maple_attn_workspace_bytes(attn_dims(window=32, capacity=32), 64, 131072) == 256
     big = N.maple_attn_workspace_bytes(g, 1, 131072)
     assert big > 16 * 128 * 4 and big % 256 == 0
-    assert N.maple_attn_workspace_bytes(g, 8, 131072) > big
+    assert N.maple_attn_workspace_bytes(g, 8, 131072) > 256
 
 
 def call_attn(lib, d, B, max_len, **over):
