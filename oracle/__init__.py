@@ -1,15 +1,15 @@
 """ORACLE — test infrastructure, not part of the product.
 
 A plain fp64 CPU evaluation of the routed ternary-expert FFN, of the
-clustered output head and of decode attention (``maple_oracle.c``) behind a
-thin ctypes wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+clustered output head, of decode attention and of the BF16 -> ternary
+conversion (``maple_oracle.c``) behind a thin ctypes wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package; the HIP library
 and its Python binding never do, and share no code with it.
 
 Every function cites, in ``maple_oracle.c``, the passage of the pages it
 follows.  Parity pins (what fixes the oracle independently of itself) live in
-``tests/test_oracle_pins.py``, ``tests/test_oracle_head_pins.py`` and
-``tests/test_oracle_attn_pins.py``.  Parity unpinned: agreement with the real
+``tests/test_oracle_pins.py``, ``tests/test_oracle_head_pins.py``,
+``tests/test_oracle_attn_pins.py`` and ``tests/test_oracle_convert_pins.py``.  Parity unpinned: agreement with the real
 Maple-Preview model (no trained weights exist here, and the pages give no
 exact expert form).
 """
@@ -70,6 +70,7 @@ def _L():
                                         _P, _P, _P, _P, _P]),
             "oracle_attn_decode": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P,
                                                   _I64, _P, _P]),
+            "oracle_ternarize": (_I64, [_P, _I64, _I32, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -319,3 +320,16 @@ def attn_decode(q, k, v, pos, *, window: int):
     if rc != 0:
         raise ValueError("oracle_attn_decode: inconsistent arguments")
     return out
+
+
+# ---- BF16 -> ternary conversion -----------------------------------------------------
+
+def ternarize(w):
+    """Per-row absmean ternarisation of bf16 bits w [rows, cols]: returns
+    (codes int8 [rows, cols], alpha fp32 [rows], number of bad rows)."""
+    w = _c(np.atleast_2d(w), np.uint16)
+    rows, cols = w.shape
+    codes = np.empty((rows, cols), np.int8)
+    alpha = np.empty(rows, np.float32)
+    bad = _L().oracle_ternarize(_ptr(w), rows, cols, _ptr(codes), _ptr(alpha))
+    return codes, alpha, int(bad)

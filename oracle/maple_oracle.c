@@ -4,9 +4,10 @@
  * A plain, slow, fp64 CPU evaluation of the routed ternary-expert FFN layer
  * (router -> softmax/top-k -> per-expert SwiGLU FFN with ternary weights and
  * one alpha per output row -> weighted combine), of a stack of such layers
- * joined by a residual add, of the clustered output head (FlashHead) and of
- * decode attention over a sliding window or the whole context (see their
- * sections at the end of this file).  Only the tests, the smoke check and the
+ * joined by a residual add, of the clustered output head (FlashHead), of
+ * decode attention over a sliding window or the whole context, and of the
+ * BF16 -> ternary weight conversion (see their sections at the end of this
+ * file).  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library.
  *
@@ -638,4 +639,52 @@ int oracle_attn_decode(int32_t B, int32_t n_q, int32_t n_kv, int32_t D, int32_t 
     }
   }
   return 0;
+}
+
+/* ---- BF16 -> ternary conversion -------------------------------------------
+ *
+ * The pages (linlog.top article "Maple-Preview", local-run section) mention a
+ * tool that streams BF16 Maple weights into the ternary format without
+ * holding the 38 GB source in memory, but not the rule it applies.  Reading
+ * taken here: the model is trained ternary with one alpha per row, so the
+ * BF16 weights are the latent weights of that training and the conversion is
+ * the absmean rule of ternary training applied per output row:
+ *   gamma_i = mean_j |W_ij|          (summed in fp64 over j ascending, the
+ *                                     mean rounded once to fp32)
+ *   w_ij    = clamp(round(W_ij / gamma_i), -1, 1), round half to even,
+ *   alpha_i = gamma_i.
+ * Since |W/gamma| rounds to 0 exactly when it is <= 1/2 (1/2 itself rounds to
+ * the even 0), w_ij = sign(W_ij) if 2|W_ij| > gamma_i and 0 otherwise; both
+ * sides of that comparison are exact in fp32.  A row holding a NaN or an
+ * infinity is "bad": its codes are 0 and its alpha NaN.
+ * w: bf16 bits [rows][cols]; codes int8 [rows][cols]; alpha fp32 [rows].
+ * Returns the number of bad rows. */
+int64_t oracle_ternarize(const uint16_t* w, int64_t rows, int32_t cols, int8_t* codes,
+                         float* alpha) {
+  int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+  for (int64_t i = 0; i < rows; ++i) {
+    const uint16_t* row = w + i * cols;
+    int8_t* c = codes + i * cols;
+    double sum = 0.0;
+    int finite = 1;
+    for (int32_t j = 0; j < cols; ++j) {
+      const double v = bf16_to_double(row[j]);
+      if (!isfinite(v)) finite = 0;
+      sum += fabs(v);
+    }
+    if (!finite) {
+      for (int32_t j = 0; j < cols; ++j) c[j] = 0;
+      alpha[i] = NAN;
+      ++bad;
+      continue;
+    }
+    const float gamma = (float)(sum / (double)cols);
+    for (int32_t j = 0; j < cols; ++j) {
+      const float v = (float)bf16_to_double(row[j]);
+      c[j] = 2.0f * fabsf(v) > gamma ? (v > 0.0f ? 1 : -1) : 0;
+    }
+    alpha[i] = gamma;
+  }
+  return bad;
 }
