@@ -13,7 +13,8 @@ with Zipf-skewed routing; ``--workload flashhead_decode`` times the clustered
 output head alone, one token per call; ``--workload hybrid_attn_decode`` times
 the attention of one decode step through the 24-layer sliding-window/global
 pattern at 131,072 positions; ``--workload prefill_4096_a8`` is the 4096-token
-layer with int8 activations.
+layer with int8 activations; ``--workload ternary_convert`` converts one whole
+layer of BF16 latent weights into ternary codes and alphas.
 
 Prints one JSON line.  Inputs are synthetic and seeded; weights are generated
 in host memory, packed on the device and resident in HBM before the timed
@@ -109,6 +110,11 @@ def prefill_ops(kernel, H, k, I, T):
 # An entry holds only while the kernel's sources hash as recorded; otherwise the
 # kernel has changed since the counters were taken and the traffic is unknown.
 TRAFFIC = {
+    "ternary_convert": {
+        "fill_i32": {"bytes": 2681, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
+        "ternarize_g32": {"bytes": 606103338, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
+        "ternarize_w2": {"bytes": 1209099636, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
+    },
     "decode_stack": {
         "d1m_down": {"bytes": 4617741, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
         "d1m_gateup": {"bytes": 6567798, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
@@ -650,6 +656,84 @@ def cpu_baseline_attn(ctx, budget_s):
                 sample=f"{n} whole steps of 24 layers ({t_used:.1f} s of oracle time)")
 
 
+def convert_bytes(n_rows, cols):
+    """Algorithmic HBM bytes of converting n_rows rows of cols bf16 values:
+    the source read once, the 2-bit codes and one fp32 alpha per row written."""
+    return n_rows * cols * 2 + n_rows * cols // 4 + 4 * n_rows
+
+
+def bench_convert(args, torch, N, S):
+    """BF16 -> ternary conversion of one whole MoE layer (256 experts, hidden
+    2048, inter 512: 805M latent weights, 1.61 GB of bf16) into the layer blob
+    and its alphas: two strided calls, the 512 gate/up rows of every expert
+    (2048 columns) and its 2048 down rows (512 columns)."""
+    w = S.WORKLOADS["decode_layer"]
+    H, I, E = w.hidden, w.inter, w.n_experts
+    n = 3 * H * I
+    dev = "cuda"
+    src = torch.empty(E * n, dtype=torch.int16, device=dev)
+    for e in range(E):
+        src[e * n:(e + 1) * n] = torch.from_numpy(S.gen_latent_expert(w, 0, e).view(np.int16)).to(dev)
+    packed = torch.empty(E * n // 4, dtype=torch.uint8, device=dev)
+    alpha = torch.empty(E * (2 * I + H), dtype=torch.float32, device=dev)
+    bad = torch.empty(1, dtype=torch.int32, device=dev)
+    log(f"latent layer drawn: {E * n * 2 / 1e9:.2f} GB of bf16")
+
+    def step():
+        N.maple_ternarize_bf16_device(src, E, 2 * I, H, n, n // 4, 2 * I + H, packed, alpha, bad)
+        N.maple_ternarize_bf16_device(src[2 * I * H:], E, H, I, n, n // 4, 2 * I + H,
+                                      packed[2 * I * H // 4:], alpha[2 * I:], bad)
+    ms_per_step = timed(torch, step, args.steps, args.warmup)
+    assert int(bad.item()) == 0, "bad rows in the latent layer"
+    src_gb = E * n * 2 / 1e9
+    log(f"ternarize: {src_gb / (ms_per_step * 1e-3):.0f} GB/s of bf16 source, {ms_per_step * 1000:.0f} us per layer")
+    prof = profile_kernels(N, step, min(args.steps, 10))
+    by = {"ternarize_w2": convert_bytes(E * 2 * I, H), "ternarize_g32": convert_bytes(E * H, I)}
+    per_kernel = {kn: dict(launches=c, avg_us=1000 * avg, algorithmic_bytes=by.get(kn),
+                           achieved_gbs=(by[kn] / (avg * 1e-3) / 1e9) if kn in by else None)
+                  for kn, (c, avg) in prof.items()}
+    dom = max((k for k in prof if k in by), key=lambda kn: prof[kn][0] * prof[kn][1])
+    dom_avg_s = prof[dom][1] * 1e-3
+    achieved = by[dom] / dom_avg_s / 1e9
+    step_bytes = sum(by.values())
+    return dict(
+        metric="BF16 -> ternary weight conversion, GB/s of bf16 source (one whole MoE layer per step)",
+        value=src_gb / (ms_per_step * 1e-3), unit="GB/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16 in, fp64 row sums, 2-bit codes + f32 alpha out",
+        data="synthetic",
+        config=dict(workload="ternary_convert", experts=E, hidden=H, inter=I,
+                    weights=E * n, step="convert one layer (two calls)"),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("ternary_convert", dom),
+                      kernel=dom, algorithmic_bytes_per_launch=by[dom],
+                      avg_launch_us=dom_avg_s * 1e6),
+        step_roofline=dict(algorithmic_bytes_per_step=step_bytes,
+                           achieved_gbs=step_bytes / (ms_per_step * 1e-3) / 1e9,
+                           frac_of_hbm_peak=step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS),
+        kernels=per_kernel,
+    ), w
+
+
+def cpu_baseline_convert(w, budget_s):
+    """The oracle on a bounded sample: whole experts (gate/up rows, then down
+    rows) until the budget is spent; GB/s of bf16 source."""
+    import oracle
+    from ternary_weight_moe_amd import synth as S
+    H, I = w.hidden, w.inter
+    n, t_used, e = 0, 0.0, 0
+    while t_used < budget_s and e < w.n_experts:
+        lat = S.gen_latent_expert(w, 0, e)
+        t0 = time.perf_counter()
+        oracle.ternarize(lat[:2 * I * H].reshape(2 * I, H))
+        oracle.ternarize(lat[2 * I * H:].reshape(H, I))
+        t_used += time.perf_counter() - t0
+        n += lat.size
+        e += 1
+    return dict(value=n * 2 / t_used / 1e9, unit="GB/s", cores=oracle.num_threads(),
+                kind="oracle", sample=f"{e} experts ({n} weights, {t_used:.1f} s of oracle time)")
+
+
 def cpu_baseline_head(ctx, budget_s):
     """The oracle on a bounded sample: the staged tokens 16 per call (its
     threads take one token each) until the budget is spent; tok/s."""
@@ -724,7 +808,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_stack",
                     choices=["decode_stack", "prefill_4096", "prefill_16384", "prefill_4096_a8",
-                             "batched_stack_zipf", "flashhead_decode", "hybrid_attn_decode"])
+                             "batched_stack_zipf", "flashhead_decode", "hybrid_attn_decode",
+                             "ternary_convert"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -752,11 +837,13 @@ def main():
         copy_probe(torch, args.copy_probe)
     runner = {"decode_stack": bench_decode, "batched_stack_zipf": bench_batched,
               "flashhead_decode": bench_head,
-              "hybrid_attn_decode": bench_attn}.get(args.workload, bench_prefill)
+              "hybrid_attn_decode": bench_attn,
+              "ternary_convert": bench_convert}.get(args.workload, bench_prefill)
     res, w = runner(args, torch, N, S)
     if not args.no_cpu_baseline:
         base = {"decode_stack": cpu_baseline_decode, "batched_stack_zipf": cpu_baseline_batched,
-                "flashhead_decode": cpu_baseline_head, "hybrid_attn_decode": cpu_baseline_attn}
+                "flashhead_decode": cpu_baseline_head, "hybrid_attn_decode": cpu_baseline_attn,
+                "ternary_convert": cpu_baseline_convert}
         if args.workload in base:
             res["cpu_baseline"] = base[args.workload](w, args.cpu_baseline_seconds)
         else:

@@ -158,6 +158,36 @@ int maple_ternary_validate_host(const uint8_t* packed, size_t n_bytes);
 int maple_ternary_pack_device(const int8_t* w, int64_t n_values, uint8_t* out,
                               int32_t* bad_count, void* stream);
 
+/* Device: BF16 -> ternary conversion into layout v1 rows with one alpha per
+ * row.  The pages (linlog.top article "Maple-Preview", local-run section)
+ * name a converter that streams BF16 Maple weights into the ternary format
+ * but not its rule; this library reads it as the per-row absmean rule of
+ * ternary training:
+ *   gamma_i = mean_j |W_ij|  (summed in fp64, the mean rounded once to fp32;
+ *             the sum is exact, hence independent of order, while a row's
+ *             magnitudes span less than about 2^40)
+ *   w_ij    = clamp(round(W_ij / gamma_i), -1, 1), ties to even, i.e.
+ *             sign(W_ij) if 2|W_ij| > gamma_i (exact in fp32), else 0
+ *   alpha_i = gamma_i.
+ * A row holding a NaN or an infinity gets codes 0 and alpha NaN.
+ * Works on n_groups groups of `rows` rows of `cols` values (a layer's experts
+ * in two calls: the 2I gate/up rows of K = H, then the H down rows of K = I):
+ *   source row i of group g: src + g * src_group_stride + i * cols (bf16
+ *                            elements, 16-byte aligned);
+ *   packed row:              out + g * out_group_stride + i * cols / 4 (bytes,
+ *                            4-byte aligned), cols / 16 words of layout v1;
+ *   alpha:                   alpha + g * alpha_group_stride + i (floats).
+ * Limits: cols % 16 == 0, 16 <= cols <= 8192, rows >= 0, n_groups >= 0,
+ * src_group_stride % 8 == 0, out_group_stride % 4 == 0.  bad_rows, if not
+ * NULL, is a device int32 receiving the number of bad rows (overwritten).
+ * Enqueues one fill and one conversion kernel on `stream`; allocates nothing.
+ * Errors: MAPLE_ERR_INVALID_ARG, MAPLE_ERR_UNSUPPORTED_SHAPE,
+ * MAPLE_ERR_ALIGNMENT, MAPLE_ERR_NO_DEVICE, MAPLE_ERR_HIP. */
+int maple_ternarize_bf16_device(const uint16_t* src, int64_t n_groups, int32_t rows, int32_t cols,
+                                int64_t src_group_stride, int64_t out_group_stride,
+                                int64_t alpha_group_stride, uint8_t* out, float* alpha,
+                                int32_t* bad_rows, void* stream);
+
 /* ---- forward ------------------------------------------------------------ */
 
 /* One MoE layer, out = MoE(x) (no residual), for n_tokens tokens.

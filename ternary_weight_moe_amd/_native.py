@@ -44,7 +44,7 @@ EXPORTS = [
     "maple_graph_destroy", "maple_profile_enable", "maple_profile_summary",
     "maple_head_workspace_bytes", "maple_flashhead_forward",
     "maple_attn_cache_bytes", "maple_attn_workspace_bytes", "maple_attn_cache_fill",
-    "maple_attn_decode",
+    "maple_attn_decode", "maple_ternarize_bf16_device",
 ]
 
 
@@ -114,6 +114,8 @@ def load() -> ctypes.CDLL:
         "maple_ternary_unpack_host": (ctypes.c_int, [_P, i64, i64, _P]),
         "maple_ternary_validate_host": (ctypes.c_int, [_P, sz]),
         "maple_ternary_pack_device": (ctypes.c_int, [_P, i64, _P, _P, _P]),
+        "maple_ternarize_bf16_device": (ctypes.c_int, [_P, i64, i32, i32, i64, i64, i64, _P, _P,
+                                                       _P, _P]),
         "maple_moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Dims), i32, _P, _P, _P, _P,
                                                    _P, _P, _P, sz, ctypes.POINTER(Debug), _P]),
         "maple_moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(Dims), i32, i32, _P, _P, _P,
@@ -386,3 +388,14 @@ def maple_attn_decode(dims: AttnDims, batch: int, max_len: int, q, k_new, v_new,
         ctypes.byref(dims), batch, max_len, _dptr(q), _dptr(k_new), _dptr(v_new), _dptr(pos),
         _dptr(k_cache), _dptr(v_cache), _dptr(out), _dptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)), "maple_attn_decode")
+
+
+# ---- BF16 -> ternary conversion ------------------------------------------------------
+
+def maple_ternarize_bf16_device(src, n_groups: int, rows: int, cols: int, src_group_stride: int,
+                                out_group_stride: int, alpha_group_stride: int, out, alpha,
+                                bad_rows=None, stream=None) -> None:
+    _check(load().maple_ternarize_bf16_device(
+        _dptr(src), n_groups, rows, cols, src_group_stride, out_group_stride, alpha_group_stride,
+        _dptr(out), _dptr(alpha), _dptr(bad_rows), _stream(stream)),
+        "maple_ternarize_bf16_device")

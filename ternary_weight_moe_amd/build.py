@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmaple_moe.so")
 SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "misc.hip", "head.hip",
-           "attn.hip"]
+           "attn.hip", "convert.hip"]
 HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(CSRC, "wave.h"),
            os.path.join(CSRC, "limbs.h"), os.path.join(ROOT, "include", "maple_moe.h"),
            os.path.join(ROOT, "include", "maple_head.h"),

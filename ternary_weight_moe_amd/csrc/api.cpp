@@ -421,6 +421,36 @@ int maple_ternary_pack_device(const int8_t* w, int64_t n_values, uint8_t* out,
   return MAPLE_OK;
 }
 
+int maple_ternarize_bf16_device(const uint16_t* src, int64_t n_groups, int32_t rows, int32_t cols,
+                                int64_t src_group_stride, int64_t out_group_stride,
+                                int64_t alpha_group_stride, uint8_t* out, float* alpha,
+                                int32_t* bad_rows, void* stream) {
+  int rc;
+  if (n_groups < 0 || rows < 0)
+    return fail(MAPLE_ERR_INVALID_ARG, "n_groups=%lld, rows=%d: need >= 0", (long long)n_groups,
+                rows);
+  if (cols < 16 || cols > 8192 || cols % 16)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "cols=%d: need a multiple of 16 in [16, 8192]",
+                cols);
+  if (n_groups > 65535)
+    return fail(MAPLE_ERR_UNSUPPORTED_SHAPE, "n_groups=%lld > 65535", (long long)n_groups);
+  if (src_group_stride < 0 || out_group_stride < 0 || alpha_group_stride < 0)
+    return fail(MAPLE_ERR_INVALID_ARG, "negative group stride");
+  if (src_group_stride % 8 || out_group_stride % 4)
+    return fail(MAPLE_ERR_ALIGNMENT,
+                "src_group_stride %% 8 and out_group_stride %% 4 must be 0 (got %lld, %lld)",
+                (long long)src_group_stride, (long long)out_group_stride);
+  if ((rc = check_ptr(src, 16, "src")) || (rc = check_ptr(out, 4, "out")) ||
+      (rc = check_ptr(alpha, 4, "alpha")) || (rc = check_opt_ptr(bad_rows, 4, "bad_rows")))
+    return rc;
+  if ((rc = device_ready())) return rc;
+  const hipError_t e = maple::launch_ternarize(src, n_groups, rows, cols, src_group_stride,
+                                               out_group_stride, alpha_group_stride, out, alpha,
+                                               bad_rows, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ternarize launch");
+  return MAPLE_OK;
+}
+
 int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const void* x,
                             const float* router_w, const float* router_bias,
                             const uint8_t* packed_w, const float* alpha, float* out,

@@ -125,6 +125,14 @@ hipError_t launch_head(const HeadDims& d, int64_t T, const float* h, const uint1
                        int32_t* token_out, float* logit_out, const HeadWorkspace& ws,
                        float* cand_out, int32_t* n_cand_out, hipStream_t s);
 
+// ---- BF16 -> ternary conversion ----
+// n_groups groups of `rows` rows of `cols` bf16 values; group strides in
+// elements (src), bytes (out) and floats (alpha).  bad_rows: zeroed, then the
+// count of rows holding NaN or Inf (may be null).
+hipError_t launch_ternarize(const uint16_t* src, int64_t n_groups, int rows, int cols,
+                            int64_t src_gs, int64_t out_gs, int64_t alpha_gs, uint8_t* out,
+                            float* alpha, int32_t* bad_rows, hipStream_t s);
+
 // ---- decode attention (sliding-window and global layers) ----
 struct AttnDims {
   int Hq, Hkv, D, W, cap;

@@ -27,6 +27,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 T_X, T_ROUTER, T_WEIGHTS, T_ALPHA, T_ZIPF = 1, 2, 3, 4, 5
 T_HEAD_SIZE, T_HEAD_CENTER, T_HEAD_ROW, T_HEAD_PERM, T_HEAD_H = 6, 7, 8, 9, 10
 T_ATTN_Q, T_ATTN_K, T_ATTN_V, T_ATTN_POS = 11, 12, 13, 14
+T_LATENT = 15
 
 
 def build_lib(force: bool = False) -> str:
@@ -201,6 +202,13 @@ def gen_alpha(w: Workload, layer: int = 0) -> np.ndarray:
     n = w.n_experts * (2 * w.inter + w.hidden)
     return uniform_f32(key(w.layer_seed(layer), T_ALPHA), n, w.alpha_lo, w.alpha_hi).reshape(
         w.n_experts, 2 * w.inter + w.hidden)
+
+
+def gen_latent_expert(w: Workload, layer: int, expert: int, sigma: float = 0.02) -> np.ndarray:
+    """BF16 latent weights of one expert for the BF16 -> ternary conversion,
+    bits [3*H*I] in the order of the packed blob: W_gate [I,H] | W_up [I,H] |
+    W_down [H,I], each value bf16(N(0, sigma^2))."""
+    return normal_bf16(key(w.layer_seed(layer), T_LATENT, expert), expert_weight_count(w), sigma)
 
 
 # ---------------------------------------------------------------------------

@@ -337,3 +337,27 @@ def test_attn_fill_validation(lib):
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
 def test_attn_valid_call_without_device_reports_no_device(lib):
     assert call_attn(lib, attn_dims(), 1, 100) == N.MAPLE_ERR_NO_DEVICE
+
+
+# ---- BF16 -> ternary conversion ---------------------------------------------------
+
+def call_ternarize(lib, G, rows, cols, ss, os_, as_, src=0x100000, out=0x200000, alpha=0x300000,
+                   bad=None):
+    return lib.maple_ternarize_bf16_device(src, G, rows, cols, ss, os_, as_, out, alpha, bad, None)
+
+
+def test_ternarize_validation_before_any_device_call(lib):
+    assert call_ternarize(lib, -1, 4, 64, 0, 0, 0) == N.MAPLE_ERR_INVALID_ARG
+    assert call_ternarize(lib, 1, -4, 64, 0, 0, 0) == N.MAPLE_ERR_INVALID_ARG
+    assert call_ternarize(lib, 1, 4, 40, 0, 0, 0) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert call_ternarize(lib, 1, 4, 8192 + 16, 0, 0, 0) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert call_ternarize(lib, 65536, 4, 64, 0, 0, 0) == N.MAPLE_ERR_UNSUPPORTED_SHAPE
+    assert call_ternarize(lib, 2, 4, 64, 4, 64, 4) == N.MAPLE_ERR_ALIGNMENT
+    assert call_ternarize(lib, 2, 4, 64, 256, 6, 4) == N.MAPLE_ERR_ALIGNMENT
+    assert call_ternarize(lib, 1, 4, 64, 0, 0, 0, src=0x100008) == N.MAPLE_ERR_ALIGNMENT
+    assert call_ternarize(lib, 1, 4, 64, 0, 0, 0, alpha=None) == N.MAPLE_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+def test_ternarize_valid_call_without_device_reports_no_device(lib):
+    assert call_ternarize(lib, 1, 4, 64, 0, 0, 0) == N.MAPLE_ERR_NO_DEVICE
