@@ -110,48 +110,61 @@ def prefill_ops(kernel, H, k, I, T):
 # An entry holds only while the kernel's sources hash as recorded; otherwise the
 # kernel has changed since the counters were taken and the traffic is unknown.
 TRAFFIC = {
-    "ternary_convert": {
-        "fill_i32": {"bytes": 2681, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
-        "ternarize_g32": {"bytes": 606103338, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
-        "ternarize_w2": {"bytes": 1209099636, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
-    },
     "decode_stack": {
-        "d1m_down": {"bytes": 4617741, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
-        "d1m_gateup": {"bytes": 6567798, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
-        "d1q_router": {"bytes": 2252610, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "5299cfdd81c6545c"},
-        "load_token": {"bytes": 15737, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7a5bfeb49a928526"},
-        "store_token": {"bytes": 42185, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7a5bfeb49a928526"},
+        "d1m_down": {"bytes": 4617540, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "9a6b3c6b720affb5"},
+        "d1m_gateup": {"bytes": 6567514, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "9a6b3c6b720affb5"},
+        "d1q_router": {"bytes": 2252513, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "9a6b3c6b720affb5"},
+        "load_token": {"bytes": 15736, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
+        "store_token": {"bytes": 42184, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 168823326, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "down_mfma": {"bytes": 240393815, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "gateup_mfma": {"bytes": 304759529, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "quant_x": {"bytes": 33759056, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "route_block": {"bytes": 359407, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
-        "route_scan": {"bytes": 149657, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
-        "route_scatter": {"bytes": 1226228, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
-        "route_topk": {"bytes": 4519504, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
-        "router_mfma": {"bytes": 37832774, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
-        "split_router": {"bytes": 4218255, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "combine": {"bytes": 168832278, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "down_mfma": {"bytes": 240446094, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "gateup_mfma": {"bytes": 304683817, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "quant_x": {"bytes": 33769605, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "route_block": {"bytes": 359404, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "route_scan": {"bytes": 149655, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "route_scatter": {"bytes": 1226218, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "route_topk": {"bytes": 4519408, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "router_mfma": {"bytes": 37832015, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "split_router": {"bytes": 4218284, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+    },
+    "prefill_4096_a8": {
+        "combine": {"bytes": 303372909, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "down_mfma": {"bytes": 414358478, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "gateup_mfma": {"bytes": 269037708, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "quant_x": {"bytes": 25364667, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "route_block": {"bytes": 359404, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "route_scan": {"bytes": 149655, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "route_scatter": {"bytes": 1226217, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "route_topk": {"bytes": 4519402, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "router_mfma": {"bytes": 37831967, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "split_router": {"bytes": 4218358, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5280333, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "down_mfma": {"bytes": 38735808, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "gateup_mfma": {"bytes": 68219709, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "quant_x": {"bytes": 1074726, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "b00262e44b2c49fe"},
-        "route_small": {"bytes": 165691, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
-        "router_small": {"bytes": 6490718, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "a3a137072c3ec9cc"},
+        "combine": {"bytes": 5267919, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "down_mfma": {"bytes": 38767866, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "gateup_mfma": {"bytes": 68218002, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "quant_x": {"bytes": 1074708, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
+        "route_small": {"bytes": 165687, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "router_small": {"bytes": 6490548, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
     },
     "hybrid_attn_decode": {
-        "attn_combine": {"bytes": 1123206, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "3776f293e49f447d"},
-        "attn_global": {"bytes": 269742773, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "3776f293e49f447d"},
-        "attn_window": {"bytes": 1164706, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "3776f293e49f447d"},
+        "attn_combine": {"bytes": 1123187, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
+        "attn_fill": {"bytes": 169768169, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
+        "attn_global": {"bytes": 269738629, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
+        "attn_window": {"bytes": 1164693, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
+    },
+    "ternary_convert": {
+        "fill_i32": {"bytes": 2681, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
+        "ternarize_g32": {"bytes": 606102832, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
+        "ternarize_w2": {"bytes": 1209100916, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
     },
     "flashhead_decode": {
-        "head_final": {"bytes": 12735, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
-        "head_scores": {"bytes": 19583752, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
-        "head_search": {"bytes": 58843185, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
-        "head_select": {"bytes": 59799, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d32a6cc5c8076aa0"},
+        "head_final": {"bytes": 12734, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
+        "head_scores": {"bytes": 19583224, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
+        "head_search": {"bytes": 58841535, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
+        "head_select": {"bytes": 59799, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
     },
 }
 
