@@ -131,3 +131,34 @@ def zipf():
 def test_batched_zipf_stack_one_step(zipf, flags):
     w, layers, x, ref = zipf
     check_stack(w, layers, x, ref, flags=flags, what=f"zipf flags={flags:#x}")
+
+
+def test_batched_stack_call_captured_in_a_graph(zipf):
+    """The 64-token stack call (grouped path) captured into a HIP graph through
+    torch and replayed three times, with eager work and a sync between the
+    replays: every replay equals the eager call bit for bit."""
+    w, layers, x, ref = zipf
+    d = dims_for(w, 0, bf16=False)
+    x0 = torch.from_numpy(S.x_as_f32(w, x).copy()).cuda()
+    xw = torch.empty_like(x0)
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, w.n_tokens), dtype=torch.uint8, device="cuda")
+    rw, rb, pk, al = dev_lists(layers)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xw.copy_(x0)
+        N.maple_moe_stack_forward(d, w.n_tokens, xw, rw, rb, pk, al, ws, stream=s)
+    torch.cuda.synchronize()
+    eager = xw.cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        xw.copy_(x0)
+        N.maple_moe_stack_forward(d, w.n_tokens, xw, rw, rb, pk, al, ws, stream=s)
+    for rep in range(3):
+        xw.fill_(float("nan"))
+        junk = torch.randn(512, 512, device="cuda")
+        (junk @ junk).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(xw.cpu().numpy(), eager), f"replay {rep} differs from the eager call"
+    x64 = S.x_as_f32(w, x).astype(np.float64)
+    assert_close(eager - x64, ref["x"] - x64, "zipf stack in a graph, x_L - x_0")
