@@ -52,6 +52,10 @@
  *   [W_gate (I rows x H)][W_up (I rows x H)][W_down (H rows x I)];
  * per layer, the E blobs back to back (expert e at byte e*3*H*I/4).
  * Alphas: fp32 [E][a_g (I) | a_u (I) | a_d (H)].  Router: fp32 [E][H].
+ *
+ * The same library also exports the clustered output head (maple_head.h) and
+ * decode attention of the sliding-window and global layers (maple_attn.h),
+ * with these conventions.
  */
 #ifndef MAPLE_MOE_H
 #define MAPLE_MOE_H

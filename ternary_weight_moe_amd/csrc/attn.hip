@@ -28,8 +28,8 @@
 //
 // The tile holding the new token takes its key and value rows from k_new and
 // v_new (staged in LDS at the start, patched into the registers) and stores
-// them into the cache; no other
-// work-group reads that slot unmasked in the same call.  Positions outside
+// them into the cache; no other work-group reads that slot unmasked in the
+// same call.  Positions outside
 // [lo, pos] in the first and last tile are masked: scores to -inf and their
 // values to zero (never-written slots may hold any bits).
 #include <math.h>
@@ -165,112 +165,112 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   // One tile: the new token's row patched in, masked rows cleared, scores,
   // the online softmax update and the value MFMAs.
   auto tile = [&](const int t, uint4 (&kr)[2 * NS], uint4 (&vr)[ND]) {
-      const int pa = t * kT;
-      const int first = max(rg.lo - pa, 0), last = min(p - pa, kT - 1);  // valid rows
-      if (t == rg.t1) {
-        // the new token's row r = p - pa: registers from k_new / v_new, stored to the cache
-        const int r = p - pa;
-        const int64_t base = (int64_t)(SLIDE ? (t * kT) % cap : t * kT) * D;
-        if (c16 == (r & 15)) {
-          const int be = r >> 4;
+    const int pa = t * kT;
+    const int first = max(rg.lo - pa, 0), last = min(p - pa, kT - 1);  // valid rows
+    if (t == rg.t1) {
+      // the new token's row r = p - pa: registers from k_new / v_new, stored to the cache
+      const int r = p - pa;
+      const int64_t base = (int64_t)(SLIDE ? (t * kT) % cap : t * kT) * D;
+      if (c16 == (r & 15)) {
+        const int be = r >> 4;
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const uint4 u = *reinterpret_cast<const uint4*>(&s_new[0][32 * s + 8 * g]);
+        for (int s = 0; s < NS; ++s) {
+          const uint4 u = *reinterpret_cast<const uint4*>(&s_new[0][32 * s + 8 * g]);
 #pragma unroll
-            for (int b2 = 0; b2 < 2; ++b2)
-              if (b2 == be) kr[2 * s + b2] = u;
-            *reinterpret_cast<uint4*>(kh + base + ((s * kT + r) * 32 + 8 * g)) = u;
-          }
-        }
-        if (g == ((r & 15) >> 2)) {
-          const int i = ((r >> 4) << 2) | (r & 3);
-#pragma unroll
-          for (int dl = 0; dl < ND; ++dl) {
-            const uint32_t val = s_new[1][16 * dl + c16];
-            uint32_t* w = reinterpret_cast<uint32_t*>(&vr[dl]);
-            // element i of the 8 is half (i & 1) of word i >> 1
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (j == (i >> 1))
-                w[j] = (i & 1) ? ((w[j] & 0x0000FFFFu) | (val << 16)) : ((w[j] & 0xFFFF0000u) | val);
-            vh[base + ((16 * dl + c16) * 4 + g) * 8 + i] = (uint16_t)val;
-          }
+          for (int b2 = 0; b2 < 2; ++b2)
+            if (b2 == be) kr[2 * s + b2] = u;
+          *reinterpret_cast<uint4*>(kh + base + ((s * kT + r) * 32 + 8 * g)) = u;
         }
       }
-      if (first > 0 || last < kT - 1) {
-        // zero the values of masked rows: element i of lane group g is row
-        // 16 (i / 4) + 4 g + i % 4
-        uint32_t keep[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t mk = 0;
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const int i = 2 * j + hb;
-            const int r = 16 * (i >> 2) + 4 * g + (i & 3);
-            if (r >= first && r <= last) mk |= 0xFFFFu << (16 * hb);
-          }
-          keep[j] = mk;
-        }
+      if (g == ((r & 15) >> 2)) {
+        const int i = ((r >> 4) << 2) | (r & 3);
 #pragma unroll
         for (int dl = 0; dl < ND; ++dl) {
-          vr[dl].x &= keep[0];
-          vr[dl].y &= keep[1];
-          vr[dl].z &= keep[2];
-          vr[dl].w &= keep[3];
+          const uint32_t val = s_new[1][16 * dl + c16];
+          uint32_t* w = reinterpret_cast<uint32_t*>(&vr[dl]);
+          // element i of the 8 is half (i & 1) of word i >> 1
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j == (i >> 1))
+              w[j] = (i & 1) ? ((w[j] & 0x0000FFFFu) | (val << 16)) : ((w[j] & 0xFFFF0000u) | val);
+          vh[base + ((16 * dl + c16) * 4 + g) * 8 + i] = (uint16_t)val;
         }
       }
-      // scores: rows 16 be + 4 g + j of the tile, query column c16
-      v4f sf[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int be = 0; be < 2; ++be)
-          sf[be] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[2 * s + be]), qf[s], sf[be], 0,
-                                                           0, 0);
-      float sv[8];
-      float tm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 16 * (i >> 2) + 4 * g + (i & 3);
-        sv[i] = (r >= first && r <= last) ? sf[i >> 2][i & 3] * sc : -INFINITY;
-        tm = fmaxf(tm, sv[i]);
-      }
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mn = fmaxf(m, tm);  // finite: every tile in range has a valid row
-      const float al = exp2f(m - mn);
-      m = mn;
-      float ps = 0.f;
-      uint32_t ph[4], pl[4];
+    }
+    if (first > 0 || last < kT - 1) {
+      // zero the values of masked rows: element i of lane group g is row
+      // 16 (i / 4) + 4 g + i % 4
+      uint32_t keep[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t hb2[2], lb2[2];
+        uint32_t mk = 0;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const float pv = exp2f(sv[2 * j + hb] - mn);
-          ps += pv;
-          const uint32_t hi = bf16_rne(pv);
-          hb2[hb] = hi;
-          lb2[hb] = bf16_rne(pv - __uint_as_float(hi << 16));
+          const int i = 2 * j + hb;
+          const int r = 16 * (i >> 2) + 4 * g + (i & 3);
+          if (r >= first && r <= last) mk |= 0xFFFFu << (16 * hb);
         }
-        ph[j] = hb2[0] | (hb2[1] << 16);
-        pl[j] = lb2[0] | (lb2[1] << 16);
+        keep[j] = mk;
       }
-      l = l * al + ps;
-      const v8bf bh = as_bf(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-      const v8bf bl = as_bf(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
       for (int dl = 0; dl < ND; ++dl) {
-        acc[dl] *= al;
-        acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bh, acc[dl], 0, 0, 0);
-        acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bl, acc[dl], 0, 0, 0);
+        vr[dl].x &= keep[0];
+        vr[dl].y &= keep[1];
+        vr[dl].z &= keep[2];
+        vr[dl].w &= keep[3];
       }
+    }
+    // scores: rows 16 be + 4 g + j of the tile, query column c16
+    v4f sf[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int be = 0; be < 2; ++be)
+        sf[be] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[2 * s + be]), qf[s], sf[be], 0,
+                                                         0, 0);
+    float sv[8];
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 16 * (i >> 2) + 4 * g + (i & 3);
+      sv[i] = (r >= first && r <= last) ? sf[i >> 2][i & 3] * sc : -INFINITY;
+      tm = fmaxf(tm, sv[i]);
+    }
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float mn = fmaxf(m, tm);  // finite: every tile in range has a valid row
+    const float al = exp2f(m - mn);
+    m = mn;
+    float ps = 0.f;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t hb2[2], lb2[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float pv = exp2f(sv[2 * j + hb] - mn);
+        ps += pv;
+        const uint32_t hi = bf16_rne(pv);
+        hb2[hb] = hi;
+        lb2[hb] = bf16_rne(pv - __uint_as_float(hi << 16));
+      }
+      ph[j] = hb2[0] | (hb2[1] << 16);
+      pl[j] = lb2[0] | (lb2[1] << 16);
+    }
+    l = l * al + ps;
+    const v8bf bh = as_bf(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const v8bf bl = as_bf(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+    for (int dl = 0; dl < ND; ++dl) {
+      acc[dl] *= al;
+      acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bh, acc[dl], 0, 0, 0);
+      acc[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(vr[dl]), bl, acc[dl], 0, 0, 0);
+    }
   };
 
-  // Two register sets in turn: the loads of the tile after next are issued
-  // before this tile's work, always (the current tile again after the last,
-  // an L2 hit), so the waits before this tile's MFMAs never drain them.
+  // Two register sets in turn: the next tile's loads go out before this
+  // tile's work, always (the current tile again after the last, an L2 hit),
+  // so the waits before this tile's MFMAs never drain them.
   int t = ts + wave;
   if (t < te) {
     load(t, ka, va);
