@@ -239,12 +239,16 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
                               next_wr, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   } else {
-    if (!gemv) {  // limbs, scales and 1/rms of x: the grouped GEMMs and large-T router use them
+    // limbs, scales and 1/rms of x for the grouped GEMMs (and the large-T
+    // router): coded by the small-T router as it reads x, else by their own kernel
+    const bool fused = !gemv && maple::router_codes_x(T);
+    if (!gemv && !fused) {
       e = maple::launch_quant_x(d, T, x, x_bf16, nl, ws, s);
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }
-    e = maple::launch_router(d, T, x, x_bf16, Wr, bias, gemv ? nullptr : ws.xs + 4 * T,
-                             ws.logits, ws.xb, ws.wb, ws.route_ctr, s);
+    e = maple::launch_router(d, T, x, x_bf16, Wr, bias,
+                             (gemv || fused) ? nullptr : ws.xs + 4 * T, ws.logits, ws.xb, ws.wb,
+                             ws.route_ctr, fused ? nl : 0, ws.xq, ws.xs, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     e = maple::launch_route(d, T, ws.logits, ws, s);
     if (e != hipSuccess) return hip_fail(e, "routing launch");

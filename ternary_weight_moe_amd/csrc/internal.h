@@ -73,10 +73,14 @@ int max_tiles(const Dims& d, int64_t T);
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
 // xb, wb: bf16-plane scratch (ws.xb, ws.wb) used above the small-T sizes;
-// route_ctr: the small-T routing kernel's arrival counter (zeroed here)
+// route_ctr: the small-T routing kernel's arrival counter (zeroed here);
+// qnl > 0 (only where router_codes_x(T)): the router also codes x into qnl
+// int8 limbs, xq / xs as launch_quant_x writes them (1/rms computed from x)
+bool router_codes_x(int64_t T);
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          const float* Wr, const float* bias, const float* rinv, float* logits,
-                         uint16_t* xb, uint16_t* wb, int32_t* route_ctr, hipStream_t s);
+                         uint16_t* xb, uint16_t* wb, int32_t* route_ctr, int qnl, int8_t* xq,
+                         float* xs, hipStream_t s);
 hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
                         hipStream_t s);
 // next_wr: the next layer's router (only read to warm the caches), or null

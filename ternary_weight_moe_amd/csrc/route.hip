@@ -17,6 +17,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "quant.h"
 #include "maple_moe.h"
 #include "wave.h"
 
@@ -54,41 +55,64 @@ __global__ __launch_bounds__(256) void k_router_small(const void* __restrict__ x
                                                       const float* __restrict__ bias, int E,
                                                       int norm, const float* __restrict__ rinv,
                                                       float* __restrict__ logits,
-                                                      int32_t* __restrict__ route_ctr) {
+                                                      int32_t* __restrict__ route_ctr, int qnl,
+                                                      int8_t* __restrict__ xq,
+                                                      float* __restrict__ xs) {
   constexpr int H = 256 * NPL;
   constexpr int TT = NPL >= 16 ? 2 : 4;           // tokens per wave
   constexpr int LB = TT == 4 ? 4 : 5;             // lane bits below the token index
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // with qnl, block x = 0 of each token group codes x (dispatched first) and
+  // the router blocks follow
+  const int e = (blockIdx.x - (qnl ? 1 : 0)) * 4 + (threadIdx.x >> 6);
   const int t0 = blockIdx.y * TT;
   if (route_ctr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *route_ctr = 0;
-  if (e >= E) return;  // wave-uniform; no block barrier follows
-  float4 w[NPL];
+  auto router_part = [&]() {
+    float4 w[NPL];
 #pragma unroll
-  for (int i = 0; i < NPL; ++i)
-    w[i] = *reinterpret_cast<const float4*>(Wr + (int64_t)e * H + 4 * lane + 256 * i);
-  const bool own_rms = norm && !rinv;
-  float acc[TT], ss[TT];
+    for (int i = 0; i < NPL; ++i)
+      w[i] = *reinterpret_cast<const float4*>(Wr + (int64_t)e * H + 4 * lane + 256 * i);
+    const bool own_rms = norm && !rinv;
+    float acc[TT], ss[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int t = min(t0 + tt, T - 1);  // rows past T repeat the last one (discarded)
-    float a = 0.f, q = 0.f;
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = min(t0 + tt, T - 1);  // rows past T repeat the last one (discarded)
+      float a = 0.f, q = 0.f;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const float4 xv = load_x4<BF16>(x, (int64_t)t * H + 4 * lane + 256 * i);
-      a = fmaf(w[i].x, xv.x, fmaf(w[i].y, xv.y, fmaf(w[i].z, xv.z, fmaf(w[i].w, xv.w, a))));
-      if (own_rms) q = fmaf(xv.x, xv.x, fmaf(xv.y, xv.y, fmaf(xv.z, xv.z, fmaf(xv.w, xv.w, q))));
+      for (int i = 0; i < NPL; ++i) {
+        const float4 xv = load_x4<BF16>(x, (int64_t)t * H + 4 * lane + 256 * i);
+        a = fmaf(w[i].x, xv.x, fmaf(w[i].y, xv.y, fmaf(w[i].z, xv.z, fmaf(w[i].w, xv.w, a))));
+        if (own_rms) q = fmaf(xv.x, xv.x, fmaf(xv.y, xv.y, fmaf(xv.z, xv.z, fmaf(xv.w, xv.w, q))));
+      }
+      acc[tt] = a;
+      ss[tt] = q;
     }
-    acc[tt] = a;
-    ss[tt] = q;
+    const float dot = wave_sum_n<TT>(acc, lane);
+    const int t = t0 + (lane >> LB);
+    float r = 1.f;
+    if (own_rms) r = rsqrtf(wave_sum_n<TT>(ss, lane) / (float)H + MAPLE_RMS_EPS);
+    else if (norm) r = rinv[min(t, T - 1)];
+    if ((lane & ((1 << LB) - 1)) == 0 && t < T)
+      logits[(int64_t)t * E + e] = dot * r + (bias ? bias[e] : 0.f);
+  };
+  // qnl > 0: one more block per token group (the first in x) codes the
+  // group's rows into qnl int8 limbs for the grouped kernels, wave w token
+  // t0 + w, alongside the router blocks; this saves a kernel that would read
+  // x once more
+  if (qnl && blockIdx.x == 0) {
+    const int tq = t0 + (threadIdx.x >> 6);
+    if ((threadIdx.x >> 6) < TT && tq < T) {  // wave-uniform
+      if (qnl == 1)
+        quant_row<BF16, 1, H>(x, tq, T, H, norm, xq, xs, lane);
+      else if (qnl == 2)
+        quant_row<BF16, 2, H>(x, tq, T, H, norm, xq, xs, lane);
+      else
+        quant_row<BF16, 3, H>(x, tq, T, H, norm, xq, xs, lane);
+    }
+    return;
   }
-  const float dot = wave_sum_n<TT>(acc, lane);
-  const int t = t0 + (lane >> LB);
-  float r = 1.f;
-  if (own_rms) r = rsqrtf(wave_sum_n<TT>(ss, lane) / (float)H + MAPLE_RMS_EPS);
-  else if (norm) r = rinv[min(t, T - 1)];
-  if ((lane & ((1 << LB) - 1)) == 0 && t < T)
-    logits[(int64_t)t * E + e] = dot * r + (bias ? bias[e] : 0.f);
+  if (e >= E) return;  // wave-uniform; no block barrier follows
+  router_part();
 }
 
 // ---- Large T: router logits on the matrix cores -----------------------------
@@ -423,17 +447,23 @@ __global__ __launch_bounds__(256) void k_route_scatter(int64_t n_slots, int E, i
 
 }  // namespace
 
+bool router_codes_x(int64_t T) { return T <= 64; }
+
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
                          const float* bias, const float* rinv, float* logits, uint16_t* xb,
-                         uint16_t* wb, int32_t* route_ctr, hipStream_t s) {
+                         uint16_t* wb, int32_t* route_ctr, int qnl, int8_t* xq, float* xs,
+                         hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
+  if (qnl && !router_codes_x(T)) return hipErrorInvalidValue;
   if (T <= 64) {
     const unsigned tt = d.H >= 4096 ? 2 : 4;  // tokens per block (k_router_small's TT)
-    const dim3 grid((unsigned)((d.E + 3) / 4), (unsigned)((T + tt - 1) / tt));
+    // with qnl, one extra block per token group codes x
+    const dim3 grid((unsigned)((d.E + 3) / 4 + (qnl ? 1 : 0)), (unsigned)((T + tt - 1) / tt));
     auto go = [&](auto npl_tag) {
       constexpr int NPL = decltype(npl_tag)::value;
       launch("router_small", x_bf16 ? k_router_small<true, NPL> : k_router_small<false, NPL>,
-             grid, 256, 0, s, x, (int)T, Wr, bias, d.E, norm, rinv, logits, route_ctr);
+             grid, 256, 0, s, x, (int)T, Wr, bias, d.E, norm, rinv, logits, route_ctr, qnl, xq,
+             xs);
     };
     switch (d.H) {
       case 256: go(std::integral_constant<int, 1>{}); break;
