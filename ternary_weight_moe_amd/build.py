@@ -21,6 +21,7 @@ SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "mi
            "attn.hip", "convert.hip"]
 HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(CSRC, "wave.h"),
            os.path.join(CSRC, "limbs.h"), os.path.join(CSRC, "quant.h"),
+           os.path.join(CSRC, "digits.h"),
            os.path.join(ROOT, "include", "maple_moe.h"),
            os.path.join(ROOT, "include", "maple_head.h"),
            os.path.join(ROOT, "include", "maple_attn.h")]

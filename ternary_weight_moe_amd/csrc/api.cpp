@@ -61,7 +61,7 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->xq = (int8_t*)take((size_t)T * 4 * d.H);
   ws->part = (int32_t*)take(sizeof(int32_t) * 4 * d.E);
   ws->xs = (float*)take(sizeof(float) * 5 * T);
-  ws->hq = (int8_t*)take((size_t)Tk * 2 * d.I);
+  ws->hq = (int8_t*)take((size_t)Tk * 9 * d.I / 4);
   ws->hs = (float*)take(sizeof(float) * 4 * Tk);
   ws->y = take(sizeof(float) * Tk * d.H);
   ws->xb = (uint16_t*)take(sizeof(uint16_t) * 2 * T * d.H);

@@ -48,13 +48,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kT = 32;   // positions per cache tile
 constexpr int kNW = 4;   // waves per work-group
 
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ v8bf as_bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
-__device__ __forceinline__ uint4 as_u4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
-
-// Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
-constexpr int kBufferWord3 = 0x00020000;
 
 // Element offsets inside one 32 x D tile (the layout of maple_attn.h).
 __device__ __forceinline__ int key_off(int r, int d) { return ((d >> 5) * kT + r) * 32 + (d & 31); }

@@ -1,5 +1,6 @@
 // Expert FFN for many tokens per expert (prefill, batched decode): grouped
-// int8 GEMMs on the matrix cores.
+// GEMMs on the matrix cores (fp4 x fp6 for the fast form, int8 for the fine
+// form and A8).
 //
 // Grouping by expert turns each expert's work into a dense contraction: the M
 // rows of an expert's tile are the slots routed to it, so one fetch of its
@@ -9,10 +10,11 @@
 //
 // Precision.  Weights enter the MFMA as their offset codes c = w + 1 in
 // {0,1,2}; sum_k w_k q_k = sum_k c_k q_k - sum_k q_k, with the row sum of q
-// taken once per row.  An activation row v (x, or h) is coded per row into
-// int8 limbs (limbs.h).  Two limbs (coding error |v|max * 2^-15 per element,
-// inside a single layer's output tolerance; one limb, |v|max * 2^-8, would not
-// be) with per-slot fp16 expert outputs make the fast form.  Three limbs with
+// taken once per row.  An activation row v (x, or h) is coded per row.  Three
+// six-bit digits (digits.h: coding error |v|max * 2^-15 per element, inside a
+// single layer's output tolerance; one int8 limb, |v|max * 2^-8, would not be)
+// on the fp4 x fp6 MFMA, with per-slot fp16 expert outputs, make the fast
+// form.  The other forms code into int8 limbs (limbs.h).  Three limbs with
 // fp32 h and fp32 expert outputs make the fine form, whose error stays near
 // fp32 rounding: a 24-layer residual stack needs that, since its routing
 // decisions sit downstream of every earlier layer's error.  The same kernels
@@ -79,28 +81,22 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
 
 // ---- x -> int8 limbs, per-token scale, limb row sums, 1/rms ---------------------
 
-// One wave per token (quant_row), 4 tokens per block.
+// One wave per token (quant_row: int8 limbs; quant_row6 with NL = 0: the
+// fast form's digit layout), 4 tokens per block.
 template <bool BF16, int NL>
 __global__ __launch_bounds__(256) void k_quant_x(const void* __restrict__ x, int T, int H,
                                                  int norm, int8_t* __restrict__ xq,
                                                  float* __restrict__ xs) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // wave-uniform
-  quant_row<BF16, NL>(x, t, T, H, norm, xq, xs, threadIdx.x & 63);
+  if constexpr (NL == 0)
+    quant_row6<BF16>(x, t, T, H, norm, xq, xs, threadIdx.x & 63);
+  else
+    quant_row<BF16, NL>(x, t, T, H, norm, xq, xs, threadIdx.x & 63);
 }
 
-// ---- gate/up + SwiGLU + re-coding of h --------------------------------------------
+// ---- gate/up + SwiGLU + re-coding of h (fast form) ---------------------------------
 
-// v_mfma_i32_32x32x32_i8: A lane l supplies row l % 32 and 16 bytes of K
-// group l / 32; B lane l column l % 32, same K group; accumulator register j
-// of lane l holds row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.  One wave
-// per SIMD issues these at nearly the full int8 rate (the 16x16x64 form needs
-// two waves per SIMD for that).
-//
-// K order.  A stage covers 256 codes of a row, 16 words of 16 codes.  Lane
-// group kg = lane / 32 holds words 4kg..4kg+3 (steps 0-3) and 8+4kg..8+4kg+3
-// (steps 4-7), so MFMA step s uses word 8 (s / 4) + 4 kg + s % 4; the x limbs
-// of the same step come from the same 16 codes.
 // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (about 1e-7
 // relative error); z -> -inf gives -0, z -> +inf gives z.
 __device__ __forceinline__ float silu_fast(float z) {
@@ -119,25 +115,33 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-__device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
+// The fast form multiplies fp4 weight codes by fp6 digit planes (digits.h) on
+// v_mfma_scale_f32_32x32x64_f8f6f4: A lane l supplies row l % 32 and 32 codes,
+// B lane l column l % 32 and the same 32 values' digits; accumulator register
+// j of lane l holds row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.
+//
+// K order.  A chunk is 128 codes of a row (32 bytes, 4 blocks of 32).  Lane
+// group kg = lane / 32 loads bytes 16 kg .. 16 kg + 15 of the chunk (blocks
+// 2 kg and 2 kg + 1, the chunk's pair kg in the digit layout) and MFMA step
+// s = 0, 1 uses block 2 kg + s: two words of the load, and the 72 digit bytes
+// of that block, so the 144 bytes of the lane's pair feed both steps.
 
 // One block (4 waves): one M tile (TM = 32 slots of one expert) x one of NS
 // column parts of h, i.e. 2I/NS weight rows.  Wave w owns h columns
 // [cb + w I/(4 NS), cb + (w+1) I/(4 NS)) of part cb: gate N-subtiles b < NBG
 // and up N-subtiles b >= NBG (32 columns each) with identical (row, column)
-// positions per lane, so silu(g)*u is formed in registers.  With NS = 2 the
-// accumulators (2 limbs x 2 NBG N-subtiles x 16) take 128 registers and two
-// blocks share a CU; h is then re-coded with one scale per slot and part, and
-// the down projection sums the parts' contributions with their own scales.
+// positions per lane, so silu(g)*u is formed in registers.  The three digit
+// planes of a step add into one fp32 accumulator per N-subtile (64 registers
+// at NS = 2, so two blocks share a CU); h is then re-coded into digits with one
+// scale per slot and part, and the down projection sums the parts'
+// contributions with their own scales.
 //
-// Weights go straight from global memory into B operands: per N-subtile and
-// stage each lane holds two 16-byte pieces of one weight row (one load
-// instruction covers 32 contiguous bytes of 32 rows), refilled with the next
-// stage right after their last use, a full stage ahead.  The x limbs
+// Weights go straight from global memory into A operands: per N-subtile and
+// chunk each lane holds 16 bytes of one weight row, refilled with the next
+// stage right after their last use, a full stage ahead.  The x digits
 // (gathered through sorted_token) pass through registers into a
-// double-buffered LDS tile, two stages ahead; rows are padded to 272 bytes.
+// double-buffered LDS tile, two stages ahead; a slot's 576 bytes of a stage
+// are padded to 592.
 template <int I, int NS>
 __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
@@ -145,20 +149,24 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     int8_t* __restrict__ hq, float* __restrict__ hs, int64_t Tk) {
-  constexpr int NL = 2;  // limbs
   constexpr int NW = 4;
-  constexpr int IP = I / NS;            // h columns of the block's part
-  constexpr int NBG = IP / 128;         // gate N-subtiles per wave (and as many up)
+  constexpr int IP = I / NS;                    // h columns of the block's part
+  constexpr int NBG = IP / 128;                 // gate N-subtiles per wave (and as many up)
   constexpr int NB = 2 * NBG;
-  constexpr int KS = 256;               // codes per stage (8 MFMA steps)
-  constexpr int ROWB = KS + 16;         // padded LDS row: one limb of one slot
-  constexpr int ABUF = NL * TM * ROWB;  // one stage of x limbs
-  constexpr int HBYTES = 2 * TM * IP;   // h-limb staging in the epilogue (two limbs)
-  constexpr int SMEM = 2 * ABUF > HBYTES ? 2 * ABUF : HBYTES;
-  static_assert(TM == 32 && NB % 2 == 0, "tile shape");
-  __shared__ __align__(16) int8_t smem[SMEM];
+  constexpr int KS = 256;                       // codes per stage: two chunks
+  constexpr int SROW = KS / 64 * kPairBytes;    // digit bytes of a slot and stage (576)
+  constexpr int ROWB = SROW + 16;               // padded LDS row
+  constexpr int ABUF = TM * ROWB;               // one stage of x digits
+  constexpr int HROWP = IP / 64 * kPairBytes;   // digit bytes of a slot's part of h
+  constexpr int HROWB = HROWP + 16;
+  constexpr int SMEM = 2 * ABUF > TM * HROWB ? 2 * ABUF : TM * HROWB;
+  constexpr int SEGS = SROW / 16;               // 16-byte units per slot and stage
+  constexpr int NU = TM * SEGS;                 // per stage
+  constexpr int NR = (NU + 255) / 256;          // per thread
+  static_assert(TM == 32 && NBG >= 1, "tile shape");
+  __shared__ __align__(16) uint8_t smem[SMEM];
   __shared__ float s_sx[TM];
-  __shared__ int s_xsum[1][TM], s_tok[TM];
+  __shared__ int s_xsum[TM], s_tok[TM];
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
   __shared__ __align__(16) float s_al[2 * I];
@@ -174,17 +182,23 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   if (tid < TM) {
     const int tok = tid < np ? sorted_tok[p0 + tid] : -1;
     s_tok[tid] = tok;
-    const int* xi = reinterpret_cast<const int*>(xs);
     s_sx[tid] = tok >= 0 ? xs[tok] * xs[4 * T + tok] : 0.f;
-    s_xsum[0][tid] = tok >= 0 ? xi[T + tok] : 0;
+    s_xsum[tid] = tok >= 0 ? reinterpret_cast<const int*>(xs)[T + tok] : 0;
   }
   const int rowb = H / 4;
+  const int64_t xrow = 9 * (int64_t)H / 4;   // digit bytes of a token
   const uint8_t* We = packed + (int64_t)e * 3 * H * I / 4;
-  const int pbase = part * IP;             // first h column of the part
+  const int pbase = part * IP;                // first h column of the part
   const int cbase = pbase + wave * (IP / 4);  // first h column of the wave
-  const uint8_t* brow = We + (int64_t)(cbase + r32) * rowb + 16 * kg;
-  auto bsrc = [&](int b, int st) -> const uint8_t* {
-    return brow + (b < NBG ? 0 : (int64_t)I * rowb) + (int64_t)(32 * (b % NBG)) * rowb + st * 64;
+  // weights by buffer loads: one descriptor for the expert's gate/up rows, the
+  // lane's row in a 32-bit offset, the N-subtile, stage and chunk in the
+  // scalar offset (one address register instead of a 64-bit pointer each)
+  const __amdgpu_buffer_rsrc_t wsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(We), 0, 2 * I * rowb, kBufferWord3);
+  const int bvoff = (cbase + r32) * rowb + 16 * kg;
+  auto bload = [&](int b, int st, int c) {
+    const int soff = (b < NBG ? 0 : I * rowb) + 32 * (b % NBG) * rowb + st * (KS / 4) + 32 * c;
+    return as_u4(__builtin_amdgcn_raw_buffer_load_b128(wsrc, bvoff, soff, 0));
   };
   // a_g | a_u of the expert (2I floats) in LDS for the epilogue
   const float* al = alpha + (int64_t)e * (2 * I + H);
@@ -192,103 +206,98 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     reinterpret_cast<float4*>(s_al)[u] = reinterpret_cast<const float4*>(al)[u];
   __syncthreads();
 
-  // x-limb units of a stage: u = r*256 + tid, limb u / 512, slot (u / 16) % 32,
-  // 16-byte segment u % 16.  Rows past np read slot 0's token (discarded).
-  constexpr int NR = 2 * NL;  // units per thread
-  const int8_t* asrc[NR];
+  // x-digit units of a stage: u = r 256 + tid (< NU), slot u / SEGS, 16-byte
+  // segment u % SEGS.  Rows past np read slot 0's token (discarded); the
+  // units past NU of the last round repeat unit NU - 1 and go to the padding
+  // of a row (never read), so the stores need no branch in the loop.
+  // sources as 32-bit offsets in 16-byte units (T xrow / 16 < 2^32)
+  uint32_t asrc[NR];
   int adst[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int u = r * 256 + tid;
-    const int limb = u >> 9, slot = (u >> 4) & 31, seg = u & 15;
+    const int u = min(r * 256 + tid, NU - 1);
+    const int slot = u / SEGS, seg = u % SEGS;
     const int tok = s_tok[slot] >= 0 ? s_tok[slot] : s_tok[0];
-    asrc[r] = xq + (int64_t)tok * NL * H + (int64_t)limb * H + 16 * seg;
-    adst[r] = (limb * TM + slot) * ROWB + 16 * seg;
+    asrc[r] = (uint32_t)tok * (uint32_t)(xrow / 16) + seg;
+    adst[r] = r * 256 + tid < NU ? slot * ROWB + 16 * seg : (tid % TM) * ROWB + SROW;
   }
-  uint4 as0, as1, as2, as3;  // one stage of x limbs in flight (named: kept in registers)
+  const uint4* xq16 = reinterpret_cast<const uint4*>(xq);
+  static_assert(NR == 5, "x units per thread");
+  uint4 as0, as1, as2, as3, as4;  // one stage of x digits in flight (named: kept in registers)
   auto fetch_a = [&](int st) {
-    as0 = *reinterpret_cast<const uint4*>(asrc[0] + st * KS);
-    as1 = *reinterpret_cast<const uint4*>(asrc[1] + st * KS);
-    as2 = *reinterpret_cast<const uint4*>(asrc[2] + st * KS);
-    as3 = *reinterpret_cast<const uint4*>(asrc[3] + st * KS);
+    const uint32_t so = st * (SROW / 16);
+    as0 = xq16[asrc[0] + so];
+    as1 = xq16[asrc[1] + so];
+    as2 = xq16[asrc[2] + so];
+    as3 = xq16[asrc[3] + so];
+    as4 = xq16[asrc[4] + so];
   };
   auto store_a = [&](int buf) {
-    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[0]) = as0;
-    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[1]) = as1;
-    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[2]) = as2;
-    *reinterpret_cast<uint4*>(smem + buf * ABUF + adst[3]) = as3;
+    uint8_t* d = smem + buf * ABUF;
+    *reinterpret_cast<uint4*>(d + adst[0]) = as0;
+    *reinterpret_cast<uint4*>(d + adst[1]) = as1;
+    *reinterpret_cast<uint4*>(d + adst[2]) = as2;
+    *reinterpret_cast<uint4*>(d + adst[3]) = as3;
+    *reinterpret_cast<uint4*>(d + adst[4]) = as4;
   };
 
-  v16i acc[NL][NB];  // [limb][N-subtile]
+  v16f_t acc[NB];
 #pragma unroll
-  for (int l = 0; l < NL; ++l)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[l][b] = v16i{};
+  for (int b = 0; b < NB; ++b) acc[b] = v16f_t{};
 
   const int nst = H / KS;
-  uint4 bq[2][NB];  // [half][N-subtile]: words of steps 0-3 / 4-7
+  uint4 bq[2][NB];  // [chunk][N-subtile]
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    bq[0][b] = *reinterpret_cast<const uint4*>(bsrc(b, 0));
-    bq[1][b] = *reinterpret_cast<const uint4*>(bsrc(b, 0) + 32);
+    bq[0][b] = bload(b, 0, 0);
+    bq[1][b] = bload(b, 0, 1);
   }
   fetch_a(0);
   store_a(0);
   fetch_a(min(1, nst - 1));
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
-    const int8_t* sa = smem + (st & 1) * ABUF + r32 * ROWB + 64 * kg;
+    const uint8_t* sb = smem + (st & 1) * ABUF + r32 * ROWB + kPairBytes * kg;
     // loads are issued unconditionally (the last stage reloads itself) so the
     // count of loads in flight is the same at every use and the waits stay
     // partial
     const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      v4i af[4][NL];  // [step in half][limb]
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
+      for (int s = 0; s < 2; ++s) {
+        v8i_t dp[3];  // the step's digit planes
 #pragma unroll
-        for (int l = 0; l < NL; ++l)
-          af[s2][l] = *reinterpret_cast<const v4i*>(sa + l * TM * ROWB + 128 * half + 16 * s2);
-      // N-subtiles in pairs: four independent accumulators between two
-      // updates of one.  The B operands of the next step are unpacked (7 VALU
-      // per word) while the MFMAs of this step run; the group barriers ask
-      // the scheduler for that interleave (an MFMA, then 3-4 VALU), and a
-      // scheduling barrier per pair bounds the registers it may hoist.
-      v4i u0 = unpack_word(word_of(bq[half][0], 0)), u1 = unpack_word(word_of(bq[half][1], 0));
-#pragma unroll
-      for (int b = 0; b < NB; b += 2) {
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const v4i b0 = u0, b1 = u1;
-          if (s2 < 3) {
-            u0 = unpack_word(word_of(bq[half][b], s2 + 1));
-            u1 = unpack_word(word_of(bq[half][b + 1], s2 + 1));
-          } else if (b + 2 < NB) {
-            u0 = unpack_word(word_of(bq[half][b + 2], 0));
-            u1 = unpack_word(word_of(bq[half][b + 3], 0));
-          }
-#pragma unroll
-          for (int l = 0; l < NL; ++l) acc[l][b] = mfma32(b0, af[s2][l], acc[l][b]);
-#pragma unroll
-          for (int l = 0; l < NL; ++l) acc[l][b + 1] = mfma32(b1, af[s2][l], acc[l][b + 1]);
+        for (int l = 0; l < 3; ++l) {
+          const uint2* p = reinterpret_cast<const uint2*>(sb + 2 * kPairBytes * c + 72 * s + 24 * l);
+          const uint2 a0 = p[0], a1 = p[1], a2 = p[2];
+          dp[l] = v8i_t{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
         }
-        bq[half][b] = *reinterpret_cast<const uint4*>(bsrc(b, st1) + 32 * half);
-        bq[half][b + 1] = *reinterpret_cast<const uint4*>(bsrc(b + 1, st1) + 32 * half);
+        v8i_t wf[NB];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          // 4 MFMAs against the 14 VALU of the next two unpacks
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int b = 0; b < NB; ++b)
+          wf[b] = unpack_fp4(word_of(bq[c][b], 2 * s), word_of(bq[c][b], 2 * s + 1));
+        // NB independent accumulators between two updates of one
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma_digits<0>(wf[b], dp[0], acc[b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma_digits<1>(wf[b], dp[1], acc[b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma_digits<2>(wf[b], dp[2], acc[b]);
       }
+      // The chunk's MFMAs, then its refill, pinned by scheduling barriers:
+      // left to itself the scheduler issues every refill at the end of the
+      // stage (or at its start, where the refilled registers then need copies),
+      // and the next chunk waits for them.
+#pragma unroll
+      for (int i = 0; i < 6 * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (unpacking)
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bq[c][b] = bload(b, st1, c);  // refill after the last use
+      __builtin_amdgcn_sched_barrier(0);
     }
     store_a((st + 1) & 1);  // stage st1; its buffer was last read in stage st - 1
     fetch_a(st2);
@@ -297,11 +306,11 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
 
   // Epilogue.  The weights were the MFMA's first operand, so lane (r32, kg)
   // holds slot m = r32 and, in register 4i + t of N-subtile b, h column
-  // cbase + 32 b + 8 i + 4 kg + t (cbase = wave I/4): four consecutive columns
-  // per register quad.
+  // cbase + 32 b + 8 i + 4 kg + t: four consecutive columns per register quad.
+  // acc = sum_k c_k q_k, so sum_k w_k q_k = acc - sum_k q_k.
   const int m = r32;
   const float sx = s_sx[m];
-  const int xsum = s_xsum[0][m];
+  const float xsum = (float)s_xsum[m];
   float hv[NBG][16];
   float mx = 0.f;
 #pragma unroll
@@ -315,8 +324,8 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int j = 4 * i + t;
-        const float gv = (float)(128 * acc[0][b][j] + acc[1][b][j] - xsum) * (sx * gs[t]);
-        const float uv = (float)(128 * acc[0][b + NBG][j] + acc[1][b + NBG][j] - xsum) * (sx * us[t]);
+        const float gv = (acc[b][j] - xsum) * (sx * gs[t]);
+        const float uv = (acc[b + NBG][j] - xsum) * (sx * us[t]);
         const float h = silu_fast(gv) * uv;
         hv[b][j] = h;
         mx = fmaxf(mx, fabsf(h));
@@ -330,35 +339,44 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   if (kg == 0) s_red[wave][m] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red[0][m], s_red[1][m]), fmaxf(s_red[2][m], s_red[3][m]));
-  const float sc = mx > 0.f ? mx / kQ2Max : 1.f;
-  const float inv = mx > 0.f ? kQ2Max / mx : 1.f;
-  // h limbs of the part staged in LDS (reusing the x buffers) as [limb][row][IP]
-  int8_t* sH = smem;
+  const float sc = mx > 0.f ? mx / kQ6Max : 1.f;
+  const float inv = mx > 0.f ? kQ6Max / mx : 1.f;
+  // the part's h digits staged in LDS (reusing the x buffers), [slot][HROWB].
+  // Block wave NBG + b of the part holds the lane's columns 8 i + 4 kg + t:
+  // fields 16 (i / 2) + 8 kg + 2 t + i % 2, i.e. for i / 2 = pc the 8 fields
+  // (48 bits) at byte 12 pc + 6 kg of each plane.
+  uint8_t* sH = smem;
   int qs = 0;
 #pragma unroll
-  for (int b = 0; b < NBG; ++b)
+  for (int b = 0; b < NBG; ++b) {
+    const int blk = wave * NBG + b;
+    uint8_t* bp = sH + m * HROWB + (blk >> 1) * kPairBytes + (blk & 1) * 72 + 6 * kg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t hw = 0u, lw = 0u;
+    for (int pc = 0; pc < 2; ++pc) {
+      uint32_t cd[3][8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int q = code_q(hv[b][4 * i + t], inv, 16256);
-        int hi, lo;
-        split2(q, &hi, &lo);
-        hw |= (uint32_t)(hi & 0xFF) << (8 * t);
-        lw |= (uint32_t)(lo & 0xFF) << (8 * t);
+      for (int f = 0; f < 8; ++f) {
+        const int q = code_q(hv[b][4 * (2 * pc + (f & 1)) + (f >> 1)], inv, kQ6);
         qs += q;
+        digits_of(q, &cd[0][f], &cd[1][f], &cd[2][f]);
       }
-      const int c = cbase - pbase + 32 * b + 8 * i + 4 * kg;
-      *reinterpret_cast<uint32_t*>(sH + m * IP + c) = hw;
-      *reinterpret_cast<uint32_t*>(sH + TM * IP + m * IP + c) = lw;
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        uint16_t o[3];
+        pack_piece(cd[l], o);
+        uint16_t* d16 = reinterpret_cast<uint16_t*>(bp + kPlaneBytes * l + 12 * pc);
+        d16[0] = o[0];
+        d16[1] = o[1];
+        d16[2] = o[2];
+      }
     }
+  }
   {
     const auto r = __builtin_amdgcn_permlane32_swap((unsigned)qs, (unsigned)qs, false, false);
     qs = (int)r[0] + (int)r[1];
   }
   if (kg == 0) s_redi[wave][m] = qs;
-  // hs: [part][scale | limb row sum (int bits)][slot]
+  // hs: [part][scale | digit row sum (int bits)][slot]
   if (wave == 0 && kg == 0 && m < np) hs[2 * part * Tk + p0 + m] = sc;
   __syncthreads();
   if (tid < np) {
@@ -367,16 +385,15 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     for (int w = 0; w < NW; ++w) tot += s_redi[w][tid];
     reinterpret_cast<int*>(hs)[(2 * part + 1) * Tk + p0 + tid] = tot;
   }
-  // rows [0, np) of both limbs to hq[slot][limb][I] (the part's columns), 16 bytes per thread
-  constexpr int segs_row = IP / 16;
+  // rows [0, np) of the part to hq[slot][9 I / 4 bytes], 16 bytes per thread
+  constexpr int HSEG = HROWP / 16;
 #pragma unroll
-  for (int c0 = 0; c0 < 2 * TM * segs_row; c0 += 256) {
+  for (int c0 = 0; c0 < TM * HSEG; c0 += 256) {
     const int c = c0 + tid;
-    const int limb = c / (TM * segs_row), r = (c / segs_row) % TM, seg = c % segs_row;
-    if (r < np)
-      *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + r) * 2 * I + (int64_t)limb * I + pbase +
-                                seg * 16) =
-          *reinterpret_cast<const uint4*>(sH + limb * TM * IP + r * IP + seg * 16);
+    const int r = c / HSEG, seg = c % HSEG;
+    if (c < TM * HSEG && r < np)
+      *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + r) * (9 * I / 4) + part * HROWP + 16 * seg) =
+          *reinterpret_cast<const uint4*>(sH + r * HROWB + 16 * seg);
   }
 }
 
@@ -385,16 +402,16 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
 // One block (NWV waves): one M tile (TM = 32 slots of one expert) x H / NHB
 // consecutive outputs (NHB blocks per tile, consecutive blocks of one XCD),
 // in chunks of 32 NBW NWV outputs: wave w owns NBW N-subtiles of 32 outputs
-// per chunk.  With 8 waves of 2 N-subtiles, two waves share each
-// SIMD and cover each other's waits.  The tile's h limbs (all of K = I) sit in
-// LDS for the whole block.  The weights are the MFMA's first operand (rows =
-// outputs) and h the second (columns = slots), so a lane ends with 4
+// per chunk.  Two blocks share a CU and cover each other's waits.  The tile's
+// h digits (all of K = I, 9 I / 4 bytes per slot) sit in LDS for the whole
+// block.  The weights are the MFMA's first operand (rows = outputs) and the
+// digit planes of h the second (columns = slots), so a lane ends with 4
 // consecutive outputs of one slot per register quad and writes them with one
 // store.  The weight registers of 128 codes are refilled with the next chunk
-// right after their last step, a full chunk ahead of their next use.  The lo
-// accumulators start at -rowsum(q) of the lane's slot (the offset-code term).
-// K order: MFMA step s uses word 8 (s / 4) + 4 kg + s % 4 of the row (I/16
-// words), so a lane holds 16 contiguous bytes per 128 codes of each row.
+// right after their last step, a full chunk ahead of their next use.  The
+// accumulators start at -sum(q) of the lane's slot and h part (the offset-code
+// term).  K order as in the gate/up kernel: chunk q is the row's 128 codes
+// 128 q .., lane group kg holds its pair kg (blocks 4q + 2kg, 4q + 2kg + 1).
 template <int I, int NBW, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H, int NHB,
@@ -402,10 +419,11 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y) {
   constexpr int NTH = 64 * NWV;
-  constexpr int NQ = I / 128;           // 16-byte pieces per lane and row
-  constexpr int ROWB = I + 16;          // padded LDS row: one limb of one slot
-  constexpr int CH = 32 * NBW * NWV;    // outputs per chunk
-  __shared__ __align__(16) int8_t sA[2][TM][ROWB];
+  constexpr int NQ = I / 128;                  // 16-byte pieces per lane and row
+  constexpr int HROW = I / 64 * kPairBytes;    // digit bytes of one slot
+  constexpr int ROWB = HROW + 16;              // padded LDS row
+  constexpr int CH = 32 * NBW * NWV;           // outputs per chunk
+  __shared__ __align__(16) uint8_t sA[TM][ROWB];
   // dynamic LDS: a_d of the block's H / NHB outputs, then one fp16 output patch per wave
   extern __shared__ __align__(16) float s_ad[];
   const int local = blockIdx.x >> 3, hp = local % NHB;
@@ -431,19 +449,19 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   for (int b = 0; b < NBW; ++b)
 #pragma unroll
     for (int q = 0; q < NQ; ++q) bq[b][q] = *bptr(0, b, q);
-  // h limbs of the tile's slots: 2 * TM rows of I bytes; rows past np are zero.
+  // h digits of the tile's slots: TM rows of HROW bytes; rows past np are zero.
   // All loads are issued before the first LDS store.
-  constexpr int SEGR = I / 16;
-  constexpr int NHU = 2 * TM * SEGR / NTH;  // 16-byte units per thread
-  static_assert(NHU >= 1, "h units");
+  constexpr int SEGR = HROW / 16;
+  constexpr int NHU = (TM * SEGR + NTH - 1) / NTH;  // 16-byte units per thread
+  const uint8_t* hsrc = reinterpret_cast<const uint8_t*>(hq) + (int64_t)p0 * HROW;
   uint4 hv[NHU];
 #pragma unroll
   for (int i = 0; i < NHU; ++i) {
     const int u = tid + NTH * i;
-    const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
-    hv[i] = r < np ? *reinterpret_cast<const uint4*>(hq + (int64_t)(p0 + r) * 2 * I +
-                                                     (int64_t)limb * I + 16 * sg)
-                   : make_uint4(0u, 0u, 0u, 0u);
+    const int r = u / SEGR, sg = u % SEGR;
+    hv[i] = u < TM * SEGR && r < np
+                ? *reinterpret_cast<const uint4*>(hsrc + (int64_t)r * HROW + 16 * sg)
+                : make_uint4(0u, 0u, 0u, 0u);
   }
   // a_d through LDS: the epilogue's reads then never wait behind the weight
   // loads in flight for the next chunk.  HB / 4 <= 4 NTH.
@@ -451,62 +469,68 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     av[i] = reinterpret_cast<const float4*>(ad)[min(tid + NTH * i, HB / 4 - 1)];
-  // this lane's slot (the accumulator column): scale and limb row sum per h part
+  // this lane's slot (the accumulator column): scale and digit row sum per h part
   const bool live = r32 < np;
-  float sc[NS];
-  int hsum[NS];
+  float sc[NS], hsum[NS];
 #pragma unroll
   for (int h2 = 0; h2 < NS; ++h2) {
     sc[h2] = live ? hs[2 * h2 * Tk + p0 + r32] : 0.f;
-    hsum[h2] = live ? reinterpret_cast<const int*>(hs)[(2 * h2 + 1) * Tk + p0 + r32] : 0;
+    hsum[h2] = live ? (float)reinterpret_cast<const int*>(hs)[(2 * h2 + 1) * Tk + p0 + r32] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < NHU; ++i) {
     const int u = tid + NTH * i;
-    const int limb = u / (TM * SEGR), r = (u / SEGR) % TM, sg = u % SEGR;
-    *reinterpret_cast<uint4*>(&sA[limb][r][16 * sg]) = hv[i];
+    if (u < TM * SEGR)
+      *reinterpret_cast<uint4*>(&sA[u / SEGR][16 * (u % SEGR)]) = hv[i];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (tid + NTH * i < HB / 4) reinterpret_cast<float4*>(s_ad)[tid + NTH * i] = av[i];
   __syncthreads();
-  const int8_t* sa = &sA[0][r32][64 * kg];
+  const uint8_t* sa = &sA[r32][kPairBytes * kg];
   constexpr int YROW = 64 * NBW + 16;  // padded row of a wave's output patch (bytes)
   int8_t* sY = reinterpret_cast<int8_t*>(s_ad + HB) + wave * 32 * YROW;
 
   for (int c = 0; c < nch; ++c) {
-    // keeps the A-operand LDS reads inside the loop (hoisted, they would hold
-    // 128 registers for the whole block and halve the blocks a CU can run)
+    // keeps the B-operand LDS reads inside the loop (hoisted, they would hold
+    // the whole h tile in registers and halve the blocks a CU can run)
     asm volatile("" ::: "memory");
     const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
-    v16i acc[NS][2][NBW];  // [h part][limb][N-subtile]
+    v16f_t acc[NS][NBW];  // [h part][N-subtile]
 #pragma unroll
     for (int h2 = 0; h2 < NS; ++h2)
 #pragma unroll
-      for (int b = 0; b < NBW; ++b) {
-        acc[h2][0][b] = v16i{};
+      for (int b = 0; b < NBW; ++b)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[h2][1][b][j] = -hsum[h2];
-      }
+        for (int j = 0; j < 16; ++j) acc[h2][b][j] = -hsum[h2];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int h2 = q / (NQ / NS);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const v4i a0 = *reinterpret_cast<const v4i*>(sa + 128 * q + 16 * s4);
-        const v4i a1 = *reinterpret_cast<const v4i*>(sa + TM * ROWB + 128 * q + 16 * s4);
+      for (int s = 0; s < 2; ++s) {
+        v8i_t dp[3];
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-          const v4i wf = unpack_word(word_of(bq[b][q], s4));
-          acc[h2][0][b] = mfma32(wf, a0, acc[h2][0][b]);
-          acc[h2][1][b] = mfma32(wf, a1, acc[h2][1][b]);
+        for (int l = 0; l < 3; ++l) {
+          const uint2* p = reinterpret_cast<const uint2*>(sa + 2 * kPairBytes * q + 72 * s + 24 * l);
+          const uint2 a0 = p[0], a1 = p[1], a2 = p[2];
+          dp[l] = v8i_t{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
         }
+        v8i_t wf[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+          wf[b] = unpack_fp4(word_of(bq[b][q], 2 * s), word_of(bq[b][q], 2 * s + 1));
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[h2][b] = mfma_digits<0>(wf[b], dp[0], acc[h2][b]);
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[h2][b] = mfma_digits<1>(wf[b], dp[1], acc[h2][b]);
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) acc[h2][b] = mfma_digits<2>(wf[b], dp[2], acc[h2][b]);
       }
 #pragma unroll
       for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
     }
     // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk:
-    // y[slot][o] = a_d[o] * sum_parts s * (128 C_hi + C_lo) as fp16, first into the wave's
+    // y[slot][o] = a_d[o] * sum_parts s * acc as fp16, first into the wave's
     // LDS patch [slot][32 NBW outputs], then out in whole 128-byte lines
 #pragma unroll
     for (int b = 0; b < NBW; ++b)
@@ -518,9 +542,7 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
 #pragma unroll
         for (int h2 = 0; h2 < NS; ++h2)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            v[t] = fmaf(sc[h2], (float)(128 * acc[h2][0][b][4 * i + t] + acc[h2][1][b][4 * i + t]),
-                        v[t]);
+          for (int t = 0; t < 4; ++t) v[t] = fmaf(sc[h2], acc[h2][b][4 * i + t], v[t]);
         const float v0 = a.x * v[0], v1 = a.y * v[1], v2 = a.z * v[2], v3 = a.w * v[3];
         *reinterpret_cast<uint2*>(sY + r32 * YROW + 2 * ol) =
             make_uint2(pack_f16(v0, v1), pack_f16(v2, v3));
@@ -983,12 +1005,13 @@ hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, 
                           const Workspace& ws, hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   const unsigned nb = (unsigned)((T + 3) / 4);
+  // nl = 2 asks for the fast form, whose x goes in the digit layout
   auto k = x_bf16 ? (nl == 1   ? k_quant_x<true, 1>
                      : nl == 3 ? k_quant_x<true, 3>
-                               : k_quant_x<true, 2>)
+                               : k_quant_x<true, 0>)
                   : (nl == 1   ? k_quant_x<false, 1>
                      : nl == 3 ? k_quant_x<false, 3>
-                               : k_quant_x<false, 2>);
+                               : k_quant_x<false, 0>);
   launch("quant_x", k, nb, 256, 0, s, x, (int)T, d.H, norm, ws.xq, ws.xs);
   return hipGetLastError();
 }
@@ -997,7 +1020,7 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
                               const float* alpha, const Workspace& ws, float* out,
                               const float* resid, float* delta, hipStream_t s) {
   const int64_t Tk = T * d.k;
-  const bool fine = nl != 2;  // the fp32-h kernels: three limbs, or one (A8)
+  const bool fine = nl != 2;  // the fp32-h kernels: three limbs, or one (A8); else the digit form
   const int mt = max_tiles(d, T);
   const unsigned nt = (unsigned)((mt + 7) & ~7);  // whole rounds of 8 XCDs
   // the down projection's outputs of a tile split over NHB blocks while the

@@ -30,13 +30,13 @@ struct Workspace {
   int32_t* n_tiles;     // [1]
   int32_t* route_ctr;   // [1]   arrival counter of the small-T routing kernel
   float* h;             // [T*k, I]  fp32 h (GEMV path, fine grouped path)
-  int8_t* xq;           // [T, 4, H] int8 limbs of x (two or three on the grouped path,
-                        //           three on the one-token path)
+  int8_t* xq;           // [T, 4, H] coded x: three int8 limbs (fine grouped form,
+                        //           one-token path), one (A8), or 9H/4 digit bytes (fast form)
   int32_t* part;        // [E, 4]    per-router-block partial limb sums (one-token path)
   float* xs;            // [5T]      scale of x's limbs | limb row sums (int bits, up to
                         //           three planes) | 1/rms(x) at plane 4
-  int8_t* hq;           // [T*k, 2, I] two int8 limbs of h
-  float* hs;            // [2, 2, T*k] per h column part: limb scale per slot | limb row sum (int bits)
+  int8_t* hq;           // [T*k, 9I/4] h in the digit layout (fast form)
+  float* hs;            // [2, 2, T*k] per h column part: scale per slot | sum q (int bits)
   void* y;              // [T*k, H]  expert outputs before the combine (grouped path):
                         //           fp16 in the fast form, fp32 in the fine form
   uint16_t* xb;         // [2, T, H] bf16 hi/lo planes of fp32 x (large-T router)
@@ -74,8 +74,9 @@ hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t*
                        hipStream_t s);
 // xb, wb: bf16-plane scratch (ws.xb, ws.wb) used above the small-T sizes;
 // route_ctr: the small-T routing kernel's arrival counter (zeroed here);
-// qnl > 0 (only where router_codes_x(T)): the router also codes x into qnl
-// int8 limbs, xq / xs as launch_quant_x writes them (1/rms computed from x)
+// qnl > 0 (only where router_codes_x(T)): the router also codes x as
+// launch_quant_x does for nl = qnl (int8 limbs, or digits for 2), xq / xs as
+// it writes them (1/rms computed from x)
 bool router_codes_x(int64_t T);
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          const float* Wr, const float* bias, const float* rinv, float* logits,
@@ -162,5 +163,11 @@ hipError_t launch_attn_decode(const AttnDims& d, int64_t B, int max_len, const u
 hipError_t launch_attn_fill(const AttnDims& d, int64_t B, int p_begin, int n_pos,
                             const uint16_t* k_lin, const uint16_t* v_lin, uint16_t* kc,
                             uint16_t* vc, hipStream_t s);
+
+// Raw buffer loads: word 3 of a descriptor (32-bit data format, no swizzle)
+// and the 16-byte result as a uint4.
+constexpr int kBufferWord3 = 0x00020000;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 as_u4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
 }  // namespace maple

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_router_small(const void* __restrict__ x
       logits[(int64_t)t * E + e] = dot * r + (bias ? bias[e] : 0.f);
   };
   // qnl > 0: one more block per token group (the first in x) codes the
-  // group's rows into qnl int8 limbs for the grouped kernels, wave w token
+  // group's rows for the grouped kernels (qnl int8 limbs, or digits for 2), wave w token
   // t0 + w, alongside the router blocks; this saves a kernel that would read
   // x once more
   if (qnl && blockIdx.x == 0) {
@@ -104,8 +104,8 @@ __global__ __launch_bounds__(256) void k_router_small(const void* __restrict__ x
     if ((threadIdx.x >> 6) < TT && tq < T) {  // wave-uniform
       if (qnl == 1)
         quant_row<BF16, 1, H>(x, tq, T, H, norm, xq, xs, lane);
-      else if (qnl == 2)
-        quant_row<BF16, 2, H>(x, tq, T, H, norm, xq, xs, lane);
+      else if (qnl == 2)  // the fast form's digit layout
+        quant_row6<BF16, H>(x, tq, T, H, norm, xq, xs, lane);
       else
         quant_row<BF16, 3, H>(x, tq, T, H, norm, xq, xs, lane);
     }
