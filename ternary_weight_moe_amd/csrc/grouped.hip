@@ -146,7 +146,7 @@ template <int I, int NS>
 __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
+    const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     int8_t* __restrict__ hq, float* __restrict__ hs, int64_t Tk) {
   constexpr int NW = 4;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   static_assert(TM == 32 && NBG >= 1, "tile shape");
   __shared__ __align__(16) uint8_t smem[SMEM];
   __shared__ float s_sx[TM];
-  __shared__ int s_xsum[TM], s_tok[TM];
+  __shared__ int s_xsum[TM];
   __shared__ float s_red[NW][TM];
   __shared__ int s_redi[NW][TM];
   __shared__ __align__(16) float s_al[2 * I];
@@ -174,16 +174,19 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   const int local = blockIdx.x >> 3, part = local % NS;
   const int tile = xcd_tile(8 * (local / NS) + (blockIdx.x & 7), *n_tiles);
   if (tile < 0) return;
-  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
-  const int p0 = offsets[e] + m0;
-  const int np = min(TM, offsets[e + 1] - p0);
+  const int2 trec = *reinterpret_cast<const int2*>(tiles + 2 * tile);
+  const int e = trec.x & 0xFFFF, np = trec.x >> 16, p0 = trec.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 5, r32 = lane & 31;
-  if (tid < TM) {
-    const int tok = tid < np ? sorted_tok[p0 + tid] : -1;
-    s_tok[tid] = tok;
-    s_sx[tid] = tok >= 0 ? xs[tok] * xs[4 * T + tok] : 0.f;
-    s_xsum[tid] = tok >= 0 ? reinterpret_cast<const int*>(xs)[T + tok] : 0;
+  // Prologue: only the loads that the first stage needs form a chain (tile
+  // record, token ids, x digits and weights); the x scales, digit sums and
+  // alphas that only the epilogue reads wait in registers until then.
+  float sxr = 0.f;
+  int xsr = 0;
+  if (tid < np) {
+    const int tok = sorted_tok[p0 + tid];
+    sxr = xs[tok] * xs[4 * T + tok];
+    xsr = reinterpret_cast<const int*>(xs)[T + tok];
   }
   const int rowb = H / 4;
   const int64_t xrow = 9 * (int64_t)H / 4;   // digit bytes of a token
@@ -200,16 +203,18 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
     const int soff = (b < NBG ? 0 : I * rowb) + 32 * (b % NBG) * rowb + st * (KS / 4) + 32 * c;
     return as_u4(__builtin_amdgcn_raw_buffer_load_b128(wsrc, bvoff, soff, 0));
   };
-  // a_g | a_u of the expert (2I floats) in LDS for the epilogue
-  const float* al = alpha + (int64_t)e * (2 * I + H);
-  for (int u = tid; u < I / 2; u += 256)
-    reinterpret_cast<float4*>(s_al)[u] = reinterpret_cast<const float4*>(al)[u];
-  __syncthreads();
+  // a_g | a_u of the expert (2I floats), for LDS before the epilogue
+  constexpr int NAL = (I / 2 + 255) / 256;
+  const float4* al = reinterpret_cast<const float4*>(alpha + (int64_t)e * (2 * I + H));
+  float4 alr[NAL];
+#pragma unroll
+  for (int i = 0; i < NAL; ++i) alr[i] = al[min(tid + 256 * i, I / 2 - 1)];
 
   // x-digit units of a stage: u = r 256 + tid (< NU), slot u / SEGS, 16-byte
-  // segment u % SEGS.  Rows past np read slot 0's token (discarded); the
-  // units past NU of the last round repeat unit NU - 1 and go to the padding
-  // of a row (never read), so the stores need no branch in the loop.
+  // segment u % SEGS, the slot's token read straight from sorted_tok.  Rows
+  // past np read slot 0's token (discarded); the units past NU of the last
+  // round repeat unit NU - 1 and go to the padding of a row (never read), so
+  // the stores need no branch in the loop.
   // sources as 32-bit offsets in 16-byte units (T xrow / 16 < 2^32)
   uint32_t asrc[NR];
   int adst[NR];
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   for (int r = 0; r < NR; ++r) {
     const int u = min(r * 256 + tid, NU - 1);
     const int slot = u / SEGS, seg = u % SEGS;
-    const int tok = s_tok[slot] >= 0 ? s_tok[slot] : s_tok[0];
+    const int tok = sorted_tok[p0 + (slot < np ? slot : 0)];
     asrc[r] = (uint32_t)tok * (uint32_t)(xrow / 16) + seg;
     adst[r] = r * 256 + tid < NU ? slot * ROWB + 16 * seg : (tid % TM) * ROWB + SROW;
   }
@@ -308,6 +313,14 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   // holds slot m = r32 and, in register 4i + t of N-subtile b, h column
   // cbase + 32 b + 8 i + 4 kg + t: four consecutive columns per register quad.
   // acc = sum_k c_k q_k, so sum_k w_k q_k = acc - sum_k q_k.
+  if (tid < TM) {
+    s_sx[tid] = sxr;
+    s_xsum[tid] = xsr;
+  }
+#pragma unroll
+  for (int i = 0; i < NAL; ++i)
+    if (tid + 256 * i < I / 2) reinterpret_cast<float4*>(s_al)[tid + 256 * i] = alr[i];
+  __syncthreads();
   const int m = r32;
   const float sx = s_sx[m];
   const float xsum = (float)s_xsum[m];
@@ -416,7 +429,7 @@ template <int I, int NBW, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H, int NHB,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y) {
   constexpr int NTH = 64 * NWV;
   constexpr int NQ = I / 128;                  // 16-byte pieces per lane and row
@@ -429,9 +442,8 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   const int local = blockIdx.x >> 3, hp = local % NHB;
   const int tile = xcd_tile(8 * (local / NHB) + (blockIdx.x & 7), *n_tiles);
   if (tile < 0) return;
-  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
-  const int p0 = offsets[e] + m0;
-  const int np = min(TM, offsets[e + 1] - p0);
+  const int2 trec = *reinterpret_cast<const int2*>(tiles + 2 * tile);
+  const int e = trec.x & 0xFFFF, np = trec.x >> 16, p0 = trec.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 5, r32 = lane & 31;
   const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4;
@@ -584,7 +596,7 @@ template <int I, int NL>
 __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int T, int H,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_tok,
+    const int32_t* __restrict__ sorted_tok,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     float* __restrict__ hf) {
   static_assert(NL == 1 || NL == 3, "one or three limbs");
@@ -599,9 +611,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
   const int local = blockIdx.x >> 3, part = local % NS;
   const int tile = xcd_tile(8 * (local / NS) + (blockIdx.x & 7), *n_tiles);
   if (tile < 0) return;
-  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
-  const int p0 = offsets[e] + m0;
-  const int np = min(TM, offsets[e + 1] - p0);
+  const int2 trec = *reinterpret_cast<const int2*>(tiles + 2 * tile);
+  const int e = trec.x & 0xFFFF, np = trec.x >> 16, p0 = trec.y;
   const bool two = np > 16;  // block-uniform: the second slot half has work
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, r16 = lane & 15;
@@ -758,9 +769,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
 template <int I, int NWV, int NL>
 __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     const float* __restrict__ hf, int H, int NHB, const uint8_t* __restrict__ packed,
-    const float* __restrict__ alpha, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    float* __restrict__ y) {
+    const float* __restrict__ alpha, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, float* __restrict__ y) {
   constexpr int NTH = 64 * NWV;
   constexpr int PW = I >= 256 ? 4 : 2;  // words per lane and piece (I = 128: 128-code pieces)
   constexpr int NQ = I / (64 * PW);     // pieces of a row (one load of PW words each)
@@ -781,9 +791,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
   const int local = blockIdx.x >> 3, hp = local % NHB;
   const int tile = xcd_tile(8 * (local / NHB) + (blockIdx.x & 7), *n_tiles);
   if (tile < 0) return;
-  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
-  const int p0 = offsets[e] + m0;
-  const int np = min(TM, offsets[e + 1] - p0);
+  const int2 trec = *reinterpret_cast<const int2*>(tiles + 2 * tile);
+  const int e = trec.x & 0xFFFF, np = trec.x >> 16, p0 = trec.y;
   const bool two = np > 16;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, r16 = lane & 15;
@@ -1035,20 +1044,20 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
     if (fine) {
       constexpr int NS_ = I_ / 128;
       launch("gateup_mfma", nl == 1 ? k_gateup3_mfma<I_, 1> : k_gateup3_mfma<I_, 3>, nt * NS_, 256,
-             0, s, ws.xq, ws.xs, (int)T, d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles,
+             0, s, ws.xq, ws.xs, (int)T, d.H, packed, alpha, ws.sorted_tok, ws.tiles,
              ws.n_tiles, ws.h);
       launch("down_mfma", nl == 1 ? k_down3_mfma<I_, 4, 1> : k_down3_mfma<I_, 4, 3>, nt * nhb, 256,
-             4 * d.H / nhb, s, ws.h, d.H, nhb, packed, alpha, ws.offsets, ws.tiles, ws.n_tiles,
+             4 * d.H / nhb, s, ws.h, d.H, nhb, packed, alpha, ws.tiles, ws.n_tiles,
              (float*)ws.y);
     } else {
       // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
       constexpr int NS_ = I_ >= 512 ? 2 : 1;
       launch("gateup_mfma", k_gateup_mfma<I_, NS_>, nt * NS_, 256, 0, s, ws.xq, ws.xs, (int)T,
-             d.H, packed, alpha, ws.offsets, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
+             d.H, packed, alpha, ws.sorted_tok, ws.tiles, ws.n_tiles, ws.hq, ws.hs, Tk);
       // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
       launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt * nhb, 256,
              4 * d.H / nhb + 4 * 32 * (64 * 2 + 16), s, ws.hq, ws.hs, Tk, d.H, nhb, packed, alpha,
-             ws.offsets, ws.tiles, ws.n_tiles, (uint16_t*)ws.y);
+             ws.tiles, ws.n_tiles, (uint16_t*)ws.y);
     }
   };
   switch (d.I) {

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 }
 
 // Per-expert counts -> offsets, the active-expert list and the grouped-GEMM
-// tile list.  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
+// tile list (per tile: expert | slot count << 16, its first slot).  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
 // the block (NWV waves, 64 NWV >= E) calls it.
 template <int NWV>
 __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
@@ -285,10 +285,10 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
     offsets[e] = off;
     s_off[e] = off;
     if (cnt > 0) active[apos] = e;
-    if (tiles)
+    if (tiles)  // tile record: expert | slots << 16, first slot (kernels need no offsets)
       for (int i = 0; i < nt; ++i) {
-        tiles[2 * (tpos + i)] = e;
-        tiles[2 * (tpos + i) + 1] = i * kTileM;
+        tiles[2 * (tpos + i)] = e | min(kTileM, cnt - i * kTileM) << 16;
+        tiles[2 * (tpos + i) + 1] = off + i * kTileM;
       }
   }
   if (e == 0) {
