@@ -113,60 +113,59 @@ def prefill_ops(kernel, H, k, I, T):
 # kernel has changed since the counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "d1m_down": {"bytes": 4617540, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "9a6b3c6b720affb5"},
-        "d1m_gateup": {"bytes": 6567514, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "9a6b3c6b720affb5"},
-        "d1q_router": {"bytes": 2252513, "sources": ["decode1.hip", "internal.h", "limbs.h", "wave.h"], "digest": "9a6b3c6b720affb5"},
-        "load_token": {"bytes": 15736, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
-        "store_token": {"bytes": 42184, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
+        "d1m_down": {"bytes": 4617500, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
+        "d1m_gateup": {"bytes": 6567455, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
+        "d1q_router": {"bytes": 2252493, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
+        "load_token": {"bytes": 15736, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
+        "store_token": {"bytes": 42183, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 168832278, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "down_mfma": {"bytes": 240446094, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "gateup_mfma": {"bytes": 304683817, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "quant_x": {"bytes": 33769605, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "route_block": {"bytes": 359404, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "route_scan": {"bytes": 149655, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "route_scatter": {"bytes": 1226218, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "route_topk": {"bytes": 4519408, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "router_mfma": {"bytes": 37832015, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "split_router": {"bytes": 4218284, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "combine": {"bytes": 168832253, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "down_mfma": {"bytes": 244677045, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "gateup_mfma": {"bytes": 326173381, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "quant_x": {"bytes": 35949090, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "route_block": {"bytes": 359404, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_scan": {"bytes": 149783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_scatter": {"bytes": 1226218, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_topk": {"bytes": 4519408, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "router_mfma": {"bytes": 37816043, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "split_router": {"bytes": 4218745, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 303372909, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "down_mfma": {"bytes": 414358478, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "gateup_mfma": {"bytes": 269037708, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "quant_x": {"bytes": 25364667, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "route_block": {"bytes": 359404, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "route_scan": {"bytes": 149655, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "route_scatter": {"bytes": 1226217, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "route_topk": {"bytes": 4519402, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "router_mfma": {"bytes": 37831967, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "split_router": {"bytes": 4218358, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "combine": {"bytes": 303367199, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "down_mfma": {"bytes": 413993695, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "gateup_mfma": {"bytes": 268979679, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "quant_x": {"bytes": 25353517, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "route_block": {"bytes": 359403, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_scan": {"bytes": 149783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_scatter": {"bytes": 1226217, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_topk": {"bytes": 4519398, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "router_mfma": {"bytes": 37815963, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "split_router": {"bytes": 4218817, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5267919, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "down_mfma": {"bytes": 38767866, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "gateup_mfma": {"bytes": 68218002, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "quant_x": {"bytes": 1074708, "sources": ["grouped.hip", "internal.h", "limbs.h", "wave.h"], "digest": "59e34b771e735772"},
-        "route_small": {"bytes": 165687, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
-        "router_small": {"bytes": 6490548, "sources": ["internal.h", "limbs.h", "route.hip", "wave.h"], "digest": "55220d1c74b472fd"},
+        "combine": {"bytes": 5271969, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "down_mfma": {"bytes": 38761617, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "gateup_mfma": {"bytes": 68212038, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "887dafff15714346"},
+        "route_small": {"bytes": 158648, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "router_small": {"bytes": 21660821, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
     },
     "hybrid_attn_decode": {
-        "attn_combine": {"bytes": 1123187, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
-        "attn_fill": {"bytes": 169768169, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
-        "attn_global": {"bytes": 269738629, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
-        "attn_window": {"bytes": 1164693, "sources": ["attn.hip", "internal.h", "limbs.h", "wave.h"], "digest": "d2bc24fda3f6dbf5"},
+        "attn_combine": {"bytes": 1123187, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_fill": {"bytes": 169769698, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_global": {"bytes": 269737602, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_window": {"bytes": 1164677, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
     },
     "ternary_convert": {
-        "fill_i32": {"bytes": 2681, "sources": ["internal.h", "limbs.h", "misc.hip", "wave.h"], "digest": "7acfc85b1f3b198b"},
-        "ternarize_g32": {"bytes": 606102832, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
-        "ternarize_w2": {"bytes": 1209100916, "sources": ["convert.hip", "internal.h", "limbs.h", "wave.h"], "digest": "ab5b95fd6cf9d1f8"},
+        "fill_i32": {"bytes": 2681, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
+        "ternarize_g32": {"bytes": 606103108, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
+        "ternarize_w2": {"bytes": 1209096705, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
     },
     "flashhead_decode": {
-        "head_final": {"bytes": 12734, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
-        "head_scores": {"bytes": 19583224, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
-        "head_search": {"bytes": 58841535, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
-        "head_select": {"bytes": 59799, "sources": ["head.hip", "internal.h", "limbs.h", "wave.h"], "digest": "bb6551e67723e09a"},
+        "head_final": {"bytes": 12734, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "head_scores": {"bytes": 19583149, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "head_search": {"bytes": 58841462, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "head_select": {"bytes": 59797, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
     },
 }
 
@@ -814,7 +813,7 @@ def bench_prefill(args, torch, N, S):
                     activations=("int8 (one limb)" if a8
                                  else "fp32 coded in three fp6 digits (14-bit integers)")),
         roofline=roof,
-        step_roofline=dict(algorithmic_int8_ops_per_step=layer_ops,
+        step_roofline=dict(algorithmic_ops_per_step=layer_ops,
                            achieved_tops=layer_ops / (ms_per_step * 1e-3) / 1e12,
                            frac_of_int8_peak=layer_ops / (ms_per_step * 1e-3) / 1e12 /
                            INT8_PEAK_TOPS),
