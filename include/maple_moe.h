@@ -84,11 +84,13 @@ typedef enum maple_status {
 #define MAPLE_RMS_NORM 0x4u       /* the layer sees x / sqrt(mean(x^2) + MAPLE_RMS_EPS) */
 #define MAPLE_RMS_EPS 1e-6f
 #define MAPLE_FORCE_GEMV 0x10u    /* expert FFN on the VALU GEMV path whatever T is */
-#define MAPLE_FORCE_GROUPED 0x20u /* expert FFN on the grouped int8-MFMA path whatever T is */
+#define MAPLE_FORCE_GROUPED 0x20u /* expert FFN on the grouped matrix-core path whatever T is */
 /* Grouped path in its fine form: activations coded in three int8 limbs, h and
- * the per-slot expert outputs kept in fp32 (error near fp32 rounding, about
- * 1.5x the matrix work of the default two-limb form).  Stack calls always use
- * the fine form; for a layer call this flag asks for it. */
+ * the per-slot expert outputs kept in fp32 (error near fp32 rounding).  The
+ * default (fast) form codes x and h into three six-bit digits multiplied with
+ * the ternary codes as fp4 x fp6 (coding error max|v| * 2^-15 per element,
+ * fp16 per-slot outputs; about 2.7e-4 relative on a layer).  Stack calls
+ * always use the fine form; for a layer call this flag asks for it. */
 #define MAPLE_FINE_LIMBS 0x40u
 /* Integer-activation (A8) variant, a different computation from the layer
  * above: x (per token, before the norm's scalar) and h (per routed token and
@@ -104,7 +106,7 @@ typedef enum maple_status {
  * [128, 2048]; 1 <= top_k <= 8; top_k <= n_experts <= 256;
  * 0 <= n_tokens <= MAPLE_MAX_TOKENS.  The fp32 VALU GEMV path (chosen for
  * n_tokens <= 2, for inter > 512, or forced) takes n_tokens <= 64; the grouped
- * int8-MFMA path (chosen otherwise, or forced) takes inter <= 512. */
+ * matrix-core path (chosen otherwise, or forced) takes inter <= 512. */
 #define MAPLE_MAX_TOKENS (1 << 20)
 #define MAPLE_GEMV_MAX_TOKENS 64
 #define MAPLE_GROUPED_MAX_INTER 512

@@ -185,7 +185,7 @@ def test_zero_tokens_is_a_no_op(dec):
     assert torch.all(out == 3.0)
 
 
-# ---- grouped int8-MFMA path -----------------------------------------------------------
+# ---- grouped matrix-core path (fast: fp4 x fp6 digits; fine: three int8 limbs) ----------
 
 GROUPED_FORMS = pytest.mark.parametrize(
     "gflags", [N.MAPLE_FORCE_GROUPED, N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS],
@@ -212,7 +212,7 @@ def test_fine_form_error_near_fp32(dec):
     """Three limbs and fp32 intermediates: the layer error is that of coding
     each activation to 2^-22 of its row's absmax (a few 1e-7 per element, so
     about 1e-6 relative on the output, within an order of the fp32 GEMV path),
-    and at least 100 times below the two-limb form's."""
+    and at least 100 times below the fast (six-bit digit) form's."""
     w, L = dec
     x, _ = layer_tokens_with_gap(w, L, 64, token0=12000)
     ref = L.oracle_layer(S.x_as_f32(w, x).astype(np.float64), w.top_k, w.inter)["out"]
