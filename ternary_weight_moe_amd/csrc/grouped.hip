@@ -694,6 +694,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
     // so the count of loads in flight is the same at every use and the waits
     // stay partial
     const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
+    // the next stage's weights first, into a second register set: a whole
+    // stage of MFMAs hides their latency (loaded after the stage, they were
+    // waited for at the start of the next one)
+    uint4 bqn[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bqn[b] = *bsrc(b, st1);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       v4i wf[4];
@@ -715,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
       }
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bq[b] = *bsrc(b, st1);
+    for (int b = 0; b < 4; ++b) bq[b] = bqn[b];
     store_a((st + 1) & 1);  // stage st1; its buffer was last read in stage st - 1
     fetch_a(st2);
     __syncthreads();
