@@ -971,26 +971,46 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
   const int64_t t = blockIdx.x;
   const int o = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (o >= H) return;
+  // all k (<= 8) rows of the token are loaded before any is added, so a
+  // thread keeps k loads in flight; the sum then runs in j order
+  constexpr int KM = 8;
+  constexpr int NV = std::is_same<YT, float>::value ? 2 : 1;  // 16-byte pieces per row
+  int sp[KM];
+  float g[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k) {
+      sp[j] = slot_pos[t * k + j];
+      g[j] = gate[t * k + j];
+    }
+  uint4 v[KM][NV];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k) {
+      const uint4* src = reinterpret_cast<const uint4*>(y + (int64_t)sp[j] * H + o);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[j][i] = src[i];
+    }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float gj = gate[t * k + j];
-    const YT* src = y + (int64_t)slot_pos[t * k + j] * H + o;
-    if constexpr (std::is_same<YT, float>::value) {
-      const float4 v0 = *reinterpret_cast<const float4*>(src);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-      const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(gj, w[q], acc[q]);
-    } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int j = 0; j < KM; ++j)
+    if (j < k) {
+      if constexpr (NV == 2) {
+        const float w[8] = {__uint_as_float(v[j][0].x), __uint_as_float(v[j][0].y),
+                            __uint_as_float(v[j][0].z), __uint_as_float(v[j][0].w),
+                            __uint_as_float(v[j][1].x), __uint_as_float(v[j][1].y),
+                            __uint_as_float(v[j][1].z), __uint_as_float(v[j][1].w)};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(gj, f16_lo(w[q]), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(gj, f16_hi(w[q]), acc[2 * q + 1]);
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(g[j], w[q], acc[q]);
+      } else {
+        const uint32_t w[4] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(g[j], f16_lo(w[q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(g[j], f16_hi(w[q]), acc[2 * q + 1]);
+        }
       }
     }
-  }
   const int64_t off = t * H + o;
   float4 a0 = make_float4(acc[0], acc[1], acc[2], acc[3]);
   float4 a1 = make_float4(acc[4], acc[5], acc[6], acc[7]);
