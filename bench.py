@@ -113,59 +113,59 @@ def prefill_ops(kernel, H, k, I, T):
 # kernel has changed since the counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "d1m_down": {"bytes": 4617543, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
-        "d1m_gateup": {"bytes": 6567514, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
-        "d1q_router": {"bytes": 2252513, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
+        "d1m_down": {"bytes": 4617509, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
+        "d1m_gateup": {"bytes": 6567467, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
+        "d1q_router": {"bytes": 2252498, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
         "load_token": {"bytes": 15736, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
-        "store_token": {"bytes": 42184, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
+        "store_token": {"bytes": 42183, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 168832125, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "down_mfma": {"bytes": 244593215, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "gateup_mfma": {"bytes": 325905900, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "quant_x": {"bytes": 35929250, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
+        "combine": {"bytes": 168855800, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "down_mfma": {"bytes": 244603755, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "gateup_mfma": {"bytes": 326146377, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "quant_x": {"bytes": 35918229, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
         "route_block": {"bytes": 359404, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
         "route_scan": {"bytes": 149783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_scatter": {"bytes": 1226218, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_topk": {"bytes": 4519408, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "router_mfma": {"bytes": 37816043, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "split_router": {"bytes": 4218822, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_scatter": {"bytes": 1226217, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_topk": {"bytes": 4519400, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "router_mfma": {"bytes": 37815979, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "split_router": {"bytes": 4218639, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 303397305, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "down_mfma": {"bytes": 414325927, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "gateup_mfma": {"bytes": 268729034, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "quant_x": {"bytes": 25353335, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
+        "combine": {"bytes": 303057223, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "down_mfma": {"bytes": 414022562, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "gateup_mfma": {"bytes": 268735714, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "quant_x": {"bytes": 25353354, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
         "route_block": {"bytes": 359404, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
         "route_scan": {"bytes": 149783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_scatter": {"bytes": 1226218, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_topk": {"bytes": 4519410, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "router_mfma": {"bytes": 37816059, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "split_router": {"bytes": 4218848, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_scatter": {"bytes": 1226217, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "route_topk": {"bytes": 4519402, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "router_mfma": {"bytes": 37815995, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "split_router": {"bytes": 4218716, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5284265, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "down_mfma": {"bytes": 38764859, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
-        "gateup_mfma": {"bytes": 68222894, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "cb1e0a4f39eb9d56"},
+        "combine": {"bytes": 5304724, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "down_mfma": {"bytes": 38764748, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
+        "gateup_mfma": {"bytes": 68222264, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
         "route_small": {"bytes": 158648, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "router_small": {"bytes": 21660860, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "router_small": {"bytes": 21660783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
     },
     "hybrid_attn_decode": {
-        "attn_combine": {"bytes": 1123188, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-        "attn_fill": {"bytes": 169783803, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-        "attn_global": {"bytes": 269739458, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-        "attn_window": {"bytes": 1164680, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_combine": {"bytes": 1123183, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_fill": {"bytes": 169793789, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_global": {"bytes": 269737003, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
+        "attn_window": {"bytes": 1164689, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
     },
     "ternary_convert": {
         "fill_i32": {"bytes": 2681, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
-        "ternarize_g32": {"bytes": 606103908, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
-        "ternarize_w2": {"bytes": 1209101147, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
+        "ternarize_g32": {"bytes": 606102532, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
+        "ternarize_w2": {"bytes": 1209101837, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
     },
     "flashhead_decode": {
         "head_final": {"bytes": 12734, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
-        "head_scores": {"bytes": 19583205, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
-        "head_search": {"bytes": 58841457, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
-        "head_select": {"bytes": 59797, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "head_scores": {"bytes": 19583241, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "head_search": {"bytes": 58841660, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "head_select": {"bytes": 59798, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
     },
 }
 
