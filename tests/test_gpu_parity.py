@@ -143,17 +143,20 @@ def test_fp32_input_and_token_independence(dec):
     assert_close(one, full[4:5], "token alone vs in batch")
 
 
-def test_edge_all_experts_and_k1():
+@pytest.mark.parametrize("flags", [0, N.MAPLE_FORCE_GROUPED,
+                                   N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS],
+                         ids=["auto", "grouped", "grouped_fine"])
+def test_edge_all_experts_and_k1(flags):
     # E == k: every token selects every expert
     w = workload("tiny_layer", n_experts=4, top_k=4, seed=1101, n_tokens=7)
     L = Layer(w, 0)
     x, _ = layer_tokens_with_gap(w, L, 7)
-    check_layer(w, L, x, what="E == k")
+    check_layer(w, L, x, flags=flags, what="E == k")
     # k = 1
     w1 = workload("tiny_layer", top_k=1, seed=1102, n_tokens=6)
     L1 = Layer(w1, 0)
     x1, _ = layer_tokens_with_gap(w1, L1, 6)
-    check_layer(w1, L1, x1, what="k = 1")
+    check_layer(w1, L1, x1, flags=flags, what="k = 1")
 
 
 @pytest.mark.parametrize("flags", [N.MAPLE_FORCE_GEMV, N.MAPLE_FORCE_GROUPED,
