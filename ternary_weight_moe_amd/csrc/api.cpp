@@ -59,7 +59,8 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->tiles = (int32_t*)take(sizeof(int32_t) * 2 * (size_t)max_tiles(d, T));
   ws->h = (float*)take(sizeof(float) * Tk * d.I);
   ws->xq = (int8_t*)take((size_t)T * 4 * d.H);
-  ws->part = (int32_t*)take(sizeof(int32_t) * 4 * d.E);
+  ws->rpart = (float*)take(sizeof(float) * maple::kDecPartStride * (d.H / 64));
+  ws->x2 = (float*)take(sizeof(float) * d.H);
   ws->xs = (float*)take(sizeof(float) * 5 * T);
   ws->hq = (int8_t*)take((size_t)Tk * 9 * d.I / 4);
   ws->hs = (float*)take(sizeof(float) * 4 * Tk);
@@ -223,11 +224,34 @@ int device_ready() {
   return MAPLE_OK;
 }
 
+// Copies the routing of the layer just enqueued into the caller's debug buffers.
+int copy_debug(const Dims& d, int64_t T, const Workspace& ws, const maple_moe_debug* dbg,
+               hipStream_t s) {
+  if (!dbg) return MAPLE_OK;
+  const int64_t Tk = T * d.k;
+  struct {
+    void* dst;
+    const void* src;
+    size_t n;
+  } cp[] = {{dbg->idx, ws.idx, sizeof(int32_t) * Tk},
+            {dbg->gate, ws.gate, sizeof(float) * Tk},
+            {dbg->logits, ws.logits, sizeof(float) * T * d.E},
+            {dbg->offsets, ws.offsets, sizeof(int32_t) * (d.E + 1)},
+            {dbg->sorted_token, ws.sorted_tok, sizeof(int32_t) * Tk},
+            {dbg->slot_pos, ws.slot_pos, sizeof(int32_t) * Tk}};
+  for (auto& c : cp)
+    if (c.dst) {
+      const hipError_t e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "debug copy");
+    }
+  return MAPLE_OK;
+}
+
 // One layer on the device: router, routing, expert FFN (+ combine).
 int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
               const float* bias, const uint8_t* packed, const float* alpha, float* out,
               const float* resid, float* delta, const Workspace& ws, const maple_moe_debug* dbg,
-              const float* next_wr, hipStream_t s) {
+              hipStream_t s) {
   const bool gemv = use_gemv(d, T);
   // stack calls take the fine grouped form: their routing sits downstream of
   // every earlier layer's error; MAPLE_ACT_INT8 asks for one-limb activations
@@ -235,8 +259,15 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
                  : (d.flags & (kStackCall | MAPLE_FINE_LIMBS)) ? 3 : 2;
   hipError_t e = hipSuccess;
   if (gemv && T == 1) {  // one token: router, top-k + gate/up, down + combine
-    e = maple::launch_decode1(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid, delta,
-                              next_wr, s);
+    if (maple::decode1_matrix_cores(d)) {
+      e = maple::launch_dec_router(d, x, x_bf16, Wr, ws, s);
+      if (e == hipSuccess)
+        e = maple::launch_dec_layer(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid,
+                                    delta, nullptr, s);
+    } else {
+      e = maple::launch_decode1_valu(d, x, x_bf16, Wr, bias, packed, alpha, ws, out, resid,
+                                     delta, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   } else {
     // limbs, scales and 1/rms of x for the grouped GEMMs (and the large-T
@@ -258,25 +289,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
       e = maple::launch_grouped_ffn(d, T, nl, packed, alpha, ws, out, resid, delta, s);
     if (e != hipSuccess) return hip_fail(e, "expert FFN launch");
   }
-  if (dbg) {
-    const int64_t Tk = T * d.k;
-    struct {
-      void* dst;
-      const void* src;
-      size_t n;
-    } cp[] = {{dbg->idx, ws.idx, sizeof(int32_t) * Tk},
-              {dbg->gate, ws.gate, sizeof(float) * Tk},
-              {dbg->logits, ws.logits, sizeof(float) * T * d.E},
-              {dbg->offsets, ws.offsets, sizeof(int32_t) * (d.E + 1)},
-              {dbg->sorted_token, ws.sorted_tok, sizeof(int32_t) * Tk},
-              {dbg->slot_pos, ws.slot_pos, sizeof(int32_t) * Tk}};
-    for (auto& c : cp)
-      if (c.dst) {
-        e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s);
-        if (e != hipSuccess) return hip_fail(e, "debug copy");
-      }
-  }
-  return MAPLE_OK;
+  return copy_debug(d, T, ws, dbg, s);
 }
 
 maple_moe_debug layer_dbg(const maple_moe_debug* dbg, int l, int64_t T, const Dims& d) {
@@ -478,7 +491,7 @@ int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const 
   if ((rc = device_ready())) return rc;
   maple::carve(d, n_tokens, static_cast<char*>(workspace), &ws);
   return run_layer(d, n_tokens, x, (d.flags & MAPLE_X_BF16) != 0, router_w, router_bias,
-                   packed_w, alpha, out, nullptr, nullptr, ws, dbg, nullptr, (hipStream_t)stream);
+                   packed_w, alpha, out, nullptr, nullptr, ws, dbg, (hipStream_t)stream);
 }
 
 static int enqueue_stack(const Dims& d, int32_t n_layers, int64_t T, float* x,
@@ -487,12 +500,33 @@ static int enqueue_stack(const Dims& d, int32_t n_layers, int64_t T, float* x,
                          void* workspace, const maple_moe_debug* dbg, hipStream_t s) {
   Workspace ws;
   maple::carve(d, T, static_cast<char*>(workspace), &ws);
+  if (T == 1 && use_gemv(d, T) && maple::decode1_matrix_cores(d)) {
+    // one token on matrix cores: two kernels per layer, each layer's router
+    // dots formed by the previous layer's down kernel; the residual stream
+    // alternates between x and ws.x2 (a down kernel cannot update in place)
+    float* buf[2] = {x, ws.x2};
+    hipError_t e = maple::launch_dec_router(d, x, false, router_w[0], ws, s);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    for (int l = 0; l < n_layers; ++l) {
+      const maple_moe_debug ld = layer_dbg(dbg, l, T, d);
+      const float* next_wr = l + 1 < n_layers ? router_w[l + 1] : nullptr;
+      e = maple::launch_dec_layer(d, buf[l & 1], false, router_w[l],
+                                  router_bias ? router_bias[l] : nullptr, packed_w[l], alpha[l],
+                                  ws, buf[(l + 1) & 1], buf[l & 1], ld.delta, next_wr, s);
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+      const int rc = copy_debug(d, T, ws, dbg ? &ld : nullptr, s);
+      if (rc) return rc;
+    }
+    if (n_layers & 1) {
+      e = maple::launch_copy_f32(ws.x2, x, d.H, s);
+      if (e != hipSuccess) return hip_fail(e, "copy launch");
+    }
+    return MAPLE_OK;
+  }
   for (int l = 0; l < n_layers; ++l) {
     const maple_moe_debug ld = layer_dbg(dbg, l, T, d);
-    const float* next_wr = l + 1 < n_layers ? router_w[l + 1] : nullptr;
     const int rc = run_layer(d, T, x, false, router_w[l], router_bias ? router_bias[l] : nullptr,
-                             packed_w[l], alpha[l], x, x, ld.delta, ws, dbg ? &ld : nullptr,
-                             next_wr, s);
+                             packed_w[l], alpha[l], x, x, ld.delta, ws, dbg ? &ld : nullptr, s);
     if (rc) return rc;
   }
   return MAPLE_OK;

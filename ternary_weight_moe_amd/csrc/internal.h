@@ -12,6 +12,9 @@ namespace maple {
 // Slots per M tile of the grouped GEMMs (granularity of the tile list).
 constexpr int kTileM = 32;
 
+// Floats per 64-row group in the one-token path's partial router slab.
+constexpr int kDecPartStride = 288;
+
 // Workspace carve-up for one layer call with T tokens.  Every region is
 // 256-byte aligned.  The same carve serves the stack (layers run one after
 // another and reuse it).
@@ -32,7 +35,9 @@ struct Workspace {
   float* h;             // [T*k, I]  fp32 h (GEMV path, fine grouped path)
   int8_t* xq;           // [T, 4, H] coded x: three int8 limbs (fine grouped form,
                         //           one-token path), one (A8), or 9H/4 digit bytes (fast form)
-  int32_t* part;        // [E, 4]    per-router-block partial limb sums (one-token path)
+  float* rpart;         // [H/64, kDecPartStride] partial router dots over 64-row groups of x,
+                        //           and each group's x statistics (one-token path)
+  float* x2;            // [H]       second residual buffer (one-token stack: layers ping-pong)
   float* xs;            // [5T]      scale of x's limbs | limb row sums (int bits, up to
                         //           three planes) | 1/rms(x) at plane 4
   int8_t* hq;           // [T*k, 9I/4] h in the digit layout (fast form)
@@ -84,11 +89,23 @@ hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          float* xs, hipStream_t s);
 hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
                         hipStream_t s);
-// next_wr: the next layer's router (only read to warm the caches), or null
-hipError_t launch_decode1(const Dims& d, const void* x, bool x_bf16, const float* Wr,
-                          const float* bias, const uint8_t* packed, const float* alpha,
-                          const Workspace& ws, float* out, const float* resid, float* delta,
-                          const float* next_wr, hipStream_t s);
+// One token on matrix cores (decode1_matrix_cores(d)): launch_dec_router
+// leaves the partial router dots of x in ws.rpart; launch_dec_layer then runs
+// one layer (router Wr) on x (whose partial dots are in ws.rpart) into out (= resid +
+// MoE(x) if resid, else MoE(x); out must not alias resid or x) and, if
+// next_wr is not null, leaves the partial dots of out for that router in
+// ws.rpart.  Other shapes: launch_decode1_valu (router, gate/up, down).
+bool decode1_matrix_cores(const Dims& d);
+hipError_t launch_dec_router(const Dims& d, const void* x, bool x_bf16, const float* Wr,
+                             const Workspace& ws, hipStream_t s);
+hipError_t launch_dec_layer(const Dims& d, const void* x, bool x_bf16, const float* Wr,
+                            const float* bias, const uint8_t* packed, const float* alpha,
+                            const Workspace& ws, float* out, const float* resid, float* delta,
+                            const float* next_wr, hipStream_t s);
+hipError_t launch_decode1_valu(const Dims& d, const void* x, bool x_bf16, const float* Wr,
+                               const float* bias, const uint8_t* packed, const float* alpha,
+                               const Workspace& ws, float* out, const float* resid, float* delta,
+                               hipStream_t s);
 // nl: int8 limbs per activation (2: fast form, 3: fine form, 1: A8); pairs
 // with launch_grouped_ffn's nl
 hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, int nl,
@@ -107,6 +124,7 @@ hipError_t launch_load_token(const void* staged, bool bf16, int n_staged, int64_
 hipError_t launch_store_token(const float* x_work, int n_staged, int64_t T, int H,
                               const int32_t* counter, float* out_all, hipStream_t s);
 hipError_t launch_set_step(int32_t* counter, int32_t step, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 // ---- output head (FlashHead) ----

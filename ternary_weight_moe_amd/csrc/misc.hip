@@ -72,6 +72,12 @@ __global__ __launch_bounds__(256) void k_store_token(const float* __restrict__ x
     out_all[slot * n + i] = x[i];
 }
 
+__global__ __launch_bounds__(256) void k_copy_f32(const float* __restrict__ src,
+                                                  float* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
 __global__ void k_set_step(int32_t* counter, int32_t step) {
   counter[0] = step;
   counter[1] = step;
@@ -108,6 +114,14 @@ hipError_t launch_store_token(const float* x_work, int n_staged, int64_t T, int 
   const int64_t n = T * H;
   const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 1024);
   k_store_token<<<blocks, 256, 0, s>>>(x_work, n_staged, n, counter, out_all);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  if (n > 0) {
+    const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 1024);
+    launch("copy", k_copy_f32, blocks, 256, 0, s, src, dst, n);
+  }
   return hipGetLastError();
 }
 

@@ -329,6 +329,181 @@ __device__ __forceinline__ void wave_topk_rounds(const float* __restrict__ lrow,
   *out_sum = s;
 }
 
+// One wave's top-k of E <= 256 logits held in registers (lane holds experts
+// e = lane + 64 m, m < 4; entries with e >= E ignored; NaN ranks as -inf), in
+// the order (logit desc, index asc), plus the softmax max and normaliser over
+// all E.  Each lane first sorts its 4 keys; a round then takes the wave max of
+// the lane heads with DPP and permlane swaps, so the value stays in VGPRs
+// (no readlane / scalar round trip on the common path), finds its holder with
+// one ballot and advances that lane's head.  Ties across lanes (equal logits)
+// take a second reduction for the lowest expert index.  Lane j < k receives
+// selection j in *sel and its logit in *val.  k <= 64.
+__device__ __forceinline__ void wave_topk_select(const float (&l)[4], int E, int k, int lane,
+                                                 int* sel, float* val, float* out_max,
+                                                 float* out_sum) {
+  int key[4], em[4];
+  float mxl = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    key[m] = e < E ? float_key(l[m]) : kKeyTaken;
+    em[m] = e;
+    mxl = fmaxf(mxl, (e < E && l[m] == l[m]) ? l[m] : -INFINITY);
+  }
+  const float mx = group_reduce<64, OpMax>(mxl);
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (em[m] < E) s += expf(key_float(key[m]) - mx);
+  s = group_reduce<64, OpSum>(s);
+  auto cs = [&](int a, int b) {
+    const bool sw = key[b] > key[a] || (key[b] == key[a] && em[b] < em[a]);
+    const int ka = key[a], ea = em[a];
+    key[a] = sw ? key[b] : key[a];
+    em[a] = sw ? em[b] : em[a];
+    key[b] = sw ? ka : key[b];
+    em[b] = sw ? ea : em[b];
+  };
+  cs(0, 1);
+  cs(2, 3);
+  cs(0, 2);
+  cs(1, 3);
+  cs(1, 2);
+  int hk = key[0], he = em[0], head = 0;
+  int my_sel = 0, my_key = kKeyTaken;
+  for (int j = 0; j < k; ++j) {
+    const int best = group_reduce_i<64, OpMax>(hk);
+    const unsigned long long b = __ballot(hk == best);
+    int e;
+    if (__popcll(b) == 1)
+      e = __builtin_amdgcn_readlane(he, (int)__builtin_ctzll(b));
+    else  // equal logits in several lanes: the lowest expert index wins
+      e = group_reduce_i<64, OpMin>(hk == best ? he : 0x7fffffff);
+    if (he == e) {
+      ++head;
+      hk = head == 1 ? key[1] : head == 2 ? key[2] : head == 3 ? key[3] : kKeyTaken;
+      he = head == 1 ? em[1] : head == 2 ? em[2] : head == 3 ? em[3] : 0x7fffffff;
+    }
+    if (lane == j) {
+      my_sel = e;
+      my_key = best;
+    }
+  }
+  *sel = my_sel;
+  *val = key_float(my_key);
+  *out_max = mx;
+  *out_sum = s;
+}
+
+// Orders a wave's own LDS writes before its later LDS reads (no block barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kTopkCands = 32;  // candidate slots of the threshold selection (LDS: 8 bytes each)
+
+// Threshold selection of the k first logits in the order (logit desc, index
+// asc), given their max and mean (all E logits finite).  A threshold
+// t = max - f (max - mean) keeps the logits >= t as candidates (f starts at f0
+// and is widened or narrowed until k <= candidates <= kTopkCands, at most 5
+// tries); the candidates are packed as (key << 8 | 255 - e) into s_cand in
+// expert order, and each candidate's rank is the number of candidates with a
+// larger packed value, i.e. its position in the order.  Writes s_sel[rank],
+// s_val[rank] for rank < k from the lanes of this wave.  Returns false, with
+// nothing written, if no threshold brackets k (many equal logits at the top,
+// or a spread that is not finite); f0 changes only the speed.  Lane holds
+// experts e = lane + 64 m (m < 4) as order keys (float_key; kKeyTaken for
+// e >= E).  k <= 8; s_cand: kTopkCands long longs of LDS.
+__device__ __forceinline__ bool wave_topk_thresh_core(const int (&key)[4], int k, float f0,
+                                                      float mx, float mean, int lane,
+                                                      long long* s_cand, int* s_sel,
+                                                      float* s_val) {
+  const float spread = mx - mean;
+  if (!(spread >= 0.f && spread < INFINITY)) return false;
+  float f = f0;
+  int tk = 0, cnt = 0;
+  bool ok = false;
+  for (int it = 0; it < 5; ++it) {
+    tk = float_key(mx - f * spread);
+    cnt = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) cnt += __popcll(__ballot(key[m] >= tk));
+    if (cnt >= k && cnt <= kTopkCands) {
+      ok = true;
+      break;
+    }
+    f = cnt < k ? f * 1.6f : f * 0.6f;
+  }
+  if (!ok) return false;
+  int base = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const unsigned long long msk = __ballot(key[m] >= tk);
+    if (key[m] >= tk) {
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                 (unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+      s_cand[pos] = ((long long)key[m] << 8) | (255 - (lane + 64 * m));
+    }
+    base += __popcll(msk);
+  }
+  if (lane >= cnt && lane < kTopkCands) s_cand[lane] = (long long)kKeyTaken << 8;  // below all
+  wave_lds_sync();
+  if (lane < cnt) {
+    const long long me = s_cand[lane];
+    int r[4] = {0, 0, 0, 0};  // four partial counts: short dependency chains
+#pragma unroll
+    for (int q = 0; q < kTopkCands; ++q) r[q & 3] += s_cand[q] > me ? 1 : 0;
+    const int rank = (r[0] + r[1]) + (r[2] + r[3]);
+    if (rank < k) {
+      s_sel[rank] = 255 - (int)(me & 255);
+      s_val[rank] = key_float((int)(me >> 8));
+    }
+  }
+  return true;
+}
+
+// The selection of wave_topk_select with fewer dependent wave-wide steps
+// (wave_topk_thresh_core), computing the max, mean and softmax normaliser of
+// the E logits itself; non-finite logits take wave_topk_select.  Writes
+// s_sel[j], s_val[j] (j < k) from the lanes of this wave.
+__device__ __forceinline__ void wave_topk_thresh(const float (&l)[4], int E, int k, float f0,
+                                                 int lane, long long* s_cand, int* s_sel,
+                                                 float* s_val, float* out_max, float* out_sum) {
+  int key[4];
+  float mxl = -INFINITY, sl = 0.f;
+  // sums relative to lane 0's first logit: a large common offset cancels
+  const float ref = __builtin_amdgcn_readfirstlane(l[0]);
+  int nfin = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    key[m] = e < E ? float_key(l[m]) : kKeyTaken;
+    const bool fin = e < E && l[m] - l[m] == 0.f;  // finite
+    mxl = fmaxf(mxl, (e < E && l[m] == l[m]) ? l[m] : -INFINITY);
+    sl += fin ? l[m] - ref : 0.f;
+    nfin += __popcll(__ballot(fin));
+  }
+  const float mx = group_reduce<64, OpMax>(mxl);
+  const float mean = ref + group_reduce<64, OpSum>(sl) / (float)max(nfin, 1);
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (lane + 64 * m < E) s += expf(key_float(key[m]) - mx);
+  s = group_reduce<64, OpSum>(s);
+  *out_max = mx;
+  *out_sum = s;
+  if (nfin == E && wave_topk_thresh_core(key, k, f0, mx, mean, lane, s_cand, s_sel, s_val)) return;
+  int sel;
+  float val, m2, s2;
+  wave_topk_select(l, E, k, lane, &sel, &val, &m2, &s2);
+  if (lane < k) {
+    s_sel[lane] = sel;
+    s_val[lane] = val;
+  }
+}
+
 // The same rounds on logits already in registers (lane holds experts lane +
 // 64 m, m < 4; entries with e >= E ignored), for NT tokens at once: the rounds
 // of the NT tokens are independent and run in lockstep, so their reduction
