@@ -19,9 +19,14 @@ layer of BF16 latent weights into ternary codes and alphas.
 Prints one JSON line.  Inputs are synthetic and seeded; weights are generated
 in host memory, packed on the device and resident in HBM before the timed
 region starts.  After the timed region, a profiled pass of the same work
-(HIP events around each kernel, recorded by the library on the stream the
-kernel runs on) gives the dominant kernel's average duration for the
-roofline entry.
+gives the dominant kernel's average duration for the roofline entry: for the
+decode stack, replays of a second graph of the same step whose one-token
+kernels stamp the GPU's real-time counter at every block's entry and exit
+(graph mode, no eager launches); elsewhere HIP events around each kernel,
+recorded by the library on the stream the kernel runs on.  The default
+decode_stack line also carries a ``prefill_4096`` object (the 4096-token
+layer, timed the same way as ``--workload prefill_4096``) unless
+``--no-prefill`` is given.
 """
 from __future__ import annotations
 
@@ -62,7 +67,9 @@ def decode_bytes(kernel, H, E, k, I, T=1):
     down = ne * (H * I // 4 + 4 * H) + 4 * ne * I + 2 * 4 * T * H
     return {
         "d1_router": router, "d1_gateup": gateup + 4 * E, "d1_down": down,
-        "d1m_gateup": gateup + 4 * E, "d1m_down": down, "d1q_router": router + 3 * H,
+        # two-kernel one-token path: the down kernel also reads the next
+        # layer's router (its partial dots); the first layer's come from dec_router
+        "dec_router": router, "dec_gateup": gateup + 4 * E, "dec_down": down + 4 * E * H,
         "router_gemv": 4 * E * H + 4 * T * H + 4 * T * E,
         "route_small": 4 * T * E + 4 * (3 * ne + 2 * E + 1),
         "gateup_gemv": ne * (2 * I * H // 4 + 4 * 2 * I) + 4 * T * H + 4 * ne * I,
@@ -295,6 +302,31 @@ def profile_kernels(N, fn, steps):
     return {k: (n, ms / n) for k, (n, ms) in summ.items()}
 
 
+def graph_stamp_profile(N, torch, make_graph, replays, burst=4):
+    """Per-kernel spans inside graph replays: a graph captured while the
+    library's device-stamp mode is on; after every burst of back-to-back
+    replays the stamps of the last one are read.  Returns ({kernel:
+    (launches per replay, avg us per launch)}, ms per stamped replay)."""
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    N.maple_profile_enable(2)
+    g = make_graph()
+    try:
+        ms_stamped = timed(torch, lambda: g.launch(stream), 64, 8)
+        acc = {}
+        for _ in range(replays):
+            for _ in range(burst):
+                g.launch(stream)
+            for kn, (n, ms) in N.maple_profile_summary().items():
+                a = acc.setdefault(kn, [0, 0.0])
+                a[0] = n
+                a[1] += 1000.0 * ms / n
+    finally:
+        N.maple_profile_enable(0)
+        g.destroy()
+    return {kn: (n, us / replays) for kn, (n, us) in acc.items()}, ms_stamped
+
+
 def copy_probe(torch, mib):
     """A plain device-to-device copy of known size, launched a few times, so that
     hardware counter runs over this script can scale FETCH_SIZE / WRITE_SIZE."""
@@ -337,33 +369,33 @@ def bench_decode(args, torch, N, S):
     out_all = torch.zeros(n_staged, 1, H, dtype=torch.float32, device="cuda")
     lists = ([l["Wr"] for l in layers], None, [l["packed"] for l in layers],
              [l["alpha"] for l in layers])
-    g = N.MapleGraph(d, 1, staged, n_staged, x_work, out_all, *lists, ws)
+    def make_graph():
+        return N.MapleGraph(d, 1, staged, n_staged, x_work, out_all, *lists, ws)
+    g = make_graph()
     stream = torch.cuda.current_stream()
     ms_per_step = timed(torch, lambda: g.launch(stream), args.steps, args.warmup)
     assert torch.isfinite(out_all).all().item(), "non-finite decode output"
     g.destroy()
     log(f"decode: {1000.0 / ms_per_step:.1f} tok/s, {ms_per_step * 1000:.1f} us/step")
 
-    # profiled eager pass over the same work: per-kernel average durations
-    dx = N.make_dims(H, E, k, I, 0)
-    xe = torch.empty(1, H, dtype=torch.float32, device="cuda")
-    tok = [0]
-
-    def eager_step():
-        xe.copy_(staged[tok[0] % n_staged].float())
-        N.maple_moe_stack_forward(dx, 1, xe, *lists, ws)
-        tok[0] += 1
-    prof = profile_kernels(N, eager_step, min(args.steps, 64))
-    per_kernel = {kn: dict(launches=n, avg_us=1000 * avg,
-                           bytes=decode_bytes(kn, H, E, k, I))
-                  for kn, (n, avg) in prof.items()}
-    known = [kn for kn in prof if decode_bytes(kn, H, E, k, I) is not None]
-    dom = max(known, key=lambda kn: prof[kn][0] * prof[kn][1])
+    # graph-mode spans of the one-token kernels (a stamped graph of the same step)
+    prof, ms_stamped = graph_stamp_profile(N, torch, make_graph, min(args.steps, 64))
+    per_kernel = {}
+    for kn, (n, avg_us) in prof.items():
+        b = decode_bytes(kn, H, E, k, I)
+        per_kernel[kn] = dict(launches_per_step=n, avg_us=avg_us, total_us_per_step=n * avg_us,
+                              bytes=b, achieved_gbs=b / (avg_us * 1e-6) / 1e9 if b else None)
+    span_sum_us = sum(v["total_us_per_step"] for v in per_kernel.values())
+    log(f"graph-mode spans: {', '.join(f'{kn} {v[1]:.2f} us' for kn, v in prof.items())}; "
+        f"sum {span_sum_us:.1f} of {ms_per_step * 1000:.1f} us per step")
+    dom = max(per_kernel, key=lambda kn: per_kernel[kn]["total_us_per_step"])
     dom_bytes = decode_bytes(dom, H, E, k, I)
-    dom_avg_s = prof[dom][1] * 1e-3
+    dom_avg_s = prof[dom][1] * 1e-6
     achieved = dom_bytes / dom_avg_s / 1e9
     bytes_tok = L * decode_bytes_per_token_layer(H, E, k, I)
     step_gbs = bytes_tok / (ms_per_step * 1e-3) / 1e9
+    # the graph also holds the two staging kernels (load the token, store the output)
+    n_kernels = sum(v["launches_per_step"] for v in per_kernel.values()) + 2
     return dict(
         metric=METRIC, value=1000.0 / ms_per_step, unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
@@ -373,9 +405,14 @@ def bench_decode(args, torch, N, S):
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("decode_stack", dom),
                       kernel=dom,
-                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=dom_avg_s * 1e6),
+                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=dom_avg_s * 1e6,
+                      timing="graph replays: first block entry to last block exit, "
+                             "device real-time counter"),
         step_roofline=dict(algorithmic_bytes_per_step=bytes_tok, achieved_gbs=step_gbs,
                            frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
+        kernels_per_token=n_kernels,
+        graph_kernel_span_sum_us=span_sum_us,
+        stamped_graph_ms_per_step=ms_stamped,
         kernels=per_kernel,
     ), w
 
@@ -767,7 +804,8 @@ def cpu_baseline_head(ctx, budget_s):
 
 def bench_prefill(args, torch, N, S):
     a8 = args.workload.endswith("_a8")
-    w = S.WORKLOADS[args.workload[:-3] if a8 else args.workload]
+    wname = args.workload[:-3] if a8 else args.workload
+    w = S.WORKLOADS[wname]
     H, E, k, I, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_tokens
     layer = build_layers(w, torch, N, S)[0]
     xs = S.gen_x(w, T)
@@ -788,6 +826,15 @@ def bench_prefill(args, torch, N, S):
     dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
     ops = prefill_ops(dom, H, k, I, T)
     dom_avg_s = prof[dom][1] * 1e-3
+    # issued MFMA work: every expert's slots padded to whole 32-slot tiles, and
+    # each product issued once per digit plane (three in the fast form, one
+    # limb in A8); the routing is the same call's, copied out
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    N.maple_moe_layer_forward(d, T, x, layer["Wr"], layer["bias"], layer["packed"],
+                              layer["alpha"], out, ws, N.make_debug(idx=idx))
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=E)
+    padded = int((-(-counts // 32) * 32).sum())
+    issued_ratio = (1 if a8 else 3) * padded / (T * k)
     # the A8 variant runs int8 MFMAs; the default (fast) form fp4 x fp6 ones,
     # priced against that instruction's own peak
     peak, unit = (INT8_PEAK_TOPS, "TOP/s") if a8 else (FP6_PEAK_TFLOPS, "TFLOP/s")
@@ -797,6 +844,9 @@ def bench_prefill(args, torch, N, S):
                     traffic=traffic_for(args.workload, dom),
                     kernel=dom, algorithmic_ops_per_launch=ops,
                     frac_of_int8_peak=ops / dom_avg_s / 1e12 / INT8_PEAK_TOPS,
+                    issued_ops_per_launch=ops * issued_ratio,
+                    issued_to_algorithmic=issued_ratio,
+                    issued_frac=ops * issued_ratio / dom_avg_s / 1e12 / peak,
                     avg_launch_us=dom_avg_s * 1e6)
     else:
         roof = dict(bound="mfma", achieved=None, peak=peak, unit=unit, frac=None,
@@ -809,7 +859,7 @@ def bench_prefill(args, torch, N, S):
         dtype=("int8 MFMA (int8 activations) + f32" if a8
                else "fp4 x fp6 MFMA (three six-bit digits) + f32"),
         config=dict(workload=args.workload, hidden=H, experts=E, top_k=k, inter=I, tokens=T,
-                    layers=1, step="one layer call",
+                    layers=1, step="one layer call", padded_slots=padded,
                     activations=("int8 (one limb)" if a8
                                  else "fp32 coded in three fp6 digits (14-bit integers)")),
         roofline=roof,
@@ -832,6 +882,8 @@ def main():
                              "ternary_convert"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode_stack: leave out the prefill_4096 object")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -869,6 +921,19 @@ def main():
         else:
             res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_baseline_seconds,
                                                        a8=args.workload.endswith("_a8"))
+    if args.workload == "decode_stack" and not args.no_prefill:
+        # the third part of the metric: the 4096-token layer, timed like
+        # --workload prefill_4096 (20 steps after 3 warm-up steps)
+        torch.cuda.empty_cache()
+        pargs = argparse.Namespace(**vars(args))
+        pargs.workload, pargs.steps, pargs.warmup = "prefill_4096", 20, 3
+        pres, pw = bench_prefill(pargs, torch, N, S)
+        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "config", "roofline",
+                "step_roofline", "kernels")
+        res["prefill_4096"] = {kk: pres[kk] for kk in keep}
+        if not args.no_cpu_baseline:
+            res["prefill_4096"]["cpu_baseline"] = cpu_baseline_prefill(
+                pw, args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -89,8 +89,13 @@ typedef enum maple_status {
  * the per-slot expert outputs kept in fp32 (error near fp32 rounding).  The
  * default (fast) form codes x and h into three six-bit digits multiplied with
  * the ternary codes as fp4 x fp6 (coding error max|v| * 2^-15 per element,
- * fp16 per-slot outputs; about 2.7e-4 relative on a layer).  Stack calls
- * always use the fine form; for a layer call this flag asks for it. */
+ * fp16 per-slot outputs; about 2.7e-4 relative on a layer).  The fp16
+ * outputs are stored relative to each slot's own h scale (times 2^-8), so
+ * the input's magnitude does not bound them; they stay finite while every
+ * down-projection alpha has |alpha| <= 1023 / inter (2.0 at inter 512), which
+ * ternary scales (a mean of |latent weight|) meet by far.  Beyond that the
+ * fast form's outputs can be infinite: use this flag.  Stack calls always
+ * use the fine form; for a layer call this flag asks for it. */
 #define MAPLE_FINE_LIMBS 0x40u
 /* Integer-activation (A8) variant, a different computation from the layer
  * above: x (per token, before the norm's scalar) and h (per routed token and
@@ -248,16 +253,29 @@ int maple_graph_destroy(maple_graph* graph);
 
 /* ---- kernel timing -------------------------------------------------------- */
 
-/* For benchmarks: while enabled on the calling thread, every kernel that the
- * forward and pack entry points enqueue is bracketed by two HIP events on its
- * own stream (events are created by the library and reused).  Not for use
- * during graph capture.  on != 0 starts a fresh record; on == 0 stops. */
+/* For benchmarks, per calling thread.  on == 1: every kernel that the forward
+ * and pack entry points enqueue is bracketed by two HIP events on its own
+ * stream (events are created by the library and reused; none are recorded
+ * inside a graph capture).  on == 2: device stamps, for graph replays: each
+ * launch of the one-token matrix-core kernels (dec_router, dec_gateup,
+ * dec_down) enqueued from then on, also while a graph is captured, gets a
+ * slot (at most 256) in a library-owned device buffer, and every block of
+ * the kernel writes the GPU's 100 MHz real-time counter into it at its entry
+ * and exit; a captured graph rewrites its slots on every replay.  on != 0
+ * starts a fresh record (slots are handed out again from the first, so a
+ * graph captured under an earlier record then shares them: destroy it or
+ * recapture); on == 0 stops handing out events and slots.  Other values give
+ * MAPLE_ERR_INVALID_ARG; mode 2 can fail with a HIP error from allocating
+ * the 4 MiB buffer on first use on a device. */
 int maple_profile_enable(int on);
-/* Waits for the recorded events and reports, per kernel name (up to max_kinds
- * of them, in order of first launch): the name (NUL-terminated, at most 63
+/* Waits for the device and reports, per kernel name (up to max_kinds of
+ * them, in order of first launch): the name (NUL-terminated, at most 63
  * characters, in names[i*64]), the number of launches and their summed
- * milliseconds.  names: max_kinds*64 bytes; launches, total_ms: max_kinds
- * entries; *n_kinds receives the count.  All are host pointers. */
+ * milliseconds: event time in mode 1; in mode 2 the span from the first
+ * block's entry to the last block's exit, as the stamps hold them now (after
+ * a graph replay: that replay's).  names: max_kinds*64 bytes; launches,
+ * total_ms: max_kinds entries; *n_kinds receives the count.  All are host
+ * pointers. */
 int maple_profile_summary(int max_kinds, char* names, int64_t* launches, double* total_ms,
                           int* n_kinds);
 

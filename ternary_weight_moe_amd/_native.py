@@ -259,8 +259,10 @@ def maple_moe_stack_forward(dims: Dims, n_tokens: int, x_inout, router_w: Sequen
         ctypes.byref(dbg) if dbg else None, _stream(stream)), "maple_moe_stack_forward")
 
 
-def maple_profile_enable(on: bool) -> None:
-    _check(load().maple_profile_enable(1 if on else 0), "maple_profile_enable")
+def maple_profile_enable(on) -> None:
+    """on: False/0 stops; True/1 events around each kernel; 2 device stamps
+    (one-token kernels, also inside graph captures)."""
+    _check(load().maple_profile_enable(int(on)), "maple_profile_enable")
 
 
 def maple_profile_summary(max_kinds: int = 64) -> dict:

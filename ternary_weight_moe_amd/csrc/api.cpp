@@ -95,11 +95,18 @@ struct ProfRecord {
   const char* name;
   hipEvent_t start, stop;
 };
+struct StampRecord {
+  const char* name;
+  int slot, blocks;
+};
 struct ProfState {
-  bool on = false;
+  int mode = 0;  // 0 off, 1 events around each kernel, 2 device stamps
   std::vector<ProfRecord> recs;
   std::vector<hipEvent_t> pool;  // events reused across records
   size_t used = 0;
+  long long* dstamp = nullptr;  // [kStampLaunches][2][kStampBlocks] (mode 2)
+  int dstamp_dev = -1;
+  std::vector<StampRecord> srecs;
 };
 thread_local ProfState g_prof;
 
@@ -114,13 +121,22 @@ hipEvent_t prof_event() {
 }  // namespace
 
 bool prof_slot(const char* name, hipEvent_t* start, hipEvent_t* stop) {
-  if (!g_prof.on) return false;
+  if (g_prof.mode != 1) return false;
   hipEvent_t a = prof_event(), b = prof_event();
   if (!a || !b) return false;
   g_prof.recs.push_back({name, a, b});
   *start = a;
   *stop = b;
   return true;
+}
+
+long long* stamp_slot(const char* name, int blocks) {
+  if (g_prof.mode != 2 || !g_prof.dstamp || blocks > kStampBlocks ||
+      (int)g_prof.srecs.size() >= kStampLaunches)
+    return nullptr;
+  const int slot = (int)g_prof.srecs.size();
+  g_prof.srecs.push_back({name, slot, blocks});
+  return g_prof.dstamp + (size_t)slot * 2 * kStampBlocks;
 }
 
 }  // namespace maple
@@ -587,8 +603,8 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
     delete g;
     return hip_fail(e, "graph setup");
   }
-  const bool prof_was_on = maple::g_prof.on;
-  maple::g_prof.on = false;  // no event records inside a capture
+  const int prof_was = maple::g_prof.mode;
+  if (prof_was == 1) maple::g_prof.mode = 0;  // no event records inside a capture (stamps stay)
   e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e == hipSuccess) {
     e = maple::launch_load_token(staged_x, staged_bf16, n_staged, n_tokens, d.H, g->counter,
@@ -602,7 +618,7 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
     const hipError_t e2 = hipStreamEndCapture(cs, &g->graph);
     if (e == hipSuccess) e = e2;
   }
-  maple::g_prof.on = prof_was_on;
+  maple::g_prof.mode = prof_was;
   if (e == hipSuccess && rc == MAPLE_OK)
     e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
   (void)hipStreamDestroy(cs);
@@ -619,10 +635,30 @@ int maple_moe_stack_graph_create(const maple_moe_dims* dims, int32_t n_layers, i
 }
 
 int maple_profile_enable(int on) {
-  maple::g_prof.on = on != 0;
+  if (on < 0 || on > 2) return fail(MAPLE_ERR_INVALID_ARG, "profile mode %d: need 0, 1 or 2", on);
+  auto& p = maple::g_prof;
+  if (on == 2) {
+    int rc = device_ready();
+    if (rc) return rc;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    // a graph captured in this mode keeps writing its slots, so a buffer is
+    // never freed (4 MiB; a new one only when the thread moves to another device)
+    if (!p.dstamp || p.dstamp_dev != dev) {
+      e = hipMalloc(&p.dstamp, sizeof(long long) * maple::kStampLaunches * 2 * maple::kStampBlocks);
+      if (e != hipSuccess) {
+        p.dstamp = nullptr;
+        return hip_fail(e, "stamp buffer");
+      }
+      p.dstamp_dev = dev;
+    }
+  }
+  p.mode = on;
   if (on) {
-    maple::g_prof.recs.clear();
-    maple::g_prof.used = 0;
+    p.recs.clear();
+    p.used = 0;
+    p.srecs.clear();
   }
   return MAPLE_OK;
 }
@@ -634,21 +670,42 @@ int maple_profile_summary(int max_kinds, char* names, int64_t* launches, double*
   std::vector<std::string> order;
   std::vector<int64_t> cnt;
   std::vector<double> ms;
+  auto add = [&](const char* name, double t) {
+    size_t i = 0;
+    while (i < order.size() && order[i] != name) ++i;
+    if (i == order.size()) {
+      order.push_back(name);
+      cnt.push_back(0);
+      ms.push_back(0.0);
+    }
+    cnt[i] += 1;
+    ms[i] += t;
+  };
+  const auto& sr = maple::g_prof.srecs;
+  if (!sr.empty()) {  // device stamps: span = last block exit - first block entry
+    std::vector<long long> h((size_t)sr.size() * 2 * maple::kStampBlocks);
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+      e = hipMemcpy(h.data(), maple::g_prof.dstamp, sizeof(long long) * h.size(),
+                    hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "stamp copy");
+    for (const auto& r : sr) {
+      const long long* t = &h[(size_t)r.slot * 2 * maple::kStampBlocks];
+      long long lo = t[0], hi = t[maple::kStampBlocks];
+      for (int b = 1; b < r.blocks; ++b) {
+        lo = std::min(lo, t[b]);
+        hi = std::max(hi, t[maple::kStampBlocks + b]);
+      }
+      add(r.name, (double)(hi - lo) * 1e-5);  // 100 MHz counter -> ms
+    }
+  }
   for (const auto& r : maple::g_prof.recs) {
     hipError_t e = hipEventSynchronize(r.stop);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     float t = 0.f;
     e = hipEventElapsedTime(&t, r.start, r.stop);
     if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-    size_t i = 0;
-    while (i < order.size() && order[i] != r.name) ++i;
-    if (i == order.size()) {
-      order.push_back(r.name);
-      cnt.push_back(0);
-      ms.push_back(0.0);
-    }
-    cnt[i] += 1;
-    ms[i] += t;
+    add(r.name, t);
   }
   const int n = (int)std::min<size_t>(order.size(), (size_t)max_kinds);
   for (int i = 0; i < n; ++i) {

@@ -423,7 +423,9 @@ __device__ __forceinline__ float route_dot16(const float4 w, const float4 v) {
 template <int H, bool BF16>
 __global__ __launch_bounds__(512) void k_dec_router(const void* __restrict__ x,
                                                     const float* __restrict__ Wr, int E,
-                                                    float* __restrict__ part) {
+                                                    float* __restrict__ part,
+                                                    long long* stamps) {
+  kstamp(stamps, 0);
   constexpr int P = H / kRouteRows;
   int grp, sub;
   route_block(blockIdx.x, P, &grp, &sub);
@@ -452,6 +454,7 @@ __global__ __launch_bounds__(512) void k_dec_router(const void* __restrict__ x,
       pg[kStatMax] = am;
     }
   }
+  kstamp(stamps, 1);
 }
 
 // Gate/up of one token.  blockIdx.y = j (selection order), blockIdx.x = block
@@ -476,7 +479,8 @@ __global__ __launch_bounds__(512) void k_dec_gateup(
     const float* __restrict__ alpha, float* __restrict__ h, int32_t* __restrict__ idx,
     float* __restrict__ gate, float* __restrict__ logits, int32_t* __restrict__ offsets,
     int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_pos) {
+    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_pos, long long* stamps) {
+  kstamp(stamps, 0);
   constexpr int NW = 8;
   constexpr int KW = H / NW;         // codes per wave
   constexpr int NSS = KW / 256;      // super-steps per wave
@@ -701,6 +705,7 @@ __global__ __launch_bounds__(512) void k_dec_gateup(
       gate[j] = expf(lgt(j) - lmax) / den;
     }
   }
+  kstamp(stamps, 1);
 }
 
 // Down projection, weighted combine and residual of one token, plus the next
@@ -720,7 +725,8 @@ __global__ __launch_bounds__(512) void k_dec_down(
     int k, const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const float* __restrict__ resid, int has_resid, float* __restrict__ out,
     float* __restrict__ delta, const float* __restrict__ next_wr, int has_next, int E,
-    float* __restrict__ part) {
+    float* __restrict__ part, long long* stamps) {
+  kstamp(stamps, 0);
   constexpr int P = H / kRouteRows;
   constexpr int PER = I / 64;           // h values per lane
   constexpr int NSS = I / 256;          // super-steps
@@ -844,6 +850,7 @@ __global__ __launch_bounds__(512) void k_dec_down(
     const float d = route_dot16(wr, xv);
     if ((tid & 15) == 0 && re < E) part[(int64_t)grp * kPartStride + re] = d;
   }
+  kstamp(stamps, 1);
 }
 
 template <int LPR_H, bool BF16>
@@ -923,8 +930,9 @@ float topk_f0(int E, int k) {
 template <int H, bool BF16>
 hipError_t dec_router(const Dims& d, const void* x, const float* Wr, const Workspace& ws,
                       hipStream_t s) {
-  launch("dec_router", k_dec_router<H, BF16>, (H / kRouteRows) * kRouteSubs, 512, 0, s, x, Wr,
-         d.E, ws.rpart);
+  constexpr int NB = (H / kRouteRows) * kRouteSubs;
+  launch("dec_router", k_dec_router<H, BF16>, NB, 512, 0, s, x, Wr, d.E, ws.rpart,
+         stamp_slot("dec_router", NB));
   return hipGetLastError();
 }
 
@@ -936,7 +944,8 @@ hipError_t dec_gateup(const Dims& d, const void* x, const float* bias, const uin
   launch("dec_gateup", k_dec_gateup<H, BF16>, dim3(d.I / 16, d.k), 512, 0, s, x, ws.rpart,
          bias ? bias : ws.x2, bias ? 1 : 0, d.E, d.k, norm, renorm, topk_f0(d.E, d.k), d.I,
          packed, alpha, ws.h, ws.idx, ws.gate, ws.logits, ws.offsets,
-         ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos);
+         ws.active, ws.n_active, ws.sorted_tok, ws.slot_pos,
+         stamp_slot("dec_gateup", d.I / 16 * d.k));
   return hipGetLastError();
 }
 
@@ -946,9 +955,10 @@ template <int H, int I>
 hipError_t dec_down(const Dims& d, const uint8_t* packed, const float* alpha, const Workspace& ws,
                     float* out, const float* resid, float* delta, const float* Wr,
                     const float* next_wr, hipStream_t s) {
-  launch("dec_down", k_dec_down<H, I>, (H / kRouteRows) * kRouteSubs, 512, 0, s, ws.h, ws.idx,
-         ws.gate, d.k, packed, alpha, resid ? resid : ws.x2, resid ? 1 : 0, out, delta,
-         next_wr ? next_wr : Wr, next_wr ? 1 : 0, d.E, ws.rpart);
+  constexpr int NB = (H / kRouteRows) * kRouteSubs;
+  launch("dec_down", k_dec_down<H, I>, NB, 512, 0, s, ws.h, ws.idx, ws.gate, d.k, packed, alpha,
+         resid ? resid : ws.x2, resid ? 1 : 0, out, delta, next_wr ? next_wr : Wr,
+         next_wr ? 1 : 0, d.E, ws.rpart, stamp_slot("dec_down", NB));
   return hipGetLastError();
 }
 

@@ -390,7 +390,9 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   }
   if (kg == 0) s_redi[wave][m] = qs;
   // hs: [part][scale | digit row sum (int bits)][slot]
-  if (wave == 0 && kg == 0 && m < np) hs[2 * part * Tk + p0 + m] = sc;
+  // a part whose h is all zero stores scale 0 (its digits are zero anyway), so
+  // it never decides a slot's output scale in the down projection
+  if (wave == 0 && kg == 0 && m < np) hs[2 * part * Tk + p0 + m] = mx > 0.f ? sc : 0.f;
   __syncthreads();
   if (tid < np) {
     int tot = 0;
@@ -489,6 +491,15 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     sc[h2] = live ? hs[2 * h2 * Tk + p0 + r32] : 0.f;
     hsum[h2] = live ? (float)reinterpret_cast<const int*>(hs)[(2 * h2 + 1) * Tk + p0 + r32] : 0.f;
   }
+  // The fp16 outputs are stored relative to the slot's largest part scale,
+  // times 2^-8 (the combine multiplies that factor back): |q| <= 16383 then
+  // bounds a stored value by |a_d| * I * 16383 / 256, whatever the input's
+  // magnitude (I <= 512: finite for |a_d| <= 2).
+  float smax = 0.f;
+#pragma unroll
+  for (int h2 = 0; h2 < NS; ++h2) smax = fmaxf(smax, sc[h2]);
+#pragma unroll
+  for (int h2 = 0; h2 < NS; ++h2) sc[h2] = smax > 0.f ? sc[h2] / smax * 0.00390625f : 0.f;
 #pragma unroll
   for (int i = 0; i < NHU; ++i) {
     const int u = tid + NTH * i;
@@ -962,12 +973,17 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 // out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order
 // in fp32; a thread owns 8 consecutive outputs (y fp16: one 16-byte load per
 // slot; fp32: two).
+// ysc (fp16 form only): the per-slot h scales hs of the down projection's
+// parts ([part][scale | sum][slot], ns parts of Tk slots); the stored outputs
+// are scaled by 2^-8 / (the slot's largest part scale), undone here.
 template <typename YT>
 __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
                                                  const float* __restrict__ gate,
                                                  const int32_t* __restrict__ slot_pos, int H,
                                                  int k, float* out, const float* resid,
-                                                 float* __restrict__ delta) {
+                                                 float* __restrict__ delta,
+                                                 const float* __restrict__ ysc, int ns,
+                                                 int64_t Tk) {
   const int64_t t = blockIdx.x;
   const int o = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (o >= H) return;
@@ -983,6 +999,15 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
       sp[j] = slot_pos[t * k + j];
       g[j] = gate[t * k + j];
     }
+  if constexpr (!std::is_same<YT, float>::value) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) {
+        float smax = 0.f;
+        for (int h2 = 0; h2 < ns; ++h2) smax = fmaxf(smax, ysc[2 * h2 * Tk + sp[j]]);
+        g[j] *= smax * 256.f;
+      }
+  }
   uint4 v[KM][NV];
 #pragma unroll
   for (int j = 0; j < KM; ++j)
@@ -1102,10 +1127,11 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
   const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
   if (fine)
     launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate, ws.slot_pos,
-           d.H, d.k, out, resid, delta);
+           d.H, d.k, out, resid, delta, (const float*)nullptr, 0, Tk);
   else
     launch("combine", k_combine<uint16_t>, cgrid, 256, 0, s, (const uint16_t*)ws.y, ws.gate,
-           ws.slot_pos, d.H, d.k, out, resid, delta);
+           ws.slot_pos, d.H, d.k, out, resid, delta, (const float*)ws.hs,
+           d.I >= 512 ? 2 : 1, Tk);
   return hipGetLastError();
 }
 

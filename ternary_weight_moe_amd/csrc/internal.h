@@ -62,6 +62,25 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws);  // base may 
 // own begin and end (the dispatch timestamps, not the queue around it).
 bool prof_slot(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
+// Device stamps (maple_profile_enable(2)): kernels that take a stamp pointer
+// write the 100 MHz real-time counter at the entry (stamps[b]) and exit
+// (stamps[kStampBlocks + b]) of each block b; stamp_slot hands out one slot
+// per launch (also inside a graph capture, whose replays then rewrite it), or
+// null when the mode is off.
+constexpr int kStampBlocks = 1024;
+constexpr int kStampLaunches = 256;
+long long* stamp_slot(const char* name, int blocks);
+// The exit stamp waits for the whole block; a null pointer (the uniform
+// production case) costs one scalar branch.
+__device__ __forceinline__ void kstamp(long long* stamps, int exit) {
+  if (stamps) {
+    if (exit) __syncthreads();
+    if (threadIdx.x == 0)
+      stamps[exit * kStampBlocks + blockIdx.x + blockIdx.y * gridDim.x] =
+          (long long)__builtin_amdgcn_s_memrealtime();
+  }
+}
+
 // Every library kernel launch goes through here, named for the timing hook.
 template <typename... P, typename... A>
 void launch(const char* name, void (*kernel)(P...), dim3 grid, dim3 block, unsigned lds,

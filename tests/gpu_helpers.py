@@ -128,3 +128,83 @@ def assert_routing_equal(idx_gpu, slot_pos_gpu, offsets_gpu, sorted_gpu, idx_ref
         ref = dict(zip(idx_ref[t].tolist(), pos_ref[t].tolist()))
         got = dict(zip(idx_gpu[t].tolist(), np.asarray(slot_pos_gpu)[t].tolist()))
         assert ref == got, f"{what}: slot positions of token {t}"
+
+
+def workload(base_name, **kw):
+    """A named workload with some fields replaced."""
+    base = S.WORKLOADS[base_name]
+    f = dict(base.__dict__)
+    f.pop("notes", None)
+    f.update(kw)
+    return S.Workload(**f)
+
+
+def run_layer(w, L, x_host, flags=0):
+    """One layer call through the C ABI; returns the outputs and the routing
+    the library reports (top-k indices and gates, logits, grouping)."""
+    import torch
+    T, H, E, k = x_host.shape[0], w.hidden, w.n_experts, w.top_k
+    d = dims_for(w, flags)
+    x = x_device(w, x_host)
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bufs = dict(idx=torch.empty(T, k, **i32),
+                gate=torch.empty(T, k, dtype=torch.float32, device="cuda"),
+                logits=torch.empty(T, E, dtype=torch.float32, device="cuda"),
+                offsets=torch.empty(E + 1, **i32), sorted_token=torch.empty(T * k, **i32),
+                slot_pos=torch.empty(T, k, **i32))
+    N.maple_moe_layer_forward(d, T, x, L.d_Wr, L.d_bias, L.packed, L.d_alpha, out, ws,
+                              N.make_debug(**bufs))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), {n: b.cpu().numpy() for n, b in bufs.items()}
+
+
+def check_layer(w, L, x_host, flags=0, renorm=False, prenorm=False, sample=None, what=""):
+    """Routing of every token bit-exact; outputs of every token, or of the
+    tokens in `sample`, within tolerance."""
+    T = x_host.shape[0]
+    log(f"{what}: T={T} flags={flags:#x}")
+    flags |= (N.MAPLE_RENORM_TOPK if renorm else 0) | (N.MAPLE_RMS_NORM if prenorm else 0)
+    got, dbg = run_layer(w, L, x_host, flags)
+    x64 = S.x_as_f32(w, x_host).astype(np.float64)
+    xr = oracle.rms_normalize(x64) if prenorm else x64
+    logits = oracle.router_logits(xr, L.Wr, L.bias)
+    idx_ref, gate_ref = oracle.topk(logits, w.top_k, renorm)
+    assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
+                         idx_ref, w.n_experts, what)
+    np.testing.assert_allclose(dbg["logits"], logits, rtol=0, atol=5e-5)
+    for t in range(T):  # gates, matched per (token, expert)
+        gr = dict(zip(idx_ref[t].tolist(), gate_ref[t].tolist()))
+        gg = dict(zip(dbg["idx"][t].tolist(), dbg["gate"][t].tolist()))
+        for e in gr:
+            assert abs(gg[e] - gr[e]) <= 1e-5 * max(1.0, abs(gr[e])), (t, e)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    ref = L.oracle_layer(x64[rows], w.top_k, w.inter, renorm=renorm, prenorm=prenorm)
+    assert np.array_equal(ref["idx"], idx_ref[rows])
+    assert_close(got[rows], ref["out"], what)
+    return got
+
+
+def check_a8(w, L, x_host, sample=None, prenorm=False, what=""):
+    """The A8 variant against the oracle's A8 mode (routing bit-exact, outputs
+    within tolerance) and, loosely, against the exact layer."""
+    flags = N.MAPLE_ACT_INT8 | (N.MAPLE_RMS_NORM if prenorm else 0)
+    got, dbg = run_layer(w, L, x_host, flags)
+    x64 = S.x_as_f32(w, x_host).astype(np.float64)
+    rows = np.arange(x_host.shape[0]) if sample is None else np.asarray(sample)
+    ref = oracle.moe_layer(x64[rows], L.Wr, L.bias, L.packed_ref, L.alpha, k=w.top_k,
+                           inter=w.inter, prenorm=prenorm, a8=True)
+    if sample is None:
+        assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
+                             ref["idx"], w.n_experts, what)
+    else:
+        assert np.array_equal(np.sort(dbg["idx"][rows], 1), np.sort(ref["idx"], 1)), what
+    assert_close(got[rows], ref["out"], f"{what} vs A8 oracle")
+    exact = oracle.moe_layer(x64[rows], L.Wr, L.bias, L.packed_ref, L.alpha, k=w.top_k,
+                             inter=w.inter, prenorm=prenorm)["out"]
+    rel = np.linalg.norm(got[rows] - exact) / np.linalg.norm(exact)
+    log(f"{what}: A8 against the exact layer rel L2 {rel:.3e}")
+    assert rel < 6e-2
+    return got

@@ -176,6 +176,17 @@ def test_valid_call_without_device_reports_no_device(lib):
     assert lib.maple_ternary_pack_device(w.addr, 64, 0x200000, None, None) == N.MAPLE_ERR_NO_DEVICE
 
 
+def test_profile_modes(lib):
+    """Timing modes 0, 1 and 2; anything else is rejected.  Mode 2 (device
+    stamps) needs a device for its buffer; modes 0 and 1 do not."""
+    assert lib.maple_profile_enable(3) == N.MAPLE_ERR_INVALID_ARG
+    assert lib.maple_profile_enable(-1) == N.MAPLE_ERR_INVALID_ARG
+    assert lib.maple_profile_enable(2) == N.MAPLE_ERR_NO_DEVICE
+    assert lib.maple_profile_enable(1) == N.MAPLE_OK
+    assert N.maple_profile_summary() == {}
+    assert lib.maple_profile_enable(0) == N.MAPLE_OK
+
+
 def test_stack_and_graph_validation(lib):
     d = dims(flags=0)
     P = ctypes.c_void_p

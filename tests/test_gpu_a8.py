@@ -15,35 +15,10 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-import oracle  # noqa: E402
-from gpu_helpers import (Layer, assert_close, assert_routing_equal, layer_tokens_with_gap,  # noqa: E402
-                         log)
-from test_gpu_parity import run_layer  # noqa: E402
-from ternary_weight_moe_amd import _native as N  # noqa: E402
+from gpu_helpers import Layer, check_a8, layer_tokens_with_gap  # noqa: E402
 from ternary_weight_moe_amd import synth as S  # noqa: E402
 
 pytestmark = pytest.mark.gpu
-
-
-def check_a8(w, L, x_host, sample=None, prenorm=False, what=""):
-    flags = N.MAPLE_ACT_INT8 | (N.MAPLE_RMS_NORM if prenorm else 0)
-    got, dbg = run_layer(w, L, x_host, flags)
-    x64 = S.x_as_f32(w, x_host).astype(np.float64)
-    rows = np.arange(x_host.shape[0]) if sample is None else np.asarray(sample)
-    ref = oracle.moe_layer(x64[rows], L.Wr, L.bias, L.packed_ref, L.alpha, k=w.top_k,
-                           inter=w.inter, prenorm=prenorm, a8=True)
-    if sample is None:
-        assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
-                             ref["idx"], w.n_experts, what)
-    else:
-        assert np.array_equal(np.sort(dbg["idx"][rows], 1), np.sort(ref["idx"], 1)), what
-    assert_close(got[rows], ref["out"], f"{what} vs A8 oracle")
-    exact = oracle.moe_layer(x64[rows], L.Wr, L.bias, L.packed_ref, L.alpha, k=w.top_k,
-                             inter=w.inter, prenorm=prenorm)["out"]
-    rel = np.linalg.norm(got[rows] - exact) / np.linalg.norm(exact)
-    log(f"{what}: A8 against the exact layer rel L2 {rel:.3e}")
-    assert rel < 6e-2
-    return got
 
 
 @pytest.fixture(scope="module")

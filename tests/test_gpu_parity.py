@@ -13,65 +13,12 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from gpu_helpers import (Layer, assert_close, assert_routing_equal, dims_for,  # noqa: E402
-                         layer_tokens_with_gap, log, stack_tokens_with_gap, x_device)
+from gpu_helpers import (Layer, assert_close, check_layer, dims_for,  # noqa: E402
+                         layer_tokens_with_gap, log, run_layer, workload)
 from ternary_weight_moe_amd import _native as N  # noqa: E402
 from ternary_weight_moe_amd import synth as S  # noqa: E402
 
 pytestmark = pytest.mark.gpu
-
-
-def workload(name, **kw):
-    base = S.WORKLOADS[name]
-    f = dict(base.__dict__)
-    f.pop("notes", None)
-    f.update(kw)
-    return S.Workload(**f)
-
-
-def run_layer(w, L, x_host, flags=0):
-    T, H, E, k = x_host.shape[0], w.hidden, w.n_experts, w.top_k
-    d = dims_for(w, flags)
-    x = x_device(w, x_host)
-    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
-    i32 = dict(dtype=torch.int32, device="cuda")
-    bufs = dict(idx=torch.empty(T, k, **i32),
-                gate=torch.empty(T, k, dtype=torch.float32, device="cuda"),
-                logits=torch.empty(T, E, dtype=torch.float32, device="cuda"),
-                offsets=torch.empty(E + 1, **i32), sorted_token=torch.empty(T * k, **i32),
-                slot_pos=torch.empty(T, k, **i32))
-    N.maple_moe_layer_forward(d, T, x, L.d_Wr, L.d_bias, L.packed, L.d_alpha, out, ws,
-                              N.make_debug(**bufs))
-    torch.cuda.synchronize()
-    return out.cpu().numpy(), {n: b.cpu().numpy() for n, b in bufs.items()}
-
-
-def check_layer(w, L, x_host, flags=0, renorm=False, prenorm=False, sample=None, what=""):
-    """Routing of every token bit-exact; outputs of every token, or of the
-    tokens in `sample`, within tolerance."""
-    T = x_host.shape[0]
-    log(f"{what}: T={T} flags={flags:#x}")
-    flags |= (N.MAPLE_RENORM_TOPK if renorm else 0) | (N.MAPLE_RMS_NORM if prenorm else 0)
-    got, dbg = run_layer(w, L, x_host, flags)
-    x64 = S.x_as_f32(w, x_host).astype(np.float64)
-    xr = oracle.rms_normalize(x64) if prenorm else x64
-    logits = oracle.router_logits(xr, L.Wr, L.bias)
-    idx_ref, gate_ref = oracle.topk(logits, w.top_k, renorm)
-    assert_routing_equal(dbg["idx"], dbg["slot_pos"], dbg["offsets"], dbg["sorted_token"],
-                         idx_ref, w.n_experts, what)
-    np.testing.assert_allclose(dbg["logits"], logits, rtol=0, atol=5e-5)
-    for t in range(T):  # gates, matched per (token, expert)
-        gr = dict(zip(idx_ref[t].tolist(), gate_ref[t].tolist()))
-        gg = dict(zip(dbg["idx"][t].tolist(), dbg["gate"][t].tolist()))
-        for e in gr:
-            assert abs(gg[e] - gr[e]) <= 1e-5 * max(1.0, abs(gr[e])), (t, e)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
-    rows = np.arange(T) if sample is None else np.asarray(sample)
-    ref = L.oracle_layer(x64[rows], w.top_k, w.inter, renorm=renorm, prenorm=prenorm)
-    assert np.array_equal(ref["idx"], idx_ref[rows])
-    assert_close(got[rows], ref["out"], what)
-    return got
 
 
 # ---- packing ----------------------------------------------------------------------
@@ -261,3 +208,53 @@ def test_prefill_layer(name, n_sample, flags):
     sample = np.sort(np.concatenate([[0, w.n_tokens - 1],
                                      rng.choice(w.n_tokens, n_sample, replace=False)]))
     check_layer(w, L, x, flags=flags, sample=sample, what=name)
+
+
+# ---- skewed routing at 4096 tokens (long expert groups, many empty experts) ------------
+
+@GROUPED_FORMS
+@pytest.mark.parametrize("skew", ["zipf", "all_to_8"])
+def test_prefill_4096_skewed(skew, gflags):
+    """4096 tokens, either under the Zipf router bias of the batched workload
+    (a few experts take hundreds of slots, over half the experts none) or all
+    routed to the same 8 experts (4096 slots, 128 tiles of 32, per expert):
+    routing bit-exact for every token, outputs on a sample of rows."""
+    if skew == "zipf":
+        w = workload("prefill_4096", zipf_beta=S.WORKLOADS["batched_stack_zipf"].zipf_beta)
+        L = Layer(w, 0)
+    else:
+        w = S.WORKLOADS["prefill_4096"]
+        L = Layer(w, 0)
+        # +50 on experts 3, 40, .., 255 (the logits' sd is about 0.9): every
+        # token's top 8 is that set, in an order its own logits decide
+        b = np.zeros(w.n_experts, np.float32)
+        b[[3, 40, 77, 114, 151, 188, 225, 255]] = 50.0
+        L.bias, L.d_bias = b, torch.from_numpy(b).cuda()
+    x, regen = layer_tokens_with_gap(w, L, w.n_tokens, token0=20000)
+    log(f"{skew}: regenerated {len(regen)} tokens")
+    rng = np.random.default_rng(w.seed + 77)
+    sample = np.sort(np.concatenate([[0, w.n_tokens - 1],
+                                     rng.choice(w.n_tokens, 126, replace=False)]))
+    check_layer(w, L, x, flags=gflags, sample=sample, what=f"prefill_4096 {skew}")
+
+
+# ---- large activations (range of the fast form's 16-bit per-slot outputs) -------------
+
+@GROUPED_FORMS
+def test_grouped_large_activations(dec, gflags):
+    """Inputs at 100 times the configs' scale: the outputs grow about
+    10^4-fold (the SwiGLU product of two terms linear in x), beyond the range
+    of 16-bit floats, which hold the fast form's per-slot partial outputs
+    only after a per-slot scale.  Routing must match, every output must be
+    finite, and the outputs must match the oracle at their own scale (both
+    divided by 10^4, the tolerances of the configs' scale)."""
+    w, L = dec
+    x, _ = layer_tokens_with_gap(w, L, 64, token0=21000)
+    xs = (S.x_as_f32(w, x) * 100.0).astype(np.float32)
+    wf = workload("decode_layer", x_bf16=False)
+    got, dbg = run_layer(wf, L, xs, gflags)
+    assert np.all(np.isfinite(got)), "non-finite outputs"
+    ref = L.oracle_layer(xs.astype(np.float64), w.top_k, w.inter)
+    assert np.array_equal(np.sort(dbg["idx"], 1), np.sort(ref["idx"], 1))
+    log(f"max |out| {np.abs(ref['out']).max():.3e}")
+    assert_close(got / 1e4, ref["out"] / 1e4, "x100 inputs")

@@ -1,0 +1,52 @@
+"""GPU parity over every shape class the ABI accepts: hidden 256..4096 and
+inter 128..2048 (powers of two), each through every path that serves it.
+
+- One token (T = 1) with automatic dispatch, with and without top-k
+  renormalisation: the matrix-core one-token kernels serve hidden 2048/4096
+  with inter 256/512; the VALU one-token kernels serve every other shape.
+- The VALU GEMV path (forced), T = 5.
+- The grouped matrix-core path for inter <= 512 (the grouped kernels' limit),
+  T = 40: the fast form, the fine form and the A8 variant.
+
+Every shape has 16 experts and top-4.  Routing is compared bit-exact and
+outputs within the layer tolerances, against the oracle on the same seeded
+inputs; tokens obey the router gap rule.  (The architecture table of the
+linlog.top article "Maple-Preview" fixes hidden 2048, 256 experts, top-8 and
+intermediate 512; the other shapes are the ones the ABI admits besides.)
+"""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_helpers import (Layer, check_a8, check_layer, layer_tokens_with_gap,  # noqa: E402
+                         log, workload)
+from ternary_weight_moe_amd import _native as N  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN = (256, 512, 1024, 2048, 4096)
+INTER = (128, 256, 512, 1024, 2048)
+GROUPED_MAX_INTER = 512
+
+
+@pytest.mark.parametrize("I", INTER, ids=lambda v: f"i{v}")
+@pytest.mark.parametrize("H", HIDDEN, ids=lambda v: f"h{v}")
+def test_shape_every_path(H, I):
+    w = workload("tiny_layer", name=f"shape_{H}_{I}", hidden=H, inter=I, n_experts=16,
+                 top_k=4, n_tokens=40, x_bf16=True, seed=6000 + H + I)
+    log(f"shape H={H} I={I}: generating the layer")
+    L = Layer(w, 0)
+    x1, _ = layer_tokens_with_gap(w, L, 2, token0=100)
+    for t in range(2):
+        for renorm in (False, True):
+            check_layer(w, L, x1[t:t + 1], renorm=renorm,
+                        what=f"H={H} I={I} one token #{t} renorm={renorm}")
+    x5, _ = layer_tokens_with_gap(w, L, 5, token0=200)
+    check_layer(w, L, x5, flags=N.MAPLE_FORCE_GEMV, what=f"H={H} I={I} gemv T=5")
+    if I > GROUPED_MAX_INTER:
+        return
+    x40, _ = layer_tokens_with_gap(w, L, 40, token0=300)
+    check_layer(w, L, x40, flags=N.MAPLE_FORCE_GROUPED, what=f"H={H} I={I} grouped fast")
+    check_layer(w, L, x40, flags=N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS,
+                what=f"H={H} I={I} grouped fine")
+    check_a8(w, L, x40, what=f"H={H} I={I} a8")

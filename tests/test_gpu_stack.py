@@ -76,8 +76,10 @@ def test_decode_stack_a8(stack3):
 
 
 def test_decode_stack_one_token_chain(stack3):
-    """One token per call: each layer's router rides on the previous layer's
-    down kernel (partial dots), checked layer by layer."""
+    """One token per call, two kernels per layer: gate/up, which sums the
+    router's partial dots, selects the top k and forms the gates, then down +
+    combine, which also forms the next layer's partial router dots (the first
+    layer's come from a router kernel).  Checked layer by layer."""
     w, layers = stack3
     x, x64, ref, regen = stack_tokens_with_gap(w, layers, 3, token0=20)
     for t in range(3):
