@@ -217,6 +217,25 @@ int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const 
                             void* workspace, size_t ws_bytes, const maple_moe_debug* dbg,
                             void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as maple_moe_layer_forward, its workspace taken from a library-owned
+ * static device array of MAPLE_STATIC_SCRATCH_BYTES on the current device
+ * (each device holds its own copy until the process ends; its address is
+ * looked up once per device, on the first call there).  The call allocates
+ * nothing.  Calls whose workspace (maple_moe_workspace_bytes(dims, n_tokens))
+ * exceeds the array give MAPLE_ERR_WORKSPACE_TOO_SMALL before touching the
+ * device: about 128 tokens at hidden 2048, 256 experts, top-8, inter 512.
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (other streams, other threads) race and must be
+ * ordered by the caller.  Arguments and errors otherwise as
+ * maple_moe_layer_forward. */
+#define MAPLE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int maple_moe_layer_forward_noalloc(const maple_moe_dims* dims, int32_t n_tokens, const void* x,
+                                    const float* router_w, const float* router_bias,
+                                    const uint8_t* packed_w, const float* alpha, float* out,
+                                    const maple_moe_debug* dbg, void* stream);
+
 /* A stack of n_layers pre-norm MoE blocks joined by a residual add, in place:
  * x <- x + MoE_l(x / rms(x)) for l = 0..n_layers-1 (MAPLE_RMS_NORM implied).  x_inout [T,H] fp32 device.
  * router_w, packed_w, alpha: host arrays of n_layers device pointers;

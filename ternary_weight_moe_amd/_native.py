@@ -25,6 +25,7 @@ MAPLE_ERR_WORKSPACE_TOO_SMALL = -4
 MAPLE_ERR_INVALID_CODE = -5
 MAPLE_ERR_NO_DEVICE = -6
 MAPLE_ERR_HIP = -7
+MAPLE_STATIC_SCRATCH_BYTES = 16 << 20
 
 MAPLE_X_BF16 = 0x1
 MAPLE_RENORM_TOPK = 0x2
@@ -42,6 +43,7 @@ EXPORTS = [
     "maple_ternary_pack_device", "maple_moe_layer_forward", "maple_moe_stack_forward",
     "maple_moe_stack_graph_create", "maple_graph_launch", "maple_graph_set_step",
     "maple_graph_destroy", "maple_profile_enable", "maple_profile_summary",
+    "maple_moe_layer_forward_noalloc",
     "maple_head_workspace_bytes", "maple_flashhead_forward",
     "maple_attn_cache_bytes", "maple_attn_workspace_bytes", "maple_attn_cache_fill",
     "maple_attn_decode", "maple_ternarize_bf16_device",
@@ -118,6 +120,9 @@ def load() -> ctypes.CDLL:
                                                        _P, _P]),
         "maple_moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Dims), i32, _P, _P, _P, _P,
                                                    _P, _P, _P, sz, ctypes.POINTER(Debug), _P]),
+        "maple_moe_layer_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Dims), i32, _P, _P,
+                                                           _P, _P, _P, _P,
+                                                           ctypes.POINTER(Debug), _P]),
         "maple_moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(Dims), i32, i32, _P, _P, _P,
                                                    _P, _P, _P, sz, ctypes.POINTER(Debug), _P]),
         "maple_moe_stack_graph_create": (ctypes.c_int, [ctypes.POINTER(Dims), i32, i32, _P, i32,
@@ -243,6 +248,15 @@ def maple_moe_layer_forward(dims: Dims, n_tokens: int, x, router_w, router_bias,
         _dptr(packed_w), _dptr(alpha), _dptr(out), _dptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(dbg) if dbg else None,
         _stream(stream)), "maple_moe_layer_forward")
+
+
+def maple_moe_layer_forward_noalloc(dims: Dims, n_tokens: int, x, router_w, router_bias,
+                                    packed_w, alpha, out, dbg: Optional[Debug] = None,
+                                    stream=None) -> None:
+    _check(load().maple_moe_layer_forward_noalloc(
+        ctypes.byref(dims), n_tokens, _dptr(x), _dptr(router_w), _dptr(router_bias),
+        _dptr(packed_w), _dptr(alpha), _dptr(out), ctypes.byref(dbg) if dbg else None,
+        _stream(stream)), "maple_moe_layer_forward_noalloc")
 
 
 def maple_moe_stack_forward(dims: Dims, n_tokens: int, x_inout, router_w: Sequence,

@@ -510,6 +510,67 @@ int maple_moe_layer_forward(const maple_moe_dims* dims, int32_t n_tokens, const 
                    packed_w, alpha, out, nullptr, nullptr, ws, dbg, (hipStream_t)stream);
 }
 
+// ---- allocation-free layer call ----------------------------------------------
+// The workspace lives in this file-scope device array.  In host code its name
+// stands for a host-side shadow, never a device address: only the address
+// that hipGetSymbolAddress returns for the current device is passed on.
+static __device__ __align__(256) unsigned char scratch[MAPLE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The array's device address on the current device, looked up on the first
+// call there.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MAPLE_ERR_INVALID_ARG, "device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MAPLE_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MAPLE_OK;
+}
+}  // namespace
+
+int maple_moe_layer_forward_noalloc(const maple_moe_dims* dims, int32_t n_tokens, const void* x,
+                                    const float* router_w, const float* router_bias,
+                                    const uint8_t* packed_w, const float* alpha, float* out,
+                                    const maple_moe_debug* dbg, void* stream) {
+  Dims d;
+  int rc;
+  if ((rc = check_dims(dims, &d))) return rc;
+  if ((rc = check_tokens(d, n_tokens))) return rc;
+  Workspace ws;
+  const size_t need = maple::carve(d, n_tokens, nullptr, &ws);
+  if (need > MAPLE_STATIC_SCRATCH_BYTES)
+    return fail(MAPLE_ERR_WORKSPACE_TOO_SMALL,
+                "n_tokens=%d needs %zu B of workspace; the static scratch holds %zu B "
+                "(use maple_moe_layer_forward with a workspace)",
+                n_tokens, need, (size_t)MAPLE_STATIC_SCRATCH_BYTES);
+  if ((rc = check_ptr(x, 16, "x")) || (rc = check_ptr(router_w, 16, "router_w")) ||
+      (rc = check_opt_ptr(router_bias, 4, "router_bias")) ||
+      (rc = check_ptr(packed_w, 256, "packed_w")) || (rc = check_ptr(alpha, 16, "alpha")) ||
+      (rc = check_ptr(out, 16, "out")))
+    return rc;
+  if (n_tokens == 0) return MAPLE_OK;
+  if ((rc = device_ready())) return rc;
+  void* base = nullptr;
+  if ((rc = scratch_address(&base))) return rc;
+  return maple_moe_layer_forward(dims, n_tokens, x, router_w, router_bias, packed_w, alpha, out,
+                                 base, MAPLE_STATIC_SCRATCH_BYTES, dbg, stream);
+}
+
 static int enqueue_stack(const Dims& d, int32_t n_layers, int64_t T, float* x,
                          const float* const* router_w, const float* const* router_bias,
                          const uint8_t* const* packed_w, const float* const* alpha,
