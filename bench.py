@@ -112,31 +112,34 @@ def prefill_ops(kernel, H, k, I, T):
 
 # ---- measured HBM traffic --------------------------------------------------------------
 
-# HBM bytes per launch of a kernel, from two rocprofv3 --pmc runs of this script
-# (FETCH_SIZE, then WRITE_SIZE; summaries in profiles/*_traffic.md), FETCH_SIZE
-# scaled by the factor a plain device copy of known size gives (2.0 here: the
-# counter formula books a 128-byte request as 64 bytes) and WRITE_SIZE by 1.0.
-# An entry holds only while the kernel's sources hash as recorded; otherwise the
-# kernel has changed since the counters were taken and the traffic is unknown.
+# HBM bytes per launch of a kernel, from rocprofv3 --pmc runs of this script
+# (summaries in profiles/*_traffic.md).  Reads: the L2's memory read requests
+# counted by size (TCC_EA0_RDREQ_32B/_64B/_128B, weighted by their sizes),
+# which a plain device copy of known size reproduces exactly; FETCH_SIZE's
+# formula books this chip's 128-byte requests as 64 bytes (TCC_BUBBLE reads
+# zero), so older entries scaled it by 2.0.  Writes: WRITE_SIZE, which the
+# same copy reproduces unscaled.  An entry holds only while the kernel's
+# sources hash as recorded; otherwise the kernel has changed since the
+# counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "d1m_down": {"bytes": 4617509, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
-        "d1m_gateup": {"bytes": 6567467, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
-        "d1q_router": {"bytes": 2252498, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "9decf271c199fff8"},
-        "load_token": {"bytes": 15736, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
-        "store_token": {"bytes": 42183, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
+        "dec_down": {"bytes": 4509671, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1261137eae3b9bf2"},
+        "dec_gateup": {"bytes": 4742253, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1261137eae3b9bf2"},
+        "dec_router": {"bytes": 2168215, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1261137eae3b9bf2"},
+        "load_token": {"bytes": 13721, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "7c034a523fd90754"},
+        "store_token": {"bytes": 29572, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "7c034a523fd90754"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 168855800, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "down_mfma": {"bytes": 244603755, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "gateup_mfma": {"bytes": 326146377, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "quant_x": {"bytes": 35918229, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "route_block": {"bytes": 359404, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_scan": {"bytes": 149783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_scatter": {"bytes": 1226217, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_topk": {"bytes": 4519400, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "router_mfma": {"bytes": 37815979, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "split_router": {"bytes": 4218639, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "combine": {"bytes": 170375668, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
+        "down_mfma": {"bytes": 244618064, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
+        "gateup_mfma": {"bytes": 325614694, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
+        "quant_x": {"bytes": 35946953, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
+        "route_block": {"bytes": 343948, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
+        "route_scan": {"bytes": 146289, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
+        "route_scatter": {"bytes": 1209143, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
+        "route_topk": {"bytes": 4488448, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
+        "router_mfma": {"bytes": 37784413, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
+        "split_router": {"bytes": 4206355, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
     },
     "prefill_4096_a8": {
         "combine": {"bytes": 303057223, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
@@ -826,14 +829,18 @@ def bench_prefill(args, torch, N, S):
     dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
     ops = prefill_ops(dom, H, k, I, T)
     dom_avg_s = prof[dom][1] * 1e-3
-    # issued MFMA work: every expert's slots padded to whole 32-slot tiles, and
-    # each product issued once per digit plane (three in the fast form, one
-    # limb in A8); the routing is the same call's, copied out
+    # issued MFMA work: every expert's slots padded to whole 32-slot tiles (the
+    # A8 kernels' 16 x 16 MFMAs skip the second half of a tile's columns when
+    # its last tile holds at most 16 slots), and each product issued once per
+    # digit plane (three in the fast form, one limb in A8); the routing is the
+    # same call's, copied out
     idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
     N.maple_moe_layer_forward(d, T, x, layer["Wr"], layer["bias"], layer["packed"],
                               layer["alpha"], out, ws, N.make_debug(idx=idx))
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=E)
-    padded = int((-(-counts // 32) * 32).sum())
+    rem = counts % 32
+    last = np.where(rem == 0, 0, np.where((rem <= 16) & a8, 16, 32))
+    padded = int((32 * (counts // 32) + last).sum())
     issued_ratio = (1 if a8 else 3) * padded / (T * k)
     # the A8 variant runs int8 MFMAs; the default (fast) form fp4 x fp6 ones,
     # priced against that instruction's own peak
