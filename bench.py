@@ -330,6 +330,33 @@ def graph_stamp_profile(N, torch, make_graph, replays, burst=4):
     return {kn: (n, us / replays) for kn, (n, us) in acc.items()}, ms_stamped
 
 
+def dependent_launch_floor(torch, n_kernels=49, replays=64):
+    """The time per kernel of a captured graph of n_kernels dependent
+    one-element kernels (torch's in-place add), replayed back to back: the
+    cost of a kernel boundary with no work, the floor under a decode step
+    that has n_kernels dependent launches."""
+    a = torch.zeros(1, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            a.add_(1.0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(n_kernels):
+            a.add_(1.0)
+    for _ in range(8):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return 1000.0 * start.elapsed_time(end) / (replays * n_kernels)
+
+
 def copy_probe(torch, mib):
     """A plain device-to-device copy of known size, launched a few times, so that
     hardware counter runs over this script can scale FETCH_SIZE / WRITE_SIZE."""
@@ -399,6 +426,9 @@ def bench_decode(args, torch, N, S):
     step_gbs = bytes_tok / (ms_per_step * 1e-3) / 1e9
     # the graph also holds the two staging kernels (load the token, store the output)
     n_kernels = sum(v["launches_per_step"] for v in per_kernel.values()) + 2
+    floor_us = dependent_launch_floor(torch, n_kernels)
+    log(f"dependent empty-kernel floor: {floor_us:.2f} us per kernel, "
+        f"{floor_us * n_kernels:.1f} us for the step's {n_kernels} kernels")
     return dict(
         metric=METRIC, value=1000.0 / ms_per_step, unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
@@ -414,6 +444,9 @@ def bench_decode(args, torch, N, S):
         step_roofline=dict(algorithmic_bytes_per_step=bytes_tok, achieved_gbs=step_gbs,
                            frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
         kernels_per_token=n_kernels,
+        launch_floor=dict(us_per_dependent_kernel=floor_us,
+                          us_per_step=floor_us * n_kernels,
+                          what="graph of one-element dependent kernels, replayed back to back"),
         graph_kernel_span_sum_us=span_sum_us,
         stamped_graph_ms_per_step=ms_stamped,
         kernels=per_kernel,

@@ -64,6 +64,7 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->xs = (float*)take(sizeof(float) * 5 * T);
   ws->hq = (int8_t*)take((size_t)Tk * 9 * d.I / 4);
   ws->hs = (float*)take(sizeof(float) * 4 * Tk);
+  ws->yfac = (float*)take(sizeof(float) * Tk);
   ws->y = take(sizeof(float) * Tk * d.H);
   ws->xb = (uint16_t*)take(sizeof(uint16_t) * 2 * T * d.H);
   ws->wb = (uint16_t*)take(sizeof(uint16_t) * 2 * d.E * d.H);

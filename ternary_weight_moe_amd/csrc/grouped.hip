@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     const int8_t* __restrict__ hq, const float* __restrict__ hs, int64_t Tk, int H, int NHB,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ n_tiles, uint16_t* __restrict__ y, float* __restrict__ yfac) {
   constexpr int NTH = 64 * NWV;
   constexpr int NQ = I / 128;                  // 16-byte pieces per lane and row
   constexpr int HROW = I / 64 * kPairBytes;    // digit bytes of one slot
@@ -492,14 +492,16 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     hsum[h2] = live ? (float)reinterpret_cast<const int*>(hs)[(2 * h2 + 1) * Tk + p0 + r32] : 0.f;
   }
   // The fp16 outputs are stored relative to the slot's largest part scale,
-  // times 2^-8 (the combine multiplies that factor back): |q| <= 16383 then
-  // bounds a stored value by |a_d| * I * 16383 / 256, whatever the input's
-  // magnitude (I <= 512: finite for |a_d| <= 2).
+  // times 2^-8; yfac[slot] (written by the tile's first output block) holds
+  // the factor that the combine multiplies back.  |q| <= 16383 then bounds a
+  // stored value by |a_d| * I * 16383 / 256, whatever the input's magnitude
+  // (I <= 512: finite for |a_d| <= 2).
   float smax = 0.f;
 #pragma unroll
   for (int h2 = 0; h2 < NS; ++h2) smax = fmaxf(smax, sc[h2]);
 #pragma unroll
   for (int h2 = 0; h2 < NS; ++h2) sc[h2] = smax > 0.f ? sc[h2] / smax * 0.00390625f : 0.f;
+  if (hp == 0 && tid < 32 && live) yfac[p0 + r32] = smax * 256.f;
 #pragma unroll
   for (int i = 0; i < NHU; ++i) {
     const int u = tid + NTH * i;
@@ -973,17 +975,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 // out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order
 // in fp32; a thread owns 8 consecutive outputs (y fp16: one 16-byte load per
 // slot; fp32: two).
-// ysc (fp16 form only): the per-slot h scales hs of the down projection's
-// parts ([part][scale | sum][slot], ns parts of Tk slots); the stored outputs
-// are scaled by 2^-8 / (the slot's largest part scale), undone here.
+// yfac (fp16 form only): per slot, the factor by which the down projection
+// scaled its stored outputs down (2^8 times the slot's largest h scale).
 template <typename YT>
 __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
                                                  const float* __restrict__ gate,
                                                  const int32_t* __restrict__ slot_pos, int H,
                                                  int k, float* out, const float* resid,
                                                  float* __restrict__ delta,
-                                                 const float* __restrict__ ysc, int ns,
-                                                 int64_t Tk) {
+                                                 const float* __restrict__ yfac) {
   const int64_t t = blockIdx.x;
   const int o = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (o >= H) return;
@@ -999,15 +999,6 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
       sp[j] = slot_pos[t * k + j];
       g[j] = gate[t * k + j];
     }
-  if constexpr (!std::is_same<YT, float>::value) {
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < k) {
-        float smax = 0.f;
-        for (int h2 = 0; h2 < ns; ++h2) smax = fmaxf(smax, ysc[2 * h2 * Tk + sp[j]]);
-        g[j] *= smax * 256.f;
-      }
-  }
   uint4 v[KM][NV];
 #pragma unroll
   for (int j = 0; j < KM; ++j)
@@ -1016,6 +1007,11 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
 #pragma unroll
       for (int i = 0; i < NV; ++i) v[j][i] = src[i];
     }
+  if constexpr (!std::is_same<YT, float>::value) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) g[j] *= yfac[sp[j]];
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < KM; ++j)
@@ -1108,7 +1104,7 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
       // 4 waves of 2 N-subtiles: two blocks share a CU and cover each other's waits
       launch("down_mfma", k_down_mfma<I_, 2, 4, NS_>, nt * nhb, 256,
              4 * d.H / nhb + 4 * 32 * (64 * 2 + 16), s, ws.hq, ws.hs, Tk, d.H, nhb, packed, alpha,
-             ws.tiles, ws.n_tiles, (uint16_t*)ws.y);
+             ws.tiles, ws.n_tiles, (uint16_t*)ws.y, ws.yfac);
     }
   };
   switch (d.I) {
@@ -1127,11 +1123,10 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
   const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
   if (fine)
     launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate, ws.slot_pos,
-           d.H, d.k, out, resid, delta, (const float*)nullptr, 0, Tk);
+           d.H, d.k, out, resid, delta, (const float*)nullptr);
   else
     launch("combine", k_combine<uint16_t>, cgrid, 256, 0, s, (const uint16_t*)ws.y, ws.gate,
-           ws.slot_pos, d.H, d.k, out, resid, delta, (const float*)ws.hs,
-           d.I >= 512 ? 2 : 1, Tk);
+           ws.slot_pos, d.H, d.k, out, resid, delta, (const float*)ws.yfac);
   return hipGetLastError();
 }
 
