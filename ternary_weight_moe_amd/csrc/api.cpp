@@ -34,6 +34,11 @@ constexpr int64_t kGemvAuto = 2;
 constexpr int64_t kGemvAutoStack = 2;
 
 int max_tiles(const Dims& d, int64_t T) { return (int)((T * d.k) / kTileM + d.E + 1); }
+int small_m_chunk(const Dims& d, int64_t T, int nl) {
+  if (T > 64 || nl == 2 || d.H < 1024 || (d.I != 256 && d.I != 512)) return 0;
+  return nl == 1 ? 16 : 5;
+}
+int max_chunks(const Dims& d, int64_t T) { return (int)((T * d.k) / 5 + d.E + 1); }
 
 size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   size_t off = 0;
@@ -52,11 +57,13 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   ws->n_active = (int32_t*)take(256);
   ws->n_tiles = ws->n_active ? ws->n_active + 16 : nullptr;
   ws->route_ctr = ws->n_active ? ws->n_active + 32 : nullptr;
+  ws->n_chunks = ws->n_active ? ws->n_active + 48 : nullptr;
   ws->sorted_tok = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->slot_pos = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->blk_count = (int32_t*)take(sizeof(int32_t) * nb * d.E);
   ws->blk_rank = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->tiles = (int32_t*)take(sizeof(int32_t) * 2 * (size_t)max_tiles(d, T));
+  ws->chunks = (int32_t*)take(sizeof(int32_t) * 2 * (size_t)max_chunks(d, T));
   ws->h = (float*)take(sizeof(float) * Tk * d.I);
   ws->xq = (int8_t*)take((size_t)T * 4 * d.H);
   ws->rpart = (float*)take(sizeof(float) * maple::kDecPartStride * (d.H / 64));
@@ -298,7 +305,7 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
                              (gemv || fused) ? nullptr : ws.xs + 4 * T, ws.logits, ws.xb, ws.wb,
                              ws.route_ctr, fused ? nl : 0, ws.xq, ws.xs, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
-    e = maple::launch_route(d, T, ws.logits, ws, s);
+    e = maple::launch_route(d, T, ws.logits, gemv ? 0 : maple::small_m_chunk(d, T, nl), ws, s);
     if (e != hipSuccess) return hip_fail(e, "routing launch");
     if (gemv)
       e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);

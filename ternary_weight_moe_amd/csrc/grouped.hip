@@ -970,6 +970,344 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
   }
 }
 
+// ---- small-M path: a few slots per expert (fine form and A8, T <= 64) -------------------
+
+// With a few slots per expert (batched decode: about 4), 32-slot tiles are
+// mostly padding, and the tiled kernels' stage loops wait on one memory round
+// trip per stage.  Here the 16 MFMA columns hold every (slot, limb) pair of
+// a chunk of SC = 16 / NL slots of one expert (the routing kernel's chunk
+// list): column c is limb c % NL of slot c / NL (a 16th column, with three
+// limbs, is zero).  A block loads its weights once, all at once.  The
+// weights are the A operand, so register j of lane l of an accumulator holds
+// weight row 4 (l / 16) + j and column l % 16; a slot's limbs sit in
+// neighbouring lanes and are combined by shuffles.  Work items are spread
+// over the XCDs like tiles (xcd_tile), the blocks of one chunk side by side
+// under one L2.  (Chunks of several such groups, run one after another
+// against the same weight registers, made the heavy experts' blocks the
+// tail: slower at 64 tokens.)
+
+// Gate/up: a block (8 waves) = one chunk x 128 h columns (I / 128 blocks per
+// chunk).  Wave w computes h columns [c0 + 16 w, c0 + 16 w + 16): the 16 gate
+// rows and the 16 matching up rows over all of K.  The chunk's x limbs (NL
+// SC rows of H bytes) are staged in LDS and read by all eight waves as B.
+// Load order matters: the vector-memory counter drains in order, so the x
+// loads go out before the weights (staging then waits for x alone), and
+// tokens and per-token scales come by scalar loads.
+template <int H, int I, int NL>
+__global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
+    const int8_t* xq, const float* __restrict__ xs, int T,
+    const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
+    const int32_t* __restrict__ sorted_tok, const int32_t* __restrict__ chunks,
+    const int32_t* __restrict__ n_chunks, float* __restrict__ hf) {
+  constexpr int SC = 16 / NL;       // slots per chunk
+  constexpr int NR = NL * SC;       // staged rows (15 or 16)
+  constexpr int NB = I / 128;       // blocks per chunk
+  constexpr int NSS = H / 256;      // super-steps of K (256 codes each)
+  constexpr int XROW = H + 16;      // padded LDS row: one limb of one slot
+  constexpr int UPR = H / 1024;     // 16-byte units per lane and row
+  constexpr int RPH = UPR <= 2 ? 2 : 1;  // rows per wave and staging phase
+  static_assert(NL == 1 || NL == 3, "one or three limbs");
+  __shared__ __align__(16) int8_t sX[16][XROW];
+  __shared__ float s_sx[16];
+  __shared__ int s_q[16][NL];
+  const int item = xcd_tile(blockIdx.x, *n_chunks * NB);
+  if (item < 0) return;
+  const int c = item / NB, cb = (item % NB) * 128;
+  const int2 crec = *reinterpret_cast<const int2*>(chunks + 2 * c);
+  const int e = crec.x & 0xFFFF, np = crec.x >> 16, p0 = crec.y;
+  // the wave index as a wave-uniform value: the staging tokens then come by
+  // scalar loads, outside the in-order vector-memory counter
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  // staging of rows r = wave + 8 i (slot r / NL, limb r % NL), RPH rows per
+  // phase; rows past NR and absent slots read the chunk's first slot and
+  // store zeros (loads stay unconditional)
+  uint4 xv[RPH][UPR];
+  uint32_t xm[RPH];
+  auto fetch = [&](int s0, int ph) {
+#pragma unroll
+    for (int i = 0; i < RPH; ++i) {
+      const int r = wave + 8 * (ph * RPH + i), sl = s0 + r / NL;
+      const bool live = r < NR && sl < np;
+      const int tok = sorted_tok[p0 + (live ? sl : 0)];  // wave-uniform
+      const int8_t* src = xq + ((int64_t)tok * NL + r % NL) * H + 16 * lane;
+      xm[i] = live ? ~0u : 0u;  // zeroing by a mask: no branch around the loads
+#pragma unroll
+      for (int q = 0; q < UPR; ++q) xv[i][q] = *reinterpret_cast<const uint4*>(src + 1024 * q);
+    }
+  };
+  auto store = [&](int ph) {
+#pragma unroll
+    for (int i = 0; i < RPH; ++i) {
+      const int r = wave + 8 * (ph * RPH + i);
+      const uint32_t m = xm[i];
+#pragma unroll
+      for (int q = 0; q < UPR; ++q)
+        *reinterpret_cast<uint4*>(&sX[r][16 * lane + 1024 * q]) =
+            make_uint4(xv[i][q].x & m, xv[i][q].y & m, xv[i][q].z & m, xv[i][q].w & m);
+    }
+  };
+  auto meta = [&](int s0) {  // per-slot scale and limb sums: wave 0, scalar loads
+    if (wave == 0) {
+      const int* xi = reinterpret_cast<const int*>(xs);
+#pragma unroll
+      for (int s = 0; s < SC; ++s) {
+        const int tk = sorted_tok[p0 + (s0 + s < np ? s0 + s : 0)];
+        const float sx = xs[tk] * xs[4 * T + tk];
+        int q[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) q[l] = xi[(1 + l) * T + tk];
+        if (lane == 0) {
+          s_sx[s] = sx;
+#pragma unroll
+          for (int l = 0; l < NL; ++l) s_q[s][l] = q[l];
+        }
+      }
+    }
+  };
+  fetch(0, 0);
+  // alphas of the lane's four output columns cb + 16 wave + 4 g + jj
+  const float* al = alpha + (int64_t)e * (2 * I + H) + cb + 16 * wave + 4 * g;
+  const float4 ag0 = *reinterpret_cast<const float4*>(al);
+  const float4 au0 = *reinterpret_cast<const float4*>(al + I);
+  // x and alpha loads stay ahead of the weights: x (an ordinary load) does
+  // not sink below this barrier, and the weight addresses come out of it
+  int row = cb + 16 * wave + c16;
+  asm volatile("" : "+v"(row) : : "memory");
+  // lane's weight rows: gate row cb + 16 wave + c16 and its up row (I rows
+  // on), 16 bytes of K group g per super-step
+  const uint8_t* Wg = packed + (int64_t)e * 3 * H * I / 4 + (int64_t)row * (H / 4) + 16 * g;
+  const uint8_t* Wu = Wg + (int64_t)I * (H / 4);
+  uint4 bg[NSS], bu[NSS];
+#pragma unroll
+  for (int ss = 0; ss < NSS; ++ss) {
+    bg[ss] = *reinterpret_cast<const uint4*>(Wg + 64 * ss);
+    bu[ss] = *reinterpret_cast<const uint4*>(Wu + 64 * ss);
+  }
+  {
+    constexpr int s0 = 0;
+    meta(s0);
+    store(0);
+#pragma unroll
+    for (int ph = 1; ph < 2 / RPH; ++ph) {
+      fetch(s0, ph);
+      store(ph);
+    }
+    __syncthreads();
+    v4i acc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+#pragma unroll
+    for (int ss = 0; ss < NSS; ++ss) {
+      // the weights' first use stays after the barrier: unpacked earlier, they
+      // made the staging wait for most weight loads
+      asm volatile("" : "+v"(bg[ss].x), "+v"(bg[ss].y), "+v"(bg[ss].z), "+v"(bg[ss].w));
+      asm volatile("" : "+v"(bu[ss].x), "+v"(bu[ss].y), "+v"(bu[ss].z), "+v"(bu[ss].w));
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const v4i bx = *reinterpret_cast<const v4i*>(&sX[c16][256 * ss + 64 * g + 16 * s4]);
+        acc[0] = mfma(unpack_word(word_of(bg[ss], s4)), bx, acc[0]);
+        acc[1] = mfma(unpack_word(word_of(bu[ss], s4)), bx, acc[1]);
+      }
+    }
+    // the alphas' first use stays here, after the weights are consumed (used
+    // earlier, their wait would also wait for every weight load before them)
+    float4 ag = ag0, au = au0;
+    asm volatile("" : "+v"(ag.x), "+v"(ag.y), "+v"(ag.z), "+v"(ag.w));
+    asm volatile("" : "+v"(au.x), "+v"(au.y), "+v"(au.z), "+v"(au.w));
+    // lane (g, c16) with c16 = NL s: slot s0 + s, h columns cb + 16 wave + 4 g + jj
+    const int s = c16 / NL, sl = s0 + s;
+    const bool act = c16 % NL == 0 && s < SC && sl < np;
+    float h4[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float v[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        if constexpr (NL == 1) {
+          v[n] = (float)(acc[n][jj] - s_q[s][0]);
+        } else {
+          const int a1 = __shfl_down(acc[n][jj], 1, 16), a2 = __shfl_down(acc[n][jj], 2, 16);
+          const int sq = s < SC ? s : 0;
+          v[n] = fmaf(16384.f, (float)(acc[n][jj] - s_q[sq][0]),
+                      fmaf(128.f, (float)(a1 - s_q[sq][1]), (float)(a2 - s_q[sq][2])));
+        }
+      }
+      const float sx = s_sx[s < SC ? s : 0];
+      const float gg = jj == 0 ? ag.x : jj == 1 ? ag.y : jj == 2 ? ag.z : ag.w;
+      const float uu = jj == 0 ? au.x : jj == 1 ? au.y : jj == 2 ? au.z : au.w;
+      h4[jj] = silu_fast(v[0] * (sx * gg)) * (v[1] * (sx * uu));
+    }
+    if (act)
+      *reinterpret_cast<float4*>(hf + (int64_t)(p0 + sl) * I + cb + 16 * wave + 4 * g) =
+          make_float4(h4[0], h4[1], h4[2], h4[3]);
+  }
+}
+
+// Down: a block (4 waves) = one chunk x 256 outputs (H / 256 blocks per
+// chunk).  The chunk's h rows (fp32) are coded into NL limbs in LDS, one
+// scale per slot over all I columns (wave w codes slots w, w + 4, ...);
+// wave w computes outputs [o0 + 64 w, o0 + 64 w + 64) as 4 subtiles of 16
+// weight rows, its accumulators starting at minus the column's limb sum.
+// fp32 per-slot outputs, as the tiled fine form's.  The h loads go out
+// before the weights (the coding then waits for h alone).
+template <int H, int I, int NL>
+__global__ __launch_bounds__(256) void k_sm_down(
+    const float* hf, const uint8_t* __restrict__ packed,
+    const float* __restrict__ alpha, const int32_t* __restrict__ chunks,
+    const int32_t* __restrict__ n_chunks, float* __restrict__ y) {
+  constexpr int SC = 16 / NL, NB = H / 256, NSS = I / 256;
+  constexpr int HROW = I + 16;
+  constexpr int VPL = I / 64;        // h values per lane and slot
+  constexpr int SPW = (SC + 3) / 4;  // slots coded per wave
+  constexpr float QM = NL == 1 ? 127.f : kQ3Max;
+  constexpr int QI = NL == 1 ? 127 : 2080768;
+  static_assert(NL == 1 || NL == 3, "one or three limbs");
+  static_assert(VPL == 4 || VPL == 8, "I = 256 or 512");
+  __shared__ __align__(16) int8_t sH[16][HROW];
+  __shared__ float s_sc[16];
+  __shared__ int s_sum[16];
+  const int item = xcd_tile(blockIdx.x, *n_chunks * NB);
+  if (item < 0) return;
+  const int c = item / NB, o0 = (item % NB) * 256;
+  const int2 crec = *reinterpret_cast<const int2*>(chunks + 2 * c);
+  const int e = crec.x & 0xFFFF, np = crec.x >> 16, p0 = crec.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  // h rows of the wave's slots (absent slots read the chunk's first slot and
+  // are zeroed when coded)
+  float hv[SPW][VPL];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int sl = s0 + wave + 4 * i;
+      const float* src = hf + (int64_t)(p0 + (sl < np ? sl : 0)) * I + VPL * lane;
+#pragma unroll
+      for (int q = 0; q < VPL / 4; ++q) {
+        const float4 f = reinterpret_cast<const float4*>(src)[q];
+        hv[i][4 * q] = f.x;
+        hv[i][4 * q + 1] = f.y;
+        hv[i][4 * q + 2] = f.z;
+        hv[i][4 * q + 3] = f.w;
+      }
+    }
+  };
+  fetch(0);
+  // h (an ordinary load) does not sink below this barrier, and the weight
+  // addresses come out of it: the h loads stay ahead of the weights
+  int wr = o0 + 64 * wave + c16;
+  asm volatile("" : "+v"(wr) : : "memory");
+  const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4 +
+                      (int64_t)wr * (I / 4) + 16 * g;
+  uint4 bq[4][NSS];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int ss = 0; ss < NSS; ++ss)
+      bq[b][ss] = *reinterpret_cast<const uint4*>(Wd + (int64_t)16 * b * (I / 4) + 64 * ss);
+  // a_d of the lane's output rows o0 + 64 wave + 16 b + 4 g + jj
+  const float* adp = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0 + 64 * wave + 4 * g;
+  if constexpr (NL * SC < 16) {  // the unused 16th column: zero, never rewritten
+    if (wave == 3) {
+      if constexpr (VPL == 8)
+        *reinterpret_cast<uint2*>(&sH[15][VPL * lane]) = make_uint2(0u, 0u);
+      else
+        *reinterpret_cast<uint32_t*>(&sH[15][VPL * lane]) = 0u;
+      if (lane == 0) s_sum[15] = 0;
+    }
+  }
+  {
+    constexpr int s0 = 0;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int s = wave + 4 * i;
+      if (s >= SC) break;  // wave-uniform
+      const bool live = s0 + s < np;
+      float mx = 0.f;
+#pragma unroll
+      for (int t = 0; t < VPL; ++t) {
+        if (!live) hv[i][t] = 0.f;
+        mx = fmaxf(mx, fabsf(hv[i][t]));
+      }
+      mx = wave_max_f(mx);
+      const float inv = mx > 0.f ? QM / mx : 1.f;
+      uint32_t wl[NL][VPL / 4] = {};
+      int sum[NL] = {};
+#pragma unroll
+      for (int t = 0; t < VPL; ++t) {
+        const int q = code_q(hv[i][t], inv, QI);
+        const int sh = 8 * (t & 3);
+        if constexpr (NL == 1) {
+          wl[0][t >> 2] |= (uint32_t)(q & 0xFF) << sh;
+          sum[0] += q;
+        } else {
+          int hi, mid, lo;
+          split3(q, &hi, &mid, &lo);
+          wl[0][t >> 2] |= (uint32_t)(hi & 0xFF) << sh;
+          wl[1][t >> 2] |= (uint32_t)(mid & 0xFF) << sh;
+          wl[NL - 1][t >> 2] |= (uint32_t)(lo & 0xFF) << sh;
+          sum[0] += hi;
+          sum[1] += mid;
+          sum[NL - 1] += lo;
+        }
+      }
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        if constexpr (VPL == 8)
+          *reinterpret_cast<uint2*>(&sH[NL * s + l][VPL * lane]) = make_uint2(wl[l][0], wl[l][1]);
+        else
+          *reinterpret_cast<uint32_t*>(&sH[NL * s + l][VPL * lane]) = wl[l][0];
+        sum[l] = wave_sum_i(sum[l]);
+      }
+      if (lane == 0) {
+        s_sc[s] = mx > 0.f ? mx / QM : 0.f;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) s_sum[NL * s + l] = sum[l];
+      }
+    }
+    __syncthreads();
+    const int S = s_sum[c16];
+    v4i acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = v4i{-S, -S, -S, -S};
+#pragma unroll
+    for (int ss = 0; ss < NSS; ++ss) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)  // first use after the barrier, as in the gate/up kernel
+        asm volatile("" : "+v"(bq[b][ss].x), "+v"(bq[b][ss].y), "+v"(bq[b][ss].z),
+                     "+v"(bq[b][ss].w));
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const v4i bx = *reinterpret_cast<const v4i*>(&sH[c16][256 * ss + 64 * g + 16 * s4]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b] = mfma(unpack_word(word_of(bq[b][ss], s4)), bx, acc[b]);
+      }
+    }
+    // lane (g, c16) with c16 = NL s: slot s0 + s, outputs o0 + 64 wave + 16 b + 4 g + jj
+    const int s = c16 / NL, sl = s0 + s;
+    const bool act = c16 % NL == 0 && s < SC && sl < np;
+    const float sc = s_sc[s < SC ? s : 0];
+    float* yo = y + (int64_t)(p0 + (act ? sl : 0)) * H + o0 + 64 * wave + 4 * g;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float v[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if constexpr (NL == 1) {
+          v[jj] = sc * (float)acc[b][jj];
+        } else {
+          const int a1 = __shfl_down(acc[b][jj], 1, 16), a2 = __shfl_down(acc[b][jj], 2, 16);
+          v[jj] = sc * fmaf(16384.f, (float)acc[b][jj], fmaf(128.f, (float)a1, (float)a2));
+        }
+      }
+      const float4 a = *reinterpret_cast<const float4*>(adp + 16 * b);
+      if (act)
+        *reinterpret_cast<float4*>(yo + 16 * b) =
+            make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
+    }
+  }
+}
+
 // ---- weighted combine ---------------------------------------------------------------
 
 // out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order
@@ -1077,6 +1415,36 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
                               const float* resid, float* delta, hipStream_t s) {
   const int64_t Tk = T * d.k;
   const bool fine = nl != 2;  // the fp32-h kernels: three limbs, or one (A8); else the digit form
+  if (small_m_chunk(d, T, nl) > 0) {
+    // chunks of up to 16 / nl slots (the routing kernel built their list)
+    const int mc = max_chunks(d, T);
+    auto grid = [](int64_t items) { return (unsigned)(8 * ((items + 7) / 8)); };
+    auto run_sm = [&](auto h_tag, auto i_tag) {
+      constexpr int H_ = decltype(h_tag)::value, I_ = decltype(i_tag)::value;
+      launch("gateup_mfma", nl == 1 ? k_sm_gateup<H_, I_, 1> : k_sm_gateup<H_, I_, 3>,
+             grid((int64_t)mc * (I_ / 128)), 512, 0, s, ws.xq, ws.xs, (int)T, packed, alpha,
+             ws.sorted_tok, ws.chunks, ws.n_chunks, ws.h);
+      launch("down_mfma", nl == 1 ? k_sm_down<H_, I_, 1> : k_sm_down<H_, I_, 3>,
+             grid((int64_t)mc * (H_ / 256)), 256, 0, s, (const float*)ws.h, packed, alpha,
+             ws.chunks, ws.n_chunks, (float*)ws.y);
+    };
+    auto run_h = [&](auto h_tag) {
+      if (d.I == 256)
+        run_sm(h_tag, std::integral_constant<int, 256>{});
+      else
+        run_sm(h_tag, std::integral_constant<int, 512>{});
+    };
+    switch (d.H) {
+      case 1024: run_h(std::integral_constant<int, 1024>{}); break;
+      case 2048: run_h(std::integral_constant<int, 2048>{}); break;
+      case 4096: run_h(std::integral_constant<int, 4096>{}); break;
+      default: return hipErrorNotSupported;
+    }
+    const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
+    launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate,
+           ws.slot_pos, d.H, d.k, out, resid, delta, (const float*)nullptr);
+    return hipGetLastError();
+  }
   const int mt = max_tiles(d, T);
   const unsigned nt = (unsigned)((mt + 7) & ~7);  // whole rounds of 8 XCDs
   // the down projection's outputs of a tile split over NHB blocks while the

@@ -31,6 +31,8 @@ struct Workspace {
   int32_t* blk_rank;    // [T*k]   rank of a slot inside its block and expert
   int32_t* tiles;       // [max_tiles*2] grouped-GEMM tile list (expert, m0)
   int32_t* n_tiles;     // [1]
+  int32_t* chunks;      // [max_chunks*2] small-M chunk list: expert | slots << 16, first slot
+  int32_t* n_chunks;    // [1]
   int32_t* route_ctr;   // [1]   arrival counter of the small-T routing kernel
   float* h;             // [T*k, I]  fp32 h (GEMV path, fine grouped path)
   int8_t* xq;           // [T, 4, H] coded x: three int8 limbs (fine grouped form,
@@ -93,6 +95,12 @@ void launch(const char* name, void (*kernel)(P...), dim3 grid, dim3 block, unsig
     hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<P>(args)...);
 }
 int max_tiles(const Dims& d, int64_t T);
+// Small-M path (fine form or A8 at T <= 64): an expert's slots in chunks of
+// up to 5 (three limbs: the 15 (slot, limb) pairs fill the 16 MFMA columns)
+// or 16 (one limb).  small_m_chunk gives the chunk size, or 0 where the
+// tiled kernels run instead.
+int small_m_chunk(const Dims& d, int64_t T, int nl);
+int max_chunks(const Dims& d, int64_t T);
 
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
@@ -107,7 +115,7 @@ hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          const float* Wr, const float* bias, const float* rinv, float* logits,
                          uint16_t* xb, uint16_t* wb, int32_t* route_ctr, int qnl, int8_t* xq,
                          float* xs, hipStream_t s);
-hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
+hipError_t launch_route(const Dims& d, int64_t T, const float* logits, int chunk_m, const Workspace& ws,
                         hipStream_t s);
 // One token on matrix cores (decode1_matrix_cores(d)): launch_dec_router
 // leaves the partial router dots of x in ws.rpart; launch_dec_layer then runs

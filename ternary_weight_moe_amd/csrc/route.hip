@@ -267,20 +267,26 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   }
 }
 
-// Per-expert counts -> offsets, the active-expert list and the grouped-GEMM
-// tile list (per tile: expert | slot count << 16, its first slot).  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
+// Per-expert counts -> offsets, the active-expert list, the grouped-GEMM
+// tile list (per tile: expert | slot count << 16, its first slot) and, with
+// cm > 0, the small-M chunk list in the same format (chunks of up to cm
+// slots).  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
 // the block (NWV waves, 64 NWV >= E) calls it.
 template <int NWV>
 __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
                                                int32_t* active, int32_t* n_active,
                                                int32_t* tiles, int32_t* n_tiles, int* s_off,
-                                               int* s_tmp) {
+                                               int* s_tmp, int cm = 0,
+                                               int32_t* chunks = nullptr,
+                                               int32_t* n_chunks = nullptr) {
   const int e = threadIdx.x;
-  int total, n_act, n_t;
+  int total, n_act, n_t, n_c = 0;
   const int off = block_excl_scan<NWV>(cnt, s_tmp, &total);
   const int apos = block_excl_scan<NWV>(cnt > 0 ? 1 : 0, s_tmp, &n_act);
   const int nt = (cnt + kTileM - 1) / kTileM;
   const int tpos = block_excl_scan<NWV>(nt, s_tmp, &n_t);
+  const int nc = cm > 0 ? (cnt + cm - 1) / cm : 0;
+  const int cpos = cm > 0 ? block_excl_scan<NWV>(nc, s_tmp, &n_c) : 0;  // cm: block-uniform
   if (e < E) {
     offsets[e] = off;
     s_off[e] = off;
@@ -290,11 +296,16 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
         tiles[2 * (tpos + i)] = e | min(kTileM, cnt - i * kTileM) << 16;
         tiles[2 * (tpos + i) + 1] = off + i * kTileM;
       }
+    for (int i = 0; i < nc; ++i) {
+      chunks[2 * (cpos + i)] = e | min(cm, cnt - i * cm) << 16;
+      chunks[2 * (cpos + i) + 1] = off + i * cm;
+    }
   }
   if (e == 0) {
     offsets[E] = total;
     *n_active = n_act;
     if (n_tiles) *n_tiles = n_t;
+    if (cm > 0) *n_chunks = n_c;
   }
 }
 
@@ -310,7 +321,8 @@ __global__ __launch_bounds__(256) void k_route_small(
     float* __restrict__ gate, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_tok,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-    int32_t* __restrict__ ctr) {
+    int32_t* __restrict__ ctr, int cm, int32_t* __restrict__ chunks,
+    int32_t* __restrict__ n_chunks) {
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
   __shared__ int s_off[256];
@@ -345,7 +357,8 @@ __global__ __launch_bounds__(256) void k_route_small(
   for (int q = tid; q < T * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   const int cnt = (tid < E) ? __popcll(s_mask[tid]) : 0;
-  finish_offsets<4>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp);
+  finish_offsets<4>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp, cm, chunks,
+                    n_chunks);
   __syncthreads();
   for (int q = tid; q < T * k; q += 256) {
     const int tq = q / k, e = s_idx[q];
@@ -495,13 +508,13 @@ hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, c
   return hipGetLastError();
 }
 
-hipError_t launch_route(const Dims& d, int64_t T, const float* logits, const Workspace& ws,
+hipError_t launch_route(const Dims& d, int64_t T, const float* logits, int chunk_m, const Workspace& ws,
                         hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
   if (T <= 64) {
     launch("route_small", k_route_small, (unsigned)((T + 3) / 4), 256, 0, s, logits, (int)T, d.E,
            d.k, renorm, ws.idx, ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok,
-           ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr);
+           ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr, chunk_m, ws.chunks, ws.n_chunks);
     return hipGetLastError();
   }
   const int nb = (int)((T + 63) / 64);
