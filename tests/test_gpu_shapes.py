@@ -50,3 +50,20 @@ def test_shape_every_path(H, I):
     check_layer(w, L, x40, flags=N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS,
                 what=f"H={H} I={I} grouped fine")
     check_a8(w, L, x40, what=f"H={H} I={I} a8")
+
+
+@pytest.mark.parametrize("a8", [False, True], ids=["fine", "a8"])
+def test_small_m_degenerate_routing(a8):
+    """The small-M chunking at its extremes, hidden 1024, inter 256, 64
+    tokens: E == k (every expert holds all 64 slots: 13 chunks of 5, or 4 of
+    16 with one limb) and k = 1 (64 slots over 16 experts)."""
+    for E, k in ((8, 8), (16, 1)):
+        w = workload("tiny_layer", name=f"small_m_{E}_{k}", hidden=1024, inter=256,
+                     n_experts=E, top_k=k, n_tokens=64, x_bf16=True, seed=7100 + E + k)
+        L = Layer(w, 0)
+        x, _ = layer_tokens_with_gap(w, L, 64, token0=400)
+        if a8:
+            check_a8(w, L, x, what=f"small-M a8 E={E} k={k}")
+        else:
+            check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS,
+                        what=f"small-M fine E={E} k={k}")
