@@ -7,7 +7,8 @@ graph step per token, 256 staged tokens with independent seeded bf16 inputs.
 A step is one token through all 24 pre-norm blocks: router, softmax/top-8,
 grouping, gate/up + SwiGLU, down projection and weighted combine with the
 residual.  ``--workload prefill_4096`` (or ``prefill_16384``) times one
-layer over that many tokens instead; a step is then one layer call.
+layer over that many tokens instead; a step is then one layer call, replayed
+from a captured HIP graph (the eager call's time is reported beside it).
 ``--workload batched_stack_zipf`` runs 64 tokens per step through the stack
 with Zipf-skewed routing; ``--workload flashhead_decode`` times the clustered
 output head alone, one token per call; ``--workload hybrid_attn_decode`` times
@@ -850,12 +851,23 @@ def bench_prefill(args, torch, N, S):
     ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
     out = torch.empty(T, H, dtype=torch.float32, device="cuda")
 
-    def step():
+    def step(st=None):
         N.maple_moe_layer_forward(d, T, x, layer["Wr"], layer["bias"], layer["packed"],
-                                  layer["alpha"], out, ws)
-    ms_per_step = timed(torch, step, args.steps, args.warmup)
+                                  layer["alpha"], out, ws, stream=st)
+    ms_eager = timed(torch, step, args.steps, args.warmup)
+    # the same call captured into a HIP graph: the host launches of the layer's
+    # ten short kernels no longer pace it
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        step(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        step(st)
+    ms_per_step = timed(torch, graph.replay, args.steps, args.warmup)
     assert torch.isfinite(out).all().item(), "non-finite prefill output"
-    log(f"{args.workload}: {T / ms_per_step * 1000:.0f} tok/s, {ms_per_step * 1000:.1f} us/layer")
+    log(f"{args.workload}: {T / ms_per_step * 1000:.0f} tok/s, {ms_per_step * 1000:.1f} us/layer "
+        f"(graph replays; eager calls {ms_eager * 1000:.1f} us)")
     prof = profile_kernels(N, step, min(args.steps, 20))
     per_kernel = {kn: dict(launches=n, avg_us=1000 * avg, ops=prefill_ops(kn, H, k, I, T))
                   for kn, (n, avg) in prof.items()}
@@ -899,7 +911,8 @@ def bench_prefill(args, torch, N, S):
         dtype=("int8 MFMA (int8 activations) + f32" if a8
                else "fp4 x fp6 MFMA (three six-bit digits) + f32"),
         config=dict(workload=args.workload, hidden=H, experts=E, top_k=k, inter=I, tokens=T,
-                    layers=1, step="one layer call", padded_slots=padded,
+                    layers=1, step="one layer call, replayed from a captured HIP graph",
+                    eager_ms_per_step=ms_eager, padded_slots=padded,
                     activations=("int8 (one limb)" if a8
                                  else "fp32 coded in three fp6 digits (14-bit integers)")),
         roofline=roof,

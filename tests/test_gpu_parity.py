@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 from gpu_helpers import (Layer, assert_close, check_layer, dims_for,  # noqa: E402
-                         layer_tokens_with_gap, log, run_layer, workload)
+                         layer_tokens_with_gap, log, run_layer, workload, x_device)
 from ternary_weight_moe_amd import _native as N  # noqa: E402
 from ternary_weight_moe_amd import synth as S  # noqa: E402
 
@@ -258,3 +258,43 @@ def test_grouped_large_activations(dec, gflags):
     assert np.array_equal(np.sort(dbg["idx"], 1), np.sort(ref["idx"], 1))
     log(f"max |out| {np.abs(ref['out']).max():.3e}")
     assert_close(got / 1e4, ref["out"] / 1e4, "x100 inputs")
+
+
+# ---- the layer call captured into a HIP graph -----------------------------------------
+
+@pytest.mark.parametrize("flags", [0, N.MAPLE_FINE_LIMBS, N.MAPLE_ACT_INT8],
+                         ids=["fast", "fine", "a8"])
+def test_prefill_layer_graph_replays(flags):
+    """The 4096-token layer call captured into a HIP graph on the caller's
+    stream (every launch of the library goes onto that stream, and nothing in
+    it is a memset) and replayed three times, with eager work and a
+    synchronisation between replays: each replay matches the eager call bit
+    for bit."""
+    w = S.WORKLOADS["prefill_4096"]
+    T, H = w.n_tokens, w.hidden
+    L = Layer(w, 0)
+    x = x_device(w, S.gen_x(w, T, token0=30000))
+    d = dims_for(w, flags)
+    ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    out_e = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    N.maple_moe_layer_forward(d, T, x, L.d_Wr, L.d_bias, L.packed, L.d_alpha, out_e, ws)
+    torch.cuda.synchronize()
+    out_g = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        N.maple_moe_layer_forward(d, T, x, L.d_Wr, L.d_bias, L.packed, L.d_alpha, out_g, ws,
+                                  stream=st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        N.maple_moe_layer_forward(d, T, x, L.d_Wr, L.d_bias, L.packed, L.d_alpha, out_g, ws,
+                                  stream=st)
+    for rep in range(3):
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        junk = torch.randn(1024, 1024, device="cuda")
+        (junk @ junk).sum().item()  # eager work and a sync between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep} differs from the eager call"
+    log(f"flags {flags:#x}: 3 graph replays equal to the eager call")
