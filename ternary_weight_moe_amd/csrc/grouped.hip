@@ -782,14 +782,17 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
 // [w TM/NWV, (w+1) TM/NWV)).  NHB blocks share a tile, each taking H / NHB
 // consecutive outputs in chunks of CH = 64 NWV; like the gate/up parts they
 // are consecutive blocks of one XCD.  Wave w owns 4 subtiles of 16 outputs per
-// chunk; its accumulators start at minus the slot's limb row sums, and the fp32
+// chunk; its accumulators start at minus the slot's limb row sums, and the
 // outputs are stored straight from them (four consecutive outputs of one slot
-// per lane and store).
+// per lane and store): fp32 with three limbs; with one limb (A8, whose coding
+// error is near 1e-2 anyway) fp16 relative to the slot's scale times 2^8
+// (yfac[slot], written by the tile's first output block, holds that factor),
+// which halves the traffic of the outputs and of the combine that reads them.
 template <int I, int NWV, int NL>
 __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     const float* __restrict__ hf, int H, int NHB, const uint8_t* __restrict__ packed,
     const float* __restrict__ alpha, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, float* __restrict__ y) {
+    const int32_t* __restrict__ n_tiles, float* __restrict__ y, float* __restrict__ yfac) {
   constexpr int NTH = 64 * NWV;
   constexpr int PW = I >= 256 ? 4 : 2;  // words per lane and piece (I = 128: 128-code pieces)
   constexpr int NQ = I / (64 * PW);     // pieces of a row (one load of PW words each)
@@ -898,6 +901,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
   for (int h2 = 0; h2 < 2; ++h2) {
     const int m = 16 * h2 + r16;
     sc[h2] = s_sc[m];
+    // one limb: the factor of the slot's fp16 outputs, stored once per slot
+    if (NL == 1 && hp == 0 && wave == 0 && kg == 0 && m < np) yfac[p0 + m] = sc[h2] * 256.f;
 #pragma unroll
     for (int l = 0; l < NL; ++l) sum[h2][l] = s_sum[l][m];
   }
@@ -948,7 +953,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     for (int h2 = 0; h2 < 2; ++h2) {
       if (h2 == 1 && !two) break;
       const int m = 16 * h2 + r16;
-      float* yrow = y + (int64_t)(p0 + m) * H + o0 + c * CH + 64 * wave;
+      const int64_t yo = (int64_t)(p0 + m) * H + o0 + c * CH + 64 * wave;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int ol = 16 * b + 4 * kg;
@@ -957,14 +962,19 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (NL == 1)
-            v[j] = sc[h2] * (float)acc[h2][0][b][j];
+            v[j] = 0.00390625f * (float)acc[h2][0][b][j];  // the slot's scale goes to yfac
           else
             v[j] = sc[h2] * fmaf(16384.f, (float)acc[h2][0][b][j],
                                  fmaf(128.f, (float)acc[h2][1][b][j], (float)acc[h2][2][b][j]));
         }
-        if (m < np)
-          *reinterpret_cast<float4*>(yrow + ol) =
-              make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
+        if (m < np) {
+          if constexpr (NL == 1)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + yo + ol) =
+                make_uint2(pack_f16(a.x * v[0], a.y * v[1]), pack_f16(a.z * v[2], a.w * v[3]));
+          else
+            *reinterpret_cast<float4*>(y + yo + ol) =
+                make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
+        }
       }
     }
   }
@@ -1463,7 +1473,7 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
              ws.n_tiles, ws.h);
       launch("down_mfma", nl == 1 ? k_down3_mfma<I_, 4, 1> : k_down3_mfma<I_, 4, 3>, nt * nhb, 256,
              4 * d.H / nhb, s, ws.h, d.H, nhb, packed, alpha, ws.tiles, ws.n_tiles,
-             (float*)ws.y);
+             (float*)ws.y, ws.yfac);
     } else {
       // I = 512: h in two column parts (two gate/up blocks per tile, two per CU)
       constexpr int NS_ = I_ >= 512 ? 2 : 1;
@@ -1489,7 +1499,7 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
       return hipErrorNotSupported;
   }
   const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
-  if (fine)
+  if (nl == 3)  // fp32 per-slot outputs; the fast form and A8 store scaled fp16
     launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate, ws.slot_pos,
            d.H, d.k, out, resid, delta, (const float*)nullptr);
   else

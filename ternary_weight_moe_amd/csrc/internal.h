@@ -44,9 +44,9 @@ struct Workspace {
                         //           three planes) | 1/rms(x) at plane 4
   int8_t* hq;           // [T*k, 9I/4] h in the digit layout (fast form)
   float* hs;            // [2, 2, T*k] per h column part: scale per slot | sum q (int bits)
-  float* yfac;          // [T*k] fast form: factor of each slot's scaled fp16 outputs
+  float* yfac;          // [T*k] fast form and tiled A8: factor of each slot's scaled fp16 outputs
   void* y;              // [T*k, H]  expert outputs before the combine (grouped path):
-                        //           fp16 in the fast form, fp32 in the fine form
+                        //           fp16 in the fast form and tiled A8, else fp32
   uint16_t* xb;         // [2, T, H] bf16 hi/lo planes of fp32 x (large-T router)
   uint16_t* wb;         // [2, E, H] bf16 hi/lo planes of the router (large-T router)
   size_t bytes;
