@@ -50,6 +50,7 @@ size_t carve(const Dims& d, int64_t T, char* base, Workspace* ws) {
   const int64_t Tk = T * d.k;
   const int64_t nb = (T + 63) / 64;
   ws->logits = (float*)take(sizeof(float) * T * d.E);
+  ws->lpart = (float*)take(T <= 64 ? sizeof(float) * (d.H / 128) * T * (256 + 1) : 0);
   ws->idx = (int32_t*)take(sizeof(int32_t) * Tk);
   ws->gate = (float*)take(sizeof(float) * Tk);
   ws->offsets = (int32_t*)take(sizeof(int32_t) * (d.E + 1));
@@ -295,17 +296,18 @@ int run_layer(const Dims& d, int64_t T, const void* x, bool x_bf16, const float*
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   } else {
     // limbs, scales and 1/rms of x for the grouped GEMMs (and the large-T
-    // router): coded by the small-T router as it reads x, else by their own kernel
+    // router): coded by blocks of the small-T routing kernel, else by their own kernel
     const bool fused = !gemv && maple::router_codes_x(T);
     if (!gemv && !fused) {
       e = maple::launch_quant_x(d, T, x, x_bf16, nl, ws, s);
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }
-    e = maple::launch_router(d, T, x, x_bf16, Wr, bias,
-                             (gemv || fused) ? nullptr : ws.xs + 4 * T, ws.logits, ws.xb, ws.wb,
-                             ws.route_ctr, fused ? nl : 0, ws.xq, ws.xs, s);
+    const float* rinv = (gemv || fused) ? nullptr : ws.xs + 4 * T;
+    e = maple::launch_router(d, T, x, x_bf16, Wr, bias, rinv, ws, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
-    e = maple::launch_route(d, T, ws.logits, gemv ? 0 : maple::small_m_chunk(d, T, nl), ws, s);
+    e = maple::launch_route(d, T, x, x_bf16, bias, rinv, fused ? nl : 0,
+                            gemv ? 0 : maple::small_m_chunk(d, T, nl), dbg && dbg->logits, ws,
+                            s);
     if (e != hipSuccess) return hip_fail(e, "routing launch");
     if (gemv)
       e = maple::launch_gemv_ffn(d, T, x, x_bf16, packed, alpha, ws, out, resid, delta, s);

@@ -20,6 +20,9 @@ constexpr int kDecPartStride = 288;
 // another and reuse it).
 struct Workspace {
   float* logits;        // [T,E]
+  float* lpart;         // T <= 64: [H/128, T, 256] partial logits over K slices of 128
+                        //           (expert e at 4 (e % 64) + e / 64), then [H/128, T]
+                        //           the slices' sums of x^2
   int32_t* idx;         // [T,k]
   float* gate;          // [T,k]
   int32_t* offsets;     // [E+1]
@@ -105,18 +108,23 @@ int max_chunks(const Dims& d, int64_t T);
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
-// xb, wb: bf16-plane scratch (ws.xb, ws.wb) used above the small-T sizes;
-// route_ctr: the small-T routing kernel's arrival counter (zeroed here);
-// qnl > 0 (only where router_codes_x(T)): the router also codes x as
-// launch_quant_x does for nl = qnl (int8 limbs, or digits for 2), xq / xs as
-// it writes them (1/rms computed from x)
+// Router and routing.  Small T (<= 64): launch_router leaves partial logits
+// over K slices in ws.lpart (and zeroes ws.route_ctr, the routing kernel's
+// arrival counter); launch_route sums them, applies 1/rms (rinv, else from x
+// when the layer normalises) and the bias, and routes, storing ws.logits only
+// with store_logits (a debug copy wants them).
+// Larger T: launch_router stores ws.logits itself (bias and rinv applied;
+// rinv required with MAPLE_RMS_NORM; ws.xb, ws.wb hold bf16 planes) and
+// launch_route reads them.  qnl > 0 (only where router_codes_x(T)): the
+// routing kernel also codes x as launch_quant_x does for nl = qnl (int8
+// limbs, or digits for 2), xq / xs as it writes them (1/rms computed from x).
 bool router_codes_x(int64_t T);
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
-                         const float* Wr, const float* bias, const float* rinv, float* logits,
-                         uint16_t* xb, uint16_t* wb, int32_t* route_ctr, int qnl, int8_t* xq,
-                         float* xs, hipStream_t s);
-hipError_t launch_route(const Dims& d, int64_t T, const float* logits, int chunk_m, const Workspace& ws,
-                        hipStream_t s);
+                         const float* Wr, const float* bias, const float* rinv,
+                         const Workspace& ws, hipStream_t s);
+hipError_t launch_route(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* bias,
+                        const float* rinv, int qnl, int chunk_m, bool store_logits,
+                        const Workspace& ws, hipStream_t s);
 // One token on matrix cores (decode1_matrix_cores(d)): launch_dec_router
 // leaves the partial router dots of x in ws.rpart; launch_dec_layer then runs
 // one layer (router Wr) on x (whose partial dots are in ws.rpart) into out (= resid +

@@ -42,77 +42,93 @@ __device__ __forceinline__ float4 load_x4(const void* x, int64_t off) {
 
 // ---- router logits ---------------------------------------------------------
 
-// Small T (<= 64): a block is 4 experts (one per wave) x TT tokens.  Lane j
-// keeps its expert row's pieces [4j + 256i, +4), i < NPL = H / 256, in
-// registers and reads the same pieces of the TT token rows, all loads in
-// flight together (the block's waves read the same rows: cache hits).
-// 1/rms(x) comes from rinv when given, else from the rows read here.  Block
-// (0,0) also zeroes the arrival counter of the routing kernel that runs next
-// on the stream.
-template <bool BF16, int NPL>
-__global__ __launch_bounds__(256) void k_router_small(const void* __restrict__ x, int T,
-                                                      const float* __restrict__ Wr,
-                                                      const float* __restrict__ bias, int E,
-                                                      int norm, const float* __restrict__ rinv,
-                                                      float* __restrict__ logits,
-                                                      int32_t* __restrict__ route_ctr, int qnl,
-                                                      int8_t* __restrict__ xq,
-                                                      float* __restrict__ xs) {
-  constexpr int H = 256 * NPL;
-  constexpr int TT = NPL >= 16 ? 2 : 4;           // tokens per wave
-  constexpr int LB = TT == 4 ? 4 : 5;             // lane bits below the token index
-  const int lane = threadIdx.x & 63;
-  // with qnl, block x = 0 of each token group codes x (dispatched first) and
-  // the router blocks follow
-  const int e = (blockIdx.x - (qnl ? 1 : 0)) * 4 + (threadIdx.x >> 6);
-  const int t0 = blockIdx.y * TT;
-  if (route_ctr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *route_ctr = 0;
-  auto router_part = [&]() {
-    float4 w[NPL];
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Small T (<= 64): partial logits over K slices of 128, on the fp32 matrix
+// cores.  Block q = (slice ks, expert group eg of 16) has 4 waves; wave w
+// multiplies the group's 16 rows of W by tokens [16w, 16w + 16) over the
+// slice with 32 v_mfma_f32_16x16x4_f32, both operands loaded straight from
+// memory: lane l takes row l % 16 of each and the 32 columns
+// 128 ks + 32 (l / 16) + [0, 32), so the contraction pairs the same column on
+// both sides (the column order inside an MFMA step does not matter to a
+// sum).  Products are exact and sums fp32, as in a plain fp32 dot product.
+// Outputs: part[ks][t][p(e)] in rows of 256 with p(e) = 4 (e % 64) + e / 64,
+// so that one 16-byte load gives lane j of the routing kernel its experts
+// j + 64 m, m < 4 (E <= 256); and with ssp, sum of x^2 over the slice
+// (ssp[ks][t], written by group 0).  The routing kernel sums the S = H / 128
+// slices in order and applies 1/rms and the bias.  Blocks are laid out
+// slice-major and dealt to the 8 XCDs in contiguous ranges (the dispatcher
+// sends block b to XCD b % 8), so each XCD's L2 fetches only its own slices
+// of W and x.  Block 0 also zeroes the arrival counter of the routing kernel
+// that runs next on the stream.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_router_split(const void* __restrict__ x, int T, int H,
+                                                      const float* __restrict__ Wr, int E,
+                                                      int per_xcd, float* __restrict__ part,
+                                                      float* __restrict__ ssp,
+                                                      int32_t* __restrict__ route_ctr) {
+  if (route_ctr && blockIdx.x == 0 && threadIdx.x == 0) *route_ctr = 0;
+  const int S = H / 128, EG = (E + 15) / 16;
+  const int q = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (q >= S * EG) return;  // block-uniform
+  const int ks = q / EG, eg = q % EG;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int t0 = (threadIdx.x >> 6) * 16;
+  if (t0 >= T) return;  // wave-uniform; no block barrier follows
+  const int kb = 128 * ks + 32 * g;
+  const int t = min(t0 + r16, T - 1);  // rows past T repeat the last one (not stored)
+  const float* wrow = Wr + (int64_t)min(16 * eg + r16, E - 1) * H + kb;
+  float xv[32];
+  if constexpr (BF16) {
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(x) + (int64_t)t * H + kb;
+    uint4 u[4];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      w[i] = *reinterpret_cast<const float4*>(Wr + (int64_t)e * H + 4 * lane + 256 * i);
-    const bool own_rms = norm && !rinv;
-    float acc[TT], ss[TT];
+    for (int n = 0; n < 4; ++n) u[n] = *reinterpret_cast<const uint4*>(xr + 8 * n);
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = min(t0 + tt, T - 1);  // rows past T repeat the last one (discarded)
-      float a = 0.f, q = 0.f;
+    for (int n = 0; n < 4; ++n) {
+      const uint32_t wd[4] = {u[n].x, u[n].y, u[n].z, u[n].w};
 #pragma unroll
-      for (int i = 0; i < NPL; ++i) {
-        const float4 xv = load_x4<BF16>(x, (int64_t)t * H + 4 * lane + 256 * i);
-        a = fmaf(w[i].x, xv.x, fmaf(w[i].y, xv.y, fmaf(w[i].z, xv.z, fmaf(w[i].w, xv.w, a))));
-        if (own_rms) q = fmaf(xv.x, xv.x, fmaf(xv.y, xv.y, fmaf(xv.z, xv.z, fmaf(xv.w, xv.w, q))));
+      for (int c = 0; c < 4; ++c) {
+        xv[8 * n + 2 * c] = __uint_as_float(wd[c] << 16);
+        xv[8 * n + 2 * c + 1] = __uint_as_float(wd[c] & 0xFFFF0000u);
       }
-      acc[tt] = a;
-      ss[tt] = q;
     }
-    const float dot = wave_sum_n<TT>(acc, lane);
-    const int t = t0 + (lane >> LB);
-    float r = 1.f;
-    if (own_rms) r = rsqrtf(wave_sum_n<TT>(ss, lane) / (float)H + MAPLE_RMS_EPS);
-    else if (norm) r = rinv[min(t, T - 1)];
-    if ((lane & ((1 << LB) - 1)) == 0 && t < T)
-      logits[(int64_t)t * E + e] = dot * r + (bias ? bias[e] : 0.f);
-  };
-  // qnl > 0: one more block per token group (the first in x) codes the
-  // group's rows for the grouped kernels (qnl int8 limbs, or digits for 2), wave w token
-  // t0 + w, alongside the router blocks; this saves a kernel that would read
-  // x once more
-  if (qnl && blockIdx.x == 0) {
-    const int tq = t0 + (threadIdx.x >> 6);
-    if ((threadIdx.x >> 6) < TT && tq < T) {  // wave-uniform
-      if (qnl == 1)
-        quant_row<BF16, 1, H>(x, tq, T, H, norm, xq, xs, lane);
-      else if (qnl == 2)  // the fast form's digit layout
-        quant_row6<BF16, H>(x, tq, T, H, norm, xq, xs, lane);
-      else
-        quant_row<BF16, 3, H>(x, tq, T, H, norm, xq, xs, lane);
+  } else {
+    const float* xr = reinterpret_cast<const float*>(x) + (int64_t)t * H + kb;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + 4 * n);
+      xv[4 * n] = v.x, xv[4 * n + 1] = v.y, xv[4 * n + 2] = v.z, xv[4 * n + 3] = v.w;
     }
-    return;
   }
-  if (e >= E) return;  // wave-uniform; no block barrier follows
-  router_part();
+  float4 wv[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) wv[n] = *reinterpret_cast<const float4*>(wrow + 4 * n);
+  // two accumulators, so consecutive MFMAs do not wait on each other
+  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[n].x, xv[4 * n], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[n].y, xv[4 * n + 1], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[n].z, xv[4 * n + 2], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[n].w, xv[4 * n + 3], acc1, 0, 0, 0);
+  }
+  // lane l holds experts 16 eg + 4 (l / 16) + [0, 4) of token t0 + l % 16
+  const int tt = t0 + r16, e0 = 16 * eg + 4 * g;  // e0 % 4 == 0: p(e0 + r) = p(e0) + 4 r
+  if (tt < T) {
+    float* dst = part + ((int64_t)ks * T + tt) * 256 + 4 * (e0 & 63) + (e0 >> 6);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (e0 + r < E) dst[4 * r] = acc0[r] + acc1[r];
+  }
+  if (ssp && eg == 0) {
+    float q2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) q2 = fmaf(xv[j], xv[j], q2);
+    q2 += __shfl_xor(q2, 16, 64);
+    q2 += __shfl_xor(q2, 32, 64);
+    if (g == 0 && tt < T) ssp[(int64_t)ks * T + tt] = q2;
+  }
 }
 
 // ---- Large T: router logits on the matrix cores -----------------------------
@@ -267,26 +283,66 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   }
 }
 
+// Exclusive scan over a block of NWV waves of four 16-bit counters packed in
+// a 64-bit word (no field's total may pass 65535, so no carry crosses a
+// field).  s_tmp: NWV words of LDS, free again only after a block barrier.
+template <int NWV>
+__device__ __forceinline__ unsigned long long block_excl_scan4x16(unsigned long long v,
+                                                                  unsigned long long* s_tmp,
+                                                                  unsigned long long* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  unsigned long long base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    base += w < wave ? s_tmp[w] : 0ull;
+    all += s_tmp[w];
+  }
+  *total = all;
+  return base + inc - v;
+}
+
 // Per-expert counts -> offsets, the active-expert list, the grouped-GEMM
 // tile list (per tile: expert | slot count << 16, its first slot) and, with
 // cm > 0, the small-M chunk list in the same format (chunks of up to cm
 // slots).  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
-// the block (NWV waves, 64 NWV >= E) calls it.
-template <int NWV>
+// the block (NWV waves, 64 NWV >= E) calls it.  PACKED (at most 64 tokens,
+// so every count and total is below 2^16): the four scans run as one over
+// 16-bit fields (s_tmp64, one barrier) instead of one after another (s_tmp).
+template <int NWV, bool PACKED = false>
 __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
                                                int32_t* active, int32_t* n_active,
                                                int32_t* tiles, int32_t* n_tiles, int* s_off,
                                                int* s_tmp, int cm = 0,
                                                int32_t* chunks = nullptr,
-                                               int32_t* n_chunks = nullptr) {
+                                               int32_t* n_chunks = nullptr,
+                                               unsigned long long* s_tmp64 = nullptr) {
   const int e = threadIdx.x;
-  int total, n_act, n_t, n_c = 0;
-  const int off = block_excl_scan<NWV>(cnt, s_tmp, &total);
-  const int apos = block_excl_scan<NWV>(cnt > 0 ? 1 : 0, s_tmp, &n_act);
   const int nt = (cnt + kTileM - 1) / kTileM;
-  const int tpos = block_excl_scan<NWV>(nt, s_tmp, &n_t);
   const int nc = cm > 0 ? (cnt + cm - 1) / cm : 0;
-  const int cpos = cm > 0 ? block_excl_scan<NWV>(nc, s_tmp, &n_c) : 0;  // cm: block-uniform
+  int total, n_act, n_t, n_c = 0, off, apos, tpos, cpos = 0;
+  if constexpr (PACKED) {
+    const unsigned long long v = (unsigned long long)cnt | (unsigned long long)(cnt > 0) << 16 |
+                                 (unsigned long long)nt << 32 | (unsigned long long)nc << 48;
+    unsigned long long all;
+    const unsigned long long ex = block_excl_scan4x16<NWV>(v, s_tmp64, &all);
+    off = (int)(ex & 0xFFFF), apos = (int)(ex >> 16 & 0xFFFF);
+    tpos = (int)(ex >> 32 & 0xFFFF), cpos = (int)(ex >> 48);
+    total = (int)(all & 0xFFFF), n_act = (int)(all >> 16 & 0xFFFF);
+    n_t = (int)(all >> 32 & 0xFFFF), n_c = (int)(all >> 48);
+  } else {
+    off = block_excl_scan<NWV>(cnt, s_tmp, &total);
+    apos = block_excl_scan<NWV>(cnt > 0 ? 1 : 0, s_tmp, &n_act);
+    tpos = block_excl_scan<NWV>(nt, s_tmp, &n_t);
+    if (cm > 0) cpos = block_excl_scan<NWV>(nc, s_tmp, &n_c);  // cm: block-uniform
+  }
   if (e < E) {
     offsets[e] = off;
     s_off[e] = off;
@@ -311,31 +367,84 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
 
 // ---- T <= 64: selection in parallel, grouping by the last block to finish ----------
 
-// One wave per token, 4 per block.  Each block publishes its selections and
-// takes a ticket from an arrival counter (zeroed by the router kernel before
-// this kernel starts); the block with the last ticket then sees every
-// selection and counts (one 64-bit token mask per expert), scans and scatters
-// for all T tokens.  Nothing waits on another block.
+// One wave per token, 4 per block (the first nt = ceil(T / 4) blocks).  The
+// wave sums its token's S = H / 128 partial logits in slice order, scales by 1/rms
+// (rinv[t] when given, else from the slices' sums of x^2 when norm), adds the
+// bias (storing the logits when logits is given), then selects.  Each block publishes its
+// selections and takes a ticket from an arrival counter (zeroed by the router
+// kernel before this kernel starts); the block with the last ticket then sees
+// every selection and counts (one 64-bit token mask per expert), scans and
+// scatters for all T tokens.  Nothing waits on another block.
+// qnl > 0: nt more blocks code x for the grouped kernels (qnl int8 limbs, or
+// digits for 2), wave w of block nt + j token 4 j + w; they take no ticket,
+// and their work overlaps the last block's grouping.
+template <bool BF16, int H>
 __global__ __launch_bounds__(256) void k_route_small(
-    const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ idx,
+    const float* __restrict__ part, const float* __restrict__ ssp, int norm,
+    const float* __restrict__ rinv, const float* __restrict__ bias, float* __restrict__ logits,
+    int T, int E, int k, int renorm, int32_t* __restrict__ idx,
     float* __restrict__ gate, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_tok,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
     int32_t* __restrict__ ctr, int cm, int32_t* __restrict__ chunks,
-    int32_t* __restrict__ n_chunks) {
+    int32_t* __restrict__ n_chunks, int qnl, const void* __restrict__ x,
+    int8_t* __restrict__ xq, float* __restrict__ xs) {
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
   __shared__ int s_off[256];
-  __shared__ int s_tmp[4];
+  __shared__ unsigned long long s_tmp64[4];
   __shared__ int s_last;
+  constexpr int S = H / 128;  // K slices of the partial logits
   const int tid = threadIdx.x, lane = tid & 63;
+  const int nt = (T + 3) / 4;
+  if ((int)blockIdx.x >= nt) {  // block-uniform: a coding block
+    const int tq = ((int)blockIdx.x - nt) * 4 + (tid >> 6);
+    if (tq < T) {  // wave-uniform
+      if (qnl == 1)
+        quant_row<BF16, 1, H>(x, tq, T, H, norm, xq, xs, lane);
+      else if (qnl == 2)  // the fast form's digit layout
+        quant_row6<BF16, H>(x, tq, T, H, norm, xq, xs, lane);
+      else
+        quant_row<BF16, 3, H>(x, tq, T, H, norm, xq, xs, lane);
+    }
+    return;
+  }
   const int t = blockIdx.x * 4 + (tid >> 6);
   if (t < T) {  // wave-uniform
+    // the bias, 1/rms or lane j's slice sum of x^2, then up to 16 slices'
+    // partials in flight at once (16-byte loads: experts j + 64 m), summed in
+    // slice order; everything is issued before the first wait
+    float bv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bv[m] = (bias && lane + 64 * m < E) ? bias[lane + 64 * m] : 0.f;
+    const float rt = rinv ? rinv[t] : 1.f;
+    const float qj = (ssp && lane < S) ? ssp[(int64_t)lane * T + t] : 0.f;
+    constexpr int SB = S < 16 ? S : 16;
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      float4 v[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        v[j] = *reinterpret_cast<const float4*>(part + ((int64_t)(s0 + j) * T + t) * 256 + 4 * lane);
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        sum[0] += v[j].x;
+        sum[1] += v[j].y;
+        sum[2] += v[j].z;
+        sum[3] += v[j].w;
+      }
+    }
+    float r = rt;
+    if (!rinv && norm) r = rsqrtf(wave_sum_f(qj) / (float)H + MAPLE_RMS_EPS);
     float lv[1][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = lane + 64 * m;
-      lv[0][m] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+      lv[0][m] = -INFINITY;  // slots past E hold stale partials: masked here
+      if (e < E) {
+        lv[0][m] = sum[m] * r + bv[m];
+        if (logits) logits[(int64_t)t * E + e] = lv[0][m];
+      }
     }
     int i[1];
     float g[1];
@@ -347,7 +456,7 @@ __global__ __launch_bounds__(256) void k_route_small(
   }
   __threadfence();  // release the selections before the ticket
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
+  if (tid == 0) s_last = atomicAdd(ctr, 1) == nt - 1;
   __syncthreads();
   if (!s_last) return;  // block-uniform
   __threadfence();      // acquire every block's selections
@@ -357,8 +466,8 @@ __global__ __launch_bounds__(256) void k_route_small(
   for (int q = tid; q < T * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   const int cnt = (tid < E) ? __popcll(s_mask[tid]) : 0;
-  finish_offsets<4>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, s_tmp, cm, chunks,
-                    n_chunks);
+  finish_offsets<4, true>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, nullptr, cm,
+                          chunks, n_chunks, s_tmp64);
   __syncthreads();
   for (int q = tid; q < T * k; q += 256) {
     const int tq = q / k, e = s_idx[q];
@@ -463,32 +572,21 @@ __global__ __launch_bounds__(256) void k_route_scatter(int64_t n_slots, int E, i
 bool router_codes_x(int64_t T) { return T <= 64; }
 
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* Wr,
-                         const float* bias, const float* rinv, float* logits, uint16_t* xb,
-                         uint16_t* wb, int32_t* route_ctr, int qnl, int8_t* xq, float* xs,
+                         const float* bias, const float* rinv, const Workspace& ws,
                          hipStream_t s) {
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
-  if (qnl && !router_codes_x(T)) return hipErrorInvalidValue;
+  if (d.H % 256 || d.H > 4096) return hipErrorNotSupported;
   if (T <= 64) {
-    const unsigned tt = d.H >= 4096 ? 2 : 4;  // tokens per block (k_router_small's TT)
-    // with qnl, one extra block per token group codes x
-    const dim3 grid((unsigned)((d.E + 3) / 4 + (qnl ? 1 : 0)), (unsigned)((T + tt - 1) / tt));
-    auto go = [&](auto npl_tag) {
-      constexpr int NPL = decltype(npl_tag)::value;
-      launch("router_small", x_bf16 ? k_router_small<true, NPL> : k_router_small<false, NPL>,
-             grid, 256, 0, s, x, (int)T, Wr, bias, d.E, norm, rinv, logits, route_ctr, qnl, xq,
-             xs);
-    };
-    switch (d.H) {
-      case 256: go(std::integral_constant<int, 1>{}); break;
-      case 512: go(std::integral_constant<int, 2>{}); break;
-      case 1024: go(std::integral_constant<int, 4>{}); break;
-      case 2048: go(std::integral_constant<int, 8>{}); break;
-      case 4096: go(std::integral_constant<int, 16>{}); break;
-      default: return hipErrorNotSupported;
-    }
+    const int nq = (d.H / 128) * ((d.E + 15) / 16);  // slices x expert groups
+    const int per_xcd = (nq + 7) / 8;
+    float* ssp = (norm && !rinv) ? ws.lpart + (int64_t)(d.H / 128) * T * 256 : nullptr;
+    launch("router_split", x_bf16 ? k_router_split<true> : k_router_split<false>,
+           (unsigned)(8 * per_xcd), 256, 0, s, x, (int)T, d.H, Wr, d.E, per_xcd, ws.lpart, ssp,
+           ws.route_ctr);
   } else {
     if (norm && !rinv) return hipErrorInvalidValue;
-    if (!xb || !wb) return hipErrorInvalidValue;
+    uint16_t *xb = ws.xb, *wb = ws.wb;
+    float* logits = ws.logits;
     const int64_t nw = (int64_t)d.E * d.H;
     launch("split_router", k_split_bf16, (unsigned)((nw / 4 + 255) / 256), 256, 0, s, Wr, nw, wb,
            wb + nw);
@@ -508,13 +606,33 @@ hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, c
   return hipGetLastError();
 }
 
-hipError_t launch_route(const Dims& d, int64_t T, const float* logits, int chunk_m, const Workspace& ws,
-                        hipStream_t s) {
+hipError_t launch_route(const Dims& d, int64_t T, const void* x, bool x_bf16, const float* bias,
+                        const float* rinv, int qnl, int chunk_m, bool store_logits,
+                        const Workspace& ws, hipStream_t s) {
   const int renorm = (d.flags & MAPLE_RENORM_TOPK) ? 1 : 0;
+  if (qnl && !router_codes_x(T)) return hipErrorInvalidValue;
+  const float* logits = ws.logits;
   if (T <= 64) {
-    launch("route_small", k_route_small, (unsigned)((T + 3) / 4), 256, 0, s, logits, (int)T, d.E,
-           d.k, renorm, ws.idx, ws.gate, ws.offsets, ws.active, ws.n_active, ws.sorted_tok,
-           ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr, chunk_m, ws.chunks, ws.n_chunks);
+    const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0, S = d.H / 128;
+    const float* ssp = (norm && !rinv) ? ws.lpart + (int64_t)S * T * 256 : nullptr;
+    const unsigned nt = (unsigned)((T + 3) / 4);
+    auto go = [&](auto h_tag) {
+      constexpr int HH = decltype(h_tag)::value;
+      launch("route_small", x_bf16 ? k_route_small<true, HH> : k_route_small<false, HH>,
+             qnl ? 2 * nt : nt, 256, 0, s, ws.lpart, ssp, norm, rinv, bias,
+             store_logits ? ws.logits : nullptr,
+             (int)T, d.E, d.k, renorm, ws.idx, ws.gate, ws.offsets, ws.active, ws.n_active,
+             ws.sorted_tok, ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr, chunk_m, ws.chunks,
+             ws.n_chunks, qnl, x, ws.xq, ws.xs);
+    };
+    switch (d.H) {
+      case 256: go(std::integral_constant<int, 256>{}); break;
+      case 512: go(std::integral_constant<int, 512>{}); break;
+      case 1024: go(std::integral_constant<int, 1024>{}); break;
+      case 2048: go(std::integral_constant<int, 2048>{}); break;
+      case 4096: go(std::integral_constant<int, 4096>{}); break;
+      default: return hipErrorNotSupported;
+    }
     return hipGetLastError();
   }
   const int nb = (int)((T + 63) / 64);
