@@ -1321,24 +1321,36 @@ __global__ __launch_bounds__(256) void k_sm_down(
 // ---- weighted combine ---------------------------------------------------------------
 
 // out[t] = resid[t] + sum_j gate[t,j] * y[slot_pos[t,j]], summed in selection order
-// in fp32; a thread owns 8 consecutive outputs (y fp16: one 16-byte load per
-// slot; fp32: two).
+// in fp32.  A one-wave block per token and 64 VPT outputs, a thread owning VPT
+// consecutive outputs: one 16-byte piece of each slot row (VPT = 4 for fp32
+// y, 8 for fp16), so every load instruction reads 1 KB of contiguous row and
+// a 64-token batch spreads over 512 blocks.  The residual load goes out first
+// (it does not wait on the slot positions, which come by scalar loads); out
+// may be resid (updated in place: each thread reads its residual before it
+// writes).
 // yfac (fp16 form only): per slot, the factor by which the down projection
 // scaled its stored outputs down (2^8 times the slot's largest h scale).
 template <typename YT>
-__global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
-                                                 const float* __restrict__ gate,
-                                                 const int32_t* __restrict__ slot_pos, int H,
-                                                 int k, float* out, const float* resid,
-                                                 float* __restrict__ delta,
-                                                 const float* __restrict__ yfac) {
+__global__ __launch_bounds__(64) void k_combine(const YT* __restrict__ y,
+                                                const float* __restrict__ gate,
+                                                const int32_t* __restrict__ slot_pos, int H,
+                                                int k, float* out, const float* resid,
+                                                float* __restrict__ delta,
+                                                const float* __restrict__ yfac) {
+  constexpr bool F32 = std::is_same<YT, float>::value;
+  constexpr int VPT = F32 ? 4 : 8;
   const int64_t t = blockIdx.x;
-  const int o = (blockIdx.y * 256 + threadIdx.x) * 8;
+  const int o = (blockIdx.y * 64 + threadIdx.x) * VPT;
   if (o >= H) return;
+  const int64_t off = t * H + o;
+  float4 r[VPT / 4];
+#pragma unroll
+  for (int i = 0; i < VPT / 4; ++i)
+    r[i] = resid ? *reinterpret_cast<const float4*>(resid + off + 4 * i)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
   // all k (<= 8) rows of the token are loaded before any is added, so a
   // thread keeps k loads in flight; the sum then runs in j order
   constexpr int KM = 8;
-  constexpr int NV = std::is_same<YT, float>::value ? 2 : 1;  // 16-byte pieces per row
   int sp[KM];
   float g[KM];
 #pragma unroll
@@ -1347,60 +1359,40 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
       sp[j] = slot_pos[t * k + j];
       g[j] = gate[t * k + j];
     }
-  uint4 v[KM][NV];
+  uint4 v[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j)
-    if (j < k) {
-      const uint4* src = reinterpret_cast<const uint4*>(y + (int64_t)sp[j] * H + o);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) v[j][i] = src[i];
-    }
-  if constexpr (!std::is_same<YT, float>::value) {
+    if (j < k) v[j] = *reinterpret_cast<const uint4*>(y + (int64_t)sp[j] * H + o);
+  if constexpr (!F32) {
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (j < k) g[j] *= yfac[sp[j]];
   }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[VPT] = {};
 #pragma unroll
   for (int j = 0; j < KM; ++j)
     if (j < k) {
-      if constexpr (NV == 2) {
-        const float w[8] = {__uint_as_float(v[j][0].x), __uint_as_float(v[j][0].y),
-                            __uint_as_float(v[j][0].z), __uint_as_float(v[j][0].w),
-                            __uint_as_float(v[j][1].x), __uint_as_float(v[j][1].y),
-                            __uint_as_float(v[j][1].z), __uint_as_float(v[j][1].w)};
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(g[j], w[q], acc[q]);
-      } else {
-        const uint32_t w[4] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (F32) {
+          acc[q] = fmaf(g[j], __uint_as_float(w[q]), acc[q]);
+        } else {
           acc[2 * q] = fmaf(g[j], f16_lo(w[q]), acc[2 * q]);
           acc[2 * q + 1] = fmaf(g[j], f16_hi(w[q]), acc[2 * q + 1]);
         }
       }
     }
-  const int64_t off = t * H + o;
-  float4 a0 = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  float4 a1 = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  if (delta) {
-    *reinterpret_cast<float4*>(delta + off) = a0;
-    *reinterpret_cast<float4*>(delta + off + 4) = a1;
+#pragma unroll
+  for (int i = 0; i < VPT / 4; ++i) {
+    float4 a = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    if (delta) *reinterpret_cast<float4*>(delta + off + 4 * i) = a;
+    a.x += r[i].x;
+    a.y += r[i].y;
+    a.z += r[i].z;
+    a.w += r[i].w;
+    *reinterpret_cast<float4*>(out + off + 4 * i) = a;
   }
-  if (resid) {
-    const float4 r0 = *reinterpret_cast<const float4*>(resid + off);
-    const float4 r1 = *reinterpret_cast<const float4*>(resid + off + 4);
-    a0.x += r0.x;
-    a0.y += r0.y;
-    a0.z += r0.z;
-    a0.w += r0.w;
-    a1.x += r1.x;
-    a1.y += r1.y;
-    a1.z += r1.z;
-    a1.w += r1.w;
-  }
-  *reinterpret_cast<float4*>(out + off) = a0;
-  *reinterpret_cast<float4*>(out + off + 4) = a1;
 }
 
 }  // namespace
@@ -1450,8 +1442,8 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
       case 4096: run_h(std::integral_constant<int, 4096>{}); break;
       default: return hipErrorNotSupported;
     }
-    const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
-    launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate,
+    const dim3 cgrid((unsigned)T, (unsigned)((d.H + 255) / 256));
+    launch("combine", k_combine<float>, cgrid, 64, 0, s, (const float*)ws.y, ws.gate,
            ws.slot_pos, d.H, d.k, out, resid, delta, (const float*)nullptr);
     return hipGetLastError();
   }
@@ -1498,13 +1490,15 @@ hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* p
     default:
       return hipErrorNotSupported;
   }
-  const dim3 cgrid((unsigned)T, (unsigned)((d.H + 2047) / 2048));
+  // one-wave blocks of 64 x (4 fp32 | 8 fp16) outputs
   if (nl == 3)  // fp32 per-slot outputs; the fast form and A8 store scaled fp16
-    launch("combine", k_combine<float>, cgrid, 256, 0, s, (const float*)ws.y, ws.gate, ws.slot_pos,
-           d.H, d.k, out, resid, delta, (const float*)nullptr);
+    launch("combine", k_combine<float>, dim3((unsigned)T, (unsigned)((d.H + 255) / 256)), 64, 0,
+           s, (const float*)ws.y, ws.gate, ws.slot_pos, d.H, d.k, out, resid, delta,
+           (const float*)nullptr);
   else
-    launch("combine", k_combine<uint16_t>, cgrid, 256, 0, s, (const uint16_t*)ws.y, ws.gate,
-           ws.slot_pos, d.H, d.k, out, resid, delta, (const float*)ws.yfac);
+    launch("combine", k_combine<uint16_t>, dim3((unsigned)T, (unsigned)((d.H + 511) / 512)), 64,
+           0, s, (const uint16_t*)ws.y, ws.gate, ws.slot_pos, d.H, d.k, out, resid, delta,
+           (const float*)ws.yfac);
   return hipGetLastError();
 }
 
