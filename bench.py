@@ -939,6 +939,9 @@ def main():
                     help="decode_stack: leave out the prefill_4096 object")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only run the read-bandwidth probe (built next to the library): the "
+                         "plain read ceiling and the expert kernels' weight-fetch shapes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -946,6 +949,16 @@ def main():
               "(every token is independent, so the path shards by tokens with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.read_probe:
+        # a child process of its own; this one touches no GPU before it
+        import subprocess
+        probe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ternary_weight_moe_amd",
+                             "read_probe")
+        if not os.path.exists(probe):
+            print(f"{probe} is missing: build first (python -c 'import __graft_entry__ as g; "
+                  "g.build()')", file=sys.stderr)
+            sys.exit(2)
+        sys.exit(subprocess.run([probe]).returncode)
     decode = args.workload in ("decode_stack", "flashhead_decode", "hybrid_attn_decode")
     if args.steps is None:
         args.steps = 256 if decode else 20
