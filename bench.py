@@ -469,12 +469,24 @@ def bench_batched(args, torch, N, S):
     lists = ([l["Wr"] for l in layers], [l["bias"] for l in layers], [l["packed"] for l in layers],
              [l["alpha"] for l in layers])
 
-    def step():
+    def step(st=None):
         x.copy_(x0)
-        N.maple_moe_stack_forward(d, T, x, *lists, ws)
-    ms_per_step = timed(torch, step, args.steps, args.warmup)
+        N.maple_moe_stack_forward(d, T, x, *lists, ws, stream=st)
+    ms_eager = timed(torch, step, args.steps, args.warmup)
+    # the same step (restore x, one stack call) captured into a HIP graph and
+    # replayed, as a serving loop at a fixed batch would run it
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        step(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        step(st)
+    ms_per_step = timed(torch, graph.replay, args.steps, args.warmup)
     assert torch.isfinite(x).all().item(), "non-finite batched output"
-    log(f"batched_stack_zipf: {T / ms_per_step * 1000:.0f} tok/s, {ms_per_step * 1000:.1f} us/step")
+    del graph
+    log(f"batched_stack_zipf: {T / ms_per_step * 1000:.0f} tok/s, {ms_per_step * 1000:.1f} us/step "
+        f"(graph replays; eager calls {ms_eager * 1000:.1f} us)")
     prof = profile_kernels(N, step, min(args.steps, 8))
     per_kernel = {kn: dict(launches=n, avg_us=1000 * avg) for kn, (n, avg) in prof.items()}
     dom = max(prof, key=lambda kn: prof[kn][0] * prof[kn][1])
@@ -503,12 +515,16 @@ def bench_batched(args, torch, N, S):
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="f32", data="synthetic",
         config=dict(workload="batched_stack_zipf", hidden=H, experts=E, top_k=k, inter=I,
-                    layers=L, tokens_per_step=T, step="one stack call on 64 tokens"),
+                    layers=L, tokens_per_step=T,
+                    step="one stack call on 64 tokens, replayed from a captured HIP graph",
+                    eager_ms_per_step=ms_eager),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS if achieved else None,
                       traffic=traffic_for("batched_stack_zipf", dom), kernel=dom,
                       algorithmic_bytes_per_launch=dom_bytes,
-                      avg_launch_us=dom_avg_s * 1e6),
+                      avg_launch_us=dom_avg_s * 1e6,
+                      timing="eager calls: each kernel's own dispatch begin to end (HIP events "
+                             "on its launch)"),
         step_roofline=dict(algorithmic_bytes_per_step=step_bytes, achieved_gbs=step_gbs,
                            frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS),
         routing=routing,
