@@ -230,25 +230,42 @@ def oracle_layers(w):
     return out
 
 
+GAP_RULE = 1e-4  # a token whose top-k logit gap falls below this in any layer is redrawn
+
+
+def gap_rule_count(gaps):
+    """gaps [L, T] of the sampled tokens (the oracle's l_(k) - l_(k+1)): how many
+    token-layers fall below the gap rule, and how many tokens a parity test
+    would redraw.  The bench's inputs are not redrawn (timing needs no unique
+    routing); this says how often the rule would act on them."""
+    g = np.asarray(gaps)
+    return dict(gap=GAP_RULE, tokens=int(g.shape[1]), token_layers=int(g.size),
+                token_layers_below=int((g < GAP_RULE).sum()),
+                tokens_to_redraw=int((g < GAP_RULE).any(axis=0).sum()))
+
+
 def cpu_baseline_decode(w, budget_s):
     """The oracle (fp64 C, OpenMP) on a bounded sample: tokens one at a time
-    through the full 24-layer stack; tok/s on this host."""
+    through the full 24-layer stack; tok/s on this host.  Also counts the
+    sampled tokens' gap-rule hits."""
     import oracle
     from ternary_weight_moe_amd import synth as S
     log("cpu baseline: packing the stack for the oracle")
     L = oracle_layers(w)
-    n, t_used = 0, 0.0
+    n, t_used, gaps = 0, 0.0, []
     while t_used < budget_s and n < 256:
         x = S.x_as_f32(w, S.gen_x(w, 1, token0=n)).astype(np.float64)
         t0 = time.perf_counter()
-        oracle.moe_stack(x, [l["Wr"] for l in L], [l["bias"] for l in L],
-                         [l["packed"] for l in L], [l["alpha"] for l in L], k=w.top_k,
-                         inter=w.inter, keep_logits=False, keep_delta=False)
+        r = oracle.moe_stack(x, [l["Wr"] for l in L], [l["bias"] for l in L],
+                             [l["packed"] for l in L], [l["alpha"] for l in L], k=w.top_k,
+                             inter=w.inter, keep_logits=True, keep_delta=False)
         t_used += time.perf_counter() - t0
+        gaps.append(oracle.topk_gap(r["logits"], w.top_k))
         n += 1
     return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{n} tokens x {w.n_layers} layers, one token per call "
-                       f"({t_used:.1f} s of oracle time)")
+                       f"({t_used:.1f} s of oracle time)",
+                gap_rule=gap_rule_count(np.concatenate(gaps, axis=1)))
 
 
 def cpu_baseline_batched(w, budget_s):
@@ -258,17 +275,19 @@ def cpu_baseline_batched(w, budget_s):
     from ternary_weight_moe_amd import synth as S
     L = oracle_layers(w)
     x_all = S.x_as_f32(w, S.gen_x(w, w.n_tokens)).astype(np.float64)
-    n, t_used = 0, 0.0
+    n, t_used, gaps = 0, 0.0, []
     while t_used < budget_s and n < w.n_tokens:
         t0 = time.perf_counter()
-        oracle.moe_stack(x_all[n:n + 8], [l["Wr"] for l in L], [l["bias"] for l in L],
-                         [l["packed"] for l in L], [l["alpha"] for l in L], k=w.top_k,
-                         inter=w.inter, keep_logits=False, keep_delta=False)
+        r = oracle.moe_stack(x_all[n:n + 8], [l["Wr"] for l in L], [l["bias"] for l in L],
+                             [l["packed"] for l in L], [l["alpha"] for l in L], k=w.top_k,
+                             inter=w.inter, keep_logits=True, keep_delta=False)
         t_used += time.perf_counter() - t0
+        gaps.append(oracle.topk_gap(r["logits"], w.top_k))
         n += 8
     return dict(value=n / t_used, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{n} of the {w.n_tokens} tokens of one step, 8 per call, "
-                       f"{w.n_layers} layers ({t_used:.1f} s of oracle time)")
+                       f"{w.n_layers} layers ({t_used:.1f} s of oracle time)",
+                gap_rule=gap_rule_count(np.concatenate(gaps, axis=1)))
 
 
 def cpu_baseline_prefill(w, budget_s, a8=False):
