@@ -124,59 +124,42 @@ def prefill_ops(kernel, H, k, I, T):
 # counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "dec_down": {"bytes": 4509671, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1261137eae3b9bf2"},
-        "dec_gateup": {"bytes": 4742253, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1261137eae3b9bf2"},
-        "dec_router": {"bytes": 2168215, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1261137eae3b9bf2"},
-        "load_token": {"bytes": 13721, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "7c034a523fd90754"},
-        "store_token": {"bytes": 29572, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "7c034a523fd90754"},
+        "dec_down": {"bytes": 4509649, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6a993e437d716e56"},
+        "dec_gateup": {"bytes": 4742233, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6a993e437d716e56"},
+        "dec_router": {"bytes": 2168177, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6a993e437d716e56"},
+        "load_token": {"bytes": 13683, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "8045bf3489503dde"},
+        "store_token": {"bytes": 29462, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "8045bf3489503dde"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 170375668, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
-        "down_mfma": {"bytes": 244618064, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
-        "gateup_mfma": {"bytes": 325614694, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
-        "quant_x": {"bytes": 35946953, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5fffb3838a8ca577"},
-        "route_block": {"bytes": 343948, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
-        "route_scan": {"bytes": 146289, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
-        "route_scatter": {"bytes": 1209143, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
-        "route_topk": {"bytes": 4488448, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
-        "router_mfma": {"bytes": 37784413, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
-        "split_router": {"bytes": 4206355, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "e2ce9ac65ccb6e24"},
+        "combine": {"bytes": 170783640, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "down_mfma": {"bytes": 244686350, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "gateup_mfma": {"bytes": 325651829, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "quant_x": {"bytes": 35971895, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "route_block": {"bytes": 343913, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "route_scan": {"bytes": 146487, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "route_scatter": {"bytes": 1209256, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "route_topk": {"bytes": 4488538, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "router_mfma": {"bytes": 37792648, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "split_router": {"bytes": 4206558, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 303057223, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "down_mfma": {"bytes": 414022562, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "gateup_mfma": {"bytes": 268735714, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "quant_x": {"bytes": 25353354, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "route_block": {"bytes": 359404, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_scan": {"bytes": 149783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_scatter": {"bytes": 1226217, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "route_topk": {"bytes": 4519402, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "router_mfma": {"bytes": 37815995, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "split_router": {"bytes": 4218716, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
+        "combine": {"bytes": 170792668, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "down_mfma": {"bytes": 275316580, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "gateup_mfma": {"bytes": 268669924, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "quant_x": {"bytes": 25316676, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "route_block": {"bytes": 344192, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "route_scan": {"bytes": 146464, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "route_scatter": {"bytes": 1209440, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "route_topk": {"bytes": 4488704, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "router_mfma": {"bytes": 37792984, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "split_router": {"bytes": 4207028, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5304724, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "down_mfma": {"bytes": 38764748, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "gateup_mfma": {"bytes": 68222264, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "f29642d828d73910"},
-        "route_small": {"bytes": 158648, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-        "router_small": {"bytes": 21660783, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "4191bf9232eee055"},
-    },
-    "hybrid_attn_decode": {
-        "attn_combine": {"bytes": 1123183, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-        "attn_fill": {"bytes": 169793789, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-        "attn_global": {"bytes": 269737003, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-        "attn_window": {"bytes": 1164689, "sources": ["attn.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a8803bbaa8cfac28"},
-    },
-    "ternary_convert": {
-        "fill_i32": {"bytes": 2681, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "206790320fd07fc4"},
-        "ternarize_g32": {"bytes": 606102532, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
-        "ternarize_w2": {"bytes": 1209101837, "sources": ["convert.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "a0ee34ff97f3e962"},
-    },
-    "flashhead_decode": {
-        "head_final": {"bytes": 12734, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
-        "head_scores": {"bytes": 19583241, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
-        "head_search": {"bytes": 58841660, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
-        "head_select": {"bytes": 59798, "sources": ["digits.h", "head.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "18c0dfac9c651570"},
+        "combine": {"bytes": 5273316, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "down_mfma": {"bytes": 39191888, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "gateup_mfma": {"bytes": 69825229, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
+        "route_small": {"bytes": 2134426, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "router_split": {"bytes": 3694941, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
     },
 }
 
