@@ -960,6 +960,9 @@ def main():
     ap.add_argument("--read-probe", action="store_true",
                     help="only run the read-bandwidth probe (built next to the library): the "
                          "plain read ceiling and the expert kernels' weight-fetch shapes")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the matrix-core probe (built next to the library): issue "
+                         "rates of the MFMA kinds the kernels use, dependent-load latency")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -967,11 +970,11 @@ def main():
               "(every token is independent, so the path shards by tokens with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.read_probe:
+    if args.read_probe or args.mfma_probe:
         # a child process of its own; this one touches no GPU before it
         import subprocess
         probe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ternary_weight_moe_amd",
-                             "read_probe")
+                             "read_probe" if args.read_probe else "mfma_probe")
         if not os.path.exists(probe):
             print(f"{probe} is missing: build first (python -c 'import __graft_entry__ as g; "
                   "g.build()')", file=sys.stderr)

@@ -3,8 +3,9 @@
 Usage: python -m ternary_weight_moe_amd.build [--force] [-j N]
 Objects go to ternary_weight_moe_amd/_build/ (not committed); the library to
 ternary_weight_moe_amd/libmaple_moe.so, where the binding loads it.  The
-read-bandwidth probe (csrc/read_probe.hip, run by bench.py --read-probe)
-builds to ternary_weight_moe_amd/read_probe.
+two measurement probes (csrc/read_probe.hip and csrc/mfma_probe.hip, run by
+bench.py --read-probe / --mfma-probe) build to ternary_weight_moe_amd/read_probe
+and ternary_weight_moe_amd/mfma_probe.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmaple_moe.so")
-PROBE = os.path.join(PKG, "read_probe")
+PROBES = ("read_probe", "mfma_probe")
 SOURCES = ["api.cpp", "route.hip", "gemv.hip", "decode1.hip", "grouped.hip", "misc.hip", "head.hip",
            "attn.hip", "convert.hip"]
 HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(CSRC, "wave.h"),
@@ -68,18 +69,21 @@ def build(force: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
-def build_probe(force: bool = False) -> str:
-    src = os.path.join(CSRC, "read_probe.hip")
-    if not force and os.path.exists(PROBE) and os.path.getmtime(PROBE) >= os.path.getmtime(src):
-        return PROBE
-    tmp = PROBE + f".tmp{os.getpid()}"
-    r = subprocess.run([HIPCC, *[f for f in FLAGS if f != "-fPIC"], src, "-o", tmp],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed on read_probe.hip")
-    os.replace(tmp, PROBE)
-    return PROBE
+def build_probes(force: bool = False) -> list:
+    outs = []
+    for name in PROBES:
+        src, exe = os.path.join(CSRC, name + ".hip"), os.path.join(PKG, name)
+        outs.append(exe)
+        if not force and os.path.exists(exe) and os.path.getmtime(exe) >= os.path.getmtime(src):
+            continue
+        tmp = exe + f".tmp{os.getpid()}"
+        r = subprocess.run([HIPCC, *[f for f in FLAGS if f != "-fPIC"], src, "-o", tmp],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {name}.hip")
+        os.replace(tmp, exe)
+    return outs
 
 
 if __name__ == "__main__":
@@ -88,4 +92,4 @@ if __name__ == "__main__":
     ap.add_argument("-j", type=int, default=8)
     a = ap.parse_args()
     print(build(a.force, a.j))
-    print(build_probe(a.force))
+    print(*build_probes(a.force), sep="\n")
