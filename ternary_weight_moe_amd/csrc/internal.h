@@ -108,11 +108,12 @@ int max_chunks(const Dims& d, int64_t T);
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
-// Router and routing.  Small T (<= 64): launch_router leaves partial logits
-// over K slices in ws.lpart (and zeroes ws.route_ctr, the routing kernel's
-// arrival counter); launch_route sums them, applies 1/rms (rinv, else from x
-// when the layer normalises) and the bias, and routes, storing ws.logits only
-// with store_logits (a debug copy wants them).
+// Router and routing.  Small T (<= 64; rinv must be null): launch_router
+// leaves partial logits over K slices in ws.lpart, with each slice's sum of
+// x^2 when the layer normalises (and zeroes ws.route_ctr, the routing
+// kernel's arrival counter); launch_route sums them, applies 1/rms and the
+// bias, and routes, storing ws.logits only with store_logits (a debug copy
+// wants them).
 // Larger T: launch_router stores ws.logits itself (bias and rinv applied;
 // rinv required with MAPLE_RMS_NORM; ws.xb, ws.wb hold bf16 planes) and
 // launch_route reads them.  qnl > 0 (only where router_codes_x(T)): the

@@ -368,9 +368,9 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
 // ---- T <= 64: selection in parallel, grouping by the last block to finish ----------
 
 // One wave per token, 4 per block (the first nt = ceil(T / 4) blocks).  The
-// wave sums its token's S = H / 128 partial logits in slice order, scales by 1/rms
-// (rinv[t] when given, else from the slices' sums of x^2 when norm), adds the
-// bias (storing the logits when logits is given), then selects.  Each block publishes its
+// wave sums its token's S = H / 128 partial logits in slice order, scales by
+// 1/rms from the slices' sums of x^2 when norm, adds the bias (storing the
+// logits when logits is given), then selects.  Each block publishes its
 // selections and takes a ticket from an arrival counter (zeroed by the router
 // kernel before this kernel starts); the block with the last ticket then sees
 // every selection and counts (one 64-bit token mask per expert), scans and
@@ -381,7 +381,7 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
 template <bool BF16, int H>
 __global__ __launch_bounds__(256) void k_route_small(
     const float* __restrict__ part, const float* __restrict__ ssp, int norm,
-    const float* __restrict__ rinv, const float* __restrict__ bias, float* __restrict__ logits,
+    const float* __restrict__ bias, float* __restrict__ logits,
     int T, int E, int k, int renorm, int32_t* __restrict__ idx,
     float* __restrict__ gate, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_tok,
@@ -411,14 +411,13 @@ __global__ __launch_bounds__(256) void k_route_small(
   }
   const int t = blockIdx.x * 4 + (tid >> 6);
   if (t < T) {  // wave-uniform
-    // the bias, 1/rms or lane j's slice sum of x^2, then up to 16 slices'
-    // partials in flight at once (16-byte loads: experts j + 64 m), summed in
-    // slice order; everything is issued before the first wait
+    // the bias and lane j's slice sum of x^2, then up to 16 slices' partials
+    // in flight at once (16-byte loads: experts j + 64 m), summed in slice
+    // order; everything is issued before the first wait
     float bv[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) bv[m] = (bias && lane + 64 * m < E) ? bias[lane + 64 * m] : 0.f;
-    const float rt = rinv ? rinv[t] : 1.f;
-    const float qj = (ssp && lane < S) ? ssp[(int64_t)lane * T + t] : 0.f;
+    const float qj = (norm && lane < S) ? ssp[(int64_t)lane * T + t] : 0.f;
     constexpr int SB = S < 16 ? S : 16;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += SB) {
@@ -434,8 +433,7 @@ __global__ __launch_bounds__(256) void k_route_small(
         sum[3] += v[j].w;
       }
     }
-    float r = rt;
-    if (!rinv && norm) r = rsqrtf(wave_sum_f(qj) / (float)H + MAPLE_RMS_EPS);
+    const float r = norm ? rsqrtf(wave_sum_f(qj) / (float)H + MAPLE_RMS_EPS) : 1.f;
     float lv[1][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -577,9 +575,10 @@ hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16, c
   const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0;
   if (d.H % 256 || d.H > 4096) return hipErrorNotSupported;
   if (T <= 64) {
+    if (rinv) return hipErrorInvalidValue;  // 1/rms is formed from the slices here
     const int nq = (d.H / 128) * ((d.E + 15) / 16);  // slices x expert groups
     const int per_xcd = (nq + 7) / 8;
-    float* ssp = (norm && !rinv) ? ws.lpart + (int64_t)(d.H / 128) * T * 256 : nullptr;
+    float* ssp = norm ? ws.lpart + (int64_t)(d.H / 128) * T * 256 : nullptr;
     launch("router_split", x_bf16 ? k_router_split<true> : k_router_split<false>,
            (unsigned)(8 * per_xcd), 256, 0, s, x, (int)T, d.H, Wr, d.E, per_xcd, ws.lpart, ssp,
            ws.route_ctr);
@@ -613,13 +612,14 @@ hipError_t launch_route(const Dims& d, int64_t T, const void* x, bool x_bf16, co
   if (qnl && !router_codes_x(T)) return hipErrorInvalidValue;
   const float* logits = ws.logits;
   if (T <= 64) {
+    if (rinv) return hipErrorInvalidValue;  // 1/rms is formed from the router's slices
     const int norm = (d.flags & MAPLE_RMS_NORM) ? 1 : 0, S = d.H / 128;
-    const float* ssp = (norm && !rinv) ? ws.lpart + (int64_t)S * T * 256 : nullptr;
+    const float* ssp = norm ? ws.lpart + (int64_t)S * T * 256 : nullptr;
     const unsigned nt = (unsigned)((T + 3) / 4);
     auto go = [&](auto h_tag) {
       constexpr int HH = decltype(h_tag)::value;
       launch("route_small", x_bf16 ? k_route_small<true, HH> : k_route_small<false, HH>,
-             qnl ? 2 * nt : nt, 256, 0, s, ws.lpart, ssp, norm, rinv, bias,
+             qnl ? 2 * nt : nt, 256, 0, s, ws.lpart, ssp, norm, bias,
              store_logits ? ws.logits : nullptr,
              (int)T, d.E, d.k, renorm, ws.idx, ws.gate, ws.offsets, ws.active, ws.n_active,
              ws.sorted_tok, ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr, chunk_m, ws.chunks,
