@@ -8,7 +8,9 @@ inter 128..2048 (powers of two), each through every path that serves it.
 - The grouped matrix-core path for inter <= 512 (the grouped kernels' limit),
   T = 40: the fast form, the fine form and the A8 variant.
 
-Every shape has 16 experts and top-4.  Routing is compared bit-exact and
+Every shape has 16 experts and top-4; expert counts that are not multiples
+of the kernels' groupings (40, 100, 250) run at hidden 1024, inter 256, and
+the small-M chunking at its extremes.  Routing is compared bit-exact and
 outputs within the layer tolerances, against the oracle on the same seeded
 inputs; tokens obey the router gap rule.  (The architecture table of the
 linlog.top article "Maple-Preview" fixes hidden 2048, 256 experts, top-8 and
@@ -67,3 +69,24 @@ def test_small_m_degenerate_routing(a8):
         else:
             check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS,
                         what=f"small-M fine E={E} k={k}")
+
+
+@pytest.mark.parametrize("E,k", [(40, 6), (100, 8), (250, 8)], ids=lambda v: str(v))
+def test_uneven_expert_counts(E, k):
+    """Expert counts that are not multiples of the kernels' groupings (16
+    experts per small-T router block, 64 per router tile, 64 per routing
+    lane set), hidden 1024, inter 256: one token, 23 tokens through the
+    small-M fine form, the tiled fast form and A8 (the split-K small-T
+    router), and 100 tokens through the large-T router."""
+    w = workload("tiny_layer", name=f"uneven_{E}_{k}", hidden=1024, inter=256, n_experts=E,
+                 top_k=k, n_tokens=100, x_bf16=True, seed=7300 + E + k)
+    L = Layer(w, 0)
+    x1, _ = layer_tokens_with_gap(w, L, 1, token0=500)
+    check_layer(w, L, x1, what=f"E={E} k={k} one token")
+    x23, _ = layer_tokens_with_gap(w, L, 23, token0=600)
+    check_layer(w, L, x23, flags=N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS,
+                what=f"E={E} k={k} T=23 fine")
+    check_layer(w, L, x23, flags=N.MAPLE_FORCE_GROUPED, what=f"E={E} k={k} T=23 fast")
+    check_a8(w, L, x23, what=f"E={E} k={k} T=23 a8")
+    x100, _ = layer_tokens_with_gap(w, L, 100, token0=700)
+    check_layer(w, L, x100, flags=N.MAPLE_FORCE_GROUPED, what=f"E={E} k={k} T=100 fast")
