@@ -909,24 +909,6 @@ hipError_t d1_gateup_h(const Dims& d, const void* x, const uint8_t* packed, cons
 }
 
 
-// First threshold fraction for wave_topk_thresh: logits taken as normal, the
-// threshold max - f (max - mean) is put where about 2k of E exceed it, with
-// the expected maximum at the upper quantile 1 - 1/(E+1) (Blom-style
-// approximation).  Only the speed depends on it.
-float topk_f0(int E, int k) {
-  if (2 * k >= E) return 8.f;
-  auto zq = [](double p) {  // upper-tail normal quantile: P(Z > z) = p
-    double lo = -8.0, hi = 8.0;
-    for (int i = 0; i < 60; ++i) {
-      const double mid = 0.5 * (lo + hi);
-      if (0.5 * std::erfc(mid / std::sqrt(2.0)) > p) lo = mid; else hi = mid;
-    }
-    return 0.5 * (lo + hi);
-  };
-  const double zmax = zq(1.0 / (E + 1)), zt = zq(2.0 * k / E);
-  return zmax > 0.0 ? (float)std::max(0.05, (zmax - zt) / zmax) : 1.f;
-}
-
 template <int H, bool BF16>
 hipError_t dec_router(const Dims& d, const void* x, const float* Wr, const Workspace& ws,
                       hipStream_t s) {
@@ -975,6 +957,24 @@ hipError_t dec_layer_h(const Dims& d, const void* x, bool x_bf16, const float* W
 }
 
 }  // namespace
+
+// First threshold fraction for wave_topk_thresh: logits taken as normal, the
+// threshold max - f (max - mean) is put where about 2k of E exceed it, with
+// the expected maximum at the upper quantile 1 - 1/(E+1) (Blom-style
+// approximation).  Only the speed depends on it.
+float topk_f0(int E, int k) {
+  if (2 * k >= E) return 8.f;
+  auto zq = [](double p) {  // upper-tail normal quantile: P(Z > z) = p
+    double lo = -8.0, hi = 8.0;
+    for (int i = 0; i < 60; ++i) {
+      const double mid = 0.5 * (lo + hi);
+      if (0.5 * std::erfc(mid / std::sqrt(2.0)) > p) lo = mid; else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+  };
+  const double zmax = zq(1.0 / (E + 1)), zt = zq(2.0 * k / E);
+  return zmax > 0.0 ? (float)std::max(0.05, (zmax - zt) / zmax) : 1.f;
+}
 
 bool decode1_matrix_cores(const Dims& d) {
   return (d.H == 2048 || d.H == 4096) && (d.I == 256 || d.I == 512) &&

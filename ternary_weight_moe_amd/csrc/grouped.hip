@@ -31,7 +31,10 @@
 // which k each of their bytes holds; both use: in a super-step of 64*SS codes,
 // lane group g = lane/16 covers words [SS*g, SS*g + SS) and MFMA step s uses
 // word SS*g + s.  A row's super-step then comes from one 16-byte load per lane.
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 #include "limbs.h"
@@ -1002,13 +1005,18 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 // SC rows of H bytes) are staged in LDS and read by all eight waves as B.
 // Load order matters: the vector-memory counter drains in order, so the x
 // loads go out before the weights (staging then waits for x alone), and
-// tokens and per-token scales come by scalar loads.
+// per-token scales come by scalar loads.  Every block first rebuilds the
+// grouping from the T k selections in LDS (a chunk's expert, first slot and
+// tokens), which spares the routing kernel a grid-wide hand-off; block 0
+// also stores the grouping (offsets, sorted tokens, slot positions, chunk
+// list) for the down and combine kernels.
 template <int H, int I, int NL>
 __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
     const int8_t* xq, const float* __restrict__ xs, int T,
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
-    const int32_t* __restrict__ sorted_tok, const int32_t* __restrict__ chunks,
-    const int32_t* __restrict__ n_chunks, float* __restrict__ hf) {
+    const int32_t* __restrict__ idx, int E, int k, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_tok, int32_t* __restrict__ slot_pos,
+    int32_t* __restrict__ chunks, int32_t* __restrict__ n_chunks, float* __restrict__ hf) {
   constexpr int SC = 16 / NL;       // slots per chunk
   constexpr int NR = NL * SC;       // staged rows (15 or 16)
   constexpr int NB = I / 128;       // blocks per chunk
@@ -1020,15 +1028,96 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
   __shared__ __align__(16) int8_t sX[16][XROW];
   __shared__ float s_sx[16];
   __shared__ int s_q[16][NL];
-  const int item = xcd_tile(blockIdx.x, *n_chunks * NB);
-  if (item < 0) return;
-  const int c = item / NB, cb = (item % NB) * 128;
-  const int2 crec = *reinterpret_cast<const int2*>(chunks + 2 * c);
-  const int e = crec.x & 0xFFFF, np = crec.x >> 16, p0 = crec.y;
-  // the wave index as a wave-uniform value: the staging tokens then come by
-  // scalar loads, outside the in-order vector-memory counter
+  __shared__ unsigned long long s_mask[256];  // expert -> mask of the tokens that chose it
+  __shared__ int s_wt[4];                     // packed totals of the four expert waves
+  __shared__ int s_off[256];                  // each expert's first slot
+  __shared__ int s_ctab[kSmMaxChunks];        // chunk -> expert | index within the expert << 8
+  // the wave index as a wave-uniform value: the staging tokens then sit in
+  // scalar registers
   const int tid = threadIdx.x, lane = tid & 63,
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Grouping, as the routing kernel defines it for larger inputs: experts in
+  // index order, each expert's slots in token order, chunks of SC slots in
+  // that order.  Thread q < T k holds selection q (slot q of token q / k);
+  // each expert's tokens form a 64-bit mask (T <= 64, and a token picks an
+  // expert at most once, so token order is slot order).
+  const int Tk = T * k;  // <= 512
+  const int sel = tid < Tk ? idx[tid] : 0;
+  if (tid < 256) s_mask[tid] = 0ull;
+  __syncthreads();
+  if (tid < Tk) atomicOr(&s_mask[sel], 1ull << (tid / k));
+  __syncthreads();
+  // thread e < 256 (waves 0 to 3): expert e's slot and chunk counts, their
+  // exclusive prefix sums packed as first slot | first chunk << 16 (totals
+  // stay below 2^16)
+  unsigned long long em = 0ull;
+  int cnt = 0, nc = 0, ex = 0;
+  if (tid < 256) {
+    em = s_mask[tid];
+    cnt = __popcll(em);
+    nc = (cnt + SC - 1) / SC;
+    const int v = cnt | nc << 16;
+    const int inc = wave_incl_scan(v, lane);
+    if (lane == 63) s_wt[wave] = inc;
+    ex = inc - v;
+  }
+  __syncthreads();
+  int all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = s_wt[w];
+    ex += w < wave ? t : 0;
+    all += t;
+  }
+  const int n_ch = all >> 16;
+  if (tid < 256) {
+    const int cpos = ex >> 16;
+    s_off[tid] = ex & 0xFFFF;
+    for (int i = 0; i < nc; ++i) s_ctab[cpos + i] = tid | i << 8;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {  // block-uniform: the grouping for the down and combine kernels
+    const int off = ex & 0xFFFF, cpos = ex >> 16;
+    if (tid < E) {
+      offsets[tid] = off;
+      for (int i = 0; i < nc; ++i) {
+        chunks[2 * (cpos + i)] = tid | min(SC, cnt - i * SC) << 16;
+        chunks[2 * (cpos + i) + 1] = off + i * SC;
+      }
+    }
+    if (tid == 0) {
+      offsets[E] = all & 0xFFFF;
+      *n_chunks = n_ch;
+    }
+    if (tid < Tk) {
+      const int tq = tid / k;
+      const int pos = s_off[sel] + __popcll(s_mask[sel] & ((1ull << tq) - 1ull));
+      slot_pos[tid] = pos;
+      sorted_tok[pos] = tq;
+    }
+  }
+  // work items (chunk, 128-column part) spread over the XCDs as xcd_tile
+  // does; the grid (a multiple of 8, at most what the chip holds at once)
+  // takes them in rounds
+  const int n_items = n_ch * NB, per_xcd = (n_items + 7) >> 3, nbx = gridDim.x >> 3;
+  for (int j = blockIdx.x >> 3; j < per_xcd; j += nbx) {
+  const int item = (blockIdx.x & 7) * per_xcd + j;
+  if (item >= n_items) break;  // block-uniform
+  const int c = item / NB, cb = (item % NB) * 128;
+  const int crec = s_ctab[c];
+  const int e = __builtin_amdgcn_readfirstlane(crec & 0xFF);
+  const int i0 = __builtin_amdgcn_readfirstlane(crec >> 8) * SC;
+  const unsigned long long cmask = s_mask[e];
+  const int p0 = __builtin_amdgcn_readfirstlane(s_off[e]) + i0;
+  const int np = min(SC, __popcll(cmask) - i0);
+  // token of the chunk's slot sl: the set bit of the mask with i0 + sl set
+  // bits below it (one ballot; wave-uniform)
+  const bool has = (cmask >> lane) & 1ull;
+  const int below = (int)__builtin_amdgcn_mbcnt_hi(
+      (unsigned)(cmask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)cmask, 0u));
+  auto tok_of = [&](int sl) -> int {
+    return (int)__builtin_ctzll(__ballot(has && below == i0 + sl));
+  };
   const int g = lane >> 4, c16 = lane & 15;
   // staging of rows r = wave + 8 i (slot r / NL, limb r % NL), RPH rows per
   // phase; rows past NR and absent slots read the chunk's first slot and
@@ -1040,7 +1129,7 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
     for (int i = 0; i < RPH; ++i) {
       const int r = wave + 8 * (ph * RPH + i), sl = s0 + r / NL;
       const bool live = r < NR && sl < np;
-      const int tok = sorted_tok[p0 + (live ? sl : 0)];  // wave-uniform
+      const int tok = tok_of(live ? sl : 0);  // wave-uniform
       const int8_t* src = xq + ((int64_t)tok * NL + r % NL) * H + 16 * lane;
       xm[i] = live ? ~0u : 0u;  // zeroing by a mask: no branch around the loads
 #pragma unroll
@@ -1063,7 +1152,7 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
       const int* xi = reinterpret_cast<const int*>(xs);
 #pragma unroll
       for (int s = 0; s < SC; ++s) {
-        const int tk = sorted_tok[p0 + (s0 + s < np ? s0 + s : 0)];
+        const int tk = tok_of(s0 + s < np ? s0 + s : 0);
         const float sx = xs[tk] * xs[4 * T + tk];
         int q[NL];
 #pragma unroll
@@ -1150,6 +1239,8 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
     if (act)
       *reinterpret_cast<float4*>(hf + (int64_t)(p0 + sl) * I + cb + 16 * wave + 4 * g) =
           make_float4(h4[0], h4[1], h4[2], h4[3]);
+  }
+  __syncthreads();  // every wave is done with sX and the slot data of this item
   }
 }
 
@@ -1412,20 +1503,47 @@ hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, 
   return hipGetLastError();
 }
 
+// Blocks of a kernel that the current device holds at once (its occupancy
+// at `threads` threads per block times the compute units), cached per kernel
+// and device; 0 if the runtime cannot tell.
+static int resident_blocks(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, dev);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cache[key] = per_cu * cus;
+  return per_cu * cus;
+}
+
 hipError_t launch_grouped_ffn(const Dims& d, int64_t T, int nl, const uint8_t* packed,
                               const float* alpha, const Workspace& ws, float* out,
                               const float* resid, float* delta, hipStream_t s) {
   const int64_t Tk = T * d.k;
   const bool fine = nl != 2;  // the fp32-h kernels: three limbs, or one (A8); else the digit form
   if (small_m_chunk(d, T, nl) > 0) {
-    // chunks of up to 16 / nl slots (the routing kernel built their list)
+    // chunks of up to 16 / nl slots (the gate/up kernel groups the selections
+    // and stores the chunk list for the down kernel)
     const int mc = max_chunks(d, T);
     auto grid = [](int64_t items) { return (unsigned)(8 * ((items + 7) / 8)); };
     auto run_sm = [&](auto h_tag, auto i_tag) {
       constexpr int H_ = decltype(h_tag)::value, I_ = decltype(i_tag)::value;
-      launch("gateup_mfma", nl == 1 ? k_sm_gateup<H_, I_, 1> : k_sm_gateup<H_, I_, 3>,
-             grid((int64_t)mc * (I_ / 128)), 512, 0, s, ws.xq, ws.xs, (int)T, packed, alpha,
-             ws.sorted_tok, ws.chunks, ws.n_chunks, ws.h);
+      const auto gu = nl == 1 ? k_sm_gateup<H_, I_, 1> : k_sm_gateup<H_, I_, 3>;
+      // gate/up: no more blocks than the chip holds at once (each block
+      // groups the selections once, then takes items in rounds)
+      unsigned gu_grid = grid((int64_t)mc * (I_ / 128));
+      const int held = resident_blocks(reinterpret_cast<const void*>(gu), 512) & ~7;
+      if (held > 0 && (unsigned)held < gu_grid) gu_grid = (unsigned)held;
+      launch("gateup_mfma", gu, gu_grid, 512, 0, s, ws.xq, ws.xs, (int)T, packed, alpha,
+             (const int32_t*)ws.idx, d.E, d.k, ws.offsets, ws.sorted_tok, ws.slot_pos, ws.chunks,
+             ws.n_chunks, ws.h);
       launch("down_mfma", nl == 1 ? k_sm_down<H_, I_, 1> : k_sm_down<H_, I_, 3>,
              grid((int64_t)mc * (H_ / 256)), 256, 0, s, (const float*)ws.h, packed, alpha,
              ws.chunks, ws.n_chunks, (float*)ws.y);

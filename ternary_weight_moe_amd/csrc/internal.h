@@ -104,10 +104,16 @@ int max_tiles(const Dims& d, int64_t T);
 // tiled kernels run instead.
 int small_m_chunk(const Dims& d, int64_t T, int nl);
 int max_chunks(const Dims& d, int64_t T);
+// max_chunks at its largest (64 tokens, top-8, 256 experts)
+constexpr int kSmMaxChunks = 64 * 8 / 5 + 256 + 1;
 
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
                        hipStream_t s);
+// First threshold fraction of the threshold top-k selection for E experts
+// and top-k; only the selection's speed depends on it.
+float topk_f0(int E, int k);
+
 // Router and routing.  Small T (<= 64; rinv must be null): launch_router
 // leaves partial logits over K slices in ws.lpart, with each slice's sum of
 // x^2 when the layer normalises (and zeroes ws.route_ctr, the routing
@@ -119,6 +125,9 @@ hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t*
 // launch_route reads them.  qnl > 0 (only where router_codes_x(T)): the
 // routing kernel also codes x as launch_quant_x does for nl = qnl (int8
 // limbs, or digits for 2), xq / xs as it writes them (1/rms computed from x).
+// chunk_m > 0 (small T, the small-M expert kernels follow): routing stores
+// the selections only; the gate/up kernel rebuilds the grouping and stores
+// offsets, sorted tokens, slot positions and the chunk list.
 bool router_codes_x(int64_t T);
 hipError_t launch_router(const Dims& d, int64_t T, const void* x, bool x_bf16,
                          const float* Wr, const float* bias, const float* rinv,

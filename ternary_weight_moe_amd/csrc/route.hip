@@ -309,39 +309,34 @@ __device__ __forceinline__ unsigned long long block_excl_scan4x16(unsigned long 
   return base + inc - v;
 }
 
-// Per-expert counts -> offsets, the active-expert list, the grouped-GEMM
-// tile list (per tile: expert | slot count << 16, its first slot) and, with
-// cm > 0, the small-M chunk list in the same format (chunks of up to cm
-// slots).  Thread e holds cnt of expert e (0 for e >= E).  Every thread of
-// the block (NWV waves, 64 NWV >= E) calls it.  PACKED (at most 64 tokens,
-// so every count and total is below 2^16): the four scans run as one over
-// 16-bit fields (s_tmp64, one barrier) instead of one after another (s_tmp).
+// Per-expert counts -> offsets, the active-expert list and the grouped-GEMM
+// tile list (per tile: expert | slot count << 16, its first slot).  Thread e
+// holds cnt of expert e (0 for e >= E).  Every thread of the block (NWV
+// waves, 64 NWV >= E) calls it.  PACKED (at most 64 tokens, so every count
+// and total is below 2^16): the three scans run as one over 16-bit fields
+// (s_tmp64, one barrier) instead of one after another (s_tmp).
 template <int NWV, bool PACKED = false>
 __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
                                                int32_t* active, int32_t* n_active,
                                                int32_t* tiles, int32_t* n_tiles, int* s_off,
-                                               int* s_tmp, int cm = 0,
-                                               int32_t* chunks = nullptr,
-                                               int32_t* n_chunks = nullptr,
+                                               int* s_tmp,
                                                unsigned long long* s_tmp64 = nullptr) {
   const int e = threadIdx.x;
   const int nt = (cnt + kTileM - 1) / kTileM;
-  const int nc = cm > 0 ? (cnt + cm - 1) / cm : 0;
-  int total, n_act, n_t, n_c = 0, off, apos, tpos, cpos = 0;
+  int total, n_act, n_t, off, apos, tpos;
   if constexpr (PACKED) {
     const unsigned long long v = (unsigned long long)cnt | (unsigned long long)(cnt > 0) << 16 |
-                                 (unsigned long long)nt << 32 | (unsigned long long)nc << 48;
+                                 (unsigned long long)nt << 32;
     unsigned long long all;
     const unsigned long long ex = block_excl_scan4x16<NWV>(v, s_tmp64, &all);
     off = (int)(ex & 0xFFFF), apos = (int)(ex >> 16 & 0xFFFF);
-    tpos = (int)(ex >> 32 & 0xFFFF), cpos = (int)(ex >> 48);
+    tpos = (int)(ex >> 32 & 0xFFFF);
     total = (int)(all & 0xFFFF), n_act = (int)(all >> 16 & 0xFFFF);
-    n_t = (int)(all >> 32 & 0xFFFF), n_c = (int)(all >> 48);
+    n_t = (int)(all >> 32 & 0xFFFF);
   } else {
     off = block_excl_scan<NWV>(cnt, s_tmp, &total);
     apos = block_excl_scan<NWV>(cnt > 0 ? 1 : 0, s_tmp, &n_act);
     tpos = block_excl_scan<NWV>(nt, s_tmp, &n_t);
-    if (cm > 0) cpos = block_excl_scan<NWV>(nc, s_tmp, &n_c);  // cm: block-uniform
   }
   if (e < E) {
     offsets[e] = off;
@@ -352,16 +347,11 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
         tiles[2 * (tpos + i)] = e | min(kTileM, cnt - i * kTileM) << 16;
         tiles[2 * (tpos + i) + 1] = off + i * kTileM;
       }
-    for (int i = 0; i < nc; ++i) {
-      chunks[2 * (cpos + i)] = e | min(cm, cnt - i * cm) << 16;
-      chunks[2 * (cpos + i) + 1] = off + i * cm;
-    }
   }
   if (e == 0) {
     offsets[E] = total;
     *n_active = n_act;
     if (n_tiles) *n_tiles = n_t;
-    if (cm > 0) *n_chunks = n_c;
   }
 }
 
@@ -370,11 +360,14 @@ __device__ __forceinline__ void finish_offsets(int cnt, int E, int32_t* offsets,
 // One wave per token, 4 per block (the first nt = ceil(T / 4) blocks).  The
 // wave sums its token's S = H / 128 partial logits in slice order, scales by
 // 1/rms from the slices' sums of x^2 when norm, adds the bias (storing the
-// logits when logits is given), then selects.  Each block publishes its
-// selections and takes a ticket from an arrival counter (zeroed by the router
-// kernel before this kernel starts); the block with the last ticket then sees
+// logits when logits is given), then selects (threshold selection for
+// k <= 8).  Each block publishes its selections and takes a ticket from an
+// arrival counter (zeroed by the router kernel before this kernel starts);
+// the block with the last ticket then sees
 // every selection and counts (one 64-bit token mask per expert), scans and
-// scatters for all T tokens.  Nothing waits on another block.
+// scatters for all T tokens.  Nothing waits on another block.  group = 0: the
+// blocks stop after publishing their selections (the small-M expert kernels
+// rebuild the grouping from them).
 // qnl > 0: nt more blocks code x for the grouped kernels (qnl int8 limbs, or
 // digits for 2), wave w of block nt + j token 4 j + w; they take no ticket,
 // and their work overlaps the last block's grouping.
@@ -382,17 +375,19 @@ template <bool BF16, int H>
 __global__ __launch_bounds__(256) void k_route_small(
     const float* __restrict__ part, const float* __restrict__ ssp, int norm,
     const float* __restrict__ bias, float* __restrict__ logits,
-    int T, int E, int k, int renorm, int32_t* __restrict__ idx,
+    int T, int E, int k, int renorm, float f0, int32_t* __restrict__ idx,
     float* __restrict__ gate, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_tok,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-    int32_t* __restrict__ ctr, int cm, int32_t* __restrict__ chunks,
-    int32_t* __restrict__ n_chunks, int qnl, const void* __restrict__ x,
+    int32_t* __restrict__ ctr, int group, int qnl, const void* __restrict__ x,
     int8_t* __restrict__ xq, float* __restrict__ xs) {
   __shared__ int s_idx[64 * 8];
   __shared__ unsigned long long s_mask[256];
   __shared__ int s_off[256];
   __shared__ unsigned long long s_tmp64[4];
+  __shared__ long long s_cand[4][kTopkCands];
+  __shared__ int s_sel[4][8];
+  __shared__ float s_val[4][8];
   __shared__ int s_last;
   constexpr int S = H / 128;  // K slices of the partial logits
   const int tid = threadIdx.x, lane = tid & 63;
@@ -444,15 +439,17 @@ __global__ __launch_bounds__(256) void k_route_small(
         if (logits) logits[(int64_t)t * E + e] = lv[0][m];
       }
     }
-    int i[1];
-    float g[1];
-    wave_topk_lanes<1>(lv, E, k, renorm != 0, lane, i, g);
+    const int w = tid >> 6;
+    int i;
+    float g;
+    wave_topk_gates(lv[0], E, k, renorm != 0, f0, lane, s_cand[w], s_sel[w], s_val[w], &i, &g);
     if (lane < k) {
-      idx[t * k + lane] = i[0];
-      gate[t * k + lane] = g[0];
+      idx[t * k + lane] = i;
+      gate[t * k + lane] = g;
     }
   }
-  __threadfence();  // release the selections before the ticket
+  if (!group) return;  // the expert kernels group the selections themselves
+  __threadfence();     // release the selections before the ticket
   __syncthreads();
   if (tid == 0) s_last = atomicAdd(ctr, 1) == nt - 1;
   __syncthreads();
@@ -464,8 +461,8 @@ __global__ __launch_bounds__(256) void k_route_small(
   for (int q = tid; q < T * k; q += 256) atomicOr(&s_mask[s_idx[q]], 1ull << (q / k));
   __syncthreads();
   const int cnt = (tid < E) ? __popcll(s_mask[tid]) : 0;
-  finish_offsets<4, true>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, nullptr, cm,
-                          chunks, n_chunks, s_tmp64);
+  finish_offsets<4, true>(cnt, E, offsets, active, n_active, tiles, n_tiles, s_off, nullptr,
+                          s_tmp64);
   __syncthreads();
   for (int q = tid; q < T * k; q += 256) {
     const int tq = q / k, e = s_idx[q];
@@ -621,9 +618,10 @@ hipError_t launch_route(const Dims& d, int64_t T, const void* x, bool x_bf16, co
       launch("route_small", x_bf16 ? k_route_small<true, HH> : k_route_small<false, HH>,
              qnl ? 2 * nt : nt, 256, 0, s, ws.lpart, ssp, norm, bias,
              store_logits ? ws.logits : nullptr,
-             (int)T, d.E, d.k, renorm, ws.idx, ws.gate, ws.offsets, ws.active, ws.n_active,
-             ws.sorted_tok, ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr, chunk_m, ws.chunks,
-             ws.n_chunks, qnl, x, ws.xq, ws.xs);
+             (int)T, d.E, d.k, renorm, topk_f0(d.E, d.k), ws.idx, ws.gate, ws.offsets, ws.active,
+             ws.n_active,
+             ws.sorted_tok, ws.slot_pos, ws.tiles, ws.n_tiles, ws.route_ctr, chunk_m > 0 ? 0 : 1,
+             qnl, x, ws.xq, ws.xs);
     };
     switch (d.H) {
       case 256: go(std::integral_constant<int, 256>{}); break;

@@ -591,4 +591,38 @@ __device__ __forceinline__ void wave_topk_lanes(const float (&l)[NT][4], int E, 
   }
 }
 
+// The result of wave_topk_lanes<1> (lane j < k: selection j and its gate,
+// renormalised over the k when asked; 0 and 0 on lanes >= k) from the
+// threshold selection when k <= 8, the rounds otherwise.  The gates are formed
+// from the same max, normaliser and logits either way, so both give the same
+// bits.  s_cand (kTopkCands long longs), s_sel and s_val (k entries each) are
+// this wave's LDS.
+__device__ __forceinline__ void wave_topk_gates(const float (&l)[4], int E, int k, bool renorm,
+                                                float f0, int lane, long long* s_cand,
+                                                int* s_sel, float* s_val, int* sel,
+                                                float* gate) {
+  if (k > 8) {
+    float l1[1][4] = {{l[0], l[1], l[2], l[3]}};
+    int i1[1];
+    float g1[1];
+    wave_topk_lanes<1>(l1, E, k, renorm, lane, i1, g1);
+    *sel = i1[0];
+    *gate = g1[0];
+    return;
+  }
+  float mx, s;
+  wave_topk_thresh(l, E, k, f0, lane, s_cand, s_sel, s_val, &mx, &s);
+  wave_lds_sync();
+  int e = 0;
+  float v = -INFINITY;
+  if (lane < k) {
+    e = s_sel[lane];
+    v = s_val[lane];
+  }
+  float g = lane < k ? expf(v - mx) / s : 0.f;
+  if (renorm) g /= wave_sum_f(g);
+  *sel = e;
+  *gate = g;
+}
+
 }  // namespace maple
