@@ -999,8 +999,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
 // against the same weight registers, made the heavy experts' blocks the
 // tail: slower at 64 tokens.)
 
-// Gate/up: a block (8 waves) = one chunk x 128 h columns (I / 128 blocks per
-// chunk).  Wave w computes h columns [c0 + 16 w, c0 + 16 w + 16): the 16 gate
+// Gate/up: a work item of a block (8 waves) = one chunk x 128 h columns
+// (I / 128 items per chunk).  Wave w computes h columns [c0 + 16 w, c0 + 16 w + 16): the 16 gate
 // rows and the 16 matching up rows over all of K.  The chunk's x limbs (NL
 // SC rows of H bytes) are staged in LDS and read by all eight waves as B.
 // Load order matters: the vector-memory counter drains in order, so the x
@@ -1028,10 +1028,8 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
   __shared__ __align__(16) int8_t sX[16][XROW];
   __shared__ float s_sx[16];
   __shared__ int s_q[16][NL];
-  __shared__ unsigned long long s_mask[256];  // expert -> mask of the tokens that chose it
-  __shared__ int s_wt[4];                     // packed totals of the four expert waves
-  __shared__ int s_off[256];                  // each expert's first slot
-  __shared__ int s_ctab[kSmMaxChunks];        // chunk -> expert | index within the expert << 8
+  __shared__ __align__(16) unsigned long long s_mask[256];  // expert -> its tokens' bits
+  __shared__ int s_off[256];                                // block 0: experts' first slots
   // the wave index as a wave-uniform value: the staging tokens then sit in
   // scalar registers
   const int tid = threadIdx.x, lane = tid & 63,
@@ -1047,48 +1045,49 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
   __syncthreads();
   if (tid < Tk) atomicOr(&s_mask[sel], 1ull << (tid / k));
   __syncthreads();
-  // thread e < 256 (waves 0 to 3): expert e's slot and chunk counts, their
-  // exclusive prefix sums packed as first slot | first chunk << 16 (totals
-  // stay below 2^16)
-  unsigned long long em = 0ull;
-  int cnt = 0, nc = 0, ex = 0;
-  if (tid < 256) {
-    em = s_mask[tid];
-    cnt = __popcll(em);
-    nc = (cnt + SC - 1) / SC;
-    const int v = cnt | nc << 16;
-    const int inc = wave_incl_scan(v, lane);
-    if (lane == 63) s_wt[wave] = inc;
-    ex = inc - v;
-  }
-  __syncthreads();
-  int all = 0;
+  // every wave, redundantly: lane l holds experts 4 l .. 4 l + 3, their slot
+  // and chunk counts (cn: count | chunks << 16) and the exclusive prefix sums
+  // of both over the experts before them (pk: first slot | first chunk << 16;
+  // totals stay below 2^16)
+  int cn[4], pk[4];
+  int all;
+  {
+    const ulonglong2 m01 = *reinterpret_cast<const ulonglong2*>(&s_mask[4 * lane]);
+    const ulonglong2 m23 = *reinterpret_cast<const ulonglong2*>(&s_mask[4 * lane + 2]);
+    const unsigned long long m4[4] = {m01.x, m01.y, m23.x, m23.y};
+    int run = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int t = s_wt[w];
-    ex += w < wave ? t : 0;
-    all += t;
+    for (int m = 0; m < 4; ++m) {
+      const int cnt = __popcll(m4[m]);
+      cn[m] = cnt | ((cnt + SC - 1) / SC) << 16;
+      pk[m] = run;
+      run += cn[m];
+    }
+    const int inc = wave_incl_scan(run, lane);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pk[m] += inc - run;
+    all = __builtin_amdgcn_readlane(inc, 63);
   }
   const int n_ch = all >> 16;
-  if (tid < 256) {
-    const int cpos = ex >> 16;
-    s_off[tid] = ex & 0xFFFF;
-    for (int i = 0; i < nc; ++i) s_ctab[cpos + i] = tid | i << 8;
-  }
-  __syncthreads();
   if (blockIdx.x == 0) {  // block-uniform: the grouping for the down and combine kernels
-    const int off = ex & 0xFFFF, cpos = ex >> 16;
-    if (tid < E) {
-      offsets[tid] = off;
-      for (int i = 0; i < nc; ++i) {
-        chunks[2 * (cpos + i)] = tid | min(SC, cnt - i * SC) << 16;
-        chunks[2 * (cpos + i) + 1] = off + i * SC;
+    if (wave == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int ee = 4 * lane + m, off = pk[m] & 0xFFFF, cpos = pk[m] >> 16;
+        const int cnt = cn[m] & 0xFFFF, nc = cn[m] >> 16;
+        s_off[ee] = off;
+        if (ee < E) offsets[ee] = off;
+        for (int i = 0; i < nc; ++i) {
+          chunks[2 * (cpos + i)] = ee | min(SC, cnt - i * SC) << 16;
+          chunks[2 * (cpos + i) + 1] = off + i * SC;
+        }
+      }
+      if (lane == 0) {
+        offsets[E] = all & 0xFFFF;
+        *n_chunks = n_ch;
       }
     }
-    if (tid == 0) {
-      offsets[E] = all & 0xFFFF;
-      *n_chunks = n_ch;
-    }
+    __syncthreads();
     if (tid < Tk) {
       const int tq = tid / k;
       const int pos = s_off[sel] + __popcll(s_mask[sel] & ((1ull << tq) - 1ull));
@@ -1096,6 +1095,9 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
       sorted_tok[pos] = tq;
     }
   }
+  // a lane's chunks: [first chunk of its expert 4 l, that plus its four
+  // experts' chunk counts)
+  const int lc0 = pk[0] >> 16, lc1 = (pk[3] + cn[3]) >> 16;
   // work items (chunk, 128-column part) spread over the XCDs as xcd_tile
   // does; the grid (a multiple of 8, at most what the chip holds at once)
   // takes them in rounds
@@ -1104,11 +1106,18 @@ __global__ __launch_bounds__(512, H <= 2048 ? 4 : 2) void k_sm_gateup(
   const int item = (blockIdx.x & 7) * per_xcd + j;
   if (item >= n_items) break;  // block-uniform
   const int c = item / NB, cb = (item % NB) * 128;
-  const int crec = s_ctab[c];
-  const int e = __builtin_amdgcn_readfirstlane(crec & 0xFF);
-  const int i0 = __builtin_amdgcn_readfirstlane(crec >> 8) * SC;
+  // chunk c's expert: the lane whose chunk range holds c, then the last of
+  // its experts that starts at or before c (experts without chunks share the
+  // next one's start)
+  const int L = (int)__builtin_ctzll(__ballot(c >= lc0 && c < lc1));
+  const int mm = (c >= (pk[1] >> 16)) + (c >= (pk[2] >> 16)) + (c >= (pk[3] >> 16));
+  const int pkm = mm == 0 ? pk[0] : mm == 1 ? pk[1] : mm == 2 ? pk[2] : pk[3];
+  const int m_own = __builtin_amdgcn_readlane(mm, L);
+  const int pk_own = __builtin_amdgcn_readlane(pkm, L);
+  const int e = 4 * L + m_own;
+  const int i0 = (c - (pk_own >> 16)) * SC;
   const unsigned long long cmask = s_mask[e];
-  const int p0 = __builtin_amdgcn_readfirstlane(s_off[e]) + i0;
+  const int p0 = (pk_own & 0xFFFF) + i0;
   const int np = min(SC, __popcll(cmask) - i0);
   // token of the chunk's slot sl: the set bit of the mask with i0 + sl set
   // bits below it (one ballot; wave-uniform)

@@ -104,8 +104,6 @@ int max_tiles(const Dims& d, int64_t T);
 // tiled kernels run instead.
 int small_m_chunk(const Dims& d, int64_t T, int nl);
 int max_chunks(const Dims& d, int64_t T);
-// max_chunks at its largest (64 tokens, top-8, 256 experts)
-constexpr int kSmMaxChunks = 64 * 8 / 5 + 256 + 1;
 
 // ---- launchers (each returns hipError_t of the launch) ----
 hipError_t launch_pack(const int8_t* w, int64_t n_words, uint32_t* out, int32_t* bad,
