@@ -124,42 +124,42 @@ def prefill_ops(kernel, H, k, I, T):
 # counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "dec_down": {"bytes": 4509649, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6a993e437d716e56"},
-        "dec_gateup": {"bytes": 4742233, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6a993e437d716e56"},
-        "dec_router": {"bytes": 2168177, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6a993e437d716e56"},
-        "load_token": {"bytes": 13683, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "8045bf3489503dde"},
-        "store_token": {"bytes": 29462, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "8045bf3489503dde"},
+        "dec_down": {"bytes": 4509649, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1574497431f75556"},
+        "dec_gateup": {"bytes": 4742239, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1574497431f75556"},
+        "dec_router": {"bytes": 2168219, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1574497431f75556"},
+        "load_token": {"bytes": 13703, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
+        "store_token": {"bytes": 29466, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 170783640, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "down_mfma": {"bytes": 244686350, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "gateup_mfma": {"bytes": 325651829, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "quant_x": {"bytes": 35971895, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "route_block": {"bytes": 343913, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "route_scan": {"bytes": 146487, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "route_scatter": {"bytes": 1209256, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "route_topk": {"bytes": 4488538, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "router_mfma": {"bytes": 37792648, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "split_router": {"bytes": 4206558, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "combine": {"bytes": 170766581, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "down_mfma": {"bytes": 244753172, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "gateup_mfma": {"bytes": 325743485, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "quant_x": {"bytes": 35977822, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "route_block": {"bytes": 343883, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scan": {"bytes": 146456, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 1209256, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 4488568, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 37792663, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4206452, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 170792668, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "down_mfma": {"bytes": 275316580, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "gateup_mfma": {"bytes": 268669924, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "quant_x": {"bytes": 25316676, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "route_block": {"bytes": 344192, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "route_scan": {"bytes": 146464, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "route_scatter": {"bytes": 1209440, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "route_topk": {"bytes": 4488704, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "router_mfma": {"bytes": 37792984, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "split_router": {"bytes": 4207028, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "combine": {"bytes": 170772832, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "down_mfma": {"bytes": 275266612, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "gateup_mfma": {"bytes": 268656012, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "quant_x": {"bytes": 25316412, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "route_block": {"bytes": 343936, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scan": {"bytes": 146400, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 1209120, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 4488576, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 37792744, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4206748, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5273316, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "down_mfma": {"bytes": 39191888, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "gateup_mfma": {"bytes": 69825229, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "223877317b4b7e88"},
-        "route_small": {"bytes": 2134426, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
-        "router_split": {"bytes": 3694941, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "c8ba0a2b265fc36b"},
+        "combine": {"bytes": 5273316, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "down_mfma": {"bytes": 39196156, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "gateup_mfma": {"bytes": 69918424, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
+        "route_small": {"bytes": 2148597, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_split": {"bytes": 3694903, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
 }
 
