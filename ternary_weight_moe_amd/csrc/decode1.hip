@@ -461,13 +461,14 @@ __global__ __launch_bounds__(512) void k_dec_router(const void* __restrict__ x,
 // of 16 gate rows and the same 16 up rows; wave w (of 8) reduces K range
 // [w H/8, (w+1) H/8).  First, with no block barrier, wave w forms the router
 // values of experts [32 w, 32 w + 32) from their partial dots (two lanes per
-// expert, half of the groups each) with their max and sum, 1/rms and the
-// coding scale of x from the groups' statistics, and the limbs of its K range
-// of x.  Without a router bias the ranking runs on the dot products
-// themselves (1/rms > 0 does not change the order), so all these reductions
-// are independent; with one the values are the logits d / rms + b.  After one
-// barrier wave 0 selects the top k while the other waves form their share of
-// the softmax normaliser; after a second the weights of expert j load.  The
+// expert, half of the groups each) with their max and sum, and 1/rms and the
+// coding scale of x from the groups' statistics.  Without a router bias the
+// ranking runs on the dot products themselves (1/rms > 0 does not change the
+// order), so all these reductions are independent; with one the values are
+// the logits d / rms + b.  After one barrier wave 0 selects the top k while
+// the other waves form their share of the softmax normaliser; after a second
+// the weights of expert j load, and meanwhile each wave codes its K range of
+// x into limbs (only it reads them, so no barrier waits on the coding).  The
 // gates (written by block (0, j) for the down kernel) are formed in the
 // epilogue; block (0, 0) also stores the logits and the one-token grouping
 // (offsets, slot positions, ...).
@@ -543,14 +544,6 @@ __global__ __launch_bounds__(512) void k_dec_gateup(
       s_wst[wave][2] = (float)nf;
     }
   }
-  // x -> limbs in LDS; the limb sums are reduced later, while the weights load
-  int qh = 0, qm = 0, ql = 0;
-  {
-    uint32_t lw[3][XPL / 4];
-    code3_row<XPL>(xv, 1.f / scale, lw, &qh, &qm, &ql);
-#pragma unroll
-    for (int l = 0; l < 3; ++l) store_words<XPL>(&s_xq[l][x0], lw[l]);
-  }
   __syncthreads();
   // the largest logit: in ranking values, and as a logit
   float vmax = -INFINITY;
@@ -606,6 +599,15 @@ __global__ __launch_bounds__(512) void k_dec_gateup(
   }
   const float ag = alpha[(int64_t)e * (2 * I + H) + row];
   const float au = alpha[(int64_t)e * (2 * I + H) + I + row];
+  // x -> limbs in LDS while the weights load: each wave codes the K range
+  // whose limbs only it reads
+  int qh = 0, qm = 0, ql = 0;
+  {
+    uint32_t lw[3][XPL / 4];
+    code3_row<XPL>(xv, 1.f / scale, lw, &qh, &qm, &ql);
+#pragma unroll
+    for (int l = 0; l < 3; ++l) store_words<XPL>(&s_xq[l][x0], lw[l]);
+  }
   if (wave == 0) {  // wave 0's share of the normaliser
     const float lg = has_bias ? rv : rv * rinv;
     const float ew = wave_sum_f(mine ? expf((lg == lg ? lg : -INFINITY) - lmax) : 0.f);
@@ -639,6 +641,7 @@ __global__ __launch_bounds__(512) void k_dec_gateup(
     s_q[wave][1] = qm;
     s_q[wave][2] = ql;
   }
+  wave_lds_sync();  // the wave's own limbs, stored by its other lanes
   v4i af[NSS][4];
 #pragma unroll
   for (int ss2 = 0; ss2 < NSS; ++ss2)
