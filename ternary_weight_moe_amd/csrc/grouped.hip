@@ -31,10 +31,8 @@
 // which k each of their bytes holds; both use: in a super-step of 64*SS codes,
 // lane group g = lane/16 covers words [SS*g, SS*g + SS) and MFMA step s uses
 // word SS*g + s.  A row's super-step then comes from one 16-byte load per lane.
-#include <map>
 #include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "internal.h"
 #include "limbs.h"
@@ -1514,21 +1512,27 @@ hipError_t launch_quant_x(const Dims& d, int64_t T, const void* x, bool x_bf16, 
 
 // Blocks of a kernel that the current device holds at once (its occupancy
 // at `threads` threads per block times the compute units), cached per kernel
-// and device; 0 if the runtime cannot tell.
+// and device in a fixed table (no allocation: the allocation-free entry point
+// launches through here too); 0 if the runtime cannot tell.
 static int resident_blocks(const void* kernel, int threads) {
+  struct Entry {
+    const void* kernel;
+    int dev, blocks;
+  };
+  constexpr int kEntries = 64;
+  static Entry table[kEntries];
+  static int used = 0;
   static std::mutex mu;
-  static std::map<std::pair<const void*, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(kernel, dev);
-  const auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
+  for (int i = 0; i < used; ++i)
+    if (table[i].kernel == kernel && table[i].dev == dev) return table[i].blocks;
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  cache[key] = per_cu * cus;
+  if (used < kEntries) table[used++] = Entry{kernel, dev, per_cu * cus};
   return per_cu * cus;
 }
 

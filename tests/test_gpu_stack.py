@@ -164,3 +164,58 @@ def test_batched_stack_call_captured_in_a_graph(zipf):
         assert np.array_equal(xw.cpu().numpy(), eager), f"replay {rep} differs from the eager call"
     x64 = S.x_as_f32(w, x).astype(np.float64)
     assert_close(eager - x64, ref["x"] - x64, "zipf stack in a graph, x_L - x_0")
+
+
+CAPTURE_FIRST = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+from ternary_weight_moe_amd import _native as N
+from ternary_weight_moe_amd import synth as S
+w = S.WORKLOADS["batched_stack_zipf"]
+H, E, k, I, T = w.hidden, w.n_experts, w.top_k, w.inter, w.n_tokens
+W = S.gen_layer_weights(w, 0)
+wt = torch.from_numpy(W.reshape(-1)).cuda()
+packed = torch.empty(W.size // 4, dtype=torch.uint8, device="cuda")
+N.maple_ternary_pack_device(wt, packed)
+bias = S.gen_router_bias(w, 0)
+Wr = torch.from_numpy(S.gen_router(w, 0)).cuda()
+b = None if bias is None else torch.from_numpy(bias).cuda()
+alpha = torch.from_numpy(S.gen_alpha(w, 0)).cuda()
+x = torch.from_numpy(S.x_as_f32(w, S.gen_x(w, T)).copy()).cuda()
+d = N.make_dims(H, E, k, I, N.MAPLE_FINE_LIMBS)
+ws = torch.empty(N.maple_moe_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+s = torch.cuda.Stream()
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=s):  # the library's first expert-kernel launch
+    N.maple_moe_layer_forward(d, T, x, Wr, b, packed, alpha, out, ws, stream=s)
+reps = []
+for rep in range(2):
+    out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    reps.append(out.cpu().numpy().copy())
+N.maple_moe_layer_forward(d, T, x, Wr, b, packed, alpha, out, ws)
+torch.cuda.synchronize()
+eager = out.cpu().numpy()
+assert np.isfinite(eager).all()
+for rep, r in enumerate(reps):
+    assert np.array_equal(r, eager), f"replay {rep} differs from the eager call"
+print("capture-first ok")
+"""
+
+
+def test_small_m_layer_captured_before_any_eager_call():
+    """A fresh process whose first expert-kernel launch happens inside a graph
+    capture (the small-M gate/up kernel sizes its grid from an occupancy query
+    on its first launch): the replays equal a later eager call bit for bit."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", CAPTURE_FIRST, root], capture_output=True,
+                       text=True, timeout=110)
+    assert r.returncode == 0 and "capture-first ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
