@@ -124,42 +124,42 @@ def prefill_ops(kernel, H, k, I, T):
 # counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "dec_down": {"bytes": 4509649, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1574497431f75556"},
-        "dec_gateup": {"bytes": 4742239, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1574497431f75556"},
-        "dec_router": {"bytes": 2168219, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "1574497431f75556"},
-        "load_token": {"bytes": 13703, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
-        "store_token": {"bytes": 29466, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
+        "dec_down": {"bytes": 4509645, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
+        "dec_gateup": {"bytes": 4742347, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
+        "dec_router": {"bytes": 2168200, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
+        "load_token": {"bytes": 13702, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
+        "store_token": {"bytes": 29470, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 170766581, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "down_mfma": {"bytes": 244753172, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "gateup_mfma": {"bytes": 325743485, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "quant_x": {"bytes": 35977822, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "route_block": {"bytes": 343883, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "combine": {"bytes": 170781853, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "down_mfma": {"bytes": 244759520, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "gateup_mfma": {"bytes": 325680370, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "quant_x": {"bytes": 35975021, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "route_block": {"bytes": 343944, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "route_scan": {"bytes": 146456, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scatter": {"bytes": 1209256, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_topk": {"bytes": 4488568, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "router_mfma": {"bytes": 37792663, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "split_router": {"bytes": 4206452, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 1209180, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 4488553, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 37792602, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4206526, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 170772832, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "down_mfma": {"bytes": 275266612, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "gateup_mfma": {"bytes": 268656012, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "quant_x": {"bytes": 25316412, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "route_block": {"bytes": 343936, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scan": {"bytes": 146400, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scatter": {"bytes": 1209120, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_topk": {"bytes": 4488576, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "router_mfma": {"bytes": 37792744, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "split_router": {"bytes": 4206748, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "combine": {"bytes": 170791856, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "down_mfma": {"bytes": 275328864, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "gateup_mfma": {"bytes": 268673224, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "quant_x": {"bytes": 25316204, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "route_block": {"bytes": 343872, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scan": {"bytes": 146464, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 1209184, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 4488640, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 37792732, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4206788, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5273316, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "down_mfma": {"bytes": 39196156, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "gateup_mfma": {"bytes": 69918424, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "fda2245ff43ebee4"},
-        "route_small": {"bytes": 2148597, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "router_split": {"bytes": 3694903, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "combine": {"bytes": 5273369, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "down_mfma": {"bytes": 39197922, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "gateup_mfma": {"bytes": 69919924, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
+        "route_small": {"bytes": 2148628, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_split": {"bytes": 3694964, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
 }
 
