@@ -1300,8 +1300,14 @@ __global__ __launch_bounds__(256) void k_sm_down(
     }
   };
   fetch(0);
-  // h (an ordinary load) does not sink below this barrier, and the weight
-  // addresses come out of it: the h loads stay ahead of the weights
+  // a_d of the lane's output rows o0 + 64 wave + 16 b + 4 g + jj, loaded
+  // here so that the epilogue does not wait a round trip for them
+  const float* adp = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0 + 64 * wave + 4 * g;
+  float4 ad4[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) ad4[b] = *reinterpret_cast<const float4*>(adp + 16 * b);
+  // h and a_d (ordinary loads) do not sink below this barrier, and the weight
+  // addresses come out of it: those loads stay ahead of the weights
   int wr = o0 + 64 * wave + c16;
   asm volatile("" : "+v"(wr) : : "memory");
   const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4 +
@@ -1312,8 +1318,6 @@ __global__ __launch_bounds__(256) void k_sm_down(
 #pragma unroll
     for (int ss = 0; ss < NSS; ++ss)
       bq[b][ss] = *reinterpret_cast<const uint4*>(Wd + (int64_t)16 * b * (I / 4) + 64 * ss);
-  // a_d of the lane's output rows o0 + 64 wave + 16 b + 4 g + jj
-  const float* adp = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0 + 64 * wave + 4 * g;
   if constexpr (NL * SC < 16) {  // the unused 16th column: zero, never rewritten
     if (wave == 3) {
       if constexpr (VPL == 8)
@@ -1408,7 +1412,10 @@ __global__ __launch_bounds__(256) void k_sm_down(
           v[jj] = sc * fmaf(16384.f, (float)acc[b][jj], fmaf(128.f, (float)a1, (float)a2));
         }
       }
-      const float4 a = *reinterpret_cast<const float4*>(adp + 16 * b);
+      // first use here, after the weights are consumed (used earlier, its
+      // wait would also wait for every weight load issued after it)
+      float4 a = ad4[b];
+      asm volatile("" : "+v"(a.x), "+v"(a.y), "+v"(a.z), "+v"(a.w));
       if (act)
         *reinterpret_cast<float4*>(yo + 16 * b) =
             make_float4(a.x * v[0], a.y * v[1], a.z * v[2], a.w * v[3]);
