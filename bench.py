@@ -124,42 +124,42 @@ def prefill_ops(kernel, H, k, I, T):
 # counters were taken and the traffic is unknown.
 TRAFFIC = {
     "decode_stack": {
-        "dec_down": {"bytes": 4509645, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
-        "dec_gateup": {"bytes": 4742347, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
-        "dec_router": {"bytes": 2168200, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
-        "load_token": {"bytes": 13702, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
-        "store_token": {"bytes": 29470, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
+        "dec_down": {"bytes": 4509757, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
+        "dec_gateup": {"bytes": 4742470, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
+        "dec_router": {"bytes": 2168254, "sources": ["decode1.hip", "digits.h", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "c6fb03326e0be294"},
+        "load_token": {"bytes": 13842, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
+        "store_token": {"bytes": 29588, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 170781853, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "down_mfma": {"bytes": 244759520, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "gateup_mfma": {"bytes": 325680370, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "quant_x": {"bytes": 35975021, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "route_block": {"bytes": 343944, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scan": {"bytes": 146456, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scatter": {"bytes": 1209180, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_topk": {"bytes": 4488553, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "router_mfma": {"bytes": 37792602, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "split_router": {"bytes": 4206526, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "combine": {"bytes": 170798523, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "down_mfma": {"bytes": 244679703, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "gateup_mfma": {"bytes": 325727273, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "quant_x": {"bytes": 35985533, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "route_block": {"bytes": 343959, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scan": {"bytes": 146366, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 1209225, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 4488568, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 37792632, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4206513, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 170791856, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "down_mfma": {"bytes": 275328864, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "gateup_mfma": {"bytes": 268673224, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "quant_x": {"bytes": 25316204, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "route_block": {"bytes": 343872, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scan": {"bytes": 146464, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_scatter": {"bytes": 1209184, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "route_topk": {"bytes": 4488640, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "router_mfma": {"bytes": 37792732, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "split_router": {"bytes": 4206788, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "combine": {"bytes": 170786084, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "down_mfma": {"bytes": 275293622, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "gateup_mfma": {"bytes": 268659664, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "quant_x": {"bytes": 25316336, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "route_block": {"bytes": 344000, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scan": {"bytes": 146208, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 1209440, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 4488576, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 37792760, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4206784, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5273369, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "down_mfma": {"bytes": 39197922, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "gateup_mfma": {"bytes": 69919924, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "3853d52285383db8"},
-        "route_small": {"bytes": 2148628, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
-        "router_split": {"bytes": 3694964, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "combine": {"bytes": 5270293, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "down_mfma": {"bytes": 39195098, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "gateup_mfma": {"bytes": 69930664, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "route_small": {"bytes": 2148644, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_split": {"bytes": 3694967, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
 }
 
