@@ -71,6 +71,28 @@ def test_small_m_degenerate_routing(a8):
                         what=f"small-M fine E={E} k={k}")
 
 
+@pytest.mark.parametrize("a8", [False, True], ids=["fine", "a8"])
+def test_small_m_many_rounds(a8):
+    """Hidden 4096, inter 512: one 8-wave small-M gate/up block fits a CU, so
+    the grid is the 256 blocks the chip holds, and 64 tokens at top-8 over 128
+    experts (about 4 slots each) give some 600 work items with three limbs
+    (5-slot chunks) or 500 with one (16-slot chunks): every block groups the
+    selections once and takes its items in two or three rounds.
+    Routing of all 64 tokens bit-exact, outputs of every fourth token."""
+    w = workload("tiny_layer", name=f"small_m_rounds_{'a8' if a8 else 'fine'}", hidden=4096,
+                 inter=512, n_experts=128, top_k=8, n_tokens=64, x_bf16=True,
+                 seed=7300 + (1 if a8 else 0))
+    log(f"small-M rounds a8={a8}: generating the layer")
+    L = Layer(w, 0)
+    x, _ = layer_tokens_with_gap(w, L, 64, token0=600)
+    sample = list(range(0, 64, 4))
+    if a8:
+        check_a8(w, L, x, sample=sample, what="small-M rounds a8")
+    else:
+        check_layer(w, L, x, flags=N.MAPLE_FORCE_GROUPED | N.MAPLE_FINE_LIMBS, sample=sample,
+                    what="small-M rounds fine")
+
+
 @pytest.mark.parametrize("E,k", [(40, 6), (100, 8), (250, 8)], ids=lambda v: str(v))
 def test_uneven_expert_counts(E, k):
     """Expert counts that are not multiples of the kernels' groupings (16
