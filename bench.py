@@ -27,7 +27,9 @@ kernels stamp the GPU's real-time counter at every block's entry and exit
 recorded by the library on the stream the kernel runs on.  The default
 decode_stack line also carries a ``prefill_4096`` object (the 4096-token
 layer, timed the same way as ``--workload prefill_4096``) unless
-``--no-prefill`` is given.
+``--no-prefill`` is given, and a ``batched_stack_zipf`` object (64 tokens
+per step through the stack, timed as ``--workload batched_stack_zipf``)
+unless ``--no-batched`` is given.
 """
 from __future__ import annotations
 
@@ -955,6 +957,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode_stack: leave out the prefill_4096 object")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="decode_stack: leave out the batched_stack_zipf object")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--read-probe", action="store_true",
@@ -1021,6 +1025,19 @@ def main():
         if not args.no_cpu_baseline:
             res["prefill_4096"]["cpu_baseline"] = cpu_baseline_prefill(
                 pw, args.cpu_baseline_seconds)
+    if args.workload == "decode_stack" and not args.no_batched:
+        # the batched-decode configuration (64 tokens per step through the
+        # stack, Zipf-skewed routing), timed like --workload batched_stack_zipf
+        torch.cuda.empty_cache()
+        bargs = argparse.Namespace(**vars(args))
+        bargs.workload, bargs.steps, bargs.warmup = "batched_stack_zipf", 20, 3
+        bres, bw = bench_batched(bargs, torch, N, S)
+        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "config", "roofline",
+                "step_roofline", "routing", "kernels")
+        res["batched_stack_zipf"] = {kk: bres[kk] for kk in keep}
+        if not args.no_cpu_baseline:
+            res["batched_stack_zipf"]["cpu_baseline"] = cpu_baseline_batched(
+                bw, args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)
 
 
