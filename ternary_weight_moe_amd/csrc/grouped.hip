@@ -262,12 +262,14 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
   store_a(0);
   fetch_a(min(1, nst - 1));
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
+  // One stage: its MFMAs on x buffer st & 1; with refill, each chunk's weights
+  // are refilled with stage st + 1 right after their last use; with next, the
+  // x digits of stage st + 1 go to the other buffer and those of stage st + 2
+  // are fetched.  Every stage but the last two does all of it, so the count of
+  // loads in flight is the same at every use in the loop and the waits stay
+  // partial; the second-last stage fetches no x, the last one loads nothing.
+  auto stage = [&](int st, bool refill, bool next) __attribute__((always_inline)) {
     const uint8_t* sb = smem + (st & 1) * ABUF + r32 * ROWB + kPairBytes * kg;
-    // loads are issued unconditionally (the last stage reloads itself) so the
-    // count of loads in flight is the same at every use and the waits stay
-    // partial
-    const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -301,14 +303,20 @@ __global__ __launch_bounds__(256, NS) void k_gateup_mfma(
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (unpacking)
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (refill) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) bq[c][b] = bload(b, st1, c);  // refill after the last use
+        for (int b = 0; b < NB; ++b) bq[c][b] = bload(b, st + 1, c);  // refill after the last use
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_a((st + 1) & 1);  // stage st1; its buffer was last read in stage st - 1
-    fetch_a(st2);
+    if (refill) store_a((st + 1) & 1);  // stage st + 1; its buffer was last read in stage st - 1
+    if (next) fetch_a(st + 2);
     __syncthreads();
-  }
+  };
+  int st = 0;
+  for (; st + 2 < nst; ++st) stage(st, true, true);
+  if (nst >= 2) stage(nst - 2, true, false);
+  stage(nst - 1, false, false);
 
   // Epilogue.  The weights were the MFMA's first operand, so lane (r32, kg)
   // holds slot m = r32 and, in register 4i + t of N-subtile b, h column
@@ -454,16 +462,25 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
   const int HB = nch * CH;       // its outputs
   const int o0 = hp * HB;        // the first of them
   const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0;
-  // lane's weight row in N-subtile b of chunk c: o0 + c*CH + 32*(NBW*wave + b) + r32
-  const uint8_t* wrow = Wd + (int64_t)(o0 + 32 * NBW * wave + r32) * (I / 4) + 16 * kg;
-  auto bptr = [&](int c, int b, int q) {
-    return reinterpret_cast<const uint4*>(wrow + (int64_t)(c * CH + 32 * b) * (I / 4) + 32 * q);
+  // Weights by buffer loads from the block's HB output rows: the lane's row in
+  // N-subtile b of chunk c is o0 + c*CH + 32*(NBW*wave + b) + r32.  wnone
+  // has no records: a load through it returns zeros and reads no memory, which
+  // is how the last chunk refills (every chunk then issues the same loads, so
+  // the waits stay partial, and none is wasted).
+  const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wd + (int64_t)o0 * (I / 4)), 0, HB * (I / 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wnone = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wd), 0, 0, kBufferWord3);
+  const int wvoff = (32 * NBW * wave + r32) * (I / 4) + 16 * kg;
+  auto bload = [&](__amdgpu_buffer_rsrc_t src, int c, int b, int q) {
+    return as_u4(__builtin_amdgcn_raw_buffer_load_b128(src, wvoff,
+                                                       (c * CH + 32 * b) * (I / 4) + 32 * q, 0));
   };
   uint4 bq[NBW][NQ];
 #pragma unroll
   for (int b = 0; b < NBW; ++b)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) bq[b][q] = *bptr(0, b, q);
+    for (int q = 0; q < NQ; ++q) bq[b][q] = bload(wsrc, 0, b, q);
   // h digits of the tile's slots: TM rows of HROW bytes; rows past np are zero.
   // All loads are issued before the first LDS store.
   constexpr int SEGR = HROW / 16;
@@ -521,7 +538,7 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
     // keeps the B-operand LDS reads inside the loop (hoisted, they would hold
     // the whole h tile in registers and halve the blocks a CU can run)
     asm volatile("" ::: "memory");
-    const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
+    const auto rsrc = c + 1 < nch ? wsrc : wnone;  // the last chunk refills from no records
     v16f_t acc[NS][NBW];  // [h part][N-subtile]
 #pragma unroll
     for (int h2 = 0; h2 < NS; ++h2)
@@ -553,7 +570,7 @@ __global__ __launch_bounds__(64 * NWV) void k_down_mfma(
         for (int b = 0; b < NBW; ++b) acc[h2][b] = mfma_digits<2>(wf[b], dp[2], acc[h2][b]);
       }
 #pragma unroll
-      for (int b = 0; b < NBW; ++b) bq[b][q] = *bptr(cn, b, q);
+      for (int b = 0; b < NBW; ++b) bq[b][q] = bload(rsrc, c + 1, b, q);
     }
     // register 4i + t holds output 32 (NBW wave + b) + 8 i + 4 kg + t of the chunk:
     // y[slot][o] = a_d[o] * sum_parts s * acc as fp16, first into the wave's
