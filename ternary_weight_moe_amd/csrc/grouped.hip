@@ -719,18 +719,21 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
   store_a(0);
   fetch_a(min(1, nst - 1));
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
+  // One stage: its MFMAs on x buffer st & 1; with refill the weights of stage
+  // st + 1 load first, into a second register set (a whole stage of MFMAs
+  // hides their latency: loaded after the stage, they were waited for at the
+  // start of the next one), and its x limbs go to the other buffer after the
+  // MFMAs; with next the x limbs of stage st + 2 are fetched.  Every stage but
+  // the last two does all of it, so the count of loads in flight is the same at
+  // every use in the loop and the waits stay partial; the second-last stage
+  // fetches no x, the last one loads nothing.
+  auto stage = [&](int st, bool refill, bool next) __attribute__((always_inline)) {
     const int8_t* sa = smem + (st & 1) * ABUF + r16 * ROWB + 64 * kg;
-    // loads are issued unconditionally (past the end a stage reloads the last)
-    // so the count of loads in flight is the same at every use and the waits
-    // stay partial
-    const int st1 = min(st + 1, nst - 1), st2 = min(st + 2, nst - 1);
-    // the next stage's weights first, into a second register set: a whole
-    // stage of MFMAs hides their latency (loaded after the stage, they were
-    // waited for at the start of the next one)
     uint4 bqn[4];
+    if (refill) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bqn[b] = *bsrc(b, st1);
+      for (int b = 0; b < 4; ++b) bqn[b] = *bsrc(b, st + 1);
+    }
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       v4i wf[4];
@@ -751,12 +754,17 @@ __global__ __launch_bounds__(256, 2) void k_gateup3_mfma(
         }
       }
     }
+    if (refill) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bq[b] = bqn[b];
-    store_a((st + 1) & 1);  // stage st1; its buffer was last read in stage st - 1
-    fetch_a(st2);
+      for (int b = 0; b < 4; ++b) bq[b] = bqn[b];
+      store_a((st + 1) & 1);  // stage st + 1; its buffer was last read in stage st - 1
+    }
+    if (next) fetch_a(st + 2);
     __syncthreads();
-  }
+  };
+  for (int st = 0; st + 2 < nst; ++st) stage(st, true, true);
+  if (nst >= 2) stage(nst - 2, true, false);
+  stage(nst - 1, false, false);
 
   // Epilogue: lane (r16, kg) holds slot 16 h2 + r16 and, in register j of
   // subtile b, h column cbase + 16 (b & 1) + 4 kg + j.
@@ -840,16 +848,30 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
   const int o0 = hp * nch * CH;  // its first output
   const uint8_t* Wd = packed + (int64_t)e * 3 * H * I / 4 + 2 * (int64_t)I * H / 4;
   const float* ad = alpha + (int64_t)e * (2 * I + H) + 2 * I + o0;
-  const uint8_t* wrow = Wd + (int64_t)(o0 + 64 * wave + r16) * (I / 4) + 4 * PW * kg;
-  auto bptr = [&](int c, int b, int q) {
-    return reinterpret_cast<const wq_t*>(wrow + (int64_t)(c * CH + 16 * b) * (I / 4) +
-                                         16 * PW * q);
+  // Weights by buffer loads from the block's nch CH output rows: the lane's
+  // row in subtile b of chunk c is o0 + c*CH + 64*wave + 16*b + r16.  wnone
+  // has no records: a load through it returns zeros and reads no memory, which
+  // is how the last chunk refills (every chunk then issues the same loads, so
+  // the waits stay partial, and none is wasted).
+  const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wd + (int64_t)o0 * (I / 4)), 0, nch * CH * (I / 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wnone = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wd), 0, 0, kBufferWord3);
+  const int wvoff = (64 * wave + r16) * (I / 4) + 4 * PW * kg;
+  auto bload = [&](__amdgpu_buffer_rsrc_t src, int c, int b, int q) -> wq_t {
+    const int soff = (c * CH + 16 * b) * (I / 4) + 16 * PW * q;
+    if constexpr (PW == 4) {
+      return as_u4(__builtin_amdgcn_raw_buffer_load_b128(src, wvoff, soff, 0));
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, wvoff, soff, 0);
+      return make_uint2(v[0], v[1]);
+    }
   };
   wq_t bq[4][NQ];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) bq[b][q] = *bptr(0, b, q);
+    for (int q = 0; q < NQ; ++q) bq[b][q] = bload(wsrc, 0, b, q);
   // the wave's h rows (rows past np are zero), all loads before any use
   typedef float hv_t __attribute__((ext_vector_type(VW)));
   hv_t hv[RPW][NPC];
@@ -930,7 +952,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
     // keeps the B-operand LDS reads inside the loop (hoisted, they would hold
     // most of the registers for the whole block)
     asm volatile("" ::: "memory");
-    const int cn = min(c + 1, nch - 1);  // the last chunk reloads itself: the waits stay partial
+    const auto rsrc = c + 1 < nch ? wsrc : wnone;  // the last chunk refills from no records
     v4i acc[2][NL][4];  // [slot half][limb][subtile]
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -964,7 +986,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_down3_mfma(
         }
       }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bq[b][q] = *bptr(cn, b, q);
+      for (int b = 0; b < 4; ++b) bq[b][q] = bload(rsrc, c + 1, b, q);
     }
     // register j of subtile b: output 64 wave + 16 b + 4 kg + j of the chunk
 #pragma unroll
