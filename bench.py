@@ -133,10 +133,10 @@ TRAFFIC = {
         "store_token": {"bytes": 29588, "sources": ["digits.h", "internal.h", "limbs.h", "misc.hip", "quant.h", "wave.h"], "digest": "bcde7b468f9449a2"},
     },
     "prefill_4096": {
-        "combine": {"bytes": 170798523, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "down_mfma": {"bytes": 244679703, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "gateup_mfma": {"bytes": 325727273, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "quant_x": {"bytes": 35985533, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "combine": {"bytes": 170791980, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "down_mfma": {"bytes": 244620696, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "gateup_mfma": {"bytes": 325966770, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "quant_x": {"bytes": 35893564, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
         "route_block": {"bytes": 343959, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "route_scan": {"bytes": 146366, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "route_scatter": {"bytes": 1209225, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
@@ -145,10 +145,10 @@ TRAFFIC = {
         "split_router": {"bytes": 4206513, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "prefill_4096_a8": {
-        "combine": {"bytes": 170786084, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "down_mfma": {"bytes": 275293622, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "gateup_mfma": {"bytes": 268659664, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "quant_x": {"bytes": 25316336, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "combine": {"bytes": 170773632, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "down_mfma": {"bytes": 274868142, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "gateup_mfma": {"bytes": 268965192, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "quant_x": {"bytes": 25316412, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
         "route_block": {"bytes": 344000, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "route_scan": {"bytes": 146208, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "route_scatter": {"bytes": 1209440, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
@@ -157,9 +157,9 @@ TRAFFIC = {
         "split_router": {"bytes": 4206784, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
     "batched_stack_zipf": {
-        "combine": {"bytes": 5270293, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "down_mfma": {"bytes": 39195098, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
-        "gateup_mfma": {"bytes": 69930664, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "6ce7b64402fc1785"},
+        "combine": {"bytes": 5270368, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "down_mfma": {"bytes": 39195102, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "gateup_mfma": {"bytes": 69929131, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
         "route_small": {"bytes": 2148644, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "router_split": {"bytes": 3694967, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
