@@ -143,17 +143,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc(vh, 0, cap * D * 2, kBufferWord3);
   const int koff = 2 * (c16 * 32 + 8 * g), voff = 2 * ((c16 * 4 + g) * 8);
-  auto load = [&](int t, uint4 (&kk)[2 * NS], uint4 (&vv)[ND]) {
+  // descriptors with no records: a load through them returns zeros and reads
+  // no memory (the prefetch past a wave's last tile)
+  const __amdgpu_buffer_rsrc_t rnone = __builtin_amdgcn_make_buffer_rsrc(kh, 0, 0, kBufferWord3);
+  auto load = [&](int t, uint4 (&kk)[2 * NS], uint4 (&vv)[ND], bool live) {
+    const auto rk_t = live ? rk : rnone, rv_t = live ? rv : rnone;
     const int tb = (SLIDE ? (t * kT) % cap : t * kT) * D * 2;  // byte offset of the tile
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int be = 0; be < 2; ++be)
         kk[2 * s + be] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(
-            rk, koff + 2 * (s * kT + 16 * be) * 32, tb, 0));
+            rk_t, koff + 2 * (s * kT + 16 * be) * 32, tb, 0));
 #pragma unroll
     for (int dl = 0; dl < ND; ++dl)
-      vv[dl] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rv, voff + 2 * 16 * dl * 4 * 8, tb, 0));
+      vv[dl] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rv_t, voff + 2 * 16 * dl * 4 * 8, tb, 0));
   };
 
   // One tile: the new token's row patched in, masked rows cleared, scores,
@@ -263,17 +267,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   };
 
   // Two register sets in turn: the next tile's loads go out before this
-  // tile's work, always (the current tile again after the last, an L2 hit),
-  // so the waits before this tile's MFMAs never drain them.
+  // tile's work, always (past the wave's last tile through the descriptors
+  // with no records), so the waits before this tile's MFMAs never drain them.
   int t = ts + wave;
   if (t < te) {
-    load(t, ka, va);
+    load(t, ka, va, true);
     for (;;) {
-      load(t + kNW < te ? t + kNW : t, kb, vb);
+      load(t + kNW, kb, vb, t + kNW < te);
       tile(t, ka, va);
       t += kNW;
       if (t >= te) break;
-      load(t + kNW < te ? t + kNW : t, ka, va);
+      load(t + kNW, ka, va, t + kNW < te);
       tile(t, kb, vb);
       t += kNW;
       if (t >= te) break;
