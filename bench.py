@@ -163,6 +163,11 @@ TRAFFIC = {
         "route_small": {"bytes": 2148644, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "router_split": {"bytes": 3694967, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
+    "hybrid_attn_decode": {
+        "attn_combine": {"bytes": 1098556, "sources": ["attn.hip", "internal.h", "wave.h"], "digest": "a964e9de4f88bd05"},
+        "attn_global": {"bytes": 269687732, "sources": ["attn.hip", "internal.h", "wave.h"], "digest": "a964e9de4f88bd05"},
+        "attn_window": {"bytes": 1122883, "sources": ["attn.hip", "internal.h", "wave.h"], "digest": "a964e9de4f88bd05"},
+    },
 }
 
 
