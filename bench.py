@@ -168,6 +168,18 @@ TRAFFIC = {
         "attn_global": {"bytes": 269687732, "sources": ["attn.hip", "internal.h", "wave.h"], "digest": "a964e9de4f88bd05"},
         "attn_window": {"bytes": 1122883, "sources": ["attn.hip", "internal.h", "wave.h"], "digest": "a964e9de4f88bd05"},
     },
+    "prefill_16384": {
+        "combine": {"bytes": 694633812, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "down_mfma": {"bytes": 765244036, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "gateup_mfma": {"bytes": 912822520, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "quant_x": {"bytes": 143332496, "sources": ["digits.h", "grouped.hip", "internal.h", "limbs.h", "quant.h", "wave.h"], "digest": "5543a65d10b19445"},
+        "route_block": {"bytes": 1327104, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scan": {"bytes": 564576, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_scatter": {"bytes": 4767776, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "route_topk": {"bytes": 17858240, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "router_mfma": {"bytes": 253037740, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+        "split_router": {"bytes": 4207272, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
+    },
 }
 
 
