@@ -180,6 +180,16 @@ TRAFFIC = {
         "router_mfma": {"bytes": 253037740, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
         "split_router": {"bytes": 4207272, "sources": ["digits.h", "internal.h", "limbs.h", "quant.h", "route.hip", "wave.h"], "digest": "72b93e69c0213f7a"},
     },
+    "flashhead_decode": {
+        "head_final": {"bytes": 10688, "sources": ["head.hip", "internal.h", "wave.h"], "digest": "67332216d341ad8c"},
+        "head_scores": {"bytes": 19559239, "sources": ["head.hip", "internal.h", "wave.h"], "digest": "67332216d341ad8c"},
+        "head_search": {"bytes": 58789133, "sources": ["head.hip", "internal.h", "wave.h"], "digest": "67332216d341ad8c"},
+        "head_select": {"bytes": 52057, "sources": ["head.hip", "internal.h", "wave.h"], "digest": "67332216d341ad8c"},
+    },
+    "ternary_convert": {
+        "ternarize_g32": {"bytes": 606126446, "sources": ["convert.hip", "internal.h"], "digest": "030a18b7bb2f229e"},
+        "ternarize_w2": {"bytes": 1209147332, "sources": ["convert.hip", "internal.h"], "digest": "030a18b7bb2f229e"},
+    },
 }
 
 
